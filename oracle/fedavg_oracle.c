@@ -1,0 +1,341 @@
+/*
+ * FedAvg aggregation oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow CPU statement of what server-side federated averaging
+ * computes.  Only the test suite, the smoke check and the bench's CPU-baseline
+ * leg may load this library; the product path never does.  It shares no code
+ * with the HIP library.
+ *
+ * What is computed, and where it comes from:
+ *
+ *  - The server combines the clients' models either as a plain average or
+ *    weighted by what each client contributed ("NVIDIA Clara implements
+ *    federated learning", epnc.co.kr, introduction and the server-side
+ *    workflow section, which names a weighted aggregation algorithm).  The
+ *    weight of client k is its sample count n_k, which each participant
+ *    reports per round (gist.science summary of the measurement-based adaptive
+ *    data partitioning paper, section "The adaptive controller",
+ *    "Measurement").  So for every parameter i
+ *
+ *        out_i = sum_{k in C_i} n_k * x_{k,i} / W_i,   W_i = sum_{k in C_i} n_k
+ *
+ *    with C_i the clients (n_k > 0) that sent parameter i.  In delta mode the
+ *    clients send deltas and out_i = base_i + that weighted mean.
+ *
+ *  - Clients may update only some model components; the update contract says
+ *    which, and component updates are averaged over the clients that sent them
+ *    ("Building Federated Multimodal AI Workflows with NVIDIA FLARE",
+ *    ai-thai.com, sections "Client Update Contract" and the FedUMM
+ *    adapter-only example).  Clients may also share only part of their weight
+ *    update, each choosing the fraction (Clara page, introduction and
+ *    client-side workflow section).  Hence C_i depends on i, and a parameter
+ *    no contributing client sent keeps the global value: out_i = base_i.
+ *
+ *  - A client whose weight is zero contributes nothing (the Ulysses sequence
+ *    parallelism page, section "Automatic weighted loss aggregation", makes
+ *    the same point for ranks holding only padding).
+ *
+ *  - Weights are stored in fp32 and rounded to nearest-even, never
+ *    stochastically ("NVFP4 training with JAX and MaxText", ai-thai.com,
+ *    training-recipe section on stochastic rounding and the data-flow figure
+ *    of a linear layer with fp32 master weights).  The oracle therefore returns
+ *    ref32_i = round_to_nearest_fp32(exact value); bf16 outputs are compared
+ *    against it.
+ *
+ * Arithmetic: every client value has at most 24 significant bits and every
+ * n_k fits in 24 bits, so each product n_k * x_{k,i} is exact in fp64.  The
+ * fp64 sum of at most 64 such products is within 64 * 2^-53 * M_i of the
+ * exact sum, where M_i = |base_i| + sum n_k |x_{k,i}| / W_i is also returned
+ * (the scale of the forward error of any floating-point weighted sum).  The
+ * result is rounded once to fp32 (after an fp64 add of the base in delta
+ * mode).  The exact-rational brute force in oracle/exact.py pins this.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_WEIGHTS = 0, ORC_DELTAS = 1 };
+enum {
+    ORC_OK = 0,
+    ORC_ERR_ARG = -1,
+    ORC_ERR_ZERO_WEIGHT = -4,
+    ORC_ERR_INDEX = -7,
+    ORC_ERR_NOMEM = -10
+};
+
+/* Value of element i of a buffer of the given type, widened exactly. */
+static double value_at(const void *buf, int dtype, int64_t i)
+{
+    if (dtype == ORC_F32)
+        return (double)((const float *)buf)[i];
+    /* bf16 is the upper half of an IEEE binary32 bit pattern */
+    uint32_t bits = ((uint32_t)((const uint16_t *)buf)[i]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static int dtype_ok(int d) { return d == ORC_F32 || d == ORC_BF16; }
+
+/*
+ * Resolve one parameter from its per-client sums.
+ *   s = sum n_k x_k, m = sum n_k |x_k|, W = sum n_k over the senders.
+ */
+static int resolve(double s, double m, uint64_t W, int mode, const void *base,
+                   int base_dtype, int64_t i, float *ref32, double *mag)
+{
+    double b = base ? value_at(base, base_dtype, i) : 0.0;
+    if (W == 0) {
+        /* nobody sent this parameter: the global value is kept as it is */
+        if (!base)
+            return ORC_ERR_ZERO_WEIGHT;
+        *ref32 = (float)b;
+        *mag = fabs(b);
+        return ORC_OK;
+    }
+    double mean = s / (double)W;
+    double r = (mode == ORC_DELTAS) ? b + mean : mean;
+    *ref32 = (float)r; /* one rounding to nearest-even */
+    *mag = (mode == ORC_DELTAS ? fabs(b) : 0.0) + m / (double)W;
+    return ORC_OK;
+}
+
+/*
+ * Weighted average over an explicit sent relation.
+ *   x[k]      client k's N values (type x_dtype)
+ *   n[k]      client k's sample count, >= 0
+ *   sent      NULL (every client sent every parameter) or K arrays of N bytes
+ *   base      N values of type base_dtype, or NULL (only allowed when every
+ *             parameter has a sender in weights mode)
+ * Outputs (N each): ref32, mag; count and wsum may be NULL.
+ */
+int orc_weighted_average(int K, const void *const *x, int x_dtype, const int64_t *n,
+                         const uint8_t *const *sent, int64_t N, int mode,
+                         const void *base, int base_dtype, float *ref32, double *mag,
+                         uint32_t *count, uint64_t *wsum)
+{
+    if (K < 1 || N < 0 || !x || !n || !ref32 || !mag || !dtype_ok(x_dtype))
+        return ORC_ERR_ARG;
+    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS)
+        return ORC_ERR_ARG;
+    if (base && !dtype_ok(base_dtype))
+        return ORC_ERR_ARG;
+    if (mode == ORC_DELTAS && !base)
+        return ORC_ERR_ARG;
+    for (int k = 0; k < K; ++k)
+        if (n[k] < 0 || (n[k] > 0 && !x[k]))
+            return ORC_ERR_ARG;
+
+    for (int64_t i = 0; i < N; ++i) {
+        double s = 0.0, m = 0.0;
+        uint64_t W = 0;
+        uint32_t c = 0;
+        for (int k = 0; k < K; ++k) {
+            if (n[k] == 0)
+                continue;
+            if (sent && !sent[k][i])
+                continue;
+            double v = value_at(x[k], x_dtype, i);
+            s += (double)n[k] * v;
+            m += (double)n[k] * fabs(v);
+            W += (uint64_t)n[k];
+            c += 1;
+        }
+        int rc = resolve(s, m, W, mode, base, base_dtype, i, &ref32[i], &mag[i]);
+        if (rc != ORC_OK)
+            return rc;
+        if (count)
+            count[i] = c;
+        if (wsum)
+            wsum[i] = W;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Sparse partial sharing: client k sends nnz[k] (index, value) pairs with
+ * strictly increasing indices below N.  Parameters a client did not send are
+ * not part of its contribution.  Accumulation runs client by client.
+ */
+int orc_sparse_average(int K, const int64_t *const *idx, const float *const *val,
+                       const int64_t *nnz, const int64_t *n, int64_t N, int mode,
+                       const float *base, float *ref32, double *mag, uint32_t *count,
+                       uint64_t *wsum)
+{
+    if (K < 1 || N < 0 || !idx || !val || !nnz || !n || !ref32 || !mag)
+        return ORC_ERR_ARG;
+    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS)
+        return ORC_ERR_ARG;
+    if (mode == ORC_DELTAS && !base)
+        return ORC_ERR_ARG;
+    for (int k = 0; k < K; ++k)
+        if (n[k] < 0 || nnz[k] < 0 || (nnz[k] > 0 && (!idx[k] || !val[k])))
+            return ORC_ERR_ARG;
+
+    double *s = calloc((size_t)(N ? N : 1), sizeof(double));
+    double *m = calloc((size_t)(N ? N : 1), sizeof(double));
+    uint64_t *W = calloc((size_t)(N ? N : 1), sizeof(uint64_t));
+    uint32_t *c = calloc((size_t)(N ? N : 1), sizeof(uint32_t));
+    int rc = ORC_OK;
+    if (!s || !m || !W || !c) {
+        rc = ORC_ERR_NOMEM;
+        goto done;
+    }
+    for (int k = 0; k < K && rc == ORC_OK; ++k) {
+        if (n[k] == 0)
+            continue;
+        for (int64_t j = 0; j < nnz[k]; ++j) {
+            int64_t i = idx[k][j];
+            if (i < 0 || i >= N || (j > 0 && i <= idx[k][j - 1])) {
+                rc = ORC_ERR_INDEX;
+                break;
+            }
+            double v = (double)val[k][j];
+            s[i] += (double)n[k] * v;
+            m[i] += (double)n[k] * fabs(v);
+            W[i] += (uint64_t)n[k];
+            c[i] += 1;
+        }
+    }
+    for (int64_t i = 0; i < N && rc == ORC_OK; ++i) {
+        rc = resolve(s[i], m[i], W[i], mode, base, ORC_F32, i, &ref32[i], &mag[i]);
+        if (count)
+            count[i] = c[i];
+        if (wsum)
+            wsum[i] = W[i];
+    }
+done:
+    free(s);
+    free(m);
+    free(W);
+    free(c);
+    return rc;
+}
+
+/* Position of i in the sorted list a[0..len), or -1 if absent. */
+static int64_t find_sorted(const int64_t *a, int64_t len, int64_t i)
+{
+    int64_t lo = 0, hi = len;
+    while (lo < hi) {
+        int64_t mid = lo + (hi - lo) / 2;
+        if (a[mid] < i)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return (lo < len && a[lo] == i) ? lo : -1;
+}
+
+/*
+ * The same definition evaluated only at the parameters listed in at[0..S):
+ * for each one, every client's list is searched for it.  Does not re-check
+ * that the lists are sorted (the full version above does).
+ */
+int orc_sparse_average_at(int K, const int64_t *const *idx, const float *const *val,
+                          const int64_t *nnz, const int64_t *n, int64_t N, int mode,
+                          const float *base, int64_t S, const int64_t *at, float *ref32,
+                          double *mag, uint32_t *count, uint64_t *wsum)
+{
+    if (K < 1 || N < 0 || S < 0 || !idx || !val || !nnz || !n || !at || !ref32 || !mag)
+        return ORC_ERR_ARG;
+    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS)
+        return ORC_ERR_ARG;
+    if (mode == ORC_DELTAS && !base)
+        return ORC_ERR_ARG;
+    for (int64_t q = 0; q < S; ++q) {
+        int64_t i = at[q];
+        if (i < 0 || i >= N)
+            return ORC_ERR_ARG;
+        double s = 0.0, m = 0.0;
+        uint64_t W = 0;
+        uint32_t c = 0;
+        for (int k = 0; k < K; ++k) {
+            if (n[k] <= 0)
+                continue;
+            int64_t j = find_sorted(idx[k], nnz[k], i);
+            if (j < 0)
+                continue;
+            double v = (double)val[k][j];
+            s += (double)n[k] * v;
+            m += (double)n[k] * fabs(v);
+            W += (uint64_t)n[k];
+            c += 1;
+        }
+        /* base is indexed by parameter, so resolve against base[i] */
+        double b = base ? (double)base[i] : 0.0;
+        if (W == 0) {
+            if (!base)
+                return ORC_ERR_ZERO_WEIGHT;
+            ref32[q] = (float)b;
+            mag[q] = fabs(b);
+        } else {
+            double mean = s / (double)W;
+            ref32[q] = (float)(mode == ORC_DELTAS ? b + mean : mean);
+            mag[q] = (mode == ORC_DELTAS ? fabs(b) : 0.0) + m / (double)W;
+        }
+        if (count)
+            count[q] = c;
+        if (wsum)
+            wsum[q] = W;
+    }
+    return ORC_OK;
+}
+
+/*
+ * fp32 -> bf16, round to nearest with ties to even, from the formats'
+ * definition: bf16 keeps the sign, the 8 exponent bits and the top 7 fraction
+ * bits of binary32.  The 16 dropped bits decide: above half an ulp rounds up,
+ * below rounds down, exactly half rounds to the even result.  A carry out of
+ * the fraction increments the exponent (the largest finite values round to
+ * infinity).  NaN stays NaN (quiet, same sign).
+ */
+void orc_round_to_bf16(const float *in, uint16_t *out, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        uint32_t u;
+        memcpy(&u, &in[i], sizeof u);
+        uint32_t exp_bits = (u >> 23) & 0xFFu;
+        uint32_t frac = u & 0x7FFFFFu;
+        if (exp_bits == 0xFFu && frac != 0) {
+            out[i] = (uint16_t)((u >> 16) | 0x0040u);
+            continue;
+        }
+        uint32_t hi = u >> 16;
+        uint32_t lo = u & 0xFFFFu;
+        if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))
+            hi += 1;
+        out[i] = (uint16_t)hi;
+    }
+}
+
+/*
+ * Order-independent checksum of a buffer of elements of the given type:
+ * H = sum over i of fmix64(i * 0x9E3779B97F4A7C15 XOR bits_i), modulo
+ * 2^64, where bits_i is the element's raw bit pattern (16 or 32 bits) and
+ * fmix64 is the 64-bit finalizer of Austin Appleby's MurmurHash3.
+ */
+static uint64_t fmix64(uint64_t k)
+{
+    k ^= k >> 33;
+    k *= 0xff51afd7ed558ccdULL;
+    k ^= k >> 33;
+    k *= 0xc4ceb9fe1a85ec53ULL;
+    k ^= k >> 33;
+    return k;
+}
+
+uint64_t orc_checksum(const void *buf, int64_t count, int dtype, int64_t first)
+{
+    /* `first` is the index of buf[0] in the whole buffer, so the checksum of
+       a buffer is the sum of the checksums of its pieces */
+    uint64_t h = 0;
+    for (int64_t j = 0; j < count; ++j) {
+        uint64_t bits = (dtype == ORC_F32) ? (uint64_t)((const uint32_t *)buf)[j]
+                                           : (uint64_t)((const uint16_t *)buf)[j];
+        uint64_t i = (uint64_t)(first + j);
+        h += fmix64((i * 0x9E3779B97F4A7C15ULL) ^ bits);
+    }
+    return h;
+}

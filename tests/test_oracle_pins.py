@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something other than its own formula:
+hand-worked values, the exact-rational brute force, closed forms and
+invariants of a weighted mean, or a library routine for a special case.
+Together they are chosen so that a dropped term, a wrong sign, a wrong index,
+a swapped operand or a wrong denominator fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import exact
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _f32(vals):
+    return np.asarray(vals, dtype=np.float32)
+
+
+def _mode(name):
+    return oracle.DELTAS if name == "deltas" else oracle.WEIGHTS
+
+
+# --------------------------------------------------------------------------
+# hand-worked examples
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", _golden()["dense"], ids=lambda c: c["name"])
+def test_hand_worked_dense(case):
+    base = _f32(case["base"]) if "base" in case else None
+    ref, mag, cnt, ws = oracle.weighted_average([_f32(x) for x in case["x"]], case["n"],
+                                                mode=_mode(case["mode"]), base=base)
+    np.testing.assert_array_equal(ref, _f32(case["expect"]))
+    for r, h in zip(ref, case.get("expect_hex", [])):
+        if h is not None:
+            assert int(np.float32(r).view(np.uint32)) == int(h, 16)
+
+
+@pytest.mark.parametrize("case", _golden()["masked"], ids=lambda c: c["name"])
+def test_hand_worked_masked(case):
+    bounds = case["segments"]
+    N = bounds[-1]
+    sent = []
+    for pres in case["present"]:
+        s = np.zeros(N, np.uint8)
+        for t, p in enumerate(pres):
+            s[bounds[t]:bounds[t + 1]] = p
+        sent.append(s)
+    ref, mag, cnt, ws = oracle.weighted_average([_f32(x) for x in case["x"]], case["n"],
+                                                mode=_mode(case["mode"]), base=_f32(case["base"]),
+                                                sent=sent)
+    np.testing.assert_array_equal(ref, _f32(case["expect"]))
+    np.testing.assert_array_equal(cnt, case["expect_count"])
+
+
+@pytest.mark.parametrize("case", _golden()["sparse"], ids=lambda c: c["name"])
+def test_hand_worked_sparse(case):
+    ref, mag, cnt, ws = oracle.sparse_average(case["idx"], case["val"], case["n"], case["N"],
+                                              mode=_mode(case["mode"]), base=_f32(case["base"]))
+    np.testing.assert_array_equal(ref, _f32(case["expect"]))
+    np.testing.assert_array_equal(cnt, case["expect_count"])
+    np.testing.assert_array_equal(ws, case["expect_wsum"])
+
+
+# --------------------------------------------------------------------------
+# exact-rational brute force on tiny random inputs
+# --------------------------------------------------------------------------
+
+def _special_values():
+    f = np.float32
+    return np.array([0.0, -0.0, 1.0, -1.0, f(1e-40), f(-3e-39), f(1e-45), f(3.3e38), f(-3.3e38),
+                     f(1.5), f(0.1), f(-2.5e-8), f(65504.0), f(1.17549435e-38)], dtype=np.float32)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 5])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["weights", "deltas"])
+def test_brute_force_dense(K, dtype, mode):
+    r = np.random.default_rng(100 + K)
+    N = 48
+    xs32 = [(r.standard_normal(N) * 10.0 ** r.integers(-3, 3)).astype(np.float32) for _ in range(K)]
+    xs32[0][:8] = _special_values()[:8]
+    n = r.integers(0, 2000, size=K)
+    n[0] = max(n[0], 1)
+    base32 = (r.standard_normal(N) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        xs = [synth.bf16_bits_from_f32(x) for x in xs32]
+        vals = [synth.f32_from_bf16_bits(x) for x in xs]
+        dt = oracle.BF16
+    else:
+        xs, vals, dt = xs32, xs32, oracle.F32
+    base = base32 if mode == "deltas" else None
+    ref, mag, cnt, ws = oracle.weighted_average(xs, n, mode=_mode(mode), base=base, x_dtype=dt)
+    want = exact.weighted_average_exact([v.astype(np.float64).tolist() for v in vals], n.tolist(),
+                                        mode=mode, base=None if base is None else base.tolist())
+    want = np.asarray(want, dtype=np.float32)
+    # fp64 accumulation can only differ from the exact result within 64*2^-53*M
+    # of a rounding boundary; on these inputs that never happens
+    np.testing.assert_array_equal(ref, want)
+
+
+def test_brute_force_masked_and_sparse():
+    r = np.random.default_rng(7)
+    K, N = 4, 40
+    xs = [r.standard_normal(N).astype(np.float32) for _ in range(K)]
+    sent = [(r.random(N) < 0.5).astype(np.uint8) for _ in range(K)]
+    n = r.integers(1, 100, size=K)
+    base = r.standard_normal(N).astype(np.float32)
+    ref, _, cnt, ws = oracle.weighted_average(xs, n, mode=oracle.DELTAS, base=base, sent=sent)
+    want = exact.weighted_average_exact([x.tolist() for x in xs], n.tolist(), mode="deltas",
+                                        base=base.tolist(), sent=[s.tolist() for s in sent])
+    np.testing.assert_array_equal(ref, np.asarray(want, np.float32))
+    # the same data expressed as sparse lists
+    idx = [np.nonzero(s)[0] for s in sent]
+    val = [x[i] for x, i in zip(xs, idx)]
+    sref, _, scnt, sws = oracle.sparse_average(idx, val, n, N, mode=oracle.DELTAS, base=base)
+    np.testing.assert_array_equal(sref, ref)
+    np.testing.assert_array_equal(scnt, cnt)
+    np.testing.assert_array_equal(sws, ws)
+
+
+def test_exact_rounding_helper_against_numpy():
+    # the brute force's own fp32 rounding agrees with numpy's binary32
+    # conversion of doubles whose value it represents exactly
+    r = np.random.default_rng(3)
+    vals = np.concatenate([r.standard_normal(500) * 10.0 ** r.integers(-40, 38, 500),
+                           [1e-45, 7e-46, 3.5e-45, 3.4028235e38, 3.4028236e38, 1e39]])
+    from fractions import Fraction
+    for v in vals:
+        assert exact.round_fp32(Fraction(float(v))) == float(np.float32(v)) or \
+            (math.isinf(exact.round_fp32(Fraction(float(v)))) and math.isinf(np.float32(v)))
+
+
+# --------------------------------------------------------------------------
+# closed forms and invariants of a weighted mean
+# --------------------------------------------------------------------------
+
+def test_single_client_is_identity():
+    x = synth.normal_f32(1, synth.ROLE_VALUES, 0, 10000, 0.02)
+    for nk in (1, 3, 977, 2 ** 24):
+        ref, mag, cnt, ws = oracle.weighted_average([x], [nk])
+        np.testing.assert_array_equal(ref, x)
+        assert (cnt == 1).all() and (ws == nk).all()
+
+
+def test_identical_clients_reproduce_input():
+    x = synth.normal_f32(1, synth.ROLE_VALUES, 1, 5000, 0.02)
+    n = synth.sample_counts(1, 16, 100, 1000)
+    ref, *_ = oracle.weighted_average([x] * 16, n)
+    np.testing.assert_array_equal(ref, x)
+    bits = synth.bf16_bits_from_f32(x)
+    ref, *_ = oracle.weighted_average([bits] * 16, n, x_dtype=oracle.BF16)
+    np.testing.assert_array_equal(ref, synth.f32_from_bf16_bits(bits))
+
+
+def test_normalised_weights_sum_to_one():
+    # all-ones clients give exactly 1 only if the weights n_k/W sum to 1
+    n = synth.sample_counts(3, 32, 100, 10000)
+    ones = [np.ones(64, np.float32)] * 32
+    ref, *_ = oracle.weighted_average(ones, n)
+    np.testing.assert_array_equal(ref, np.ones(64, np.float32))
+    w = n.astype(np.float64) / n.sum()
+    assert abs(w.sum() - 1.0) <= 32 * 2.0 ** -53
+
+
+def test_linearity():
+    K, N = 6, 3000
+    n = synth.sample_counts(1, K, 100, 1000)
+    X = synth.dense_clients_f32(1, K, N, 0.02)
+    Y = synth.dense_clients_f32(9, K, N, 0.5)
+    a, b = 0.75, -3.0  # exact in binary32 combinations below
+    Z = [(a * x.astype(np.float64) + b * y.astype(np.float64)).astype(np.float32) for x, y in zip(X, Y)]
+    rx, mx, *_ = oracle.weighted_average(X, n)
+    ry, my, *_ = oracle.weighted_average(Y, n)
+    rz, mz, *_ = oracle.weighted_average(Z, n)
+    lhs = rz.astype(np.float64)
+    rhs = a * rx.astype(np.float64) + b * ry.astype(np.float64)
+    scale = np.maximum(mz, abs(a) * mx + abs(b) * my)
+    assert np.all(np.abs(lhs - rhs) <= 4 * 2.0 ** -24 * scale)
+
+
+def test_weight_scale_invariance():
+    K, N = 5, 2000
+    n = synth.sample_counts(1, K, 100, 1000)
+    X = synth.dense_clients_f32(2, K, N, 0.02)
+    r1, *_ = oracle.weighted_average(X, n)
+    r2, *_ = oracle.weighted_average(X, n * 8)      # power of two: bit-identical
+    np.testing.assert_array_equal(r1, r2)
+    r3, *_ = oracle.weighted_average(X, n * 3)
+    assert np.max(np.abs(r3.view(np.int32).astype(np.int64) - r1.view(np.int32).astype(np.int64))) <= 1
+
+
+def test_client_permutation():
+    K, N = 7, 2000
+    n = synth.sample_counts(4, K, 100, 1000)
+    X = synth.dense_clients_f32(4, K, N, 0.02)
+    perm = np.random.default_rng(0).permutation(K)
+    r1, *_ = oracle.weighted_average(X, n)
+    r2, *_ = oracle.weighted_average([X[p] for p in perm], n[perm])
+    d = np.abs(r1.view(np.int32).astype(np.int64) - r2.view(np.int32).astype(np.int64))
+    assert d.max() <= 1
+
+
+def test_uniform_weights_equal_numpy_mean():
+    K, N = 9, 4000
+    X = synth.dense_clients_f32(5, K, N, 0.02)
+    ref, *_ = oracle.weighted_average(X, [42] * K)
+    want = np.mean(np.stack(X).astype(np.float64), axis=0).astype(np.float32)
+    d = np.abs(ref.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert d.max() <= 1 and (d == 0).mean() > 0.999
+
+
+def test_masks_all_one_and_none():
+    K, N = 4, 1000
+    n = synth.sample_counts(2, K, 500, 5000)
+    X = synth.dense_clients_f32(2, K, N, 0.01)
+    base = synth.normal_f32(2, synth.ROLE_BASE, 0, N, 0.01)
+    dense, *_ = oracle.weighted_average(X, n)
+    allsent, *_ = oracle.weighted_average(X, n, base=base, sent=[np.ones(N, np.uint8)] * K)
+    np.testing.assert_array_equal(dense, allsent)
+    none, _, cnt, ws = oracle.weighted_average(X, n, base=base, sent=[np.zeros(N, np.uint8)] * K)
+    np.testing.assert_array_equal(none, base)
+    assert (cnt == 0).all() and (ws == 0).all()
+    # exactly one sender per parameter: that sender's value
+    owner = np.random.default_rng(1).integers(0, K, N)
+    sent = [(owner == k).astype(np.uint8) for k in range(K)]
+    one, *_ = oracle.weighted_average(X, n, base=base, sent=sent)
+    np.testing.assert_array_equal(one, np.choose(owner, X))
+
+
+def test_no_sender_and_no_base_is_an_error():
+    with pytest.raises(oracle.OracleError):
+        oracle.weighted_average([np.ones(4, np.float32)], [1], sent=[np.zeros(4, np.uint8)])
+    with pytest.raises(oracle.OracleError):
+        oracle.weighted_average([np.ones(4, np.float32)], [-1])
+
+
+def test_sparse_full_support_equals_dense_deltas():
+    K, N = 5, 3000
+    n = synth.sample_counts(5, K, 100, 1000)
+    D = synth.dense_clients_f32(5, K, N, 1e-3)
+    base = synth.normal_f32(5, synth.ROLE_BASE, 0, N, 0.02)
+    full = [np.arange(N)] * K
+    sref, _, scnt, sws = oracle.sparse_average(full, D, n, N, base=base)
+    dref, *_ = oracle.weighted_average(D, n, mode=oracle.DELTAS, base=base)
+    np.testing.assert_array_equal(sref, dref)
+    assert (scnt == K).all() and (sws == n.sum()).all()
+
+
+def test_sparse_disjoint_supports_add_the_delta():
+    K, N = 4, 4000
+    n = synth.sample_counts(5, K, 100, 1000)
+    owner = np.random.default_rng(2).integers(-1, K, N)   # -1: nobody
+    base = synth.normal_f32(5, synth.ROLE_BASE, 0, N, 0.02)
+    D = synth.dense_clients_f32(6, K, N, 1e-3)
+    idx = [np.nonzero(owner == k)[0] for k in range(K)]
+    val = [D[k][i] for k, i in enumerate(idx)]
+    ref, _, cnt, ws = oracle.sparse_average(idx, val, n, N, base=base)
+    want = base.copy()
+    for k in range(K):
+        want[idx[k]] = base[idx[k]] + val[k]   # binary32 add is correctly rounded
+    np.testing.assert_array_equal(ref, want)
+    np.testing.assert_array_equal(cnt, (owner >= 0).astype(np.uint32))
+
+
+def test_sparse_counts_and_weight_sums_are_bincounts():
+    K, N = 6, 5000
+    n = synth.sample_counts(5, K, 100, 1000)
+    base = synth.normal_f32(5, synth.ROLE_BASE, 0, N, 0.02)
+    idx, val = zip(*[synth.topk_sparse_deltas(5, k, N, 0.1, 1e-3) for k in range(K)])
+    ref, _, cnt, ws = oracle.sparse_average(idx, val, n, N, base=base)
+    allidx = np.concatenate(idx)
+    np.testing.assert_array_equal(cnt, np.bincount(allidx, minlength=N))
+    wts = np.concatenate([np.full(len(i), n[k], np.float64) for k, i in enumerate(idx)])
+    np.testing.assert_array_equal(ws, np.bincount(allidx, weights=wts, minlength=N).astype(np.uint64))
+    # unsent parameters keep the base bit for bit
+    np.testing.assert_array_equal(ref[cnt == 0], base[cnt == 0])
+
+
+def test_sparse_at_matches_full():
+    K, N = 5, 6000
+    n = synth.sample_counts(5, K, 100, 1000)
+    base = synth.normal_f32(5, synth.ROLE_BASE, 0, N, 0.02)
+    idx, val = zip(*[synth.topk_sparse_deltas(5, k, N, 0.1, 1e-3) for k in range(K)])
+    ref, mag, cnt, ws = oracle.sparse_average(idx, val, n, N, base=base)
+    at = np.random.default_rng(0).choice(N, 500, replace=False)
+    r2, m2, c2, w2 = oracle.sparse_average_at(idx, val, n, N, at, base=base)
+    np.testing.assert_array_equal(r2, ref[at])
+    np.testing.assert_array_equal(c2, cnt[at])
+    np.testing.assert_array_equal(w2, ws[at])
+
+
+def test_sparse_rejects_unsorted_or_out_of_range():
+    base = np.zeros(8, np.float32)
+    with pytest.raises(oracle.OracleError):
+        oracle.sparse_average([[3, 2]], [[1.0, 1.0]], [1], 8, base=base)
+    with pytest.raises(oracle.OracleError):
+        oracle.sparse_average([[1, 1]], [[1.0, 1.0]], [1], 8, base=base)
+    with pytest.raises(oracle.OracleError):
+        oracle.sparse_average([[8]], [[1.0]], [1], 8, base=base)
+
+
+def test_nan_propagates_and_zero_weight_nan_is_skipped():
+    x0 = np.array([np.nan, 1.0], np.float32)
+    x1 = np.array([2.0, 3.0], np.float32)
+    ref, *_ = oracle.weighted_average([x0, x1], [1, 1])
+    assert math.isnan(ref[0]) and ref[1] == 2.0
+    ref, *_ = oracle.weighted_average([x0, x1], [0, 1])
+    np.testing.assert_array_equal(ref, x1)
+
+
+def test_bf16_rounding_matches_library_conversion():
+    # round-to-nearest-even to bf16 is what torch's dtype conversion does
+    import torch
+    r = np.random.default_rng(11)
+    a = np.concatenate([r.standard_normal(20000).astype(np.float32),
+                        np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, 3.4028235e38, 1e-40,
+                                  -1e-45, 1.0039062, 1.0117188], np.float32)])
+    # exact ties: low half exactly 0x8000 with odd and even upper halves
+    ties = (np.arange(0x3f80, 0x3f90, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    a = np.concatenate([a, ties])
+    ours = oracle.round_to_bf16(a)
+    lib = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, lib)
+    q = oracle.round_to_bf16(np.array([np.nan, -np.nan], np.float32))
+    assert all((v & 0x7f80) == 0x7f80 and (v & 0x7f) != 0 for v in q)
+
+
+def test_checksum_split_additivity_and_sensitivity():
+    r = np.random.default_rng(5)
+    a = r.standard_normal(1000).astype(np.float32)
+    h = oracle.checksum(a, oracle.F32)
+    # the checksum of a buffer equals the sum (mod 2^64) of its pieces', for
+    # any split, so it does not depend on the order elements are visited
+    for m in (1, 333, 999):
+        parts = oracle.checksum(a[:m], oracle.F32) + oracle.checksum(a[m:], oracle.F32, first=m)
+        assert h == parts % 2 ** 64
+    b = a.copy()
+    b[500] = np.nextafter(b[500], np.float32(np.inf))
+    assert oracle.checksum(b, oracle.F32) != h
+    # swapping two different values changes it (indices are part of the hash)
+    c = a.copy()
+    c[[3, 4]] = c[[4, 3]]
+    assert oracle.checksum(c, oracle.F32) != h
+    # bf16 buffers hash their 16-bit patterns
+    bits = synth.bf16_bits_from_f32(a)
+    assert oracle.checksum(bits, oracle.BF16) != oracle.checksum(bits ^ np.uint16(1), oracle.BF16)
+
+
+def test_topk_generator_support_and_tail():
+    N = 10007
+    idx, val = synth.topk_sparse_deltas(5, 0, N, 0.1, 1e-3)
+    assert len(idx) == N // 10
+    assert np.all(np.diff(idx) > 0) and idx[0] >= 0 and idx[-1] < N
+    # top-10% of Laplace(0,b) magnitudes sit above about b*ln(10)
+    assert np.quantile(np.abs(val), 0.05) > 0.8 * 1e-3 * math.log(10)
