@@ -1,0 +1,282 @@
+/*
+ * fedavg.h -- C ABI of the MI355X FedAvg aggregation library (libfedavg.so).
+ *
+ * Server-side federated averaging: the server combines the models (or model
+ * deltas) sent by K clients into one global model, weighting client k by its
+ * sample count n_k.  For every parameter i
+ *
+ *     out_i = sum_{k in C_i} n_k * x_{k,i} / W_i           (FA_WEIGHTS)
+ *     out_i = base_i + sum_{k in C_i} n_k * d_{k,i} / W_i  (FA_DELTAS)
+ *     W_i   = sum_{k in C_i} n_k
+ *
+ * where C_i is the set of clients with n_k > 0 that sent parameter i.  A
+ * parameter that no such client sent keeps its global value: out_i = base_i.
+ *
+ * Sources of the definition:
+ *   - plain or contribution-weighted averaging of the clients' models by the
+ *     server: "NVIDIA Clara implements federated learning" (epnc.co.kr),
+ *     introduction and section "Server-side workflow" (weighted aggregation
+ *     algorithm);  n_k is the per-round sample count each participant reports
+ *     (gist.science summary of the measurement-based adaptive data
+ *     partitioning paper, section "The adaptive controller");
+ *   - component-level updates averaged over the clients that sent them, and
+ *     adapter-only federation: "Building Federated Multimodal AI Workflows with
+ *     NVIDIA FLARE" (ai-thai.com), sections "Client Update Contract" and the
+ *     FedUMM example;
+ *   - partial sharing, each client choosing the fraction of its update it
+ *     sends: the Clara page, introduction and section "Client-side workflow";
+ *   - streamed, chunk-at-a-time transfer with a tunable chunk size, and server
+ *     memory that must not grow linearly with the number of clients: the FLARE
+ *     page, sections on tensor streaming (Tensor Downloader) and "Offload
+ *     Aggregation to Disk" (Tensor Disk Offload);
+ *   - fp32 master weights, round-to-nearest-even (never stochastic rounding)
+ *     for weights: "NVFP4 training with JAX and MaxText" (ai-thai.com),
+ *     training-recipe section and the linear-layer data-flow figure.
+ *
+ * Arithmetic contract.  Accumulation is fp32 with one fused multiply-add per
+ * contributing client, in client order (resident lists: list order; streaming:
+ * arrival order), starting from 0; then one IEEE division by fp32(W_i); then,
+ * in delta mode, one fp32 addition of base_i; then round-to-nearest-even to
+ * the output type.  Results are deterministic (no floating-point atomics), and
+ * a streamed aggregation is bit-identical to the resident one over the same
+ * clients in the same order.  NaN/Inf in a contributing client propagate;
+ * fp32 denormals are kept.
+ *
+ * Conventions for every call:
+ *   - Return value: FA_OK (0) or a negative fa_status; the message of the most
+ *     recent failure on the calling thread is available from
+ *     fedavg_last_error().  No C++ exception crosses the ABI.
+ *   - Argument errors are detected and returned before any device work is
+ *     enqueued.  Device work is asynchronous on the stream(s) given (a
+ *     hipStream_t passed as void*; NULL is the default stream).
+ *   - The caller owns every device buffer, pinned host buffer and stream.
+ *     Only the streaming handle (host memory and its HIP events, plus one
+ *     internal copy stream when the caller passes none) belongs to the
+ *     library; fedavg_destroy releases it.
+ *   - Limits: K <= FA_MAX_CLIENTS resident clients per call;
+ *     0 <= n_k <= FA_MAX_WEIGHT (so fp32(n_k) is exact); sums of weights
+ *     below 2^32.
+ *   - Aliasing: `out` may be the same buffer as `base` or as one client input
+ *     (every element is read before it is written); partial overlap is not
+ *     allowed.
+ *   - Alignment: 16-byte aligned buffers take the vector path; others a
+ *     slower element-wise path with identical results.
+ */
+#ifndef FEDAVG_H
+#define FEDAVG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FEDAVG_ABI_VERSION 1
+#define FA_MAX_CLIENTS 64
+#define FA_MAX_WEIGHT (1 << 24)
+#define FA_MAX_STREAM_CLIENTS 255
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_ARG = -1,         /* bad pointer, size, count or combination */
+    FA_ERR_DTYPE = -2,       /* unsupported element type */
+    FA_ERR_RANGE = -3,       /* a limit above is exceeded */
+    FA_ERR_ZERO_WEIGHT = -4, /* dense weights mode with sum of n_k == 0 */
+    FA_ERR_STATE = -5,       /* streaming call out of order */
+    FA_ERR_INCOMPLETE = -6,  /* dense streaming: a client did not cover [0,N) */
+    FA_ERR_INDEX = -7,       /* unsorted, duplicate or out-of-range index */
+    FA_ERR_WORKSPACE = -8,   /* workspace missing or too small */
+    FA_ERR_HIP = -9          /* HIP runtime error */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+typedef enum { FA_WEIGHTS = 0, FA_DELTAS = 1 } fa_mode;
+typedef enum { FA_COUNT_U8 = 0, FA_COUNT_U32 = 1 } fa_count_dtype;
+
+/* FEDAVG_ABI_VERSION of the loaded library. */
+int fedavg_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). The pointer
+   stays valid until the next call on this thread. */
+const char *fedavg_last_error(void);
+
+/*
+ * fedavg_aggregate -- resident K-client aggregation in one pass over HBM.
+ *
+ * x        host array of K device pointers; x[k] holds N elements of x_dtype
+ *          (client models in FA_WEIGHTS mode, client deltas in FA_DELTAS).
+ * n        host array of K sample counts.  n_k == 0: client k is skipped and
+ *          x[k] is never read (it may be NULL).
+ * N        parameters per client (N == 0 is a no-op).
+ * base     device, N elements of base_dtype.  Required in FA_DELTAS mode and
+ *          whenever T > 0; unused in dense FA_WEIGHTS mode (may be NULL).
+ * out      device, N elements of out_dtype.
+ * T        0: dense -- every client sent every parameter (FA_WEIGHTS then
+ *          needs sum n_k > 0, else FA_ERR_ZERO_WEIGHT).
+ *          T > 0: per-segment (per-tensor) masks, for adapter-only or
+ *          partially shared updates: parameters are split into T contiguous
+ *          segments and client k sent segment t iff present[k*T + t] != 0.
+ *          Segments no client sent are never read and copy base.
+ * seg_bounds device int64[T+1]: seg_bounds[0] = 0, nondecreasing,
+ *          seg_bounds[T] = N; segment t is [seg_bounds[t], seg_bounds[t+1]).
+ *          Device data is not validated on the host; a malformed table gives
+ *          unspecified values but every access stays inside the buffers.
+ * present  device uint8[K*T], row-major by client.
+ * stream   hipStream_t the work is enqueued on.
+ * Traffic: one read of every element of every contributing (segment of a)
+ * client, one write of out, plus base where it is used.
+ */
+int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_t *n, int64_t N,
+                     fa_mode mode, const void *base, fa_dtype base_dtype, void *out,
+                     fa_dtype out_dtype, int T, const int64_t *seg_bounds, const uint8_t *present,
+                     void *stream);
+
+/* ------------------------------------------------------------------------
+ * Streaming: clients arrive one after another, each as chunks, into one
+ * resident fp32 accumulator, so device memory does not grow with K.
+ * ------------------------------------------------------------------------ */
+typedef struct fa_stream_state *fa_handle;
+
+/*
+ * fedavg_workspace_size -- device bytes the caller must provide.
+ * partial      0: dense (every client covers [0,N) exactly once);
+ *              1: partial (clients send ranges, masked ranges or index lists;
+ *                 each parameter is averaged over the clients that sent it).
+ * chunk_bytes  largest chunk payload per call (values), > 0.
+ * n_slots      staging slots for host-resident chunks (>= 1; 2 or more lets
+ *              the next copy overlap the current accumulate).
+ * acc_bytes    N fp32;  wsum_bytes  N uint32 (partial only, else 0);
+ * count_bytes  N uint8 (partial only, else 0);
+ * staging_bytes per-slot staging plus a small header (error flag).
+ */
+int fedavg_workspace_size(int64_t N, int partial, int64_t chunk_bytes, int n_slots,
+                          size_t *acc_bytes, size_t *wsum_bytes, size_t *count_bytes,
+                          size_t *staging_bytes);
+
+/*
+ * fedavg_begin -- start an aggregation; zeroes acc (and wsum, count) on
+ * compute_stream.
+ * acc, wsum, count, staging: caller device buffers of at least the sizes from
+ *     fedavg_workspace_size (wsum/count only in partial mode; count may be
+ *     NULL in partial mode when per-parameter client counts are not wanted).
+ * compute_stream: where accumulate and finalize kernels run.
+ * copy_stream: where host-to-device chunk copies run (NULL: the handle creates
+ *     its own stream).  Copies and kernels are ordered with HIP events.
+ */
+int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc, uint32_t *wsum,
+                 uint8_t *count, void *staging, size_t staging_bytes, int64_t chunk_bytes,
+                 int n_slots, void *compute_stream, void *copy_stream);
+
+/*
+ * fedavg_accumulate -- add one chunk of one client: acc[i] += n_k * value_i
+ * for every parameter i the chunk carries (and, in partial mode,
+ * wsum[i] += n_k, count[i] += 1).
+ *
+ * client_id   caller's id of the client (>= 0); a client keeps one n_k.
+ * n_k         the client's sample count; n_k == 0 returns FA_OK, no work.
+ * chunk       pinned host memory (staged with hipMemcpyAsync on the copy
+ *             stream) or device memory (read in place).  Pageable host memory
+ *             is rejected with FA_ERR_ARG.
+ * offset,len  without mask/indices: the chunk holds parameters
+ *             [offset, offset+len).  Dense mode: each client's chunks must
+ *             arrive in ascending order and tile [0,N) exactly.  Partial
+ *             mode: a client's ranges must be ascending and non-overlapping.
+ * mask        partial mode only, nullable: len bytes, nonzero = sent.
+ * indices     partial mode only, nullable: len strictly increasing int64
+ *             indices relative to offset (parameter offset+indices[j] gets
+ *             value j).  Violations are detected on the device and reported
+ *             by fedavg_sync as FA_ERR_INDEX; the bad entries are skipped.
+ *             The caller must not send one parameter twice for a client.
+ *             mask and indices live where chunk lives.
+ * A host buffer passed here may be reused once n_slots further accumulate
+ * calls have returned on this handle, or after fedavg_sync.
+ */
+int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk, fa_dtype dtype,
+                      int64_t offset, int64_t len, const uint8_t *mask, const int64_t *indices);
+
+/*
+ * fedavg_finalize -- out_i = base_i + acc_i / W_i (FA_DELTAS) or acc_i / W_i
+ * (FA_WEIGHTS), W_i = sum of n_k (dense) or wsum_i (partial); parameters with
+ * W_i == 0 copy base_i.  base (device, N of base_dtype) is required in
+ * FA_DELTAS and partial modes; out may alias base.  Dense mode returns
+ * FA_ERR_INCOMPLETE if some client has not covered [0,N).  The accumulator is
+ * left intact, so finalize may be repeated; no accumulate may follow.
+ */
+int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *out,
+                    fa_dtype out_dtype);
+
+/* Wait for all work of the handle; returns a deferred device error
+   (FA_ERR_INDEX) if one was raised, else FA_OK. */
+int fedavg_sync(fa_handle h);
+
+/* Wait for the handle's work, then release its host state and events. */
+int fedavg_destroy(fa_handle h);
+
+/* ------------------------------------------------------------------------
+ * Resident sparse partial sharing.
+ * ------------------------------------------------------------------------ */
+
+/* Device workspace bytes sparse_masked_accumulate needs for K clients, N. */
+int sparse_workspace_size(int K, int64_t N, size_t *bytes);
+
+/*
+ * sparse_masked_accumulate -- K clients each send a sorted list of
+ * (index, value) pairs, e.g. the top p% of their |delta| (partial sharing,
+ * Clara page, introduction and client-side workflow).  One pass:
+ *     count_i = |C_i|, W_i = sum_{k in C_i} n_k,
+ *     out_i   = W_i > 0 ? base_i + sum_{k in C_i} n_k v_{k,i} / W_i : base_i
+ * (FA_DELTAS; FA_WEIGHTS drops base_i from the first branch), accumulating
+ * client by client in list order.
+ *
+ * idx, val   host arrays of K device pointers: nnz[k] int64 indices, strictly
+ *            increasing, in [0,N), and nnz[k] fp32 values (SoA layout).
+ * nnz, n     host arrays of K (nnz[k] >= 0; n_k as for fedavg_aggregate).
+ * base, out  device fp32[N]; out may alias base.
+ * counts     device, N of counts_dtype (nullable): per-parameter client count.
+ * wsum       device uint32[N] (nullable): per-parameter weight sum W_i.
+ * workspace  device, >= sparse_workspace_size bytes.
+ * err_flag   device int (nullable): set to 0 by this call, then to
+ *            FA_ERR_INDEX if some list is unsorted, has duplicates or an
+ *            index outside [0,N) (those entries are skipped).
+ */
+int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *const *val,
+                             const int64_t *nnz, const int64_t *n, int64_t N, fa_mode mode,
+                             const float *base, float *out, void *counts,
+                             fa_count_dtype counts_dtype, uint32_t *wsum, void *workspace,
+                             size_t workspace_bytes, int *err_flag, void *stream);
+
+/*
+ * fedavg_checksum -- order-independent checksum of a device buffer of `count`
+ * elements: *hash_dev = sum over i of fmix64(i * 0x9E3779B97F4A7C15 XOR
+ * bits_i) mod 2^64 (bits_i: the element's raw 16- or 32-bit pattern; fmix64:
+ * the 64-bit finalizer of MurmurHash3).  Lets a caller compare large outputs
+ * or chunks bit for bit without copying them back.  hash_dev: device uint64,
+ * overwritten.
+ */
+int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *hash_dev,
+                    void *stream);
+
+/* ------------------------------------------------------------------------
+ * Launch-shape options (process-wide, for tuning and measurement).  They
+ * change how work is spread over the GPU, never the results.
+ * ------------------------------------------------------------------------ */
+typedef enum {
+    FA_OPT_BLOCKS_PER_CU = 1,          /* grid-stride kernels: workgroups per CU
+                                          (default 8; 0 = one 8-parameter
+                                          vector per thread, no striding) */
+    FA_OPT_MASK_VECTORS_PER_BLOCK = 2, /* masked aggregate: 8-parameter vectors
+                                          per workgroup (default 1024) */
+    FA_OPT_SPARSE_BLOCKS = 3           /* sparse merge: parameter ranges, i.e.
+                                          workgroups (default 2048, max 4096) */
+} fa_option;
+
+/* Set one option; FA_ERR_ARG for an unknown option, FA_ERR_RANGE for a value
+   outside the option's range.  Not thread-safe with concurrent launches. */
+int fedavg_set_option(int option, int64_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FEDAVG_H */

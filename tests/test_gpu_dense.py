@@ -1,0 +1,176 @@
+"""GPU parity: resident dense aggregation (fedavg_aggregate, T = 0) against
+the CPU oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import weighted_model_update_amd as fa
+from parity import check
+from gpu_util import dev_of, dev_f32, host_of, empty
+
+pytestmark = pytest.mark.gpu
+
+ODT = {"f32": oracle.F32, "bf16": oracle.BF16}
+
+
+def make_clients(seed, K, N, xdt, sigma=0.02):
+    r = np.random.default_rng(seed)
+    xs32 = [(r.standard_normal(N) * sigma).astype(np.float32) for _ in range(K)]
+    if xdt == "bf16":
+        return [synth.bf16_bits_from_f32(x) for x in xs32]
+    return xs32
+
+
+def make_base(seed, N, bdt, sigma=0.02):
+    b = (np.random.default_rng(seed + 1000).standard_normal(N) * sigma).astype(np.float32)
+    return synth.bf16_bits_from_f32(b) if bdt == "bf16" else b
+
+
+CASES = [
+    # K, N, x dtype, out dtype, mode, base dtype
+    (1, 1000, "f32", "f32", "weights", None),
+    (2, 7, "f32", "f32", "weights", None),
+    (3, 1_000_000, "f32", "f32", "weights", None),      # the K=3, 10^6 fp32 workload
+    (3, 4099, "bf16", "bf16", "weights", None),
+    (5, 100_003, "bf16", "f32", "deltas", "bf16"),
+    (8, 65_537, "f32", "bf16", "deltas", "f32"),
+    (16, 262_147, "bf16", "bf16", "weights", None),     # the K=16 bf16 shape, shrunk
+    (20, 9, "f32", "f32", "deltas", "f32"),
+    (33, 5000, "bf16", "bf16", "weights", None),        # runtime client count
+    (64, 3001, "f32", "f32", "weights", None),          # largest K
+    (4, 1, "bf16", "bf16", "deltas", "bf16"),
+]
+
+
+@pytest.mark.parametrize("K,N,xdt,odt,mode,bdt", CASES)
+def test_dense_matches_oracle(K, N, xdt, odt, mode, bdt):
+    n = synth.sample_counts(synth.CFG_DENSE_SMALL, K, 100, 1000)
+    xs = make_clients(K * 7919 + N, K, N, xdt, sigma=1e-3 if mode == "deltas" else 0.02)
+    base = make_base(N, N, bdt) if bdt else None
+    out = empty(N, odt)
+    fa.fedavg_aggregate([dev_of(x, xdt) for x in xs], n.tolist(), out, mode=mode,
+                        base=None if base is None else dev_of(base, bdt))
+    torch.cuda.synchronize()
+    ref, mag, _, _ = oracle.weighted_average(xs, n, mode=oracle.DELTAS if mode == "deltas" else oracle.WEIGHTS,
+                                             base=base, x_dtype=ODT[xdt],
+                                             base_dtype=ODT[bdt] if bdt else oracle.F32)
+    check(host_of(out), ref, mag, odt, label=f"K={K} N={N}")
+
+
+def test_dense_is_deterministic_and_order_sensitive_only_by_rounding():
+    K, N = 16, 1 << 20
+    n = synth.sample_counts(3, K, 100, 1000)
+    xs = [dev_of(x, "bf16") for x in make_clients(1, K, N, "bf16")]
+    a, b = empty(N, "bf16"), empty(N, "bf16")
+    fa.fedavg_aggregate(xs, n.tolist(), a)
+    fa.fedavg_aggregate(xs, n.tolist(), b)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_dense_unaligned_views_take_the_elementwise_path_with_same_bits(xdt):
+    K, N = 4, 50_001
+    n = synth.sample_counts(4, K, 100, 1000)
+    xs = make_clients(2, K, N + 1, xdt)
+    dx = [dev_of(x, xdt) for x in xs]
+    shifted = [t[1:] for t in dx]                 # 2 or 4 bytes off alignment
+    out_a = empty(N + 1, "f32")
+    out_b = empty(N, "f32")
+    fa.fedavg_aggregate([t[1:].clone() for t in dx], n.tolist(), out_b)   # aligned copies
+    fa.fedavg_aggregate(shifted, n.tolist(), out_a[1:])
+    torch.cuda.synchronize()
+    assert torch.equal(out_a[1:].view(torch.int32), out_b.view(torch.int32))
+    ref, mag, _, _ = oracle.weighted_average([x[1:] for x in xs], n, x_dtype=ODT[xdt])
+    check(host_of(out_b), ref, mag, "f32")
+
+
+def test_dense_zero_weight_client_is_never_read():
+    K, N = 3, 10_000
+    xs = make_clients(3, K, N, "f32")
+    poisoned = np.full(N, np.nan, np.float32)
+    out = empty(N, "f32")
+    fa.fedavg_aggregate([dev_f32(xs[0]), dev_f32(poisoned), dev_f32(xs[2])], [10, 0, 30], out)
+    torch.cuda.synchronize()
+    ref, mag, _, _ = oracle.weighted_average([xs[0], poisoned, xs[2]], [10, 0, 30])
+    assert not np.isnan(ref).any()
+    check(host_of(out), ref, mag, "f32")
+    # a NULL pointer for an n_k = 0 client is accepted
+    fa.fedavg_aggregate([dev_f32(xs[0]), None, dev_f32(xs[2])], [10, 0, 30], out)
+    torch.cuda.synchronize()
+    check(host_of(out), ref, mag, "f32")
+
+
+def test_dense_special_values_propagate():
+    N = 64
+    x0 = np.zeros(N, np.float32)
+    x1 = np.zeros(N, np.float32)
+    x0[:6] = [np.nan, np.inf, -np.inf, 1e-40, 1.5e38, -1e-45]
+    x1[:6] = [1.0, 1.0, np.inf, 1e-40, 1.5e38, 1e-45]
+    out = empty(N, "f32")
+    fa.fedavg_aggregate([dev_f32(x0), dev_f32(x1)], [1, 1], out)
+    torch.cuda.synchronize()
+    ref, mag, _, _ = oracle.weighted_average([x0, x1], [1, 1])
+    got = host_of(out)
+    check(got, ref, mag, "f32")
+    assert got[3] == np.float32(1e-40)             # denormals are kept, not flushed
+    assert got[4] == np.float32(1.5e38)
+
+
+def test_dense_in_place_alias_out_is_a_client():
+    K, N = 3, 4096
+    n = [100, 200, 300]
+    xs = make_clients(5, K, N, "f32")
+    dx = [dev_f32(x) for x in xs]
+    fa.fedavg_aggregate(dx, n, dx[1])
+    torch.cuda.synchronize()
+    ref, mag, _, _ = oracle.weighted_average(xs, n)
+    check(host_of(dx[1]), ref, mag, "f32")
+
+
+def test_dense_delta_mode_in_place_on_base():
+    K, N = 4, 8192 + 5
+    n = synth.sample_counts(4, K, 100, 10000)
+    ds = make_clients(6, K, N, "bf16", sigma=1e-3)
+    base = make_base(6, N, "bf16")
+    dbase = dev_of(base, "bf16")
+    fa.fedavg_aggregate([dev_of(d, "bf16") for d in ds], n.tolist(), dbase, mode="deltas", base=dbase)
+    torch.cuda.synchronize()
+    ref, mag, _, _ = oracle.weighted_average(ds, n, mode=oracle.DELTAS, base=base, x_dtype=oracle.BF16,
+                                             base_dtype=oracle.BF16)
+    check(host_of(dbase), ref, mag, "bf16")
+
+
+def test_dense_no_contributor_in_delta_mode_copies_base():
+    N = 1001
+    base = make_base(7, N, "f32")
+    out = empty(N, "bf16")
+    fa.fedavg_aggregate([dev_f32(np.ones(N, np.float32))], [0], out, mode="deltas", base=dev_f32(base))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_of(out), oracle.round_to_bf16(base))
+
+
+def test_dense_argument_errors():
+    x = torch.zeros(16, device="cuda")
+    out = torch.zeros(16, device="cuda")
+    with pytest.raises(fa.FedAvgError) as e:
+        fa.fedavg_aggregate([x], [0], out)
+    assert e.value.code == -4
+    with pytest.raises(fa.FedAvgError) as e:
+        fa.fedavg_aggregate([x], [-1], out)
+    assert e.value.code == -3
+    with pytest.raises(fa.FedAvgError) as e:
+        fa.fedavg_aggregate([x], [1 << 25], out)
+    assert e.value.code == -3
+    with pytest.raises(fa.FedAvgError) as e:
+        fa.fedavg_aggregate([x], [1], out, mode="deltas")
+    assert e.value.code == -1
+    with pytest.raises(fa.FedAvgError) as e:
+        fa.fedavg_aggregate([x[:15]], [1], x[1:])     # partial overlap of out and a client
+    assert e.value.code == -1
+    with pytest.raises(fa.FedAvgError) as e:
+        fa.fedavg_aggregate([x] * 65, [1] * 65, out)
+    assert e.value.code == -3

@@ -1,0 +1,151 @@
+"""GPU parity: one-pass sparse partial-sharing merge (sparse_masked_accumulate)
+against the oracle: values to tolerance, client counts, weight sums and the
+set of touched parameters bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import weighted_model_update_amd as fa
+from parity import check
+from gpu_util import dev_f32, host_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _restore_options():
+    yield
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 2048)
+
+
+def run_sparse(idx, val, n, N, base, mode="deltas", counts_dtype=torch.uint8, want_wsum=True,
+               out_is_base=False):
+    d_idx = [torch.from_numpy(np.ascontiguousarray(i, np.int64)).cuda() for i in idx]
+    d_val = [dev_f32(v) for v in val]
+    d_base = dev_f32(base)
+    out = d_base if out_is_base else torch.empty(N, dtype=torch.float32, device="cuda")
+    counts = torch.empty(N, dtype=counts_dtype, device="cuda")
+    wsum = torch.empty(N, dtype=torch.int32, device="cuda") if want_wsum else None
+    err = torch.full((1,), 123, dtype=torch.int32, device="cuda")
+    fa.sparse_masked_accumulate(d_idx, d_val, list(n), N, d_base, out, mode=mode, counts=counts,
+                                wsum=wsum, err_flag=err)
+    torch.cuda.synchronize()
+    return (host_of(out), counts.cpu().numpy(), None if wsum is None else wsum.cpu().numpy().view(np.uint32),
+            int(err.item()))
+
+
+def topk_case(N, K, frac, seed):
+    idx, val = zip(*[synth.topk_sparse_deltas(seed, k, N, frac, 1e-3) for k in range(K)])
+    base = synth.normal_f32(seed, synth.ROLE_BASE, 0, N, 0.02)
+    n = synth.sample_counts(seed, K, 100, 1000)
+    return list(idx), list(val), n, base
+
+
+@pytest.mark.parametrize("blocks", [2048, 3, 4096])
+def test_topk_partial_sharing_matches_oracle(blocks):
+    # K=20 clients each sending its top-10% |delta|: several tiles per block
+    # (3 blocks), one tile per block (4096), and the default
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, blocks)
+    N, K = 300_007, 20
+    idx, val, n, base = topk_case(N, K, 0.1, synth.CFG_SPARSE_1B)
+    got, cnt, ws, err = run_sparse(idx, val, n, N, base)
+    assert err == 0
+    ref, mag, rcnt, rws = oracle.sparse_average(idx, val, n, N, base=base)
+    assert np.array_equal(cnt, rcnt.astype(np.uint8))
+    assert np.array_equal(ws, rws.astype(np.uint32))
+    check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base, label=f"blocks={blocks}")
+
+
+def test_dense_support_overflows_batches():
+    # 60% density: about 2450 entries of each client per 4096-parameter tile,
+    # several 512-entry batches per client per tile
+    N, K = 50_001, 6
+    idx, val, n, base = topk_case(N, K, 0.6, 77)
+    got, cnt, ws, err = run_sparse(idx, val, n, N, base, counts_dtype=torch.int32)
+    assert err == 0
+    ref, mag, rcnt, rws = oracle.sparse_average(idx, val, n, N, base=base)
+    assert np.array_equal(cnt, rcnt.astype(np.int32))
+    assert np.array_equal(ws, rws.astype(np.uint32))
+    check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base)
+
+
+def test_full_support_equals_dense_delta_aggregate():
+    N, K = 20_000, 4
+    r = np.random.default_rng(1)
+    vals = [(r.standard_normal(N) * 1e-3).astype(np.float32) for _ in range(K)]
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    n = [11, 22, 33, 44]
+    got, cnt, ws, err = run_sparse([np.arange(N)] * K, vals, n, N, base)
+    dense = torch.empty(N, dtype=torch.float32, device="cuda")
+    fa.fedavg_aggregate([dev_f32(v) for v in vals], n, dense, mode="deltas", base=dev_f32(base))
+    torch.cuda.synchronize()
+    assert err == 0 and (cnt == K).all()
+    assert np.array_equal(got.view(np.uint32), host_of(dense).view(np.uint32))
+
+
+def test_weights_mode_empty_and_zero_weight_clients_in_place():
+    N = 70_000
+    r = np.random.default_rng(2)
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    idx = [np.sort(r.choice(N, 5000, replace=False)), np.array([], np.int64),
+           np.sort(r.choice(N, 9000, replace=False)), np.sort(r.choice(N, 100, replace=False))]
+    val = [r.standard_normal(len(i)).astype(np.float32) for i in idx]
+    n = [5, 7, 0, 13]
+    got, cnt, ws, err = run_sparse(idx, val, n, N, base, mode="weights", out_is_base=True)
+    assert err == 0
+    ref, mag, rcnt, rws = oracle.sparse_average(idx, val, n, N, mode=oracle.WEIGHTS, base=base)
+    assert np.array_equal(cnt, rcnt.astype(np.uint8))
+    check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base)
+
+
+@pytest.mark.parametrize("bad", ["unsorted", "duplicate", "too_large", "negative"])
+def test_bad_index_lists_are_flagged(bad):
+    N = 10_000
+    base = np.zeros(N, np.float32)
+    good = np.arange(0, N, 7, dtype=np.int64)
+    broken = good.copy()
+    if bad == "unsorted":
+        broken[100], broken[101] = broken[101], broken[100]
+    elif bad == "duplicate":
+        broken[200] = broken[199]
+    elif bad == "too_large":
+        broken[-1] = N + 5
+    else:
+        broken[0] = -3
+    val = np.ones(len(good), np.float32)
+    _, _, _, err = run_sparse([good, broken], [val, val], [1, 1], N, base)
+    assert err == -7
+    _, _, _, err = run_sparse([good, good], [val, val], [1, 1], N, base)
+    assert err == 0
+
+
+def test_tiny_and_ragged_sizes():
+    for N in (1, 7, 4095, 4097, 8193):
+        r = np.random.default_rng(N)
+        K = 3
+        idx = [np.sort(r.choice(N, max(1, N // 3), replace=False)) for _ in range(K)]
+        val = [r.standard_normal(len(i)).astype(np.float32) for i in idx]
+        base = r.standard_normal(N).astype(np.float32)
+        n = [1, 2, 3]
+        got, cnt, ws, err = run_sparse(idx, val, n, N, base)
+        assert err == 0
+        ref, mag, rcnt, rws = oracle.sparse_average(idx, val, n, N, base=base)
+        assert np.array_equal(cnt, rcnt.astype(np.uint8))
+        check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base, label=f"N={N}")
+
+
+def test_sparse_argument_errors():
+    N = 100
+    b = torch.zeros(N, device="cuda")
+    i = torch.arange(10, device="cuda")
+    v = torch.ones(10, device="cuda")
+    with pytest.raises(fa.FedAvgError) as e:
+        fa.sparse_masked_accumulate([i], [v], [1], N, b, b, workspace=torch.empty(8, dtype=torch.uint8,
+                                                                                   device="cuda"))
+    assert e.value.code == -8
+    with pytest.raises(fa.FedAvgError) as e:
+        fa.sparse_masked_accumulate([i], [v], [-1], N, b, b)
+    assert e.value.code == -3

@@ -1,0 +1,225 @@
+"""GPU parity: streamed, chunk-at-a-time aggregation (fedavg_begin /
+accumulate / finalize) from pinned host memory and from device memory."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import weighted_model_update_amd as fa
+from parity import check, base_copy_expect
+from gpu_util import dev_of, host_of, empty
+
+pytestmark = pytest.mark.gpu
+
+ODT = {"f32": oracle.F32, "bf16": oracle.BF16}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+# Host buffers handed to accumulate must stay alive until the copies that read
+# them are done (n_slots later calls, or a sync); tests keep them here.
+_KEEP = []
+
+
+def host_tensor(a, dt, pinned=True):
+    if dt == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    t = t.pin_memory() if pinned else t.clone()
+    _KEEP.append(t)
+    return t
+
+
+@pytest.fixture(autouse=True)
+def _release_host_buffers():
+    yield
+    torch.cuda.synchronize()
+    _KEEP.clear()
+
+
+def stream_dense(xs, n, dt, chunk, mode, base_dev, odt, where="pinned", n_slots=2, order=None):
+    N = len(xs[0])
+    chunk_bytes = chunk * (2 if dt == "bf16" else 4)
+    out = empty(N, odt)
+    with fa.StreamingAccumulator(N, mode=mode, partial=False, chunk_bytes=chunk_bytes,
+                                 n_slots=n_slots) as acc:
+        for k in (order if order is not None else range(len(xs))):
+            src = host_tensor(xs[k], dt) if where == "pinned" else dev_of(xs[k], dt)
+            for off in range(0, N, chunk):
+                acc.accumulate(k, int(n[k]), src[off:off + chunk], offset=off)
+        acc.finalize(base_dev, out)
+        acc.sync()
+    return out
+
+
+@pytest.mark.parametrize("where", ["pinned", "device"])
+@pytest.mark.parametrize("chunk", [4096, 1000, 1 << 20])
+def test_stream_deltas_match_oracle_and_resident(where, chunk):
+    K, N = 5, 100_003
+    n = synth.sample_counts(synth.CFG_STREAM_8B, K, 100, 10000)
+    r = np.random.default_rng(1)
+    ds = [synth.bf16_bits_from_f32((r.standard_normal(N) * 1e-3).astype(np.float32)) for _ in range(K)]
+    base = synth.bf16_bits_from_f32((r.standard_normal(N) * 0.02).astype(np.float32))
+    dbase = dev_of(base, "bf16")
+    out = stream_dense(ds, n, "bf16", chunk, "deltas", dbase, "bf16", where=where)
+    ref, mag, _, _ = oracle.weighted_average(ds, n, mode=oracle.DELTAS, base=base, x_dtype=oracle.BF16,
+                                             base_dtype=oracle.BF16)
+    got = host_of(out)
+    check(got, ref, mag, "bf16", label=f"chunk={chunk} {where}")
+    # the same clients aggregated resident give the same bits
+    res = empty(N, "bf16")
+    fa.fedavg_aggregate([dev_of(d, "bf16") for d in ds], n.tolist(), res, mode="deltas", base=dbase)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, host_of(res))
+
+
+@pytest.mark.parametrize("n_slots", [1, 3])
+def test_stream_weights_fp32(n_slots):
+    K, N = 4, 70_001
+    n = synth.sample_counts(1, K, 100, 1000)
+    xs = synth.dense_clients_f32(1, K, N, 0.02)
+    out = stream_dense(xs, n, "f32", 8192, "weights", None, "f32", n_slots=n_slots)
+    ref, mag, _, _ = oracle.weighted_average(xs, n)
+    check(host_of(out), ref, mag, "f32")
+
+
+def test_stream_in_place_on_base_and_client_order():
+    K, N = 3, 50_000
+    n = [300, 100, 200]
+    r = np.random.default_rng(2)
+    ds = [synth.bf16_bits_from_f32((r.standard_normal(N) * 1e-3).astype(np.float32)) for _ in range(K)]
+    base = synth.bf16_bits_from_f32((r.standard_normal(N) * 0.02).astype(np.float32))
+    dbase = dev_of(base, "bf16")
+    N_ = N
+    with fa.StreamingAccumulator(N_, mode="deltas", chunk_bytes=2 * 8192) as acc:
+        for k in (2, 0, 1):                         # arrival order differs from list order
+            src = host_tensor(ds[k], "bf16")
+            for off in range(0, N, 8192):
+                acc.accumulate(k, n[k], src[off:off + 8192], offset=off)
+        acc.finalize(dbase, dbase)                  # out aliases base
+        acc.sync()
+    order = [2, 0, 1]
+    ref, mag, _, _ = oracle.weighted_average([ds[k] for k in order], [n[k] for k in order],
+                                             mode=oracle.DELTAS, base=base, x_dtype=oracle.BF16,
+                                             base_dtype=oracle.BF16)
+    check(host_of(dbase), ref, mag, "bf16")
+
+
+def test_stream_partial_ranges_masks_and_indices():
+    """Partial mode: client 0 sends whole ranges, client 1 a masked chunk set,
+    client 2 an index list, client 3 index lists in device memory; each
+    parameter is averaged over its senders, unsent ones keep base."""
+    N = 40_000
+    r = np.random.default_rng(3)
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    n = [120, 450, 9000, 77]
+    vals = [(r.standard_normal(N) * 1e-3).astype(np.float32) for _ in range(4)]
+    sent = [np.zeros(N, np.uint8) for _ in range(4)]
+    out = empty(N, "f32")
+    with fa.StreamingAccumulator(N, mode="deltas", partial=True, chunk_bytes=4 * 4096,
+                                 n_slots=2) as acc:
+        # client 0: two tensors' ranges
+        for lo, hi in ((0, 3000), (10_000, 14_096)):
+            acc.accumulate(0, n[0], host_tensor(vals[0][lo:hi], "f32"), offset=lo)
+            sent[0][lo:hi] = 1
+        # client 1: masked chunks of 4096
+        for off in range(0, N, 4096):
+            ln = min(4096, N - off)
+            m = (r.random(ln) < 0.3).astype(np.uint8)
+            mt = torch.from_numpy(m).pin_memory()
+            _KEEP.append(mt)
+            acc.accumulate(1, n[1], host_tensor(vals[1][off:off + ln], "f32"), offset=off, mask=mt)
+            sent[1][off:off + ln] = m
+        # client 2: sorted index lists relative to the chunk offset
+        for off in range(0, N, 8000):
+            local = np.sort(r.choice(8000, 1000, replace=False)).astype(np.int64)
+            it = torch.from_numpy(local).pin_memory()
+            _KEEP.append(it)
+            acc.accumulate(2, n[2], host_tensor(vals[2][off + local], "f32"), offset=off, indices=it)
+            sent[2][off + local] = 1
+        # client 3: device-resident index list over the whole model
+        idx = np.sort(r.choice(N, 5000, replace=False)).astype(np.int64)
+        acc.accumulate(3, n[3], dev_of(vals[3][idx], "f32"), offset=0,
+                       indices=torch.from_numpy(idx).cuda())
+        sent[3][idx] = 1
+        acc.finalize(dev_of(base, "f32"), out)
+        acc.sync()
+    ref, mag, cnt, _ = oracle.weighted_average(vals, n, mode=oracle.DELTAS, base=base, sent=sent)
+    check(host_of(out), ref, mag, "f32", copied=cnt == 0, copy_expect=base)
+
+
+def test_stream_partial_counts_and_weight_sums_are_exact():
+    N = 9_999
+    r = np.random.default_rng(4)
+    n = [5, 7, 11]
+    sent = [(r.random(N) < p).astype(np.uint8) for p in (0.2, 0.5, 0.9)]
+    vals = [(r.standard_normal(N)).astype(np.float32) for _ in range(3)]
+    base = np.zeros(N, np.float32)
+    acc = fa.StreamingAccumulator(N, mode="weights", partial=True, chunk_bytes=4 * N)
+    try:
+        for k in range(3):
+            acc.accumulate(k, n[k], dev_of(vals[k], "f32"), offset=0,
+                           mask=torch.from_numpy(sent[k]).cuda())
+        out = empty(N, "f32")
+        acc.finalize(dev_of(base, "f32"), out)
+        acc.sync()
+        ref, mag, cnt, ws = oracle.weighted_average(vals, n, base=base, sent=sent)
+        check(host_of(out), ref, mag, "f32", copied=cnt == 0, copy_expect=base)
+        assert np.array_equal(acc.count[:N].cpu().numpy(), cnt.astype(np.uint8))
+        assert np.array_equal(acc.wsum[:N].cpu().numpy().view(np.uint32), ws.astype(np.uint32))
+    finally:
+        acc.close()
+
+
+def test_stream_bad_indices_are_reported_by_sync():
+    N = 1000
+    with fa.StreamingAccumulator(N, mode="weights", partial=True, chunk_bytes=4096) as acc:
+        acc.accumulate(0, 3, dev_of(np.ones(3, np.float32), "f32"), offset=0,
+                       indices=torch.tensor([5, 4, 9], dtype=torch.int64, device="cuda"))
+        with pytest.raises(fa.FedAvgError) as e:
+            acc.sync()
+        assert e.value.code == -7
+    with fa.StreamingAccumulator(N, mode="weights", partial=True, chunk_bytes=4096) as acc:
+        acc.accumulate(0, 3, dev_of(np.ones(2, np.float32), "f32"), offset=990,
+                       indices=torch.tensor([1, 10], dtype=torch.int64, device="cuda"))
+        with pytest.raises(fa.FedAvgError) as e:
+            acc.sync()
+        assert e.value.code == -7
+
+
+def test_stream_state_errors():
+    N = 100
+    x = dev_of(np.ones(N, np.float32), "f32")
+    base = dev_of(np.zeros(N, np.float32), "f32")
+    out = empty(N, "f32")
+    with fa.StreamingAccumulator(N, mode="weights", chunk_bytes=4 * N) as acc:
+        acc.accumulate(0, 1, x[:50], offset=0)
+        with pytest.raises(fa.FedAvgError) as e:          # gap in client 0's chunks
+            acc.accumulate(0, 1, x[60:], offset=60)
+        assert e.value.code == -1
+        with pytest.raises(fa.FedAvgError) as e:          # client 0 incomplete
+            acc.finalize(base, out)
+        assert e.value.code == -6
+        with pytest.raises(fa.FedAvgError) as e:          # n_k changes
+            acc.accumulate(0, 2, x[50:], offset=50)
+        assert e.value.code == -1
+        acc.accumulate(0, 1, x[50:], offset=50)
+        acc.finalize(base, out)
+        with pytest.raises(fa.FedAvgError) as e:
+            acc.accumulate(1, 1, x, offset=0)
+        assert e.value.code == -5
+        acc.sync()
+    assert torch.equal(out, torch.ones(N, device="cuda"))
+    with fa.StreamingAccumulator(N, mode="weights", chunk_bytes=4 * N) as acc:
+        with pytest.raises(fa.FedAvgError) as e:          # pageable host memory
+            acc.accumulate(0, 1, torch.ones(N), offset=0)
+        assert e.value.code == -1
+        with pytest.raises(fa.FedAvgError) as e:          # chunk beyond N
+            acc.accumulate(0, 1, x, offset=1)
+        assert e.value.code == -3
+        with pytest.raises(fa.FedAvgError) as e:          # no client at all
+            acc.finalize(base, out)
+        assert e.value.code == -4
+

@@ -1,0 +1,697 @@
+// Host side of the FedAvg aggregation library: the extern "C" entry points of
+// include/fedavg.h -- argument checks, weight sums in exact integers, launch
+// shapes, and the streaming pipeline (staging slots, copy/compute streams,
+// events, per-client coverage).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "fedavg_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return FA_OK;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int d) { return d == FA_F32 || d == FA_BF16; }
+size_t dsize(int d) { return d == FA_F32 ? 4 : 2; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Two byte ranges either coincide exactly or do not overlap at all.
+bool overlap_ok(const void *a, size_t abytes, const void *b, size_t bbytes)
+{
+    if (!a || !b || abytes == 0 || bbytes == 0)
+        return true;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    if (a0 == b0 && abytes == bbytes)
+        return true;
+    return a0 + abytes <= b0 || b0 + bbytes <= a0;
+}
+
+// Launch-shape options (fedavg_set_option).
+int64_t g_blocks_per_cu = 8;     // grid-stride kernels: workgroups per CU
+int64_t g_mask_vpb = 1024;       // masked kernel: 8-parameter vectors per block
+int64_t g_sparse_blocks = 2048;  // sparse merge: parameter ranges (workgroups)
+constexpr int64_t SPARSE_MAX_BLOCKS = 4096;
+constexpr size_t HEADER_BYTES = 256;
+
+int cu_count()
+{
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+int64_t grid_cap() { return g_blocks_per_cu > 0 ? g_blocks_per_cu * cu_count() : 0; }
+
+enum class Residence { Device, PinnedHost, Pageable };
+
+Residence residence_of(const void *p)
+{
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return Residence::Pageable;
+    }
+    if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged)
+        return Residence::Device;
+    if (attr.type == hipMemoryTypeHost)
+        return Residence::PinnedHost;
+    return Residence::Pageable;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t slot_bytes(int64_t chunk_bytes, int partial)
+{
+    // values, plus room for a mask or an index list of the largest chunk
+    // (at most chunk_bytes/2 entries, 8 bytes each)
+    size_t b = round_up((size_t)chunk_bytes, 256);
+    if (partial)
+        b += round_up((size_t)chunk_bytes * 4, 256);
+    return b;
+}
+
+} // namespace
+
+// ============================================================ streaming state
+
+struct fa_stream_state {
+    struct Client {
+        int64_t n;
+        int64_t covered; // dense: next expected offset; partial: end of the last range
+    };
+    int device = 0;
+    int64_t N = 0;
+    int mode = FA_WEIGHTS;
+    int partial = 0;
+    float *acc = nullptr;
+    uint32_t *wsum = nullptr;
+    uint8_t *count = nullptr;
+    char *staging = nullptr;
+    int64_t chunk_bytes = 0;
+    size_t slot_size = 0;
+    int n_slots = 0;
+    hipStream_t compute = nullptr;
+    hipStream_t copy = nullptr;
+    bool own_copy = false;
+    std::vector<hipEvent_t> copy_done, slot_free;
+    std::vector<bool> slot_used;
+    int64_t calls = 0;
+    bool finalized = false;
+    std::unordered_map<int, Client> clients;
+    int *err_flag() { return reinterpret_cast<int *>(staging); }
+    char *slot(int s) { return staging + HEADER_BYTES + (size_t)s * slot_size; }
+};
+
+extern "C" {
+
+int fedavg_abi_version(void) { return FEDAVG_ABI_VERSION; }
+
+const char *fedavg_last_error(void) { return g_last_error.c_str(); }
+
+int fedavg_set_option(int option, int64_t value)
+{
+    switch (option) {
+    case FA_OPT_BLOCKS_PER_CU:
+        if (value < 0 || value > 1024)
+            return fail(FA_ERR_RANGE, "blocks per CU must be in [0, 1024]");
+        g_blocks_per_cu = value;
+        return ok();
+    case FA_OPT_MASK_VECTORS_PER_BLOCK:
+        if (value < 1 || value > (1 << 24))
+            return fail(FA_ERR_RANGE, "vectors per block must be in [1, 2^24]");
+        g_mask_vpb = value;
+        return ok();
+    case FA_OPT_SPARSE_BLOCKS:
+        if (value < 1 || value > SPARSE_MAX_BLOCKS)
+            return fail(FA_ERR_RANGE, "sparse blocks must be in [1, %lld]",
+                        (long long)SPARSE_MAX_BLOCKS);
+        g_sparse_blocks = value;
+        return ok();
+    default:
+        return fail(FA_ERR_ARG, "unknown option %d", option);
+    }
+}
+
+// ============================================================ resident
+
+int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_t *n, int64_t N,
+                     fa_mode mode, const void *base, fa_dtype base_dtype, void *out,
+                     fa_dtype out_dtype, int T, const int64_t *seg_bounds, const uint8_t *present,
+                     void *stream)
+{
+    if (K < 1 || K > FA_MAX_CLIENTS)
+        return fail(FA_ERR_RANGE, "K=%d outside [1, %d]", K, FA_MAX_CLIENTS);
+    if (!x || !n)
+        return fail(FA_ERR_ARG, "x and n must not be NULL");
+    if (N < 0)
+        return fail(FA_ERR_ARG, "N=%lld is negative", (long long)N);
+    if (!dtype_ok(x_dtype) || !dtype_ok(out_dtype) || !dtype_ok(base_dtype))
+        return fail(FA_ERR_DTYPE, "dtypes must be FA_F32 or FA_BF16");
+    if (mode != FA_WEIGHTS && mode != FA_DELTAS)
+        return fail(FA_ERR_ARG, "unknown mode %d", (int)mode);
+    if (T < 0)
+        return fail(FA_ERR_ARG, "T=%d is negative", T);
+    if (mode == FA_DELTAS && !base)
+        return fail(FA_ERR_ARG, "delta mode needs base");
+    if (T > 0 && (!base || !seg_bounds || !present))
+        return fail(FA_ERR_ARG, "segment masks need base, seg_bounds and present");
+    if (N > 0 && !out)
+        return fail(FA_ERR_ARG, "out must not be NULL");
+
+    fa::DenseArgs d;
+    std::memset(&d, 0, sizeof d);
+    fa::MaskedArgs m;
+    std::memset(&m, 0, sizeof m);
+    int Kc = 0;
+    uint64_t S = 0;
+    const size_t xbytes = (size_t)N * dsize(x_dtype), obytes = (size_t)N * dsize(out_dtype);
+    bool aligned = aligned16(out);
+    for (int k = 0; k < K; ++k) {
+        if (n[k] < 0 || n[k] > FA_MAX_WEIGHT)
+            return fail(FA_ERR_RANGE, "n[%d]=%lld outside [0, 2^24]", k, (long long)n[k]);
+        if (n[k] == 0)
+            continue;
+        if (!x[k] && N > 0)
+            return fail(FA_ERR_ARG, "x[%d] is NULL", k);
+        if (!overlap_ok(out, obytes, x[k], xbytes))
+            return fail(FA_ERR_ARG, "out partially overlaps x[%d]", k);
+        aligned = aligned && aligned16(x[k]);
+        d.x[Kc] = m.x[Kc] = x[k];
+        d.w[Kc] = m.w[Kc] = (float)n[k];
+        m.wi[Kc] = (uint32_t)n[k];
+        m.row[Kc] = k;
+        S += (uint64_t)n[k];
+        ++Kc;
+    }
+    if (S >= (1ull << 32))
+        return fail(FA_ERR_RANGE, "sum of n_k must be below 2^32");
+    if (base && !overlap_ok(out, obytes, base, (size_t)N * dsize(base_dtype)))
+        return fail(FA_ERR_ARG, "out partially overlaps base");
+    if (N == 0)
+        return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (T == 0) {
+        if (S == 0) {
+            if (mode == FA_WEIGHTS)
+                return fail(FA_ERR_ZERO_WEIGHT, "sum of n_k is 0 in dense weights mode");
+            // no contributor: every parameter keeps the global value
+            hipError_t e = fa::launch_convert(base, base_dtype, out, out_dtype, N, s);
+            return e == hipSuccess ? ok() : hip_fail(e, "convert launch");
+        }
+        if (mode == FA_DELTAS)
+            aligned = aligned && aligned16(base);
+        d.K = Kc;
+        d.N = N;
+        d.base = base;
+        d.out = out;
+        d.S = (float)S;
+        hipError_t e = fa::launch_dense(d, x_dtype, out_dtype, base_dtype, mode, aligned,
+                                        grid_cap(), s);
+        return e == hipSuccess ? ok() : hip_fail(e, "dense aggregate launch");
+    }
+
+    aligned = aligned && aligned16(base);
+    m.K = Kc;
+    m.T = T;
+    m.N = N;
+    m.vpb = g_mask_vpb;
+    m.bounds = seg_bounds;
+    m.present = present;
+    m.base = base;
+    m.out = out;
+    hipError_t e = fa::launch_masked(m, x_dtype, out_dtype, base_dtype, mode, aligned, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "masked aggregate launch");
+}
+
+// ============================================================ streaming
+
+int fedavg_workspace_size(int64_t N, int partial, int64_t chunk_bytes, int n_slots,
+                          size_t *acc_bytes, size_t *wsum_bytes, size_t *count_bytes,
+                          size_t *staging_bytes)
+{
+    if (N < 0 || chunk_bytes <= 0 || n_slots < 1)
+        return fail(FA_ERR_ARG, "need N >= 0, chunk_bytes > 0, n_slots >= 1");
+    if (partial != 0 && partial != 1)
+        return fail(FA_ERR_ARG, "partial must be 0 or 1");
+    if (acc_bytes)
+        *acc_bytes = (size_t)N * 4;
+    if (wsum_bytes)
+        *wsum_bytes = partial ? (size_t)N * 4 : 0;
+    if (count_bytes)
+        *count_bytes = partial ? (size_t)N : 0;
+    if (staging_bytes)
+        *staging_bytes = HEADER_BYTES + (size_t)n_slots * slot_bytes(chunk_bytes, partial);
+    return ok();
+}
+
+int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc, uint32_t *wsum,
+                 uint8_t *count, void *staging, size_t staging_bytes, int64_t chunk_bytes,
+                 int n_slots, void *compute_stream, void *copy_stream)
+{
+    if (!h)
+        return fail(FA_ERR_ARG, "handle pointer is NULL");
+    *h = nullptr;
+    if (N < 0 || chunk_bytes <= 0 || n_slots < 1 || n_slots > 64)
+        return fail(FA_ERR_ARG, "need N >= 0, chunk_bytes > 0, 1 <= n_slots <= 64");
+    if (mode != FA_WEIGHTS && mode != FA_DELTAS)
+        return fail(FA_ERR_ARG, "unknown mode %d", (int)mode);
+    if (partial != 0 && partial != 1)
+        return fail(FA_ERR_ARG, "partial must be 0 or 1");
+    if (!acc || !staging || (partial && !wsum))
+        return fail(FA_ERR_WORKSPACE, "acc, staging (and wsum in partial mode) are required");
+    size_t need = HEADER_BYTES + (size_t)n_slots * slot_bytes(chunk_bytes, partial);
+    if (staging_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "staging has %zu bytes, needs %zu", staging_bytes, need);
+    if (!aligned16(acc) || !aligned16(staging) || (wsum && !aligned16(wsum)) ||
+        (count && !aligned16(count)))
+        return fail(FA_ERR_ARG, "acc, wsum, count and staging must be 16-byte aligned");
+
+    fa_stream_state *st = new (std::nothrow) fa_stream_state();
+    if (!st)
+        return fail(FA_ERR_ARG, "out of host memory");
+    (void)hipGetDevice(&st->device);
+    st->N = N;
+    st->mode = mode;
+    st->partial = partial;
+    st->acc = acc;
+    st->wsum = partial ? wsum : nullptr;
+    st->count = partial ? count : nullptr;
+    st->staging = static_cast<char *>(staging);
+    st->chunk_bytes = chunk_bytes;
+    st->slot_size = slot_bytes(chunk_bytes, partial);
+    st->n_slots = n_slots;
+    st->compute = static_cast<hipStream_t>(compute_stream);
+    st->copy = static_cast<hipStream_t>(copy_stream);
+    hipError_t e = hipSuccess;
+    if (!st->copy) {
+        e = hipStreamCreateWithFlags(&st->copy, hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            delete st;
+            return hip_fail(e, "copy stream");
+        }
+        st->own_copy = true;
+    }
+    st->copy_done.resize(n_slots);
+    st->slot_free.resize(n_slots);
+    st->slot_used.assign(n_slots, false);
+    for (int i = 0; i < n_slots && e == hipSuccess; ++i) {
+        e = hipEventCreateWithFlags(&st->copy_done[i], hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&st->slot_free[i], hipEventDisableTiming);
+    }
+    if (e == hipSuccess)
+        e = fa::launch_fill_u32(st->staging, HEADER_BYTES / 4, 0u, st->compute);
+    if (e == hipSuccess)
+        e = fa::launch_fill_u32(acc, N, 0u, st->compute);
+    if (e == hipSuccess && partial)
+        e = fa::launch_fill_u32(wsum, N, 0u, st->compute);
+    if (e == hipSuccess && partial && count)
+        e = fa::launch_fill_u32(count, (N + 3) / 4, 0u, st->compute);
+    if (e != hipSuccess) {
+        fedavg_destroy(st);
+        return hip_fail(e, "begin");
+    }
+    *h = st;
+    return ok();
+}
+
+int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk, fa_dtype dtype,
+                      int64_t offset, int64_t len, const uint8_t *mask, const int64_t *indices)
+{
+    if (!h)
+        return fail(FA_ERR_ARG, "NULL handle");
+    fa_stream_state &st = *h;
+    if (st.finalized)
+        return fail(FA_ERR_STATE, "accumulate after finalize");
+    if (client_id < 0)
+        return fail(FA_ERR_ARG, "client_id must be >= 0");
+    if (n_k < 0 || n_k > FA_MAX_WEIGHT)
+        return fail(FA_ERR_RANGE, "n_k=%lld outside [0, 2^24]", (long long)n_k);
+    if (!dtype_ok(dtype))
+        return fail(FA_ERR_DTYPE, "chunk dtype must be FA_F32 or FA_BF16");
+    if (len < 0 || offset < 0)
+        return fail(FA_ERR_ARG, "offset and len must be >= 0");
+    if (mask && indices)
+        return fail(FA_ERR_ARG, "pass a mask or indices, not both");
+    if ((mask || indices) && !st.partial)
+        return fail(FA_ERR_ARG, "masks and indices need a partial-mode handle");
+    if (!indices && offset + len > st.N)
+        return fail(FA_ERR_RANGE, "chunk [%lld, %lld) exceeds N=%lld", (long long)offset,
+                    (long long)(offset + len), (long long)st.N);
+    if (indices && offset > st.N)
+        return fail(FA_ERR_RANGE, "offset beyond N");
+    if (len > 0 && !chunk)
+        return fail(FA_ERR_ARG, "chunk is NULL");
+
+    auto it = st.clients.find(client_id);
+    if (it != st.clients.end() && it->second.n != n_k)
+        return fail(FA_ERR_ARG, "client %d changed its n_k", client_id);
+    if (n_k == 0)
+        return ok();
+    if (it == st.clients.end()) {
+        if (st.partial && st.clients.size() >= FA_MAX_STREAM_CLIENTS)
+            return fail(FA_ERR_RANGE, "more than %d clients in partial mode", FA_MAX_STREAM_CLIENTS);
+        uint64_t S = (uint64_t)n_k;
+        for (auto &c : st.clients)
+            S += (uint64_t)c.second.n;
+        if (S >= (1ull << 32))
+            return fail(FA_ERR_RANGE, "sum of n_k must be below 2^32");
+    }
+    fa_stream_state::Client cl = it != st.clients.end() ? it->second : fa_stream_state::Client{n_k, 0};
+    if (!st.partial) {
+        if (offset != cl.covered)
+            return fail(FA_ERR_ARG,
+                        "dense mode: client %d chunk starts at %lld, expected %lld (chunks must "
+                        "arrive in order and tile [0,N))",
+                        client_id, (long long)offset, (long long)cl.covered);
+        cl.covered = offset + len;
+    } else if (!indices) {
+        if (offset < cl.covered)
+            return fail(FA_ERR_ARG, "client %d ranges must be ascending and non-overlapping",
+                        client_id);
+        cl.covered = offset + len;
+    }
+    if (len == 0) {
+        st.clients[client_id] = cl;
+        return ok();
+    }
+
+    const size_t esize = dsize(dtype);
+    const size_t vbytes = (size_t)len * esize;
+    const Residence res = residence_of(chunk);
+    if (res == Residence::Pageable)
+        return fail(FA_ERR_ARG, "chunk must be pinned host memory or device memory");
+    if (mask && residence_of(mask) != res)
+        return fail(FA_ERR_ARG, "mask must live where the chunk lives");
+    if (indices && residence_of(indices) != res)
+        return fail(FA_ERR_ARG, "indices must live where the chunk lives");
+
+    fa::StreamArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.acc = st.acc;
+    a.wsum = st.wsum;
+    a.count = st.count;
+    a.offset = offset;
+    a.len = len;
+    a.N = st.N;
+    a.w = (float)n_k;
+    a.wi = (uint32_t)n_k;
+    a.err = st.err_flag();
+
+    hipError_t e = hipSuccess;
+    int slot = -1;
+    if (res == Residence::PinnedHost) {
+        if (vbytes > (size_t)st.chunk_bytes)
+            return fail(FA_ERR_RANGE, "chunk of %zu bytes exceeds chunk_bytes=%lld", vbytes,
+                        (long long)st.chunk_bytes);
+        slot = (int)(st.calls % st.n_slots);
+        char *dst = st.slot(slot);
+        char *aux = dst + round_up((size_t)st.chunk_bytes, 256);
+        if (st.slot_used[slot]) {
+            // the host buffer of the copy that last used this slot is free once
+            // that copy is done; the slot itself once its kernel is done
+            e = hipEventSynchronize(st.copy_done[slot]);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(st.copy, st.slot_free[slot], 0);
+        }
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(dst, chunk, vbytes, hipMemcpyHostToDevice, st.copy);
+        if (e == hipSuccess && mask)
+            e = hipMemcpyAsync(aux, mask, (size_t)len, hipMemcpyHostToDevice, st.copy);
+        if (e == hipSuccess && indices)
+            e = hipMemcpyAsync(aux, indices, (size_t)len * 8, hipMemcpyHostToDevice, st.copy);
+        if (e == hipSuccess)
+            e = hipEventRecord(st.copy_done[slot], st.copy);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(st.compute, st.copy_done[slot], 0);
+        if (e != hipSuccess)
+            return hip_fail(e, "staging copy");
+        a.chunk = dst;
+        a.mask = mask ? reinterpret_cast<const uint8_t *>(aux) : nullptr;
+        a.idx = indices ? reinterpret_cast<const int64_t *>(aux) : nullptr;
+    } else {
+        a.chunk = chunk;
+        a.mask = mask;
+        a.idx = indices;
+    }
+
+    if (indices) {
+        e = fa::launch_stream_accumulate_indices(a, dtype, st.compute);
+    } else {
+        const int part = !st.partial ? fa::PART_DENSE : (mask ? fa::PART_MASK : fa::PART_RANGE);
+        const bool aligned = (offset % fa::VEC) == 0 && aligned16(a.chunk) &&
+                             (!a.mask || (reinterpret_cast<uintptr_t>(a.mask) & 7u) == 0);
+        e = fa::launch_stream_accumulate(a, dtype, part, aligned, grid_cap(), st.compute);
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "accumulate launch");
+    if (slot >= 0) {
+        e = hipEventRecord(st.slot_free[slot], st.compute);
+        if (e != hipSuccess)
+            return hip_fail(e, "event record");
+        st.slot_used[slot] = true;
+        ++st.calls;
+    }
+    st.clients[client_id] = cl;
+    return ok();
+}
+
+int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *out,
+                    fa_dtype out_dtype)
+{
+    if (!h)
+        return fail(FA_ERR_ARG, "NULL handle");
+    fa_stream_state &st = *h;
+    if (!dtype_ok(base_dtype) || !dtype_ok(out_dtype))
+        return fail(FA_ERR_DTYPE, "dtypes must be FA_F32 or FA_BF16");
+    if (st.N > 0 && !out)
+        return fail(FA_ERR_ARG, "out must not be NULL");
+    if ((st.mode == FA_DELTAS || st.partial) && !base)
+        return fail(FA_ERR_ARG, "base is required in delta and partial modes");
+    if (base && !overlap_ok(out, (size_t)st.N * dsize(out_dtype), base,
+                            (size_t)st.N * dsize(base_dtype)))
+        return fail(FA_ERR_ARG, "out partially overlaps base");
+    uint64_t S = 0;
+    for (auto &c : st.clients) {
+        if (!st.partial && c.second.covered != st.N)
+            return fail(FA_ERR_INCOMPLETE, "client %d covered [0, %lld) of [0, %lld)", c.first,
+                        (long long)c.second.covered, (long long)st.N);
+        S += (uint64_t)c.second.n;
+    }
+    st.finalized = true;
+    if (st.N == 0)
+        return ok();
+    hipError_t e;
+    if (!st.partial && S == 0) {
+        if (st.mode == FA_WEIGHTS)
+            return fail(FA_ERR_ZERO_WEIGHT, "no client was accumulated in dense weights mode");
+        e = fa::launch_convert(base, base_dtype, out, out_dtype, st.N, st.compute);
+        return e == hipSuccess ? ok() : hip_fail(e, "convert launch");
+    }
+    fa::FinalizeArgs a;
+    a.acc = st.acc;
+    a.wsum = st.wsum;
+    a.base = base;
+    a.out = out;
+    a.N = st.N;
+    a.S = (float)S;
+    const bool aligned = aligned16(out) && (!base || aligned16(base));
+    e = fa::launch_stream_finalize(a, base_dtype, out_dtype, st.mode, st.partial, aligned,
+                                   grid_cap(), st.compute);
+    return e == hipSuccess ? ok() : hip_fail(e, "finalize launch");
+}
+
+int fedavg_sync(fa_handle h)
+{
+    if (!h)
+        return fail(FA_ERR_ARG, "NULL handle");
+    fa_stream_state &st = *h;
+    hipError_t e = hipStreamSynchronize(st.copy);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(st.compute);
+    int flag = 0;
+    if (e == hipSuccess)
+        e = hipMemcpy(&flag, st.err_flag(), sizeof flag, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return hip_fail(e, "sync");
+    if (flag != 0)
+        return fail(FA_ERR_INDEX, "a chunk held unsorted, duplicate or out-of-range indices");
+    return ok();
+}
+
+int fedavg_destroy(fa_handle h)
+{
+    if (!h)
+        return ok();
+    fa_stream_state *st = h;
+    hipError_t e = hipStreamSynchronize(st->copy);
+    hipError_t e2 = hipStreamSynchronize(st->compute);
+    for (auto ev : st->copy_done)
+        if (ev)
+            (void)hipEventDestroy(ev);
+    for (auto ev : st->slot_free)
+        if (ev)
+            (void)hipEventDestroy(ev);
+    if (st->own_copy && st->copy)
+        (void)hipStreamDestroy(st->copy);
+    delete st;
+    if (e != hipSuccess)
+        return hip_fail(e, "destroy");
+    if (e2 != hipSuccess)
+        return hip_fail(e2, "destroy");
+    return ok();
+}
+
+// ============================================================ sparse
+
+static int64_t sparse_blocks_for(int64_t N)
+{
+    const int64_t tiles = (N + fa::SP_TILE - 1) / fa::SP_TILE;
+    int64_t nb = std::min<int64_t>(tiles, g_sparse_blocks);
+    if (nb < 1)
+        nb = 1;
+    const int64_t tiles_per_block = (tiles + nb - 1) / nb;
+    const int64_t R = tiles_per_block * fa::SP_TILE;
+    return (N + R - 1) / R;
+}
+
+int sparse_workspace_size(int K, int64_t N, size_t *bytes)
+{
+    if (K < 1 || K > FA_MAX_CLIENTS)
+        return fail(FA_ERR_RANGE, "K=%d outside [1, %d]", K, FA_MAX_CLIENTS);
+    if (N < 0 || !bytes)
+        return fail(FA_ERR_ARG, "need N >= 0 and a result pointer");
+    *bytes = HEADER_BYTES + (size_t)K * (SPARSE_MAX_BLOCKS + 1) * sizeof(int64_t);
+    return ok();
+}
+
+int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *const *val,
+                             const int64_t *nnz, const int64_t *n, int64_t N, fa_mode mode,
+                             const float *base, float *out, void *counts,
+                             fa_count_dtype counts_dtype, uint32_t *wsum, void *workspace,
+                             size_t workspace_bytes, int *err_flag, void *stream)
+{
+    if (K < 1 || K > FA_MAX_CLIENTS)
+        return fail(FA_ERR_RANGE, "K=%d outside [1, %d]", K, FA_MAX_CLIENTS);
+    if (!idx || !val || !nnz || !n)
+        return fail(FA_ERR_ARG, "idx, val, nnz and n must not be NULL");
+    if (N < 0)
+        return fail(FA_ERR_ARG, "N is negative");
+    if (mode != FA_WEIGHTS && mode != FA_DELTAS)
+        return fail(FA_ERR_ARG, "unknown mode %d", (int)mode);
+    if (counts_dtype != FA_COUNT_U8 && counts_dtype != FA_COUNT_U32)
+        return fail(FA_ERR_DTYPE, "counts dtype must be FA_COUNT_U8 or FA_COUNT_U32");
+    if (N > 0 && (!base || !out))
+        return fail(FA_ERR_ARG, "base and out are required");
+    size_t need = 0;
+    sparse_workspace_size(K, N, &need);
+    if (!workspace || workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (!overlap_ok(out, (size_t)N * 4, base, (size_t)N * 4))
+        return fail(FA_ERR_ARG, "out partially overlaps base");
+
+    fa::SparseArgs a;
+    std::memset(&a, 0, sizeof a);
+    uint64_t S = 0;
+    int Kc = 0;
+    for (int k = 0; k < K; ++k) {
+        if (n[k] < 0 || n[k] > FA_MAX_WEIGHT)
+            return fail(FA_ERR_RANGE, "n[%d]=%lld outside [0, 2^24]", k, (long long)n[k]);
+        if (nnz[k] < 0)
+            return fail(FA_ERR_ARG, "nnz[%d] is negative", k);
+        if (n[k] == 0 || nnz[k] == 0)
+            continue;
+        if (!idx[k] || !val[k])
+            return fail(FA_ERR_ARG, "idx[%d] or val[%d] is NULL", k, k);
+        a.idx[Kc] = idx[k];
+        a.val[Kc] = val[k];
+        a.nnz[Kc] = nnz[k];
+        a.w[Kc] = (float)n[k];
+        a.wi[Kc] = (uint32_t)n[k];
+        S += (uint64_t)n[k];
+        ++Kc;
+    }
+    if (S >= (1ull << 32))
+        return fail(FA_ERR_RANGE, "sum of n_k must be below 2^32");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int *flag = err_flag ? err_flag : static_cast<int *>(workspace);
+    hipError_t e = fa::launch_fill_u32(flag, 1, 0u, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "flag reset");
+    if (N == 0)
+        return ok();
+    const int64_t NB = sparse_blocks_for(N);
+    const int64_t tiles = (N + fa::SP_TILE - 1) / fa::SP_TILE;
+    const int64_t R = ((tiles + NB - 1) / NB) * fa::SP_TILE;
+    a.K = Kc;
+    a.NB = (int)NB;
+    a.N = N;
+    a.R = R;
+    a.offs = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + HEADER_BYTES);
+    a.base = base;
+    a.out = out;
+    a.counts = counts;
+    a.counts_u32 = counts_dtype == FA_COUNT_U32;
+    a.wsum = wsum;
+    a.mode = mode;
+    a.aligned = aligned16(base) && aligned16(out) && (!wsum || aligned16(wsum)) &&
+                (!counts || aligned16(counts));
+    a.err = flag;
+    e = fa::launch_sparse(a, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "sparse launch");
+}
+
+// ============================================================ checksum
+
+int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *hash_dev, void *stream)
+{
+    if (!hash_dev || (count > 0 && !buf) || count < 0)
+        return fail(FA_ERR_ARG, "need a hash pointer, a buffer and count >= 0");
+    if (!dtype_ok(dtype))
+        return fail(FA_ERR_DTYPE, "dtype must be FA_F32 or FA_BF16");
+    hipError_t e = fa::launch_checksum(buf, count, dtype, hash_dev, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "checksum launch");
+}
+
+} // extern "C"

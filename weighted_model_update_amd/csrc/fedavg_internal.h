@@ -1,0 +1,116 @@
+// Internal interface between the host library (fedavg_api.hip) and the
+// gfx950 kernels (fedavg_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fedavg.h"
+
+namespace fa {
+
+enum { DT_F32 = FA_F32, DT_BF16 = FA_BF16 };
+enum { MODE_WEIGHTS = FA_WEIGHTS, MODE_DELTAS = FA_DELTAS };
+
+// Elements handled per thread per step on the vector paths: 8 bf16 are one
+// 16-byte load, 8 fp32 are two.
+constexpr int VEC = 8;
+
+// ---------------------------------------------------------------- resident
+struct DenseArgs {
+    const void *x[FA_MAX_CLIENTS]; // contributing clients only (n_k > 0)
+    float w[FA_MAX_CLIENTS];       // fp32(n_k), exact
+    int K;                         // number of contributing clients
+    int64_t N;
+    const void *base;
+    void *out;
+    float S; // fp32(sum n_k)
+};
+
+struct MaskedArgs {
+    const void *x[FA_MAX_CLIENTS];
+    float w[FA_MAX_CLIENTS];
+    uint32_t wi[FA_MAX_CLIENTS];
+    int row[FA_MAX_CLIENTS]; // row of each contributing client in `present`
+    int K;
+    int T;
+    int64_t N;
+    int64_t vpb; // vectors per block
+    const int64_t *bounds;
+    const uint8_t *present;
+    const void *base;
+    void *out;
+};
+
+// ---------------------------------------------------------------- streaming
+enum { PART_DENSE = 0, PART_RANGE = 1, PART_MASK = 2 };
+
+struct StreamArgs {
+    const void *chunk;
+    const uint8_t *mask;
+    const int64_t *idx;
+    float *acc;
+    uint32_t *wsum;
+    uint8_t *count;
+    int64_t offset;
+    int64_t len;
+    int64_t N;
+    float w;
+    uint32_t wi;
+    int *err;
+};
+
+struct FinalizeArgs {
+    const float *acc;
+    const uint32_t *wsum;
+    const void *base;
+    void *out;
+    int64_t N;
+    float S;
+};
+
+// ---------------------------------------------------------------- sparse
+constexpr int SP_TILE = 4096;   // parameters per LDS tile
+constexpr int SP_THREADS = 512; // threads per merge block
+constexpr int SP_GROUP = 8;     // clients whose batches are loaded together
+
+struct SparseArgs {
+    const int64_t *idx[FA_MAX_CLIENTS];
+    const float *val[FA_MAX_CLIENTS];
+    int64_t nnz[FA_MAX_CLIENTS];
+    float w[FA_MAX_CLIENTS];
+    uint32_t wi[FA_MAX_CLIENTS];
+    int K;
+    int NB;    // blocks (parameter ranges)
+    int64_t N;
+    int64_t R; // parameters per block range, a multiple of SP_TILE
+    int64_t *offs; // [K][NB+1] first list position at or after each range start
+    const float *base;
+    float *out;
+    void *counts;
+    int counts_u32;
+    uint32_t *wsum;
+    int mode;
+    int aligned; // base/out/counts/wsum allow the 8-wide finalize
+    int *err;
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  `grid_cap` bounds the number
+// of workgroups of grid-stride kernels (0: one element group per thread).
+hipError_t launch_dense(const DenseArgs &a, int xdt, int odt, int bdt, int mode, bool aligned,
+                        int64_t grid_cap, hipStream_t s);
+hipError_t launch_masked(const MaskedArgs &a, int xdt, int odt, int bdt, int mode, bool aligned,
+                         hipStream_t s);
+hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool aligned,
+                                    int64_t grid_cap, hipStream_t s);
+hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStream_t s);
+hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int mode, int partial,
+                                  bool aligned, int64_t grid_cap, hipStream_t s);
+hipError_t launch_sparse(const SparseArgs &a, hipStream_t s);
+hipError_t launch_checksum(const void *buf, int64_t count, int dt, uint64_t *hash,
+                           hipStream_t s);
+hipError_t launch_fill_u32(void *p, int64_t words, uint32_t value, hipStream_t s);
+hipError_t launch_convert(const void *src, int sdt, void *dst, int ddt, int64_t N, hipStream_t s);
+
+} // namespace fa

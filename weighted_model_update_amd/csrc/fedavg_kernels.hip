@@ -1,0 +1,1026 @@
+// gfx950 (CDNA4) kernels of the FedAvg aggregation library.
+//
+// Every kernel here is bound by memory traffic (a weighted sum does one FMA
+// per 2 or 4 bytes read), so the design goals are: each byte read from HBM
+// once, 16-byte coalesced loads with many independent loads in flight per
+// lane, non-temporal streaming stores, and no floating-point atomics (results
+// must be deterministic).  There is no matrix-core work: nothing here is a
+// contraction.
+//
+// Arithmetic order shared by all kernels, per parameter: acc = 0; for every
+// contributing client in order, acc = fma(fp32(n_k), x_k, acc); q = acc /
+// fp32(W) (IEEE division); in delta mode r = base + q; then
+// round-to-nearest-even to the output type.  This is the fp32 weighted mean
+// of the Clara page ("NVIDIA Clara implements federated learning",
+// introduction and server-side workflow) with fp32 master-weight
+// accumulation and nearest-even rounding of weights ("NVFP4 training with JAX
+// and MaxText", training-recipe section).
+#include "fedavg_internal.h"
+
+namespace fa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- formats
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even.  Adding 0x7fff plus the
+// lowest kept bit to the pattern carries into the kept half exactly when the
+// dropped half is above one half, or exactly one half with an odd kept half;
+// a carry out of the fraction bumps the exponent, which also turns the
+// largest finite values into infinity as required.  NaN is kept quiet.
+__device__ __forceinline__ uint32_t to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+template <int DT> struct io;
+
+template <> struct io<DT_F32> {
+    static __device__ __forceinline__ void load8(const void *p, int64_t e, float (&v)[VEC])
+    {
+        const f32x4 *q = reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + e);
+        f32x4 a = __builtin_nontemporal_load(q);
+        f32x4 b = __builtin_nontemporal_load(q + 1);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    static __device__ __forceinline__ float load1(const void *p, int64_t e)
+    {
+        return static_cast<const float *>(p)[e];
+    }
+    static __device__ __forceinline__ void store8(void *p, int64_t e, const float (&v)[VEC])
+    {
+        f32x4 *q = reinterpret_cast<f32x4 *>(static_cast<float *>(p) + e);
+        f32x4 a = {v[0], v[1], v[2], v[3]};
+        f32x4 b = {v[4], v[5], v[6], v[7]};
+        __builtin_nontemporal_store(a, q);
+        __builtin_nontemporal_store(b, q + 1);
+    }
+    static __device__ __forceinline__ void store1(void *p, int64_t e, float v)
+    {
+        static_cast<float *>(p)[e] = v;
+    }
+};
+
+template <> struct io<DT_BF16> {
+    static __device__ __forceinline__ void load8(const void *p, int64_t e, float (&v)[VEC])
+    {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p) + e);
+        u32x4 w = __builtin_nontemporal_load(q);
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+    }
+    static __device__ __forceinline__ float load1(const void *p, int64_t e)
+    {
+        return bf16_lo(static_cast<const uint16_t *>(p)[e]);
+    }
+    static __device__ __forceinline__ void store8(void *p, int64_t e, const float (&v)[VEC])
+    {
+        u32x4 w;
+        w.x = to_bf16(v[0]) | (to_bf16(v[1]) << 16);
+        w.y = to_bf16(v[2]) | (to_bf16(v[3]) << 16);
+        w.z = to_bf16(v[4]) | (to_bf16(v[5]) << 16);
+        w.w = to_bf16(v[6]) | (to_bf16(v[7]) << 16);
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p) + e));
+    }
+    static __device__ __forceinline__ void store1(void *p, int64_t e, float v)
+    {
+        static_cast<uint16_t *>(p)[e] = (uint16_t)to_bf16(v);
+    }
+};
+
+__device__ __forceinline__ int64_t global_tid() { return (int64_t)blockIdx.x * blockDim.x + threadIdx.x; }
+__device__ __forceinline__ int64_t grid_threads() { return (int64_t)gridDim.x * blockDim.x; }
+
+// ================================================================ resident dense
+
+// One pass over K client buffers: each lane owns 8 consecutive parameters per
+// step, issues the 16-byte loads of every client (KC of them when the client
+// count is a compile-time constant, batches of 8 otherwise) before its FMAs,
+// then writes the 8 results with one non-temporal store.
+template <int XDT, int ODT, int BDT, int MODE, int KC>
+__global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64_t nvec)
+{
+    const int K = KC > 0 ? KC : a.K;
+    for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
+        const int64_t e = v * VEC;
+        float acc[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            acc[j] = 0.0f;
+        if constexpr (KC > 0) {
+            float xv[KC][VEC];
+#pragma unroll
+            for (int k = 0; k < KC; ++k)
+                io<XDT>::load8(a.x[k], e, xv[k]);
+#pragma unroll
+            for (int k = 0; k < KC; ++k)
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    acc[j] = __builtin_fmaf(a.w[k], xv[k][j], acc[j]);
+        } else {
+            for (int k0 = 0; k0 < K; k0 += 8) {
+                float xv[8][VEC];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (k0 + k < K)
+                        io<XDT>::load8(a.x[k0 + k], e, xv[k]);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (k0 + k < K)
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j)
+                            acc[j] = __builtin_fmaf(a.w[k0 + k], xv[k][j], acc[j]);
+            }
+        }
+        float r[VEC];
+        if constexpr (MODE == MODE_DELTAS) {
+            float b[VEC];
+            io<BDT>::load8(a.base, e, b);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                r[j] = b[j] + acc[j] / a.S;
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                r[j] = acc[j] / a.S;
+        }
+        io<ODT>::store8(a.out, e, r);
+    }
+}
+
+// Element-wise form (unaligned buffers and the last N % 8 parameters), same
+// operation order as the vector form, so results are bit-identical.
+template <int XDT, int ODT, int BDT, int MODE>
+__global__ __launch_bounds__(256) void dense_scalar_kernel(const DenseArgs a, int64_t first,
+                                                           int64_t count)
+{
+    for (int64_t t = global_tid(); t < count; t += grid_threads()) {
+        const int64_t e = first + t;
+        float acc = 0.0f;
+        for (int k = 0; k < a.K; ++k)
+            acc = __builtin_fmaf(a.w[k], io<XDT>::load1(a.x[k], e), acc);
+        float r = acc / a.S;
+        if constexpr (MODE == MODE_DELTAS)
+            r = io<BDT>::load1(a.base, e) + r;
+        io<ODT>::store1(a.out, e, r);
+    }
+}
+
+// ================================================================ per-segment masks
+
+constexpr int SEG_WIN = 64; // segments staged in LDS at a time
+
+// Last segment index t in [0, T-1] with bounds[t] <= e (a thread alone).
+__device__ __forceinline__ int64_t thread_find_segment(const int64_t *bounds, int64_t T, int64_t e)
+{
+    int64_t lo = 0, hi = T - 1;
+    while (lo < hi) {
+        int64_t mid = lo + (hi - lo + 1) / 2;
+        if (bounds[mid] <= e)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Same search done by one whole wavefront: each round the 64 lanes probe 64
+// evenly spaced bounds and a ballot narrows the range 64-fold, so a table of
+// T segments costs ceil(log64(T+1)) dependent loads instead of log2(T).
+__device__ int64_t wave_find_segment(const int64_t *bounds, int64_t T, int64_t e, int lane)
+{
+    int64_t lo = 0, hi = T; // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int64_t span = hi - lo;
+        const int64_t step = (span + 63) / 64;
+        const int64_t pos = lo + (int64_t)lane * step;
+        const bool le = pos < hi && bounds[pos] <= e;
+        int c = __popcll(__ballot(le));
+        if (c < 1)
+            c = 1; // malformed table: stay in range
+        const int64_t nlo = lo + (int64_t)(c - 1) * step;
+        const int64_t nhi = lo + (int64_t)c * step;
+        lo = nlo;
+        hi = nhi < hi ? nhi : hi;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void segment_weights(const MaskedArgs &a, int64_t t, uint64_t &mask,
+                                                uint32_t &W)
+{
+    uint64_t m = 0;
+    uint32_t s = 0;
+    for (int k = 0; k < a.K; ++k) {
+        if (a.present[(int64_t)a.row[k] * a.T + t]) {
+            m |= 1ull << k;
+            s += a.wi[k];
+        }
+    }
+    mask = m;
+    W = s;
+}
+
+template <int XDT, int ODT, int BDT, int MODE>
+__device__ __forceinline__ void masked_element(const MaskedArgs &a, int64_t e)
+{
+    uint64_t mask;
+    uint32_t W;
+    segment_weights(a, thread_find_segment(a.bounds, a.T, e), mask, W);
+    float r;
+    if (W > 0) {
+        float acc = 0.0f;
+        for (int k = 0; k < a.K; ++k)
+            if ((mask >> k) & 1)
+                acc = __builtin_fmaf(a.w[k], io<XDT>::load1(a.x[k], e), acc);
+        r = acc / (float)W;
+        if constexpr (MODE == MODE_DELTAS)
+            r = io<BDT>::load1(a.base, e) + r;
+    } else {
+        r = io<BDT>::load1(a.base, e);
+    }
+    io<ODT>::store1(a.out, e, r);
+}
+
+// Each workgroup owns a contiguous run of `vpb` 8-parameter vectors.  Wave 0
+// locates the segment holding the run's first parameter; the block stages up
+// to SEG_WIN consecutive segments (bounds, client mask, weight sum) in LDS and
+// walks its vectors through them, window after window.  A vector lying inside
+// one segment reads only the clients present there; one that straddles a
+// segment boundary (or the end of the buffer) is done element by element.
+template <int XDT, int ODT, int BDT, int MODE>
+__global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
+{
+    __shared__ int64_t s_lo[SEG_WIN + 1];
+    __shared__ uint64_t s_mask[SEG_WIN];
+    __shared__ uint32_t s_W[SEG_WIN];
+    __shared__ int64_t s_t0;
+
+    const int tid = threadIdx.x;
+    const int64_t nvec_all = (a.N + VEC - 1) / VEC;
+    const int64_t v_begin = (int64_t)blockIdx.x * a.vpb;
+    if (v_begin >= nvec_all)
+        return;
+    const int64_t v_end = min(v_begin + a.vpb, nvec_all);
+    const int64_t e_end = min(v_end * VEC, a.N);
+    int64_t e_cur = v_begin * VEC;
+    int64_t t_next = -1;
+
+    while (e_cur < e_end) {
+        if (tid < 64) {
+            const int64_t t0 = t_next >= 0 ? t_next : wave_find_segment(a.bounds, a.T, e_cur, tid);
+            if (tid == 0)
+                s_t0 = t0;
+        }
+        __syncthreads();
+        const int64_t t0 = s_t0;
+        const int cnt = (int)min((int64_t)SEG_WIN, (int64_t)a.T - t0);
+        if (tid <= cnt)
+            s_lo[tid] = a.bounds[t0 + tid];
+        if (tid < cnt)
+            segment_weights(a, t0 + tid, s_mask[tid], s_W[tid]);
+        __syncthreads();
+
+        int64_t win_end = min(s_lo[cnt], e_end);
+        if (win_end <= e_cur)
+            win_end = e_end; // malformed table: finish with element-wise lookups
+        const int64_t vw0 = (e_cur + VEC - 1) / VEC;
+        const int64_t vw1 = min((win_end + VEC - 1) / VEC, v_end);
+
+        int64_t c_lo = 0, c_hi = 0;
+        uint64_t c_mask = 0;
+        uint32_t c_W = 0;
+        for (int64_t v = vw0 + tid; v < vw1; v += blockDim.x) {
+            const int64_t e = v * VEC;
+            if (!(e >= c_lo && e + VEC <= c_hi)) {
+                int lo = 0, hi = cnt - 1;
+                while (lo < hi) {
+                    int mid = (lo + hi + 1) / 2;
+                    if (s_lo[mid] <= e)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                c_lo = s_lo[lo];
+                c_hi = s_lo[lo + 1];
+                c_mask = s_mask[lo];
+                c_W = s_W[lo];
+            }
+            if (e >= c_lo && e + VEC <= c_hi && e + VEC <= a.N) {
+                float r[VEC];
+                if (c_W > 0) {
+                    float acc[VEC];
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j)
+                        acc[j] = 0.0f;
+                    for (int k0 = 0; k0 < a.K; k0 += 8) {
+                        float xv[8][VEC];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            if (k0 + k < a.K && ((c_mask >> (k0 + k)) & 1))
+                                io<XDT>::load8(a.x[k0 + k], e, xv[k]);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            if (k0 + k < a.K && ((c_mask >> (k0 + k)) & 1))
+#pragma unroll
+                                for (int j = 0; j < VEC; ++j)
+                                    acc[j] = __builtin_fmaf(a.w[k0 + k], xv[k][j], acc[j]);
+                    }
+                    const float Wf = (float)c_W;
+                    if constexpr (MODE == MODE_DELTAS) {
+                        float b[VEC];
+                        io<BDT>::load8(a.base, e, b);
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j)
+                            r[j] = b[j] + acc[j] / Wf;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j)
+                            r[j] = acc[j] / Wf;
+                    }
+                } else {
+                    io<BDT>::load8(a.base, e, r);
+                }
+                io<ODT>::store8(a.out, e, r);
+            } else {
+                for (int j = 0; j < VEC; ++j)
+                    if (e + j < a.N)
+                        masked_element<XDT, ODT, BDT, MODE>(a, e + j);
+            }
+        }
+        e_cur = win_end;
+        t_next = t0 + cnt;
+        if (t_next >= a.T)
+            t_next = a.T - 1;
+        __syncthreads(); // LDS window is rewritten next
+    }
+}
+
+template <int XDT, int ODT, int BDT, int MODE>
+__global__ __launch_bounds__(256) void masked_scalar_kernel(const MaskedArgs a)
+{
+    for (int64_t e = global_tid(); e < a.N; e += grid_threads())
+        masked_element<XDT, ODT, BDT, MODE>(a, e);
+}
+
+// ================================================================ streaming
+
+// acc[offset + e] += n_k * chunk[e] over one chunk; in partial modes also the
+// per-parameter weight sum and client count of the parameters sent.
+template <int DT, int PART>
+__global__ __launch_bounds__(256) void stream_acc_vec_kernel(const StreamArgs a, int64_t nvec)
+{
+    for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
+        const int64_t e = v * VEC;
+        const int64_t g = a.offset + e;
+        float xv[VEC];
+        io<DT>::load8(a.chunk, e, xv);
+        f32x4 *ap = reinterpret_cast<f32x4 *>(a.acc + g);
+        f32x4 lo = __builtin_nontemporal_load(ap);
+        f32x4 hi = __builtin_nontemporal_load(ap + 1);
+        uint32_t sent = 0xffu;
+        if constexpr (PART == PART_MASK) {
+            u32x2 mb = *reinterpret_cast<const u32x2 *>(a.mask + e);
+            sent = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sent |= (((mb.x >> (8 * j)) & 0xffu) != 0) << j;
+                sent |= (((mb.y >> (8 * j)) & 0xffu) != 0) << (j + 4);
+            }
+        }
+        float acc[VEC] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            if ((sent >> j) & 1)
+                acc[j] = __builtin_fmaf(a.w, xv[j], acc[j]);
+        lo = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        hi = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        __builtin_nontemporal_store(lo, ap);
+        __builtin_nontemporal_store(hi, ap + 1);
+        if constexpr (PART != PART_DENSE) {
+            u32x4 *wp = reinterpret_cast<u32x4 *>(a.wsum + g);
+            u32x4 w0 = wp[0], w1 = wp[1];
+            w0.x += (sent & 1) ? a.wi : 0u;
+            w0.y += (sent & 2) ? a.wi : 0u;
+            w0.z += (sent & 4) ? a.wi : 0u;
+            w0.w += (sent & 8) ? a.wi : 0u;
+            w1.x += (sent & 16) ? a.wi : 0u;
+            w1.y += (sent & 32) ? a.wi : 0u;
+            w1.z += (sent & 64) ? a.wi : 0u;
+            w1.w += (sent & 128) ? a.wi : 0u;
+            wp[0] = w0;
+            wp[1] = w1;
+            if (a.count) {
+                // one byte per parameter; a client adds at most 1 and there
+                // are at most 255 clients, so no byte carries into the next
+                u32x2 *cp = reinterpret_cast<u32x2 *>(a.count + g);
+                u32x2 c = *cp;
+                uint32_t add_lo = 0, add_hi = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    add_lo |= ((sent >> j) & 1u) << (8 * j);
+                    add_hi |= ((sent >> (j + 4)) & 1u) << (8 * j);
+                }
+                c.x += add_lo;
+                c.y += add_hi;
+                *cp = c;
+            }
+        }
+    }
+}
+
+template <int DT, int PART>
+__global__ __launch_bounds__(256) void stream_acc_scalar_kernel(const StreamArgs a, int64_t first,
+                                                                int64_t count)
+{
+    for (int64_t t = global_tid(); t < count; t += grid_threads()) {
+        const int64_t e = first + t;
+        const int64_t g = a.offset + e;
+        if constexpr (PART == PART_MASK) {
+            if (!a.mask[e])
+                continue;
+        }
+        a.acc[g] = __builtin_fmaf(a.w, io<DT>::load1(a.chunk, e), a.acc[g]);
+        if constexpr (PART != PART_DENSE) {
+            a.wsum[g] += a.wi;
+            if (a.count)
+                a.count[g] += 1;
+        }
+    }
+}
+
+// Client-at-a-time sparse accumulate: value j goes to parameter
+// offset + idx[j].  Indices are unique within a call, so no two lanes touch
+// the same parameter and no atomics are needed; bad entries are skipped and
+// flagged.
+template <int DT>
+__global__ __launch_bounds__(256) void stream_acc_index_kernel(const StreamArgs a)
+{
+    for (int64_t j = global_tid(); j < a.len; j += grid_threads()) {
+        const int64_t ix = a.idx[j];
+        const int64_t prev = j > 0 ? a.idx[j - 1] : -1;
+        const int64_t g = a.offset + ix;
+        if (ix <= prev || g >= a.N) {
+            *a.err = FA_ERR_INDEX;
+            continue;
+        }
+        a.acc[g] = __builtin_fmaf(a.w, io<DT>::load1(a.chunk, j), a.acc[g]);
+        a.wsum[g] += a.wi;
+        if (a.count)
+            a.count[g] += 1;
+    }
+}
+
+template <int BDT, int ODT, int MODE, int PARTIAL>
+__device__ __forceinline__ float finalize_one(float acc, uint32_t W, float S, float b)
+{
+    if constexpr (PARTIAL) {
+        if (W == 0)
+            return b;
+        const float q = acc / (float)W;
+        return MODE == MODE_DELTAS ? b + q : q;
+    } else {
+        const float q = acc / S;
+        return MODE == MODE_DELTAS ? b + q : q;
+    }
+}
+
+template <int BDT, int ODT, int MODE, int PARTIAL>
+__global__ __launch_bounds__(256) void stream_finalize_vec_kernel(const FinalizeArgs a, int64_t nvec)
+{
+    for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
+        const int64_t e = v * VEC;
+        const f32x4 *ap = reinterpret_cast<const f32x4 *>(a.acc + e);
+        const f32x4 lo = __builtin_nontemporal_load(ap);
+        const f32x4 hi = __builtin_nontemporal_load(ap + 1);
+        const float acc[VEC] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        uint32_t W[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (PARTIAL) {
+            const u32x4 *wp = reinterpret_cast<const u32x4 *>(a.wsum + e);
+            const u32x4 w0 = wp[0], w1 = wp[1];
+            W[0] = w0.x; W[1] = w0.y; W[2] = w0.z; W[3] = w0.w;
+            W[4] = w1.x; W[5] = w1.y; W[6] = w1.z; W[7] = w1.w;
+        }
+        float b[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (MODE == MODE_DELTAS || PARTIAL)
+            io<BDT>::load8(a.base, e, b);
+        float r[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            r[j] = finalize_one<BDT, ODT, MODE, PARTIAL>(acc[j], W[j], a.S, b[j]);
+        io<ODT>::store8(a.out, e, r);
+    }
+}
+
+template <int BDT, int ODT, int MODE, int PARTIAL>
+__global__ __launch_bounds__(256) void stream_finalize_scalar_kernel(const FinalizeArgs a,
+                                                                     int64_t first, int64_t count)
+{
+    for (int64_t t = global_tid(); t < count; t += grid_threads()) {
+        const int64_t e = first + t;
+        const uint32_t W = PARTIAL ? a.wsum[e] : 0u;
+        const float b = (MODE == MODE_DELTAS || PARTIAL) ? io<BDT>::load1(a.base, e) : 0.0f;
+        io<ODT>::store1(a.out, e, finalize_one<BDT, ODT, MODE, PARTIAL>(a.acc[e], W, a.S, b));
+    }
+}
+
+// ================================================================ sparse merge
+
+// For every client k and range boundary b (0..NB), the first position of k's
+// sorted index list at or after parameter b*R.  Also flags lists that hold
+// negative indices or indices >= N (those fall outside every range).
+__global__ __launch_bounds__(256) void sparse_offsets_kernel(const SparseArgs a)
+{
+    const int64_t total = (int64_t)a.K * (a.NB + 1);
+    for (int64_t t = global_tid(); t < total; t += grid_threads()) {
+        const int k = (int)(t / (a.NB + 1));
+        const int b = (int)(t % (a.NB + 1));
+        const int64_t target = min((int64_t)b * a.R, a.N);
+        const int64_t *ix = a.idx[k];
+        int64_t lo = 0, hi = a.nnz[k];
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (ix[mid] < target)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        a.offs[t] = lo;
+        if ((b == 0 && lo > 0) || (b == a.NB && lo < a.nnz[k]))
+            *a.err = FA_ERR_INDEX;
+    }
+}
+
+// One workgroup per parameter range of R = (whole tiles) parameters.  For
+// each tile of SP_TILE parameters the fp32 sums, weight sums and client
+// counts live in LDS.  Clients are merged strictly in order, with a barrier
+// between clients, so each parameter sees the same FMA order as the dense
+// path; inside one client the indices are unique, so lanes never collide and
+// no atomics are used.  A client's entries for the tile are fetched as one
+// coalesced batch of SP_THREADS (index, value) pairs from its cursor; the
+// batches of SP_GROUP clients are loaded together so their latencies overlap.
+// The in-tile entries of a sorted batch are a prefix, counted with one
+// barrier-count; the cursor advances by that count (a full batch loads the
+// next one).  After the last client the tile is finalized and written once.
+__global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseArgs a)
+{
+    __shared__ float s_acc[SP_TILE];
+    __shared__ uint32_t s_W[SP_TILE];
+    __shared__ uint32_t s_cnt[SP_TILE];
+    __shared__ int64_t s_cur[FA_MAX_CLIENTS];
+    __shared__ int64_t s_end[FA_MAX_CLIENTS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int b = blockIdx.x;
+    const int64_t r0 = (int64_t)b * a.R;
+    const int64_t r1 = min(r0 + a.R, a.N);
+    bool bad = false;
+
+    if (tid < a.K) {
+        const int64_t c0 = a.offs[(int64_t)tid * (a.NB + 1) + b];
+        int64_t c1 = a.offs[(int64_t)tid * (a.NB + 1) + b + 1];
+        c1 = max(c1, c0);
+        s_cur[tid] = c0;
+        s_end[tid] = min(c1, a.nnz[tid]);
+    }
+    for (int l = tid; l < SP_TILE; l += SP_THREADS) {
+        s_acc[l] = 0.0f;
+        s_W[l] = 0;
+        s_cnt[l] = 0;
+    }
+    __syncthreads();
+
+    for (int64_t t0 = r0; t0 < r1; t0 += SP_TILE) {
+        const int64_t t1 = min(t0 + SP_TILE, r1);
+        for (int k0 = 0; k0 < a.K; k0 += SP_GROUP) {
+            int64_t gix[SP_GROUP];
+            float gval[SP_GROUP];
+#pragma unroll
+            for (int g = 0; g < SP_GROUP; ++g) {
+                gix[g] = INT64_MAX;
+                gval[g] = 0.0f;
+                const int k = k0 + g;
+                if (k < a.K) {
+                    const int64_t p = s_cur[k] + tid;
+                    if (p < s_end[k]) {
+                        gix[g] = a.idx[k][p];
+                        gval[g] = a.val[k][p];
+                    }
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < SP_GROUP; ++g) {
+                const int k = k0 + g;
+                if (k < a.K) {
+                int64_t p0 = s_cur[k];
+                const int64_t pend = s_end[k];
+                int64_t ix = gix[g];
+                float val = gval[g];
+                while (true) {
+                    // predecessor of this lane's entry: the previous lane's,
+                    // or for lane 0 the one before it in the list
+                    int64_t prev = __shfl_up(ix, 1);
+                    if (lane == 0) {
+                        const int64_t pp = p0 + tid - 1;
+                        prev = (pp >= 0 && pp < pend) ? a.idx[k][pp] : -1;
+                        if (pp >= 0 && pp >= pend)
+                            prev = INT64_MAX; // this lane holds no entry
+                    }
+                    const bool in = ix < t1;
+                    const int c = __syncthreads_count(in);
+                    if (in) {
+                        if (ix <= prev || ix < t0) {
+                            bad = true;
+                        } else {
+                            const int l = (int)(ix - t0);
+                            s_acc[l] = __builtin_fmaf(a.w[k], val, s_acc[l]);
+                            s_W[l] += a.wi[k];
+                            s_cnt[l] += 1;
+                        }
+                    }
+                    p0 += c;
+                    if (c < SP_THREADS || p0 >= pend)
+                        break;
+                    const int64_t p = p0 + tid;
+                    ix = INT64_MAX;
+                    if (p < pend) {
+                        ix = a.idx[k][p];
+                        val = a.val[k][p];
+                    }
+                }
+                if (tid == 0)
+                    s_cur[k] = p0;
+                }
+            }
+        }
+        __syncthreads();
+
+        // finalize the tile: 8 consecutive parameters per lane
+        const int l0 = tid * VEC;
+        const int64_t e0 = t0 + l0;
+        if (a.aligned && e0 + VEC <= t1) {
+            float base8[VEC];
+            io<DT_F32>::load8(a.base, e0, base8);
+            float r[VEC];
+            uint32_t cnt[VEC], W[VEC];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                W[j] = s_W[l0 + j];
+                cnt[j] = s_cnt[l0 + j];
+                if (W[j] > 0) {
+                    const float q = s_acc[l0 + j] / (float)W[j];
+                    r[j] = a.mode == MODE_DELTAS ? base8[j] + q : q;
+                } else {
+                    r[j] = base8[j];
+                }
+                s_acc[l0 + j] = 0.0f;
+                s_W[l0 + j] = 0;
+                s_cnt[l0 + j] = 0;
+            }
+            io<DT_F32>::store8(a.out, e0, r);
+            if (a.counts) {
+                if (a.counts_u32) {
+                    u32x4 *cp = reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(a.counts) + e0);
+                    __builtin_nontemporal_store(u32x4{cnt[0], cnt[1], cnt[2], cnt[3]}, cp);
+                    __builtin_nontemporal_store(u32x4{cnt[4], cnt[5], cnt[6], cnt[7]}, cp + 1);
+                } else {
+                    u32x2 c8;
+                    c8.x = cnt[0] | (cnt[1] << 8) | (cnt[2] << 16) | (cnt[3] << 24);
+                    c8.y = cnt[4] | (cnt[5] << 8) | (cnt[6] << 16) | (cnt[7] << 24);
+                    __builtin_nontemporal_store(
+                        c8, reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(a.counts) + e0));
+                }
+            }
+            if (a.wsum) {
+                u32x4 *wp = reinterpret_cast<u32x4 *>(a.wsum + e0);
+                __builtin_nontemporal_store(u32x4{W[0], W[1], W[2], W[3]}, wp);
+                __builtin_nontemporal_store(u32x4{W[4], W[5], W[6], W[7]}, wp + 1);
+            }
+        } else {
+            for (int j = 0; j < VEC; ++j) {
+                const int l = l0 + j;
+                const int64_t e = e0 + j;
+                if (e < t1) {
+                    const uint32_t W = s_W[l];
+                    const float bv = a.base[e];
+                    float r = bv;
+                    if (W > 0) {
+                        const float q = s_acc[l] / (float)W;
+                        r = a.mode == MODE_DELTAS ? bv + q : q;
+                    }
+                    a.out[e] = r;
+                    if (a.counts) {
+                        if (a.counts_u32)
+                            static_cast<uint32_t *>(a.counts)[e] = s_cnt[l];
+                        else
+                            static_cast<uint8_t *>(a.counts)[e] = (uint8_t)s_cnt[l];
+                    }
+                    if (a.wsum)
+                        a.wsum[e] = W;
+                }
+                s_acc[l] = 0.0f;
+                s_W[l] = 0;
+                s_cnt[l] = 0;
+            }
+        }
+        // the next tile's first barrier-count orders these zeroes before use
+    }
+    if (bad)
+        *a.err = FA_ERR_INDEX;
+}
+
+// ================================================================ checksum
+
+__device__ __forceinline__ uint64_t fmix64(uint64_t k)
+{
+    k ^= k >> 33;
+    k *= 0xff51afd7ed558ccdull;
+    k ^= k >> 33;
+    k *= 0xc4ceb9fe1a85ec53ull;
+    k ^= k >> 33;
+    return k;
+}
+
+// Integer sum of per-element hashes: exact and independent of the order the
+// lanes add in.  Lanes reduce across the wavefront with butterfly shuffles,
+// then one 64-bit atomic add per wavefront.
+template <int DT>
+__global__ __launch_bounds__(256) void checksum_kernel(const void *buf, int64_t count,
+                                                       unsigned long long *out)
+{
+    uint64_t h = 0;
+    for (int64_t i = global_tid(); i < count; i += grid_threads()) {
+        const uint64_t bits = DT == DT_F32 ? (uint64_t) static_cast<const uint32_t *>(buf)[i]
+                                           : (uint64_t) static_cast<const uint16_t *>(buf)[i];
+        h += fmix64(((uint64_t)i * 0x9E3779B97F4A7C15ull) ^ bits);
+    }
+    unsigned long long v = h;
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0)
+        atomicAdd(out, v);
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t words, uint32_t value)
+{
+    for (int64_t i = global_tid(); i < words; i += grid_threads())
+        p[i] = value;
+}
+
+// Element copy with type conversion (round-to-nearest-even when narrowing):
+// the result when no client contributed at all.
+template <int SDT, int DDT>
+__global__ __launch_bounds__(256) void convert_kernel(const void *src, void *dst, int64_t N)
+{
+    for (int64_t e = global_tid(); e < N; e += grid_threads())
+        io<DDT>::store1(dst, e, io<SDT>::load1(src, e));
+}
+
+// ================================================================ launchers
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static inline unsigned grid_for(int64_t work, int threads, int64_t cap)
+{
+    int64_t g = ceil_div(work, threads);
+    if (cap > 0 && g > cap)
+        g = cap;
+    if (g < 1)
+        g = 1;
+    if (g > 0x7fffffff)
+        g = 0x7fffffff;
+    return (unsigned)g;
+}
+
+template <int XDT, int ODT, int BDT, int MODE>
+static hipError_t dense_launch_t(const DenseArgs &a, bool aligned, int64_t cap, hipStream_t s)
+{
+    const int64_t nvec = aligned ? a.N / VEC : 0;
+    if (nvec > 0) {
+        const unsigned g = grid_for(nvec, 256, cap);
+        switch (a.K) {
+        case 3: dense_vec_kernel<XDT, ODT, BDT, MODE, 3><<<g, 256, 0, s>>>(a, nvec); break;
+        case 8: dense_vec_kernel<XDT, ODT, BDT, MODE, 8><<<g, 256, 0, s>>>(a, nvec); break;
+        case 16: dense_vec_kernel<XDT, ODT, BDT, MODE, 16><<<g, 256, 0, s>>>(a, nvec); break;
+        default: dense_vec_kernel<XDT, ODT, BDT, MODE, 0><<<g, 256, 0, s>>>(a, nvec); break;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t first = nvec * VEC;
+    const int64_t rest = a.N - first;
+    if (rest > 0) {
+        dense_scalar_kernel<XDT, ODT, BDT, MODE><<<grid_for(rest, 256, cap), 256, 0, s>>>(a, first, rest);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <template <int, int, int, int> class F, typename... Args>
+static hipError_t dispatch4(int xdt, int odt, int bdt, int mode, Args &&...args)
+{
+    // 2 x 2 x 2 x 2 instantiations
+#define FA_CASE(X, O, B, M)                                                                        \
+    if (xdt == X && odt == O && bdt == B && mode == M)                                            \
+        return F<X, O, B, M>::run(args...);
+    FA_CASE(DT_F32, DT_F32, DT_F32, MODE_WEIGHTS)
+    FA_CASE(DT_F32, DT_F32, DT_F32, MODE_DELTAS)
+    FA_CASE(DT_F32, DT_F32, DT_BF16, MODE_WEIGHTS)
+    FA_CASE(DT_F32, DT_F32, DT_BF16, MODE_DELTAS)
+    FA_CASE(DT_F32, DT_BF16, DT_F32, MODE_WEIGHTS)
+    FA_CASE(DT_F32, DT_BF16, DT_F32, MODE_DELTAS)
+    FA_CASE(DT_F32, DT_BF16, DT_BF16, MODE_WEIGHTS)
+    FA_CASE(DT_F32, DT_BF16, DT_BF16, MODE_DELTAS)
+    FA_CASE(DT_BF16, DT_F32, DT_F32, MODE_WEIGHTS)
+    FA_CASE(DT_BF16, DT_F32, DT_F32, MODE_DELTAS)
+    FA_CASE(DT_BF16, DT_F32, DT_BF16, MODE_WEIGHTS)
+    FA_CASE(DT_BF16, DT_F32, DT_BF16, MODE_DELTAS)
+    FA_CASE(DT_BF16, DT_BF16, DT_F32, MODE_WEIGHTS)
+    FA_CASE(DT_BF16, DT_BF16, DT_F32, MODE_DELTAS)
+    FA_CASE(DT_BF16, DT_BF16, DT_BF16, MODE_WEIGHTS)
+    FA_CASE(DT_BF16, DT_BF16, DT_BF16, MODE_DELTAS)
+#undef FA_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int X, int O, int B, int M> struct DenseRun {
+    static hipError_t run(const DenseArgs &a, bool aligned, int64_t cap, hipStream_t s)
+    {
+        return dense_launch_t<X, O, B, M>(a, aligned, cap, s);
+    }
+};
+
+template <int X, int O, int B, int M> struct MaskedRun {
+    static hipError_t run(const MaskedArgs &a, bool aligned, hipStream_t s)
+    {
+        if (aligned) {
+            const int64_t nvec_all = ceil_div(a.N, VEC);
+            const unsigned g = grid_for(nvec_all, (int)a.vpb, 0);
+            masked_vec_kernel<X, O, B, M><<<g, 256, 0, s>>>(a);
+        } else {
+            masked_scalar_kernel<X, O, B, M><<<grid_for(a.N, 256, 65536), 256, 0, s>>>(a);
+        }
+        return hipGetLastError();
+    }
+};
+
+hipError_t launch_dense(const DenseArgs &a, int xdt, int odt, int bdt, int mode, bool aligned,
+                        int64_t grid_cap, hipStream_t s)
+{
+    return dispatch4<DenseRun>(xdt, odt, bdt, mode, a, aligned, grid_cap, s);
+}
+
+hipError_t launch_masked(const MaskedArgs &a, int xdt, int odt, int bdt, int mode, bool aligned,
+                         hipStream_t s)
+{
+    return dispatch4<MaskedRun>(xdt, odt, bdt, mode, a, aligned, s);
+}
+
+template <int DT, int PART>
+static hipError_t stream_acc_t(const StreamArgs &a, bool aligned, int64_t cap, hipStream_t s)
+{
+    const int64_t nvec = aligned ? a.len / VEC : 0;
+    if (nvec > 0) {
+        stream_acc_vec_kernel<DT, PART><<<grid_for(nvec, 256, cap), 256, 0, s>>>(a, nvec);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t first = nvec * VEC;
+    const int64_t rest = a.len - first;
+    if (rest > 0) {
+        stream_acc_scalar_kernel<DT, PART><<<grid_for(rest, 256, cap), 256, 0, s>>>(a, first, rest);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool aligned,
+                                    int64_t cap, hipStream_t s)
+{
+#define FA_CASE(D, P)                                                                              \
+    if (dt == D && part == P)                                                                      \
+        return stream_acc_t<D, P>(a, aligned, cap, s);
+    FA_CASE(DT_F32, PART_DENSE)
+    FA_CASE(DT_F32, PART_RANGE)
+    FA_CASE(DT_F32, PART_MASK)
+    FA_CASE(DT_BF16, PART_DENSE)
+    FA_CASE(DT_BF16, PART_RANGE)
+    FA_CASE(DT_BF16, PART_MASK)
+#undef FA_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStream_t s)
+{
+    const unsigned g = grid_for(a.len, 256, 65536);
+    if (dt == DT_F32)
+        stream_acc_index_kernel<DT_F32><<<g, 256, 0, s>>>(a);
+    else
+        stream_acc_index_kernel<DT_BF16><<<g, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int B, int O, int M, int P>
+static hipError_t finalize_t(const FinalizeArgs &a, bool aligned, int64_t cap, hipStream_t s)
+{
+    const int64_t nvec = aligned ? a.N / VEC : 0;
+    if (nvec > 0) {
+        stream_finalize_vec_kernel<B, O, M, P><<<grid_for(nvec, 256, cap), 256, 0, s>>>(a, nvec);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t first = nvec * VEC;
+    const int64_t rest = a.N - first;
+    if (rest > 0) {
+        stream_finalize_scalar_kernel<B, O, M, P><<<grid_for(rest, 256, cap), 256, 0, s>>>(a, first, rest);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int mode, int partial,
+                                  bool aligned, int64_t cap, hipStream_t s)
+{
+#define FA_CASE(B, O, M, P)                                                                        \
+    if (bdt == B && odt == O && mode == M && partial == P)                                        \
+        return finalize_t<B, O, M, P>(a, aligned, cap, s);
+#define FA_CASES(B, O)                                                                             \
+    FA_CASE(B, O, MODE_WEIGHTS, 0)                                                                 \
+    FA_CASE(B, O, MODE_WEIGHTS, 1)                                                                 \
+    FA_CASE(B, O, MODE_DELTAS, 0)                                                                  \
+    FA_CASE(B, O, MODE_DELTAS, 1)
+    FA_CASES(DT_F32, DT_F32)
+    FA_CASES(DT_F32, DT_BF16)
+    FA_CASES(DT_BF16, DT_F32)
+    FA_CASES(DT_BF16, DT_BF16)
+#undef FA_CASES
+#undef FA_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_sparse(const SparseArgs &a, hipStream_t s)
+{
+    const int64_t total = (int64_t)a.K * (a.NB + 1);
+    sparse_offsets_kernel<<<grid_for(total, 256, 0), 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    sparse_merge_kernel<<<a.NB, SP_THREADS, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_checksum(const void *buf, int64_t count, int dt, uint64_t *hash, hipStream_t s)
+{
+    fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t *>(hash), 2, 0u);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || count == 0)
+        return e;
+    const unsigned g = grid_for(count, 256, 4096);
+    if (dt == DT_F32)
+        checksum_kernel<DT_F32><<<g, 256, 0, s>>>(buf, count, reinterpret_cast<unsigned long long *>(hash));
+    else
+        checksum_kernel<DT_BF16><<<g, 256, 0, s>>>(buf, count, reinterpret_cast<unsigned long long *>(hash));
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(void *p, int64_t words, uint32_t value, hipStream_t s)
+{
+    if (words <= 0)
+        return hipSuccess;
+    fill_u32_kernel<<<grid_for(words, 256, 8192), 256, 0, s>>>(static_cast<uint32_t *>(p), words, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_convert(const void *src, int sdt, void *dst, int ddt, int64_t N, hipStream_t s)
+{
+    if (N <= 0)
+        return hipSuccess;
+    const unsigned g = grid_for(N, 256, 65536);
+    if (sdt == DT_F32 && ddt == DT_F32)
+        convert_kernel<DT_F32, DT_F32><<<g, 256, 0, s>>>(src, dst, N);
+    else if (sdt == DT_F32)
+        convert_kernel<DT_F32, DT_BF16><<<g, 256, 0, s>>>(src, dst, N);
+    else if (ddt == DT_F32)
+        convert_kernel<DT_BF16, DT_F32><<<g, 256, 0, s>>>(src, dst, N);
+    else
+        convert_kernel<DT_BF16, DT_BF16><<<g, 256, 0, s>>>(src, dst, N);
+    return hipGetLastError();
+}
+
+} // namespace fa

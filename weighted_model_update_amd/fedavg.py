@@ -1,0 +1,351 @@
+"""Python binding of libfedavg.so (include/fedavg.h) over torch tensors.
+
+Argument marshalling only: every step of the aggregation runs in the HIP
+kernels of the library.  Torch provides device memory, pinned host memory and
+streams.  The names follow the C ABI.  There is no fallback path: if the
+library cannot be loaded, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+FA_OK = 0
+FA_F32, FA_BF16 = 0, 1
+FA_WEIGHTS, FA_DELTAS = 0, 1
+FA_COUNT_U8, FA_COUNT_U32 = 0, 1
+FA_OPT_BLOCKS_PER_CU, FA_OPT_MASK_VECTORS_PER_BLOCK, FA_OPT_SPARSE_BLOCKS = 1, 2, 3
+FA_MAX_CLIENTS = 64
+
+STATUS_NAMES = {
+    0: "FA_OK", -1: "FA_ERR_ARG", -2: "FA_ERR_DTYPE", -3: "FA_ERR_RANGE",
+    -4: "FA_ERR_ZERO_WEIGHT", -5: "FA_ERR_STATE", -6: "FA_ERR_INCOMPLETE",
+    -7: "FA_ERR_INDEX", -8: "FA_ERR_WORKSPACE", -9: "FA_ERR_HIP",
+}
+
+# every symbol include/fedavg.h declares
+EXPORTS = [
+    "fedavg_abi_version", "fedavg_last_error", "fedavg_aggregate", "fedavg_workspace_size",
+    "fedavg_begin", "fedavg_accumulate", "fedavg_finalize", "fedavg_sync", "fedavg_destroy",
+    "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
+]
+
+
+class FedAvgError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def library_path():
+    return _build.LIB_PATH
+
+
+def load(build_if_missing=True):
+    """Load libfedavg.so (building it first if it does not exist).  torch is
+    imported before the library so both share torch's HIP runtime."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB_PATH):
+        if not build_if_missing:
+            raise RuntimeError(f"{_build.LIB_PATH} is not built")
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "fedavg_abi_version": ([], i32),
+        "fedavg_last_error": ([], ctypes.c_char_p),
+        "fedavg_aggregate": ([i32, P, i32, P, i64, i32, P, i32, P, i32, i32, P, P, P], i32),
+        "fedavg_workspace_size": ([i64, i32, i64, i32, P, P, P, P], i32),
+        "fedavg_begin": ([P, i64, i32, i32, P, P, P, P, sz, i64, i32, P, P], i32),
+        "fedavg_accumulate": ([P, i32, i64, P, i32, i64, i64, P, P], i32),
+        "fedavg_finalize": ([P, P, i32, P, i32], i32),
+        "fedavg_sync": ([P], i32),
+        "fedavg_destroy": ([P], i32),
+        "sparse_workspace_size": ([i32, i64, P], i32),
+        "sparse_masked_accumulate": ([i32, P, P, P, P, i64, i32, P, P, P, i32, P, P, sz, P, P], i32),
+        "fedavg_checksum": ([P, i64, i32, P, P], i32),
+        "fedavg_set_option": ([i32, i64], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != FA_OK:
+        msg = load().fedavg_last_error()
+        raise FedAvgError(rc, msg.decode() if msg else "")
+
+
+def _dtype(t):
+    if t.dtype == torch.float32:
+        return FA_F32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _mode(mode):
+    if mode in ("weights", FA_WEIGHTS):
+        return FA_WEIGHTS
+    if mode in ("deltas", FA_DELTAS):
+        return FA_DELTAS
+    raise ValueError(f"mode must be 'weights' or 'deltas', got {mode!r}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _contig(t, name):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _i64_array(vals):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for k, t in enumerate(tensors):
+        arr[k] = t.data_ptr() if t is not None else None
+    return arr
+
+
+def fedavg_abi_version():
+    return load().fedavg_abi_version()
+
+
+def fedavg_set_option(option, value):
+    _check(load().fedavg_set_option(int(option), int(value)))
+
+
+# ------------------------------------------------------------------ resident
+
+def fedavg_aggregate(xs, n, out, mode="weights", base=None, seg_bounds=None, present=None,
+                     stream=None):
+    """out <- weighted average of the K client tensors `xs` with weights `n`
+    (see fedavg_aggregate in include/fedavg.h).  seg_bounds (int64 [T+1]) and
+    present (uint8 [K, T]) select per-segment masks; both live on the GPU."""
+    lib = load()
+    K = len(xs)
+    if K == 0:
+        raise ValueError("need at least one client")
+    N = out.numel()
+    xdt = None
+    for k, x in enumerate(xs):
+        if x is None:
+            continue
+        _contig(x, f"xs[{k}]")
+        if x.numel() != N:
+            raise ValueError(f"xs[{k}] has {x.numel()} elements, out has {N}")
+        d = _dtype(x)
+        if xdt is not None and d != xdt:
+            raise TypeError("all clients must share one dtype")
+        xdt = d
+    _contig(out, "out")
+    _contig(base, "base")
+    if base is not None and base.numel() != N:
+        raise ValueError("base must have as many elements as out")
+    T = 0
+    if seg_bounds is not None or present is not None:
+        if seg_bounds is None or present is None:
+            raise ValueError("seg_bounds and present go together")
+        _contig(seg_bounds, "seg_bounds")
+        _contig(present, "present")
+        if seg_bounds.dtype != torch.int64 or present.dtype != torch.uint8:
+            raise TypeError("seg_bounds must be int64 and present uint8")
+        T = seg_bounds.numel() - 1
+        if T < 1 or present.numel() != K * T:
+            raise ValueError("present must hold K*T flags for T = len(seg_bounds) - 1")
+    rc = lib.fedavg_aggregate(K, _ptr_array(xs), xdt if xdt is not None else FA_F32, _i64_array(n), N,
+                              _mode(mode), _ptr(base), _dtype(base) if base is not None else FA_F32,
+                              _ptr(out), _dtype(out), T, _ptr(seg_bounds), _ptr(present),
+                              _stream_handle(stream))
+    _check(rc)
+
+
+# ------------------------------------------------------------------ streaming
+
+def fedavg_workspace_size(N, partial, chunk_bytes, n_slots):
+    """(acc_bytes, wsum_bytes, count_bytes, staging_bytes)."""
+    out = [ctypes.c_size_t(0) for _ in range(4)]
+    _check(load().fedavg_workspace_size(int(N), int(bool(partial)), int(chunk_bytes), int(n_slots),
+                                        *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def fedavg_begin(N, mode, partial, acc, wsum, count, staging, chunk_bytes, n_slots,
+                 compute_stream=None, copy_stream=None):
+    """Returns an opaque handle (ctypes pointer)."""
+    h = ctypes.c_void_p(0)
+    rc = load().fedavg_begin(ctypes.byref(h), int(N), _mode(mode), int(bool(partial)), _ptr(acc),
+                             _ptr(wsum), _ptr(count), _ptr(staging),
+                             staging.numel() * staging.element_size(), int(chunk_bytes),
+                             int(n_slots), _stream_handle(compute_stream),
+                             None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream))
+    _check(rc)
+    return h
+
+
+def fedavg_accumulate(h, client_id, n_k, chunk, offset=0, mask=None, indices=None):
+    _contig(chunk, "chunk")
+    _contig(mask, "mask")
+    _contig(indices, "indices")
+    if mask is not None and mask.dtype not in (torch.uint8, torch.bool):
+        raise TypeError("mask must be uint8 or bool")
+    if indices is not None and indices.dtype != torch.int64:
+        raise TypeError("indices must be int64")
+    rc = load().fedavg_accumulate(h, int(client_id), int(n_k), _ptr(chunk), _dtype(chunk),
+                                  int(offset), chunk.numel(), _ptr(mask), _ptr(indices))
+    _check(rc)
+
+
+def fedavg_finalize(h, base, out):
+    _contig(base, "base")
+    _contig(out, "out")
+    rc = load().fedavg_finalize(h, _ptr(base), _dtype(base) if base is not None else FA_F32,
+                                _ptr(out), _dtype(out))
+    _check(rc)
+
+
+def fedavg_sync(h):
+    _check(load().fedavg_sync(h))
+
+
+def fedavg_destroy(h):
+    _check(load().fedavg_destroy(h))
+
+
+class StreamingAccumulator:
+    """begin/accumulate/finalize over a caller-held set of workspace tensors.
+
+    Allocates the accumulator (N fp32), in partial mode the per-parameter
+    weight sums (uint32 stored as int32) and client counts (uint8), and the
+    staging slots, then calls fedavg_begin.  Use as a context manager or call
+    close()."""
+
+    def __init__(self, N, mode="weights", partial=False, chunk_bytes=64 << 20, n_slots=2,
+                 counts=True, device="cuda", compute_stream=None, copy_stream=None):
+        acc_b, wsum_b, count_b, stag_b = fedavg_workspace_size(N, partial, chunk_bytes, n_slots)
+        self.N = N
+        self.acc = torch.empty(max(acc_b // 4, 1), dtype=torch.float32, device=device)
+        self.wsum = torch.empty(max(wsum_b // 4, 1), dtype=torch.int32, device=device) if partial else None
+        self.count = (torch.empty(max(count_b, 1), dtype=torch.uint8, device=device)
+                      if partial and counts else None)
+        self.staging = torch.empty(stag_b, dtype=torch.uint8, device=device)
+        self.handle = fedavg_begin(N, mode, partial, self.acc, self.wsum, self.count, self.staging,
+                                   chunk_bytes, n_slots, compute_stream, copy_stream)
+
+    def accumulate(self, client_id, n_k, chunk, offset=0, mask=None, indices=None):
+        fedavg_accumulate(self.handle, client_id, n_k, chunk, offset, mask, indices)
+
+    def finalize(self, base, out):
+        fedavg_finalize(self.handle, base, out)
+
+    def sync(self):
+        fedavg_sync(self.handle)
+
+    def close(self):
+        if self.handle is not None:
+            h, self.handle = self.handle, None
+            fedavg_destroy(h)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------ sparse
+
+def sparse_workspace_size(K, N):
+    b = ctypes.c_size_t(0)
+    _check(load().sparse_workspace_size(int(K), int(N), ctypes.byref(b)))
+    return b.value
+
+
+def sparse_masked_accumulate(idx, val, n, N, base, out, mode="deltas", counts=None, wsum=None,
+                             workspace=None, err_flag=None, stream=None):
+    """One-pass merge of K sorted sparse client lists (see include/fedavg.h).
+    counts: uint8 or int32 tensor of N (nullable); wsum: int32 tensor of N
+    holding the uint32 weight sums (nullable); err_flag: int32 tensor of 1."""
+    lib = load()
+    K = len(idx)
+    if len(val) != K or len(n) != K:
+        raise ValueError("idx, val and n must have one entry per client")
+    for k in range(K):
+        _contig(idx[k], f"idx[{k}]")
+        _contig(val[k], f"val[{k}]")
+        if idx[k].dtype != torch.int64 or val[k].dtype != torch.float32:
+            raise TypeError("indices must be int64 and values float32")
+        if idx[k].numel() != val[k].numel():
+            raise ValueError(f"idx[{k}] and val[{k}] differ in length")
+    for t, name in ((base, "base"), (out, "out")):
+        _contig(t, name)
+        if t.dtype != torch.float32 or t.numel() != N:
+            raise ValueError(f"{name} must be float32 with N elements")
+    cdt = FA_COUNT_U8
+    if counts is not None:
+        _contig(counts, "counts")
+        if counts.numel() != N or counts.dtype not in (torch.uint8, torch.int32):
+            raise ValueError("counts must be uint8 or int32 with N elements")
+        cdt = FA_COUNT_U8 if counts.dtype == torch.uint8 else FA_COUNT_U32
+    if wsum is not None:
+        _contig(wsum, "wsum")
+        if wsum.numel() != N or wsum.dtype != torch.int32:
+            raise ValueError("wsum must be int32 (holding uint32) with N elements")
+    if workspace is None:
+        workspace = torch.empty(sparse_workspace_size(K, N), dtype=torch.uint8, device=out.device)
+    rc = lib.sparse_masked_accumulate(K, _ptr_array(idx), _ptr_array(val),
+                                      _i64_array([t.numel() for t in idx]), _i64_array(n), int(N),
+                                      _mode(mode), _ptr(base), _ptr(out), _ptr(counts), cdt,
+                                      _ptr(wsum), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _ptr(err_flag),
+                                      _stream_handle(stream))
+    _check(rc)
+    return workspace
+
+
+# ------------------------------------------------------------------ checksum
+
+def fedavg_checksum(t, stream=None, hash_out=None):
+    """Order-independent 64-bit checksum of a contiguous float32/bfloat16 GPU
+    tensor.  Returns the value as a Python int (synchronizes the stream)
+    unless hash_out (an int64 tensor of one element) is given."""
+    _contig(t, "tensor")
+    own = hash_out is None
+    if own:
+        hash_out = torch.empty(1, dtype=torch.int64, device=t.device)
+    _check(load().fedavg_checksum(_ptr(t), t.numel(), _dtype(t), _ptr(hash_out),
+                                  _stream_handle(stream)))
+    if own:
+        return int(hash_out.item()) & 0xFFFFFFFFFFFFFFFF
+    return None
