@@ -1,0 +1,399 @@
+#!/usr/bin/env python3
+"""FedAvg aggregation benchmark on one MI355X.
+
+Headline: resident dense FedAvg of K=16 bf16 clients of a 1,921,878,016-
+parameter transformer-shaped tensor list (fp32 accumulation, bf16 output);
+one step = one fedavg_aggregate call over all clients.  The same JSON line
+also carries every other aggregation mode at its full workload size:
+
+  dense_small  K=3 fp32 clients of 10^6 parameters (launch-latency bound)
+  adapter      K=8 clients, LoRA q,k,v,o adapters of 32 layers (16.8M bf16),
+               each client sending a Bernoulli(0.6) subset of the modules
+  streaming    8,030,261,248 bf16 parameters, K=32 clients arriving one by
+               one as 64 MiB chunks from pinned host memory (PCIe bound), and
+               the accumulate kernel alone on device-resident chunks
+  sparse       10^9 fp32 parameters, K=20 clients each sending its top 10%
+               (sorted int64 index, fp32 value) pairs
+
+Inputs are seeded synthetic data generated on the GPU before timing.  The
+roofline object reports the headline kernel against MI355X's 8 TB/s HBM; the
+cpu_baseline object times the CPU oracle on a sample of the headline
+workload.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+PCIE_PEAK_GBS = 64.0       # PCIe Gen5 x16 per direction, GB/s
+METRIC = "aggregated params/sec and achieved HBM GB/s (% of MI355X peak), K clients"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "dense_k16_bf16_2b_hbm_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "weighted_model_update_amd", "csrc", "fedavg_kernels.hip")
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def kernel_source_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def timed(fn, steps, warmup):
+    """Run fn(i) warmup times untimed, then exactly `steps` times between two
+    device synchronizations.  Returns (wall seconds over the steps, list of
+    per-step event durations in ms measured on the current stream)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn(warmup + i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def free_gpu():
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# headline: dense K=16, 2B bf16
+# --------------------------------------------------------------------------
+
+def bench_dense_2b(steps, warmup):
+    import torch
+    import synth.device as sd
+    import weighted_model_update_amd as fa
+    log("dense 2B: generating 16 bf16 clients")
+    n, xs = sd.dense_2b()
+    K, N = len(xs), xs[0].numel()
+    out = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    nl = n.tolist()
+    log(f"dense 2B: K={K} N={N} timing {steps} steps")
+    wall, durs = timed(lambda i: fa.fedavg_aggregate(xs, nl, out), steps, warmup)
+    out_hash = fa.fedavg_checksum(out)
+    del xs, out
+    free_gpu()
+    algo_bytes = (K + 1) * 2 * N
+    avg_ms = sum(durs) / len(durs)
+    return {
+        "K": K, "N": N, "wall_s": wall, "avg_launch_ms": avg_ms, "min_launch_ms": min(durs),
+        "algo_bytes": algo_bytes, "out_checksum": f"{out_hash:016x}",
+    }
+
+
+# --------------------------------------------------------------------------
+# other modes
+# --------------------------------------------------------------------------
+
+def bench_dense_small(reps=2000, replicas=64):
+    import torch
+    import synth.device as sd
+    import weighted_model_update_amd as fa
+    n, xs = sd.dense_small()
+    N = xs[0].numel()
+    sets = [[x.clone() for x in xs] for _ in range(replicas)]     # 64 x 12 MB: beyond the caches
+    outs = [torch.empty(N, dtype=torch.float32, device="cuda") for _ in range(replicas)]
+    nl = n.tolist()
+    fn = lambda i: fa.fedavg_aggregate(sets[i % replicas], nl, outs[i % replicas])
+    for i in range(50):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(reps):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1000.0 / reps
+    bytes_ = 4 * 4 * N
+    del sets, outs
+    free_gpu()
+    return {"K": 3, "N": N, "dtype": "f32", "us_per_call": us, "algo_bytes": bytes_,
+            "hbm_gbs": bytes_ / (us * 1e-6) / 1e9, "params_per_s": 3 * N / (us * 1e-6),
+            "replica_sets": replicas,
+            "note": "launch-latency bound: 16 MB of traffic is 2 us at 8 TB/s"}
+
+
+def bench_adapter(reps=400, replicas=4):
+    import numpy as np
+    import torch
+    import synth.device as sd
+    import weighted_model_update_amd as fa
+    n, xs, base, bounds, present = sd.adapter()
+    K, N = len(xs), xs[0].numel()
+    seg = np.diff(bounds)
+    sent_params = int((present * seg[None, :]).sum())
+    nobody = int(seg[present.sum(0) == 0].sum())
+    algo_bytes = 2 * sent_params + 2 * N + 2 * nobody
+    d_bounds = torch.from_numpy(bounds).cuda()
+    d_present = torch.from_numpy(np.ascontiguousarray(present, np.uint8)).cuda()
+    sets = [([x.clone() for x in xs], base.clone()) for _ in range(replicas)]   # > 2x the 256 MB MALL
+    outs = [torch.empty(N, dtype=torch.bfloat16, device="cuda") for _ in range(replicas)]
+    nl = n.tolist()
+
+    def fn(i):
+        c, b = sets[i % replicas]
+        fa.fedavg_aggregate(c, nl, outs[i % replicas], base=b, seg_bounds=d_bounds, present=d_present)
+
+    for i in range(20):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(reps):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1000.0 / reps
+    del sets, outs, xs, base
+    free_gpu()
+    return {"K": K, "N": N, "dtype": "bf16", "segments": int(len(seg)),
+            "client_segments_sent": int(present.sum()), "us_per_call": us,
+            "algo_bytes": algo_bytes, "hbm_gbs": algo_bytes / (us * 1e-6) / 1e9,
+            "hbm_frac": algo_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "params_per_s": sent_params / (us * 1e-6), "replica_sets": replicas}
+
+
+def bench_streaming(clients=32, slots=3):
+    import torch
+    import synth.device as sd
+    import synth
+    import weighted_model_update_amd as fa
+    chunk_bytes = synth.CHUNK_BYTES_8B
+    per = chunk_bytes // 2
+    log("streaming: building the pinned 4 GiB chunk pool and the 8B bf16 base")
+    pool = sd.stream_8b_pool()
+    P = pool.shape[0]
+    base = sd.stream_8b_base()
+    N = base.numel()
+    n = sd.stream_8b_counts(32)[:clients]
+    cpc = (N + per - 1) // per
+    acc_b, _, _, stag_b = fa.fedavg_workspace_size(N, 0, chunk_bytes, slots)
+    acc = torch.empty(acc_b // 4, dtype=torch.float32, device="cuda")
+    staging = torch.empty(stag_b, dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
+
+    def one_pass(n_clients):
+        h = fa.fedavg_begin(N, "deltas", False, acc, None, None, staging, chunk_bytes, slots,
+                            copy_stream=copy_stream)
+        for k in range(n_clients):
+            for c in range(cpc):
+                off = c * per
+                ln = min(per, N - off)
+                fa.fedavg_accumulate(h, k, int(n[k]), pool[sd.pool_index(k, c, cpc, P)][:ln], off)
+        fa.fedavg_finalize(h, base, base)        # in place: global += weighted mean delta
+        fa.fedavg_sync(h)
+        fa.fedavg_destroy(h)
+
+    log("streaming: warm-up pass with 1 client")
+    one_pass(1)
+    torch.cuda.synchronize()
+    log(f"streaming: timed pass, {clients} clients x {cpc} chunks")
+    t0 = time.perf_counter()
+    one_pass(clients)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pcie_bytes = 2 * N * clients
+
+    # the accumulate kernel alone, chunks already in HBM
+    dchunk = pool[0].cuda()
+    h = fa.fedavg_begin(N, "deltas", False, acc, None, None, staging, chunk_bytes, slots)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fa.fedavg_accumulate(h, 0, 1, dchunk, 0)
+    torch.cuda.synchronize()
+    s.record()
+    for c in range(1, cpc - 1):
+        fa.fedavg_accumulate(h, 0, 1, dchunk, c * per)
+    e.record()
+    torch.cuda.synchronize()
+    k_us = s.elapsed_time(e) * 1000.0 / (cpc - 2)
+    fa.fedavg_destroy(h)
+    k_bytes = 10 * per                      # bf16 chunk read + fp32 acc read and write
+    del pool, base, acc, staging, dchunk
+    free_gpu()
+    return {"K": clients, "N": N, "dtype": "bf16 in, fp32 accumulator", "chunk_bytes": chunk_bytes,
+            "staging_slots": slots, "wall_s": wall, "pcie_bytes": pcie_bytes,
+            "pcie_gbs": pcie_bytes / wall / 1e9, "pcie_frac": pcie_bytes / wall / 1e9 / PCIE_PEAK_GBS,
+            "params_per_s": N * clients / wall,
+            "accumulate_kernel": {"us_per_chunk": k_us, "algo_bytes": k_bytes,
+                                  "hbm_gbs": k_bytes / (k_us * 1e-6) / 1e9,
+                                  "hbm_frac": k_bytes / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+
+
+def bench_sparse(steps=10, warmup=2):
+    import torch
+    import synth.device as sd
+    import weighted_model_update_amd as fa
+    log("sparse: generating 20 top-10% client lists over 10^9 parameters")
+    n, idx, val, base = sd.sparse_1b()
+    K, N = len(idx), base.numel()
+    nnz = sum(int(i.numel()) for i in idx)
+    out = torch.empty(N, dtype=torch.float32, device="cuda")
+    counts = torch.empty(N, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(fa.sparse_workspace_size(K, N), dtype=torch.uint8, device="cuda")
+    nl = n.tolist()
+    fn = lambda i: fa.sparse_masked_accumulate(idx, val, nl, N, base, out, counts=counts, workspace=ws,
+                                               err_flag=err)
+    wall, durs = timed(fn, steps, warmup)
+    assert int(err.item()) == 0
+    algo = 12 * nnz + 9 * N
+    avg = sum(durs) / len(durs)
+    del idx, val, base, out, counts, ws
+    free_gpu()
+    return {"K": K, "N": N, "dtype": "f32", "pairs": nnz, "ms_per_call": avg, "algo_bytes": algo,
+            "hbm_gbs": algo / (avg * 1e-3) / 1e9, "hbm_frac": algo / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "params_per_s": nnz / (avg * 1e-3)}
+
+
+def bench_copy_calibration(gib=4):
+    """A plain device copy of known size (torch's copy kernel), so hardware
+    byte counters can be scaled: it must fetch and write exactly `gib` GiB."""
+    import torch
+    n = (gib << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    free_gpu()
+    return {"bytes_read": gib << 30, "bytes_written": gib << 30, "launches": 3}
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline
+# --------------------------------------------------------------------------
+
+def cpu_baseline(target_s=10.0):
+    import numpy as np
+    import oracle
+    import synth
+    K, S = 16, 1 << 22
+    log(f"cpu baseline: oracle on a {S}-parameter sample of the K=16 bf16 workload")
+    base, xs = synth.dense_clients_bf16(synth.CFG_DENSE_2B, K, S, 0.02, 1e-3)
+    n = synth.sample_counts(synth.CFG_DENSE_2B, K, 100, 1000)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.weighted_average(xs, n, x_dtype=oracle.BF16)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    return {"value": K * S * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {S} parameters of the K=16 bf16 dense workload (same distributions), "
+                      f"{reps} passes, {el:.1f} s, single-threaded C oracle (fp64)"}
+
+
+def traffic_from_counters():
+    """HBM bytes per launch of the headline kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs, or None when absent or when the kernel source
+    has changed since they were taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default="all",
+                    help="comma list of: dense,dense_small,adapter,streaming,sparse,cpu,copycal "
+                         "(default all but copycal)")
+    ap.add_argument("--stream-clients", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the aggregation shards by parameter range, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import weighted_model_update_amd as fa
+    fa.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    only = set(args.only.split(",")) if args.only != "all" else {"dense", "dense_small", "adapter",
+                                                                 "streaming", "sparse", "cpu"}
+    if args.no_cpu_baseline:
+        only.discard("cpu")
+
+    modes = {}
+    head = None
+    if "dense" in only:
+        head = bench_dense_2b(args.steps, args.warmup)
+        log(f"dense 2B: {head['avg_launch_ms']:.3f} ms/launch")
+    if "dense_small" in only:
+        modes["dense_small"] = bench_dense_small()
+        log(f"dense_small: {modes['dense_small']['us_per_call']:.2f} us/call")
+    if "adapter" in only:
+        modes["adapter"] = bench_adapter()
+        log(f"adapter: {modes['adapter']['us_per_call']:.2f} us/call")
+    if "sparse" in only:
+        modes["sparse"] = bench_sparse()
+        log(f"sparse: {modes['sparse']['ms_per_call']:.3f} ms/call")
+    if "streaming" in only:
+        modes["streaming"] = bench_streaming(args.stream_clients)
+        log(f"streaming: {modes['streaming']['wall_s']:.2f} s")
+    if "copycal" in only:
+        modes["copy_calibration"] = bench_copy_calibration()
+    cpu = cpu_baseline() if "cpu" in only else None
+
+    rec = {"metric": METRIC, "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic (seeded, generated on the GPU)"}
+    if head is not None:
+        ms = head["wall_s"] * 1000.0 / args.steps
+        achieved = head["algo_bytes"] / (head["avg_launch_ms"] * 1e-3) / 1e9
+        rec.update({
+            "value": head["K"] * head["N"] / (ms * 1e-3),
+            "ms_per_step": ms,
+            "config": {"workload": "dense FedAvg, K=16 resident bf16 clients of a 1,921,878,016-parameter "
+                                   "transformer tensor list, fp32 accumulation, bf16 output",
+                       "K": head["K"], "N": head["N"], "mode": "weights", "io_dtype": "bf16",
+                       "hbm_gbs": achieved},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(),
+                         "kernel": "dense_vec_kernel<bf16,bf16,K=16>",
+                         "algo_bytes_per_launch": head["algo_bytes"],
+                         "avg_launch_ms": head["avg_launch_ms"]},
+        })
+    else:
+        rec.update({"value": None, "ms_per_step": None, "config": {"workload": "partial run: " + args.only}})
+    rec["cpu_baseline"] = cpu
+    rec["modes"] = modes
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -262,13 +262,19 @@ int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *ha
  * change how work is spread over the GPU, never the results.
  * ------------------------------------------------------------------------ */
 typedef enum {
-    FA_OPT_BLOCKS_PER_CU = 1,          /* grid-stride kernels: workgroups per CU
-                                          (default 8; 0 = one 8-parameter
-                                          vector per thread, no striding) */
+    FA_OPT_BLOCKS_PER_CU = 1,          /* cap on the grid of the streaming
+                                          kernels, in workgroups per CU, each
+                                          thread then striding over the data
+                                          (default 0: no cap, one 8-parameter
+                                          vector per thread) */
     FA_OPT_MASK_VECTORS_PER_BLOCK = 2, /* masked aggregate: 8-parameter vectors
                                           per workgroup (default 1024) */
-    FA_OPT_SPARSE_BLOCKS = 3           /* sparse merge: parameter ranges, i.e.
-                                          workgroups (default 2048, max 4096) */
+    FA_OPT_SPARSE_BLOCKS = 3,          /* sparse merge: parameter ranges, i.e.
+                                          workgroups (default 0: one per
+                                          resident slot of the GPU; max 4096) */
+    FA_OPT_RESIDENT_PER_CU = 4         /* resident dense kernel: workgroups of
+                                          256 threads resident per CU
+                                          (default 0 = hardware limit) */
 } fa_option;
 
 /* Set one option; FA_ERR_ARG for an unknown option, FA_ERR_RANGE for a value

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True)
 def _restore_options():
     yield
-    fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 2048)
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 0)
 
 
 def run_sparse(idx, val, n, N, base, mode="deltas", counts_dtype=torch.uint8, want_wsum=True,

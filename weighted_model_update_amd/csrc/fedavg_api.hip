@@ -56,9 +56,10 @@ bool overlap_ok(const void *a, size_t abytes, const void *b, size_t bbytes)
 }
 
 // Launch-shape options (fedavg_set_option).
-int64_t g_blocks_per_cu = 8;     // grid-stride kernels: workgroups per CU
+int64_t g_blocks_per_cu = 0;     // grid-stride cap, workgroups per CU (0: none)
+int64_t g_resident_per_cu = 0;   // dense kernel: resident workgroups per CU (0: no cap)
 int64_t g_mask_vpb = 1024;       // masked kernel: 8-parameter vectors per block
-int64_t g_sparse_blocks = 2048;  // sparse merge: parameter ranges (workgroups)
+int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: one per resident slot)
 constexpr int64_t SPARSE_MAX_BLOCKS = 4096;
 constexpr size_t HEADER_BYTES = 256;
 
@@ -161,9 +162,14 @@ int fedavg_set_option(int option, int64_t value)
             return fail(FA_ERR_RANGE, "vectors per block must be in [1, 2^24]");
         g_mask_vpb = value;
         return ok();
+    case FA_OPT_RESIDENT_PER_CU:
+        if (value < 0 || value > 32)
+            return fail(FA_ERR_RANGE, "resident workgroups per CU must be in [0, 32]");
+        g_resident_per_cu = value;
+        return ok();
     case FA_OPT_SPARSE_BLOCKS:
-        if (value < 1 || value > SPARSE_MAX_BLOCKS)
-            return fail(FA_ERR_RANGE, "sparse blocks must be in [1, %lld]",
+        if (value < 0 || value > SPARSE_MAX_BLOCKS)
+            return fail(FA_ERR_RANGE, "sparse blocks must be in [0, %lld]",
                         (long long)SPARSE_MAX_BLOCKS);
         g_sparse_blocks = value;
         return ok();
@@ -247,7 +253,7 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
         d.out = out;
         d.S = (float)S;
         hipError_t e = fa::launch_dense(d, x_dtype, out_dtype, base_dtype, mode, aligned,
-                                        grid_cap(), s);
+                                        grid_cap(), (int)g_resident_per_cu, s);
         return e == hipSuccess ? ok() : hip_fail(e, "dense aggregate launch");
     }
 
@@ -482,7 +488,7 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
         const int part = !st.partial ? fa::PART_DENSE : (mask ? fa::PART_MASK : fa::PART_RANGE);
         const bool aligned = (offset % fa::VEC) == 0 && aligned16(a.chunk) &&
                              (!a.mask || (reinterpret_cast<uintptr_t>(a.mask) & 7u) == 0);
-        e = fa::launch_stream_accumulate(a, dtype, part, aligned, grid_cap(), st.compute);
+        e = fa::launch_stream_accumulate(a, dtype, part, aligned, grid_cap(), 0, st.compute);
     }
     if (e != hipSuccess)
         return hip_fail(e, "accumulate launch");
@@ -538,7 +544,7 @@ int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *ou
     a.S = (float)S;
     const bool aligned = aligned16(out) && (!base || aligned16(base));
     e = fa::launch_stream_finalize(a, base_dtype, out_dtype, st.mode, st.partial, aligned,
-                                   grid_cap(), st.compute);
+                                   grid_cap(), 0, st.compute);
     return e == hipSuccess ? ok() : hip_fail(e, "finalize launch");
 }
 
@@ -588,7 +594,12 @@ int fedavg_destroy(fa_handle h)
 static int64_t sparse_blocks_for(int64_t N)
 {
     const int64_t tiles = (N + fa::SP_TILE - 1) / fa::SP_TILE;
-    int64_t nb = std::min<int64_t>(tiles, g_sparse_blocks);
+    // default: exactly one workgroup per resident slot, so all ranges run in
+    // a single round with no tail
+    int64_t want = g_sparse_blocks > 0 ? g_sparse_blocks
+                                       : (int64_t)fa::sparse_resident_blocks_per_cu() * cu_count();
+    want = std::min<int64_t>(want, SPARSE_MAX_BLOCKS);
+    int64_t nb = std::min<int64_t>(tiles, want);
     if (nb < 1)
         nb = 1;
     const int64_t tiles_per_block = (tiles + nb - 1) / nb;

@@ -97,16 +97,18 @@ struct SparseArgs {
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  `grid_cap` bounds the number
-// of workgroups of grid-stride kernels (0: one element group per thread).
+// of workgroups of grid-stride kernels (0: one 8-element group per thread);
+// `resident` caps the workgroups resident per CU (0: hardware limit).
 hipError_t launch_dense(const DenseArgs &a, int xdt, int odt, int bdt, int mode, bool aligned,
-                        int64_t grid_cap, hipStream_t s);
+                        int64_t grid_cap, int resident, hipStream_t s);
 hipError_t launch_masked(const MaskedArgs &a, int xdt, int odt, int bdt, int mode, bool aligned,
                          hipStream_t s);
 hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool aligned,
-                                    int64_t grid_cap, hipStream_t s);
+                                    int64_t grid_cap, int resident, hipStream_t s);
 hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStream_t s);
 hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int mode, int partial,
-                                  bool aligned, int64_t grid_cap, hipStream_t s);
+                                  bool aligned, int64_t grid_cap, int resident, hipStream_t s);
+int sparse_resident_blocks_per_cu();
 hipError_t launch_sparse(const SparseArgs &a, hipStream_t s);
 hipError_t launch_checksum(const void *buf, int64_t count, int dt, uint64_t *hash,
                            hipStream_t s);

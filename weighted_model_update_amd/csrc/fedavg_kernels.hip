@@ -45,6 +45,25 @@ __device__ __forceinline__ uint32_t to_bf16(float f)
 template <int DT> struct io;
 
 template <> struct io<DT_F32> {
+    struct raw {
+        f32x4 a, b;
+    };
+    static __device__ __forceinline__ raw load_raw(const void *p, int64_t e)
+    {
+        const f32x4 *q = reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + e);
+        return raw{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1)};
+    }
+    static __device__ __forceinline__ void fma8(const raw &r, float w, float (&acc)[VEC])
+    {
+        acc[0] = __builtin_fmaf(w, r.a.x, acc[0]);
+        acc[1] = __builtin_fmaf(w, r.a.y, acc[1]);
+        acc[2] = __builtin_fmaf(w, r.a.z, acc[2]);
+        acc[3] = __builtin_fmaf(w, r.a.w, acc[3]);
+        acc[4] = __builtin_fmaf(w, r.b.x, acc[4]);
+        acc[5] = __builtin_fmaf(w, r.b.y, acc[5]);
+        acc[6] = __builtin_fmaf(w, r.b.z, acc[6]);
+        acc[7] = __builtin_fmaf(w, r.b.w, acc[7]);
+    }
     static __device__ __forceinline__ void load8(const void *p, int64_t e, float (&v)[VEC])
     {
         const f32x4 *q = reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + e);
@@ -72,6 +91,26 @@ template <> struct io<DT_F32> {
 };
 
 template <> struct io<DT_BF16> {
+    // eight bf16 kept packed until they are used
+    struct raw {
+        u32x4 v;
+    };
+    static __device__ __forceinline__ raw load_raw(const void *p, int64_t e)
+    {
+        return raw{__builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p) + e))};
+    }
+    static __device__ __forceinline__ void fma8(const raw &r, float w, float (&acc)[VEC])
+    {
+        acc[0] = __builtin_fmaf(w, bf16_lo(r.v.x), acc[0]);
+        acc[1] = __builtin_fmaf(w, bf16_hi(r.v.x), acc[1]);
+        acc[2] = __builtin_fmaf(w, bf16_lo(r.v.y), acc[2]);
+        acc[3] = __builtin_fmaf(w, bf16_hi(r.v.y), acc[3]);
+        acc[4] = __builtin_fmaf(w, bf16_lo(r.v.z), acc[4]);
+        acc[5] = __builtin_fmaf(w, bf16_hi(r.v.z), acc[5]);
+        acc[6] = __builtin_fmaf(w, bf16_lo(r.v.w), acc[6]);
+        acc[7] = __builtin_fmaf(w, bf16_hi(r.v.w), acc[7]);
+    }
     static __device__ __forceinline__ void load8(const void *p, int64_t e, float (&v)[VEC])
     {
         const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p) + e);
@@ -120,28 +159,24 @@ __global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64
         for (int j = 0; j < VEC; ++j)
             acc[j] = 0.0f;
         if constexpr (KC > 0) {
-            float xv[KC][VEC];
+            typename io<XDT>::raw xr[KC];
 #pragma unroll
             for (int k = 0; k < KC; ++k)
-                io<XDT>::load8(a.x[k], e, xv[k]);
+                xr[k] = io<XDT>::load_raw(a.x[k], e);
 #pragma unroll
             for (int k = 0; k < KC; ++k)
-#pragma unroll
-                for (int j = 0; j < VEC; ++j)
-                    acc[j] = __builtin_fmaf(a.w[k], xv[k][j], acc[j]);
+                io<XDT>::fma8(xr[k], a.w[k], acc);
         } else {
             for (int k0 = 0; k0 < K; k0 += 8) {
-                float xv[8][VEC];
+                typename io<XDT>::raw xr[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
                     if (k0 + k < K)
-                        io<XDT>::load8(a.x[k0 + k], e, xv[k]);
+                        xr[k] = io<XDT>::load_raw(a.x[k0 + k], e);
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
                     if (k0 + k < K)
-#pragma unroll
-                        for (int j = 0; j < VEC; ++j)
-                            acc[j] = __builtin_fmaf(a.w[k0 + k], xv[k][j], acc[j]);
+                        io<XDT>::fma8(xr[k], a.w[k0 + k], acc);
             }
         }
         float r[VEC];
@@ -254,12 +289,25 @@ __device__ __forceinline__ void masked_element(const MaskedArgs &a, int64_t e)
     io<ODT>::store1(a.out, e, r);
 }
 
-// Each workgroup owns a contiguous run of `vpb` 8-parameter vectors.  Wave 0
-// locates the segment holding the run's first parameter; the block stages up
-// to SEG_WIN consecutive segments (bounds, client mask, weight sum) in LDS and
-// walks its vectors through them, window after window.  A vector lying inside
-// one segment reads only the clients present there; one that straddles a
-// segment boundary (or the end of the buffer) is done element by element.
+// Element-wise path for a vector whose 8 parameters do not all lie in one
+// segment (or run past the end of the buffer).
+template <int XDT, int ODT, int BDT, int MODE>
+__device__ __forceinline__ void masked_vector_elementwise(const MaskedArgs &a, int64_t e)
+{
+    for (int j = 0; j < VEC; ++j)
+        if (e + j < a.N)
+            masked_element<XDT, ODT, BDT, MODE>(a, e + j);
+}
+
+// Each workgroup owns a contiguous run of `vpb` 8-parameter vectors, walked
+// as spans of blockDim vectors (one per lane).  Wave 0 locates the segment
+// holding the run's first parameter; the block stages up to SEG_WIN
+// consecutive segments (bounds, client mask, weight sum) in LDS and walks its
+// spans through them, window after window.  A span inside one segment -- the
+// usual case, segments being whole tensors -- has one client mask for all
+// lanes, held in scalar registers: the lanes read only the clients present
+// there, with no divergence.  A span that straddles a segment boundary falls
+// back to per-element lookups.
 template <int XDT, int ODT, int BDT, int MODE>
 __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
 {
@@ -299,46 +347,48 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
         const int64_t vw0 = (e_cur + VEC - 1) / VEC;
         const int64_t vw1 = min((win_end + VEC - 1) / VEC, v_end);
 
-        int64_t c_lo = 0, c_hi = 0;
-        uint64_t c_mask = 0;
-        uint32_t c_W = 0;
-        for (int64_t v = vw0 + tid; v < vw1; v += blockDim.x) {
-            const int64_t e = v * VEC;
-            if (!(e >= c_lo && e + VEC <= c_hi)) {
-                int lo = 0, hi = cnt - 1;
-                while (lo < hi) {
-                    int mid = (lo + hi + 1) / 2;
-                    if (s_lo[mid] <= e)
-                        lo = mid;
-                    else
-                        hi = mid - 1;
-                }
-                c_lo = s_lo[lo];
-                c_hi = s_lo[lo + 1];
-                c_mask = s_mask[lo];
-                c_W = s_W[lo];
+        for (int64_t s0 = vw0; s0 < vw1; s0 += blockDim.x) {
+            // block-uniform span [s0, s1) of vectors and its parameters
+            const int64_t s1 = min(s0 + (int64_t)blockDim.x, vw1);
+            const int64_t E0 = s0 * VEC;
+            const int64_t E1 = min(s1 * VEC, a.N);
+            int lo = 0, hi = cnt - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) / 2;
+                if (s_lo[mid] <= E0)
+                    lo = mid;
+                else
+                    hi = mid - 1;
             }
-            if (e >= c_lo && e + VEC <= c_hi && e + VEC <= a.N) {
+            const bool one_segment = s_lo[lo] <= E0 && E1 <= s_lo[lo + 1];
+            const int64_t v = s0 + tid;
+            if (v >= s1)
+                continue;
+            const int64_t e = v * VEC;
+            if (one_segment && e + VEC <= a.N) {
+                const uint64_t smask = s_mask[lo];
+                const uint32_t mlo = __builtin_amdgcn_readfirstlane((uint32_t)smask);
+                const uint32_t mhi = __builtin_amdgcn_readfirstlane((uint32_t)(smask >> 32));
+                const uint64_t mask = ((uint64_t)mhi << 32) | mlo;
+                const uint32_t W = __builtin_amdgcn_readfirstlane(s_W[lo]);
                 float r[VEC];
-                if (c_W > 0) {
+                if (W > 0) {
                     float acc[VEC];
 #pragma unroll
                     for (int j = 0; j < VEC; ++j)
                         acc[j] = 0.0f;
                     for (int k0 = 0; k0 < a.K; k0 += 8) {
-                        float xv[8][VEC];
+                        typename io<XDT>::raw xr[8];
 #pragma unroll
                         for (int k = 0; k < 8; ++k)
-                            if (k0 + k < a.K && ((c_mask >> (k0 + k)) & 1))
-                                io<XDT>::load8(a.x[k0 + k], e, xv[k]);
+                            if (k0 + k < a.K && ((mask >> (k0 + k)) & 1))
+                                xr[k] = io<XDT>::load_raw(a.x[k0 + k], e);
 #pragma unroll
                         for (int k = 0; k < 8; ++k)
-                            if (k0 + k < a.K && ((c_mask >> (k0 + k)) & 1))
-#pragma unroll
-                                for (int j = 0; j < VEC; ++j)
-                                    acc[j] = __builtin_fmaf(a.w[k0 + k], xv[k][j], acc[j]);
+                            if (k0 + k < a.K && ((mask >> (k0 + k)) & 1))
+                                io<XDT>::fma8(xr[k], a.w[k0 + k], acc);
                     }
-                    const float Wf = (float)c_W;
+                    const float Wf = (float)W;
                     if constexpr (MODE == MODE_DELTAS) {
                         float b[VEC];
                         io<BDT>::load8(a.base, e, b);
@@ -355,9 +405,7 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
                 }
                 io<ODT>::store8(a.out, e, r);
             } else {
-                for (int j = 0; j < VEC; ++j)
-                    if (e + j < a.N)
-                        masked_element<XDT, ODT, BDT, MODE>(a, e + j);
+                masked_vector_elementwise<XDT, ODT, BDT, MODE>(a, e);
             }
         }
         e_cur = win_end;
@@ -564,30 +612,42 @@ __global__ __launch_bounds__(256) void sparse_offsets_kernel(const SparseArgs a)
 }
 
 // One workgroup per parameter range of R = (whole tiles) parameters.  For
-// each tile of SP_TILE parameters the fp32 sums, weight sums and client
-// counts live in LDS.  Clients are merged strictly in order, with a barrier
-// between clients, so each parameter sees the same FMA order as the dense
-// path; inside one client the indices are unique, so lanes never collide and
-// no atomics are used.  A client's entries for the tile are fetched as one
-// coalesced batch of SP_THREADS (index, value) pairs from its cursor; the
-// batches of SP_GROUP clients are loaded together so their latencies overlap.
-// The in-tile entries of a sorted batch are a prefix, counted with one
-// barrier-count; the cursor advances by that count (a full batch loads the
-// next one).  After the last client the tile is finalized and written once.
+// each tile of SP_TILE parameters, LDS holds the fp32 sum and a bit mask of
+// the clients that sent the parameter (MW 32-bit words: K <= 32 * MW); the
+// weight sum W and the client count follow from the mask when the tile is
+// finalized.  Clients are merged strictly in order, one barrier between
+// client batches, so each parameter sees the same FMA order as the dense
+// path; inside one batch the indices are unique, so lanes never collide on a
+// sum and no float atomics are used (the mask bit is set with an LDS OR).
+//
+// A client's entries for the tile come as one coalesced batch of SP_THREADS
+// (index, value) pairs read from its cursor, together with each entry's
+// predecessor index for the sortedness check; the batches of SP_GROUP
+// clients are loaded together so their latencies overlap.  The in-tile
+// entries of a sorted batch are a prefix: each wave counts its own with a
+// ballot and the counts meet in LDS (double-buffered, so one barrier per
+// batch suffices).  The cursor advances by the count; a batch that lies
+// wholly inside the tile loads the next one.  After the last client the tile
+// is finalized and written once.
+template <int MW>
 __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseArgs a)
 {
-    __shared__ float s_acc[SP_TILE];
-    __shared__ uint32_t s_W[SP_TILE];
-    __shared__ uint32_t s_cnt[SP_TILE];
+    constexpr int WAVES = SP_THREADS / 64;
+    __shared__ __attribute__((aligned(16))) float s_acc[SP_TILE];
+    __shared__ __attribute__((aligned(16))) uint32_t s_mask[MW][SP_TILE];
     __shared__ int64_t s_cur[FA_MAX_CLIENTS];
     __shared__ int64_t s_end[FA_MAX_CLIENTS];
+    __shared__ uint32_t s_nk[FA_MAX_CLIENTS];
+    __shared__ int s_count[2][WAVES];
 
     const int tid = threadIdx.x;
+    const int wave = tid >> 6;
     const int lane = tid & 63;
     const int b = blockIdx.x;
     const int64_t r0 = (int64_t)b * a.R;
     const int64_t r1 = min(r0 + a.R, a.N);
     bool bad = false;
+    int parity = 0;
 
     if (tid < a.K) {
         const int64_t c0 = a.offs[(int64_t)tid * (a.NB + 1) + b];
@@ -595,22 +655,28 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
         c1 = max(c1, c0);
         s_cur[tid] = c0;
         s_end[tid] = min(c1, a.nnz[tid]);
+        s_nk[tid] = a.wi[tid];
     }
     for (int l = tid; l < SP_TILE; l += SP_THREADS) {
         s_acc[l] = 0.0f;
-        s_W[l] = 0;
-        s_cnt[l] = 0;
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+            s_mask[m][l] = 0u;
     }
     __syncthreads();
 
     for (int64_t t0 = r0; t0 < r1; t0 += SP_TILE) {
         const int64_t t1 = min(t0 + SP_TILE, r1);
         for (int k0 = 0; k0 < a.K; k0 += SP_GROUP) {
-            int64_t gix[SP_GROUP];
+            // one batch per client of the group: this lane's entry, its
+            // value and the index of the entry before it (-1 before the
+            // first; INT64_MAX where the lane holds no entry)
+            int64_t gix[SP_GROUP], gprev[SP_GROUP];
             float gval[SP_GROUP];
 #pragma unroll
             for (int g = 0; g < SP_GROUP; ++g) {
                 gix[g] = INT64_MAX;
+                gprev[g] = INT64_MAX;
                 gval[g] = 0.0f;
                 const int k = k0 + g;
                 if (k < a.K) {
@@ -618,6 +684,7 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
                     if (p < s_end[k]) {
                         gix[g] = a.idx[k][p];
                         gval[g] = a.val[k][p];
+                        gprev[g] = p > 0 ? a.idx[k][p - 1] : -1;
                     }
                 }
             }
@@ -625,44 +692,48 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
             for (int g = 0; g < SP_GROUP; ++g) {
                 const int k = k0 + g;
                 if (k < a.K) {
-                int64_t p0 = s_cur[k];
-                const int64_t pend = s_end[k];
-                int64_t ix = gix[g];
-                float val = gval[g];
-                while (true) {
-                    // predecessor of this lane's entry: the previous lane's,
-                    // or for lane 0 the one before it in the list
-                    int64_t prev = __shfl_up(ix, 1);
-                    if (lane == 0) {
-                        const int64_t pp = p0 + tid - 1;
-                        prev = (pp >= 0 && pp < pend) ? a.idx[k][pp] : -1;
-                        if (pp >= 0 && pp >= pend)
-                            prev = INT64_MAX; // this lane holds no entry
-                    }
-                    const bool in = ix < t1;
-                    const int c = __syncthreads_count(in);
-                    if (in) {
-                        if (ix <= prev || ix < t0) {
-                            bad = true;
-                        } else {
-                            const int l = (int)(ix - t0);
-                            s_acc[l] = __builtin_fmaf(a.w[k], val, s_acc[l]);
-                            s_W[l] += a.wi[k];
-                            s_cnt[l] += 1;
+                    int64_t p0 = s_cur[k];
+                    const int64_t pend = s_end[k];
+                    const float w = a.w[k];
+                    const uint32_t bit = 1u << (k & 31);
+                    uint32_t *mrow = s_mask[MW > 1 ? (k >> 5) : 0];
+                    int64_t ix = gix[g], prev = gprev[g];
+                    float val = gval[g];
+                    while (true) {
+                        const bool in = ix < t1;
+                        const uint64_t bal = __ballot(in);
+                        if (lane == 0)
+                            s_count[parity][wave] = __popcll(bal);
+                        __syncthreads();
+                        int c = 0;
+#pragma unroll
+                        for (int v = 0; v < WAVES; ++v)
+                            c += s_count[parity][v];
+                        parity ^= 1;
+                        if (in) {
+                            if (ix <= prev || ix < t0) {
+                                bad = true;
+                            } else {
+                                const int l = (int)(ix - t0);
+                                s_acc[l] = __builtin_fmaf(w, val, s_acc[l]);
+                                atomicOr(&mrow[l], bit);
+                            }
+                        }
+                        p0 += c;
+                        if (c < SP_THREADS || p0 >= pend)
+                            break;
+                        // a whole batch was inside the tile: fetch the next
+                        const int64_t p = p0 + tid;
+                        ix = INT64_MAX;
+                        prev = INT64_MAX;
+                        if (p < pend) {
+                            ix = a.idx[k][p];
+                            val = a.val[k][p];
+                            prev = a.idx[k][p - 1];
                         }
                     }
-                    p0 += c;
-                    if (c < SP_THREADS || p0 >= pend)
-                        break;
-                    const int64_t p = p0 + tid;
-                    ix = INT64_MAX;
-                    if (p < pend) {
-                        ix = a.idx[k][p];
-                        val = a.val[k][p];
-                    }
-                }
-                if (tid == 0)
-                    s_cur[k] = p0;
+                    if (tid == 0)
+                        s_cur[k] = p0;
                 }
             }
         }
@@ -671,24 +742,38 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
         // finalize the tile: 8 consecutive parameters per lane
         const int l0 = tid * VEC;
         const int64_t e0 = t0 + l0;
+        float acc[VEC];
+        uint32_t W[VEC], cnt[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            uint32_t wsum = 0, c = 0;
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                uint32_t bits = s_mask[m][l0 + j];
+                c += __popc(bits);
+                while (bits) {
+                    wsum += s_nk[m * 32 + __ffs(bits) - 1];
+                    bits &= bits - 1;
+                }
+                s_mask[m][l0 + j] = 0u;
+            }
+            W[j] = wsum;
+            cnt[j] = c;
+            acc[j] = s_acc[l0 + j];
+            s_acc[l0 + j] = 0.0f;
+        }
         if (a.aligned && e0 + VEC <= t1) {
             float base8[VEC];
             io<DT_F32>::load8(a.base, e0, base8);
             float r[VEC];
-            uint32_t cnt[VEC], W[VEC];
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
-                W[j] = s_W[l0 + j];
-                cnt[j] = s_cnt[l0 + j];
                 if (W[j] > 0) {
-                    const float q = s_acc[l0 + j] / (float)W[j];
+                    const float q = acc[j] / (float)W[j];
                     r[j] = a.mode == MODE_DELTAS ? base8[j] + q : q;
                 } else {
                     r[j] = base8[j];
                 }
-                s_acc[l0 + j] = 0.0f;
-                s_W[l0 + j] = 0;
-                s_cnt[l0 + j] = 0;
             }
             io<DT_F32>::store8(a.out, e0, r);
             if (a.counts) {
@@ -711,32 +796,27 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
             }
         } else {
             for (int j = 0; j < VEC; ++j) {
-                const int l = l0 + j;
                 const int64_t e = e0 + j;
                 if (e < t1) {
-                    const uint32_t W = s_W[l];
                     const float bv = a.base[e];
                     float r = bv;
-                    if (W > 0) {
-                        const float q = s_acc[l] / (float)W;
+                    if (W[j] > 0) {
+                        const float q = acc[j] / (float)W[j];
                         r = a.mode == MODE_DELTAS ? bv + q : q;
                     }
                     a.out[e] = r;
                     if (a.counts) {
                         if (a.counts_u32)
-                            static_cast<uint32_t *>(a.counts)[e] = s_cnt[l];
+                            static_cast<uint32_t *>(a.counts)[e] = cnt[j];
                         else
-                            static_cast<uint8_t *>(a.counts)[e] = (uint8_t)s_cnt[l];
+                            static_cast<uint8_t *>(a.counts)[e] = (uint8_t)cnt[j];
                     }
                     if (a.wsum)
-                        a.wsum[e] = W;
+                        a.wsum[e] = W[j];
                 }
-                s_acc[l] = 0.0f;
-                s_W[l] = 0;
-                s_cnt[l] = 0;
             }
         }
-        // the next tile's first barrier-count orders these zeroes before use
+        // the next tile's first barrier orders these zeroes before use
     }
     if (bad)
         *a.err = FA_ERR_INDEX;
@@ -793,6 +873,49 @@ __global__ __launch_bounds__(256) void convert_kernel(const void *src, void *dst
 
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+static int lds_bytes_per_cu()
+{
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    if (cache[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess ||
+            v <= 0)
+            v = 65536;
+        cache[dev] = v;
+    }
+    return cache[dev];
+}
+
+// Streaming kernels over HBM run fastest with few resident waves per CU (a
+// measured property of MI355X when reads and writes mix: more waves in
+// flight only add DRAM read/write turnarounds).  Residency is capped by
+// reserving dynamic LDS: a request between 1/(cap+1) and 1/cap of the CU's
+// LDS admits exactly `cap` workgroups per CU.  The kernels do not use it.
+template <typename F>
+static size_t residency_lds(F *kernel, int cap)
+{
+    if (cap <= 0)
+        return 0;
+    const int lds = lds_bytes_per_cu();
+    if (lds <= 0)
+        return 0;
+    const size_t bytes = ((size_t)lds / cap + (size_t)lds / (cap + 1)) / 2;
+    static int configured_max = 0; // one per kernel instantiation
+    if ((int)bytes > configured_max) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        configured_max = (int)bytes;
+    }
+    return bytes;
+}
+
 static inline unsigned grid_for(int64_t work, int threads, int64_t cap)
 {
     int64_t g = ceil_div(work, threads);
@@ -805,17 +928,24 @@ static inline unsigned grid_for(int64_t work, int threads, int64_t cap)
     return (unsigned)g;
 }
 
+template <int XDT, int ODT, int BDT, int MODE, int KC>
+static void dense_vec_launch(const DenseArgs &a, int64_t nvec, int64_t cap, int resident, hipStream_t s)
+{
+    auto *k = &dense_vec_kernel<XDT, ODT, BDT, MODE, KC>;
+    k<<<grid_for(nvec, 256, cap), 256, residency_lds(k, resident), s>>>(a, nvec);
+}
+
 template <int XDT, int ODT, int BDT, int MODE>
-static hipError_t dense_launch_t(const DenseArgs &a, bool aligned, int64_t cap, hipStream_t s)
+static hipError_t dense_launch_t(const DenseArgs &a, bool aligned, int64_t cap, int resident,
+                                 hipStream_t s)
 {
     const int64_t nvec = aligned ? a.N / VEC : 0;
     if (nvec > 0) {
-        const unsigned g = grid_for(nvec, 256, cap);
         switch (a.K) {
-        case 3: dense_vec_kernel<XDT, ODT, BDT, MODE, 3><<<g, 256, 0, s>>>(a, nvec); break;
-        case 8: dense_vec_kernel<XDT, ODT, BDT, MODE, 8><<<g, 256, 0, s>>>(a, nvec); break;
-        case 16: dense_vec_kernel<XDT, ODT, BDT, MODE, 16><<<g, 256, 0, s>>>(a, nvec); break;
-        default: dense_vec_kernel<XDT, ODT, BDT, MODE, 0><<<g, 256, 0, s>>>(a, nvec); break;
+        case 3: dense_vec_launch<XDT, ODT, BDT, MODE, 3>(a, nvec, cap, resident, s); break;
+        case 8: dense_vec_launch<XDT, ODT, BDT, MODE, 8>(a, nvec, cap, resident, s); break;
+        case 16: dense_vec_launch<XDT, ODT, BDT, MODE, 16>(a, nvec, cap, resident, s); break;
+        default: dense_vec_launch<XDT, ODT, BDT, MODE, 0>(a, nvec, cap, resident, s); break;
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -858,9 +988,9 @@ static hipError_t dispatch4(int xdt, int odt, int bdt, int mode, Args &&...args)
 }
 
 template <int X, int O, int B, int M> struct DenseRun {
-    static hipError_t run(const DenseArgs &a, bool aligned, int64_t cap, hipStream_t s)
+    static hipError_t run(const DenseArgs &a, bool aligned, int64_t cap, int resident, hipStream_t s)
     {
-        return dense_launch_t<X, O, B, M>(a, aligned, cap, s);
+        return dense_launch_t<X, O, B, M>(a, aligned, cap, resident, s);
     }
 };
 
@@ -879,9 +1009,9 @@ template <int X, int O, int B, int M> struct MaskedRun {
 };
 
 hipError_t launch_dense(const DenseArgs &a, int xdt, int odt, int bdt, int mode, bool aligned,
-                        int64_t grid_cap, hipStream_t s)
+                        int64_t grid_cap, int resident, hipStream_t s)
 {
-    return dispatch4<DenseRun>(xdt, odt, bdt, mode, a, aligned, grid_cap, s);
+    return dispatch4<DenseRun>(xdt, odt, bdt, mode, a, aligned, grid_cap, resident, s);
 }
 
 hipError_t launch_masked(const MaskedArgs &a, int xdt, int odt, int bdt, int mode, bool aligned,
@@ -891,11 +1021,13 @@ hipError_t launch_masked(const MaskedArgs &a, int xdt, int odt, int bdt, int mod
 }
 
 template <int DT, int PART>
-static hipError_t stream_acc_t(const StreamArgs &a, bool aligned, int64_t cap, hipStream_t s)
+static hipError_t stream_acc_t(const StreamArgs &a, bool aligned, int64_t cap, int resident,
+                               hipStream_t s)
 {
     const int64_t nvec = aligned ? a.len / VEC : 0;
     if (nvec > 0) {
-        stream_acc_vec_kernel<DT, PART><<<grid_for(nvec, 256, cap), 256, 0, s>>>(a, nvec);
+        auto *k = &stream_acc_vec_kernel<DT, PART>;
+        k<<<grid_for(nvec, 256, cap), 256, residency_lds(k, resident), s>>>(a, nvec);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -910,11 +1042,11 @@ static hipError_t stream_acc_t(const StreamArgs &a, bool aligned, int64_t cap, h
 }
 
 hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool aligned,
-                                    int64_t cap, hipStream_t s)
+                                    int64_t cap, int resident, hipStream_t s)
 {
 #define FA_CASE(D, P)                                                                              \
     if (dt == D && part == P)                                                                      \
-        return stream_acc_t<D, P>(a, aligned, cap, s);
+        return stream_acc_t<D, P>(a, aligned, cap, resident, s);
     FA_CASE(DT_F32, PART_DENSE)
     FA_CASE(DT_F32, PART_RANGE)
     FA_CASE(DT_F32, PART_MASK)
@@ -936,11 +1068,13 @@ hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStre
 }
 
 template <int B, int O, int M, int P>
-static hipError_t finalize_t(const FinalizeArgs &a, bool aligned, int64_t cap, hipStream_t s)
+static hipError_t finalize_t(const FinalizeArgs &a, bool aligned, int64_t cap, int resident,
+                             hipStream_t s)
 {
     const int64_t nvec = aligned ? a.N / VEC : 0;
     if (nvec > 0) {
-        stream_finalize_vec_kernel<B, O, M, P><<<grid_for(nvec, 256, cap), 256, 0, s>>>(a, nvec);
+        auto *k = &stream_finalize_vec_kernel<B, O, M, P>;
+        k<<<grid_for(nvec, 256, cap), 256, residency_lds(k, resident), s>>>(a, nvec);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -955,11 +1089,11 @@ static hipError_t finalize_t(const FinalizeArgs &a, bool aligned, int64_t cap, h
 }
 
 hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int mode, int partial,
-                                  bool aligned, int64_t cap, hipStream_t s)
+                                  bool aligned, int64_t cap, int resident, hipStream_t s)
 {
 #define FA_CASE(B, O, M, P)                                                                        \
     if (bdt == B && odt == O && mode == M && partial == P)                                        \
-        return finalize_t<B, O, M, P>(a, aligned, cap, s);
+        return finalize_t<B, O, M, P>(a, aligned, cap, resident, s);
 #define FA_CASES(B, O)                                                                             \
     FA_CASE(B, O, MODE_WEIGHTS, 0)                                                                 \
     FA_CASE(B, O, MODE_WEIGHTS, 1)                                                                 \
@@ -974,6 +1108,18 @@ hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int m
     return hipErrorInvalidValue;
 }
 
+int sparse_resident_blocks_per_cu()
+{
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, sparse_merge_kernel<1>, SP_THREADS, 0) !=
+            hipSuccess ||
+        occ <= 0) {
+        (void)hipGetLastError();
+        occ = 1;
+    }
+    return occ;
+}
+
 hipError_t launch_sparse(const SparseArgs &a, hipStream_t s)
 {
     const int64_t total = (int64_t)a.K * (a.NB + 1);
@@ -981,7 +1127,10 @@ hipError_t launch_sparse(const SparseArgs &a, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    sparse_merge_kernel<<<a.NB, SP_THREADS, 0, s>>>(a);
+    if (a.K <= 32)
+        sparse_merge_kernel<1><<<a.NB, SP_THREADS, 0, s>>>(a);
+    else
+        sparse_merge_kernel<2><<<a.NB, SP_THREADS, 0, s>>>(a);
     return hipGetLastError();
 }
 
