@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -35,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 PCIE_PEAK_GBS = 64.0       # PCIe Gen5 x16 per direction, GB/s
 METRIC = "aggregated params/sec and achieved HBM GB/s (% of MI355X peak), K clients"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "dense_k16_bf16_2b_hbm_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "dense_k16_bf16_2b_hbm_counters.md")
 KERNEL_SOURCE = os.path.join(ROOT, "weighted_model_update_amd", "csrc", "fedavg_kernels.hip")
 
 
@@ -269,18 +270,23 @@ def bench_sparse(steps=10, warmup=2):
 
 
 def bench_copy_calibration(gib=4):
-    """A plain device copy of known size (torch's copy kernel), so hardware
-    byte counters can be scaled: it must fetch and write exactly `gib` GiB."""
+    """A plain device copy of known size, so hardware byte counters can be
+    scaled: the library's element copy (the no-contributor path of
+    fedavg_aggregate, convert_kernel<f32,f32>) reads and writes exactly
+    `gib` GiB."""
     import torch
+    import weighted_model_update_amd as fa
     n = (gib << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    dummy = torch.empty(n, dtype=torch.float32, device="cuda")
     for _ in range(3):
-        dst.copy_(src)
+        fa.fedavg_aggregate([dummy], [0], dst, mode="deltas", base=src)
     torch.cuda.synchronize()
-    del src, dst
+    del src, dst, dummy
     free_gpu()
-    return {"bytes_read": gib << 30, "bytes_written": gib << 30, "launches": 3}
+    return {"kernel": "convert_kernel<0, 0>", "bytes_read": gib << 30, "bytes_written": gib << 30,
+            "launches": 3}
 
 
 # --------------------------------------------------------------------------
@@ -310,16 +316,20 @@ def cpu_baseline(target_s=10.0):
 
 def traffic_from_counters():
     """HBM bytes per launch of the headline kernel from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE runs, or None when absent or when the kernel source
-    has changed since they were taken."""
+    FETCH_SIZE/WRITE_SIZE summary (scaled by a copy of known size), or None
+    when it is absent or the kernel source has changed since it was taken."""
     try:
         with open(COUNTERS_FILE) as f:
-            c = json.load(f)
-    except (OSError, ValueError):
+            text = f.read()
+    except OSError:
         return None
-    if c.get("kernel_source_sha256") != kernel_source_sha():
+    fields = dict(re.findall(r"^(kernel_source_sha256|traffic_bytes_per_launch):\s*(\S+)\s*$", text, re.M))
+    if fields.get("kernel_source_sha256") != kernel_source_sha():
         return None
-    return c.get("traffic_bytes_per_launch")
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():

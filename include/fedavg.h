@@ -270,11 +270,13 @@ typedef enum {
     FA_OPT_MASK_VECTORS_PER_BLOCK = 2, /* masked aggregate: 8-parameter vectors
                                           per workgroup (default 1024) */
     FA_OPT_SPARSE_BLOCKS = 3,          /* sparse merge: parameter ranges, i.e.
-                                          workgroups (default 0: one per
-                                          resident slot of the GPU; max 4096) */
-    FA_OPT_RESIDENT_PER_CU = 4         /* resident dense kernel: workgroups of
+                                          workgroups (default 0: 16384, fewer
+                                          when N is small; max 65536) */
+    FA_OPT_RESIDENT_PER_CU = 4,        /* resident dense kernel: workgroups of
                                           256 threads resident per CU
-                                          (default 0 = hardware limit) */
+                                          (default 3; 0 = hardware limit) */
+    FA_OPT_SPARSE_TILE = 5             /* sparse merge: parameters per LDS tile,
+                                          2048 (default), 4096 or 8192 */
 } fa_option;
 
 /* Set one option; FA_ERR_ARG for an unknown option, FA_ERR_RANGE for a value

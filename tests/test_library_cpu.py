@@ -63,7 +63,7 @@ def test_host_side_argument_errors_need_no_device():
                                         (ctypes.c_int64 * 1)(1), 100, 1, P(1 << 22), P(1 << 23), None, 0,
                                         None, P(1 << 24), 8, None, None) == -8
     assert lib.fedavg_set_option(99, 1) == -1
-    assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 5000) == -3
+    assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 70000) == -3
     assert lib.fedavg_checksum(None, 10, 0, None, None) == -1
 
 
@@ -75,7 +75,8 @@ def test_workspace_sizes_do_not_depend_on_the_number_of_clients():
     assert ws == 4 * 10 ** 6 and cnt == 10 ** 6 and stag2 > stag
     with pytest.raises(fa.FedAvgError):
         fa.fedavg_workspace_size(10, 0, 0, 2)
-    assert fa.sparse_workspace_size(20, 10 ** 9) < 1 << 20
+    assert fa.sparse_workspace_size(20, 10 ** 9) < 16 << 20
+    assert fa.sparse_workspace_size(20, 4096) < 1024
 
 
 def test_streaming_null_handle_and_state():

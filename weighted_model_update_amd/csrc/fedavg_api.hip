@@ -57,10 +57,12 @@ bool overlap_ok(const void *a, size_t abytes, const void *b, size_t bbytes)
 
 // Launch-shape options (fedavg_set_option).
 int64_t g_blocks_per_cu = 0;     // grid-stride cap, workgroups per CU (0: none)
-int64_t g_resident_per_cu = 0;   // dense kernel: resident workgroups per CU (0: no cap)
+int64_t g_resident_per_cu = 3;   // dense kernel: resident workgroups per CU (0: no cap)
 int64_t g_mask_vpb = 1024;       // masked kernel: 8-parameter vectors per block
-int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: one per resident slot)
-constexpr int64_t SPARSE_MAX_BLOCKS = 4096;
+int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: SPARSE_DEFAULT_BLOCKS)
+int64_t g_sparse_tile = fa::SP_DEFAULT_TILE;
+constexpr int64_t SPARSE_MAX_BLOCKS = 65536;
+constexpr int64_t SPARSE_DEFAULT_BLOCKS = 16384;
 constexpr size_t HEADER_BYTES = 256;
 
 int cu_count()
@@ -166,6 +168,11 @@ int fedavg_set_option(int option, int64_t value)
         if (value < 0 || value > 32)
             return fail(FA_ERR_RANGE, "resident workgroups per CU must be in [0, 32]");
         g_resident_per_cu = value;
+        return ok();
+    case FA_OPT_SPARSE_TILE:
+        if (value != 2048 && value != 4096 && value != 8192)
+            return fail(FA_ERR_RANGE, "sparse tile must be 2048, 4096 or 8192");
+        g_sparse_tile = value;
         return ok();
     case FA_OPT_SPARSE_BLOCKS:
         if (value < 0 || value > SPARSE_MAX_BLOCKS)
@@ -591,19 +598,20 @@ int fedavg_destroy(fa_handle h)
 
 // ============================================================ sparse
 
-static int64_t sparse_blocks_for(int64_t N)
+static int64_t sparse_blocks_for(int64_t N, int64_t tile)
 {
-    const int64_t tiles = (N + fa::SP_TILE - 1) / fa::SP_TILE;
-    // default: exactly one workgroup per resident slot, so all ranges run in
-    // a single round with no tail
-    int64_t want = g_sparse_blocks > 0 ? g_sparse_blocks
-                                       : (int64_t)fa::sparse_resident_blocks_per_cu() * cu_count();
+    const int64_t tiles = (N + tile - 1) / tile;
+    // Many short ranges rather than one per resident slot: workgroups start
+    // in range order, so the ones running at any moment read neighbouring
+    // stretches of every client's list (measured faster on MI355X than
+    // persistent workgroups spread over the whole index space)
+    int64_t want = g_sparse_blocks > 0 ? g_sparse_blocks : SPARSE_DEFAULT_BLOCKS;
     want = std::min<int64_t>(want, SPARSE_MAX_BLOCKS);
     int64_t nb = std::min<int64_t>(tiles, want);
     if (nb < 1)
         nb = 1;
     const int64_t tiles_per_block = (tiles + nb - 1) / nb;
-    const int64_t R = tiles_per_block * fa::SP_TILE;
+    const int64_t R = tiles_per_block * tile;
     return (N + R - 1) / R;
 }
 
@@ -613,7 +621,10 @@ int sparse_workspace_size(int K, int64_t N, size_t *bytes)
         return fail(FA_ERR_RANGE, "K=%d outside [1, %d]", K, FA_MAX_CLIENTS);
     if (N < 0 || !bytes)
         return fail(FA_ERR_ARG, "need N >= 0 and a result pointer");
-    *bytes = HEADER_BYTES + (size_t)K * (SPARSE_MAX_BLOCKS + 1) * sizeof(int64_t);
+    // one list offset per client and range boundary; there are never more
+    // ranges than tiles of the smallest size
+    const int64_t max_ranges = std::min<int64_t>(SPARSE_MAX_BLOCKS, std::max<int64_t>(1, (N + 2047) / 2048));
+    *bytes = HEADER_BYTES + (size_t)K * (size_t)(max_ranges + 1) * sizeof(int64_t);
     return ok();
 }
 
@@ -672,13 +683,15 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
         return hip_fail(e, "flag reset");
     if (N == 0)
         return ok();
-    const int64_t NB = sparse_blocks_for(N);
-    const int64_t tiles = (N + fa::SP_TILE - 1) / fa::SP_TILE;
-    const int64_t R = ((tiles + NB - 1) / NB) * fa::SP_TILE;
+    const int64_t tile = g_sparse_tile;
+    const int64_t NB = sparse_blocks_for(N, tile);
+    const int64_t tiles = (N + tile - 1) / tile;
+    const int64_t R = ((tiles + NB - 1) / NB) * tile;
     a.K = Kc;
     a.NB = (int)NB;
     a.N = N;
     a.R = R;
+    a.tile = (int)tile;
     a.offs = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + HEADER_BYTES);
     a.base = base;
     a.out = out;

@@ -70,9 +70,8 @@ struct FinalizeArgs {
 };
 
 // ---------------------------------------------------------------- sparse
-constexpr int SP_TILE = 4096;   // parameters per LDS tile
-constexpr int SP_THREADS = 512; // threads per merge block
 constexpr int SP_GROUP = 8;     // clients whose batches are loaded together
+constexpr int SP_DEFAULT_TILE = 2048; // parameters per LDS tile (2048, 4096 or 8192)
 
 struct SparseArgs {
     const int64_t *idx[FA_MAX_CLIENTS];
@@ -83,7 +82,8 @@ struct SparseArgs {
     int K;
     int NB;    // blocks (parameter ranges)
     int64_t N;
-    int64_t R; // parameters per block range, a multiple of SP_TILE
+    int64_t R; // parameters per block range, a multiple of the tile
+    int tile;  // parameters per LDS tile: 2048, 4096 or 8192
     int64_t *offs; // [K][NB+1] first list position at or after each range start
     const float *base;
     float *out;
@@ -108,7 +108,7 @@ hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool 
 hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStream_t s);
 hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int mode, int partial,
                                   bool aligned, int64_t grid_cap, int resident, hipStream_t s);
-int sparse_resident_blocks_per_cu();
+int sparse_resident_blocks_per_cu(int tile);
 hipError_t launch_sparse(const SparseArgs &a, hipStream_t s);
 hipError_t launch_checksum(const void *buf, int64_t count, int dt, uint64_t *hash,
                            hipStream_t s);

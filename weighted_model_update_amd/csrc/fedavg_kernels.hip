@@ -629,9 +629,10 @@ __global__ __launch_bounds__(256) void sparse_offsets_kernel(const SparseArgs a)
 // batch suffices).  The cursor advances by the count; a batch that lies
 // wholly inside the tile loads the next one.  After the last client the tile
 // is finalized and written once.
-template <int MW>
+template <int MW, int SP_TILE, int SP_THREADS>
 __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseArgs a)
 {
+    static_assert(SP_TILE == SP_THREADS * VEC, "one 8-parameter group per lane at finalize");
     constexpr int WAVES = SP_THREADS / 64;
     __shared__ __attribute__((aligned(16))) float s_acc[SP_TILE];
     __shared__ __attribute__((aligned(16))) uint32_t s_mask[MW][SP_TILE];
@@ -1108,16 +1109,33 @@ hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int m
     return hipErrorInvalidValue;
 }
 
-int sparse_resident_blocks_per_cu()
+template <int TILE, int THREADS> static int resident_blocks()
 {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, sparse_merge_kernel<1>, SP_THREADS, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, sparse_merge_kernel<1, TILE, THREADS>,
+                                                     THREADS, 0) != hipSuccess ||
         occ <= 0) {
         (void)hipGetLastError();
         occ = 1;
     }
     return occ;
+}
+
+int sparse_resident_blocks_per_cu(int tile)
+{
+    switch (tile) {
+    case 2048: return resident_blocks<2048, 256>();
+    case 8192: return resident_blocks<8192, 1024>();
+    default: return resident_blocks<4096, 512>();
+    }
+}
+
+template <int TILE, int THREADS> static void merge_launch(const SparseArgs &a, hipStream_t s)
+{
+    if (a.K <= 32)
+        sparse_merge_kernel<1, TILE, THREADS><<<a.NB, THREADS, 0, s>>>(a);
+    else
+        sparse_merge_kernel<2, TILE, THREADS><<<a.NB, THREADS, 0, s>>>(a);
 }
 
 hipError_t launch_sparse(const SparseArgs &a, hipStream_t s)
@@ -1127,10 +1145,11 @@ hipError_t launch_sparse(const SparseArgs &a, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    if (a.K <= 32)
-        sparse_merge_kernel<1><<<a.NB, SP_THREADS, 0, s>>>(a);
-    else
-        sparse_merge_kernel<2><<<a.NB, SP_THREADS, 0, s>>>(a);
+    switch (a.tile) {
+    case 2048: merge_launch<2048, 256>(a, s); break;
+    case 8192: merge_launch<8192, 1024>(a, s); break;
+    default: merge_launch<4096, 512>(a, s); break;
+    }
     return hipGetLastError();
 }
 
