@@ -270,7 +270,7 @@ typedef enum {
     FA_OPT_MASK_VECTORS_PER_BLOCK = 2, /* masked aggregate: 8-parameter vectors
                                           per workgroup (default 1024) */
     FA_OPT_SPARSE_BLOCKS = 3,          /* sparse merge: parameter ranges, i.e.
-                                          workgroups (default 0: 16384, fewer
+                                          workgroups (default 0: 65536, fewer
                                           when N is small; max 65536) */
     FA_OPT_RESIDENT_PER_CU = 4,        /* resident dense kernel: workgroups of
                                           256 threads resident per CU

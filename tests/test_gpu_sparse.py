@@ -19,6 +19,11 @@ pytestmark = pytest.mark.gpu
 def _restore_options():
     yield
     fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 0)
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, DEFAULT_TILE)
+
+
+DEFAULT_TILE = 2048
+TILES = [2048, 4096, 8192]
 
 
 def run_sparse(idx, val, n, N, base, mode="deltas", counts_dtype=torch.uint8, want_wsum=True,
@@ -44,10 +49,12 @@ def topk_case(N, K, frac, seed):
     return list(idx), list(val), n, base
 
 
-@pytest.mark.parametrize("blocks", [2048, 3, 4096])
-def test_topk_partial_sharing_matches_oracle(blocks):
-    # K=20 clients each sending its top-10% |delta|: several tiles per block
-    # (3 blocks), one tile per block (4096), and the default
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("blocks", [0, 3, 64])
+def test_topk_partial_sharing_matches_oracle(blocks, tile):
+    # K=20 clients each sending its top-10% |delta|: many tiles per block
+    # (3 blocks), a few (64), and the default (one or two per block)
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
     fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, blocks)
     N, K = 300_007, 20
     idx, val, n, base = topk_case(N, K, 0.1, synth.CFG_SPARSE_1B)
@@ -59,9 +66,10 @@ def test_topk_partial_sharing_matches_oracle(blocks):
     check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base, label=f"blocks={blocks}")
 
 
-def test_dense_support_overflows_batches():
-    # 60% density: about 2450 entries of each client per 4096-parameter tile,
-    # several 512-entry batches per client per tile
+@pytest.mark.parametrize("tile", TILES)
+def test_dense_support_overflows_batches(tile):
+    # 60% density: several batches of each client per tile
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
     N, K = 50_001, 6
     idx, val, n, base = topk_case(N, K, 0.6, 77)
     got, cnt, ws, err = run_sparse(idx, val, n, N, base, counts_dtype=torch.int32)
@@ -72,7 +80,9 @@ def test_dense_support_overflows_batches():
     check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base)
 
 
-def test_full_support_equals_dense_delta_aggregate():
+@pytest.mark.parametrize("tile", [2048, 4096])
+def test_full_support_equals_dense_delta_aggregate(tile):
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
     N, K = 20_000, 4
     r = np.random.default_rng(1)
     vals = [(r.standard_normal(N) * 1e-3).astype(np.float32) for _ in range(K)]
@@ -86,7 +96,9 @@ def test_full_support_equals_dense_delta_aggregate():
     assert np.array_equal(got.view(np.uint32), host_of(dense).view(np.uint32))
 
 
-def test_weights_mode_empty_and_zero_weight_clients_in_place():
+@pytest.mark.parametrize("tile", [2048, 8192])
+def test_weights_mode_empty_and_zero_weight_clients_in_place(tile):
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
     N = 70_000
     r = np.random.default_rng(2)
     base = (r.standard_normal(N) * 0.02).astype(np.float32)
@@ -101,8 +113,10 @@ def test_weights_mode_empty_and_zero_weight_clients_in_place():
     check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base)
 
 
-@pytest.mark.parametrize("bad", ["unsorted", "duplicate", "too_large", "negative"])
-def test_bad_index_lists_are_flagged(bad):
+@pytest.mark.parametrize("tile", [2048, 4096])
+@pytest.mark.parametrize("bad", ["unsorted", "duplicate", "too_large", "negative", "unsorted_far"])
+def test_bad_index_lists_are_flagged(bad, tile):
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
     N = 10_000
     base = np.zeros(N, np.float32)
     good = np.arange(0, N, 7, dtype=np.int64)
@@ -113,6 +127,8 @@ def test_bad_index_lists_are_flagged(bad):
         broken[200] = broken[199]
     elif bad == "too_large":
         broken[-1] = N + 5
+    elif bad == "unsorted_far":
+        broken[300] = 5    # far below its neighbours, inside another range
     else:
         broken[0] = -3
     val = np.ones(len(good), np.float32)
@@ -122,8 +138,10 @@ def test_bad_index_lists_are_flagged(bad):
     assert err == 0
 
 
-def test_tiny_and_ragged_sizes():
-    for N in (1, 7, 4095, 4097, 8193):
+@pytest.mark.parametrize("tile", TILES)
+def test_tiny_and_ragged_sizes(tile):
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
+    for N in (1, 7, 255, 257, 4095, 4097, 8193):
         r = np.random.default_rng(N)
         K = 3
         idx = [np.sort(r.choice(N, max(1, N // 3), replace=False)) for _ in range(K)]
@@ -149,3 +167,19 @@ def test_sparse_argument_errors():
     with pytest.raises(fa.FedAvgError) as e:
         fa.sparse_masked_accumulate([i], [v], [-1], N, b, b)
     assert e.value.code == -3
+
+
+@pytest.mark.parametrize("tile", [2048, 4096])
+@pytest.mark.parametrize("K", [1, 9, 17, 25, 33, 64])
+def test_client_counts_across_kernel_variants(K, tile):
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
+    # client counts below and above one group of batches, and the two-word
+    # client masks of K > 32
+    N = 40_000
+    idx, val, n, base = topk_case(N, K, 0.15, 100 + K)
+    got, cnt, ws, err = run_sparse(idx, val, n, N, base)
+    assert err == 0
+    ref, mag, rcnt, rws = oracle.sparse_average(idx, val, n, N, base=base)
+    assert np.array_equal(cnt, rcnt.astype(np.uint8))
+    assert np.array_equal(ws, rws.astype(np.uint32))
+    check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base, label=f"K={K}")

@@ -84,3 +84,41 @@ def test_streaming_null_handle_and_state():
     assert lib.fedavg_accumulate(None, 0, 1, None, 0, 0, 0, None, None) == -1
     assert lib.fedavg_finalize(None, None, 0, None, 0) == -1
     assert lib.fedavg_destroy(None) == 0
+
+
+def _no_gpu_here():
+    # these checks pass fake device pointers and rely on the first HIP launch
+    # failing; they must never run where a GPU could execute that launch
+    if os.path.exists("/dev/kfd"):
+        return False
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu_here(), reason="host-only check; needs a machine without a GPU")
+@pytest.mark.parametrize("tile", [2048, 4096, 8192])
+@pytest.mark.parametrize("blocks", [0, 1, 7, 65536])
+def test_sparse_workspace_covers_every_range_plan(tile, blocks):
+    """With exactly sparse_workspace_size bytes, the library's range plan
+    always fits: the call gets past argument and workspace checks and fails
+    only at its first HIP launch (no device here), never with
+    FA_ERR_WORKSPACE.  One byte less is refused before any launch."""
+    lib = _lib()
+    P = ctypes.c_void_p
+    assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile) == 0
+    assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, blocks) == 0
+    try:
+        for K in (1, 20, 33, 64):
+            for N in (1, 255, 256, 257, 4096, 300_007, 1_000_003, 10 ** 9):
+                need = fa.sparse_workspace_size(K, N)
+                fake = (P * K)(*([1 << 40] * K))
+                nnz = (ctypes.c_int64 * K)(*([1] * K))
+                n = (ctypes.c_int64 * K)(*([1] * K))
+                args = (K, fake, fake, nnz, n, N, 1, P(1 << 41), P(1 << 42), None, 0, None, P(1 << 43))
+                rc = lib.sparse_masked_accumulate(*args, need, None, None)
+                assert rc == -9, (K, N, rc, lib.fedavg_last_error())
+                rc = lib.sparse_masked_accumulate(*args, need - 1, None, None)
+                assert rc == -8, (K, N, rc)
+    finally:
+        lib.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, 2048)
+        lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 0)

@@ -62,7 +62,8 @@ int64_t g_mask_vpb = 1024;       // masked kernel: 8-parameter vectors per block
 int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: SPARSE_DEFAULT_BLOCKS)
 int64_t g_sparse_tile = fa::SP_DEFAULT_TILE;
 constexpr int64_t SPARSE_MAX_BLOCKS = 65536;
-constexpr int64_t SPARSE_DEFAULT_BLOCKS = 16384;
+constexpr int64_t SPARSE_DEFAULT_BLOCKS = 65536;
+constexpr int64_t SPARSE_MIN_TILE = 2048;
 constexpr size_t HEADER_BYTES = 256;
 
 int cu_count()
@@ -622,8 +623,9 @@ int sparse_workspace_size(int K, int64_t N, size_t *bytes)
     if (N < 0 || !bytes)
         return fail(FA_ERR_ARG, "need N >= 0 and a result pointer");
     // one list offset per client and range boundary; there are never more
-    // ranges than tiles of the smallest size
-    const int64_t max_ranges = std::min<int64_t>(SPARSE_MAX_BLOCKS, std::max<int64_t>(1, (N + 2047) / 2048));
+    // ranges than tiles of the smallest tile size
+    const int64_t max_ranges =
+        std::min<int64_t>(SPARSE_MAX_BLOCKS, std::max<int64_t>(1, (N + SPARSE_MIN_TILE - 1) / SPARSE_MIN_TILE));
     *bytes = HEADER_BYTES + (size_t)K * (size_t)(max_ranges + 1) * sizeof(int64_t);
     return ok();
 }
@@ -676,6 +678,16 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
     }
     if (S >= (1ull << 32))
         return fail(FA_ERR_RANGE, "sum of n_k must be below 2^32");
+    // plan the ranges and check the workspace before anything is enqueued:
+    // the offsets kernel writes Kc * (NB + 1) list positions
+    const int64_t tile = g_sparse_tile;
+    const int64_t NB = N > 0 ? sparse_blocks_for(N, tile) : 0;
+    const int64_t tiles = (N + tile - 1) / tile;
+    const int64_t R = NB > 0 ? ((tiles + NB - 1) / NB) * tile : tile;
+    const size_t used = HEADER_BYTES + (size_t)Kc * (size_t)(NB + 1) * sizeof(int64_t);
+    if (used > workspace_bytes)
+        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %lld ranges need %zu", workspace_bytes,
+                    (long long)NB, used);
     hipStream_t s = static_cast<hipStream_t>(stream);
     int *flag = err_flag ? err_flag : static_cast<int *>(workspace);
     hipError_t e = fa::launch_fill_u32(flag, 1, 0u, s);
@@ -683,10 +695,6 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
         return hip_fail(e, "flag reset");
     if (N == 0)
         return ok();
-    const int64_t tile = g_sparse_tile;
-    const int64_t NB = sparse_blocks_for(N, tile);
-    const int64_t tiles = (N + tile - 1) / tile;
-    const int64_t R = ((tiles + NB - 1) / NB) * tile;
     a.K = Kc;
     a.NB = (int)NB;
     a.N = N;
