@@ -76,17 +76,18 @@ def test_adapter_masks_match_oracle(vpb):
                                               ("f32", "bf16", "f32", "deltas"),
                                               ("bf16", "bf16", "f32", "weights")])
 @pytest.mark.parametrize("vpb", [8, 1024])
-def test_ragged_segments_match_oracle(xdt, bdt, odt, mode, vpb):
-    # segment sizes from 0 to ~3000, most not a multiple of 8, T > the LDS window
+@pytest.mark.parametrize("T,max_size", [(150, 3000), (1500, 300)])
+def test_ragged_segments_match_oracle(xdt, bdt, odt, mode, vpb, T, max_size):
+    # segment sizes from 0 to max_size, most not a multiple of 8; 150
+    # segments fit the whole-table LDS kernel, 1500 take the windowed one
     fa.fedavg_set_option(fa.FA_OPT_MASK_VECTORS_PER_BLOCK, vpb)
-    r = np.random.default_rng(11)
-    sizes = r.integers(0, 3000, size=150)
+    r = np.random.default_rng(11 + T)
+    sizes = r.integers(0, max_size, size=T)
     sizes[::17] = 0
     sizes[5] = 1
     bounds = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     N = int(bounds[-1])
     K = 5
-    T = len(sizes)
     present = (r.random((K, T)) < 0.5).astype(np.uint8)
     present[:, 3] = 0           # nobody sent segment 3
     present[:, 4] = 1           # everybody sent segment 4
@@ -100,6 +101,27 @@ def test_ragged_segments_match_oracle(xdt, bdt, odt, mode, vpb):
     got = run_masked(xs, n, bounds, present, base, xdt, bdt, odt, mode)
     ref, mag, cnt, _ = oracle_masked(xs, n, bounds, present, base, xdt, bdt, mode)
     check(got, ref, mag, odt, copied=cnt == 0, copy_expect=base_copy_expect(base, bdt, odt))
+
+
+@pytest.mark.parametrize("T", [511, 512, 513])
+def test_table_size_boundary(T):
+    """Tables of 512 segments are staged whole in LDS, 513 are windowed;
+    both sides of the switch agree with the oracle, with a zero-length last
+    segment and segments that end mid-vector."""
+    r = np.random.default_rng(100 + T)
+    sizes = r.integers(1, 200, size=T)
+    sizes[-1] = 0
+    sizes[T // 2] = 8 * 257 + 3
+    bounds = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N = int(bounds[-1])
+    K = 3
+    present = (r.random((K, T)) < 0.7).astype(np.uint8)
+    n = [4, 9, 2]
+    xs = [(r.standard_normal(N) * 0.05).astype(np.float32) for _ in range(K)]
+    base = (r.standard_normal(N) * 0.05).astype(np.float32)
+    got = run_masked(xs, n, bounds, present, base, "f32", "f32", "f32", "deltas")
+    ref, mag, cnt, _ = oracle_masked(xs, n, bounds, present, base, "f32", "f32", "deltas")
+    check(got, ref, mag, "f32", copied=cnt == 0, copy_expect=base, label=f"T={T}")
 
 
 def test_all_present_equals_dense_bit_for_bit():

@@ -15,6 +15,7 @@ enum { MODE_WEIGHTS = FA_WEIGHTS, MODE_DELTAS = FA_DELTAS };
 // Elements handled per thread per step on the vector paths: 8 bf16 are one
 // 16-byte load, 8 fp32 are two.
 constexpr int VEC = 8;
+constexpr int TAB_SEGS = 512; // segment tables up to this size are staged whole in LDS
 
 // ---------------------------------------------------------------- resident
 struct DenseArgs {

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void dense_scalar_kernel(const DenseArgs a, in
 
 // ================================================================ per-segment masks
 
-constexpr int SEG_WIN = 64; // segments staged in LDS at a time
+constexpr int SEG_WIN = 64; // segments staged in LDS at a time (windowed kernel)
 
 // Last segment index t in [0, T-1] with bounds[t] <= e (a thread alone).
 __device__ __forceinline__ int64_t thread_find_segment(const int64_t *bounds, int64_t T, int64_t e)
@@ -413,6 +413,150 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
         if (t_next >= a.T)
             t_next = a.T - 1;
         __syncthreads(); // LDS window is rewritten next
+    }
+}
+
+// Last segment index t in [lo, T-1] with s_lo[t] <= e, over a table staged
+// in LDS (lo <= T-1).
+__device__ __forceinline__ int lds_find_segment(const int64_t *s_lo, int lo, int T, int64_t e)
+{
+    int hi = T - 1;
+    while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (s_lo[mid] <= e)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// One parameter of the masked aggregate, its segment looked up in the LDS
+// table.
+template <int XDT, int ODT, int BDT, int MODE>
+__device__ __forceinline__ void masked_element_lds(const MaskedArgs &a, const int64_t *s_lo,
+                                                   const uint64_t *s_mask, const uint32_t *s_W,
+                                                   int64_t e)
+{
+    const int t = lds_find_segment(s_lo, 0, (int)a.T, e);
+    const uint64_t m = s_mask[t];
+    const uint32_t W = s_W[t];
+    float r;
+    if (W > 0) {
+        float acc = 0.0f;
+        for (int k = 0; k < a.K; ++k)
+            if ((m >> k) & 1)
+                acc = __builtin_fmaf(a.w[k], io<XDT>::load1(a.x[k], e), acc);
+        r = acc / (float)W;
+        if constexpr (MODE == MODE_DELTAS)
+            r = io<BDT>::load1(a.base, e) + r;
+    } else {
+        r = io<BDT>::load1(a.base, e);
+    }
+    io<ODT>::store1(a.out, e, r);
+}
+
+// Tables of at most TAB_SEGS segments (LoRA-style adapter sets: a few hundred
+// tensors) are staged whole in LDS by every workgroup, in one round of
+// independent loads -- bounds and client presence together -- instead of a
+// search followed by a windowed fetch.  Each thread then walks its vectors
+// (vpb per workgroup, blockDim apart) NV at a time with a segment cursor that
+// only moves forward, so a vector costs one LDS compare in the usual case.
+// The loads of all NV vectors are issued before the first FMA: absent
+// clients are skipped, which leaves a wave fewer bytes in flight than the
+// dense kernel has, and NV restores them.  Lanes whose vector straddles a
+// segment boundary or the buffer end go element by element.
+template <int XDT, int ODT, int BDT, int MODE, int NV>
+__global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
+{
+    __shared__ int64_t s_lo[TAB_SEGS + 1];
+    __shared__ uint64_t s_mask[TAB_SEGS];
+    __shared__ uint32_t s_W[TAB_SEGS];
+
+    const int tid = threadIdx.x;
+    const int T = (int)a.T;
+    for (int t = tid; t <= T; t += blockDim.x)
+        s_lo[t] = a.bounds[t];
+    for (int t = tid; t < T; t += blockDim.x)
+        segment_weights(a, t, s_mask[t], s_W[t]);
+    __syncthreads();
+
+    const int64_t nvec_all = (a.N + VEC - 1) / VEC;
+    const int64_t v_begin = (int64_t)blockIdx.x * a.vpb;
+    const int64_t v_end = min(v_begin + a.vpb, nvec_all);
+    const int64_t stride = blockDim.x;
+    int t = -1;
+    for (int64_t v = v_begin + tid; v < v_end; v += NV * stride) {
+        int64_t ev[NV];
+        bool has[NV], fast[NV];
+        uint64_t m[NV];
+        uint32_t W[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            ev[u] = (v + u * stride) * VEC;
+            has[u] = v + u * stride < v_end;
+            fast[u] = false;
+            m[u] = 0;
+            W[u] = 0;
+            if (has[u]) {
+                if (t < 0 || s_lo[t + 1] <= ev[u])
+                    t = lds_find_segment(s_lo, min(t + 1, T - 1), T, ev[u]);
+                fast[u] = s_lo[t] <= ev[u] && ev[u] + VEC <= s_lo[t + 1] && ev[u] + VEC <= a.N;
+                if (fast[u]) {
+                    m[u] = s_mask[t];
+                    W[u] = s_W[t];
+                }
+            }
+        }
+        float acc[NV][VEC];
+#pragma unroll
+        for (int u = 0; u < NV; ++u)
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                acc[u][j] = 0.0f;
+        for (int k0 = 0; k0 < a.K; k0 += 8) {
+            typename io<XDT>::raw xr[NV][8];
+#pragma unroll
+            for (int u = 0; u < NV; ++u)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (k0 + k < a.K && ((m[u] >> (k0 + k)) & 1))
+                        xr[u][k] = io<XDT>::load_raw(a.x[k0 + k], ev[u]);
+#pragma unroll
+            for (int u = 0; u < NV; ++u)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (k0 + k < a.K && ((m[u] >> (k0 + k)) & 1))
+                        io<XDT>::fma8(xr[u][k], a.w[k0 + k], acc[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            if (!has[u])
+                continue;
+            if (!fast[u]) {
+                for (int j = 0; j < VEC && ev[u] + j < a.N; ++j)
+                    masked_element_lds<XDT, ODT, BDT, MODE>(a, s_lo, s_mask, s_W, ev[u] + j);
+                continue;
+            }
+            float r[VEC];
+            if (W[u] > 0) {
+                const float Wf = (float)W[u];
+                if constexpr (MODE == MODE_DELTAS) {
+                    float b[VEC];
+                    io<BDT>::load8(a.base, ev[u], b);
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j)
+                        r[j] = b[j] + acc[u][j] / Wf;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j)
+                        r[j] = acc[u][j] / Wf;
+                }
+            } else {
+                io<BDT>::load8(a.base, ev[u], r);
+            }
+            io<ODT>::store8(a.out, ev[u], r);
+        }
     }
 }
 
@@ -1001,7 +1145,10 @@ template <int X, int O, int B, int M> struct MaskedRun {
         if (aligned) {
             const int64_t nvec_all = ceil_div(a.N, VEC);
             const unsigned g = grid_for(nvec_all, (int)a.vpb, 0);
-            masked_vec_kernel<X, O, B, M><<<g, 256, 0, s>>>(a);
+            if (a.T <= TAB_SEGS)
+                masked_table_kernel<X, O, B, M, 1><<<g, 256, 0, s>>>(a);
+            else
+                masked_vec_kernel<X, O, B, M><<<g, 256, 0, s>>>(a);
         } else {
             masked_scalar_kernel<X, O, B, M><<<grid_for(a.N, 256, 65536), 256, 0, s>>>(a);
         }
