@@ -276,7 +276,8 @@ typedef enum {
                                           256 threads resident per CU
                                           (default 3; 0 = hardware limit) */
     FA_OPT_SPARSE_TILE = 5             /* sparse merge: parameters per LDS tile,
-                                          2048 (default), 4096 or 8192 */
+                                          512, 1024, 2048 (default), 4096 or
+                                          8192 */
 } fa_option;
 
 /* Set one option; FA_ERR_ARG for an unknown option, FA_ERR_RANGE for a value

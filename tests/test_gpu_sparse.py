@@ -23,7 +23,7 @@ def _restore_options():
 
 
 DEFAULT_TILE = 2048
-TILES = [2048, 4096, 8192]
+TILES = [512, 1024, 2048, 4096, 8192]
 
 
 def run_sparse(idx, val, n, N, base, mode="deltas", counts_dtype=torch.uint8, want_wsum=True,
@@ -136,6 +136,37 @@ def test_bad_index_lists_are_flagged(bad, tile):
     assert err == -7
     _, _, _, err = run_sparse([good, good], [val, val], [1, 1], N, base)
     assert err == 0
+
+
+@pytest.mark.parametrize("tile", [512, 2048, 4096])
+@pytest.mark.parametrize("blocks", [0, 7])
+def test_order_violations_at_every_kind_of_edge(tile, blocks):
+    """Each entry is checked against its predecessor, which the merge finds in
+    different places: the lane below, the last lane of the wave before, the
+    last entry of the batch before (full support: every batch lies inside the
+    tile), or the entry before a range's first one.  A swapped or repeated
+    pair at each of those edges must be flagged; the intact list must not."""
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, blocks)
+    N = 50_000
+    tiles = -(-N // tile)
+    nb = min(tiles, blocks if blocks > 0 else 65536)
+    R = -(-tiles // nb) * tile                     # parameters per range
+    base = np.zeros(N, np.float32)
+    good = np.arange(N, dtype=np.int64)
+    val = np.ones(N, np.float32)
+    edges = {0, 62, 63, 64, 127, 255, 256, 511, 512, tile - 1, tile, R - 2, R - 1, R, 2 * R - 1}
+    for p in sorted(e for e in edges if 0 <= e < N - 1):
+        for kind in ("swap", "repeat"):
+            broken = good.copy()
+            if kind == "swap":
+                broken[p], broken[p + 1] = broken[p + 1], broken[p]
+            else:
+                broken[p + 1] = broken[p]
+            _, _, _, err = run_sparse([good, broken], [val, val], [1, 1], N, base)
+            assert err == -7, (kind, p)
+    _, cnt, _, err = run_sparse([good, good], [val, val], [1, 1], N, base)
+    assert err == 0 and (cnt == 2).all()
 
 
 @pytest.mark.parametrize("tile", TILES)

@@ -63,7 +63,7 @@ int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: SPARSE_DE
 int64_t g_sparse_tile = fa::SP_DEFAULT_TILE;
 constexpr int64_t SPARSE_MAX_BLOCKS = 65536;
 constexpr int64_t SPARSE_DEFAULT_BLOCKS = 65536;
-constexpr int64_t SPARSE_MIN_TILE = 2048;
+constexpr int64_t SPARSE_MIN_TILE = 512;
 constexpr size_t HEADER_BYTES = 256;
 
 int cu_count()
@@ -171,8 +171,8 @@ int fedavg_set_option(int option, int64_t value)
         g_resident_per_cu = value;
         return ok();
     case FA_OPT_SPARSE_TILE:
-        if (value != 2048 && value != 4096 && value != 8192)
-            return fail(FA_ERR_RANGE, "sparse tile must be 2048, 4096 or 8192");
+        if (value != 512 && value != 1024 && value != 2048 && value != 4096 && value != 8192)
+            return fail(FA_ERR_RANGE, "sparse tile must be 512, 1024, 2048, 4096 or 8192");
         g_sparse_tile = value;
         return ok();
     case FA_OPT_SPARSE_BLOCKS:

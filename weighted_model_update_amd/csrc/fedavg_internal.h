@@ -72,7 +72,7 @@ struct FinalizeArgs {
 
 // ---------------------------------------------------------------- sparse
 constexpr int SP_GROUP = 8;     // clients whose batches are loaded together
-constexpr int SP_DEFAULT_TILE = 2048; // parameters per LDS tile (2048, 4096 or 8192)
+constexpr int SP_DEFAULT_TILE = 2048; // parameters per LDS tile (512 ... 8192, powers of 2)
 
 struct SparseArgs {
     const int64_t *idx[FA_MAX_CLIENTS];
@@ -84,7 +84,7 @@ struct SparseArgs {
     int NB;    // blocks (parameter ranges)
     int64_t N;
     int64_t R; // parameters per block range, a multiple of the tile
-    int tile;  // parameters per LDS tile: 2048, 4096 or 8192
+    int tile;  // parameters per LDS tile: 512, 1024, 2048, 4096 or 8192
     int64_t *offs; // [K][NB+1] first list position at or after each range start
     const float *base;
     float *out;

@@ -765,16 +765,26 @@ __global__ __launch_bounds__(256) void sparse_offsets_kernel(const SparseArgs a)
 // sum and no float atomics are used (the mask bit is set with an LDS OR).
 //
 // A client's entries for the tile come as one coalesced batch of SP_THREADS
-// (index, value) pairs read from its cursor, together with each entry's
-// predecessor index for the sortedness check; the batches of SP_GROUP
-// clients are loaded together so their latencies overlap.  The in-tile
-// entries of a sorted batch are a prefix: each wave counts its own with a
-// ballot and the counts meet in LDS (double-buffered, so one barrier per
-// batch suffices).  The cursor advances by the count; a batch that lies
-// wholly inside the tile loads the next one.  After the last client the tile
-// is finalized and written once.
+// (index, value) pairs read from its cursor; the batches of SP_GROUP clients
+// are loaded together so their latencies overlap.  The in-tile entries of a
+// sorted batch are a prefix: each wave counts its own with a ballot and the
+// counts meet in LDS (double-buffered, so one barrier per batch suffices).
+// The cursor advances by the count; a batch that lies wholly inside the tile
+// loads the next one.  After the last client the tile is finalized and
+// written once.
+//
+// Sortedness: each entry is checked against its predecessor -- the lane
+// below it in the wave, the last lane of the wave before (exchanged in LDS
+// with the counts), the last entry of the batch before, or at the range
+// start the entry before the range, read once per workgroup -- and at the
+// range's end every cursor must have reached its end offset.
+//
+// Eight waves per SIMD for tiles of up to 512 lanes: the merge is bound by
+// how many batches are in flight, and the scalar registers would otherwise
+// cap residency at seven.
 template <int MW, int SP_TILE, int SP_THREADS>
-__global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseArgs a)
+__global__ __launch_bounds__(SP_THREADS, SP_THREADS <= 512 ? 2048 / SP_THREADS : 1) void
+sparse_merge_kernel(const SparseArgs a)
 {
     static_assert(SP_TILE == SP_THREADS * VEC, "one 8-parameter group per lane at finalize");
     constexpr int WAVES = SP_THREADS / 64;
@@ -783,7 +793,9 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
     __shared__ int64_t s_cur[FA_MAX_CLIENTS];
     __shared__ int64_t s_end[FA_MAX_CLIENTS];
     __shared__ uint32_t s_nk[FA_MAX_CLIENTS];
+    __shared__ int64_t s_prev0[FA_MAX_CLIENTS];
     __shared__ int s_count[2][WAVES];
+    __shared__ int64_t s_edge[2][WAVES];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -797,10 +809,14 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
     if (tid < a.K) {
         const int64_t c0 = a.offs[(int64_t)tid * (a.NB + 1) + b];
         int64_t c1 = a.offs[(int64_t)tid * (a.NB + 1) + b + 1];
+        if (c1 < c0)
+            bad = true; // offsets out of order: the list is not sorted
         c1 = max(c1, c0);
         s_cur[tid] = c0;
         s_end[tid] = min(c1, a.nnz[tid]);
         s_nk[tid] = a.wi[tid];
+        // the entry before the range's first one, for the sortedness check
+        s_prev0[tid] = c0 > 0 && c0 <= a.nnz[tid] ? a.idx[tid][c0 - 1] : -1;
     }
     for (int l = tid; l < SP_TILE; l += SP_THREADS) {
         s_acc[l] = 0.0f;
@@ -813,15 +829,13 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
     for (int64_t t0 = r0; t0 < r1; t0 += SP_TILE) {
         const int64_t t1 = min(t0 + SP_TILE, r1);
         for (int k0 = 0; k0 < a.K; k0 += SP_GROUP) {
-            // one batch per client of the group: this lane's entry, its
-            // value and the index of the entry before it (-1 before the
-            // first; INT64_MAX where the lane holds no entry)
-            int64_t gix[SP_GROUP], gprev[SP_GROUP];
+            // one batch per client of the group: this lane's entry and its
+            // value (INT64_MAX where the lane holds no entry)
+            int64_t gix[SP_GROUP];
             float gval[SP_GROUP];
 #pragma unroll
             for (int g = 0; g < SP_GROUP; ++g) {
                 gix[g] = INT64_MAX;
-                gprev[g] = INT64_MAX;
                 gval[g] = 0.0f;
                 const int k = k0 + g;
                 if (k < a.K) {
@@ -829,7 +843,6 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
                     if (p < s_end[k]) {
                         gix[g] = a.idx[k][p];
                         gval[g] = a.val[k][p];
-                        gprev[g] = p > 0 ? a.idx[k][p - 1] : -1;
                     }
                 }
             }
@@ -842,18 +855,30 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
                     const float w = a.w[k];
                     const uint32_t bit = 1u << (k & 31);
                     uint32_t *mrow = s_mask[MW > 1 ? (k >> 5) : 0];
-                    int64_t ix = gix[g], prev = gprev[g];
+                    int64_t ix = gix[g];
                     float val = gval[g];
+                    // index of the entry before this batch's first: before
+                    // the range, the previous range's last entry; in later
+                    // tiles the previous entry lies below t0, which the
+                    // ix >= t0 test covers; after a refill, the last entry
+                    // of the batch before
+                    int64_t first_prev = t0 == r0 ? s_prev0[k] : -1;
                     while (true) {
                         const bool in = ix < t1;
                         const uint64_t bal = __ballot(in);
+                        const int64_t up = __shfl_up(ix, 1, 64);
                         if (lane == 0)
                             s_count[parity][wave] = __popcll(bal);
+                        if (lane == 63)
+                            s_edge[parity][wave] = ix;
                         __syncthreads();
                         int c = 0;
 #pragma unroll
                         for (int v = 0; v < WAVES; ++v)
                             c += s_count[parity][v];
+                        const int64_t prev =
+                            lane > 0 ? up : (wave > 0 ? s_edge[parity][wave - 1] : first_prev);
+                        const int64_t batch_last = s_edge[parity][WAVES - 1];
                         parity ^= 1;
                         if (in) {
                             if (ix <= prev || ix < t0) {
@@ -868,13 +893,12 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
                         if (c < SP_THREADS || p0 >= pend)
                             break;
                         // a whole batch was inside the tile: fetch the next
+                        first_prev = batch_last;
                         const int64_t p = p0 + tid;
                         ix = INT64_MAX;
-                        prev = INT64_MAX;
                         if (p < pend) {
                             ix = a.idx[k][p];
                             val = a.val[k][p];
-                            prev = a.idx[k][p - 1];
                         }
                     }
                     if (tid == 0)
@@ -963,6 +987,12 @@ __global__ __launch_bounds__(SP_THREADS) void sparse_merge_kernel(const SparseAr
         }
         // the next tile's first barrier orders these zeroes before use
     }
+    // every entry between the range's offsets lies inside the range when the
+    // list is sorted, so each cursor has reached its end; entries left over
+    // mean the list is out of order (the tile loop's barriers order the last
+    // cursor update before this read)
+    if (tid < a.K && s_cur[tid] != s_end[tid])
+        bad = true;
     if (bad)
         *a.err = FA_ERR_INDEX;
 }
@@ -1271,6 +1301,8 @@ template <int TILE, int THREADS> static int resident_blocks()
 int sparse_resident_blocks_per_cu(int tile)
 {
     switch (tile) {
+    case 512: return resident_blocks<512, 64>();
+    case 1024: return resident_blocks<1024, 128>();
     case 2048: return resident_blocks<2048, 256>();
     case 8192: return resident_blocks<8192, 1024>();
     default: return resident_blocks<4096, 512>();
@@ -1293,6 +1325,8 @@ hipError_t launch_sparse(const SparseArgs &a, hipStream_t s)
     if (e != hipSuccess)
         return e;
     switch (a.tile) {
+    case 512: merge_launch<512, 64>(a, s); break;
+    case 1024: merge_launch<1024, 128>(a, s); break;
     case 2048: merge_launch<2048, 256>(a, s); break;
     case 8192: merge_launch<8192, 1024>(a, s); break;
     default: merge_launch<4096, 512>(a, s); break;
