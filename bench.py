@@ -243,6 +243,46 @@ def bench_streaming(clients=32, slots=3):
                                   "hbm_frac": k_bytes / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS}}
 
 
+def bench_hierarchical(silos=4):
+    """Two-level aggregation at the 8B streaming workload's size: the top-level
+    accumulator takes `silos` silo partials (fp32 sums over all N parameters,
+    already in HBM) as pseudo-clients; each merge reads the partial and
+    reads and writes the accumulator (12 B per parameter)."""
+    import torch
+    import synth
+    import weighted_model_update_amd as fa
+    N = synth.numel_of(synth.stream_8b_tensor_shapes())
+    log(f"hierarchical: {silos} silo partials of {N} fp32 sums")
+    acc_b, _, _, stag_b = fa.fedavg_workspace_size(N, 0, 1 << 20, 1)
+    acc = torch.empty(acc_b // 4, dtype=torch.float32, device="cuda")
+    staging = torch.empty(stag_b, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2026)
+    part = torch.empty(N, dtype=torch.float32, device="cuda")
+    part.normal_(0.0, 1.0, generator=g)
+    W = [int(w) for w in synth.sample_counts(synth.CFG_STREAM_8B, silos, 1000, 80000)]
+    h = fa.fedavg_begin(N, "deltas", False, acc, None, None, staging, 1 << 20, 1)
+    fa.fedavg_accumulate_partial(h, 0, W[0], 8, part, offset=0)       # warm-up merge
+    torch.cuda.synchronize()
+    fa.fedavg_destroy(h)
+    h = fa.fedavg_begin(N, "deltas", False, acc, None, None, staging, 1 << 20, 1)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for k in range(silos):
+        fa.fedavg_accumulate_partial(h, k, W[k], 8, part, offset=0)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / silos
+    fa.fedavg_destroy(h)
+    algo = 12 * N
+    del acc, staging, part
+    free_gpu()
+    return {"silos": silos, "N": N, "dtype": "fp32 partial sums", "ms_per_merge": ms,
+            "algo_bytes_per_merge": algo, "hbm_gbs": algo / (ms * 1e-3) / 1e9,
+            "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_sparse(steps=10, warmup=2):
     import torch
     import synth.device as sd
@@ -375,6 +415,9 @@ def main():
     if "streaming" in only:
         modes["streaming"] = bench_streaming(args.stream_clients)
         log(f"streaming: {modes['streaming']['wall_s']:.2f} s")
+    if "hierarchical" in only:
+        modes["hierarchical"] = bench_hierarchical()
+        log(f"hierarchical: {modes['hierarchical']['ms_per_merge']:.3f} ms per silo merge")
     if "copycal" in only:
         modes["copy_calibration"] = bench_copy_calibration()
     cpu = cpu_baseline() if "cpu" in only else None

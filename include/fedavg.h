@@ -196,6 +196,47 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
                       int64_t offset, int64_t len, const uint8_t *mask, const int64_t *indices);
 
 /*
+ * fedavg_accumulate_partial -- two-level (hierarchical) aggregation: add the
+ * unnormalised partial sums of a lower-level aggregation as one pseudo-client
+ * of h.  The regime this serves groups devices into fixed silos that
+ * aggregate inside and whose models are then aggregated at the federated
+ * round boundary (HFL-DDP: gist.science summary of the measurement-based
+ * adaptive data partitioning paper, section "Execution regimes").  Regrouping
+ * the sum makes this equal, in exact arithmetic, to aggregating all the
+ * silos' clients in one flat pass:
+ *     sum_s sum_{k in s} n_k x_k / sum_s W_s,   W_s = sum_{k in s} n_k.
+ *
+ * client_id  the pseudo-client's id in h (>= 0); it keeps one W and
+ *            n_clients, and follows a client's range rules (dense mode: its
+ *            calls arrive in ascending order and tile [0,N) exactly; partial
+ *            mode: ascending, non-overlapping ranges).
+ * W          the silo's total weight (fedavg_partial_info of the silo's
+ *            handle), in [0, 2^32); W == 0 returns FA_OK, no work.  It enters
+ *            the dense divisor S the way a client's n_k does.
+ * n_clients  clients behind the partial, in [1, 255]; in partial mode the
+ *            handle's clients, counted this way, stay at most 255.
+ * acc_src    float[len]: the silo's sums over parameters [offset, offset+len),
+ *            i.e. its accumulator after fedavg_sync and before (or after)
+ *            its finalize.
+ * wsum_src   uint32[len], required when h is in partial mode (the silo's
+ *            per-parameter weight sums); ignored otherwise.
+ * count_src  uint8[len], required when h has a count buffer; else ignored.
+ * Residence: all device, or all pinned host (staged like chunks; then 4*len
+ * must not exceed chunk_bytes).  Pageable host memory: FA_ERR_ARG.
+ * Arithmetic: acc_i = acc_i + acc_src_i, one IEEE fp32 addition (RNE); the
+ * weight sums and counts add exactly.  The silo's own order of FMAs is kept
+ * inside acc_src; partials enter in call order.
+ */
+int fedavg_accumulate_partial(fa_handle h, int client_id, int64_t W, int n_clients,
+                              const float *acc_src, const uint32_t *wsum_src,
+                              const uint8_t *count_src, int64_t offset, int64_t len);
+
+/* Total weight (sum of the clients' n_k and the partials' W) and number of
+   clients (a partial counts n_clients) accumulated so far in h.  Either
+   output pointer may be NULL. */
+int fedavg_partial_info(fa_handle h, int64_t *W, int *n_clients);
+
+/*
  * fedavg_finalize -- out_i = base_i + acc_i / W_i (FA_DELTAS) or acc_i / W_i
  * (FA_WEIGHTS), W_i = sum of n_k (dense) or wsum_i (partial); parameters with
  * W_i == 0 copy base_i.  base (device, N of base_dtype) is required in
@@ -205,6 +246,44 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
  */
 int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *out,
                     fa_dtype out_dtype);
+
+/*
+ * Spill and resume.  Server memory must not have to hold every client's
+ * update at once, and partial aggregation state may live on disk between
+ * uses (FLARE page, section "Offload Aggregation to Disk": incoming updates
+ * go to temporary files and are read back when needed).  Here the running
+ * aggregate is the whole state: the caller's acc (and wsum, count) buffers
+ * plus the handle's host-side record -- mode, N, and per client its id,
+ * weight, coverage and client count.
+ *
+ * fedavg_state_size   bytes fedavg_export_state writes for h now.
+ * fedavg_export_state waits for h's work (as fedavg_sync, returning
+ *                     FA_ERR_INDEX if a deferred index error was raised,
+ *                     without writing), then writes the host-side record to
+ *                     buf (host memory, at least fedavg_state_size bytes).  The
+ *                     caller then copies acc/wsum/count out (e.g. to disk) and
+ *                     may destroy h and free the device buffers.
+ * fedavg_resume       opens a handle like fedavg_begin, except that acc, wsum
+ *                     and count are NOT cleared: the caller has restored them
+ *                     bit for bit from the export, and the client record comes
+ *                     from state.  Accumulating on and finalizing then gives
+ *                     exactly the bits an uninterrupted run gives.  The state
+ *                     is checked (format, version, checksum, limits) before
+ *                     anything is created: FA_ERR_ARG when it fails.  count
+ *                     must be non-NULL exactly when the exported handle kept
+ *                     client counts.  chunk_bytes, n_slots and the streams may
+ *                     differ from the exporting handle's; N, mode and
+ *                     partial must equal the exported ones (they size the
+ *                     caller's buffers), else FA_ERR_ARG.
+ * The record is versioned, little-endian and ends with a 64-bit FNV-1a
+ * checksum of its bytes.
+ */
+int fedavg_state_size(fa_handle h, size_t *bytes);
+int fedavg_export_state(fa_handle h, void *buf, size_t bytes);
+int fedavg_resume(fa_handle *h, const void *state, size_t state_bytes, int64_t N, fa_mode mode,
+                  int partial, float *acc, uint32_t *wsum, uint8_t *count, void *staging,
+                  size_t staging_bytes, int64_t chunk_bytes, int n_slots, void *compute_stream,
+                  void *copy_stream);
 
 /* Wait for all work of the handle; returns a deferred device error
    (FA_ERR_INDEX) if one was raised, else FA_OK. */

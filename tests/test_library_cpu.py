@@ -83,6 +83,8 @@ def test_streaming_null_handle_and_state():
     lib = _lib()
     assert lib.fedavg_accumulate(None, 0, 1, None, 0, 0, 0, None, None) == -1
     assert lib.fedavg_finalize(None, None, 0, None, 0) == -1
+    assert lib.fedavg_accumulate_partial(None, 0, 1, 1, None, None, None, 0, 0) == -1
+    assert lib.fedavg_partial_info(None, None, None) == -1
     assert lib.fedavg_destroy(None) == 0
 
 
@@ -122,3 +124,68 @@ def test_sparse_workspace_covers_every_range_plan(tile, blocks):
     finally:
         lib.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, 2048)
         lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 0)
+
+
+# ---------------------------------------------------------------- spill/resume
+
+def _fnv1a64(b):
+    h = 0xcbf29ce484222325
+    for c in b:
+        h ^= c
+        h = (h * 0x100000001b3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def _state(N=1000, mode=0, partial=0, has_count=0, finalized=0, clients=((0, 1, 5, 1000),),
+           magic=0x54534146, version=1, corrupt=False):
+    """An exported-state record built from the layout include/fedavg.h
+    documents."""
+    import struct
+    body = struct.pack("<IIqiiiiII", magic, version, N, mode, partial, has_count, finalized,
+                       len(clients), 0)
+    for cid, members, w, covered in clients:
+        body += struct.pack("<iiqq", cid, members, w, covered)
+    h = _fnv1a64(body) ^ (1 if corrupt else 0)
+    return body + struct.pack("<Q", h)
+
+
+def _resume(state, N=1000, mode=0, partial=0, count=None, staging_bytes=1 << 30):
+    lib = _lib()
+    P = ctypes.c_void_p
+    h = P(0)
+    buf = ctypes.create_string_buffer(state, len(state))
+    return lib.fedavg_resume(ctypes.byref(h), buf, len(state), N, mode, partial, P(1 << 40),
+                             P(1 << 41) if partial else None, count, P(1 << 42), staging_bytes,
+                             4096, 2, None, None)
+
+
+def test_resume_rejects_bad_state_records():
+    P = ctypes.c_void_p
+    assert _resume(_state(magic=0x12345678)) == -1
+    assert _resume(_state(version=2)) == -1
+    assert _resume(_state(corrupt=True)) == -1
+    assert b"checksum" in _lib().fedavg_last_error()
+    assert _resume(_state()[:-1]) == -1                                   # truncated
+    assert _resume(_state(), N=999) == -1                                 # other N
+    assert _resume(_state(), mode=1) == -1                                # other mode
+    assert _resume(_state(partial=1, has_count=1), partial=1) == -1       # counts saved, none given
+    assert _resume(_state(partial=1), partial=1, count=P(1 << 43)) == -1  # no counts saved
+    assert _resume(_state(has_count=1)) == -1                             # counts without partial
+    assert _resume(_state(clients=((0, 1, 5, 1000), (0, 1, 7, 1000)))) == -1   # repeated id
+    assert _resume(_state(clients=((-1, 1, 5, 1000),))) == -1
+    assert _resume(_state(clients=((0, 0, 5, 1000),))) == -1             # no members
+    assert _resume(_state(clients=((0, 1, 5, 1001),))) == -1             # covered beyond N
+    assert _resume(_state(clients=((0, 1, 1 << 31, 1000), (1, 1, 1 << 31, 1000)))) == -1  # S >= 2^32
+    many = tuple((i, 1, 1, 0) for i in range(256))
+    assert _resume(_state(partial=1, clients=many), partial=1) == -1     # 256 clients behind counts
+    lib = _lib()
+    assert lib.fedavg_state_size(None, None) == -1
+    assert lib.fedavg_export_state(None, None, 0) == -1
+
+
+@pytest.mark.skipif(not _no_gpu_here(), reason="host-only check; needs a machine without a GPU")
+def test_resume_accepts_a_good_record_up_to_the_first_hip_call():
+    # validation passes; the first HIP call (stream creation) fails here
+    assert _resume(_state(clients=((3, 1, 5, 400), (9, 4, 70000, 1000)))) == -9
+    assert _resume(_state(partial=1, has_count=1, clients=((0, 255, 7, 10),)), partial=1,
+                   count=ctypes.c_void_p(1 << 43)) == -9

@@ -114,14 +114,52 @@ size_t slot_bytes(int64_t chunk_bytes, int partial)
     return b;
 }
 
+// ------------------------------------------------------------ spill / resume
+//
+// Exported state (host bytes, little-endian):
+//   u32 magic "FAST", u32 version, i64 N, i32 mode, i32 partial, i32 has_count,
+//   i32 finalized, u32 clients, u32 reserved, then per client
+//   {i32 id, i32 members, i64 weight, i64 covered}, then u64 FNV-1a of all the
+//   bytes before it.
+
+constexpr uint32_t STATE_MAGIC = 0x54534146u; // "FAST"
+constexpr uint32_t STATE_VERSION = 1;
+constexpr size_t STATE_HEAD = 4 + 4 + 8 + 4 * 4 + 4 + 4;
+constexpr size_t STATE_CLIENT = 4 + 4 + 8 + 8;
+
+uint64_t fnv1a64(const unsigned char *p, size_t n)
+{
+    uint64_t h = 0xcbf29ce484222325ull;
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= 0x100000001b3ull;
+    }
+    return h;
+}
+
+template <class T> void put(unsigned char *&p, T v)
+{
+    std::memcpy(p, &v, sizeof v);
+    p += sizeof v;
+}
+
+template <class T> T get(const unsigned char *&p)
+{
+    T v;
+    std::memcpy(&v, p, sizeof v);
+    p += sizeof v;
+    return v;
+}
+
 } // namespace
 
 // ============================================================ streaming state
 
 struct fa_stream_state {
     struct Client {
-        int64_t n;
+        int64_t n;       // weight: n_k, or a merged partial's W
         int64_t covered; // dense: next expected offset; partial: end of the last range
+        int members;     // clients behind it: 1, or a merged partial's client count
     };
     int device = 0;
     int64_t N = 0;
@@ -143,6 +181,83 @@ struct fa_stream_state {
     bool finalized = false;
     std::unordered_map<int, Client> clients;
     int *err_flag() { return reinterpret_cast<int *>(staging); }
+    uint64_t total_weight() const
+    {
+        uint64_t S = 0;
+        for (auto &c : clients)
+            S += (uint64_t)c.second.n;
+        return S;
+    }
+    int64_t total_members() const
+    {
+        int64_t m = 0;
+        for (auto &c : clients)
+            m += c.second.members;
+        return m;
+    }
+    // Admits a new client (or merged partial) of weight n standing for
+    // `members` clients; returns an error status, or FA_OK.
+    int admit(int64_t n, int members)
+    {
+        if (partial && total_members() + members > FA_MAX_STREAM_CLIENTS)
+            return fail(FA_ERR_RANGE, "more than %d clients in partial mode", FA_MAX_STREAM_CLIENTS);
+        if (total_weight() + (uint64_t)n >= (1ull << 32))
+            return fail(FA_ERR_RANGE, "sum of weights must be below 2^32");
+        return FA_OK;
+    }
+    // Checks a chunk's range against the client's coverage and advances it.
+    int cover(int client_id, Client &cl, int64_t offset, int64_t len)
+    {
+        if (!partial) {
+            if (offset != cl.covered)
+                return fail(FA_ERR_ARG,
+                            "dense mode: client %d chunk starts at %lld, expected %lld (chunks "
+                            "must arrive in order and tile [0,N))",
+                            client_id, (long long)offset, (long long)cl.covered);
+        } else if (offset < cl.covered) {
+            return fail(FA_ERR_ARG, "client %d ranges must be ascending and non-overlapping",
+                        client_id);
+        }
+        cl.covered = offset + len;
+        return FA_OK;
+    }
+    // Stages `parts` host arrays into the next slot (host buffers given as
+    // (src, bytes, offset in slot)); returns the slot, or -1 after a failure
+    // of a HIP call (recorded as FA_ERR_HIP).
+    int stage(const void *const *src, const size_t *bytes, const size_t *at, int parts)
+    {
+        const int sl = (int)(calls % n_slots);
+        hipError_t e = hipSuccess;
+        if (slot_used[sl]) {
+            // the host buffer of the copy that last used this slot is free once
+            // that copy is done; the slot itself once its kernel is done
+            e = hipEventSynchronize(copy_done[sl]);
+            if (e == hipSuccess)
+                e = hipStreamWaitEvent(copy, slot_free[sl], 0);
+        }
+        for (int i = 0; i < parts && e == hipSuccess; ++i)
+            if (src[i] && bytes[i])
+                e = hipMemcpyAsync(slot(sl) + at[i], src[i], bytes[i], hipMemcpyHostToDevice, copy);
+        if (e == hipSuccess)
+            e = hipEventRecord(copy_done[sl], copy);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(compute, copy_done[sl], 0);
+        if (e != hipSuccess) {
+            hip_fail(e, "staging copy");
+            return -1;
+        }
+        return sl;
+    }
+    // Marks a staged slot busy until the kernel just launched on it is done.
+    int release(int sl)
+    {
+        hipError_t e = hipEventRecord(slot_free[sl], compute);
+        if (e != hipSuccess)
+            return hip_fail(e, "event record");
+        slot_used[sl] = true;
+        ++calls;
+        return FA_OK;
+    }
     char *slot(int s) { return staging + HEADER_BYTES + (size_t)s * slot_size; }
 };
 
@@ -299,9 +414,11 @@ int fedavg_workspace_size(int64_t N, int partial, int64_t chunk_bytes, int n_slo
     return ok();
 }
 
-int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc, uint32_t *wsum,
-                 uint8_t *count, void *staging, size_t staging_bytes, int64_t chunk_bytes,
-                 int n_slots, void *compute_stream, void *copy_stream)
+// Checks begin/resume arguments and creates the handle with its events and
+// copy stream; device buffers are not touched.
+static int open_handle(fa_handle *h, int64_t N, int mode, int partial, float *acc, uint32_t *wsum,
+                       uint8_t *count, void *staging, size_t staging_bytes, int64_t chunk_bytes,
+                       int n_slots, void *compute_stream, void *copy_stream)
 {
     if (!h)
         return fail(FA_ERR_ARG, "handle pointer is NULL");
@@ -309,7 +426,7 @@ int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc,
     if (N < 0 || chunk_bytes <= 0 || n_slots < 1 || n_slots > 64)
         return fail(FA_ERR_ARG, "need N >= 0, chunk_bytes > 0, 1 <= n_slots <= 64");
     if (mode != FA_WEIGHTS && mode != FA_DELTAS)
-        return fail(FA_ERR_ARG, "unknown mode %d", (int)mode);
+        return fail(FA_ERR_ARG, "unknown mode %d", mode);
     if (partial != 0 && partial != 1)
         return fail(FA_ERR_ARG, "partial must be 0 or 1");
     if (!acc || !staging || (partial && !wsum))
@@ -354,19 +471,146 @@ int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc,
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&st->slot_free[i], hipEventDisableTiming);
     }
+    // the staging header holds the deferred error flag
     if (e == hipSuccess)
         e = fa::launch_fill_u32(st->staging, HEADER_BYTES / 4, 0u, st->compute);
-    if (e == hipSuccess)
-        e = fa::launch_fill_u32(acc, N, 0u, st->compute);
-    if (e == hipSuccess && partial)
-        e = fa::launch_fill_u32(wsum, N, 0u, st->compute);
-    if (e == hipSuccess && partial && count)
-        e = fa::launch_fill_u32(count, (N + 3) / 4, 0u, st->compute);
     if (e != hipSuccess) {
         fedavg_destroy(st);
-        return hip_fail(e, "begin");
+        return hip_fail(e, "handle set-up");
     }
     *h = st;
+    return FA_OK;
+}
+
+int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc, uint32_t *wsum,
+                 uint8_t *count, void *staging, size_t staging_bytes, int64_t chunk_bytes,
+                 int n_slots, void *compute_stream, void *copy_stream)
+{
+    int rc = open_handle(h, N, mode, partial, acc, wsum, count, staging, staging_bytes, chunk_bytes,
+                         n_slots, compute_stream, copy_stream);
+    if (rc != FA_OK)
+        return rc;
+    fa_stream_state *st = *h;
+    hipError_t e = fa::launch_fill_u32(acc, N, 0u, st->compute);
+    if (e == hipSuccess && st->partial)
+        e = fa::launch_fill_u32(st->wsum, N, 0u, st->compute);
+    if (e == hipSuccess && st->count)
+        e = fa::launch_fill_u32(st->count, (N + 3) / 4, 0u, st->compute);
+    if (e != hipSuccess) {
+        fedavg_destroy(st);
+        *h = nullptr;
+        return hip_fail(e, "begin");
+    }
+    return ok();
+}
+
+int fedavg_state_size(fa_handle h, size_t *bytes)
+{
+    if (!h || !bytes)
+        return fail(FA_ERR_ARG, "need a handle and a result pointer");
+    *bytes = STATE_HEAD + h->clients.size() * STATE_CLIENT + 8;
+    return ok();
+}
+
+int fedavg_export_state(fa_handle h, void *buf, size_t bytes)
+{
+    if (!h || !buf)
+        return fail(FA_ERR_ARG, "need a handle and a buffer");
+    fa_stream_state &st = *h;
+    const size_t need = STATE_HEAD + st.clients.size() * STATE_CLIENT + 8;
+    if (bytes < need)
+        return fail(FA_ERR_ARG, "state buffer has %zu bytes, needs %zu", bytes, need);
+    // the accumulator must be final before the caller copies it out
+    int rc = fedavg_sync(h);
+    if (rc != FA_OK)
+        return rc;
+    std::vector<std::pair<int, fa_stream_state::Client>> cl(st.clients.begin(), st.clients.end());
+    std::sort(cl.begin(), cl.end(), [](const auto &a, const auto &b) { return a.first < b.first; });
+    unsigned char *p = static_cast<unsigned char *>(buf);
+    unsigned char *p0 = p;
+    put<uint32_t>(p, STATE_MAGIC);
+    put<uint32_t>(p, STATE_VERSION);
+    put<int64_t>(p, st.N);
+    put<int32_t>(p, st.mode);
+    put<int32_t>(p, st.partial);
+    put<int32_t>(p, st.count ? 1 : 0);
+    put<int32_t>(p, st.finalized ? 1 : 0);
+    put<uint32_t>(p, (uint32_t)cl.size());
+    put<uint32_t>(p, 0u);
+    for (auto &c : cl) {
+        put<int32_t>(p, c.first);
+        put<int32_t>(p, c.second.members);
+        put<int64_t>(p, c.second.n);
+        put<int64_t>(p, c.second.covered);
+    }
+    put<uint64_t>(p, fnv1a64(p0, (size_t)(p - p0)));
+    return ok();
+}
+
+int fedavg_resume(fa_handle *h, const void *state, size_t state_bytes, int64_t N_expect,
+                  fa_mode mode_expect, int partial_expect, float *acc, uint32_t *wsum,
+                  uint8_t *count, void *staging, size_t staging_bytes, int64_t chunk_bytes,
+                  int n_slots, void *compute_stream, void *copy_stream)
+{
+    if (h)
+        *h = nullptr;
+    if (!state || state_bytes < STATE_HEAD + 8)
+        return fail(FA_ERR_ARG, "state is missing or too short");
+    const unsigned char *p = static_cast<const unsigned char *>(state);
+    const unsigned char *p0 = p;
+    if (get<uint32_t>(p) != STATE_MAGIC)
+        return fail(FA_ERR_ARG, "not an exported accumulator state");
+    if (get<uint32_t>(p) != STATE_VERSION)
+        return fail(FA_ERR_ARG, "unsupported state version");
+    const int64_t N = get<int64_t>(p);
+    const int32_t mode = get<int32_t>(p);
+    const int32_t partial = get<int32_t>(p);
+    const int32_t has_count = get<int32_t>(p);
+    const int32_t finalized = get<int32_t>(p);
+    const uint32_t nc = get<uint32_t>(p);
+    (void)get<uint32_t>(p);
+    if (nc > (1u << 20) || state_bytes != STATE_HEAD + (size_t)nc * STATE_CLIENT + 8)
+        return fail(FA_ERR_ARG, "state size does not match its client count");
+    {
+        const unsigned char *q = p0 + STATE_HEAD + (size_t)nc * STATE_CLIENT;
+        if (get<uint64_t>(q) != fnv1a64(p0, STATE_HEAD + (size_t)nc * STATE_CLIENT))
+            return fail(FA_ERR_ARG, "state checksum mismatch");
+    }
+    if (N < 0 || (partial != 0 && partial != 1) || (has_count != 0 && has_count != 1) ||
+        (finalized != 0 && finalized != 1) || (!partial && has_count))
+        return fail(FA_ERR_ARG, "state header is inconsistent");
+    if (N != N_expect || mode != (int32_t)mode_expect || partial != partial_expect)
+        return fail(FA_ERR_ARG, "state is for N=%lld mode=%d partial=%d, not N=%lld mode=%d partial=%d",
+                    (long long)N, mode, partial, (long long)N_expect, (int)mode_expect,
+                    partial_expect);
+    if ((bool)has_count != (partial && count != nullptr))
+        return fail(FA_ERR_ARG, "the state %s client counts; pass a count buffer %s",
+                    has_count ? "has" : "has no", has_count ? "(restored)" : "of NULL");
+    std::unordered_map<int, fa_stream_state::Client> clients;
+    uint64_t S = 0;
+    int64_t members = 0;
+    for (uint32_t i = 0; i < nc; ++i) {
+        const int32_t id = get<int32_t>(p);
+        fa_stream_state::Client c;
+        c.members = get<int32_t>(p);
+        c.n = get<int64_t>(p);
+        c.covered = get<int64_t>(p);
+        if (id < 0 || clients.count(id) || c.members < 1 || c.n <= 0 || c.n >= (1ll << 32) ||
+            c.covered < 0 || c.covered > N)
+            return fail(FA_ERR_ARG, "state client record %u is invalid", i);
+        S += (uint64_t)c.n;
+        members += c.members;
+        clients[id] = c;
+    }
+    if (S >= (1ull << 32) || (partial && members > FA_MAX_STREAM_CLIENTS))
+        return fail(FA_ERR_ARG, "state totals exceed the handle limits");
+
+    int rc = open_handle(h, N, mode, partial, acc, wsum, count, staging, staging_bytes, chunk_bytes,
+                         n_slots, compute_stream, copy_stream);
+    if (rc != FA_OK)
+        return rc;
+    (*h)->clients = std::move(clients);
+    (*h)->finalized = finalized != 0;
     return ok();
 }
 
@@ -399,32 +643,21 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
         return fail(FA_ERR_ARG, "chunk is NULL");
 
     auto it = st.clients.find(client_id);
-    if (it != st.clients.end() && it->second.n != n_k)
+    if (it != st.clients.end() && (it->second.n != n_k || it->second.members != 1))
         return fail(FA_ERR_ARG, "client %d changed its n_k", client_id);
     if (n_k == 0)
         return ok();
     if (it == st.clients.end()) {
-        if (st.partial && st.clients.size() >= FA_MAX_STREAM_CLIENTS)
-            return fail(FA_ERR_RANGE, "more than %d clients in partial mode", FA_MAX_STREAM_CLIENTS);
-        uint64_t S = (uint64_t)n_k;
-        for (auto &c : st.clients)
-            S += (uint64_t)c.second.n;
-        if (S >= (1ull << 32))
-            return fail(FA_ERR_RANGE, "sum of n_k must be below 2^32");
+        const int rc = st.admit(n_k, 1);
+        if (rc != FA_OK)
+            return rc;
     }
-    fa_stream_state::Client cl = it != st.clients.end() ? it->second : fa_stream_state::Client{n_k, 0};
-    if (!st.partial) {
-        if (offset != cl.covered)
-            return fail(FA_ERR_ARG,
-                        "dense mode: client %d chunk starts at %lld, expected %lld (chunks must "
-                        "arrive in order and tile [0,N))",
-                        client_id, (long long)offset, (long long)cl.covered);
-        cl.covered = offset + len;
-    } else if (!indices) {
-        if (offset < cl.covered)
-            return fail(FA_ERR_ARG, "client %d ranges must be ascending and non-overlapping",
-                        client_id);
-        cl.covered = offset + len;
+    fa_stream_state::Client cl =
+        it != st.clients.end() ? it->second : fa_stream_state::Client{n_k, 0, 1};
+    if (!indices) {
+        const int rc = st.cover(client_id, cl, offset, len);
+        if (rc != FA_OK)
+            return rc;
     }
     if (len == 0) {
         st.clients[client_id] = cl;
@@ -459,28 +692,15 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
         if (vbytes > (size_t)st.chunk_bytes)
             return fail(FA_ERR_RANGE, "chunk of %zu bytes exceeds chunk_bytes=%lld", vbytes,
                         (long long)st.chunk_bytes);
-        slot = (int)(st.calls % st.n_slots);
+        const size_t aux_at = round_up((size_t)st.chunk_bytes, 256);
+        const void *src[2] = {chunk, mask ? (const void *)mask : (const void *)indices};
+        const size_t bytes[2] = {vbytes, mask ? (size_t)len : (indices ? (size_t)len * 8 : 0)};
+        const size_t at[2] = {0, aux_at};
+        slot = st.stage(src, bytes, at, 2);
+        if (slot < 0)
+            return FA_ERR_HIP; // message recorded by stage()
         char *dst = st.slot(slot);
-        char *aux = dst + round_up((size_t)st.chunk_bytes, 256);
-        if (st.slot_used[slot]) {
-            // the host buffer of the copy that last used this slot is free once
-            // that copy is done; the slot itself once its kernel is done
-            e = hipEventSynchronize(st.copy_done[slot]);
-            if (e == hipSuccess)
-                e = hipStreamWaitEvent(st.copy, st.slot_free[slot], 0);
-        }
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(dst, chunk, vbytes, hipMemcpyHostToDevice, st.copy);
-        if (e == hipSuccess && mask)
-            e = hipMemcpyAsync(aux, mask, (size_t)len, hipMemcpyHostToDevice, st.copy);
-        if (e == hipSuccess && indices)
-            e = hipMemcpyAsync(aux, indices, (size_t)len * 8, hipMemcpyHostToDevice, st.copy);
-        if (e == hipSuccess)
-            e = hipEventRecord(st.copy_done[slot], st.copy);
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(st.compute, st.copy_done[slot], 0);
-        if (e != hipSuccess)
-            return hip_fail(e, "staging copy");
+        char *aux = dst + aux_at;
         a.chunk = dst;
         a.mask = mask ? reinterpret_cast<const uint8_t *>(aux) : nullptr;
         a.idx = indices ? reinterpret_cast<const int64_t *>(aux) : nullptr;
@@ -501,13 +721,128 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
     if (e != hipSuccess)
         return hip_fail(e, "accumulate launch");
     if (slot >= 0) {
-        e = hipEventRecord(st.slot_free[slot], st.compute);
-        if (e != hipSuccess)
-            return hip_fail(e, "event record");
-        st.slot_used[slot] = true;
-        ++st.calls;
+        const int rc = st.release(slot);
+        if (rc != FA_OK)
+            return rc;
     }
     st.clients[client_id] = cl;
+    return ok();
+}
+
+int fedavg_accumulate_partial(fa_handle h, int client_id, int64_t W, int n_clients,
+                              const float *acc_src, const uint32_t *wsum_src,
+                              const uint8_t *count_src, int64_t offset, int64_t len)
+{
+    if (!h)
+        return fail(FA_ERR_ARG, "NULL handle");
+    fa_stream_state &st = *h;
+    if (st.finalized)
+        return fail(FA_ERR_STATE, "accumulate after finalize");
+    if (client_id < 0)
+        return fail(FA_ERR_ARG, "client_id must be >= 0");
+    if (W < 0 || W >= (1ll << 32))
+        return fail(FA_ERR_RANGE, "W=%lld outside [0, 2^32)", (long long)W);
+    if (n_clients < 1 || n_clients > FA_MAX_STREAM_CLIENTS)
+        return fail(FA_ERR_RANGE, "n_clients=%d outside [1, %d]", n_clients, FA_MAX_STREAM_CLIENTS);
+    if (len < 0 || offset < 0 || offset + len > st.N)
+        return fail(FA_ERR_RANGE, "range [%lld, %lld) outside [0, N=%lld)", (long long)offset,
+                    (long long)(offset + len), (long long)st.N);
+    if (len > 0 && !acc_src)
+        return fail(FA_ERR_ARG, "acc_src is NULL");
+    if (st.partial && len > 0 && !wsum_src)
+        return fail(FA_ERR_ARG, "a partial-mode handle needs wsum_src");
+    if (st.partial && st.count && len > 0 && !count_src)
+        return fail(FA_ERR_ARG, "a handle with client counts needs count_src");
+
+    auto it = st.clients.find(client_id);
+    if (it != st.clients.end() && (it->second.n != W || it->second.members != n_clients))
+        return fail(FA_ERR_ARG, "client %d changed its weight or client count", client_id);
+    if (W == 0)
+        return ok();
+    if (it == st.clients.end()) {
+        const int rc = st.admit(W, n_clients);
+        if (rc != FA_OK)
+            return rc;
+    }
+    fa_stream_state::Client cl =
+        it != st.clients.end() ? it->second : fa_stream_state::Client{W, 0, n_clients};
+    {
+        const int rc = st.cover(client_id, cl, offset, len);
+        if (rc != FA_OK)
+            return rc;
+    }
+    if (len == 0) {
+        st.clients[client_id] = cl;
+        return ok();
+    }
+
+    const bool use_wsum = st.partial;
+    const bool use_count = st.partial && st.count;
+    const Residence res = residence_of(acc_src);
+    if (res == Residence::Pageable)
+        return fail(FA_ERR_ARG, "acc_src must be pinned host memory or device memory");
+    if ((use_wsum && residence_of(wsum_src) != res) || (use_count && residence_of(count_src) != res))
+        return fail(FA_ERR_ARG, "wsum_src and count_src must live where acc_src lives");
+
+    fa::StreamArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.acc = st.acc;
+    a.wsum = st.wsum;
+    a.count = st.count;
+    a.offset = offset;
+    a.len = len;
+    a.N = st.N;
+    a.err = st.err_flag();
+    int slot = -1;
+    if (res == Residence::PinnedHost) {
+        // sums in the slot's value area, weight sums and counts in its aux area
+        const size_t vbytes = (size_t)len * 4;
+        if (vbytes > (size_t)st.chunk_bytes)
+            return fail(FA_ERR_RANGE, "%zu bytes of partial sums exceed chunk_bytes=%lld", vbytes,
+                        (long long)st.chunk_bytes);
+        const size_t aux_at = round_up((size_t)st.chunk_bytes, 256);
+        const size_t cnt_at = aux_at + round_up(vbytes, 256);
+        const size_t end = use_count ? cnt_at + (size_t)len : (use_wsum ? aux_at + vbytes : vbytes);
+        if (end > st.slot_size)
+            return fail(FA_ERR_RANGE, "a partial of %lld parameters does not fit a staging slot of "
+                        "%zu bytes", (long long)len, st.slot_size);
+        const void *src[3] = {acc_src, use_wsum ? wsum_src : nullptr, use_count ? count_src : nullptr};
+        const size_t bytes[3] = {vbytes, use_wsum ? vbytes : 0, use_count ? (size_t)len : 0};
+        const size_t at[3] = {0, aux_at, cnt_at};
+        slot = st.stage(src, bytes, at, 3);
+        if (slot < 0)
+            return FA_ERR_HIP; // message recorded by stage()
+        a.chunk = st.slot(slot);
+        a.src_wsum = reinterpret_cast<const uint32_t *>(st.slot(slot) + aux_at);
+        a.src_count = reinterpret_cast<const uint8_t *>(st.slot(slot) + cnt_at);
+    } else {
+        a.chunk = acc_src;
+        a.src_wsum = wsum_src;
+        a.src_count = count_src;
+    }
+    const bool aligned = (offset % fa::VEC) == 0 && aligned16(a.chunk) &&
+                         (!use_wsum || aligned16(a.src_wsum)) &&
+                         (!use_count || (reinterpret_cast<uintptr_t>(a.src_count) & 7u) == 0);
+    hipError_t e = fa::launch_stream_merge(a, use_wsum, aligned, grid_cap(), st.compute);
+    if (e != hipSuccess)
+        return hip_fail(e, "merge launch");
+    if (slot >= 0) {
+        const int rc = st.release(slot);
+        if (rc != FA_OK)
+            return rc;
+    }
+    st.clients[client_id] = cl;
+    return ok();
+}
+
+int fedavg_partial_info(fa_handle h, int64_t *W, int *n_clients)
+{
+    if (!h)
+        return fail(FA_ERR_ARG, "NULL handle");
+    if (W)
+        *W = (int64_t)h->total_weight();
+    if (n_clients)
+        *n_clients = (int)h->total_members();
     return ok();
 }
 
@@ -526,13 +861,12 @@ int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *ou
     if (base && !overlap_ok(out, (size_t)st.N * dsize(out_dtype), base,
                             (size_t)st.N * dsize(base_dtype)))
         return fail(FA_ERR_ARG, "out partially overlaps base");
-    uint64_t S = 0;
     for (auto &c : st.clients) {
         if (!st.partial && c.second.covered != st.N)
             return fail(FA_ERR_INCOMPLETE, "client %d covered [0, %lld) of [0, %lld)", c.first,
                         (long long)c.second.covered, (long long)st.N);
-        S += (uint64_t)c.second.n;
     }
+    const uint64_t S = st.total_weight();
     st.finalized = true;
     if (st.N == 0)
         return ok();

@@ -59,6 +59,10 @@ struct StreamArgs {
     float w;
     uint32_t wi;
     int *err;
+    // merging another accumulator's partial sums: its per-parameter weight
+    // sums and client counts (chunk then holds its fp32 sums)
+    const uint32_t *src_wsum;
+    const uint8_t *src_count;
 };
 
 struct FinalizeArgs {
@@ -107,6 +111,8 @@ hipError_t launch_masked(const MaskedArgs &a, int xdt, int odt, int bdt, int mod
 hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool aligned,
                                     int64_t grid_cap, int resident, hipStream_t s);
 hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStream_t s);
+hipError_t launch_stream_merge(const StreamArgs &a, bool partial, bool aligned, int64_t cap,
+                               hipStream_t s);
 hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int mode, int partial,
                                   bool aligned, int64_t grid_cap, int resident, hipStream_t s);
 int sparse_resident_blocks_per_cu(int tile);

@@ -675,6 +675,67 @@ __global__ __launch_bounds__(256) void stream_acc_index_kernel(const StreamArgs 
     }
 }
 
+// Two-level aggregation: a lower-level accumulator's unnormalised partial
+// sums enter this one as a single pseudo-client, acc += src (one fp32
+// addition per parameter), and in partial mode its weight sums and client
+// counts add to these.  The counts add as packed bytes: the handle keeps the
+// total number of clients at most 255, so no byte carries into the next.
+template <int PARTIAL>
+__global__ __launch_bounds__(256) void stream_merge_vec_kernel(const StreamArgs a, int64_t nvec)
+{
+    const float *src = static_cast<const float *>(a.chunk);
+    for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
+        const int64_t e = v * VEC;
+        const int64_t g = a.offset + e;
+        const f32x4 *sp = reinterpret_cast<const f32x4 *>(src + e);
+        f32x4 *ap = reinterpret_cast<f32x4 *>(a.acc + g);
+        const f32x4 s0 = __builtin_nontemporal_load(sp);
+        const f32x4 s1 = __builtin_nontemporal_load(sp + 1);
+        f32x4 lo = __builtin_nontemporal_load(ap);
+        f32x4 hi = __builtin_nontemporal_load(ap + 1);
+        lo = f32x4{lo.x + s0.x, lo.y + s0.y, lo.z + s0.z, lo.w + s0.w};
+        hi = f32x4{hi.x + s1.x, hi.y + s1.y, hi.z + s1.z, hi.w + s1.w};
+        __builtin_nontemporal_store(lo, ap);
+        __builtin_nontemporal_store(hi, ap + 1);
+        if constexpr (PARTIAL) {
+            const u32x4 *ws = reinterpret_cast<const u32x4 *>(a.src_wsum + e);
+            u32x4 *wp = reinterpret_cast<u32x4 *>(a.wsum + g);
+            const u32x4 a0 = __builtin_nontemporal_load(ws);
+            const u32x4 a1 = __builtin_nontemporal_load(ws + 1);
+            u32x4 w0 = wp[0], w1 = wp[1];
+            w0 = u32x4{w0.x + a0.x, w0.y + a0.y, w0.z + a0.z, w0.w + a0.w};
+            w1 = u32x4{w1.x + a1.x, w1.y + a1.y, w1.z + a1.z, w1.w + a1.w};
+            wp[0] = w0;
+            wp[1] = w1;
+            if (a.count) {
+                const u32x2 cs = *reinterpret_cast<const u32x2 *>(a.src_count + e);
+                u32x2 *cp = reinterpret_cast<u32x2 *>(a.count + g);
+                u32x2 c = *cp;
+                c.x += cs.x;
+                c.y += cs.y;
+                *cp = c;
+            }
+        }
+    }
+}
+
+template <int PARTIAL>
+__global__ __launch_bounds__(256) void stream_merge_scalar_kernel(const StreamArgs a, int64_t first,
+                                                                  int64_t count)
+{
+    const float *src = static_cast<const float *>(a.chunk);
+    for (int64_t t = global_tid(); t < count; t += grid_threads()) {
+        const int64_t e = first + t;
+        const int64_t g = a.offset + e;
+        a.acc[g] = a.acc[g] + src[e];
+        if constexpr (PARTIAL) {
+            a.wsum[g] += a.src_wsum[e];
+            if (a.count)
+                a.count[g] = (uint8_t)(a.count[g] + a.src_count[e]);
+        }
+    }
+}
+
 template <int BDT, int ODT, int MODE, int PARTIAL>
 __device__ __forceinline__ float finalize_one(float acc, uint32_t W, float S, float b)
 {
@@ -1243,6 +1304,31 @@ hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStre
     else
         stream_acc_index_kernel<DT_BF16><<<g, 256, 0, s>>>(a);
     return hipGetLastError();
+}
+
+template <int PARTIAL>
+static hipError_t merge_t(const StreamArgs &a, bool aligned, int64_t cap, hipStream_t s)
+{
+    const int64_t nvec = aligned ? a.len / VEC : 0;
+    if (nvec > 0) {
+        stream_merge_vec_kernel<PARTIAL><<<grid_for(nvec, 256, cap), 256, 0, s>>>(a, nvec);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t first = nvec * VEC;
+    const int64_t rest = a.len - first;
+    if (rest > 0) {
+        stream_merge_scalar_kernel<PARTIAL><<<grid_for(rest, 256, cap), 256, 0, s>>>(a, first, rest);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_stream_merge(const StreamArgs &a, bool partial, bool aligned, int64_t cap,
+                               hipStream_t s)
+{
+    return partial ? merge_t<1>(a, aligned, cap, s) : merge_t<0>(a, aligned, cap, s);
 }
 
 template <int B, int O, int M, int P>

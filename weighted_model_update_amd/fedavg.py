@@ -31,7 +31,8 @@ STATUS_NAMES = {
 EXPORTS = [
     "fedavg_abi_version", "fedavg_last_error", "fedavg_aggregate", "fedavg_workspace_size",
     "fedavg_begin", "fedavg_accumulate", "fedavg_finalize", "fedavg_sync", "fedavg_destroy",
-    "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
+    "fedavg_accumulate_partial", "fedavg_partial_info", "fedavg_state_size", "fedavg_export_state",
+    "fedavg_resume", "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
 ]
 
 
@@ -67,6 +68,11 @@ def load(build_if_missing=True):
         "fedavg_workspace_size": ([i64, i32, i64, i32, P, P, P, P], i32),
         "fedavg_begin": ([P, i64, i32, i32, P, P, P, P, sz, i64, i32, P, P], i32),
         "fedavg_accumulate": ([P, i32, i64, P, i32, i64, i64, P, P], i32),
+        "fedavg_accumulate_partial": ([P, i32, i64, i32, P, P, P, i64, i64], i32),
+        "fedavg_partial_info": ([P, P, P], i32),
+        "fedavg_state_size": ([P, P], i32),
+        "fedavg_export_state": ([P, P, sz], i32),
+        "fedavg_resume": ([P, P, sz, i64, i32, i32, P, P, P, P, sz, i64, i32, P, P], i32),
         "fedavg_finalize": ([P, P, i32, P, i32], i32),
         "fedavg_sync": ([P], i32),
         "fedavg_destroy": ([P], i32),
@@ -222,6 +228,59 @@ def fedavg_accumulate(h, client_id, n_k, chunk, offset=0, mask=None, indices=Non
     _check(rc)
 
 
+def fedavg_accumulate_partial(h, client_id, W, n_clients, acc_src, wsum_src=None, count_src=None,
+                              offset=0):
+    """Add a lower-level aggregation's partial sums (fp32 acc_src over
+    [offset, offset+len), with its uint32 weight sums and uint8 counts in
+    partial mode) as one pseudo-client of weight W standing for n_clients
+    clients."""
+    _contig(acc_src, "acc_src")
+    _contig(wsum_src, "wsum_src")
+    _contig(count_src, "count_src")
+    if acc_src.dtype != torch.float32:
+        raise TypeError("acc_src must be float32")
+    n = acc_src.numel()
+    if wsum_src is not None and (wsum_src.numel() != n or wsum_src.element_size() != 4):
+        raise ValueError("wsum_src must hold one 32-bit weight sum per element of acc_src")
+    if count_src is not None and (count_src.numel() != n or count_src.dtype != torch.uint8):
+        raise ValueError("count_src must hold one uint8 count per element of acc_src")
+    rc = load().fedavg_accumulate_partial(h, int(client_id), int(W), int(n_clients), _ptr(acc_src),
+                                          _ptr(wsum_src), _ptr(count_src), int(offset), n)
+    _check(rc)
+
+
+def fedavg_partial_info(h):
+    """(total weight, number of clients) accumulated so far in h."""
+    W = ctypes.c_int64(0)
+    m = ctypes.c_int(0)
+    _check(load().fedavg_partial_info(h, ctypes.byref(W), ctypes.byref(m)))
+    return W.value, m.value
+
+
+def fedavg_export_state(h):
+    """The handle's host-side record as bytes (waits for its work first)."""
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.fedavg_state_size(h, ctypes.byref(n)))
+    buf = ctypes.create_string_buffer(n.value)
+    _check(lib.fedavg_export_state(h, buf, n.value))
+    return buf.raw
+
+
+def fedavg_resume(state, N, mode, partial, acc, wsum, count, staging, chunk_bytes, n_slots,
+                  compute_stream=None, copy_stream=None):
+    """Open a handle over restored acc/wsum/count tensors and an exported
+    record (bytes).  Returns the handle."""
+    h = ctypes.c_void_p(0)
+    rc = load().fedavg_resume(ctypes.byref(h), state, len(state), int(N), _mode(mode),
+                              int(bool(partial)), _ptr(acc), _ptr(wsum), _ptr(count),
+                              _ptr(staging), staging.numel() * staging.element_size(), int(chunk_bytes),
+                              int(n_slots), _stream_handle(compute_stream),
+                              None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream))
+    _check(rc)
+    return h
+
+
 def fedavg_finalize(h, base, out):
     _contig(base, "base")
     _contig(out, "out")
@@ -247,7 +306,7 @@ class StreamingAccumulator:
     close()."""
 
     def __init__(self, N, mode="weights", partial=False, chunk_bytes=64 << 20, n_slots=2,
-                 counts=True, device="cuda", compute_stream=None, copy_stream=None):
+                 counts=True, device="cuda", compute_stream=None, copy_stream=None, _resume=None):
         acc_b, wsum_b, count_b, stag_b = fedavg_workspace_size(N, partial, chunk_bytes, n_slots)
         self.N = N
         self.acc = torch.empty(max(acc_b // 4, 1), dtype=torch.float32, device=device)
@@ -255,11 +314,106 @@ class StreamingAccumulator:
         self.count = (torch.empty(max(count_b, 1), dtype=torch.uint8, device=device)
                       if partial and counts else None)
         self.staging = torch.empty(stag_b, dtype=torch.uint8, device=device)
-        self.handle = fedavg_begin(N, mode, partial, self.acc, self.wsum, self.count, self.staging,
-                                   chunk_bytes, n_slots, compute_stream, copy_stream)
+        if _resume is None:
+            self.handle = fedavg_begin(N, mode, partial, self.acc, self.wsum, self.count, self.staging,
+                                       chunk_bytes, n_slots, compute_stream, copy_stream)
+        else:
+            # the library checks the record against N, mode and partial first;
+            # the buffers are filled before anything can be accumulated
+            state, restore = _resume
+            self.handle = fedavg_resume(state, N, mode, partial, self.acc, self.wsum, self.count,
+                                        self.staging, chunk_bytes, n_slots, compute_stream,
+                                        copy_stream)
+            try:
+                restore(self)
+            except BaseException:
+                self.close()
+                raise
+
+    # spill to / resume from a directory: state.bin (the handle's record) and
+    # the raw acc.f32, wsum.u32, count.u8 buffers, copied through a pinned
+    # bounce buffer piece by piece
+    _SPILL_PIECE = 64 << 20
+
+    def save(self, path):
+        """Write the running aggregate to directory `path` (created if needed).
+        The accumulator stays usable."""
+        import os
+        import numpy as np
+        state = fedavg_export_state(self.handle)
+        os.makedirs(path, exist_ok=True)
+        with open(os.path.join(path, "state.bin"), "wb") as f:
+            f.write(state)
+        for name, t in (("acc.f32", self.acc), ("wsum.u32", self.wsum), ("count.u8", self.count)):
+            if t is None:
+                continue
+            flat = t[:self.N].view(torch.uint8) if self.N > 0 else t[:0].view(torch.uint8)
+            total = flat.numel()
+            mm = np.memmap(os.path.join(path, name), dtype=np.uint8, mode="w+", shape=(max(total, 1),))
+            bounce = torch.empty(min(self._SPILL_PIECE, max(total, 1)), dtype=torch.uint8, pin_memory=True)
+            for off in range(0, total, bounce.numel()):
+                n = min(bounce.numel(), total - off)
+                bounce[:n].copy_(flat[off:off + n])
+                mm[off:off + n] = bounce[:n].numpy()
+            mm.flush()
+            del mm
+
+    @classmethod
+    def load(cls, path, N, mode="weights", partial=False, chunk_bytes=64 << 20, n_slots=2,
+             device="cuda", compute_stream=None, copy_stream=None):
+        """Resume an aggregate written by save().  N, mode and partial must be
+        the saved ones (the library checks N, mode and partial against the
+        saved record)."""
+        import os
+        import numpy as np
+        with open(os.path.join(path, "state.bin"), "rb") as f:
+            state = f.read()
+        counts = os.path.exists(os.path.join(path, "count.u8"))
+
+        def restore(self):
+            for name, t in (("acc.f32", self.acc), ("wsum.u32", self.wsum), ("count.u8", self.count)):
+                if t is None:
+                    continue
+                flat = t[:N].view(torch.uint8)
+                total = flat.numel()
+                if total == 0:
+                    continue
+                mm = np.memmap(os.path.join(path, name), dtype=np.uint8, mode="r")
+                if mm.shape[0] != total:
+                    raise ValueError(f"{name} holds {mm.shape[0]} bytes, expected {total}")
+                bounce = torch.empty(min(self._SPILL_PIECE, total), dtype=torch.uint8, pin_memory=True)
+                for off in range(0, total, bounce.numel()):
+                    n = min(bounce.numel(), total - off)
+                    bounce[:n].copy_(torch.from_numpy(np.asarray(mm[off:off + n])))
+                    flat[off:off + n].copy_(bounce[:n])
+                torch.cuda.synchronize()
+                del mm
+
+        return cls(N, mode=mode, partial=partial, chunk_bytes=chunk_bytes, n_slots=n_slots,
+                   counts=counts, device=device, compute_stream=compute_stream,
+                   copy_stream=copy_stream, _resume=(state, restore))
 
     def accumulate(self, client_id, n_k, chunk, offset=0, mask=None, indices=None):
         fedavg_accumulate(self.handle, client_id, n_k, chunk, offset, mask, indices)
+
+    def accumulate_partial(self, client_id, W, n_clients, acc_src, wsum_src=None, count_src=None,
+                           offset=0):
+        fedavg_accumulate_partial(self.handle, client_id, W, n_clients, acc_src, wsum_src, count_src,
+                                  offset)
+
+    def add_silo(self, client_id, silo):
+        """Feed another StreamingAccumulator's whole partial (after its work
+        is done) as one pseudo-client of this one."""
+        silo.sync()
+        W, members = fedavg_partial_info(silo.handle)
+        N = self.N
+        fedavg_accumulate_partial(self.handle, client_id, W, members, silo.acc[:N],
+                                  None if silo.wsum is None else silo.wsum[:N],
+                                  None if silo.count is None else silo.count[:N], 0)
+
+    def info(self):
+        """(total weight, number of clients) accumulated so far."""
+        return fedavg_partial_info(self.handle)
 
     def finalize(self, base, out):
         fedavg_finalize(self.handle, base, out)
