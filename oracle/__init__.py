@@ -61,6 +61,8 @@ def _load():
     lib.orc_round_to_bf16.restype = None
     lib.orc_checksum.argtypes = [P, i64, ctypes.c_int, i64]
     lib.orc_checksum.restype = ctypes.c_uint64
+    lib.orc_topk.argtypes = [P, ctypes.c_int, i64, i64, P, P]
+    lib.orc_topk.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -181,3 +183,18 @@ def checksum(a, dtype, first=0):
     lib = _load()
     a = _raw(a, dtype)
     return int(lib.orc_checksum(_ptr(a), a.size, dtype, first))
+
+
+def topk(x, dtype, k):
+    """The k entries of largest magnitude of a client's update (ties to the
+    lower index; NaNs above infinity), as increasing int64 indices and their
+    float32 values.  x: float32 array, or uint16 bf16 bits."""
+    lib = _load()
+    x = _raw(x, dtype)
+    N = x.size
+    idx = np.empty(k, np.int64)
+    val = np.empty(k, np.float32)
+    rc = lib.orc_topk(_ptr(x), dtype, N, k, _ptr(idx), _ptr(val))
+    if rc != 0:
+        raise OracleError(f"orc_topk failed: {rc}")
+    return idx, val

@@ -339,3 +339,70 @@ uint64_t orc_checksum(const void *buf, int64_t count, int dtype, int64_t first)
     }
     return h;
 }
+
+/*
+ * Client-side top-k selection for partial sharing.  A client shares only a
+ * fraction of its update, which it chooses itself (Clara page, introduction
+ * and client-side workflow section); the fraction kept is the k = floor(p*N)
+ * entries of largest magnitude.  Readings where the page is silent: the
+ * order is by |value| -- precisely, by the magnitude bit pattern (the value's
+ * bits with the sign cleared, of the fp32 value; a bf16 value is widened to
+ * fp32 exactly), which orders finite values and infinities by |value| and
+ * places NaNs above infinity; -0 and +0 tie; ties go to the lower index.  The
+ * result is the k chosen indices in increasing order with their values.
+ *
+ * Written as the definition: every (key, index) pair sorted by key
+ * descending then index ascending, the first k taken, then re-sorted by
+ * index.
+ */
+typedef struct {
+    uint32_t key;
+    int64_t index;
+} orc_rank;
+
+static int by_key_desc_then_index(const void *a, const void *b)
+{
+    const orc_rank *x = (const orc_rank *)a, *y = (const orc_rank *)b;
+    if (x->key != y->key)
+        return x->key > y->key ? -1 : 1;
+    return (x->index > y->index) - (x->index < y->index);
+}
+
+static int by_index(const void *a, const void *b)
+{
+    int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+static uint32_t magnitude_key(const void *buf, int dtype, int64_t i)
+{
+    uint32_t bits;
+    if (dtype == ORC_F32)
+        memcpy(&bits, (const char *)buf + 4 * i, 4);
+    else
+        bits = (uint32_t)((const uint16_t *)buf)[i] << 16;
+    return bits & 0x7FFFFFFFu;
+}
+
+int orc_topk(const void *x, int dtype, int64_t N, int64_t k, int64_t *idx_out, float *val_out)
+{
+    if (!dtype_ok(dtype) || N < 0 || k < 0 || k > N || (N > 0 && !x))
+        return ORC_ERR_ARG;
+    if (k == 0)
+        return ORC_OK;
+    orc_rank *r = (orc_rank *)malloc((size_t)N * sizeof *r);
+    if (!r)
+        return ORC_ERR_NOMEM;
+    for (int64_t i = 0; i < N; ++i) {
+        r[i].key = magnitude_key(x, dtype, i);
+        r[i].index = i;
+    }
+    qsort(r, (size_t)N, sizeof *r, by_key_desc_then_index);
+    for (int64_t j = 0; j < k; ++j)
+        idx_out[j] = r[j].index;
+    free(r);
+    qsort(idx_out, (size_t)k, sizeof *idx_out, by_index);
+    for (int64_t j = 0; j < k; ++j)
+        val_out[j] = (float)value_at(x, dtype, idx_out[j]);
+    return ORC_OK;
+}

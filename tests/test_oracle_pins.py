@@ -367,3 +367,78 @@ def test_topk_generator_support_and_tail():
     assert np.all(np.diff(idx) > 0) and idx[0] >= 0 and idx[-1] < N
     # top-10% of Laplace(0,b) magnitudes sit above about b*ln(10)
     assert np.quantile(np.abs(val), 0.05) > 0.8 * 1e-3 * math.log(10)
+
+
+# ---------------------------------------------------------------- top-k selection
+
+def _bits_array(case):
+    if case["dtype"] == "f32":
+        return np.array([int(h, 16) for h in case["x_hex"]], np.uint32).view(np.float32), oracle.F32
+    return np.array([int(h, 16) for h in case["x_hex"]], np.uint16), oracle.BF16
+
+
+@pytest.mark.parametrize("case", _golden()["topk"], ids=lambda c: c["name"])
+def test_hand_worked_topk(case):
+    x, dt = _bits_array(case)
+    for c in case["cases"]:
+        idx, val = oracle.topk(x, dt, c["k"])
+        assert idx.tolist() == c["idx"], c
+        want = x[idx] if dt == oracle.F32 else synth.f32_from_bf16_bits(x[idx])
+        assert np.array_equal(val.view(np.uint32), np.asarray(want, np.float32).view(np.uint32))
+
+
+def _dominates(keys, S):
+    """S (a set of indices) is the top-k: every chosen entry outranks every
+    other -- larger key, or equal key and lower index."""
+    out = [j for j in range(len(keys)) if j not in S]
+    return all(keys[i] > keys[j] or (keys[i] == keys[j] and i < j) for i in S for j in out)
+
+
+def test_topk_brute_force_over_all_subsets():
+    import itertools
+    r = np.random.default_rng(5)
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.inf, -np.inf, np.nan, 1e-40, 3.0], np.float32)
+    for trial in range(60):
+        N = int(r.integers(1, 9))
+        x = r.choice(pool, N)
+        # rank by |x| with NaN above infinity, compared as tuples so that no
+        # comparison ever involves a NaN
+        rank_key = [(2 if np.isnan(v) else 1 if np.isinf(v) else 0, 0.0 if np.isnan(v) or np.isinf(v)
+                     else float(abs(v))) for v in x]
+        for k in range(N + 1):
+            winners = [set(S) for S in itertools.combinations(range(N), k) if _dominates(rank_key, set(S))]
+            assert len(winners) == 1
+            idx, _ = oracle.topk(x, oracle.F32, k)
+            assert set(idx.tolist()) == winners[0] and list(idx) == sorted(idx)
+
+
+def test_topk_magnitude_order_for_finite_values():
+    r = np.random.default_rng(6)
+    x = (r.standard_normal(20000) * np.exp(r.uniform(-30, 30, 20000))).astype(np.float32)
+    x[::97] = 0.0
+    x[::89] *= -1
+    k = 777
+    idx, val = oracle.topk(x, oracle.F32, k)
+    a = np.abs(x.astype(np.float64))
+    chosen = np.zeros(len(x), bool)
+    chosen[idx] = True
+    assert a[chosen].min() >= a[~chosen].max()
+    # distinct magnitudes: a plain stable sort by magnitude gives the same set
+    u = np.unique(a, return_index=True)[1]
+    xd = x[np.sort(u)]
+    kd = 500
+    got, _ = oracle.topk(xd, oracle.F32, kd)
+    want = np.sort(np.argsort(-np.abs(xd.astype(np.float64)), kind="stable")[:kd])
+    assert np.array_equal(got, want)
+
+
+def test_topk_bf16_equals_widened_fp32_and_edge_counts():
+    r = np.random.default_rng(7)
+    bits = synth.bf16_bits_from_f32((r.standard_normal(5000) * 0.01).astype(np.float32))
+    wide = synth.f32_from_bf16_bits(bits)
+    for k in (0, 1, 500, 4999, 5000):
+        a = oracle.topk(bits, oracle.BF16, k)
+        b = oracle.topk(wide, oracle.F32, k)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    with pytest.raises(oracle.OracleError):
+        oracle.topk(wide, oracle.F32, 5001)
