@@ -283,6 +283,34 @@ def bench_hierarchical(silos=4):
             "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_topk(steps=10, warmup=2):
+    """Client-side top-10% selection over one 10^9-parameter fp32 update
+    (Laplace(0, 1e-3) deltas): the radix-select passes, tile counts, scan and
+    ordered compaction, timed as one call.  Algorithmic bytes: one read of the
+    update (4 B per parameter) and the kept (int64 index, fp32 value) pairs."""
+    import torch
+    import synth.device as sd
+    import weighted_model_update_amd as fa
+    N = 10 ** 9
+    log("topk: generating a 10^9-parameter Laplace client update")
+    x = sd.client_delta_1b(0, N)
+    k = fa.topk_count(N, 0.1)
+    idx = torch.empty(k, dtype=torch.int64, device="cuda")
+    val = torch.empty(k, dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.topk_workspace_size(N), dtype=torch.uint8, device="cuda")
+    fn = lambda i: fa.topk_select(x, k, idx, val, ws)
+    _, times = timed(fn, steps, warmup)
+    ms = sum(times) / len(times)
+    algo = 4 * N + 12 * k
+    del x, idx, val, ws
+    free_gpu()
+    return {"N": N, "k": k, "dtype": "f32", "ms_per_call": ms, "algo_bytes": algo,
+            "hbm_gbs": algo / (ms * 1e-3) / 1e9, "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "params_per_s": N / (ms * 1e-3), "input_passes": 5,
+            "note": "three radix-select histogram passes, a tile-count pass and the compaction pass "
+                    "each read the update once"}
+
+
 def bench_sparse(steps=10, warmup=2):
     import torch
     import synth.device as sd
@@ -415,6 +443,9 @@ def main():
     if "streaming" in only:
         modes["streaming"] = bench_streaming(args.stream_clients)
         log(f"streaming: {modes['streaming']['wall_s']:.2f} s")
+    if "topk" in only:
+        modes["topk"] = bench_topk()
+        log(f"topk: {modes['topk']['ms_per_call']:.3f} ms/call")
     if "hierarchical" in only:
         modes["hierarchical"] = bench_hierarchical()
         log(f"hierarchical: {modes['hierarchical']['ms_per_merge']:.3f} ms per silo merge")

@@ -325,6 +325,31 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
                              fa_count_dtype counts_dtype, uint32_t *wsum, void *workspace,
                              size_t workspace_bytes, int *err_flag, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Client-side top-k selection (partial sharing).
+ * ------------------------------------------------------------------------ */
+
+/* Device workspace bytes topk_select needs for N values. */
+int topk_workspace_size(int64_t N, size_t *bytes);
+
+/*
+ * topk_select -- the client's side of partial sharing: of its update x
+ * (device, N values of dtype) keep the k entries of largest magnitude, the
+ * fraction p of the update it chooses to send (k = floor(p*N); Clara page,
+ * introduction and client-side workflow section).  Order: by the magnitude
+ * bit pattern (the fp32 bits with the sign cleared; bf16 is widened to fp32
+ * exactly) -- |x| order, with NaNs above infinity and -0 tied with +0; ties go
+ * to the lower index.  The k kept indices are written to idx_out (device
+ * int64[k]) in increasing order and their values, widened to fp32, to val_out
+ * (device float[k]): exactly the per-client lists sparse_masked_accumulate
+ * takes.  The result is unique, hence deterministic.
+ * k == 0 returns FA_OK with no work; k > N is FA_ERR_RANGE.  workspace:
+ * device, 16-byte aligned, topk_workspace_size(N) bytes, overwritten.
+ * Outputs must not overlap x.  Asynchronous on `stream`.
+ */
+int topk_select(const void *x, fa_dtype dtype, int64_t N, int64_t k, int64_t *idx_out,
+                float *val_out, void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * fedavg_checksum -- order-independent checksum of a device buffer of `count`
  * elements: *hash_dev = sum over i of fmix64(i * 0x9E3779B97F4A7C15 XOR

@@ -138,3 +138,22 @@ def sparse_1b(device="cuda", K=20, N=10 ** 9, frac=0.1, scale=1e-3):
         val.append(laplace_tail(k, scale, frac, generator(CFG_SPARSE_1B, ROLE_VALUES, c, device), device))
     base = normal(N, 0.02, generator(CFG_SPARSE_1B, ROLE_BASE, 0, device), device=device)
     return n, idx, val, base
+
+
+def laplace(N, scale, g, device="cuda"):
+    """N i.i.d. Laplace(0, scale) draws (scale = b, the Laplace scale) as
+    float32, by inverting the CDF of uniform draws in (-1/2, 1/2)."""
+    u = torch.empty(N, dtype=torch.float32, device=device)
+    u.uniform_(-0.5, 0.5, generator=g)
+    # x = -b * sign(u) * ln(1 - 2|u|); |u| = 0.5 exactly never occurs because
+    # uniform_ draws from [-0.5, 0.5)
+    a = u.abs()
+    a.mul_(-2.0).add_(1.0).log_().mul_(-scale)
+    return a.copysign_(u)
+
+
+def client_delta_1b(client=0, N=10 ** 9, scale=1e-3, device="cuda"):
+    """One client's full fp32 update of the 10^9-parameter model before
+    sparsification: i.i.d. Laplace(0, 1e-3) deltas (the distribution whose
+    top-10% the sparse workload stands in for)."""
+    return laplace(N, scale, generator(CFG_SPARSE_1B, ROLE_VALUES, 1000 + client, device), device)

@@ -5,6 +5,7 @@ inputs gathered at those parameters), and whole-buffer properties that hold
 at any size are checked exactly."""
 
 import gc
+import math
 
 import numpy as np
 import pytest
@@ -136,3 +137,41 @@ def test_streaming_8b_k32_sampled():
     ref, mag, _, _ = oracle.weighted_average(deltas, n, mode=oracle.DELTAS, base=base_before,
                                              x_dtype=oracle.BF16, base_dtype=oracle.BF16)
     check(got, ref, mag, "bf16", label="streaming 8B sampled")
+
+
+def test_topk_1b_client_update_properties():
+    """Top-10% of a 10^9-parameter fp32 client update.  The kept set is
+    unique, and these properties pin it at any size: k entries, strictly
+    increasing indices, the values read at those indices, every kept key at
+    least every dropped key, and among keys equal to the threshold the kept
+    ones all lie below the dropped ones."""
+    N = 10 ** 9
+    x = sd.client_delta_1b(0, N)
+    k = fa.topk_count(N, 0.1)
+    idx, val = fa.topk_select(x, k)
+    torch.cuda.synchronize()
+    assert idx.numel() == k
+    assert bool((idx[1:] > idx[:-1]).all()) and int(idx[0]) >= 0 and int(idx[-1]) < N
+    assert torch.equal(val.view(torch.int32), x[idx].view(torch.int32))
+    key = x.view(torch.int32) & 0x7FFFFFFF
+    kept = torch.zeros(N, dtype=torch.bool, device="cuda")
+    kept[idx] = True
+    T = int(key[idx].min())
+    dropped_max = int(key.masked_fill(kept, -1).max())
+    assert dropped_max <= T
+    if dropped_max == T:
+        tie = key == T
+        kept_ties = torch.nonzero(tie & kept).flatten()
+        dropped_ties = torch.nonzero(tie & ~kept).flatten()
+        assert int(kept_ties.max()) < int(dropped_ties.min())
+    # the threshold sits where the distribution says: b*ln(10) for Laplace(0, b)
+    t = float(torch.tensor(T, dtype=torch.int32).view(torch.float32))
+    assert abs(t / (1e-3 * math.log(10)) - 1) < 0.01
+    # and the oracle agrees on a window of the update (its own top-k of the
+    # window, compared with the GPU's on the same window)
+    w = x[:2_000_000].cpu().numpy()
+    kw = 200_000
+    wi, wv = fa.topk_select(x[:2_000_000], kw)
+    oi, ov = oracle.topk(w, oracle.F32, kw)
+    assert np.array_equal(wi.cpu().numpy(), oi) and np.array_equal(wv.cpu().numpy().view(np.uint32),
+                                                                   ov.view(np.uint32))

@@ -9,6 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libfedavg.so")
 SOURCES = [os.path.join(HERE, "csrc", "fedavg_kernels.hip"),
+           os.path.join(HERE, "csrc", "topk.hip"),
            os.path.join(HERE, "csrc", "fedavg_api.hip")]
 HEADERS = [os.path.join(HERE, "csrc", "fedavg_internal.h"),
            os.path.join(ROOT, "include", "fedavg.h")]

@@ -1050,6 +1050,45 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
 
 // ============================================================ checksum
 
+// ============================================================ top-k selection
+
+int topk_workspace_size(int64_t N, size_t *bytes)
+{
+    if (N < 0 || !bytes)
+        return fail(FA_ERR_ARG, "need N >= 0 and a result pointer");
+    *bytes = fa::topk_workspace_bytes(N);
+    return ok();
+}
+
+int topk_select(const void *x, fa_dtype dtype, int64_t N, int64_t k, int64_t *idx_out,
+                float *val_out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!dtype_ok(dtype))
+        return fail(FA_ERR_DTYPE, "x must be FA_F32 or FA_BF16");
+    if (N < 0 || k < 0 || k > N)
+        return fail(FA_ERR_RANGE, "need 0 <= k <= N (k=%lld, N=%lld)", (long long)k, (long long)N);
+    if (k == 0)
+        return ok();
+    if (!x || !idx_out || !val_out || !workspace)
+        return fail(FA_ERR_ARG, "x, idx_out, val_out and workspace are required");
+    if ((N + fa::TK_TILE - 1) / fa::TK_TILE > 0x7fffffffll)
+        return fail(FA_ERR_RANGE, "N=%lld is too large", (long long)N);
+    const size_t need = fa::topk_workspace_bytes(N);
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(idx_out) & 7u) != 0 ||
+        (reinterpret_cast<uintptr_t>(val_out) & 3u) != 0)
+        return fail(FA_ERR_ARG, "workspace must be 16-byte aligned, idx_out 8 and val_out 4");
+    const size_t xbytes = (size_t)N * dsize(dtype);
+    if (!overlap_ok(idx_out, (size_t)k * 8, x, xbytes) || !overlap_ok(val_out, (size_t)k * 4, x, xbytes) ||
+        idx_out == x || val_out == x)
+        return fail(FA_ERR_ARG, "outputs must not overlap the input");
+    hipError_t e = fa::launch_topk(x, dtype, N, k, idx_out, val_out, workspace, cu_count(),
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "top-k launch");
+}
+
 int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *hash_dev, void *stream)
 {
     if (!hash_dev || (count > 0 && !buf) || count < 0)

@@ -117,6 +117,11 @@ hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int m
                                   bool aligned, int64_t grid_cap, int resident, hipStream_t s);
 int sparse_resident_blocks_per_cu(int tile);
 hipError_t launch_sparse(const SparseArgs &a, hipStream_t s);
+// client-side top-k selection (topk.hip)
+constexpr int TK_TILE = 8192; // elements per tile of the count and write passes
+size_t topk_workspace_bytes(int64_t N);
+hipError_t launch_topk(const void *x, int dt, int64_t N, int64_t k, int64_t *idx_out,
+                       float *val_out, void *ws, int cus, hipStream_t s);
 hipError_t launch_checksum(const void *buf, int64_t count, int dt, uint64_t *hash,
                            hipStream_t s);
 hipError_t launch_fill_u32(void *p, int64_t words, uint32_t value, hipStream_t s);

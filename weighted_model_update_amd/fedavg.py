@@ -32,7 +32,7 @@ EXPORTS = [
     "fedavg_abi_version", "fedavg_last_error", "fedavg_aggregate", "fedavg_workspace_size",
     "fedavg_begin", "fedavg_accumulate", "fedavg_finalize", "fedavg_sync", "fedavg_destroy",
     "fedavg_accumulate_partial", "fedavg_partial_info", "fedavg_state_size", "fedavg_export_state",
-    "fedavg_resume", "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
+    "fedavg_resume", "topk_workspace_size", "topk_select", "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
 ]
 
 
@@ -79,6 +79,8 @@ def load(build_if_missing=True):
         "sparse_workspace_size": ([i32, i64, P], i32),
         "sparse_masked_accumulate": ([i32, P, P, P, P, i64, i32, P, P, P, i32, P, P, sz, P, P], i32),
         "fedavg_checksum": ([P, i64, i32, P, P], i32),
+        "topk_workspace_size": ([i64, P], i32),
+        "topk_select": ([P, i32, i64, i64, P, P, P, sz, P], i32),
         "fedavg_set_option": ([i32, i64], i32),
     }
     for name, (args, res) in sig.items():
@@ -504,3 +506,40 @@ def fedavg_checksum(t, stream=None, hash_out=None):
     if own:
         return int(hash_out.item()) & 0xFFFFFFFFFFFFFFFF
     return None
+
+
+# ------------------------------------------------------------------ top-k
+
+def topk_workspace_size(N):
+    b = ctypes.c_size_t(0)
+    _check(load().topk_workspace_size(int(N), ctypes.byref(b)))
+    return b.value
+
+
+def topk_select(x, k, idx_out=None, val_out=None, workspace=None, stream=None):
+    """The k entries of largest magnitude of the 1-D update x (ties to the
+    lower index), as (int64 indices in increasing order, float32 values)."""
+    _contig(x, "x")
+    N = x.numel()
+    k = int(k)
+    dev = x.device
+    if idx_out is None:
+        idx_out = torch.empty(k, dtype=torch.int64, device=dev)
+    if val_out is None:
+        val_out = torch.empty(k, dtype=torch.float32, device=dev)
+    if idx_out.numel() < k or val_out.numel() < k or idx_out.dtype != torch.int64 \
+            or val_out.dtype != torch.float32:
+        raise ValueError("idx_out must be int64 and val_out float32, each with room for k entries")
+    if workspace is None:
+        workspace = torch.empty(max(topk_workspace_size(N), 1), dtype=torch.uint8, device=dev)
+    rc = load().topk_select(_ptr(x), _dtype(x), N, k, _ptr(idx_out), _ptr(val_out), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(rc)
+    return idx_out[:k], val_out[:k]
+
+
+def topk_count(N, frac):
+    """k = floor(frac * N), with frac read as the decimal it is written as."""
+    from fractions import Fraction
+    import math
+    return int(math.floor(Fraction(str(frac)) * int(N)))
