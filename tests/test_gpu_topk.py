@@ -68,6 +68,18 @@ def test_threshold_inside_a_tie_group(dt):
         same(run_topk(x, dt, k), expect(x, dt, k))
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_candidate_overflow_falls_back_to_the_whole_input(dt):
+    # three magnitudes: the threshold bin holds about a third of the input,
+    # more than the candidate buffer (N/16 + 65536 entries) takes
+    r = np.random.default_rng(8)
+    N = 2_000_003
+    x = (r.integers(-2, 3, N)).astype(np.float32)
+    x = synth.bf16_bits_from_f32(x) if dt == "bf16" else x
+    for k in (500_000, 1_000_001, 1_700_000):
+        same(run_topk(x, dt, k), expect(x, dt, k))
+
+
 def test_special_values_and_signed_zeros():
     r = np.random.default_rng(4)
     N = 50_000
