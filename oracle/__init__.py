@@ -26,7 +26,7 @@ _SRC = os.path.join(_HERE, "fedavg_oracle.c")
 _LIB = os.path.join(_HERE, "libfedavg_oracle.so")
 
 F32, BF16 = 0, 1
-WEIGHTS, DELTAS = 0, 1
+WEIGHTS, DELTAS, DELTAS_ZERO_FILL = 0, 1, 2
 
 _lib = None
 

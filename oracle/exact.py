@@ -53,9 +53,13 @@ def round_fp32(q):
 def weighted_average_exact(xs, n, mode="weights", base=None, sent=None):
     """xs: K lists of N finite floats (each exactly an fp32 or bf16 value);
     n: K non-negative ints; base: N floats or None; sent: None or K lists of
-    N bools.  Returns the N correctly rounded fp32 results as floats."""
+    N bools.  mode "deltas_zero_fill": a client that did not send a
+    parameter counts as sending a zero delta, so the mean divides by the
+    total weight of all clients.  Returns the N correctly rounded fp32
+    results as floats."""
     K = len(xs)
     N = len(xs[0])
+    S_all = sum(v for v in n if v > 0)
     out = []
     for i in range(N):
         s = Fraction(0)
@@ -71,6 +75,6 @@ def weighted_average_exact(xs, n, mode="weights", base=None, sent=None):
                 raise ValueError("parameter without sender and no base")
             out.append(round_fp32(b))
             continue
-        v = s / W
-        out.append(round_fp32(b + v if mode == "deltas" else v))
+        v = s / (S_all if mode == "deltas_zero_fill" else W)
+        out.append(round_fp32(v if mode == "weights" else b + v))
     return out

@@ -56,7 +56,7 @@
 #include <string.h>
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
-enum { ORC_WEIGHTS = 0, ORC_DELTAS = 1 };
+enum { ORC_WEIGHTS = 0, ORC_DELTAS = 1, ORC_DELTAS_ZERO_FILL = 2 };
 enum {
     ORC_OK = 0,
     ORC_ERR_ARG = -1,
@@ -81,9 +81,14 @@ static int dtype_ok(int d) { return d == ORC_F32 || d == ORC_BF16; }
 
 /*
  * Resolve one parameter from its per-client sums.
- *   s = sum n_k x_k, m = sum n_k |x_k|, W = sum n_k over the senders.
+ *   s = sum n_k x_k, m = sum n_k |x_k|, W = sum n_k over the senders,
+ *   S = sum n_k over every client with n_k > 0.
+ * Zero-fill delta mode reads partial sharing the other way: a client that
+ * did not send a parameter counts as having sent a zero delta for it, so the
+ * mean is taken over all clients, sum n_k d_k / S (parameters nobody sent
+ * still keep base_i exactly).
  */
-static int resolve(double s, double m, uint64_t W, int mode, const void *base,
+static int resolve(double s, double m, uint64_t W, uint64_t S, int mode, const void *base,
                    int base_dtype, int64_t i, float *ref32, double *mag)
 {
     double b = base ? value_at(base, base_dtype, i) : 0.0;
@@ -95,10 +100,11 @@ static int resolve(double s, double m, uint64_t W, int mode, const void *base,
         *mag = fabs(b);
         return ORC_OK;
     }
-    double mean = s / (double)W;
-    double r = (mode == ORC_DELTAS) ? b + mean : mean;
+    const double D = (mode == ORC_DELTAS_ZERO_FILL) ? (double)S : (double)W;
+    double mean = s / D;
+    double r = (mode == ORC_WEIGHTS) ? mean : b + mean;
     *ref32 = (float)r; /* one rounding to nearest-even */
-    *mag = (mode == ORC_DELTAS ? fabs(b) : 0.0) + m / (double)W;
+    *mag = (mode == ORC_WEIGHTS ? 0.0 : fabs(b)) + m / D;
     return ORC_OK;
 }
 
@@ -118,15 +124,18 @@ int orc_weighted_average(int K, const void *const *x, int x_dtype, const int64_t
 {
     if (K < 1 || N < 0 || !x || !n || !ref32 || !mag || !dtype_ok(x_dtype))
         return ORC_ERR_ARG;
-    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS)
+    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS && mode != ORC_DELTAS_ZERO_FILL)
         return ORC_ERR_ARG;
     if (base && !dtype_ok(base_dtype))
         return ORC_ERR_ARG;
-    if (mode == ORC_DELTAS && !base)
+    if (mode != ORC_WEIGHTS && !base)
         return ORC_ERR_ARG;
-    for (int k = 0; k < K; ++k)
+    uint64_t S = 0;
+    for (int k = 0; k < K; ++k) {
         if (n[k] < 0 || (n[k] > 0 && !x[k]))
             return ORC_ERR_ARG;
+        S += (uint64_t)n[k];
+    }
 
     for (int64_t i = 0; i < N; ++i) {
         double s = 0.0, m = 0.0;
@@ -143,7 +152,7 @@ int orc_weighted_average(int K, const void *const *x, int x_dtype, const int64_t
             W += (uint64_t)n[k];
             c += 1;
         }
-        int rc = resolve(s, m, W, mode, base, base_dtype, i, &ref32[i], &mag[i]);
+        int rc = resolve(s, m, W, S, mode, base, base_dtype, i, &ref32[i], &mag[i]);
         if (rc != ORC_OK)
             return rc;
         if (count)
@@ -166,13 +175,16 @@ int orc_sparse_average(int K, const int64_t *const *idx, const float *const *val
 {
     if (K < 1 || N < 0 || !idx || !val || !nnz || !n || !ref32 || !mag)
         return ORC_ERR_ARG;
-    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS)
+    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS && mode != ORC_DELTAS_ZERO_FILL)
         return ORC_ERR_ARG;
-    if (mode == ORC_DELTAS && !base)
+    if (mode != ORC_WEIGHTS && !base)
         return ORC_ERR_ARG;
-    for (int k = 0; k < K; ++k)
+    uint64_t S = 0;
+    for (int k = 0; k < K; ++k) {
         if (n[k] < 0 || nnz[k] < 0 || (nnz[k] > 0 && (!idx[k] || !val[k])))
             return ORC_ERR_ARG;
+        S += (uint64_t)n[k];
+    }
 
     double *s = calloc((size_t)(N ? N : 1), sizeof(double));
     double *m = calloc((size_t)(N ? N : 1), sizeof(double));
@@ -200,7 +212,7 @@ int orc_sparse_average(int K, const int64_t *const *idx, const float *const *val
         }
     }
     for (int64_t i = 0; i < N && rc == ORC_OK; ++i) {
-        rc = resolve(s[i], m[i], W[i], mode, base, ORC_F32, i, &ref32[i], &mag[i]);
+        rc = resolve(s[i], m[i], W[i], S, mode, base, ORC_F32, i, &ref32[i], &mag[i]);
         if (count)
             count[i] = c[i];
         if (wsum)
@@ -240,10 +252,14 @@ int orc_sparse_average_at(int K, const int64_t *const *idx, const float *const *
 {
     if (K < 1 || N < 0 || S < 0 || !idx || !val || !nnz || !n || !at || !ref32 || !mag)
         return ORC_ERR_ARG;
-    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS)
+    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS && mode != ORC_DELTAS_ZERO_FILL)
         return ORC_ERR_ARG;
-    if (mode == ORC_DELTAS && !base)
+    if (mode != ORC_WEIGHTS && !base)
         return ORC_ERR_ARG;
+    uint64_t Sall = 0; /* total weight of the clients, for zero-fill mode */
+    for (int k = 0; k < K; ++k)
+        if (n[k] > 0)
+            Sall += (uint64_t)n[k];
     for (int64_t q = 0; q < S; ++q) {
         int64_t i = at[q];
         if (i < 0 || i >= N)
@@ -264,17 +280,9 @@ int orc_sparse_average_at(int K, const int64_t *const *idx, const float *const *
             c += 1;
         }
         /* base is indexed by parameter, so resolve against base[i] */
-        double b = base ? (double)base[i] : 0.0;
-        if (W == 0) {
-            if (!base)
-                return ORC_ERR_ZERO_WEIGHT;
-            ref32[q] = (float)b;
-            mag[q] = fabs(b);
-        } else {
-            double mean = s / (double)W;
-            ref32[q] = (float)(mode == ORC_DELTAS ? b + mean : mean);
-            mag[q] = (mode == ORC_DELTAS ? fabs(b) : 0.0) + m / (double)W;
-        }
+        int rc = resolve(s, m, W, Sall, mode, base, ORC_F32, i, &ref32[q], &mag[q]);
+        if (rc != ORC_OK)
+            return rc;
         if (count)
             count[q] = c;
         if (wsum)

@@ -442,3 +442,64 @@ def test_topk_bf16_equals_widened_fp32_and_edge_counts():
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     with pytest.raises(oracle.OracleError):
         oracle.topk(wide, oracle.F32, 5001)
+
+
+# ---------------------------------------------------------------- zero-fill denominator
+
+def test_zero_fill_brute_force_masked_sparse_and_sampled():
+    """Zero-fill delta mode (unsent entries count as zero deltas, so the mean
+    divides by the total weight of all clients) against the exact-rational
+    statement, through the dense-with-masks, sparse and sampled entry points."""
+    r = np.random.default_rng(17)
+    K, N = 5, 60
+    xs = [(r.standard_normal(N) * 10.0 ** r.integers(-3, 2)).astype(np.float32) for _ in range(K)]
+    sent = [(r.random(N) < 0.4).astype(np.uint8) for _ in range(K)]
+    for s_ in sent:
+        s_[:3] = 0                               # nobody sent 0..2: base kept
+    n = r.integers(0, 900, size=K)
+    n[1] = 0                                     # a zero-weight client is no client at all
+    n[0] = max(n[0], 1)
+    base = r.standard_normal(N).astype(np.float32)
+    want = np.asarray(exact.weighted_average_exact([x.tolist() for x in xs], n.tolist(),
+                                                   mode="deltas_zero_fill", base=base.tolist(),
+                                                   sent=[s_.tolist() for s_ in sent]), np.float32)
+    ref, _, cnt, ws = oracle.weighted_average(xs, n, mode=oracle.DELTAS_ZERO_FILL, base=base, sent=sent)
+    np.testing.assert_array_equal(ref, want)
+    assert np.array_equal(ref[:3].view(np.uint32), base[:3].view(np.uint32))
+    idx = [np.nonzero(s_)[0] for s_ in sent]
+    val = [x[i] for x, i in zip(xs, idx)]
+    sref, _, scnt, sws = oracle.sparse_average(idx, val, n, N, mode=oracle.DELTAS_ZERO_FILL, base=base)
+    np.testing.assert_array_equal(sref, want)
+    np.testing.assert_array_equal(scnt, cnt)
+    at = np.array([0, 5, 17, 59], np.int64)
+    aref, _, _, _ = oracle.sparse_average_at(idx, val, n, N, at, mode=oracle.DELTAS_ZERO_FILL, base=base)
+    np.testing.assert_array_equal(aref, want[at])
+
+
+def test_zero_fill_special_cases():
+    r = np.random.default_rng(18)
+    K, N = 4, 500
+    xs = [(r.standard_normal(N) * 1e-3).astype(np.float32) for _ in range(K)]
+    n = np.array([3, 5, 7, 11])
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    # everyone sends everything: W_i = S, the two readings coincide
+    a = oracle.weighted_average(xs, n, mode=oracle.DELTAS_ZERO_FILL, base=base)[0]
+    b = oracle.weighted_average(xs, n, mode=oracle.DELTAS, base=base)[0]
+    assert np.array_equal(a, b)
+    # disjoint supports: each parameter gets base + n_k * d / S exactly rounded
+    owner = r.integers(0, K, N)
+    sent = [(owner == k).astype(np.uint8) for k in range(K)]
+    z = oracle.weighted_average(xs, n, mode=oracle.DELTAS_ZERO_FILL, base=base, sent=sent)[0]
+    S = int(n.sum())
+    want = np.array([float(base[i]) + n[owner[i]] * float(xs[owner[i]][i]) / S for i in range(N)])
+    assert np.max(np.abs(z - want.astype(np.float32))) <= 2 * np.spacing(np.abs(want).astype(np.float32)).max()
+
+
+@pytest.mark.parametrize("case", _golden()["sparse_zero_fill"], ids=lambda c: c["name"])
+def test_hand_worked_sparse_zero_fill(case):
+    idx = [np.array(i, np.int64) for i in case["idx"]]
+    val = [np.array(v, np.float32) for v in case["val"]]
+    base = np.array(case["base"], np.float32)
+    ref, _, _, _ = oracle.sparse_average(idx, val, case["n"], case["N"], mode=oracle.DELTAS_ZERO_FILL,
+                                         base=base)
+    assert ref.tolist() == case["expect"]
