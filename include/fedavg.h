@@ -91,7 +91,19 @@ typedef enum {
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
-typedef enum { FA_WEIGHTS = 0, FA_DELTAS = 1 } fa_mode;
+/*
+ * FA_WEIGHTS: clients send weights; out_i = sum n_k x_k / W_i.
+ * FA_DELTAS:  clients send deltas;  out_i = base_i + sum n_k d_k / W_i.
+ * FA_DELTAS_ZERO_FILL: clients send deltas and a parameter a client did not
+ *     send counts as a zero delta from it: out_i = base_i + sum n_k d_k / S,
+ *     S = sum of n_k over every client with n_k > 0 (in streaming: every
+ *     client accumulated so far, merged partials by their W).  A parameter no
+ *     client sent keeps base_i exactly.  With every client sending every
+ *     parameter this equals FA_DELTAS.  This is the other reading of
+ *     averaging partially shared updates (Clara page, client-side workflow:
+ *     each client sends a fraction of its update); the divisor is fp32(S).
+ */
+typedef enum { FA_WEIGHTS = 0, FA_DELTAS = 1, FA_DELTAS_ZERO_FILL = 2 } fa_mode;
 typedef enum { FA_COUNT_U8 = 0, FA_COUNT_U32 = 1 } fa_count_dtype;
 
 /* FEDAVG_ABI_VERSION of the loaded library. */

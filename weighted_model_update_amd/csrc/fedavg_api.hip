@@ -316,12 +316,15 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
         return fail(FA_ERR_ARG, "N=%lld is negative", (long long)N);
     if (!dtype_ok(x_dtype) || !dtype_ok(out_dtype) || !dtype_ok(base_dtype))
         return fail(FA_ERR_DTYPE, "dtypes must be FA_F32 or FA_BF16");
-    if (mode != FA_WEIGHTS && mode != FA_DELTAS)
+    if (mode != FA_WEIGHTS && mode != FA_DELTAS && mode != FA_DELTAS_ZERO_FILL)
         return fail(FA_ERR_ARG, "unknown mode %d", (int)mode);
     if (T < 0)
         return fail(FA_ERR_ARG, "T=%d is negative", T);
-    if (mode == FA_DELTAS && !base)
-        return fail(FA_ERR_ARG, "delta mode needs base");
+    if (mode != FA_WEIGHTS && !base)
+        return fail(FA_ERR_ARG, "delta modes need base");
+    // kernels see weights or deltas; zero fill only changes the divisor of
+    // the masked path (with every client sending everything, W_i = S)
+    const int kmode = mode == FA_WEIGHTS ? FA_WEIGHTS : FA_DELTAS;
     if (T > 0 && (!base || !seg_bounds || !present))
         return fail(FA_ERR_ARG, "segment masks need base, seg_bounds and present");
     if (N > 0 && !out)
@@ -368,14 +371,14 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
             hipError_t e = fa::launch_convert(base, base_dtype, out, out_dtype, N, s);
             return e == hipSuccess ? ok() : hip_fail(e, "convert launch");
         }
-        if (mode == FA_DELTAS)
+        if (kmode == FA_DELTAS)
             aligned = aligned && aligned16(base);
         d.K = Kc;
         d.N = N;
         d.base = base;
         d.out = out;
         d.S = (float)S;
-        hipError_t e = fa::launch_dense(d, x_dtype, out_dtype, base_dtype, mode, aligned,
+        hipError_t e = fa::launch_dense(d, x_dtype, out_dtype, base_dtype, kmode, aligned,
                                         grid_cap(), (int)g_resident_per_cu, s);
         return e == hipSuccess ? ok() : hip_fail(e, "dense aggregate launch");
     }
@@ -389,7 +392,9 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
     m.present = present;
     m.base = base;
     m.out = out;
-    hipError_t e = fa::launch_masked(m, x_dtype, out_dtype, base_dtype, mode, aligned, s);
+    m.zero_fill = mode == FA_DELTAS_ZERO_FILL;
+    m.S_all = (float)S;
+    hipError_t e = fa::launch_masked(m, x_dtype, out_dtype, base_dtype, kmode, aligned, s);
     return e == hipSuccess ? ok() : hip_fail(e, "masked aggregate launch");
 }
 
@@ -425,7 +430,7 @@ static int open_handle(fa_handle *h, int64_t N, int mode, int partial, float *ac
     *h = nullptr;
     if (N < 0 || chunk_bytes <= 0 || n_slots < 1 || n_slots > 64)
         return fail(FA_ERR_ARG, "need N >= 0, chunk_bytes > 0, 1 <= n_slots <= 64");
-    if (mode != FA_WEIGHTS && mode != FA_DELTAS)
+    if (mode != FA_WEIGHTS && mode != FA_DELTAS && mode != FA_DELTAS_ZERO_FILL)
         return fail(FA_ERR_ARG, "unknown mode %d", mode);
     if (partial != 0 && partial != 1)
         return fail(FA_ERR_ARG, "partial must be 0 or 1");
@@ -856,7 +861,7 @@ int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *ou
         return fail(FA_ERR_DTYPE, "dtypes must be FA_F32 or FA_BF16");
     if (st.N > 0 && !out)
         return fail(FA_ERR_ARG, "out must not be NULL");
-    if ((st.mode == FA_DELTAS || st.partial) && !base)
+    if ((st.mode != FA_WEIGHTS || st.partial) && !base)
         return fail(FA_ERR_ARG, "base is required in delta and partial modes");
     if (base && !overlap_ok(out, (size_t)st.N * dsize(out_dtype), base,
                             (size_t)st.N * dsize(base_dtype)))
@@ -884,9 +889,11 @@ int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *ou
     a.out = out;
     a.N = st.N;
     a.S = (float)S;
+    a.zero_fill = st.mode == FA_DELTAS_ZERO_FILL;
     const bool aligned = aligned16(out) && (!base || aligned16(base));
-    e = fa::launch_stream_finalize(a, base_dtype, out_dtype, st.mode, st.partial, aligned,
-                                   grid_cap(), 0, st.compute);
+    e = fa::launch_stream_finalize(a, base_dtype, out_dtype,
+                                   st.mode == FA_WEIGHTS ? FA_WEIGHTS : FA_DELTAS, st.partial,
+                                   aligned, grid_cap(), 0, st.compute);
     return e == hipSuccess ? ok() : hip_fail(e, "finalize launch");
 }
 
@@ -976,7 +983,7 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
         return fail(FA_ERR_ARG, "idx, val, nnz and n must not be NULL");
     if (N < 0)
         return fail(FA_ERR_ARG, "N is negative");
-    if (mode != FA_WEIGHTS && mode != FA_DELTAS)
+    if (mode != FA_WEIGHTS && mode != FA_DELTAS && mode != FA_DELTAS_ZERO_FILL)
         return fail(FA_ERR_ARG, "unknown mode %d", (int)mode);
     if (counts_dtype != FA_COUNT_U8 && counts_dtype != FA_COUNT_U32)
         return fail(FA_ERR_DTYPE, "counts dtype must be FA_COUNT_U8 or FA_COUNT_U32");
@@ -991,13 +998,14 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
 
     fa::SparseArgs a;
     std::memset(&a, 0, sizeof a);
-    uint64_t S = 0;
+    uint64_t S = 0, S_all = 0; // over the clients that sent entries / over all with n_k > 0
     int Kc = 0;
     for (int k = 0; k < K; ++k) {
         if (n[k] < 0 || n[k] > FA_MAX_WEIGHT)
             return fail(FA_ERR_RANGE, "n[%d]=%lld outside [0, 2^24]", k, (long long)n[k]);
         if (nnz[k] < 0)
             return fail(FA_ERR_ARG, "nnz[%d] is negative", k);
+        S_all += (uint64_t)n[k];
         if (n[k] == 0 || nnz[k] == 0)
             continue;
         if (!idx[k] || !val[k])
@@ -1010,7 +1018,7 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
         S += (uint64_t)n[k];
         ++Kc;
     }
-    if (S >= (1ull << 32))
+    if (S_all >= (1ull << 32))
         return fail(FA_ERR_RANGE, "sum of n_k must be below 2^32");
     // plan the ranges and check the workspace before anything is enqueued:
     // the offsets kernel writes Kc * (NB + 1) list positions
@@ -1040,7 +1048,9 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
     a.counts = counts;
     a.counts_u32 = counts_dtype == FA_COUNT_U32;
     a.wsum = wsum;
-    a.mode = mode;
+    a.mode = mode == FA_WEIGHTS ? FA_WEIGHTS : FA_DELTAS;
+    a.zero_fill = mode == FA_DELTAS_ZERO_FILL;
+    a.S_all = (float)S_all;
     a.aligned = aligned16(base) && aligned16(out) && (!wsum || aligned16(wsum)) &&
                 (!counts || aligned16(counts));
     a.err = flag;

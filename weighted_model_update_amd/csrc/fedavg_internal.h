@@ -41,6 +41,8 @@ struct MaskedArgs {
     const uint8_t *present;
     const void *base;
     void *out;
+    int zero_fill; // divide by S_all (all clients' weight) instead of W_i
+    float S_all;
 };
 
 // ---------------------------------------------------------------- streaming
@@ -72,6 +74,7 @@ struct FinalizeArgs {
     void *out;
     int64_t N;
     float S;
+    int zero_fill; // partial mode: divide by S instead of the weight sums
 };
 
 // ---------------------------------------------------------------- sparse
@@ -98,6 +101,8 @@ struct SparseArgs {
     int mode;
     int aligned; // base/out/counts/wsum allow the 8-wide finalize
     int *err;
+    int zero_fill; // divide by S_all (all clients' weight) instead of W_i
+    float S_all;
 };
 
 // ---------------------------------------------------------------- launchers

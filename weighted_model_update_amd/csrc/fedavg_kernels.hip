@@ -280,7 +280,7 @@ __device__ __forceinline__ void masked_element(const MaskedArgs &a, int64_t e)
         for (int k = 0; k < a.K; ++k)
             if ((mask >> k) & 1)
                 acc = __builtin_fmaf(a.w[k], io<XDT>::load1(a.x[k], e), acc);
-        r = acc / (float)W;
+        r = acc / (a.zero_fill ? a.S_all : (float)W);
         if constexpr (MODE == MODE_DELTAS)
             r = io<BDT>::load1(a.base, e) + r;
     } else {
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
                             if (k0 + k < a.K && ((mask >> (k0 + k)) & 1))
                                 io<XDT>::fma8(xr[k], a.w[k0 + k], acc);
                     }
-                    const float Wf = (float)W;
+                    const float Wf = a.zero_fill ? a.S_all : (float)W;
                     if constexpr (MODE == MODE_DELTAS) {
                         float b[VEC];
                         io<BDT>::load8(a.base, e, b);
@@ -447,7 +447,7 @@ __device__ __forceinline__ void masked_element_lds(const MaskedArgs &a, const in
         for (int k = 0; k < a.K; ++k)
             if ((m >> k) & 1)
                 acc = __builtin_fmaf(a.w[k], io<XDT>::load1(a.x[k], e), acc);
-        r = acc / (float)W;
+        r = acc / (a.zero_fill ? a.S_all : (float)W);
         if constexpr (MODE == MODE_DELTAS)
             r = io<BDT>::load1(a.base, e) + r;
     } else {
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
             }
             float r[VEC];
             if (W[u] > 0) {
-                const float Wf = (float)W[u];
+                const float Wf = a.zero_fill ? a.S_all : (float)W[u];
                 if constexpr (MODE == MODE_DELTAS) {
                     float b[VEC];
                     io<BDT>::load8(a.base, ev[u], b);
@@ -737,12 +737,12 @@ __global__ __launch_bounds__(256) void stream_merge_scalar_kernel(const StreamAr
 }
 
 template <int BDT, int ODT, int MODE, int PARTIAL>
-__device__ __forceinline__ float finalize_one(float acc, uint32_t W, float S, float b)
+__device__ __forceinline__ float finalize_one(float acc, uint32_t W, float S, float b, int zero_fill)
 {
     if constexpr (PARTIAL) {
         if (W == 0)
             return b;
-        const float q = acc / (float)W;
+        const float q = acc / (zero_fill ? S : (float)W);
         return MODE == MODE_DELTAS ? b + q : q;
     } else {
         const float q = acc / S;
@@ -772,7 +772,7 @@ __global__ __launch_bounds__(256) void stream_finalize_vec_kernel(const Finalize
         float r[VEC];
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
-            r[j] = finalize_one<BDT, ODT, MODE, PARTIAL>(acc[j], W[j], a.S, b[j]);
+            r[j] = finalize_one<BDT, ODT, MODE, PARTIAL>(acc[j], W[j], a.S, b[j], a.zero_fill);
         io<ODT>::store8(a.out, e, r);
     }
 }
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(256) void stream_finalize_scalar_kernel(const Final
         const int64_t e = first + t;
         const uint32_t W = PARTIAL ? a.wsum[e] : 0u;
         const float b = (MODE == MODE_DELTAS || PARTIAL) ? io<BDT>::load1(a.base, e) : 0.0f;
-        io<ODT>::store1(a.out, e, finalize_one<BDT, ODT, MODE, PARTIAL>(a.acc[e], W, a.S, b));
+        io<ODT>::store1(a.out, e, finalize_one<BDT, ODT, MODE, PARTIAL>(a.acc[e], W, a.S, b, a.zero_fill));
     }
 }
 
@@ -999,7 +999,7 @@ sparse_merge_kernel(const SparseArgs a)
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
                 if (W[j] > 0) {
-                    const float q = acc[j] / (float)W[j];
+                    const float q = acc[j] / (a.zero_fill ? a.S_all : (float)W[j]);
                     r[j] = a.mode == MODE_DELTAS ? base8[j] + q : q;
                 } else {
                     r[j] = base8[j];
@@ -1031,7 +1031,7 @@ sparse_merge_kernel(const SparseArgs a)
                     const float bv = a.base[e];
                     float r = bv;
                     if (W[j] > 0) {
-                        const float q = acc[j] / (float)W[j];
+                        const float q = acc[j] / (a.zero_fill ? a.S_all : (float)W[j]);
                         r = a.mode == MODE_DELTAS ? bv + q : q;
                     }
                     a.out[e] = r;

@@ -15,7 +15,7 @@ from . import build as _build
 
 FA_OK = 0
 FA_F32, FA_BF16 = 0, 1
-FA_WEIGHTS, FA_DELTAS = 0, 1
+FA_WEIGHTS, FA_DELTAS, FA_DELTAS_ZERO_FILL = 0, 1, 2
 FA_COUNT_U8, FA_COUNT_U32 = 0, 1
 FA_OPT_BLOCKS_PER_CU, FA_OPT_MASK_VECTORS_PER_BLOCK, FA_OPT_SPARSE_BLOCKS, FA_OPT_RESIDENT_PER_CU = 1, 2, 3, 4
 FA_OPT_SPARSE_TILE = 5
@@ -110,7 +110,9 @@ def _mode(mode):
         return FA_WEIGHTS
     if mode in ("deltas", FA_DELTAS):
         return FA_DELTAS
-    raise ValueError(f"mode must be 'weights' or 'deltas', got {mode!r}")
+    if mode in ("deltas_zero_fill", FA_DELTAS_ZERO_FILL):
+        return FA_DELTAS_ZERO_FILL
+    raise ValueError(f"mode must be 'weights', 'deltas' or 'deltas_zero_fill', got {mode!r}")
 
 
 def _ptr(t):
