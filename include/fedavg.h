@@ -338,6 +338,43 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
                              size_t workspace_bytes, int *err_flag, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Per-round sample counts (host only, no device work).
+ * ------------------------------------------------------------------------ */
+
+typedef struct {
+    double w_time;   /* weight of the time cost, >= 0 */
+    double w_energy; /* weight of the energy cost, >= 0 (not both 0) */
+    double ema;      /* smoothing: s <- ema * x + (1 - ema) * s, in (0, 1] */
+    double deadband; /* keep the current counts when no count would change by
+                        more than this fraction of itself, >= 0 */
+} fa_controller;
+
+/*
+ * fedavg_controller_step -- the n_k of the next round from this round's
+ * measurements, after the measurement-based adaptive controller (gist.science
+ * summary of the adaptive data partitioning paper, section "The adaptive
+ * controller"): per-sample costs tau_i = t_i / n_i and eps_i = e_i / n_i,
+ * smoothed by an exponential moving average; a combined cost
+ *     c_i = w_time * tau_i / median(tau) + w_energy * eps_i / median(eps)
+ * (a term with weight 0 is left out; the median of an even count is the mean
+ * of the middle two); samples in inverse proportion to c_i.  These n_k are the
+ * FedAvg weights of the next round.
+ * P participants; t, e: their time and energy this round (>= 0); n: their
+ * counts this round (> 0); total: samples to hand out (>= P).
+ * tau_state, eps_state: the smoothed costs, P doubles each, read unless
+ * first_round and always written back.
+ * n_next (P): largest-remainder integers summing to total (ties to the lower
+ * index), at least 1 each (taken from the largest count, lowest index) so
+ * every cost stays measurable; but if total equals the current sum and no
+ * count would move by more than deadband * n_i, n_next = n.
+ * All arithmetic is IEEE binary64 in the order written.  Errors: FA_ERR_ARG
+ * (bad pointer, value or a zero median), FA_ERR_RANGE (total < P).
+ */
+int fedavg_controller_step(int P, const double *t, const double *e, const int64_t *n,
+                           int64_t total, const fa_controller *c, double *tau_state,
+                           double *eps_state, int first_round, int64_t *n_next);
+
+/* ------------------------------------------------------------------------
  * Client-side top-k selection (partial sharing).
  * ------------------------------------------------------------------------ */
 

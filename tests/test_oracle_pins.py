@@ -503,3 +503,42 @@ def test_hand_worked_sparse_zero_fill(case):
     ref, _, _, _ = oracle.sparse_average(idx, val, case["n"], case["N"], mode=oracle.DELTAS_ZERO_FILL,
                                          base=base)
     assert ref.tolist() == case["expect"]
+
+
+# ---------------------------------------------------------------- sample allocation
+
+import oracle.controller as controller
+
+
+@pytest.mark.parametrize("case", _golden()["controller"]["cases"], ids=lambda c: c["name"])
+def test_hand_worked_controller(case):
+    state = None
+    for rnd in case["rounds"]:
+        got, state = controller.controller_step(rnd["t"], rnd["e"], rnd["n"], case["total"], case["w_time"],
+                                                case["w_energy"], case["ema"], case["deadband"], state)
+        assert got == rnd["expect"], (case["name"], got)
+
+
+def test_controller_invariants():
+    r = np.random.default_rng(9)
+    for trial in range(200):
+        P = int(r.integers(1, 12))
+        n = r.integers(1, 5000, P).tolist()
+        t = (r.random(P) * 100 + 0.01).tolist()
+        e = (r.random(P) * 50 + 0.01).tolist()
+        total = int(r.integers(P, 100_000))
+        wt, we = float(r.random()), float(r.random())
+        got, (tau, eps) = controller.controller_step(t, e, n, total, wt, we, 1.0, 0.0)
+        assert sum(got) == total and min(got) >= 1
+        # lower cost never gets fewer samples than a higher cost (up to one
+        # sample of rounding); medians by numpy
+        mt, me = float(np.median(tau)), float(np.median(eps))
+        c = [wt * tau[i] / mt + we * eps[i] / me for i in range(P)]
+        for i in range(P):
+            for j in range(P):
+                if c[i] < c[j]:
+                    assert got[i] + 1 >= got[j]
+    # rescaling every time by the same factor changes nothing (median normalisation)
+    a, _ = controller.controller_step([3, 5, 7], [1, 1, 1], [10, 10, 10], 999, 1.0, 0.0, 1.0, 0.0)
+    b, _ = controller.controller_step([30, 50, 70], [1, 1, 1], [10, 10, 10], 999, 1.0, 0.0, 1.0, 0.0)
+    assert a == b

@@ -12,5 +12,5 @@ from .fedavg import (  # noqa: F401
     fedavg_begin, fedavg_accumulate, fedavg_finalize, fedavg_sync, fedavg_destroy,
     fedavg_accumulate_partial, fedavg_partial_info, fedavg_export_state, fedavg_resume,
     sparse_workspace_size, sparse_masked_accumulate, fedavg_checksum,
-    topk_workspace_size, topk_select, topk_count,
+    topk_workspace_size, topk_select, topk_count, SampleController,
 )

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -1059,6 +1060,112 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
 }
 
 // ============================================================ checksum
+
+// ============================================================ sample allocation
+
+namespace {
+
+double median_of(std::vector<double> v)
+{
+    std::sort(v.begin(), v.end());
+    const size_t m = v.size();
+    return m % 2 ? v[m / 2] : (v[m / 2 - 1] + v[m / 2]) / 2.0;
+}
+
+} // namespace
+
+int fedavg_controller_step(int P, const double *t, const double *e, const int64_t *n,
+                           int64_t total, const fa_controller *c, double *tau_state,
+                           double *eps_state, int first_round, int64_t *n_next)
+{
+    if (P < 1 || !t || !e || !n || !c || !tau_state || !eps_state || !n_next)
+        return fail(FA_ERR_ARG, "need P >= 1 and every array");
+    if (total < P)
+        return fail(FA_ERR_RANGE, "total=%lld is below the %d participants", (long long)total, P);
+    if (!(c->ema > 0.0 && c->ema <= 1.0) || !(c->deadband >= 0.0) || !(c->w_time >= 0.0) ||
+        !(c->w_energy >= 0.0) || (c->w_time == 0.0 && c->w_energy == 0.0))
+        return fail(FA_ERR_ARG, "need 0 < ema <= 1, deadband >= 0, weights >= 0 and not both 0");
+    int64_t nsum = 0;
+    for (int i = 0; i < P; ++i) {
+        if (n[i] <= 0 || !(t[i] >= 0.0) || !(e[i] >= 0.0))
+            return fail(FA_ERR_ARG, "participant %d: need n > 0, time and energy >= 0", i);
+        nsum += n[i];
+    }
+    // per-sample costs, smoothed
+    std::vector<double> tau(P), eps(P);
+    for (int i = 0; i < P; ++i) {
+        tau[i] = t[i] / (double)n[i];
+        eps[i] = e[i] / (double)n[i];
+        if (!first_round) {
+            tau[i] = c->ema * tau[i] + (1.0 - c->ema) * tau_state[i];
+            eps[i] = c->ema * eps[i] + (1.0 - c->ema) * eps_state[i];
+        }
+    }
+    // combined cost, each term normalised by its median
+    std::vector<double> cost(P, 0.0);
+    if (c->w_time != 0.0) {
+        const double mt = median_of(tau);
+        if (!(mt > 0.0))
+            return fail(FA_ERR_ARG, "the median time cost is zero");
+        for (int i = 0; i < P; ++i)
+            cost[i] += c->w_time * tau[i] / mt;
+    }
+    if (c->w_energy != 0.0) {
+        const double me = median_of(eps);
+        if (!(me > 0.0))
+            return fail(FA_ERR_ARG, "the median energy cost is zero");
+        for (int i = 0; i < P; ++i)
+            cost[i] += c->w_energy * eps[i] / me;
+    }
+    std::vector<double> inv(P);
+    double z = 0.0;
+    for (int i = 0; i < P; ++i) {
+        if (!(cost[i] > 0.0))
+            return fail(FA_ERR_ARG, "participant %d has a cost that is not positive", i);
+        inv[i] = 1.0 / cost[i];
+    }
+    for (int i = 0; i < P; ++i)
+        z += inv[i];
+    // samples in inverse proportion to the cost: largest remainder
+    std::vector<double> target(P);
+    std::vector<int64_t> cnt(P);
+    int64_t given = 0;
+    for (int i = 0; i < P; ++i) {
+        target[i] = (double)total * (inv[i] / z);
+        cnt[i] = (int64_t)std::floor(target[i]);
+        given += cnt[i];
+    }
+    std::vector<int> order(P);
+    for (int i = 0; i < P; ++i)
+        order[i] = i;
+    std::sort(order.begin(), order.end(), [&](int a, int b) {
+        const double fa_ = target[a] - (double)cnt[a], fb_ = target[b] - (double)cnt[b];
+        return fa_ != fb_ ? fa_ > fb_ : a < b;
+    });
+    for (int64_t j = 0; j < total - given && j < P; ++j)
+        cnt[order[j]] += 1;
+    // everyone keeps a sample, taken from the largest count (lowest index)
+    for (int i = 0; i < P; ++i) {
+        while (cnt[i] < 1) {
+            int big = 0;
+            for (int q = 1; q < P; ++q)
+                if (cnt[q] > cnt[big])
+                    big = q;
+            cnt[big] -= 1;
+            cnt[i] += 1;
+        }
+    }
+    // deadband: keep the current counts when every change is within it
+    bool keep = nsum == total;
+    for (int i = 0; i < P && keep; ++i)
+        keep = std::fabs((double)(cnt[i] - n[i])) <= c->deadband * (double)n[i];
+    for (int i = 0; i < P; ++i) {
+        n_next[i] = keep ? n[i] : cnt[i];
+        tau_state[i] = tau[i];
+        eps_state[i] = eps[i];
+    }
+    return ok();
+}
 
 // ============================================================ top-k selection
 

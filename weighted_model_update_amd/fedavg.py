@@ -32,7 +32,8 @@ EXPORTS = [
     "fedavg_abi_version", "fedavg_last_error", "fedavg_aggregate", "fedavg_workspace_size",
     "fedavg_begin", "fedavg_accumulate", "fedavg_finalize", "fedavg_sync", "fedavg_destroy",
     "fedavg_accumulate_partial", "fedavg_partial_info", "fedavg_state_size", "fedavg_export_state",
-    "fedavg_resume", "topk_workspace_size", "topk_select", "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
+    "fedavg_resume", "topk_workspace_size", "topk_select", "fedavg_controller_step",
+    "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
 ]
 
 
@@ -80,6 +81,7 @@ def load(build_if_missing=True):
         "sparse_masked_accumulate": ([i32, P, P, P, P, i64, i32, P, P, P, i32, P, P, sz, P, P], i32),
         "fedavg_checksum": ([P, i64, i32, P, P], i32),
         "topk_workspace_size": ([i64, P], i32),
+        "fedavg_controller_step": ([i32, P, P, P, i64, P, P, P, i32, P], i32),
         "topk_select": ([P, i32, i64, i64, P, P, P, sz, P], i32),
         "fedavg_set_option": ([i32, i64], i32),
     }
@@ -545,3 +547,38 @@ def topk_count(N, frac):
     from fractions import Fraction
     import math
     return int(math.floor(Fraction(str(frac)) * int(N)))
+
+
+# ------------------------------------------------------------------ sample allocation
+
+class _Controller(ctypes.Structure):
+    _fields_ = [("w_time", ctypes.c_double), ("w_energy", ctypes.c_double),
+                ("ema", ctypes.c_double), ("deadband", ctypes.c_double)]
+
+
+class SampleController:
+    """Next-round sample counts n_k (the FedAvg weights) from each
+    participant's measured time and energy (fedavg_controller_step)."""
+
+    def __init__(self, P, w_time=1.0, w_energy=0.0, ema=0.5, deadband=0.05):
+        self.P = int(P)
+        self.params = _Controller(float(w_time), float(w_energy), float(ema), float(deadband))
+        self.tau = (ctypes.c_double * self.P)()
+        self.eps = (ctypes.c_double * self.P)()
+        self.first = True
+
+    def step(self, t, e, n, total):
+        P = self.P
+        if not (len(t) == len(e) == len(n) == P):
+            raise ValueError(f"need {P} times, energies and counts")
+        out = (ctypes.c_int64 * P)()
+        rc = load().fedavg_controller_step(P, (ctypes.c_double * P)(*map(float, t)),
+                                           (ctypes.c_double * P)(*map(float, e)), _i64_array(n),
+                                           int(total), ctypes.byref(self.params), self.tau, self.eps,
+                                           int(self.first), out)
+        _check(rc)
+        self.first = False
+        return [int(v) for v in out]
+
+    def state(self):
+        return list(self.tau), list(self.eps)
