@@ -285,8 +285,8 @@ def bench_hierarchical(silos=4):
 
 def bench_topk(steps=10, warmup=2):
     """Client-side top-10% selection over one 10^9-parameter fp32 update
-    (Laplace(0, 1e-3) deltas): the radix-select passes, tile counts, scan and
-    ordered compaction, timed as one call.  Algorithmic bytes: one read of the
+    (Laplace(0, 1e-3) deltas): radix select, candidate split, tile counts,
+    scan and ordered compaction, timed as one call.  Algorithmic bytes: one read of the
     update (4 B per parameter) and the kept (int64 index, fp32 value) pairs."""
     import torch
     import synth.device as sd
@@ -306,9 +306,10 @@ def bench_topk(steps=10, warmup=2):
     free_gpu()
     return {"N": N, "k": k, "dtype": "f32", "ms_per_call": ms, "algo_bytes": algo,
             "hbm_gbs": algo / (ms * 1e-3) / 1e9, "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "params_per_s": N / (ms * 1e-3), "input_passes": 5,
-            "note": "three radix-select histogram passes, a tile-count pass and the compaction pass "
-                    "each read the update once"}
+            "params_per_s": N / (ms * 1e-3), "input_passes": 3,
+            "note": "the first radix-select histogram, the split into candidates and the ordered "
+                    "write each read the update once; the later digits and tile counts read "
+                    "only the candidates"}
 
 
 def bench_sparse(steps=10, warmup=2):
@@ -406,15 +407,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    help="comma list of: dense,dense_small,adapter,streaming,sparse,cpu,copycal "
+                    help="comma list of: dense,dense_small,adapter,streaming,sparse,topk,hierarchical,cpu,copycal "
                          "(default all but copycal)")
     ap.add_argument("--stream-clients", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the aggregation shards by parameter range, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: every output "
+              f"parameter depends only on the same parameter of each client, so more GPUs would each "
+              f"run these kernels on one contiguous slice of the parameters", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -422,7 +424,8 @@ def main():
     fa.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     only = set(args.only.split(",")) if args.only != "all" else {"dense", "dense_small", "adapter",
-                                                                 "streaming", "sparse", "cpu"}
+                                                                 "streaming", "sparse", "topk",
+                                                                 "hierarchical", "cpu"}
     if args.no_cpu_baseline:
         only.discard("cpu")
 
