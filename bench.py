@@ -46,8 +46,17 @@ def log(msg):
 
 
 def kernel_source_sha():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of the source the headline kernel is built from: the kernels
+    file up to the end of its resident-dense section (shared load/store
+    helpers and the dense kernels) and the launch code from the residency
+    helper through the dense launcher.  Edits elsewhere in the file leave it
+    unchanged."""
+    with open(KERNEL_SOURCE) as f:
+        text = f.read()
+    head = text[:text.index("// ================================================================ per-segment masks")]
+    i0 = text.index("// Streaming kernels over HBM run fastest with few resident waves per CU")
+    i1 = text.index("template <int X, int O, int B, int M> struct DenseRun")
+    return hashlib.sha256((head + text[i0:i1]).encode()).hexdigest()
 
 
 def timed(fn, steps, warmup):

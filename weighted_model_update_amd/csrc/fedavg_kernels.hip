@@ -840,11 +840,18 @@ __global__ __launch_bounds__(256) void sparse_offsets_kernel(const SparseArgs a)
 // start the entry before the range, read once per workgroup -- and at the
 // range's end every cursor must have reached its end offset.
 //
-// Eight waves per SIMD for tiles of up to 512 lanes: the merge is bound by
-// how many batches are in flight, and the scalar registers would otherwise
-// cap residency at seven.
+// Eight waves per SIMD for the 256- and 512-lane tiles with one mask word
+// (the measured configurations): the merge is bound by how many batches are
+// in flight, and the scalar registers would otherwise cap residency at seven.
+// Two mask words take more LDS than eight resident workgroups leave.
 template <int MW, int SP_TILE, int SP_THREADS>
-__global__ __launch_bounds__(SP_THREADS, SP_THREADS <= 512 ? 2048 / SP_THREADS : 1) void
+constexpr int sparse_min_blocks()
+{
+    return (MW == 1 && (SP_THREADS == 256 || SP_THREADS == 512)) ? 2048 / SP_THREADS : 1;
+}
+
+template <int MW, int SP_TILE, int SP_THREADS>
+__global__ __launch_bounds__(SP_THREADS, (sparse_min_blocks<MW, SP_TILE, SP_THREADS>())) void
 sparse_merge_kernel(const SparseArgs a)
 {
     static_assert(SP_TILE == SP_THREADS * VEC, "one 8-parameter group per lane at finalize");
