@@ -999,7 +999,7 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
 
     fa::SparseArgs a;
     std::memset(&a, 0, sizeof a);
-    uint64_t S = 0, S_all = 0; // over the clients that sent entries / over all with n_k > 0
+    uint64_t S_all = 0; // every client with n_k > 0, also one whose list is empty
     int Kc = 0;
     for (int k = 0; k < K; ++k) {
         if (n[k] < 0 || n[k] > FA_MAX_WEIGHT)
@@ -1016,7 +1016,6 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
         a.nnz[Kc] = nnz[k];
         a.w[Kc] = (float)n[k];
         a.wi[Kc] = (uint32_t)n[k];
-        S += (uint64_t)n[k];
         ++Kc;
     }
     if (S_all >= (1ull << 32))
