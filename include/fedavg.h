@@ -378,8 +378,11 @@ int fedavg_controller_step(int P, const double *t, const double *e, const int64_
  * Client-side top-k selection (partial sharing).
  * ------------------------------------------------------------------------ */
 
-/* Device workspace bytes topk_select needs for N values. */
-int topk_workspace_size(int64_t N, size_t *bytes);
+/* Device workspace bytes topk_select needs to keep k of N values of dtype
+   (it grows with k: below N/4 kept fp32 values, N/8 bf16, it holds a
+   staging copy of the entries near and above the threshold).  FA_ERR_RANGE
+   unless 0 <= k <= N. */
+int topk_workspace_size(fa_dtype dtype, int64_t N, int64_t k, size_t *bytes);
 
 /*
  * topk_select -- the client's side of partial sharing: of its update x
@@ -392,9 +395,13 @@ int topk_workspace_size(int64_t N, size_t *bytes);
  * int64[k]) in increasing order and their values, widened to fp32, to val_out
  * (device float[k]): exactly the per-client lists sparse_masked_accumulate
  * takes.  The result is unique, hence deterministic.
- * k == 0 returns FA_OK with no work; k > N is FA_ERR_RANGE.  workspace:
- * device, 16-byte aligned, topk_workspace_size(N) bytes, overwritten.
- * Outputs must not overlap x.  Asynchronous on `stream`.
+ * k == 0 returns FA_OK with no work; k > N or N > 2^39 is FA_ERR_RANGE.  workspace:
+ * device, 16-byte aligned, topk_workspace_size(dtype, N, k) bytes,
+ * overwritten.  Outputs must not overlap x.  Asynchronous on `stream`.
+ * The threshold is bounded first from a sample of about 2^20 values, so that
+ * the update is read once; when the bound fails (or FA_OPT_TOPK_SAMPLED is
+ * 0) the call finishes with three passes over it instead, on the device and
+ * with the same result.
  */
 int topk_select(const void *x, fa_dtype dtype, int64_t N, int64_t k, int64_t *idx_out,
                 float *val_out, void *workspace, size_t workspace_bytes, void *stream);
@@ -428,9 +435,12 @@ typedef enum {
     FA_OPT_RESIDENT_PER_CU = 4,        /* resident dense kernel: workgroups of
                                           256 threads resident per CU
                                           (default 3; 0 = hardware limit) */
-    FA_OPT_SPARSE_TILE = 5             /* sparse merge: parameters per LDS tile,
+    FA_OPT_SPARSE_TILE = 5,            /* sparse merge: parameters per LDS tile,
                                           512, 1024, 2048 (default), 4096 or
                                           8192 */
+    FA_OPT_TOPK_SAMPLED = 6            /* top-k: 1 (default) bounds the
+                                          threshold from a sample first; 0
+                                          always takes the three-pass path */
 } fa_option;
 
 /* Set one option; FA_ERR_ARG for an unknown option, FA_ERR_RANGE for a value

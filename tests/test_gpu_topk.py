@@ -17,6 +17,15 @@ pytestmark = pytest.mark.gpu
 DT = {"f32": oracle.F32, "bf16": oracle.BF16}
 
 
+@pytest.fixture(params=[1, 0], ids=["sampled", "three_pass"])
+def path(request):
+    """Run a test on the sampled path (the default: the threshold bounded
+    from a sample, one read of the update) and on the three-pass path."""
+    fa.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, request.param)
+    yield request.param
+    fa.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 1)
+
+
 def run_topk(x, dt, k, misalign=False):
     """x: float32 array or uint16 bf16 bits.  misalign: place the input one
     element past a 16-byte boundary (the unvectorised path)."""
@@ -49,14 +58,14 @@ def same(got, want):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1, 7, 4095, 8192, 8193, 100_003, 1_000_000])
-def test_topk_matches_oracle(dt, N):
+def test_topk_matches_oracle(dt, N, path):
     x = laplace(N, N, dt)
     for k in sorted({0, 1, N // 10, N // 2, N - 1, N}):
         same(run_topk(x, dt, k), expect(x, dt, k))
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_threshold_inside_a_tie_group(dt):
+def test_threshold_inside_a_tie_group(dt, path):
     # few distinct magnitudes: the k-th key sits inside a large group of
     # equal keys spread over many tiles, so the kept ties are the lowest
     # indices across tiles
@@ -69,7 +78,7 @@ def test_threshold_inside_a_tie_group(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_candidate_overflow_falls_back_to_the_whole_input(dt):
+def test_candidate_overflow_falls_back_to_the_whole_input(dt, path):
     # three magnitudes: the threshold bin holds about a third of the input,
     # more than the candidate buffer (N/16 + 65536 entries) takes
     r = np.random.default_rng(8)
@@ -80,7 +89,7 @@ def test_candidate_overflow_falls_back_to_the_whole_input(dt):
         same(run_topk(x, dt, k), expect(x, dt, k))
 
 
-def test_special_values_and_signed_zeros():
+def test_special_values_and_signed_zeros(path):
     r = np.random.default_rng(4)
     N = 50_000
     x = r.standard_normal(N).astype(np.float32)
@@ -96,11 +105,46 @@ def test_special_values_and_signed_zeros():
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_unaligned_input(dt):
+def test_unaligned_input(dt, path):
     N = 40_001
     x = laplace(7, N, dt)
     for k in (1, 4000, 40_000):
         same(run_topk(x, dt, k, misalign=True), expect(x, dt, k))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("sampled_small", [True, False])
+def test_a_misleading_sample_falls_back_to_the_full_path(dt, sampled_small):
+    """The sample takes every stride-th 16-byte vector of the update (2^20
+    keys in all).  Give exactly those vectors magnitudes unlike the rest's:
+    the sampled range then misses the threshold (far too many keys above it,
+    or too few at or above its floor), the check fails and the call finishes
+    on the three-pass path -- with the same result."""
+    N = 1 << 22
+    V = 4 if dt == "f32" else 8
+    stride = (N // V) // ((1 << 20) // V)
+    r = np.random.default_rng(12 + sampled_small)
+    in_sample = (np.arange(N) // V) % stride == 0
+    small = r.laplace(0.0, 1e-6, N).astype(np.float32)
+    large = r.laplace(0.0, 1.0, N).astype(np.float32)
+    x = np.where(in_sample == sampled_small, small, large)
+    x = synth.bf16_bits_from_f32(x) if dt == "bf16" else x
+    for k in (N // 10, N // 40 + 3):
+        same(run_topk(x, dt, k), expect(x, dt, k))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_layered_update(dt, path):
+    """An update made of layers of very different scales and sizes (a few
+    small layers dominate the top entries): the kept set crosses layers."""
+    r = np.random.default_rng(61)
+    sizes = r.integers(1, 200_000, 40)
+    scales = 10.0 ** r.uniform(-6, 0, 40)
+    x = np.concatenate([r.laplace(0.0, s, n) for s, n in zip(scales, sizes)]).astype(np.float32)
+    x = synth.bf16_bits_from_f32(x) if dt == "bf16" else x
+    N = x.shape[0]
+    for k in (N // 100, N // 20, N // 5):
+        same(run_topk(x, dt, k), expect(x, dt, k))
 
 
 def test_topk_feeds_the_sparse_merge():

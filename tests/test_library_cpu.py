@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import weighted_model_update_amd as fa
 
@@ -64,7 +65,23 @@ def test_host_side_argument_errors_need_no_device():
                                         None, P(1 << 24), 8, None, None) == -8
     assert lib.fedavg_set_option(99, 1) == -1
     assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 70000) == -3
+    assert lib.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 2) == -3
+    b = ctypes.c_size_t(0)
+    assert lib.topk_workspace_size(0, 100, 101, ctypes.byref(b)) == -3   # k > N
+    assert lib.topk_workspace_size(7, 100, 10, ctypes.byref(b)) == -2    # unknown dtype
+    assert lib.topk_workspace_size(0, 100, 10, None) == -1
     assert lib.fedavg_checksum(None, 10, 0, None, None) == -1
+
+
+def test_topk_workspace_holds_a_staging_copy_only_while_it_pays():
+    """Up to N/4 kept fp32 values (N/8 bf16) the workspace grows by 8 bytes
+    per kept entry for the staging copy; beyond that it does not grow."""
+    N = 10 ** 6
+    f = [fa.topk_workspace_size(N, k, torch.float32) for k in (1, 1001, N // 4 - 1, N // 4, N)]
+    assert abs((f[1] - f[0]) - 8 * 1000) <= 8 * 256     # staging is carved in 256 regions
+    assert f[3] < f[2] and f[3] == f[4]
+    h = [fa.topk_workspace_size(N, k, torch.bfloat16) for k in (N // 8 - 1, N // 8)]
+    assert h[1] < h[0] and h[1] == f[4]
 
 
 def test_workspace_sizes_do_not_depend_on_the_number_of_clients():

@@ -291,6 +291,11 @@ int fedavg_set_option(int option, int64_t value)
             return fail(FA_ERR_RANGE, "sparse tile must be 512, 1024, 2048, 4096 or 8192");
         g_sparse_tile = value;
         return ok();
+    case FA_OPT_TOPK_SAMPLED:
+        if (value != 0 && value != 1)
+            return fail(FA_ERR_RANGE, "top-k sampled path must be 0 or 1");
+        fa::topk_set_sampled((int)value);
+        return ok();
     case FA_OPT_SPARSE_BLOCKS:
         if (value < 0 || value > SPARSE_MAX_BLOCKS)
             return fail(FA_ERR_RANGE, "sparse blocks must be in [0, %lld]",
@@ -1168,11 +1173,15 @@ int fedavg_controller_step(int P, const double *t, const double *e, const int64_
 
 // ============================================================ top-k selection
 
-int topk_workspace_size(int64_t N, size_t *bytes)
+int topk_workspace_size(fa_dtype dtype, int64_t N, int64_t k, size_t *bytes)
 {
-    if (N < 0 || !bytes)
-        return fail(FA_ERR_ARG, "need N >= 0 and a result pointer");
-    *bytes = fa::topk_workspace_bytes(N);
+    if (!bytes)
+        return fail(FA_ERR_ARG, "need a result pointer");
+    if (!dtype_ok(dtype))
+        return fail(FA_ERR_DTYPE, "dtype must be FA_F32 or FA_BF16");
+    if (N < 0 || k < 0 || k > N)
+        return fail(FA_ERR_RANGE, "need 0 <= k <= N (k=%lld, N=%lld)", (long long)k, (long long)N);
+    *bytes = fa::topk_workspace_bytes(dtype, N, k);
     return ok();
 }
 
@@ -1187,9 +1196,9 @@ int topk_select(const void *x, fa_dtype dtype, int64_t N, int64_t k, int64_t *id
         return ok();
     if (!x || !idx_out || !val_out || !workspace)
         return fail(FA_ERR_ARG, "x, idx_out, val_out and workspace are required");
-    if ((N + fa::TK_TILE - 1) / fa::TK_TILE > 0x7fffffffll)
-        return fail(FA_ERR_RANGE, "N=%lld is too large", (long long)N);
-    const size_t need = fa::topk_workspace_bytes(N);
+    if (N > (1ll << 39)) // the per-region reservation counters hold 32-bit fields
+        return fail(FA_ERR_RANGE, "N=%lld is too large (at most 2^39)", (long long)N);
+    const size_t need = fa::topk_workspace_bytes(dtype, N, k);
     if (workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0 ||

@@ -124,7 +124,8 @@ int sparse_resident_blocks_per_cu(int tile);
 hipError_t launch_sparse(const SparseArgs &a, hipStream_t s);
 // client-side top-k selection (topk.hip)
 constexpr int TK_TILE = 8192; // elements per tile of the count and write passes
-size_t topk_workspace_bytes(int64_t N);
+size_t topk_workspace_bytes(int dt, int64_t N, int64_t k);
+void topk_set_sampled(int on); // 0: always the full three-pass path
 hipError_t launch_topk(const void *x, int dt, int64_t N, int64_t k, int64_t *idx_out,
                        float *val_out, void *ws, int cus, hipStream_t s);
 hipError_t launch_checksum(const void *buf, int64_t count, int dt, uint64_t *hash,

@@ -9,25 +9,34 @@
 // output is the k chosen indices in increasing order, with their values as
 // fp32 -- the (index, value) list the sparse merge takes.
 //
-// Exact radix select over the 31-bit key, most significant digit first, in
-// digits of 11, 11 and 9 bits (bf16 keys have 15 bits: two digits decide
-// them).  Three passes read the whole input:
-//   1. a histogram of the top digit (LDS histograms, one global add per bin
-//      and workgroup), after which one workgroup picks the digit b1 that
-//      holds the k-th largest key;
-//   2. per tile of TK_TILE elements: the keys above bin b1 are counted, and
-//      the keys inside it -- the candidates, a few per cent of the input for
-//      smooth data -- are compacted into a buffer as (key, position in tile);
-//   3. after the remaining digits are chosen from histograms of the
-//      candidates only, and each tile's counts of keys above and equal to the
-//      threshold T come from its candidates, one workgroup scans the counts
-//      into output offsets and each tile's share of the ties (the lowest
-//      indices), and each tile writes its kept entries in index order.
-// If the candidates outgrow their buffer (heavily tied data), a flag in the
-// workspace sends every later kernel down the same steps over the whole
-// input instead; the result is the same.  No workgroup ever waits on
-// another.
+// The k-th largest key T is found exactly by radix select, most significant
+// digit first, in digits of 11, 11 and 9 bits (bf16 keys have 15 bits: two
+// digits decide them); each tile of TK_TILE elements then writes its kept
+// entries from an output offset given by a scan of the per-tile counts.
+//
+// Sampled path (the usual one).  A systematic sample of about 2^20 keys
+// bounds T from both sides: K_lo and K_hi are the sample's order statistics
+// a wide margin (8 binomial standard deviations plus 32) below and above
+// T's expected rank, rounded outwards to 22-bit key prefixes.  One pass over
+// the update then, per tile, counts the keys above K_hi, compacts the keys
+// inside [K_lo, K_hi] -- the candidates, well under one per cent of the input
+// for smooth data -- and, when k is small enough for it to pay, copies every
+// key at or above K_lo with its position into the tile's segment of a
+// staging buffer, in index order.  One workgroup checks that the range holds
+// T (fewer than k keys above K_hi, at least k at or above K_lo, no buffer
+// overflowed); the digits of T are chosen from histograms of the candidates
+// only, and the ordered write reads the staging segments (or, without them,
+// the update).  The update is read once (twice without staging).
+//
+// Full path.  When the check fails, the sample cannot bound T (k near N) or
+// the caller asks for it, a flag in the workspace sends every later kernel
+// down three passes over the update: a histogram of the top digit; a split
+// that counts the keys above T's top-digit bin and compacts those inside it
+// as candidates (or, when they outgrow their buffer, a second flag that makes
+// the later kernels use the whole input again); and the ordered write.  The
+// result is the same on both paths.  No workgroup ever waits on another.
 #include <hip/hip_runtime.h>
+#include <math.h>
 
 #include "fedavg_internal.h"
 
@@ -42,62 +51,108 @@ constexpr int TT_WAVES = TT_THREADS / 64;
 constexpr int TK_MAX_BINS = 2048;
 constexpr int TK_SELECT_THREADS = 1024;
 constexpr int TK_TOP_SHIFT = 20; // first digit: key bits 30..20
+constexpr int TK_SUB_SHIFT = 9;  // second digit: key bits 19..9
+constexpr int TK_REGIONS = 256;  // candidate / staging regions, each with its own counter
+constexpr int TK_CSTRIDE = 16;   // region counters lie 128 bytes apart: atomics on
+                                 // different regions never share a cache line
+constexpr int TK_STAGE = 2048;   // entries a per-tile kernel stages in LDS
+constexpr int TK_SCAN_CHUNK = 4 * 256; // tiles per workgroup of the offset scan
+constexpr int64_t TK_SAMPLE_KEYS = 1 << 20;
 
 using u32x2 = __attribute__((ext_vector_type(2))) unsigned int;
 using u32x4 = __attribute__((ext_vector_type(4))) unsigned int;
 
-constexpr int TK_REGIONS = 256; // candidate regions, each with its own counter
-
 struct TopkState {
-    uint32_t prefix;             // key bits chosen so far (the threshold T at the end)
-    uint32_t overflow;           // candidates did not fit: use the whole input
-    int64_t rank;                // keys matching `prefix` still to be kept
+    uint32_t prefix;   // key bits chosen so far (the threshold T at the end)
+    uint32_t overflow; // full path: candidates did not fit, use the whole input
+    int64_t rank;      // keys matching `prefix` still to be kept
+    uint32_t fast;     // the sampled range held T: the sampled path is on
+    uint32_t ranged;   // the sample gave a range [klo, khi]
+    uint32_t fov;      // sampled path: a candidate or staging region overflowed
+    uint32_t klo, khi;
+    uint32_t sbin_hi, sbin_lo;  // sample: top-digit bins of the two order statistics
+    int64_t srank_hi, srank_lo; // and their ranks inside those bins
 };
+static_assert(sizeof(TopkState) <= 256, "state slot");
 
 // Where the pieces of the workspace live.
 struct TopkWs {
-    unsigned long long *hist;
+    unsigned long long *hist; // 2 x TK_MAX_BINS
     TopkState *st;
-    int64_t *off;        // per tile: first output position
-    uint32_t *gt, *eq;   // per tile: keys above / equal to T
-    uint32_t *take;      // per tile: ties kept
-    uint32_t *def;       // per tile: keys above bin b1
-    uint32_t *ccnt;      // per tile: candidates
-    unsigned long long *coff; // per tile: first candidate
-    u32x2 *cand;         // (key, position in tile), TK_REGIONS regions of rcap
-    unsigned long long *rcount; // per region: candidates reserved
-    int64_t rcap;        // candidates per region
+    unsigned long long *rcnt;   // per region, TK_CSTRIDE apart: (staging entries << 32) |
+                                // candidates reserved (the full path: candidates only)
+    int64_t *off;               // per tile: first output position
+    unsigned long long *coff;   // per tile: first candidate
+    unsigned long long *toff;   // per tile: first staging entry
+    uint32_t *gt, *eq;          // per tile: keys above / equal to T
+    uint32_t *take;             // per tile: ties kept
+    uint32_t *def;              // per tile: keys above the candidates
+    uint32_t *ccnt;             // per tile: candidates
+    uint32_t *tcnt;             // per tile: staging entries
+    int64_t *ch_eq, *ch_gt;     // per scan chunk: sums of eq and gt
+    int64_t *ch_ties, *ch_off;  // per scan chunk: ties before it, first output position
+    u32x2 *cand;                // (key, position in tile), TK_REGIONS regions of rcap
+    int64_t rcap;
+    u32x2 *stage;               // (raw bits, position in tile), TK_REGIONS regions of tcap
+    int64_t tcap;
 };
 
 __host__ __device__ constexpr int64_t round4(int64_t n) { return (n + 3) / 4 * 4; }
 
-// Candidates per region: the regions together hold N/16 + 64Ki entries.
-int64_t region_capacity(int64_t N) { return (N / 16 + 65536 + TK_REGIONS - 1) / TK_REGIONS; }
+// Staging pays when writing and re-reading 8 bytes per kept entry costs less
+// than a second read of the update: k < N/4 for fp32, k < N/8 for bf16.
+bool staging_pays(int64_t N, int64_t k, int dt) { return dt == DT_F32 ? 4 * k < N : 8 * k < N; }
 
-TopkWs carve(void *ws, int64_t N)
+struct Sizes {
+    int64_t nt, ntp, nch, rcap, tcap;
+    size_t bytes;
+};
+
+Sizes sizes_of(int64_t N, int64_t k, int dt)
 {
-    const int64_t nt = (N + TK_TILE - 1) / TK_TILE;
-    const int64_t ntp = round4(nt);
+    Sizes s;
+    s.nt = (N + TK_TILE - 1) / TK_TILE;
+    s.ntp = round4(s.nt);
+    s.nch = (s.nt + TK_SCAN_CHUNK - 1) / TK_SCAN_CHUNK;
+    // candidates: N/16 + 64Ki in all; staging: k + N/64 + 64Ki in all
+    s.rcap = (N / 16 + 65536 + TK_REGIONS - 1) / TK_REGIONS;
+    s.tcap = staging_pays(N, k, dt) ? (k + N / 64 + 65536 + TK_REGIONS - 1) / TK_REGIONS : 0;
+    s.bytes = (size_t)2 * TK_MAX_BINS * 8 + 256 + (size_t)TK_REGIONS * TK_CSTRIDE * 8 +
+              (size_t)s.ntp * (3 * 8 + 6 * 4) + (size_t)s.nch * 4 * 8 +
+              (size_t)TK_REGIONS * (s.rcap + s.tcap) * 8;
+    return s;
+}
+
+TopkWs carve(void *ws, const Sizes &s)
+{
     char *w = static_cast<char *>(ws);
     TopkWs p;
     p.hist = reinterpret_cast<unsigned long long *>(w);
-    w += TK_MAX_BINS * 8;
+    w += 2 * TK_MAX_BINS * 8;
     p.st = reinterpret_cast<TopkState *>(w);
     w += 256;
-    p.rcount = reinterpret_cast<unsigned long long *>(w);
-    w += TK_REGIONS * 8;
+    p.rcnt = reinterpret_cast<unsigned long long *>(w);
+    w += TK_REGIONS * TK_CSTRIDE * 8;
     p.off = reinterpret_cast<int64_t *>(w);
-    w += ntp * 8;
-    p.coff = reinterpret_cast<unsigned long long *>(w);
-    w += ntp * 8;
-    p.gt = reinterpret_cast<uint32_t *>(w);
-    p.eq = p.gt + ntp;
-    p.take = p.eq + ntp;
-    p.def = p.take + ntp;
-    p.ccnt = p.def + ntp;
-    w += ntp * 4 * 5;
+    p.coff = reinterpret_cast<unsigned long long *>(p.off + s.ntp);
+    p.toff = p.coff + s.ntp;
+    w += s.ntp * 3 * 8;
+    p.gt = reinterpret_cast<uint32_t *>(w); // 16-byte aligned: the scan loads 4 at a time
+    p.eq = p.gt + s.ntp;
+    p.take = p.eq + s.ntp;
+    p.def = p.take + s.ntp;
+    p.ccnt = p.def + s.ntp;
+    p.tcnt = p.ccnt + s.ntp;
+    w += s.ntp * 6 * 4;
+    p.ch_eq = reinterpret_cast<int64_t *>(w);
+    p.ch_gt = p.ch_eq + s.nch;
+    p.ch_ties = p.ch_gt + s.nch;
+    p.ch_off = p.ch_ties + s.nch;
+    w += s.nch * 4 * 8;
     p.cand = reinterpret_cast<u32x2 *>(w);
-    p.rcap = region_capacity(N);
+    p.rcap = s.rcap;
+    p.stage = p.cand + TK_REGIONS * s.rcap;
+    p.tcap = s.tcap;
     return p;
 }
 
@@ -141,99 +196,531 @@ template <> struct Vec<DT_BF16> {
 
 // A whole tile in registers: thread t holds, for round j, the V elements
 // starting at tile0 + (j * TT_THREADS + t) * V (so each round's loads are
-// coalesced); `valid` masks elements past N.
+// coalesced).  Elements past N read as 0 (key 0); in index order they come
+// after every element of the tile that exists, so a kernel needs no
+// per-element bounds test: it takes the pad() of them out of any count whose
+// predicate key 0 meets, and bounds its writes by the corrected count.  The
+// thread index is passed through an empty asm statement so that a loop over
+// tiles recomputes per-element offsets (one add each) rather than keeping
+// them all in registers.
 template <int DT> struct Tile {
     static constexpr int V = Vec<DT>::N;
     static constexpr int ROUNDS = TK_TILE / (TT_THREADS * V);
     uint32_t b[ROUNDS][V];
-    __device__ static int64_t first(int64_t tile0, int j) { return tile0 + (int64_t)(j * TT_THREADS + threadIdx.x) * V; }
+    uint32_t t;   // this thread's index
+    uint32_t lim; // elements of the tile below N
+    __device__ uint32_t local(int j, int q) const { return (uint32_t)(j * TT_THREADS + t) * V + q; }
+    __device__ uint32_t pad() const { return (uint32_t)TK_TILE - lim; }
+    // Before a second pass over the tile: the values pass through empty asm
+    // statements, so the pass derives keys and compares from the raw bits
+    // again rather than keeping the first pass's results live.
+    __device__ void reuse()
+    {
+#pragma unroll
+        for (int j = 0; j < ROUNDS; ++j)
+#pragma unroll
+            for (int q = 0; q < V; ++q)
+                asm volatile("" : "+v"(b[j][q]));
+        asm volatile("" : "+v"(t));
+    }
     __device__ void load(const void *x, int64_t N, bool vec_ok, int64_t tile0)
     {
-        if (vec_ok && tile0 + TK_TILE <= N) {
+        t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        const int64_t left = N - tile0;
+        lim = left < TK_TILE ? (uint32_t)left : (uint32_t)TK_TILE;
+        if (vec_ok && lim == (uint32_t)TK_TILE) {
 #pragma unroll
             for (int j = 0; j < ROUNDS; ++j)
-                Vec<DT>::load(x, first(tile0, j) / V, b[j]);
+                Vec<DT>::load(x, tile0 / V + (j * TT_THREADS + t), b[j]);
         } else {
 #pragma unroll
             for (int j = 0; j < ROUNDS; ++j)
 #pragma unroll
                 for (int q = 0; q < V; ++q) {
-                    const int64_t e = first(tile0, j) + q;
-                    b[j][q] = e < N ? bits_at<DT>(x, e) : 0u;
+                    const uint32_t l = local(j, q);
+                    b[j][q] = l < lim ? bits_at<DT>(x, tile0 + l) : 0u;
                 }
         }
     }
-    __device__ static bool in(int64_t N, int64_t tile0, int j, int q) { return first(tile0, j) + q < N; }
 };
 
-// Workgroup-wide exclusive scan of one value per thread (TT_THREADS
-// threads); returns the prefix, and the total through `total`.
-__device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t *s_wave, uint32_t &total)
+// Inclusive scan over the 64 lanes of a wave with DPP adds: Hillis-Steele
+// inside each row of 16 lanes (row_shr 1, 2, 4, 8; lanes with no source read
+// 0), then lane 15 of rows 0 and 2 is added into rows 1 and 3 (row_bcast:15)
+// and lane 31 into rows 2 and 3 (row_bcast:31).  Lanes a row mask leaves out
+// read the `old` operand, 0.  Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t inc = v;
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(inc, d, 64);
-        if (lane >= d)
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true); // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true); // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true); // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true); // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+    return v;
+}
+
+// Workgroup-wide exclusive scan of one 64-bit value per thread (THREADS
+// threads); returns the prefix, and the total through `total`.  Ends with a
+// barrier, so s_tmp may be reused at once.
+template <int THREADS>
+__device__ int64_t block_exclusive_scan64(int64_t v, int64_t *s_tmp, int64_t &total)
+{
+    constexpr int WAVES = THREADS / 64;
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    int64_t inc = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t o = __shfl_up(inc, off, 64);
+        if (lane >= off)
             inc += o;
     }
     if (lane == 63)
-        s_wave[wave] = inc;
+        s_tmp[wave] = inc;
     __syncthreads();
-    uint32_t before = 0, sum = 0;
-#pragma unroll
-    for (int w = 0; w < TT_WAVES; ++w) {
-        const uint32_t s = s_wave[w];
-        before += w < wave ? s : 0u;
-        sum += s;
+    if (t == 0) {
+        int64_t run = 0;
+        for (int u = 0; u < WAVES; ++u) {
+            const int64_t s = s_tmp[u];
+            s_tmp[u] = run;
+            run += s;
+        }
+        s_tmp[WAVES] = run;
     }
     __syncthreads();
-    total = sum;
-    return before + inc - v;
+    const int64_t ex = s_tmp[wave] + inc - v;
+    total = s_tmp[WAVES];
+    __syncthreads();
+    return ex;
 }
 
 __global__ void topk_init_kernel(TopkWs w, int64_t k)
 {
-    for (int b = threadIdx.x; b < TK_MAX_BINS; b += blockDim.x)
+    for (int b = threadIdx.x; b < 2 * TK_MAX_BINS; b += blockDim.x)
         w.hist[b] = 0ull;
-    for (int r = threadIdx.x; r < TK_REGIONS; r += blockDim.x)
-        w.rcount[r] = 0ull;
+    for (int r = threadIdx.x; r < TK_REGIONS; r += blockDim.x) {
+        w.rcnt[r * TK_CSTRIDE] = 0ull;
+    }
     if (threadIdx.x == 0) {
-        w.st->prefix = 0u;
-        w.st->overflow = 0u;
-        w.st->rank = k;
+        TopkState s = {};
+        s.rank = k;
+        *w.st = s;
     }
 }
 
+// ------------------------------------------------------------ the sample
+
+// Histograms of the sampled keys.  Sample unit s (0 <= s < mu) is unit
+// floor(s * units / mu) of the update: one 16-byte vector (vec_units) or one
+// element.  Level 1: the top digit (bits 30..20) into hist[0..2048).  Level
+// 2: the second digit (bits 19..9) of the keys whose top digit is the bin of
+// the upper order statistic (into hist[0..2048)) and of the lower one (into
+// hist[2048..4096)).
+template <int DT>
+__global__ __launch_bounds__(TK_THREADS) void topk_sample_hist_kernel(const void *x, bool vec_units,
+                                                                      int64_t units, int64_t mu,
+                                                                      TopkWs w, int level, bool has_hi)
+{
+    __shared__ uint32_t s_h[2][TK_MAX_BINS];
+    for (int b = threadIdx.x; b < 2 * TK_MAX_BINS; b += blockDim.x)
+        s_h[b / TK_MAX_BINS][b % TK_MAX_BINS] = 0u;
+    __syncthreads();
+    const uint32_t bhi = level == 2 ? w.st->sbin_hi : 0u;
+    const uint32_t blo = level == 2 ? w.st->sbin_lo : 0u;
+    auto count = [&](uint32_t key) {
+        const uint32_t top = key >> TK_TOP_SHIFT;
+        if (level == 1) {
+            atomicAdd(&s_h[0][top], 1u);
+        } else {
+            const uint32_t d = (key >> TK_SUB_SHIFT) & (TK_MAX_BINS - 1);
+            if (has_hi && top == bhi)
+                atomicAdd(&s_h[0][d], 1u);
+            if (top == blo)
+                atomicAdd(&s_h[1][d], 1u);
+        }
+    };
+    // floor(s * units / mu) without overflow: s * q + floor(s * rem / mu)
+    const int64_t q = units / mu, rem = units % mu;
+    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < mu;
+         s += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t u = s * q + (s * rem) / mu;
+        if (vec_units) {
+            constexpr int V = Vec<DT>::N;
+            uint32_t b[V];
+            Vec<DT>::load(x, u, b);
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                count(key_of_bits(b[i]));
+        } else {
+            count(key_of_bits(bits_at<DT>(x, u)));
+        }
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < TK_MAX_BINS; b += blockDim.x) {
+        const uint32_t c0 = s_h[0][b];
+        if (c0)
+            atomicAdd(&w.hist[b], (unsigned long long)c0);
+        if (level == 2) {
+            const uint32_t c1 = s_h[1][b];
+            if (c1)
+                atomicAdd(&w.hist[TK_MAX_BINS + b], (unsigned long long)c1);
+        }
+    }
+}
+
+// s[b] = sum over u >= b of hist[u] for b < bins, s[bins] = 0, by a
+// Hillis-Steele scan from the top bin down (each step reads before any
+// thread writes).  TK_SELECT_THREADS threads; ends with a barrier.
+__device__ void suffix_sums(const unsigned long long *hist, int bins, unsigned long long *s)
+{
+    const int t = threadIdx.x;
+    for (int b = t; b < bins; b += blockDim.x)
+        s[b] = hist[b];
+    if (t == 0)
+        s[bins] = 0ull;
+    __syncthreads();
+    for (int d = 1; d < bins; d <<= 1) {
+        unsigned long long add[2] = {0ull, 0ull};
+        for (int i = 0, b = t; b < bins; b += blockDim.x, ++i)
+            add[i] = b + d < bins ? s[b + d] : 0ull;
+        __syncthreads();
+        for (int i = 0, b = t; b < bins; b += blockDim.x, ++i)
+            s[b] += add[i];
+        __syncthreads();
+    }
+}
+
+// The bin b with s[b] >= rank > s[b + 1] (there is one when 1 <= rank <=
+// s[0]), else -1; every thread gets it.  Ends with a barrier.
+__device__ int find_bin(const unsigned long long *s, int bins, int64_t rank, int *s_pick)
+{
+    if (threadIdx.x == 0)
+        *s_pick = -1;
+    __syncthreads();
+    for (int b = threadIdx.x; b < bins; b += blockDim.x)
+        if ((int64_t)s[b] >= rank && (int64_t)s[b + 1] < rank)
+            *s_pick = b;
+    __syncthreads();
+    const int b = *s_pick;
+    __syncthreads();
+    return b;
+}
+
+// One workgroup.  Level 1: the top-digit bins holding the sample's r_hi-th
+// and r_lo-th largest keys (ranks from the top, 1-based) and the ranks left
+// inside them.  Level 2: their second digits, giving K_hi = the upper one's
+// 22-bit prefix with all lower bits set (no upper bound when !has_hi) and
+// K_lo = the lower one's prefix with the lower bits clear.  The histograms
+// are cleared for the next pass.
+__global__ __launch_bounds__(TK_SELECT_THREADS) void topk_sample_select_kernel(TopkWs w, int level,
+                                                                               bool has_hi,
+                                                                               int64_t r_hi,
+                                                                               int64_t r_lo)
+{
+    __shared__ unsigned long long s_suffix[TK_MAX_BINS + 1];
+    __shared__ int s_pick;
+    TopkState *st = w.st;
+    const int t = threadIdx.x;
+    if (level == 1) {
+        suffix_sums(w.hist, TK_MAX_BINS, s_suffix);
+        const int bh = has_hi ? find_bin(s_suffix, TK_MAX_BINS, r_hi, &s_pick) : 0;
+        const int bl = find_bin(s_suffix, TK_MAX_BINS, r_lo, &s_pick);
+        if (t == 0) {
+            st->sbin_hi = bh < 0 ? 0u : (uint32_t)bh;
+            st->srank_hi = has_hi && bh >= 0 ? r_hi - (int64_t)s_suffix[bh + 1] : 0;
+            st->sbin_lo = bl < 0 ? 0u : (uint32_t)bl;
+            st->srank_lo = bl >= 0 ? r_lo - (int64_t)s_suffix[bl + 1] : 0;
+            st->ranged = bh >= 0 && bl >= 0;
+        }
+        for (int b = t; b < TK_MAX_BINS; b += blockDim.x)
+            w.hist[b] = 0ull;
+    } else {
+        // read before the barriers: thread 0 rewrites `ranged` at the end
+        const int64_t sr_hi = st->srank_hi, sr_lo = st->srank_lo;
+        const uint32_t bh = st->sbin_hi, bl = st->sbin_lo;
+        const bool ok = st->ranged != 0u;
+        int dh = TK_MAX_BINS - 1;
+        if (has_hi) {
+            suffix_sums(w.hist, TK_MAX_BINS, s_suffix);
+            dh = find_bin(s_suffix, TK_MAX_BINS, sr_hi, &s_pick);
+        }
+        suffix_sums(w.hist + TK_MAX_BINS, TK_MAX_BINS, s_suffix);
+        const int dl = find_bin(s_suffix, TK_MAX_BINS, sr_lo, &s_pick);
+        if (t == 0) {
+            st->khi = has_hi ? (bh << TK_TOP_SHIFT) | ((uint32_t)max(dh, 0) << TK_SUB_SHIFT) |
+                                   ((1u << TK_SUB_SHIFT) - 1u)
+                             : 0x7FFFFFFFu;
+            st->klo = (bl << TK_TOP_SHIFT) | ((uint32_t)max(dl, 0) << TK_SUB_SHIFT);
+            st->ranged = ok && dh >= 0 && dl >= 0;
+        }
+        for (int b = t; b < 2 * TK_MAX_BINS; b += blockDim.x)
+            w.hist[b] = 0ull;
+    }
+}
+
+// ------------------------------------------------------------ sampled path
+
+// Per tile, with the range [klo, khi] known: count the keys above khi,
+// compact the keys inside the range into the tile's candidate segment and,
+// with staging, every key at or above klo with its position into the tile's
+// staging segment -- both in index order.  Segments are reserved in the
+// tile's region (tile mod TK_REGIONS) with one atomic each; a region that
+// runs out sets `fov` and the check sends the call down the full path.
+template <int DT>
+__global__ __launch_bounds__(TT_THREADS, 5) void topk_split_range_kernel(const void *x, int64_t N,
+                                                                      bool vec_ok, int64_t nt,
+                                                                      TopkWs w, bool staging)
+{
+    using TL = Tile<DT>;
+    __shared__ uint32_t s_tot[TL::ROUNDS][TT_WAVES];
+    __shared__ u32x2 s_ent[TK_STAGE];
+    __shared__ unsigned long long s_toff, s_coff;
+    if (!w.st->ranged)
+        return;
+    const uint32_t lo = w.st->klo, hi = w.st->khi;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
+        const int64_t tile0 = tile * TK_TILE;
+        TL tl;
+        tl.load(x, N, vec_ok, tile0);
+        // per round: (keys >= lo) << 16 | (keys in [lo, hi]); a tile holds at
+        // most TK_TILE < 2^16 of either, so the fields never carry
+        uint32_t exw[TL::ROUNDS];
+#pragma unroll
+        for (int j = 0; j < TL::ROUNDS; ++j) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int q = 0; q < TL::V; ++q) {
+                const uint32_t key = key_of_bits(tl.b[j][q]);
+                v += key >= lo ? ((1u << 16) | (key <= hi ? 1u : 0u)) : 0u;
+            }
+            const uint32_t sc = wave_inclusive_scan(v);
+            if (lane == 63)
+                s_tot[j][wave] = sc;
+            exw[j] = sc - v; // this lane's exclusive prefix inside its wave
+        }
+        __syncthreads();
+        uint32_t tot = 0;
+#pragma unroll
+        for (int j = 0; j < TL::ROUNDS; ++j)
+#pragma unroll
+            for (int v = 0; v < TT_WAVES; ++v)
+                tot += s_tot[j][v];
+        // padding (key 0) meets key >= lo only when lo is 0, and then also
+        // key <= hi
+        const uint32_t pad_in = lo == 0u ? tl.pad() : 0u;
+        const uint32_t n_ge = (tot >> 16) - pad_in, n_cand = (tot & 0xFFFFu) - pad_in;
+        if (threadIdx.x == 0) {
+            const int region = (int)(tile % TK_REGIONS);
+            // one atomic reserves both segments; the staging count runs with
+            // or without staging: the check reads the keys >= klo from it
+            const unsigned long long o =
+                n_ge ? atomicAdd(&w.rcnt[region * TK_CSTRIDE], ((unsigned long long)n_ge << 32) | n_cand) : 0ull;
+            const unsigned long long ot = o >> 32, oc = o & 0xFFFFFFFFull;
+            const bool tfits = !staging || (int64_t)(ot + n_ge) <= w.tcap;
+            const bool cfits = (int64_t)(oc + n_cand) <= w.rcap;
+            if (!tfits || !cfits)
+                w.st->fov = 1u;
+            s_toff = staging && tfits ? (unsigned long long)region * w.tcap + ot : ~0ull;
+            s_coff = cfits ? (unsigned long long)region * w.rcap + oc : ~0ull;
+            w.def[tile] = n_ge - n_cand;
+            w.ccnt[tile] = n_cand;
+            w.coff[tile] = (unsigned long long)region * w.rcap + oc;
+            w.tcnt[tile] = n_ge;
+            w.toff[tile] = staging ? (unsigned long long)region * w.tcap + ot : 0ull;
+        }
+        __syncthreads();
+        const unsigned long long toff = s_toff, coff = s_coff;
+        tl.reuse();
+        uint32_t carry = 0;
+#pragma unroll
+        for (int j = 0; j < TL::ROUNDS; ++j) {
+            uint32_t before = 0, round_total = 0;
+#pragma unroll
+            for (int v = 0; v < TT_WAVES; ++v) {
+                const uint32_t t = s_tot[j][v];
+                before += v < wave ? t : 0u;
+                round_total += t;
+            }
+            const uint32_t run = carry + before + exw[j];
+            carry += round_total;
+            uint32_t rt = run >> 16, rc = run & 0xFFFFu;
+#pragma unroll
+            for (int q = 0; q < TL::V; ++q) {
+                const uint32_t bits = tl.b[j][q];
+                const uint32_t key = key_of_bits(bits);
+                if (key < lo)
+                    continue;
+                const uint32_t local = tl.local(j, q);
+                if (toff != ~0ull && rt < n_ge) { // padding ranks last: rt >= n_ge
+                    if (rt < TK_STAGE)
+                        s_ent[rt] = u32x2{bits, local};
+                    else
+                        w.stage[toff + rt] = u32x2{bits, local};
+                }
+                ++rt;
+                if (key <= hi) {
+                    if (coff != ~0ull && rc < n_cand)
+                        w.cand[coff + rc] = u32x2{key, local};
+                    ++rc;
+                }
+            }
+        }
+        __syncthreads();
+        if (toff != ~0ull) {
+            const int n = (int)min((uint32_t)TK_STAGE, n_ge);
+            for (int i = threadIdx.x; i < n; i += TT_THREADS)
+                w.stage[toff + i] = s_ent[i];
+        }
+        __syncthreads(); // s_tot and s_ent are reused by the next tile
+    }
+}
+
+// One workgroup of TK_REGIONS threads: the range holds T iff fewer than k
+// keys lie above khi and at least k at or above klo, and nothing overflowed.
+// Then the sampled path is on, and T's rank among the candidates is k minus
+// the keys above khi; else the candidate counters are cleared for the full
+// path.
+__global__ __launch_bounds__(TK_REGIONS) void topk_check_kernel(TopkWs w, int64_t k)
+{
+    __shared__ unsigned long long s_ge[TK_REGIONS / 64], s_in[TK_REGIONS / 64];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const unsigned long long c = w.rcnt[t * TK_CSTRIDE];
+    unsigned long long ge = c >> 32, in = c & 0xFFFFFFFFull;
+    for (int d = 32; d > 0; d >>= 1) {
+        ge += __shfl_down(ge, d, 64);
+        in += __shfl_down(in, d, 64);
+    }
+    if (lane == 0) {
+        s_ge[wave] = ge;
+        s_in[wave] = in;
+    }
+    const bool ranged = w.st->ranged != 0u, fov = w.st->fov != 0u;
+    __syncthreads();
+    unsigned long long n_ge = 0, n_in = 0;
+#pragma unroll
+    for (int v = 0; v < TK_REGIONS / 64; ++v) {
+        n_ge += s_ge[v];
+        n_in += s_in[v];
+    }
+    const int64_t above = (int64_t)(n_ge - n_in);
+    const bool fast = ranged && !fov && above < k && k <= (int64_t)n_ge;
+    if (!fast)
+        w.rcnt[t * TK_CSTRIDE] = 0ull;
+    if (t == 0) {
+        w.st->fast = fast;
+        if (fast)
+            w.st->rank = k - above;
+    }
+}
+
+// ------------------------------------------------------------ full path
+
+// Per tile, once the top digit b1 of T is known: count the keys above bin
+// b1 and compact the keys inside it into the tile's candidate segment.
+template <int DT>
+__global__ __launch_bounds__(TT_THREADS) void topk_split_bin_kernel(const void *x, int64_t N,
+                                                                    bool vec_ok, int64_t nt, TopkWs w)
+{
+    __shared__ uint32_t s_wave[TT_WAVES];
+    __shared__ unsigned long long s_off;
+    using TL = Tile<DT>;
+    if (w.st->fast)
+        return;
+    const uint32_t b1 = w.st->prefix >> TK_TOP_SHIFT;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
+        const int64_t tile0 = tile * TK_TILE;
+        TL tl;
+        tl.load(x, N, vec_ok, tile0);
+        uint32_t v = 0; // (keys above bin b1) << 16 | (keys inside it)
+#pragma unroll
+        for (int j = 0; j < TL::ROUNDS; ++j)
+#pragma unroll
+            for (int q = 0; q < TL::V; ++q) {
+                const uint32_t bin = key_of_bits(tl.b[j][q]) >> TK_TOP_SHIFT;
+                v += bin > b1 ? (1u << 16) : 0u;
+                v += bin == b1 ? 1u : 0u;
+            }
+        const uint32_t inc = wave_inclusive_scan(v);
+        if (lane == 63)
+            s_wave[wave] = inc;
+        __syncthreads();
+        uint32_t before = 0, tot = 0;
+#pragma unroll
+        for (int u = 0; u < TT_WAVES; ++u) {
+            before += u < wave ? s_wave[u] : 0u;
+            tot += s_wave[u];
+        }
+        // padding (key 0) lies in bin b1 only when b1 is 0, never above it
+        const uint32_t tot_def = tot >> 16, tot_cand = (tot & 0xFFFFu) - (b1 == 0u ? tl.pad() : 0u);
+        if (threadIdx.x == 0) {
+            const int region = (int)(tile % TK_REGIONS);
+            const unsigned long long o = tot_cand ? atomicAdd(&w.rcnt[region * TK_CSTRIDE], (unsigned long long)tot_cand) : 0ull;
+            const bool fits = (int64_t)(o + tot_cand) <= w.rcap;
+            if (!fits)
+                w.st->overflow = 1u;
+            s_off = fits ? (unsigned long long)region * w.rcap + o : ~0ull;
+            w.def[tile] = tot_def;
+            w.ccnt[tile] = tot_cand;
+            w.coff[tile] = (unsigned long long)region * w.rcap + o;
+        }
+        __syncthreads();
+        const unsigned long long o = s_off;
+        tl.reuse();
+        if (o != ~0ull && (v & 0xFFFFu)) {
+            uint32_t rank = (before + inc - v) & 0xFFFFu;
+#pragma unroll
+            for (int j = 0; j < TL::ROUNDS; ++j)
+#pragma unroll
+                for (int q = 0; q < TL::V; ++q) {
+                    const uint32_t key = key_of_bits(tl.b[j][q]);
+                    if ((key >> TK_TOP_SHIFT) == b1) {
+                        if (rank < tot_cand) // padding ranks last
+                            w.cand[o + rank] = u32x2{key, tl.local(j, q)};
+                        ++rank;
+                    }
+                }
+        }
+        __syncthreads(); // s_wave and s_off are reused by the next tile
+    }
+}
+
+// ------------------------------------------------------------ both paths
+
 // LDS histogram of digit (key >> shift) & (bins-1) over keys whose bits
 // above the digit equal the prefix; added to the global histogram once per
-// workgroup.  Source: the whole input (from_input), or the candidates
-// unless they overflowed (then the whole input after all).
+// workgroup.  Source: the candidates -- on the sampled path, and on the full
+// path after the first digit unless they overflowed -- else the whole
+// input.  The grid is a multiple of TK_REGIONS: gridDim / TK_REGIONS
+// workgroups share each candidate region.
 template <int DT>
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, int64_t N,
                                                                bool vec_ok, TopkWs w, int shift,
-                                                               int bits, bool from_input)
+                                                               int bits, bool first_digit)
 {
     __shared__ uint32_t s_hist[TK_WAVES][TK_MAX_BINS];
     const int bins = 1 << bits;
     const uint32_t above =
         (shift + bits >= 31) ? 0u : (0x7FFFFFFFu >> (shift + bits)) << (shift + bits);
     const uint32_t prefix = w.st->prefix & above;
-    const bool input = from_input || w.st->overflow;
+    const bool fast = w.st->fast != 0u;
+    const bool input = first_digit ? !fast : (!fast && w.st->overflow);
     const int wave = threadIdx.x >> 6;
     for (int b = threadIdx.x; b < TK_WAVES * bins; b += blockDim.x)
         s_hist[b / bins][b % bins] = 0u;
     __syncthreads();
 
     uint32_t *h = s_hist[wave];
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     auto count = [&](uint32_t key) {
         if ((key & above) == prefix)
             atomicAdd(&h[(key >> shift) & (uint32_t)(bins - 1)], 1u);
     };
     if (input) {
         constexpr int V = Vec<DT>::N;
+        const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+        const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
         const int64_t nvec = vec_ok ? N / V : 0;
         for (int64_t v = t0; v < nvec; v += stride) {
             uint32_t b[V];
@@ -245,13 +732,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
         for (int64_t e = nvec * V + t0; e < N; e += stride)
             count(key_of_bits(bits_at<DT>(x, e)));
     } else {
-        // every region's used part; unused slots are skipped
-        const int64_t total = (int64_t)TK_REGIONS * w.rcap;
-        for (int64_t c = t0; c < total; c += stride) {
-            const int64_t r = c / w.rcap;
-            if (c - r * w.rcap < (int64_t)w.rcount[r])
-                count(w.cand[c].x);
-        }
+        const int r = (int)(blockIdx.x % TK_REGIONS);
+        const int64_t parts = gridDim.x / TK_REGIONS, part = blockIdx.x / TK_REGIONS;
+        const int64_t n = min((int64_t)(w.rcnt[r * TK_CSTRIDE] & 0xFFFFFFFFull), w.rcap);
+        const u32x2 *c = w.cand + (int64_t)r * w.rcap;
+        for (int64_t i = part * blockDim.x + threadIdx.x; i < n; i += parts * blockDim.x)
+            count(c[i].x);
     }
     __syncthreads();
     for (int b = threadIdx.x; b < bins; b += blockDim.x) {
@@ -267,320 +753,351 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
 // One workgroup: the largest digit d with sum_{u >= d} hist[u] >= rank joins
 // the prefix, rank drops by the count of larger digits, and the histogram is
 // cleared for the next pass.
-__global__ __launch_bounds__(TK_SELECT_THREADS) void topk_select_kernel(unsigned long long *hist,
-                                                                        TopkState *st, int shift,
-                                                                        int bits)
+__global__ __launch_bounds__(TK_SELECT_THREADS) void topk_select_kernel(TopkWs w, int shift, int bits)
 {
     __shared__ unsigned long long s_suffix[TK_MAX_BINS + 1];
+    __shared__ int s_pick;
     const int bins = 1 << bits;
-    const int t = threadIdx.x;
-    // read before the first barrier: one thread rewrites it at the end
-    const int64_t rank = st->rank;
-    for (int b = t; b < bins; b += blockDim.x)
-        s_suffix[b] = hist[b];
-    if (t == 0)
-        s_suffix[bins] = 0ull;
-    __syncthreads();
-    // suffix sums from the top bin down: a Hillis-Steele scan, each step
-    // reading before any thread writes
-    for (int d = 1; d < bins; d <<= 1) {
-        unsigned long long add[2] = {0ull, 0ull};
-        for (int i = 0, b = t; b < bins; b += blockDim.x, ++i)
-            add[i] = b + d < bins ? s_suffix[b + d] : 0ull;
-        __syncthreads();
-        for (int i = 0, b = t; b < bins; b += blockDim.x, ++i)
-            s_suffix[b] += add[i];
-        __syncthreads();
+    // read before the first barrier: thread 0 rewrites it at the end
+    const int64_t rank = w.st->rank;
+    suffix_sums(w.hist, bins, s_suffix);
+    const int b = find_bin(s_suffix, bins, rank, &s_pick);
+    if (threadIdx.x == 0 && b >= 0) {
+        w.st->prefix |= (uint32_t)b << shift;
+        w.st->rank = rank - (int64_t)s_suffix[b + 1];
     }
-    for (int b = t; b < bins; b += blockDim.x) {
-        if ((int64_t)s_suffix[b] >= rank && (int64_t)s_suffix[b + 1] < rank) {
-            st->prefix |= (uint32_t)b << shift;
-            st->rank = rank - (int64_t)s_suffix[b + 1];
-        }
-    }
-    for (int b = t; b < TK_MAX_BINS; b += blockDim.x)
-        hist[b] = 0ull;
+    for (int u = threadIdx.x; u < bins; u += blockDim.x)
+        w.hist[u] = 0ull;
 }
 
-// Per tile, once the top digit b1 is known: count the keys above bin b1 and
-// compact the keys inside it into the candidate buffer (in tile order).
-template <int DT>
-__global__ __launch_bounds__(TT_THREADS) void topk_split_kernel(const void *x, int64_t N,
-                                                                bool vec_ok, TopkWs w)
+// Per tile, one wave each: keys above and equal to T from the tile's
+// candidates, plus its keys above them.  Skipped after a candidate overflow
+// on the full path (topk_tile_count_input_kernel counts then).
+__global__ __launch_bounds__(TT_THREADS) void topk_tile_count_kernel(int64_t nt, TopkWs w)
 {
-    __shared__ uint32_t s_wave[TT_WAVES];
-    __shared__ unsigned long long s_off;
-    using TL = Tile<DT>;
-    const uint32_t b1 = w.st->prefix >> TK_TOP_SHIFT;
-    const int64_t tile0 = (int64_t)blockIdx.x * TK_TILE;
-    TL tl;
-    tl.load(x, N, vec_ok, tile0);
-    uint32_t ndef = 0, ncand = 0;
-#pragma unroll
-    for (int j = 0; j < TL::ROUNDS; ++j)
-#pragma unroll
-        for (int q = 0; q < TL::V; ++q) {
-            const uint32_t bin = key_of_bits(tl.b[j][q]) >> TK_TOP_SHIFT;
-            const bool in = TL::in(N, tile0, j, q);
-            ndef += in && bin > b1;
-            ncand += in && bin == b1;
-        }
-    uint32_t tot_def, tot_cand;
-    // packed: both counts stay below 2^16 within a tile
-    const uint32_t ex = wg_exclusive_scan((ndef << 16) | ncand, s_wave, tot_def);
-    tot_cand = tot_def & 0xFFFFu;
-    tot_def >>= 16;
-    // reserve room in this tile's region (spreading the reservations over
-    // TK_REGIONS counters keeps them from queueing on one address)
-    const int region = (int)(blockIdx.x % TK_REGIONS);
-    if (threadIdx.x == 0) {
-        const unsigned long long o = tot_cand ? atomicAdd(&w.rcount[region], (unsigned long long)tot_cand) : 0ull;
-        const bool fits = (int64_t)(o + tot_cand) <= w.rcap;
-        if (!fits)
-            w.st->overflow = 1u;
-        s_off = fits ? (unsigned long long)region * w.rcap + o : ~0ull;
-        w.def[blockIdx.x] = tot_def;
-        w.ccnt[blockIdx.x] = tot_cand;
-        w.coff[blockIdx.x] = (unsigned long long)region * w.rcap + o;
-    }
-    __syncthreads();
-    const unsigned long long o = s_off;
-    if (o == ~0ull || ncand == 0)
+    if (!w.st->fast && w.st->overflow)
         return;
-    unsigned long long pos = o + (ex & 0xFFFFu);
-#pragma unroll
-    for (int j = 0; j < TL::ROUNDS; ++j)
-#pragma unroll
-        for (int q = 0; q < TL::V; ++q) {
-            const uint32_t key = key_of_bits(tl.b[j][q]);
-            if (TL::in(N, tile0, j, q) && (key >> TK_TOP_SHIFT) == b1) {
-                w.cand[pos] = u32x2{key, (uint32_t)(TL::first(0, j) + q)};
-                ++pos;
-            }
-        }
+    const int64_t tile = (int64_t)blockIdx.x * TT_WAVES + (threadIdx.x >> 6);
+    if (tile >= nt)
+        return; // no barriers below
+    const int lane = threadIdx.x & 63;
+    const uint32_t T = w.st->prefix;
+    const unsigned long long c0 = w.coff[tile];
+    const uint32_t n = w.ccnt[tile];
+    uint32_t c = 0; // (above T) << 16 | (equal to T); each below 2^16
+    for (uint32_t i = lane; i < n; i += 64) {
+        const uint32_t key = w.cand[c0 + i].x;
+        c += key > T ? (1u << 16) : (key == T ? 1u : 0u);
+    }
+    for (int d = 32; d > 0; d >>= 1)
+        c += __shfl_down(c, d, 64);
+    if (lane == 0) {
+        w.gt[tile] = (c >> 16) + w.def[tile];
+        w.eq[tile] = c & 0xFFFFu;
+    }
 }
 
-// Per tile: keys above and equal to the threshold T -- from the tile's
-// candidates plus its keys above bin b1, or from the whole tile after an
-// overflow.
+// The same counts from the whole tile, after a candidate overflow on the
+// full path.
 template <int DT>
-__global__ __launch_bounds__(TT_THREADS) void topk_tile_count_kernel(const void *x, int64_t N,
-                                                                     bool vec_ok, TopkWs w)
+__global__ __launch_bounds__(TT_THREADS) void topk_tile_count_input_kernel(const void *x, int64_t N,
+                                                                           bool vec_ok, int64_t nt,
+                                                                           TopkWs w)
 {
     __shared__ uint32_t s_sum[TT_WAVES];
+    if (w.st->fast || !w.st->overflow)
+        return;
+    using TL = Tile<DT>;
     const uint32_t T = w.st->prefix;
-    const int64_t tile0 = (int64_t)blockIdx.x * TK_TILE;
-    uint32_t ngt = 0, neq = 0;
-    if (w.st->overflow) {
-        using TL = Tile<DT>;
+    for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
+        const int64_t tile0 = tile * TK_TILE;
         TL tl;
         tl.load(x, N, vec_ok, tile0);
+        uint32_t c = 0;
 #pragma unroll
         for (int j = 0; j < TL::ROUNDS; ++j)
 #pragma unroll
             for (int q = 0; q < TL::V; ++q) {
                 const uint32_t key = key_of_bits(tl.b[j][q]);
-                const bool in = TL::in(N, tile0, j, q);
-                ngt += in && key > T;
-                neq += in && key == T;
+                c += key > T ? (1u << 16) : 0u;
+                c += key == T ? 1u : 0u;
             }
-    } else {
-        const unsigned long long c0 = w.coff[blockIdx.x];
-        const uint32_t n = w.ccnt[blockIdx.x];
-        for (uint32_t c = threadIdx.x; c < n; c += TT_THREADS) {
-            const uint32_t key = w.cand[c0 + c].x;
-            ngt += key > T;
-            neq += key == T;
-        }
-    }
-    uint32_t c = (ngt << 16) | neq;
-    for (int d = 32; d > 0; d >>= 1)
-        c += __shfl_down(c, d, 64);
-    if ((threadIdx.x & 63) == 0)
-        s_sum[threadIdx.x >> 6] = c;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t s = 0;
+        for (int d = 32; d > 0; d >>= 1)
+            c += __shfl_down(c, d, 64);
+        if ((threadIdx.x & 63) == 0)
+            s_sum[threadIdx.x >> 6] = c;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t s = 0;
 #pragma unroll
-        for (int v = 0; v < TT_WAVES; ++v)
-            s += s_sum[v];
-        w.gt[blockIdx.x] = (s >> 16) + (w.st->overflow ? 0u : w.def[blockIdx.x]);
-        w.eq[blockIdx.x] = s & 0xFFFFu;
-    }
-}
-
-// Workgroup-wide exclusive scan of 64-bit values (TK_SELECT_THREADS threads).
-__device__ int64_t big_exclusive_scan(int64_t v, int64_t *s_tmp, int64_t &total)
-{
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    int64_t inc = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        const int64_t o = __shfl_up(inc, off, 64);
-        if (lane >= off)
-            inc += o;
-    }
-    if (lane == 63)
-        s_tmp[wave] = inc;
-    __syncthreads();
-    if (t == 0) {
-        int64_t run = 0;
-        for (int v = 0; v < TK_SELECT_THREADS / 64; ++v) {
-            const int64_t s = s_tmp[v];
-            s_tmp[v] = run;
-            run += s;
+            for (int v = 0; v < TT_WAVES; ++v)
+                s += s_sum[v];
+            w.gt[tile] = s >> 16;
+            w.eq[tile] = (s & 0xFFFFu) - (T == 0u ? tl.pad() : 0u); // padding is key 0
         }
-        s_tmp[TK_SELECT_THREADS / 64] = run;
+        __syncthreads();
     }
-    __syncthreads();
-    const int64_t ex = s_tmp[wave] + inc - v;
-    total = s_tmp[TK_SELECT_THREADS / 64];
-    __syncthreads();
-    return ex;
 }
 
-// One workgroup, tiles in chunks of 4 per thread (coalesced 16-byte loads):
-// tile b keeps take[b] = clamp(r - ties before b, 0, eq[b]) of its ties and
-// writes from off[b] = sum over earlier tiles of gt + take.
-__global__ __launch_bounds__(TK_SELECT_THREADS) void topk_scan_kernel(int64_t nt, TopkWs w)
+// ------------------------------------------------------------ offsets
+
+// Tile b keeps take[b] = clamp(r - ties before b, 0, eq[b]) of its ties and
+// writes from off[b] = sum over earlier tiles of gt + take.  Three kernels:
+// per chunk of TK_SCAN_CHUNK tiles the sums of eq and gt; one workgroup over
+// the chunks; then each chunk's tiles.
+
+// Four tiles' counts from b0 (the arrays are padded to a multiple of 4).
+__device__ __forceinline__ void load4(const uint32_t *a, int64_t b0, int64_t nt, uint32_t o[4])
+{
+    o[0] = o[1] = o[2] = o[3] = 0u;
+    if (b0 < nt) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(a + b0);
+        const int64_t live = nt - b0;
+        o[0] = v.x;
+        o[1] = live > 1 ? v.y : 0u;
+        o[2] = live > 2 ? v.z : 0u;
+        o[3] = live > 3 ? v.w : 0u;
+    }
+}
+
+__global__ __launch_bounds__(256) void topk_scan_reduce_kernel(int64_t nt, TopkWs w)
+{
+    __shared__ int64_t s_tmp[256 / 64 + 1];
+    const int64_t b0 = (int64_t)blockIdx.x * TK_SCAN_CHUNK + 4 * (int64_t)threadIdx.x;
+    uint32_t g[4], e[4];
+    load4(w.gt, b0, nt, g);
+    load4(w.eq, b0, nt, e);
+    int64_t tot_e, tot_g;
+    block_exclusive_scan64<256>((int64_t)e[0] + e[1] + e[2] + e[3], s_tmp, tot_e);
+    block_exclusive_scan64<256>((int64_t)g[0] + g[1] + g[2] + g[3], s_tmp, tot_g);
+    if (threadIdx.x == 0) {
+        w.ch_eq[blockIdx.x] = tot_e;
+        w.ch_gt[blockIdx.x] = tot_g;
+    }
+}
+
+__global__ __launch_bounds__(TK_SELECT_THREADS) void topk_scan_top_kernel(int64_t nch, TopkWs w)
 {
     __shared__ int64_t s_tmp[TK_SELECT_THREADS / 64 + 1];
     const int64_t r = w.st->rank;
     int64_t ties_carry = 0, sel_carry = 0;
-    for (int64_t c0 = 0; c0 < nt; c0 += 4 * TK_SELECT_THREADS) {
-        const int64_t b0 = c0 + 4 * (int64_t)threadIdx.x;
-        uint32_t g[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
-        if (b0 < nt) { // arrays are padded to a multiple of 4 tiles
-            const u32x4 gv = *reinterpret_cast<const u32x4 *>(w.gt + b0);
-            const u32x4 ev = *reinterpret_cast<const u32x4 *>(w.eq + b0);
-            const int live = (int)min((int64_t)4, nt - b0);
-            g[0] = gv.x; g[1] = live > 1 ? gv.y : 0u; g[2] = live > 2 ? gv.z : 0u; g[3] = live > 3 ? gv.w : 0u;
-            e[0] = ev.x; e[1] = live > 1 ? ev.y : 0u; e[2] = live > 2 ? ev.z : 0u; e[3] = live > 3 ? ev.w : 0u;
-        }
+    for (int64_t c0 = 0; c0 < nch; c0 += TK_SELECT_THREADS) {
+        const int64_t c = c0 + threadIdx.x;
+        const int64_t e = c < nch ? w.ch_eq[c] : 0, g = c < nch ? w.ch_gt[c] : 0;
         int64_t total;
-        int64_t tb = ties_carry + big_exclusive_scan((int64_t)e[0] + e[1] + e[2] + e[3], s_tmp, total);
+        const int64_t tb = ties_carry + block_exclusive_scan64<TK_SELECT_THREADS>(e, s_tmp, total);
         ties_carry += total;
-        uint32_t tk[4];
-        int64_t sel = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            tk[i] = (uint32_t)max((int64_t)0, min(r - tb, (int64_t)e[i]));
-            tb += e[i];
-            sel += g[i] + tk[i];
-        }
-        int64_t ob = sel_carry + big_exclusive_scan(sel, s_tmp, total);
+        const int64_t sel = g + max((int64_t)0, min(r - tb, e));
+        const int64_t ob = sel_carry + block_exclusive_scan64<TK_SELECT_THREADS>(sel, s_tmp, total);
         sel_carry += total;
-        if (b0 < nt) {
-            const int live = (int)min((int64_t)4, nt - b0);
-            for (int i = 0; i < live; ++i) {
-                w.take[b0 + i] = tk[i];
-                w.off[b0 + i] = ob;
-                ob += g[i] + tk[i];
-            }
+        if (c < nch) {
+            w.ch_ties[c] = tb;
+            w.ch_off[c] = ob;
         }
     }
 }
 
-// Per tile: the kept entries in index order.  The tile is loaded whole into
-// registers; every round's elements get their rank among the tile's kept
-// entries from wave scans of the packed (above, tie) counts and one exchange
-// of the per-wave round totals in LDS.  The first TK_STAGE kept entries are
-// staged in LDS and then written out as two contiguous runs; any beyond that
-// (a tile keeping more than a quarter of its elements) go straight out.
-constexpr int TK_STAGE = 2048;
+__global__ __launch_bounds__(256) void topk_scan_down_kernel(int64_t nt, TopkWs w)
+{
+    __shared__ int64_t s_tmp[256 / 64 + 1];
+    const int64_t r = w.st->rank;
+    const int64_t b0 = (int64_t)blockIdx.x * TK_SCAN_CHUNK + 4 * (int64_t)threadIdx.x;
+    uint32_t g[4], e[4];
+    load4(w.gt, b0, nt, g);
+    load4(w.eq, b0, nt, e);
+    int64_t total;
+    int64_t tb = w.ch_ties[blockIdx.x] +
+                 block_exclusive_scan64<256>((int64_t)e[0] + e[1] + e[2] + e[3], s_tmp, total);
+    uint32_t tk[4];
+    int64_t sel = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        tk[i] = (uint32_t)max((int64_t)0, min(r - tb, (int64_t)e[i]));
+        tb += e[i];
+        sel += g[i] + tk[i];
+    }
+    int64_t ob = w.ch_off[blockIdx.x] + block_exclusive_scan64<256>(sel, s_tmp, total);
+    const int live = b0 < nt ? (int)min((int64_t)4, nt - b0) : 0;
+    for (int i = 0; i < live; ++i) {
+        w.take[b0 + i] = tk[i];
+        w.off[b0 + i] = ob;
+        ob += g[i] + tk[i];
+    }
+}
 
+// ------------------------------------------------------------ the write
+
+// Sampled path with staging: each tile's kept entries from its staging
+// segment (already in index order), in chunks of TW_ROUNDS x TW_THREADS
+// entries; every round's entries get their rank among the kept ones from wave
+// scans of the packed (above, tie) counts and one exchange of per-wave totals
+// in LDS.  Small workgroups with many entries per thread keep more tiles,
+// and so more loads, in flight per CU.
+constexpr int TW_THREADS = 128;
+constexpr int TW_WAVES = TW_THREADS / 64;
+constexpr int TW_ROUNDS = 8;
+
+__global__ __launch_bounds__(TW_THREADS) void topk_write_staged_kernel(int64_t nt, TopkWs w,
+                                                                       int64_t k_out,
+                                                                       int64_t *idx_out,
+                                                                       float *val_out)
+{
+    constexpr int R = TW_ROUNDS;
+    __shared__ uint32_t s_tot[R][TW_WAVES];
+    if (!w.st->fast)
+        return;
+    const uint32_t T = w.st->prefix;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
+        const uint32_t n = w.tcnt[tile];
+        const u32x2 *seg = w.stage + w.toff[tile];
+        const uint32_t tk = w.take[tile];
+        const int64_t base = w.off[tile];
+        const int64_t tile0 = tile * TK_TILE;
+        uint32_t carry = 0; // packed counts of the entries before this chunk
+        for (uint32_t c0 = 0; c0 < n; c0 += R * TW_THREADS) {
+            u32x2 ent[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
+                ent[i] = p < n ? seg[p] : u32x2{0u, 0u};
+            }
+            uint32_t exw[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
+                const uint32_t key = key_of_bits(ent[i].x);
+                const uint32_t v = p < n ? (key > T ? (1u << 16) : (key == T ? 1u : 0u)) : 0u;
+                const uint32_t sc = wave_inclusive_scan(v);
+                if (lane == 63)
+                    s_tot[i][wave] = sc;
+                exw[i] = sc - v;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                uint32_t before = 0, round_total = 0;
+#pragma unroll
+                for (int v = 0; v < TW_WAVES; ++v) {
+                    const uint32_t t = s_tot[i][v];
+                    before += v < wave ? t : 0u;
+                    round_total += t;
+                }
+                const uint32_t run = carry + before + exw[i];
+                carry += round_total;
+                const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
+                const uint32_t key = key_of_bits(ent[i].x);
+                if (p >= n || key < T)
+                    continue;
+                const uint32_t gt_before = run >> 16, eq_before = run & 0xFFFFu;
+                if (key == T && eq_before >= tk)
+                    continue;
+                const int64_t r = base + gt_before + min(eq_before, tk);
+                if (r < k_out) { // keeps inconsistent counts from writing out of range
+                    idx_out[r] = tile0 + ent[i].y;
+                    val_out[r] = __uint_as_float(ent[i].x);
+                }
+            }
+            __syncthreads(); // s_tot is reused by the next chunk
+        }
+    }
+}
+
+// From the update itself (full path, or the sampled path without staging):
+// the tile is loaded whole into registers and ranked as above; the first
+// TK_STAGE kept entries are staged in LDS and written out as two contiguous
+// runs, any beyond that (a tile keeping more than a quarter of its elements)
+// go straight out.
 template <int DT>
-__global__ __launch_bounds__(TT_THREADS) void topk_write_kernel(const void *x, int64_t N,
-                                                                bool vec_ok, TopkWs w, int64_t k_out,
-                                                                int64_t *idx_out, float *val_out)
+__global__ __launch_bounds__(TT_THREADS) void topk_write_input_kernel(const void *x, int64_t N,
+                                                                      bool vec_ok, int64_t nt,
+                                                                      TopkWs w, bool staged,
+                                                                      int64_t k_out, int64_t *idx_out,
+                                                                      float *val_out)
 {
     using TL = Tile<DT>;
     __shared__ uint32_t s_tot[TL::ROUNDS][TT_WAVES];
     __shared__ uint32_t s_idx[TK_STAGE];
     __shared__ float s_val[TK_STAGE];
+    if (staged && w.st->fast)
+        return;
     const uint32_t T = w.st->prefix;
-    const int64_t tile0 = (int64_t)blockIdx.x * TK_TILE;
-    const uint32_t tk = w.take[blockIdx.x];
-    const int64_t base = w.off[blockIdx.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    TL tl;
-    tl.load(x, N, vec_ok, tile0);
-    uint32_t inc[TL::ROUNDS];
+    for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
+        const int64_t tile0 = tile * TK_TILE;
+        const uint32_t tk = w.take[tile];
+        const int64_t base = w.off[tile];
+        TL tl;
+        tl.load(x, N, vec_ok, tile0);
+        uint32_t exw[TL::ROUNDS];
 #pragma unroll
-    for (int j = 0; j < TL::ROUNDS; ++j) {
-        uint32_t ngt = 0, neq = 0;
+        for (int j = 0; j < TL::ROUNDS; ++j) {
+            uint32_t v = 0;
 #pragma unroll
-        for (int q = 0; q < TL::V; ++q) {
-            const uint32_t key = key_of_bits(tl.b[j][q]);
-            const bool in = TL::in(N, tile0, j, q);
-            ngt += in && key > T;
-            neq += in && key == T;
+            for (int q = 0; q < TL::V; ++q) {
+                const uint32_t key = key_of_bits(tl.b[j][q]);
+                v += key > T ? (1u << 16) : 0u;
+                v += key == T ? 1u : 0u;
+            }
+            const uint32_t sc = wave_inclusive_scan(v);
+            if (lane == 63)
+                s_tot[j][wave] = sc;
+            exw[j] = sc - v; // this lane's exclusive prefix inside its wave
         }
-        uint32_t v = (ngt << 16) | neq;
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t o = __shfl_up(v, d, 64);
-            if (lane >= d)
-                v += o;
-        }
-        inc[j] = v;
-        if (lane == 63)
-            s_tot[j][wave] = v;
-    }
-    __syncthreads();
-    uint32_t carry = 0; // packed counts of the rounds before j
-    uint32_t kept_total = 0;
+        __syncthreads();
+        tl.reuse();
+        uint32_t carry = 0; // packed counts of the rounds before j
 #pragma unroll
-    for (int j = 0; j < TL::ROUNDS; ++j) {
-        uint32_t before = 0, round_total = 0;
+        for (int j = 0; j < TL::ROUNDS; ++j) {
+            uint32_t before = 0, round_total = 0;
 #pragma unroll
-        for (int v = 0; v < TT_WAVES; ++v) {
-            const uint32_t t = s_tot[j][v];
-            before += v < wave ? t : 0u;
-            round_total += t;
-        }
-        // this thread's exclusive prefix: everything before it in this round;
-        // the lanes below it come from the inclusive scan of the lane below
-        // (the shuffle runs on every lane: a disabled source lane would give
-        // no data)
-        const uint32_t below = __shfl_up(inc[j], 1, 64);
-        uint32_t run = carry + before + (lane > 0 ? below : 0u);
-        carry += round_total;
-        uint32_t gt_before = run >> 16, eq_before = run & 0xFFFFu;
+            for (int v = 0; v < TT_WAVES; ++v) {
+                const uint32_t t = s_tot[j][v];
+                before += v < wave ? t : 0u;
+                round_total += t;
+            }
+            const uint32_t run = carry + before + exw[j];
+            carry += round_total;
+            uint32_t gt_before = run >> 16, eq_before = run & 0xFFFFu;
 #pragma unroll
-        for (int q = 0; q < TL::V; ++q) {
-            const uint32_t bits = tl.b[j][q];
-            const uint32_t key = key_of_bits(bits);
-            if (!TL::in(N, tile0, j, q) || key < T)
-                continue;
-            const bool above = key > T;
-            const bool kept = above || eq_before < tk;
-            // rank among the tile's kept entries
-            const uint32_t r = gt_before + min(eq_before, tk);
-            if (above)
-                ++gt_before;
-            else
-                ++eq_before;
-            if (!kept)
-                continue;
-            const uint32_t local = (uint32_t)(TL::first(0, j) + q);
-            if (r < TK_STAGE) {
-                s_idx[r] = local;
-                s_val[r] = __uint_as_float(bits);
-            } else if (base + r < k_out) {
-                // the bound keeps inconsistent counts from writing out of range
-                idx_out[base + r] = tile0 + local;
-                val_out[base + r] = __uint_as_float(bits);
+            for (int q = 0; q < TL::V; ++q) {
+                const uint32_t bits = tl.b[j][q];
+                const uint32_t key = key_of_bits(bits);
+                // padding (key 0) is never above T, and as a tie it ranks
+                // after the tile's own ties, of which at most tk are kept
+                if (key < T)
+                    continue;
+                const bool above = key > T;
+                const bool kept = above || eq_before < tk;
+                // rank among the tile's kept entries
+                const uint32_t r = gt_before + min(eq_before, tk);
+                if (above)
+                    ++gt_before;
+                else
+                    ++eq_before;
+                if (!kept)
+                    continue;
+                const uint32_t local = tl.local(j, q);
+                if (r < TK_STAGE) {
+                    s_idx[r] = local;
+                    s_val[r] = __uint_as_float(bits);
+                } else if (base + r < k_out) {
+                    // the bound keeps inconsistent counts from writing out of range
+                    idx_out[base + r] = tile0 + local;
+                    val_out[base + r] = __uint_as_float(bits);
+                }
             }
         }
-    }
-    kept_total = (carry >> 16) + min(carry & 0xFFFFu, tk);
-    __syncthreads();
-    const int n = (int)min((uint32_t)TK_STAGE, kept_total);
-    for (int i = threadIdx.x; i < n; i += TT_THREADS) {
-        if (base + i < k_out) {
-            idx_out[base + i] = tile0 + s_idx[i];
-            val_out[base + i] = s_val[i];
+        const uint32_t kept_total = (carry >> 16) + min(carry & 0xFFFFu, tk);
+        __syncthreads();
+        const int n = (int)min((uint32_t)TK_STAGE, kept_total);
+        for (int i = threadIdx.x; i < n; i += TT_THREADS) {
+            if (base + i < k_out) {
+                idx_out[base + i] = tile0 + s_idx[i];
+                val_out[base + i] = s_val[i];
+            }
         }
+        __syncthreads(); // s_tot and the staging arrays are reused by the next tile
     }
 }
 
@@ -592,45 +1109,101 @@ unsigned grid_of(int64_t work, int64_t cap)
     return (unsigned)(g < 1 ? 1 : g);
 }
 
+int g_topk_sampled = 1; // FA_OPT_TOPK_SAMPLED
+
+// The sample and the two order statistics that bound T.  m keys are
+// sampled; T has expected rank rho = k m / N among them (from the top) with
+// binomial standard deviation sigma = sqrt(rho (1 - k/N)); K_hi comes from
+// the sample's r_hi-th largest key, r_hi = floor(rho - 8 sigma - 32) (no
+// upper bound when r_hi < 1), and K_lo from its r_lo-th, r_lo = ceil(rho +
+// 8 sigma + 32) (no sampled path when r_lo > m).
+struct SamplePlan {
+    bool on, has_hi, vec_units;
+    int64_t units, mu, r_hi, r_lo;
+};
+
+template <int DT> SamplePlan plan_sample(int64_t N, int64_t k, bool vec_ok)
+{
+    SamplePlan p = {};
+    p.vec_units = vec_ok;
+    const int64_t width = vec_ok ? Vec<DT>::N : 1;
+    p.units = vec_ok ? N / Vec<DT>::N : N;
+    const int64_t cap = TK_SAMPLE_KEYS / width;
+    p.mu = p.units < cap ? p.units : cap;
+    if (!g_topk_sampled || p.mu < 1 || k >= N)
+        return p;
+    const double m = (double)(p.mu * width);
+    const double rho = (double)k * m / (double)N;
+    const double sigma = sqrt(rho * (1.0 - (double)k / (double)N));
+    const double margin = 8.0 * sigma + 32.0;
+    p.r_hi = (int64_t)floor(rho - margin);
+    p.has_hi = p.r_hi >= 1;
+    p.r_lo = (int64_t)ceil(rho + margin);
+    p.on = p.r_lo <= p.mu * width;
+    return p;
+}
+
 template <int DT>
 hipError_t topk_run(const void *x, int64_t N, int64_t k, int64_t *idx_out, float *val_out,
                     void *ws, int cus, hipStream_t s)
 {
-    const TopkWs w = carve(ws, N);
-    const int64_t nt = (N + TK_TILE - 1) / TK_TILE;
+    const Sizes sz = sizes_of(N, k, DT);
+    const TopkWs w = carve(ws, sz);
+    const int64_t nt = sz.nt;
     const bool vec_ok = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+    const bool staging = sz.tcap > 0;
+    const SamplePlan plan = plan_sample<DT>(N, k, vec_ok);
     const unsigned full_grid = grid_of(N / Vec<DT>::N + 1, (int64_t)cus * 4);
-    const unsigned cand_grid = grid_of((int64_t)TK_REGIONS * w.rcap, (int64_t)cus * 4);
+    // a multiple of TK_REGIONS, so every candidate region gets the same share
+    const unsigned hist_grid = (full_grid + TK_REGIONS - 1) / TK_REGIONS * TK_REGIONS;
+    // Per-tile kernels loop over tiles, so any grid is correct.  One that
+    // will most likely do the work gets a workgroup per tile (the dispatcher
+    // then overlaps the phases of many tiles per CU); one that most likely
+    // finds its path off and exits gets a small grid.
+    const unsigned work_grid = (unsigned)nt;
+    const int64_t idle_cap = (int64_t)cus * 2;
+    const unsigned idle_grid = (unsigned)(nt < idle_cap ? nt : idle_cap);
 
     topk_init_kernel<<<1, 256, 0, s>>>(w, k);
-    // digit 1: key bits 30..20, over the whole input
-    topk_hist_kernel<DT><<<full_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, TK_TOP_SHIFT, 11, true);
-    topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w.hist, w.st, TK_TOP_SHIFT, 11);
-    topk_split_kernel<DT><<<(unsigned)nt, TT_THREADS, 0, s>>>(x, N, vec_ok, w);
-    // digits 2 (bits 19..9) and, for fp32, 3 (bits 8..0), over the candidates
-    // (a bf16 key has zeros below bit 16, so two digits decide it); after an
-    // overflow the grid covers the whole input
-    const unsigned later_grid = full_grid > cand_grid ? full_grid : cand_grid;
-    topk_hist_kernel<DT><<<later_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, 9, 11, false);
-    topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w.hist, w.st, 9, 11);
-    if (DT == DT_F32) {
-        topk_hist_kernel<DT><<<later_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, 0, 9, false);
-        topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w.hist, w.st, 0, 9);
+    if (plan.on) {
+        const unsigned sg = grid_of(plan.mu, 256);
+        topk_sample_hist_kernel<DT><<<sg, TK_THREADS, 0, s>>>(x, plan.vec_units, plan.units, plan.mu, w, 1, plan.has_hi);
+        topk_sample_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 1, plan.has_hi, plan.r_hi, plan.r_lo);
+        topk_sample_hist_kernel<DT><<<sg, TK_THREADS, 0, s>>>(x, plan.vec_units, plan.units, plan.mu, w, 2, plan.has_hi);
+        topk_sample_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 2, plan.has_hi, plan.r_hi, plan.r_lo);
+        topk_split_range_kernel<DT><<<work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w, staging);
+        topk_check_kernel<<<1, TK_REGIONS, 0, s>>>(w, k);
     }
-    topk_tile_count_kernel<DT><<<(unsigned)nt, TT_THREADS, 0, s>>>(x, N, vec_ok, w);
-    topk_scan_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(nt, w);
-    topk_write_kernel<DT><<<(unsigned)nt, TT_THREADS, 0, s>>>(x, N, vec_ok, w, k, idx_out, val_out);
+    // digit 1 (key bits 30..20): from the candidates on the sampled path,
+    // else from the whole input, followed on the full path by the split
+    topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, TK_TOP_SHIFT, 11, true);
+    topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, TK_TOP_SHIFT, 11);
+    topk_split_bin_kernel<DT><<<plan.on ? idle_grid : work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w);
+    // digits 2 (bits 19..9) and, for fp32, 3 (bits 8..0); a bf16 key has
+    // zeros below bit 16, so two digits decide it
+    topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, TK_SUB_SHIFT, 11, false);
+    topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, TK_SUB_SHIFT, 11);
+    if (DT == DT_F32) {
+        topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, 0, 9, false);
+        topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 0, 9);
+    }
+    topk_tile_count_kernel<<<(unsigned)((nt + TT_WAVES - 1) / TT_WAVES), TT_THREADS, 0, s>>>(nt, w);
+    topk_tile_count_input_kernel<DT><<<idle_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w);
+    topk_scan_reduce_kernel<<<(unsigned)sz.nch, 256, 0, s>>>(nt, w);
+    topk_scan_top_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(sz.nch, w);
+    topk_scan_down_kernel<<<(unsigned)sz.nch, 256, 0, s>>>(nt, w);
+    const bool staged = plan.on && staging;
+    if (staged)
+        topk_write_staged_kernel<<<work_grid, TW_THREADS, 0, s>>>(nt, w, k, idx_out, val_out);
+    topk_write_input_kernel<DT><<<staged ? idle_grid : work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w, staged, k, idx_out, val_out);
     return hipGetLastError();
 }
 
 } // namespace
 
-size_t topk_workspace_bytes(int64_t N)
-{
-    const int64_t ntp = round4((N + TK_TILE - 1) / TK_TILE);
-    return (size_t)TK_MAX_BINS * 8 + 256 + (size_t)TK_REGIONS * 8 + (size_t)ntp * (8 + 8 + 4 * 5) +
-           (size_t)TK_REGIONS * region_capacity(N) * 8;
-}
+size_t topk_workspace_bytes(int dt, int64_t N, int64_t k) { return sizes_of(N, k, dt).bytes; }
+
+void topk_set_sampled(int on) { g_topk_sampled = on; }
 
 hipError_t launch_topk(const void *x, int dt, int64_t N, int64_t k, int64_t *idx_out,
                        float *val_out, void *ws, int cus, hipStream_t s)

@@ -19,6 +19,7 @@ FA_WEIGHTS, FA_DELTAS, FA_DELTAS_ZERO_FILL = 0, 1, 2
 FA_COUNT_U8, FA_COUNT_U32 = 0, 1
 FA_OPT_BLOCKS_PER_CU, FA_OPT_MASK_VECTORS_PER_BLOCK, FA_OPT_SPARSE_BLOCKS, FA_OPT_RESIDENT_PER_CU = 1, 2, 3, 4
 FA_OPT_SPARSE_TILE = 5
+FA_OPT_TOPK_SAMPLED = 6
 FA_MAX_CLIENTS = 64
 
 STATUS_NAMES = {
@@ -80,7 +81,7 @@ def load(build_if_missing=True):
         "sparse_workspace_size": ([i32, i64, P], i32),
         "sparse_masked_accumulate": ([i32, P, P, P, P, i64, i32, P, P, P, i32, P, P, sz, P, P], i32),
         "fedavg_checksum": ([P, i64, i32, P, P], i32),
-        "topk_workspace_size": ([i64, P], i32),
+        "topk_workspace_size": ([i32, i64, i64, P], i32),
         "fedavg_controller_step": ([i32, P, P, P, i64, P, P, P, i32, P], i32),
         "topk_select": ([P, i32, i64, i64, P, P, P, sz, P], i32),
         "fedavg_set_option": ([i32, i64], i32),
@@ -99,12 +100,16 @@ def _check(rc):
         raise FedAvgError(rc, msg.decode() if msg else "")
 
 
-def _dtype(t):
-    if t.dtype == torch.float32:
+def _dtype_code(dt):
+    if dt == torch.float32:
         return FA_F32
-    if t.dtype == torch.bfloat16:
+    if dt == torch.bfloat16:
         return FA_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+
+
+def _dtype(t):
+    return _dtype_code(t.dtype)
 
 
 def _mode(mode):
@@ -514,9 +519,10 @@ def fedavg_checksum(t, stream=None, hash_out=None):
 
 # ------------------------------------------------------------------ top-k
 
-def topk_workspace_size(N):
+def topk_workspace_size(N, k, dtype=torch.float32):
+    """Device workspace bytes topk_select needs to keep k of N values."""
     b = ctypes.c_size_t(0)
-    _check(load().topk_workspace_size(int(N), ctypes.byref(b)))
+    _check(load().topk_workspace_size(_dtype_code(dtype), int(N), int(k), ctypes.byref(b)))
     return b.value
 
 
@@ -535,7 +541,7 @@ def topk_select(x, k, idx_out=None, val_out=None, workspace=None, stream=None):
             or val_out.dtype != torch.float32:
         raise ValueError("idx_out must be int64 and val_out float32, each with room for k entries")
     if workspace is None:
-        workspace = torch.empty(max(topk_workspace_size(N), 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(topk_workspace_size(N, k, x.dtype), 1), dtype=torch.uint8, device=dev)
     rc = load().topk_select(_ptr(x), _dtype(x), N, k, _ptr(idx_out), _ptr(val_out), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(rc)
