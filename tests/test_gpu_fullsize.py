@@ -144,7 +144,8 @@ def test_topk_1b_client_update_properties():
     unique, and these properties pin it at any size: k entries, strictly
     increasing indices, the values read at those indices, every kept key at
     least every dropped key, and among keys equal to the threshold the kept
-    ones all lie below the dropped ones."""
+    ones all lie below the dropped ones.  The sampled and the three-pass
+    paths agree bit for bit."""
     N = 10 ** 9
     x = sd.client_delta_1b(0, N)
     k = fa.topk_count(N, 0.1)
@@ -167,6 +168,15 @@ def test_topk_1b_client_update_properties():
     # the threshold sits where the distribution says: b*ln(10) for Laplace(0, b)
     t = float(torch.tensor(T, dtype=torch.int32).view(torch.float32))
     assert abs(t / (1e-3 * math.log(10)) - 1) < 0.01
+    # the three-pass path (no sample) keeps exactly the same entries
+    fa.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 0)
+    try:
+        i3, v3 = fa.topk_select(x, k)
+        torch.cuda.synchronize()
+    finally:
+        fa.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 1)
+    assert torch.equal(i3, idx) and torch.equal(v3.view(torch.int32), val.view(torch.int32))
+    del i3, v3
     # and the oracle agrees on a window of the update (its own top-k of the
     # window, compared with the GPU's on the same window)
     w = x[:2_000_000].cpu().numpy()
