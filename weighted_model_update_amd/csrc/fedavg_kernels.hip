@@ -923,15 +923,11 @@ sparse_merge_kernel(const SparseArgs a)
                     const float w = a.w[k];
                     const uint32_t bit = 1u << (k & 31);
                     uint32_t *mrow = s_mask[MW > 1 ? (k >> 5) : 0];
-                    int64_t ix = gix[g];
-                    float val = gval[g];
-                    // index of the entry before this batch's first: before
-                    // the range, the previous range's last entry; in later
-                    // tiles the previous entry lies below t0, which the
-                    // ix >= t0 test covers; after a refill, the last entry
-                    // of the batch before
-                    int64_t first_prev = t0 == r0 ? s_prev0[k] : -1;
-                    while (true) {
+                    // One round: the batch's in-tile entries (a prefix) are
+                    // counted by wave ballots that meet in LDS, checked
+                    // against their predecessors and merged; returns the
+                    // count, and the batch's last index through batch_last.
+                    auto round = [&](int64_t ix, float val, int64_t first_prev, int64_t &batch_last) {
                         const bool in = ix < t1;
                         const uint64_t bal = __ballot(in);
                         const int64_t up = __shfl_up(ix, 1, 64);
@@ -946,7 +942,7 @@ sparse_merge_kernel(const SparseArgs a)
                             c += s_count[parity][v];
                         const int64_t prev =
                             lane > 0 ? up : (wave > 0 ? s_edge[parity][wave - 1] : first_prev);
-                        const int64_t batch_last = s_edge[parity][WAVES - 1];
+                        batch_last = s_edge[parity][WAVES - 1];
                         parity ^= 1;
                         if (in) {
                             if (ix <= prev || ix < t0) {
@@ -957,17 +953,33 @@ sparse_merge_kernel(const SparseArgs a)
                                 atomicOr(&mrow[l], bit);
                             }
                         }
-                        p0 += c;
-                        if (c < SP_THREADS || p0 >= pend)
-                            break;
-                        // a whole batch was inside the tile: fetch the next
-                        first_prev = batch_last;
-                        const int64_t p = p0 + tid;
-                        ix = INT64_MAX;
-                        if (p < pend) {
-                            ix = a.idx[k][p];
-                            val = a.val[k][p];
-                        }
+                        return c;
+                    };
+                    // index of the entry before this batch's first: before
+                    // the range, the previous range's last entry; in later
+                    // tiles the previous entry lies below t0, which the
+                    // ix >= t0 test covers; after a refill, the last entry
+                    // of the batch before
+                    int64_t batch_last;
+                    int c = round(gix[g], gval[g], t0 == r0 ? s_prev0[k] : -1, batch_last);
+                    p0 += c;
+                    // A whole batch inside the tile (rare at the default
+                    // tile): read the next ones.  The refills live in their
+                    // own loop so the group's batches keep their own,
+                    // partial load waits.
+                    if (c == SP_THREADS && p0 < pend) {
+                        do {
+                            const int64_t first_prev = batch_last;
+                            const int64_t p = p0 + tid;
+                            int64_t rix = INT64_MAX;
+                            float rval = 0.0f;
+                            if (p < pend) {
+                                rix = a.idx[k][p];
+                                rval = a.val[k][p];
+                            }
+                            c = round(rix, rval, first_prev, batch_last);
+                            p0 += c;
+                        } while (c == SP_THREADS && p0 < pend);
                     }
                     if (tid == 0)
                         s_cur[k] = p0;
