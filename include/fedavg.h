@@ -379,9 +379,9 @@ int fedavg_controller_step(int P, const double *t, const double *e, const int64_
  * ------------------------------------------------------------------------ */
 
 /* Device workspace bytes topk_select needs to keep k of N values of dtype
-   (it grows with k: below N/4 kept fp32 values, N/8 bf16, it holds a
-   staging copy of the entries near and above the threshold).  FA_ERR_RANGE
-   unless 0 <= k <= N. */
+   (it grows with k: while k < N/3 for fp32, N/4 for bf16, it holds a
+   staging copy of the entries near and above the threshold, 6 or 4 bytes
+   each).  FA_ERR_RANGE unless 0 <= k <= N. */
 int topk_workspace_size(fa_dtype dtype, int64_t N, int64_t k, size_t *bytes);
 
 /*

@@ -74,14 +74,16 @@ def test_host_side_argument_errors_need_no_device():
 
 
 def test_topk_workspace_holds_a_staging_copy_only_while_it_pays():
-    """Up to N/4 kept fp32 values (N/8 bf16) the workspace grows by 8 bytes
-    per kept entry for the staging copy; beyond that it does not grow."""
+    """While 3k < N for fp32 (4k < N for bf16) the workspace grows by 6 (4)
+    bytes per kept entry for the staging copy; beyond that it does not grow."""
     N = 10 ** 6
-    f = [fa.topk_workspace_size(N, k, torch.float32) for k in (1, 1001, N // 4 - 1, N // 4, N)]
-    assert abs((f[1] - f[0]) - 8 * 1000) <= 8 * 256     # staging is carved in 256 regions
+    kf, kb = (N - 1) // 3, (N - 1) // 4          # the largest k that still stages
+    f = [fa.topk_workspace_size(N, k, torch.float32) for k in (1, 1001, kf, kf + 1, N)]
+    assert abs((f[1] - f[0]) - 6 * 1000) <= 6 * 256     # staging is carved in 256 regions
     assert f[3] < f[2] and f[3] == f[4]
-    h = [fa.topk_workspace_size(N, k, torch.bfloat16) for k in (N // 8 - 1, N // 8)]
-    assert h[1] < h[0] and h[1] == f[4]
+    h = [fa.topk_workspace_size(N, k, torch.bfloat16) for k in (1, 1001, kb, kb + 1)]
+    assert abs((h[1] - h[0]) - 4 * 1000) <= 4 * 256
+    assert h[3] < h[2] and h[3] == f[4]
 
 
 def test_workspace_sizes_do_not_depend_on_the_number_of_clients():

@@ -93,15 +93,19 @@ struct TopkWs {
     int64_t *ch_ties, *ch_off;  // per scan chunk: ties before it, first output position
     u32x2 *cand;                // (key, position in tile), TK_REGIONS regions of rcap
     int64_t rcap;
-    u32x2 *stage;               // (raw bits, position in tile), TK_REGIONS regions of tcap
+    void *sval;                 // staged value bits (uint32 for fp32, uint16 for bf16) and
+    uint16_t *sloc;             // position in tile, parallel arrays: TK_REGIONS regions of tcap
     int64_t tcap;
 };
 
 __host__ __device__ constexpr int64_t round4(int64_t n) { return (n + 3) / 4 * 4; }
 
-// Staging pays when writing and re-reading 8 bytes per kept entry costs less
-// than a second read of the update: k < N/4 for fp32, k < N/8 for bf16.
-bool staging_pays(int64_t N, int64_t k, int dt) { return dt == DT_F32 ? 4 * k < N : 8 * k < N; }
+// A staged entry is the value's bits (4 bytes for fp32, 2 for bf16) and its
+// 2-byte position in the tile.  Staging pays when writing and re-reading the
+// entries costs less than a second read of the update: 12 k < 4 N for fp32,
+// 8 k < 2 N for bf16.
+constexpr int64_t staged_bytes(int dt) { return dt == DT_F32 ? 6 : 4; }
+bool staging_pays(int64_t N, int64_t k, int dt) { return dt == DT_F32 ? 3 * k < N : 4 * k < N; }
 
 struct Sizes {
     int64_t nt, ntp, nch, rcap, tcap;
@@ -119,11 +123,11 @@ Sizes sizes_of(int64_t N, int64_t k, int dt)
     s.tcap = staging_pays(N, k, dt) ? (k + N / 64 + 65536 + TK_REGIONS - 1) / TK_REGIONS : 0;
     s.bytes = (size_t)2 * TK_MAX_BINS * 8 + 256 + (size_t)TK_REGIONS * TK_CSTRIDE * 8 +
               (size_t)s.ntp * (3 * 8 + 6 * 4) + (size_t)s.nch * 4 * 8 +
-              (size_t)TK_REGIONS * (s.rcap + s.tcap) * 8;
+              (size_t)TK_REGIONS * s.rcap * 8 + (size_t)TK_REGIONS * s.tcap * staged_bytes(dt);
     return s;
 }
 
-TopkWs carve(void *ws, const Sizes &s)
+TopkWs carve(void *ws, const Sizes &s, int dt)
 {
     char *w = static_cast<char *>(ws);
     TopkWs p;
@@ -151,7 +155,9 @@ TopkWs carve(void *ws, const Sizes &s)
     w += s.nch * 4 * 8;
     p.cand = reinterpret_cast<u32x2 *>(w);
     p.rcap = s.rcap;
-    p.stage = p.cand + TK_REGIONS * s.rcap;
+    p.sval = p.cand + TK_REGIONS * s.rcap;
+    p.sloc = reinterpret_cast<uint16_t *>(static_cast<char *>(p.sval) +
+                                          TK_REGIONS * s.tcap * (staged_bytes(dt) - 2));
     p.tcap = s.tcap;
     return p;
 }
@@ -461,6 +467,24 @@ __global__ __launch_bounds__(TK_SELECT_THREADS) void topk_sample_select_kernel(T
 
 // ------------------------------------------------------------ sampled path
 
+// A staged entry: the value (bf16 keeps its 16 bits) and its position.
+template <int DT> __device__ __forceinline__ void stage_put(const TopkWs &w, uint64_t at, uint32_t bits,
+                                                            uint32_t local)
+{
+    if constexpr (DT == DT_F32)
+        static_cast<uint32_t *>(w.sval)[at] = bits;
+    else
+        static_cast<uint16_t *>(w.sval)[at] = (uint16_t)(bits >> 16);
+    w.sloc[at] = (uint16_t)local;
+}
+template <int DT> __device__ __forceinline__ uint32_t stage_bits(const TopkWs &w, uint64_t at)
+{
+    if constexpr (DT == DT_F32)
+        return static_cast<const uint32_t *>(w.sval)[at];
+    else
+        return (uint32_t) static_cast<const uint16_t *>(w.sval)[at] << 16;
+}
+
 // Per tile, with the range [klo, khi] known: count the keys above khi,
 // compact the keys inside the range into the tile's candidate segment and,
 // with staging, every key at or above klo with its position into the tile's
@@ -557,7 +581,7 @@ __global__ __launch_bounds__(TT_THREADS, 5) void topk_split_range_kernel(const v
                     if (rt < TK_STAGE)
                         s_ent[rt] = u32x2{bits, local};
                     else
-                        w.stage[toff + rt] = u32x2{bits, local};
+                        stage_put<DT>(w, toff + rt, bits, local);
                 }
                 ++rt;
                 if (key <= hi) {
@@ -570,8 +594,10 @@ __global__ __launch_bounds__(TT_THREADS, 5) void topk_split_range_kernel(const v
         __syncthreads();
         if (toff != ~0ull) {
             const int n = (int)min((uint32_t)TK_STAGE, n_ge);
-            for (int i = threadIdx.x; i < n; i += TT_THREADS)
-                w.stage[toff + i] = s_ent[i];
+            for (int i = threadIdx.x; i < n; i += TT_THREADS) {
+                const u32x2 e = s_ent[i];
+                stage_put<DT>(w, toff + i, e.x, e.y);
+            }
         }
         __syncthreads(); // s_tot and s_ent are reused by the next tile
     }
@@ -937,6 +963,7 @@ constexpr int TW_THREADS = 128;
 constexpr int TW_WAVES = TW_THREADS / 64;
 constexpr int TW_ROUNDS = 8;
 
+template <int DT>
 __global__ __launch_bounds__(TW_THREADS) void topk_write_staged_kernel(int64_t nt, TopkWs w,
                                                                        int64_t k_out,
                                                                        int64_t *idx_out,
@@ -950,7 +977,7 @@ __global__ __launch_bounds__(TW_THREADS) void topk_write_staged_kernel(int64_t n
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
         const uint32_t n = w.tcnt[tile];
-        const u32x2 *seg = w.stage + w.toff[tile];
+        const uint64_t seg = w.toff[tile];
         const uint32_t tk = w.take[tile];
         const int64_t base = w.off[tile];
         const int64_t tile0 = tile * TK_TILE;
@@ -960,7 +987,7 @@ __global__ __launch_bounds__(TW_THREADS) void topk_write_staged_kernel(int64_t n
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
-                ent[i] = p < n ? seg[p] : u32x2{0u, 0u};
+                ent[i] = p < n ? u32x2{stage_bits<DT>(w, seg + p), (uint32_t)w.sloc[seg + p]} : u32x2{0u, 0u};
             }
             uint32_t exw[R];
 #pragma unroll
@@ -1148,7 +1175,7 @@ hipError_t topk_run(const void *x, int64_t N, int64_t k, int64_t *idx_out, float
                     void *ws, int cus, hipStream_t s)
 {
     const Sizes sz = sizes_of(N, k, DT);
-    const TopkWs w = carve(ws, sz);
+    const TopkWs w = carve(ws, sz, DT);
     const int64_t nt = sz.nt;
     const bool vec_ok = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
     const bool staging = sz.tcap > 0;
@@ -1194,7 +1221,7 @@ hipError_t topk_run(const void *x, int64_t N, int64_t k, int64_t *idx_out, float
     topk_scan_down_kernel<<<(unsigned)sz.nch, 256, 0, s>>>(nt, w);
     const bool staged = plan.on && staging;
     if (staged)
-        topk_write_staged_kernel<<<work_grid, TW_THREADS, 0, s>>>(nt, w, k, idx_out, val_out);
+        topk_write_staged_kernel<DT><<<work_grid, TW_THREADS, 0, s>>>(nt, w, k, idx_out, val_out);
     topk_write_input_kernel<DT><<<staged ? idle_grid : work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w, staged, k, idx_out, val_out);
     return hipGetLastError();
 }
