@@ -134,6 +134,22 @@ def test_a_misleading_sample_falls_back_to_the_full_path(dt, sampled_small):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_threshold_in_a_gap_between_clusters(dt, path):
+    """Half the magnitudes near 1e-6, half near 1: at k = N/2 the sampled
+    range reaches across the gap, many octaves wide, so the sampled path
+    cannot count its digits in two passes and the call takes the full
+    path.  At k = N/2 +- 1000 the threshold sits inside a cluster."""
+    r = np.random.default_rng(71)
+    N = 1 << 21
+    big = r.random(N) < 0.5
+    x = np.where(big, r.laplace(0.0, 1.0, N), r.laplace(0.0, 1e-6, N)).astype(np.float32)
+    x = synth.bf16_bits_from_f32(x) if dt == "bf16" else x
+    nbig = int(big.sum())
+    for k in (nbig, nbig - 1000, nbig + 1000):
+        same(run_topk(x, dt, k), expect(x, dt, k))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_layered_update(dt, path):
     """An update made of layers of very different scales and sizes (a few
     small layers dominate the top entries): the kept set crosses layers."""

@@ -72,6 +72,9 @@ struct TopkState {
     uint32_t klo, khi;
     uint32_t sbin_hi, sbin_lo;  // sample: top-digit bins of the two order statistics
     int64_t srank_hi, srank_lo; // and their ranks inside those bins
+    // sampled path: T's digits are those of d = (key - klo) >> g, the upper
+    // one d >> sh1 (found first, kept in dprefix) and the lower sh1 bits
+    uint32_t g, sh1, dprefix;
 };
 static_assert(sizeof(TopkState) <= 256, "state slot");
 
@@ -375,40 +378,46 @@ __global__ __launch_bounds__(TK_THREADS) void topk_sample_hist_kernel(const void
     }
 }
 
-// s[b] = sum over u >= b of hist[u] for b < bins, s[bins] = 0, by a
-// Hillis-Steele scan from the top bin down (each step reads before any
-// thread writes).  TK_SELECT_THREADS threads; ends with a barrier.
-__device__ void suffix_sums(const unsigned long long *hist, int bins, unsigned long long *s)
+// The bin b of hist[0..bins) holding the rank-th largest key, counting from
+// the top bin down: suffix(b) >= rank > suffix(b + 1), with suffix(b) the sum
+// of hist[u] for u >= b (there is one when 1 <= rank <= suffix(0)); *rem
+// gets rank - suffix(b + 1), the rank left inside the bin.  Every thread
+// gets both; -1 when there is no such bin.  Thread t holds bins
+// bins-1-2t and bins-2-2t, so a prefix scan over threads is the suffix scan
+// over bins.  TK_SELECT_THREADS threads; ends with a barrier.
+__device__ int select_bin(const unsigned long long *hist, int bins, int64_t rank, int64_t *rem,
+                          unsigned long long *s_wtot, int *s_bin, int64_t *s_rem)
 {
-    const int t = threadIdx.x;
-    for (int b = t; b < bins; b += blockDim.x)
-        s[b] = hist[b];
-    if (t == 0)
-        s[bins] = 0ull;
-    __syncthreads();
-    for (int d = 1; d < bins; d <<= 1) {
-        unsigned long long add[2] = {0ull, 0ull};
-        for (int i = 0, b = t; b < bins; b += blockDim.x, ++i)
-            add[i] = b + d < bins ? s[b + d] : 0ull;
-        __syncthreads();
-        for (int i = 0, b = t; b < bins; b += blockDim.x, ++i)
-            s[b] += add[i];
-        __syncthreads();
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int hi = bins - 1 - 2 * t, lo = hi - 1;
+    const unsigned long long hh = hi >= 0 ? hist[hi] : 0ull, hl = lo >= 0 ? hist[lo] : 0ull;
+    const unsigned long long pair = hh + hl;
+    unsigned long long inc = pair;
+    for (int d = 1; d < 64; d <<= 1) {
+        const unsigned long long o = __shfl_up(inc, d, 64);
+        if (lane >= d)
+            inc += o;
     }
-}
-
-// The bin b with s[b] >= rank > s[b + 1] (there is one when 1 <= rank <=
-// s[0]), else -1; every thread gets it.  Ends with a barrier.
-__device__ int find_bin(const unsigned long long *s, int bins, int64_t rank, int *s_pick)
-{
-    if (threadIdx.x == 0)
-        *s_pick = -1;
+    if (lane == 63)
+        s_wtot[wave] = inc;
+    if (t == 0)
+        *s_bin = -1;
     __syncthreads();
-    for (int b = threadIdx.x; b < bins; b += blockDim.x)
-        if ((int64_t)s[b] >= rank && (int64_t)s[b + 1] < rank)
-            *s_pick = b;
+    for (int v = 0; v < wave; ++v)
+        inc += s_wtot[v];
+    // suffix(hi + 1) = ex, suffix(hi) = ex + hh = suffix(lo + 1), suffix(lo) = inc
+    const int64_t ex = (int64_t)(inc - pair), mid = ex + (int64_t)hh, all = (int64_t)inc;
+    if (hi >= 0 && mid >= rank && ex < rank) {
+        *s_bin = hi;
+        *s_rem = rank - ex;
+    }
+    if (lo >= 0 && all >= rank && mid < rank) {
+        *s_bin = lo;
+        *s_rem = rank - mid;
+    }
     __syncthreads();
-    const int b = *s_pick;
+    const int b = *s_bin;
+    *rem = *s_rem;
     __syncthreads();
     return b;
 }
@@ -424,19 +433,20 @@ __global__ __launch_bounds__(TK_SELECT_THREADS) void topk_sample_select_kernel(T
                                                                                int64_t r_hi,
                                                                                int64_t r_lo)
 {
-    __shared__ unsigned long long s_suffix[TK_MAX_BINS + 1];
-    __shared__ int s_pick;
+    __shared__ unsigned long long s_wtot[TK_SELECT_THREADS / 64];
+    __shared__ int s_bin;
+    __shared__ int64_t s_rem;
     TopkState *st = w.st;
     const int t = threadIdx.x;
+    int64_t rem_hi = 0, rem_lo = 0;
     if (level == 1) {
-        suffix_sums(w.hist, TK_MAX_BINS, s_suffix);
-        const int bh = has_hi ? find_bin(s_suffix, TK_MAX_BINS, r_hi, &s_pick) : 0;
-        const int bl = find_bin(s_suffix, TK_MAX_BINS, r_lo, &s_pick);
+        const int bh = has_hi ? select_bin(w.hist, TK_MAX_BINS, r_hi, &rem_hi, s_wtot, &s_bin, &s_rem) : 0;
+        const int bl = select_bin(w.hist, TK_MAX_BINS, r_lo, &rem_lo, s_wtot, &s_bin, &s_rem);
         if (t == 0) {
             st->sbin_hi = bh < 0 ? 0u : (uint32_t)bh;
-            st->srank_hi = has_hi && bh >= 0 ? r_hi - (int64_t)s_suffix[bh + 1] : 0;
+            st->srank_hi = has_hi && bh >= 0 ? rem_hi : 0;
             st->sbin_lo = bl < 0 ? 0u : (uint32_t)bl;
-            st->srank_lo = bl >= 0 ? r_lo - (int64_t)s_suffix[bl + 1] : 0;
+            st->srank_lo = bl >= 0 ? rem_lo : 0;
             st->ranged = bh >= 0 && bl >= 0;
         }
         for (int b = t; b < TK_MAX_BINS; b += blockDim.x)
@@ -447,12 +457,9 @@ __global__ __launch_bounds__(TK_SELECT_THREADS) void topk_sample_select_kernel(T
         const uint32_t bh = st->sbin_hi, bl = st->sbin_lo;
         const bool ok = st->ranged != 0u;
         int dh = TK_MAX_BINS - 1;
-        if (has_hi) {
-            suffix_sums(w.hist, TK_MAX_BINS, s_suffix);
-            dh = find_bin(s_suffix, TK_MAX_BINS, sr_hi, &s_pick);
-        }
-        suffix_sums(w.hist + TK_MAX_BINS, TK_MAX_BINS, s_suffix);
-        const int dl = find_bin(s_suffix, TK_MAX_BINS, sr_lo, &s_pick);
+        if (has_hi)
+            dh = select_bin(w.hist, TK_MAX_BINS, sr_hi, &rem_hi, s_wtot, &s_bin, &s_rem);
+        const int dl = select_bin(w.hist + TK_MAX_BINS, TK_MAX_BINS, sr_lo, &rem_lo, s_wtot, &s_bin, &s_rem);
         if (t == 0) {
             st->khi = has_hi ? (bh << TK_TOP_SHIFT) | ((uint32_t)max(dh, 0) << TK_SUB_SHIFT) |
                                    ((1u << TK_SUB_SHIFT) - 1u)
@@ -604,11 +611,12 @@ __global__ __launch_bounds__(TT_THREADS, 5) void topk_split_range_kernel(const v
 }
 
 // One workgroup of TK_REGIONS threads: the range holds T iff fewer than k
-// keys lie above khi and at least k at or above klo, and nothing overflowed.
+// keys lie above khi and at least k at or above klo, and nothing overflowed
+// (and the range is narrow enough for two digit passes, as below).
 // Then the sampled path is on, and T's rank among the candidates is k minus
 // the keys above khi; else the candidate counters are cleared for the full
 // path.
-__global__ __launch_bounds__(TK_REGIONS) void topk_check_kernel(TopkWs w, int64_t k)
+__global__ __launch_bounds__(TK_REGIONS) void topk_check_kernel(TopkWs w, int64_t k, int g)
 {
     __shared__ unsigned long long s_ge[TK_REGIONS / 64], s_in[TK_REGIONS / 64];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -631,13 +639,22 @@ __global__ __launch_bounds__(TK_REGIONS) void topk_check_kernel(TopkWs w, int64_
         n_in += s_in[v];
     }
     const int64_t above = (int64_t)(n_ge - n_in);
-    const bool fast = ranged && !fov && above < k && k <= (int64_t)n_ge;
+    // T's digits are then taken from d = (key - klo) >> g (g = 16 for bf16,
+    // whose keys have zeros below bit 16) in two passes of at most 11 bits:
+    // the range must span fewer than 2^22 values of d
+    const uint32_t span = (w.st->khi - w.st->klo) >> g;
+    const int B = span ? 32 - __clz(span) : 0;
+    const bool fast = ranged && !fov && above < k && k <= (int64_t)n_ge && B <= 22;
     if (!fast)
         w.rcnt[t * TK_CSTRIDE] = 0ull;
     if (t == 0) {
         w.st->fast = fast;
-        if (fast)
+        if (fast) {
             w.st->rank = k - above;
+            w.st->g = (uint32_t)g;
+            w.st->sh1 = B > 11 ? (uint32_t)(B - 11) : 0u;
+            w.st->dprefix = 0u;
+        }
     }
 }
 
@@ -715,24 +732,29 @@ __global__ __launch_bounds__(TT_THREADS) void topk_split_bin_kernel(const void *
 
 // ------------------------------------------------------------ both paths
 
-// LDS histogram of digit (key >> shift) & (bins-1) over keys whose bits
-// above the digit equal the prefix; added to the global histogram once per
-// workgroup.  Source: the candidates -- on the sampled path, and on the full
-// path after the first digit unless they overflowed -- else the whole
-// input.  The grid is a multiple of TK_REGIONS: gridDim / TK_REGIONS
-// workgroups share each candidate region.
+// LDS histogram of one digit, added to the global histogram once per
+// workgroup.  Full path: digit (key >> shift) & (bins-1) of the keys whose
+// bits above it equal the prefix, over the whole input for the first digit
+// (pass 1) and over the candidates after it unless they overflowed.
+// Sampled path, over the candidates: pass 1 the upper digit d >> sh1 of
+// d = (key - klo) >> g, pass 2 the lower sh1 bits of the candidates whose
+// upper digit is dprefix; pass 3 has nothing to do.  The grid is a multiple
+// of TK_REGIONS: gridDim / TK_REGIONS workgroups share each candidate region.
 template <int DT>
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, int64_t N,
-                                                               bool vec_ok, TopkWs w, int shift,
-                                                               int bits, bool first_digit)
+                                                               bool vec_ok, TopkWs w, int pass,
+                                                               int shift, int bits)
 {
     __shared__ uint32_t s_hist[TK_WAVES][TK_MAX_BINS];
-    const int bins = 1 << bits;
+    const bool fast = w.st->fast != 0u;
+    if (fast && pass == 3)
+        return;
+    const int bins = fast ? TK_MAX_BINS : 1 << bits;
     const uint32_t above =
         (shift + bits >= 31) ? 0u : (0x7FFFFFFFu >> (shift + bits)) << (shift + bits);
     const uint32_t prefix = w.st->prefix & above;
-    const bool fast = w.st->fast != 0u;
-    const bool input = first_digit ? !fast : (!fast && w.st->overflow);
+    const uint32_t klo = w.st->klo, g = w.st->g, sh1 = w.st->sh1, dprefix = w.st->dprefix;
+    const bool input = pass == 1 ? !fast : (!fast && w.st->overflow);
     const int wave = threadIdx.x >> 6;
     for (int b = threadIdx.x; b < TK_WAVES * bins; b += blockDim.x)
         s_hist[b / bins][b % bins] = 0u;
@@ -740,8 +762,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
 
     uint32_t *h = s_hist[wave];
     auto count = [&](uint32_t key) {
-        if ((key & above) == prefix)
+        if (fast) {
+            const uint32_t d = (key - klo) >> g;
+            if (pass == 1)
+                atomicAdd(&h[d >> sh1], 1u);
+            else if ((d >> sh1) == dprefix)
+                atomicAdd(&h[d & ((1u << sh1) - 1u)], 1u);
+        } else if ((key & above) == prefix) {
             atomicAdd(&h[(key >> shift) & (uint32_t)(bins - 1)], 1u);
+        }
     };
     if (input) {
         constexpr int V = Vec<DT>::N;
@@ -776,50 +805,83 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
     }
 }
 
-// One workgroup: the largest digit d with sum_{u >= d} hist[u] >= rank joins
-// the prefix, rank drops by the count of larger digits, and the histogram is
-// cleared for the next pass.
-__global__ __launch_bounds__(TK_SELECT_THREADS) void topk_select_kernel(TopkWs w, int shift, int bits)
+// One workgroup: the digit holding the rank-th key is chosen, the rank drops
+// to the rank inside it, and the histogram is cleared for the next pass.
+// Full path: the digit joins the prefix at `shift`.  Sampled path: pass 1
+// keeps the upper digit, pass 2 completes T = klo + (((dprefix << sh1) |
+// digit) << g); pass 3 has nothing to do.
+__global__ __launch_bounds__(TK_SELECT_THREADS) void topk_select_kernel(TopkWs w, int pass, int shift,
+                                                                        int bits)
 {
-    __shared__ unsigned long long s_suffix[TK_MAX_BINS + 1];
-    __shared__ int s_pick;
-    const int bins = 1 << bits;
-    // read before the first barrier: thread 0 rewrites it at the end
-    const int64_t rank = w.st->rank;
-    suffix_sums(w.hist, bins, s_suffix);
-    const int b = find_bin(s_suffix, bins, rank, &s_pick);
+    __shared__ unsigned long long s_wtot[TK_SELECT_THREADS / 64];
+    __shared__ int s_bin;
+    __shared__ int64_t s_rem;
+    TopkState *st = w.st;
+    const bool fast = st->fast != 0u;
+    if (fast && pass == 3)
+        return;
+    const int bins = fast ? TK_MAX_BINS : 1 << bits;
+    // read before the first barrier: thread 0 rewrites them at the end
+    const int64_t rank = st->rank;
+    const uint32_t dprefix = st->dprefix;
+    int64_t rem;
+    const int b = select_bin(w.hist, bins, rank, &rem, s_wtot, &s_bin, &s_rem);
     if (threadIdx.x == 0 && b >= 0) {
-        w.st->prefix |= (uint32_t)b << shift;
-        w.st->rank = rank - (int64_t)s_suffix[b + 1];
+        if (!fast)
+            st->prefix |= (uint32_t)b << shift;
+        else if (pass == 1)
+            st->dprefix = (uint32_t)b;
+        else
+            st->prefix = st->klo + ((((dprefix << st->sh1) | (uint32_t)b)) << st->g);
+        st->rank = rem;
     }
     for (int u = threadIdx.x; u < bins; u += blockDim.x)
         w.hist[u] = 0ull;
 }
 
-// Per tile, one wave each: keys above and equal to T from the tile's
-// candidates, plus its keys above them.  Skipped after a candidate overflow
-// on the full path (topk_tile_count_input_kernel counts then).
+// Per tile: keys above and equal to T from the tile's candidates, plus its
+// keys above them.  Each wave takes TC_TPW tiles and issues their first
+// loads together.  Skipped after a candidate overflow on the full path
+// (topk_tile_count_input_kernel counts then).
+constexpr int TC_TPW = 4;
+
+__device__ __forceinline__ uint32_t above_or_tie(uint32_t key, uint32_t T)
+{
+    return key > T ? (1u << 16) : (key == T ? 1u : 0u);
+}
+
 __global__ __launch_bounds__(TT_THREADS) void topk_tile_count_kernel(int64_t nt, TopkWs w)
 {
     if (!w.st->fast && w.st->overflow)
         return;
-    const int64_t tile = (int64_t)blockIdx.x * TT_WAVES + (threadIdx.x >> 6);
-    if (tile >= nt)
+    const int64_t tile0 = ((int64_t)blockIdx.x * TT_WAVES + (threadIdx.x >> 6)) * TC_TPW;
+    if (tile0 >= nt)
         return; // no barriers below
-    const int lane = threadIdx.x & 63;
+    const uint32_t lane = threadIdx.x & 63;
     const uint32_t T = w.st->prefix;
-    const unsigned long long c0 = w.coff[tile];
-    const uint32_t n = w.ccnt[tile];
-    uint32_t c = 0; // (above T) << 16 | (equal to T); each below 2^16
-    for (uint32_t i = lane; i < n; i += 64) {
-        const uint32_t key = w.cand[c0 + i].x;
-        c += key > T ? (1u << 16) : (key == T ? 1u : 0u);
+    uint32_t n[TC_TPW], c[TC_TPW];
+    unsigned long long c0[TC_TPW];
+#pragma unroll
+    for (int i = 0; i < TC_TPW; ++i) {
+        const bool ok = tile0 + i < nt;
+        n[i] = ok ? w.ccnt[tile0 + i] : 0u;
+        c0[i] = ok ? w.coff[tile0 + i] : 0ull;
     }
-    for (int d = 32; d > 0; d >>= 1)
-        c += __shfl_down(c, d, 64);
-    if (lane == 0) {
-        w.gt[tile] = (c >> 16) + w.def[tile];
-        w.eq[tile] = c & 0xFFFFu;
+#pragma unroll
+    for (int i = 0; i < TC_TPW; ++i)
+        c[i] = lane < n[i] ? above_or_tie(w.cand[c0[i] + lane].x, T) : 0u;
+#pragma unroll
+    for (int i = 0; i < TC_TPW; ++i)
+        for (uint32_t j = lane + 64; j < n[i]; j += 64)
+            c[i] += above_or_tie(w.cand[c0[i] + j].x, T);
+    // each below 2^16 per tile, so the packed sums never carry
+#pragma unroll
+    for (int i = 0; i < TC_TPW; ++i) {
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(c[i]), 63);
+        if (lane == 0 && tile0 + i < nt) {
+            w.gt[tile0 + i] = (tot >> 16) + w.def[tile0 + i];
+            w.eq[tile0 + i] = tot & 0xFFFFu;
+        }
     }
 }
 
@@ -1199,22 +1261,23 @@ hipError_t topk_run(const void *x, int64_t N, int64_t k, int64_t *idx_out, float
         topk_sample_hist_kernel<DT><<<sg, TK_THREADS, 0, s>>>(x, plan.vec_units, plan.units, plan.mu, w, 2, plan.has_hi);
         topk_sample_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 2, plan.has_hi, plan.r_hi, plan.r_lo);
         topk_split_range_kernel<DT><<<work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w, staging);
-        topk_check_kernel<<<1, TK_REGIONS, 0, s>>>(w, k);
+        topk_check_kernel<<<1, TK_REGIONS, 0, s>>>(w, k, DT == DT_BF16 ? 16 : 0);
     }
-    // digit 1 (key bits 30..20): from the candidates on the sampled path,
-    // else from the whole input, followed on the full path by the split
-    topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, TK_TOP_SHIFT, 11, true);
-    topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, TK_TOP_SHIFT, 11);
+    // Full path: digit 1 (key bits 30..20) from the whole input, the split,
+    // then digits 2 (bits 19..9) and, for fp32, 3 (bits 8..0) from the
+    // candidates; a bf16 key has zeros below bit 16, so two digits decide it.
+    // Sampled path: two digits of (key - klo) >> g from the candidates; the
+    // third pair of launches exits.
+    topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, 1, TK_TOP_SHIFT, 11);
+    topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 1, TK_TOP_SHIFT, 11);
     topk_split_bin_kernel<DT><<<plan.on ? idle_grid : work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w);
-    // digits 2 (bits 19..9) and, for fp32, 3 (bits 8..0); a bf16 key has
-    // zeros below bit 16, so two digits decide it
-    topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, TK_SUB_SHIFT, 11, false);
-    topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, TK_SUB_SHIFT, 11);
+    topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, 2, TK_SUB_SHIFT, 11);
+    topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 2, TK_SUB_SHIFT, 11);
     if (DT == DT_F32) {
-        topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, 0, 9, false);
-        topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 0, 9);
+        topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, 3, 0, 9);
+        topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 3, 0, 9);
     }
-    topk_tile_count_kernel<<<(unsigned)((nt + TT_WAVES - 1) / TT_WAVES), TT_THREADS, 0, s>>>(nt, w);
+    topk_tile_count_kernel<<<(unsigned)((nt + TT_WAVES * TC_TPW - 1) / (TT_WAVES * TC_TPW)), TT_THREADS, 0, s>>>(nt, w);
     topk_tile_count_input_kernel<DT><<<idle_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w);
     topk_scan_reduce_kernel<<<(unsigned)sz.nch, 256, 0, s>>>(nt, w);
     topk_scan_top_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(sz.nch, w);
