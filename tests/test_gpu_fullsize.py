@@ -139,6 +139,52 @@ def test_streaming_8b_k32_sampled():
     check(got, ref, mag, "bf16", label="streaming 8B sampled")
 
 
+def test_two_level_8b_three_silos_sampled():
+    """Two-level aggregation at the 8B size, through the call the benchmark
+    times: each of three silos is one client with n = W_g (its partial is
+    W_g * x_g, one fp32 rounding, as a silo accumulator forms it), the
+    partials enter the top-level accumulator as pseudo-clients in deltas
+    mode, and finalize writes bf16.  In exact arithmetic this is the flat
+    weighted average of the silos' clients: the flat oracle checks sampled
+    outputs."""
+    N = synth.numel_of(synth.stream_8b_tensor_shapes())
+    assert N == 8_030_261_248
+    W = [int(w) for w in synth.sample_counts(synth.CFG_STREAM_8B, 3, 1000, 80000)]
+    at = sample_positions(N, 100_000, 11)
+    at_dev = torch.from_numpy(at).cuda()
+    acc_b, _, _, stag_b = fa.fedavg_workspace_size(N, 0, 1 << 20, 1)
+    acc = torch.empty(acc_b // 4, dtype=torch.float32, device="cuda")
+    staging = torch.empty(stag_b, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda")
+    xs = []
+    h = fa.fedavg_begin(N, "deltas", False, acc, None, None, staging, 1 << 20, 1)
+    try:
+        for k in range(3):
+            g.manual_seed(9100 + k)
+            x = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+            x.normal_(0.0, 1e-3, generator=g)
+            xs.append(gather_bits(x, at_dev))
+            part = x.float()
+            del x
+            part.mul_(float(W[k]))
+            fa.fedavg_accumulate_partial(h, k, W[k], 1, part, offset=0)
+            torch.cuda.synchronize()
+            del part
+        g.manual_seed(9200)
+        base = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+        base.normal_(0.0, 0.02, generator=g)
+        base_at = gather_bits(base, at_dev)
+        out = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+        fa.fedavg_finalize(h, base, out)
+        fa.fedavg_sync(h)
+    finally:
+        fa.fedavg_destroy(h)
+    got = gather_bits(out, at_dev)
+    ref, mag, _, _ = oracle.weighted_average(xs, np.array(W, np.int64), mode=oracle.DELTAS, base=base_at,
+                                             x_dtype=oracle.BF16, base_dtype=oracle.BF16)
+    check(got, ref, mag, "bf16", label="two-level 8B sampled")
+
+
 def test_topk_1b_client_update_properties():
     """Top-10% of a 10^9-parameter fp32 client update.  The kept set is
     unique, and these properties pin it at any size: k entries, strictly
