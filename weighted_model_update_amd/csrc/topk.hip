@@ -498,8 +498,12 @@ template <int DT> __device__ __forceinline__ uint32_t stage_bits(const TopkWs &w
 // staging segment -- both in index order.  Segments are reserved in the
 // tile's region (tile mod TK_REGIONS) with one atomic each; a region that
 // runs out sets `fov` and the check sends the call down the full path.
+// Resident waves per SIMD the split is compiled for: 6 fits fp32 tiles with a
+// 12-byte spill and is faster; bf16 tiles spill heavily above 5.
+template <int DT> constexpr int split_waves() { return DT == DT_F32 ? 6 : 5; }
+
 template <int DT>
-__global__ __launch_bounds__(TT_THREADS, 5) void topk_split_range_kernel(const void *x, int64_t N,
+__global__ __launch_bounds__(TT_THREADS, split_waves<DT>()) void topk_split_range_kernel(const void *x, int64_t N,
                                                                       bool vec_ok, int64_t nt,
                                                                       TopkWs w, bool staging)
 {
