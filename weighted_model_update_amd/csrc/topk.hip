@@ -349,21 +349,36 @@ __global__ __launch_bounds__(TK_THREADS) void topk_sample_hist_kernel(const void
                 atomicAdd(&s_h[1][d], 1u);
         }
     };
-    // floor(s * units / mu) without overflow: s * q + floor(s * rem / mu)
+    // floor(s * units / mu) without overflow: s * q + floor(s * rem / mu);
+    // SU units' loads are issued before any is counted
+    constexpr int SU = 4;
     const int64_t q = units / mu, rem = units % mu;
-    for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < mu;
-         s += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t u = s * q + (s * rem) / mu;
-        if (vec_units) {
-            constexpr int V = Vec<DT>::N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    auto unit = [&](int64_t s) { return s * q + (s * rem) / mu; };
+    int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (vec_units) {
+        constexpr int V = Vec<DT>::N;
+        for (; s + (SU - 1) * stride < mu; s += SU * stride) {
+            uint32_t b[SU][V];
+#pragma unroll
+            for (int j = 0; j < SU; ++j)
+                Vec<DT>::load(x, unit(s + j * stride), b[j]);
+#pragma unroll
+            for (int j = 0; j < SU; ++j)
+#pragma unroll
+                for (int i = 0; i < V; ++i)
+                    count(key_of_bits(b[j][i]));
+        }
+        for (; s < mu; s += stride) {
             uint32_t b[V];
-            Vec<DT>::load(x, u, b);
+            Vec<DT>::load(x, unit(s), b);
 #pragma unroll
             for (int i = 0; i < V; ++i)
                 count(key_of_bits(b[i]));
-        } else {
-            count(key_of_bits(bits_at<DT>(x, u)));
         }
+    } else {
+        for (; s < mu; s += stride)
+            count(key_of_bits(bits_at<DT>(x, unit(s))));
     }
     __syncthreads();
     for (int b = threadIdx.x; b < TK_MAX_BINS; b += blockDim.x) {
@@ -776,12 +791,27 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
             atomicAdd(&h[(key >> shift) & (uint32_t)(bins - 1)], 1u);
         }
     };
+    // the loops issue HU loads before counting any of them, so a thread
+    // waits for one round trip per HU elements rather than per element
+    constexpr int HU = 8;
     if (input) {
         constexpr int V = Vec<DT>::N;
         const int64_t stride = (int64_t)gridDim.x * blockDim.x;
         const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
         const int64_t nvec = vec_ok ? N / V : 0;
-        for (int64_t v = t0; v < nvec; v += stride) {
+        int64_t v = t0;
+        for (; v + (HU / 2 - 1) * stride < nvec; v += (HU / 2) * stride) {
+            uint32_t b[HU / 2][V];
+#pragma unroll
+            for (int u = 0; u < HU / 2; ++u)
+                Vec<DT>::load(x, v + u * stride, b[u]);
+#pragma unroll
+            for (int u = 0; u < HU / 2; ++u)
+#pragma unroll
+                for (int q = 0; q < V; ++q)
+                    count(key_of_bits(b[u][q]));
+        }
+        for (; v < nvec; v += stride) {
             uint32_t b[V];
             Vec<DT>::load(x, v, b);
 #pragma unroll
@@ -795,7 +825,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
         const int64_t parts = gridDim.x / TK_REGIONS, part = blockIdx.x / TK_REGIONS;
         const int64_t n = min((int64_t)(w.rcnt[r * TK_CSTRIDE] & 0xFFFFFFFFull), w.rcap);
         const u32x2 *c = w.cand + (int64_t)r * w.rcap;
-        for (int64_t i = part * blockDim.x + threadIdx.x; i < n; i += parts * blockDim.x)
+        const int64_t step = parts * blockDim.x;
+        int64_t i = part * blockDim.x + threadIdx.x;
+        for (; i + (HU - 1) * step < n; i += HU * step) {
+            uint32_t kk[HU];
+#pragma unroll
+            for (int u = 0; u < HU; ++u)
+                kk[u] = c[i + u * step].x;
+#pragma unroll
+            for (int u = 0; u < HU; ++u)
+                count(kk[u]);
+        }
+        for (; i < n; i += step)
             count(c[i].x);
     }
     __syncthreads();
