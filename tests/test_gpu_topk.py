@@ -104,6 +104,35 @@ def test_special_values_and_signed_zeros(path):
         same(run_topk(x, "f32", k), expect(x, "f32", k))
 
 
+def test_special_values_bf16(path):
+    """The same specials in bf16: NaNs above infinity, -0 tied with +0,
+    subnormals (bf16 keeps fp32's exponent range)."""
+    r = np.random.default_rng(5)
+    N = 50_000
+    x = r.standard_normal(N).astype(np.float32)
+    x[r.choice(N, 50, replace=False)] = np.inf
+    x[r.choice(N, 50, replace=False)] = -np.inf
+    x[r.choice(N, 30, replace=False)] = np.nan
+    x[r.choice(N, 2000, replace=False)] = 0.0
+    x[r.choice(N, 2000, replace=False)] = -0.0
+    x[r.choice(N, 100, replace=False)] = 1e-39          # subnormal, kept by bf16
+    xb = synth.bf16_bits_from_f32(x)
+    xb[r.choice(N, 30, replace=False)] = 0xFFC1        # negative NaN with payload
+    for k in (10, 60, 110, 130, 20_000, 49_000):
+        same(run_topk(xb, "bf16", k), expect(xb, "bf16", k))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [1, 37, 5000])
+def test_small_k_on_a_large_update(dt, k, path):
+    """k far below the sample's resolution: the sample gives no upper bound,
+    the candidates are every key at or above its floor, and their absolute
+    digits decide the threshold."""
+    N = 3_000_017
+    x = laplace(81 + k, N, dt)
+    same(run_topk(x, dt, k), expect(x, dt, k))
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_unaligned_input(dt, path):
     N = 40_001
@@ -136,9 +165,10 @@ def test_a_misleading_sample_falls_back_to_the_full_path(dt, sampled_small):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_threshold_in_a_gap_between_clusters(dt, path):
     """Half the magnitudes near 1e-6, half near 1: at k = N/2 the sampled
-    range reaches across the gap, many octaves wide, so the sampled path
-    cannot count its digits in two passes and the call takes the full
-    path.  At k = N/2 +- 1000 the threshold sits inside a cluster."""
+    range reaches across the gap, many octaves wide, too wide for two
+    digits counted from its floor, so the candidates' absolute digits are
+    counted instead.  At k = N/2 +- 1000 the threshold sits inside a
+    cluster."""
     r = np.random.default_rng(71)
     N = 1 << 21
     big = r.random(N) < 0.5

@@ -72,9 +72,10 @@ struct TopkState {
     uint32_t klo, khi;
     uint32_t sbin_hi, sbin_lo;  // sample: top-digit bins of the two order statistics
     int64_t srank_hi, srank_lo; // and their ranks inside those bins
-    // sampled path: T's digits are those of d = (key - klo) >> g, the upper
-    // one d >> sh1 (found first, kept in dprefix) and the lower sh1 bits
-    uint32_t g, sh1, dprefix;
+    // sampled path with rel set: T's digits are those of d = (key - klo) >> g,
+    // the upper one d >> sh1 (found first, kept in dprefix) and the lower sh1
+    // bits; with rel clear (a range too wide) the candidates' absolute digits
+    uint32_t rel, g, sh1, dprefix;
 };
 static_assert(sizeof(TopkState) <= 256, "state slot");
 
@@ -630,8 +631,7 @@ __global__ __launch_bounds__(TT_THREADS, split_waves<DT>()) void topk_split_rang
 }
 
 // One workgroup of TK_REGIONS threads: the range holds T iff fewer than k
-// keys lie above khi and at least k at or above klo, and nothing overflowed
-// (and the range is narrow enough for two digit passes, as below).
+// keys lie above khi and at least k at or above klo, and nothing overflowed.
 // Then the sampled path is on, and T's rank among the candidates is k minus
 // the keys above khi; else the candidate counters are cleared for the full
 // path.
@@ -658,18 +658,20 @@ __global__ __launch_bounds__(TK_REGIONS) void topk_check_kernel(TopkWs w, int64_
         n_in += s_in[v];
     }
     const int64_t above = (int64_t)(n_ge - n_in);
+    const bool fast = ranged && !fov && above < k && k <= (int64_t)n_ge;
     // T's digits are then taken from d = (key - klo) >> g (g = 16 for bf16,
-    // whose keys have zeros below bit 16) in two passes of at most 11 bits:
-    // the range must span fewer than 2^22 values of d
+    // whose keys have zeros below bit 16) in two passes of at most 11 bits
+    // when the range spans fewer than 2^22 values of d; a wider range (no
+    // upper bound, for a small k) takes the candidates' absolute digits
     const uint32_t span = (w.st->khi - w.st->klo) >> g;
     const int B = span ? 32 - __clz(span) : 0;
-    const bool fast = ranged && !fov && above < k && k <= (int64_t)n_ge && B <= 22;
     if (!fast)
         w.rcnt[t * TK_CSTRIDE] = 0ull;
     if (t == 0) {
         w.st->fast = fast;
         if (fast) {
             w.st->rank = k - above;
+            w.st->rel = B <= 22;
             w.st->g = (uint32_t)g;
             w.st->sh1 = B > 11 ? (uint32_t)(B - 11) : 0u;
             w.st->dprefix = 0u;
@@ -752,13 +754,15 @@ __global__ __launch_bounds__(TT_THREADS) void topk_split_bin_kernel(const void *
 // ------------------------------------------------------------ both paths
 
 // LDS histogram of one digit, added to the global histogram once per
-// workgroup.  Full path: digit (key >> shift) & (bins-1) of the keys whose
-// bits above it equal the prefix, over the whole input for the first digit
-// (pass 1) and over the candidates after it unless they overflowed.
-// Sampled path, over the candidates: pass 1 the upper digit d >> sh1 of
-// d = (key - klo) >> g, pass 2 the lower sh1 bits of the candidates whose
-// upper digit is dprefix; pass 3 has nothing to do.  The grid is a multiple
-// of TK_REGIONS: gridDim / TK_REGIONS workgroups share each candidate region.
+// workgroup.  Absolute digits: digit (key >> shift) & (bins-1) of the keys
+// whose bits above it equal the prefix -- on the full path over the whole
+// input for the first digit (pass 1) and over the candidates after it unless
+// they overflowed, on the sampled path over the candidates.  Relative digits
+// (sampled path, narrow range), over the candidates: pass 1 the upper digit
+// d >> sh1 of d = (key - klo) >> g, pass 2 the lower sh1 bits of the
+// candidates whose upper digit is dprefix; pass 3 has nothing to do.  The
+// grid is a multiple of TK_REGIONS: gridDim / TK_REGIONS workgroups share
+// each candidate region.
 template <int DT>
 __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, int64_t N,
                                                                bool vec_ok, TopkWs w, int pass,
@@ -766,14 +770,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
 {
     __shared__ uint32_t s_hist[TK_WAVES][TK_MAX_BINS];
     const bool fast = w.st->fast != 0u;
-    if (fast && pass == 3)
+    const bool rel = fast && w.st->rel != 0u;
+    if (rel && pass == 3)
         return;
-    const int bins = fast ? TK_MAX_BINS : 1 << bits;
+    const int bins = rel ? TK_MAX_BINS : 1 << bits;
     const uint32_t above =
         (shift + bits >= 31) ? 0u : (0x7FFFFFFFu >> (shift + bits)) << (shift + bits);
     const uint32_t prefix = w.st->prefix & above;
     const uint32_t klo = w.st->klo, g = w.st->g, sh1 = w.st->sh1, dprefix = w.st->dprefix;
-    const bool input = pass == 1 ? !fast : (!fast && w.st->overflow);
+    const bool input = !fast && (pass == 1 || w.st->overflow);
     const int wave = threadIdx.x >> 6;
     for (int b = threadIdx.x; b < TK_WAVES * bins; b += blockDim.x)
         s_hist[b / bins][b % bins] = 0u;
@@ -781,7 +786,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
 
     uint32_t *h = s_hist[wave];
     auto count = [&](uint32_t key) {
-        if (fast) {
+        if (rel) {
             const uint32_t d = (key - klo) >> g;
             if (pass == 1)
                 atomicAdd(&h[d >> sh1], 1u);
@@ -852,9 +857,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const void *x, in
 
 // One workgroup: the digit holding the rank-th key is chosen, the rank drops
 // to the rank inside it, and the histogram is cleared for the next pass.
-// Full path: the digit joins the prefix at `shift`.  Sampled path: pass 1
-// keeps the upper digit, pass 2 completes T = klo + (((dprefix << sh1) |
-// digit) << g); pass 3 has nothing to do.
+// Absolute digits: the digit joins the prefix at `shift`.  Relative digits:
+// pass 1 keeps the upper digit, pass 2 completes T = klo + (((dprefix <<
+// sh1) | digit) << g); pass 3 has nothing to do.
 __global__ __launch_bounds__(TK_SELECT_THREADS) void topk_select_kernel(TopkWs w, int pass, int shift,
                                                                         int bits)
 {
@@ -862,17 +867,17 @@ __global__ __launch_bounds__(TK_SELECT_THREADS) void topk_select_kernel(TopkWs w
     __shared__ int s_bin;
     __shared__ int64_t s_rem;
     TopkState *st = w.st;
-    const bool fast = st->fast != 0u;
-    if (fast && pass == 3)
+    const bool rel = st->fast != 0u && st->rel != 0u;
+    if (rel && pass == 3)
         return;
-    const int bins = fast ? TK_MAX_BINS : 1 << bits;
+    const int bins = rel ? TK_MAX_BINS : 1 << bits;
     // read before the first barrier: thread 0 rewrites them at the end
     const int64_t rank = st->rank;
     const uint32_t dprefix = st->dprefix;
     int64_t rem;
     const int b = select_bin(w.hist, bins, rank, &rem, s_wtot, &s_bin, &s_rem);
     if (threadIdx.x == 0 && b >= 0) {
-        if (!fast)
+        if (!rel)
             st->prefix |= (uint32_t)b << shift;
         else if (pass == 1)
             st->dprefix = (uint32_t)b;
@@ -1311,8 +1316,9 @@ hipError_t topk_run(const void *x, int64_t N, int64_t k, int64_t *idx_out, float
     // Full path: digit 1 (key bits 30..20) from the whole input, the split,
     // then digits 2 (bits 19..9) and, for fp32, 3 (bits 8..0) from the
     // candidates; a bf16 key has zeros below bit 16, so two digits decide it.
-    // Sampled path: two digits of (key - klo) >> g from the candidates; the
-    // third pair of launches exits.
+    // Sampled path: the same digits from the candidates, or for a narrow
+    // range two digits of (key - klo) >> g and the third pair of launches
+    // exits.
     topk_hist_kernel<DT><<<hist_grid, TK_THREADS, 0, s>>>(x, N, vec_ok, w, 1, TK_TOP_SHIFT, 11);
     topk_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 1, TK_TOP_SHIFT, 11);
     topk_split_bin_kernel<DT><<<plan.on ? idle_grid : work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w);
