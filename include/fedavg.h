@@ -428,7 +428,8 @@ typedef enum {
                                           (default 0: no cap, one 8-parameter
                                           vector per thread) */
     FA_OPT_MASK_VECTORS_PER_BLOCK = 2, /* masked aggregate: 8-parameter vectors
-                                          per workgroup (default 1024) */
+                                          per workgroup, which sets the grid
+                                          (default 2048) */
     FA_OPT_SPARSE_BLOCKS = 3,          /* sparse merge: parameter ranges, i.e.
                                           workgroups (default 0: 65536, fewer
                                           when N is small; max 65536) */

@@ -59,7 +59,7 @@ bool overlap_ok(const void *a, size_t abytes, const void *b, size_t bbytes)
 // Launch-shape options (fedavg_set_option).
 int64_t g_blocks_per_cu = 0;     // grid-stride cap, workgroups per CU (0: none)
 int64_t g_resident_per_cu = 3;   // dense kernel: resident workgroups per CU (0: no cap)
-int64_t g_mask_vpb = 1024;       // masked kernel: 8-parameter vectors per block
+int64_t g_mask_vpb = 2048;       // masked kernel: 8-parameter vectors per block
 int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: SPARSE_DEFAULT_BLOCKS)
 int64_t g_sparse_tile = fa::SP_DEFAULT_TILE;
 constexpr int64_t SPARSE_MAX_BLOCKS = 65536;

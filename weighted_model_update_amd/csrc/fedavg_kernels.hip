@@ -48,6 +48,7 @@ template <> struct io<DT_F32> {
     struct raw {
         f32x4 a, b;
     };
+    static __device__ __forceinline__ raw zero_raw() { return raw{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}; }
     static __device__ __forceinline__ raw load_raw(const void *p, int64_t e)
     {
         const f32x4 *q = reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + e);
@@ -95,6 +96,7 @@ template <> struct io<DT_BF16> {
     struct raw {
         u32x4 v;
     };
+    static __device__ __forceinline__ raw zero_raw() { return raw{u32x4{0u, 0u, 0u, 0u}}; }
     static __device__ __forceinline__ raw load_raw(const void *p, int64_t e)
     {
         return raw{__builtin_nontemporal_load(
@@ -460,7 +462,7 @@ __device__ __forceinline__ void masked_element_lds(const MaskedArgs &a, const in
 // tensors) are staged whole in LDS by every workgroup, in one round of
 // independent loads -- bounds and client presence together -- instead of a
 // search followed by a windowed fetch.  Each thread then walks its vectors
-// (vpb per workgroup, blockDim apart) NV at a time with a segment cursor that
+// (the grid strides over all of them) NV at a time with a segment cursor that
 // only moves forward, so a vector costs one LDS compare in the usual case.
 // The loads of all NV vectors are issued before the first FMA: absent
 // clients are skipped, which leaves a wave fewer bytes in flight than the
@@ -481,12 +483,14 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
         segment_weights(a, t, s_mask[t], s_W[t]);
     __syncthreads();
 
+    // Grid-stride over the vectors (the grid holds about N / (8 vpb)
+    // workgroups): the resident workgroups sweep one window of the buffers
+    // together, which the DRAM serves better than as many separate runs.
     const int64_t nvec_all = (a.N + VEC - 1) / VEC;
-    const int64_t v_begin = (int64_t)blockIdx.x * a.vpb;
-    const int64_t v_end = min(v_begin + a.vpb, nvec_all);
-    const int64_t stride = blockDim.x;
+    const int64_t v_end = nvec_all;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int t = -1;
-    for (int64_t v = v_begin + tid; v < v_end; v += NV * stride) {
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + tid; v < v_end; v += NV * stride) {
         int64_t ev[NV];
         bool has[NV], fast[NV];
         uint64_t m[NV];
@@ -515,19 +519,27 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
             for (int j = 0; j < VEC; ++j)
                 acc[u][j] = 0.0f;
         for (int k0 = 0; k0 < a.K; k0 += 8) {
+            // Only present clients are read.  Every FMA runs, an absent
+            // client's as 0 * 0 (exact: acc starts at +0 and cannot become
+            // -0), so each load is consumed on every path and the compiler
+            // does not serialize the next loads behind a wait for all of them.
             typename io<XDT>::raw xr[NV][8];
+            float wk[NV][8];
 #pragma unroll
             for (int u = 0; u < NV; ++u)
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (k0 + k < a.K && ((m[u] >> (k0 + k)) & 1))
+                for (int k = 0; k < 8; ++k) {
+                    const bool on = k0 + k < a.K && ((m[u] >> (k0 + k)) & 1);
+                    xr[u][k] = io<XDT>::zero_raw();
+                    wk[u][k] = on ? a.w[k0 + k] : 0.0f;
+                    if (on)
                         xr[u][k] = io<XDT>::load_raw(a.x[k0 + k], ev[u]);
+                }
 #pragma unroll
             for (int u = 0; u < NV; ++u)
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
-                    if (k0 + k < a.K && ((m[u] >> (k0 + k)) & 1))
-                        io<XDT>::fma8(xr[u][k], a.w[k0 + k], acc[u]);
+                    io<XDT>::fma8(xr[u][k], wk[u][k], acc[u]);
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
