@@ -349,6 +349,72 @@ def bench_sparse(steps=10, warmup=2):
             "params_per_s": nnz / (avg * 1e-3)}
 
 
+def bench_sparse_stream(clients=20):
+    """Client-at-a-time sparse accumulate: the 10^9-parameter top-10% lists
+    of the sparse workload, each client's (index, value) pairs scattered into
+    the streaming accumulator in partial mode (fp32 sum, uint32 weight sum,
+    uint8 count per parameter), then one finalize.  Pair-level bytes are 12 B
+    read plus 18 B of read-modify-write per pair; DRAM moves whole lines, so
+    the line-level figure counts every 64-byte line of the three arrays a
+    client touches, read and written, plus the pairs."""
+    import torch
+    import synth.device as sd
+    import weighted_model_update_amd as fa
+    log("sparse_stream: generating 20 top-10% client lists over 10^9 parameters")
+    n, idx, val, base = sd.sparse_1b(K=clients)
+    K, N = len(idx), base.numel()
+    nnz = [int(i.numel()) for i in idx]
+    lines = []
+    for i in idx:
+        lines.append(int(torch.unique_consecutive(i // 16).numel()) * 2 * 64 * 2   # acc, wsum
+                     + int(torch.unique_consecutive(i // 64).numel()) * 64 * 2)    # count
+    out = torch.empty(N, dtype=torch.float32, device="cuda")
+    times = []
+    with fa.StreamingAccumulator(N, mode="deltas", partial=True, chunk_bytes=1 << 20, n_slots=2) as acc:
+        for k in range(K):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            acc.accumulate(k, int(n[k]), val[k], indices=idx[k])
+            e.record()
+            times.append((s, e))
+        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fs.record()
+        acc.finalize(base, out)
+        fe.record()
+        acc.sync()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in times[1:]]     # the first client warms up
+    ms = sum(per) / len(per)
+    pair_bytes = 30 * sum(nnz[1:]) / len(per)
+    line_bytes = (12 * sum(nnz[1:]) + sum(lines[1:])) / len(per)
+    fin_ms = fs.elapsed_time(fe)
+    del idx, val, base, out
+    free_gpu()
+    return {"K": K, "N": N, "pairs_per_client": nnz[0], "ms_per_client": ms,
+            "pair_bytes_per_client": pair_bytes, "line_bytes_per_client": line_bytes,
+            "hbm_gbs_lines": line_bytes / (ms * 1e-3) / 1e9,
+            "hbm_frac_lines": line_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "finalize_ms": fin_ms, "finalize_bytes": 13 * N,
+            "note": "each client's scatter moves whole 64-byte lines of acc, wsum and count; the one-pass "
+                    "sparse merge (mode sparse) avoids this"}
+
+
+def bench_checksum(reps=10):
+    """Checksum of a 10^9-parameter fp32 buffer: one read, 4 B per element."""
+    import torch
+    import weighted_model_update_amd as fa
+    N = 10 ** 9
+    x = torch.empty(N, dtype=torch.float32, device="cuda")
+    x.normal_()
+    h = torch.zeros(1, dtype=torch.int64, device="cuda")
+    _, durs = timed(lambda i: fa.fedavg_checksum(x, hash_out=h), reps, 2)
+    ms = sum(durs) / len(durs)
+    del x, h
+    free_gpu()
+    return {"N": N, "dtype": "f32", "ms_per_call": ms, "algo_bytes": 4 * N,
+            "hbm_gbs": 4 * N / (ms * 1e-3) / 1e9, "hbm_frac": 4 * N / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def bench_copy_calibration(gib=4):
     """A plain device copy of known size, so hardware byte counters can be
     scaled: the library's element copy (the no-contributor path of
@@ -418,7 +484,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    help="comma list of: dense,dense_small,adapter,streaming,sparse,topk,hierarchical,cpu,copycal "
+                    help="comma list of: dense,dense_small,adapter,streaming,sparse,topk,hierarchical,"
+                         "sparse_stream,checksum,cpu,copycal "
                          "(default all but copycal)")
     ap.add_argument("--stream-clients", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -436,7 +503,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     only = set(args.only.split(",")) if args.only != "all" else {"dense", "dense_small", "adapter",
                                                                  "streaming", "sparse", "topk",
-                                                                 "hierarchical", "cpu"}
+                                                                 "hierarchical", "sparse_stream",
+                                                                 "checksum", "cpu"}
     if args.no_cpu_baseline:
         only.discard("cpu")
 
@@ -463,6 +531,12 @@ def main():
     if "hierarchical" in only:
         modes["hierarchical"] = bench_hierarchical()
         log(f"hierarchical: {modes['hierarchical']['ms_per_merge']:.3f} ms per silo merge")
+    if "sparse_stream" in only:
+        modes["sparse_stream"] = bench_sparse_stream()
+        log(f"sparse_stream: {modes['sparse_stream']['ms_per_client']:.3f} ms per client")
+    if "checksum" in only:
+        modes["checksum"] = bench_checksum()
+        log(f"checksum: {modes['checksum']['ms_per_call']:.3f} ms/call")
     if "copycal" in only:
         modes["copy_calibration"] = bench_copy_calibration()
     cpu = cpu_baseline() if "cpu" in only else None
