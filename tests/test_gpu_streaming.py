@@ -189,6 +189,41 @@ def test_stream_bad_indices_are_reported_by_sync():
         assert e.value.code == -7
 
 
+@pytest.mark.parametrize("case", ["negative_run", "huge", "wraps_with_offset"])
+def test_stream_bad_indices_never_touch_memory_outside_the_accumulator(case):
+    """Indices below 0 -- also a run of them that increases, so each one
+    passes the order test -- or at or past N - offset (including values
+    where offset + index would wrap past 2^63) are reported and skipped; the
+    accumulator's neighbours in the same allocation stay untouched and the
+    good entries land."""
+    N, G = 1000, 4096
+    whole = torch.zeros(G + 2 * N + G, dtype=torch.float32, device="cuda")
+    acc_t = whole[G:G + N]
+    wsum_t = torch.zeros(N, dtype=torch.int32, device="cuda")
+    acc_b, wsum_b, cnt_b, stag_b = fa.fedavg_workspace_size(N, 1, 4096, 2)
+    staging = torch.empty(stag_b, dtype=torch.uint8, device="cuda")
+    if case == "negative_run":
+        offset, idx = 0, [-9, -5, -3, 2, 7]
+    elif case == "huge":
+        offset, idx = 0, [3, 4, 1 << 40, (1 << 62) + 5]
+    else:
+        offset, idx = 10, [1, 2, (1 << 63) - 8, (1 << 63) - 2]
+    vals = torch.ones(len(idx), dtype=torch.float32, device="cuda")
+    h = fa.fedavg_begin(N, "weights", True, acc_t, wsum_t, None, staging, 4096, 2)
+    try:
+        fa.fedavg_accumulate(h, 0, 3, vals, offset, None, torch.tensor(idx, dtype=torch.int64, device="cuda"))
+        with pytest.raises(fa.FedAvgError) as e:
+            fa.fedavg_sync(h)
+        assert e.value.code == -7
+    finally:
+        fa.fedavg_destroy(h)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(whole[:G])) == 0 and int(torch.count_nonzero(whole[G + N:])) == 0
+    good = [offset + i for i in idx if 0 <= i < N - offset]
+    got = torch.nonzero(acc_t).flatten().cpu().tolist()
+    assert got == good and all(float(acc_t[g]) == 3.0 for g in good)
+
+
 def test_stream_state_errors():
     N = 100
     x = dev_of(np.ones(N, np.float32), "f32")

@@ -672,14 +672,19 @@ __global__ __launch_bounds__(256) void stream_acc_scalar_kernel(const StreamArgs
 template <int DT>
 __global__ __launch_bounds__(256) void stream_acc_index_kernel(const StreamArgs a)
 {
+    // an index is good when it lies in [0, N - offset) and above its
+    // predecessor; the bounds are tested on the index itself, so neither a
+    // negative one (also in a run that increases) nor offset + index
+    // wrapping past 2^63 can address memory outside the accumulator
+    const int64_t span = a.N - a.offset;
     for (int64_t j = global_tid(); j < a.len; j += grid_threads()) {
         const int64_t ix = a.idx[j];
         const int64_t prev = j > 0 ? a.idx[j - 1] : -1;
-        const int64_t g = a.offset + ix;
-        if (ix <= prev || g >= a.N) {
+        if (ix < 0 || ix >= span || ix <= prev) {
             *a.err = FA_ERR_INDEX;
             continue;
         }
+        const int64_t g = a.offset + ix;
         a.acc[g] = __builtin_fmaf(a.w, io<DT>::load1(a.chunk, j), a.acc[g]);
         a.wsum[g] += a.wi;
         if (a.count)
