@@ -380,15 +380,21 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
                     for (int j = 0; j < VEC; ++j)
                         acc[j] = 0.0f;
                     for (int k0 = 0; k0 < a.K; k0 += 8) {
+                        // as in masked_table_kernel: absent clients are not
+                        // read, their FMA runs as 0 * 0 so the loads issue together
                         typename io<XDT>::raw xr[8];
+                        float wk[8];
 #pragma unroll
-                        for (int k = 0; k < 8; ++k)
-                            if (k0 + k < a.K && ((mask >> (k0 + k)) & 1))
+                        for (int k = 0; k < 8; ++k) {
+                            const bool on = k0 + k < a.K && ((mask >> (k0 + k)) & 1);
+                            xr[k] = io<XDT>::zero_raw();
+                            wk[k] = on ? a.w[k0 + k] : 0.0f;
+                            if (on)
                                 xr[k] = io<XDT>::load_raw(a.x[k0 + k], e);
+                        }
 #pragma unroll
                         for (int k = 0; k < 8; ++k)
-                            if (k0 + k < a.K && ((mask >> (k0 + k)) & 1))
-                                io<XDT>::fma8(xr[k], a.w[k0 + k], acc);
+                            io<XDT>::fma8(xr[k], wk[k], acc);
                     }
                     const float Wf = a.zero_fill ? a.S_all : (float)W;
                     if constexpr (MODE == MODE_DELTAS) {
