@@ -55,7 +55,8 @@
  *     library; fedavg_destroy releases it.
  *   - Limits: K <= FA_MAX_CLIENTS resident clients per call;
  *     0 <= n_k <= FA_MAX_WEIGHT (so fp32(n_k) is exact); sums of weights
- *     below 2^32.
+ *     below 2^32; at most FA_MAX_N parameters per buffer and chunk_bytes at
+ *     most FA_MAX_N (FA_ERR_RANGE beyond: no byte count can overflow).
  *   - Aliasing: `out` may be the same buffer as `base` or as one client input
  *     (every element is read before it is written); partial overlap is not
  *     allowed.
@@ -76,6 +77,7 @@ extern "C" {
 #define FA_MAX_CLIENTS 64
 #define FA_MAX_WEIGHT (1 << 24)
 #define FA_MAX_STREAM_CLIENTS 255
+#define FA_MAX_N (1ll << 40)
 
 typedef enum {
     FA_OK = 0,

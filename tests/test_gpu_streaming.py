@@ -224,6 +224,35 @@ def test_stream_bad_indices_never_touch_memory_outside_the_accumulator(case):
     assert got == good and all(float(acc_t[g]) == 3.0 for g in good)
 
 
+@pytest.mark.parametrize("partial", [False, True])
+def test_stream_ranges_that_wrap_past_2_63_are_range_errors(partial):
+    """A chunk or merged partial whose offset + length would wrap past 2^63
+    is refused before any launch (FA_ERR_RANGE); the accumulator and its
+    neighbours in the same allocation stay untouched."""
+    N, G = 1000, 4096
+    whole = torch.zeros(G + N + G, dtype=torch.float32, device="cuda")
+    acc_t = whole[G:G + N]
+    wsum_t = torch.zeros(N, dtype=torch.int32, device="cuda") if partial else None
+    _, _, _, stag_b = fa.fedavg_workspace_size(N, int(partial), 4096, 2)
+    staging = torch.empty(stag_b, dtype=torch.uint8, device="cuda")
+    vals = torch.ones(16, dtype=torch.float32, device="cuda")
+    h = fa.fedavg_begin(N, "weights", partial, acc_t, wsum_t, None, staging, 4096, 2)
+    try:
+        for off in ((1 << 63) - 8, (1 << 63) - 1, N - 15, N + 1):
+            with pytest.raises(fa.FedAvgError) as e:
+                fa.fedavg_accumulate(h, 0, 3, vals, off)
+            assert e.value.code == -3
+            with pytest.raises(fa.FedAvgError) as e:
+                fa.fedavg_accumulate_partial(h, 1, 5, 2, vals, wsum_src=vals.view(torch.int32) if partial else None,
+                                             offset=off)
+            assert e.value.code == -3
+        fa.fedavg_sync(h)
+    finally:
+        fa.fedavg_destroy(h)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(whole)) == 0
+
+
 def test_stream_state_errors():
     N = 100
     x = dev_of(np.ones(N, np.float32), "f32")

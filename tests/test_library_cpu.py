@@ -98,6 +98,27 @@ def test_workspace_sizes_do_not_depend_on_the_number_of_clients():
     assert fa.sparse_workspace_size(20, 4096) < 2048
 
 
+def test_sizes_beyond_the_parameter_cap_are_range_errors():
+    """At most 2^40 parameters (and chunk_bytes at most 2^40), so that no
+    byte count the library forms can overflow 64 bits."""
+    lib = fa.load()
+    z = ctypes.c_size_t(0)
+    M = fa.FA_MAX_N
+    assert lib.fedavg_workspace_size(M, 1, 1 << 20, 2, None, None, None, ctypes.byref(z)) == 0
+    assert lib.fedavg_workspace_size(M + 1, 1, 1 << 20, 2, None, None, None, ctypes.byref(z)) == -3
+    assert lib.fedavg_workspace_size(10, 1, M + 1, 2, None, None, None, ctypes.byref(z)) == -3
+    assert lib.fedavg_workspace_size(10, 1, (1 << 63) - 1, 64, None, None, None, ctypes.byref(z)) == -3
+    assert lib.fedavg_workspace_size(10, 1, 4096, 65, None, None, None, ctypes.byref(z)) == -3
+    assert lib.sparse_workspace_size(4, M + 1, ctypes.byref(z)) == -3
+    assert lib.sparse_workspace_size(4, M, ctypes.byref(z)) == 0
+    x = (ctypes.c_void_p * 1)(1 << 20)
+    n = (ctypes.c_int64 * 1)(5)
+    P = ctypes.c_void_p
+    assert lib.fedavg_aggregate(1, x, 0, n, M + 1, 0, None, 0, P(1 << 21), 0, 0, None, None, None) == -3
+    assert lib.fedavg_checksum(P(1 << 20), M + 1, 0, P(1 << 21), None) == -3
+    assert b"2^40" in lib.fedavg_last_error()
+
+
 def test_streaming_null_handle_and_state():
     lib = _lib()
     assert lib.fedavg_accumulate(None, 0, 1, None, 0, 0, 0, None, None) == -1

@@ -320,6 +320,8 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
         return fail(FA_ERR_ARG, "x and n must not be NULL");
     if (N < 0)
         return fail(FA_ERR_ARG, "N=%lld is negative", (long long)N);
+    if (N > FA_MAX_N)
+        return fail(FA_ERR_RANGE, "N=%lld exceeds 2^40", (long long)N);
     if (!dtype_ok(x_dtype) || !dtype_ok(out_dtype) || !dtype_ok(base_dtype))
         return fail(FA_ERR_DTYPE, "dtypes must be FA_F32 or FA_BF16");
     if (mode != FA_WEIGHTS && mode != FA_DELTAS && mode != FA_DELTAS_ZERO_FILL)
@@ -412,6 +414,8 @@ int fedavg_workspace_size(int64_t N, int partial, int64_t chunk_bytes, int n_slo
 {
     if (N < 0 || chunk_bytes <= 0 || n_slots < 1)
         return fail(FA_ERR_ARG, "need N >= 0, chunk_bytes > 0, n_slots >= 1");
+    if (N > FA_MAX_N || chunk_bytes > FA_MAX_N || n_slots > 64)
+        return fail(FA_ERR_RANGE, "need N <= 2^40, chunk_bytes <= 2^40, n_slots <= 64");
     if (partial != 0 && partial != 1)
         return fail(FA_ERR_ARG, "partial must be 0 or 1");
     if (acc_bytes)
@@ -436,6 +440,8 @@ static int open_handle(fa_handle *h, int64_t N, int mode, int partial, float *ac
     *h = nullptr;
     if (N < 0 || chunk_bytes <= 0 || n_slots < 1 || n_slots > 64)
         return fail(FA_ERR_ARG, "need N >= 0, chunk_bytes > 0, 1 <= n_slots <= 64");
+    if (N > FA_MAX_N || chunk_bytes > FA_MAX_N)
+        return fail(FA_ERR_RANGE, "need N <= 2^40 and chunk_bytes <= 2^40");
     if (mode != FA_WEIGHTS && mode != FA_DELTAS && mode != FA_DELTAS_ZERO_FILL)
         return fail(FA_ERR_ARG, "unknown mode %d", mode);
     if (partial != 0 && partial != 1)
@@ -645,9 +651,10 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
         return fail(FA_ERR_ARG, "pass a mask or indices, not both");
     if ((mask || indices) && !st.partial)
         return fail(FA_ERR_ARG, "masks and indices need a partial-mode handle");
-    if (!indices && offset + len > st.N)
-        return fail(FA_ERR_RANGE, "chunk [%lld, %lld) exceeds N=%lld", (long long)offset,
-                    (long long)(offset + len), (long long)st.N);
+    // written so that no sum can overflow: offset + len may exceed 2^63
+    if (!indices && (offset > st.N || len > st.N - offset))
+        return fail(FA_ERR_RANGE, "chunk at %lld of %lld elements exceeds N=%lld", (long long)offset,
+                    (long long)len, (long long)st.N);
     if (indices && offset > st.N)
         return fail(FA_ERR_RANGE, "offset beyond N");
     if (len > 0 && !chunk)
@@ -755,9 +762,9 @@ int fedavg_accumulate_partial(fa_handle h, int client_id, int64_t W, int n_clien
         return fail(FA_ERR_RANGE, "W=%lld outside [0, 2^32)", (long long)W);
     if (n_clients < 1 || n_clients > FA_MAX_STREAM_CLIENTS)
         return fail(FA_ERR_RANGE, "n_clients=%d outside [1, %d]", n_clients, FA_MAX_STREAM_CLIENTS);
-    if (len < 0 || offset < 0 || offset + len > st.N)
-        return fail(FA_ERR_RANGE, "range [%lld, %lld) outside [0, N=%lld)", (long long)offset,
-                    (long long)(offset + len), (long long)st.N);
+    if (len < 0 || offset < 0 || offset > st.N || len > st.N - offset)
+        return fail(FA_ERR_RANGE, "range at %lld of %lld elements outside [0, N=%lld)",
+                    (long long)offset, (long long)len, (long long)st.N);
     if (len > 0 && !acc_src)
         return fail(FA_ERR_ARG, "acc_src is NULL");
     if (st.partial && len > 0 && !wsum_src)
@@ -969,6 +976,8 @@ int sparse_workspace_size(int K, int64_t N, size_t *bytes)
         return fail(FA_ERR_RANGE, "K=%d outside [1, %d]", K, FA_MAX_CLIENTS);
     if (N < 0 || !bytes)
         return fail(FA_ERR_ARG, "need N >= 0 and a result pointer");
+    if (N > FA_MAX_N)
+        return fail(FA_ERR_RANGE, "N=%lld exceeds 2^40", (long long)N);
     // one list offset per client and range boundary; there are never more
     // ranges than tiles of the smallest tile size
     const int64_t max_ranges =
@@ -989,6 +998,8 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
         return fail(FA_ERR_ARG, "idx, val, nnz and n must not be NULL");
     if (N < 0)
         return fail(FA_ERR_ARG, "N is negative");
+    if (N > FA_MAX_N)
+        return fail(FA_ERR_RANGE, "N=%lld exceeds 2^40", (long long)N);
     if (mode != FA_WEIGHTS && mode != FA_DELTAS && mode != FA_DELTAS_ZERO_FILL)
         return fail(FA_ERR_ARG, "unknown mode %d", (int)mode);
     if (counts_dtype != FA_COUNT_U8 && counts_dtype != FA_COUNT_U32)
@@ -1062,8 +1073,6 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
     e = fa::launch_sparse(a, s);
     return e == hipSuccess ? ok() : hip_fail(e, "sparse launch");
 }
-
-// ============================================================ checksum
 
 // ============================================================ sample allocation
 
@@ -1214,10 +1223,14 @@ int topk_select(const void *x, fa_dtype dtype, int64_t N, int64_t k, int64_t *id
     return e == hipSuccess ? ok() : hip_fail(e, "top-k launch");
 }
 
+// ============================================================ checksum
+
 int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *hash_dev, void *stream)
 {
     if (!hash_dev || (count > 0 && !buf) || count < 0)
         return fail(FA_ERR_ARG, "need a hash pointer, a buffer and count >= 0");
+    if (count > FA_MAX_N)
+        return fail(FA_ERR_RANGE, "count=%lld exceeds 2^40", (long long)count);
     if (!dtype_ok(dtype))
         return fail(FA_ERR_DTYPE, "dtype must be FA_F32 or FA_BF16");
     hipError_t e = fa::launch_checksum(buf, count, dtype, hash_dev, static_cast<hipStream_t>(stream));

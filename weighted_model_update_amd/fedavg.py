@@ -21,6 +21,7 @@ FA_OPT_BLOCKS_PER_CU, FA_OPT_MASK_VECTORS_PER_BLOCK, FA_OPT_SPARSE_BLOCKS, FA_OP
 FA_OPT_SPARSE_TILE = 5
 FA_OPT_TOPK_SAMPLED = 6
 FA_MAX_CLIENTS = 64
+FA_MAX_N = 1 << 40
 
 STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_ARG", -2: "FA_ERR_DTYPE", -3: "FA_ERR_RANGE",
@@ -395,7 +396,7 @@ class StreamingAccumulator:
                 bounce = torch.empty(min(self._SPILL_PIECE, total), dtype=torch.uint8, pin_memory=True)
                 for off in range(0, total, bounce.numel()):
                     n = min(bounce.numel(), total - off)
-                    bounce[:n].copy_(torch.from_numpy(np.asarray(mm[off:off + n])))
+                    bounce[:n].numpy()[:] = mm[off:off + n]
                     flat[off:off + n].copy_(bounce[:n])
                 torch.cuda.synchronize()
                 del mm
