@@ -61,6 +61,10 @@ def _load():
     lib.orc_round_to_bf16.restype = None
     lib.orc_checksum.argtypes = [P, i64, ctypes.c_int, i64]
     lib.orc_checksum.restype = ctypes.c_uint64
+    lib.orc_sum.argtypes = [P, i64, ctypes.c_int]
+    lib.orc_sum.restype = ctypes.c_double
+    lib.orc_sum_set_carry_period.argtypes = [i64]
+    lib.orc_sum_set_carry_period.restype = None
     lib.orc_topk.argtypes = [P, ctypes.c_int, i64, i64, P, P]
     lib.orc_topk.restype = ctypes.c_int
     _lib = lib
@@ -183,6 +187,20 @@ def checksum(a, dtype, first=0):
     lib = _load()
     a = _raw(a, dtype)
     return int(lib.orc_checksum(_ptr(a), a.size, dtype, first))
+
+
+def value_sum(a, dtype):
+    """The exact sum of a raw fp32 or bf16-bits array's values, rounded once
+    to the nearest fp64 (ties to even); NaN or +-infinity as IEEE addition
+    gives them; a zero sum is +0."""
+    lib = _load()
+    a = _raw(a, dtype)
+    return float(lib.orc_sum(_ptr(a), a.size, dtype))
+
+
+def set_sum_carry_period(p):
+    """Test hook: run the sum's carry pass every p additions (0: the default)."""
+    _load().orc_sum_set_carry_period(int(p))
 
 
 def topk(x, dtype, k):

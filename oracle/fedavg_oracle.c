@@ -349,6 +349,102 @@ uint64_t orc_checksum(const void *buf, int64_t count, int dtype, int64_t first)
 }
 
 /*
+ * Sum of a buffer's element values, a diagnostic that goes with the
+ * checksum (no page defines one).  Its definition: the exact real sum of the
+ * values, rounded once to the nearest fp64 value (ties to even), so that no
+ * order of addition enters.  Every finite fp32 value is an integer multiple
+ * of 2^-149 (and a bf16 value is an fp32 value), so the exact sum is an
+ * integer number of 2^-149 units; it is held in base-2^32 digits kept in
+ * int64 (room for 2^30 additions between carry passes).  Special values
+ * follow IEEE addition, whose result does not depend on the order either:
+ * a NaN, or infinities of both signs, give NaN; otherwise an infinity gives
+ * itself.  A zero sum is +0.
+ */
+#define SUM_DIGITS 12
+static int64_t sum_carry_period = (int64_t)1 << 30;
+
+/* test hook: carry passes more often, to exercise them on small inputs */
+void orc_sum_set_carry_period(int64_t p) { sum_carry_period = p > 0 ? p : (int64_t)1 << 30; }
+
+static void sum_carry(int64_t *d)
+{
+    const int64_t R = (int64_t)1 << 32;
+    for (int L = 0; L + 1 < SUM_DIGITS; ++L) {
+        int64_t c = d[L] >= 0 ? d[L] / R : -((-d[L] + R - 1) / R); /* floor(d / R) */
+        d[L] -= c * R;
+        d[L + 1] += c;
+    }
+}
+
+static int sum_bit(const int64_t *d, int i) { return (int)((d[i / 32] >> (i % 32)) & 1); }
+
+double orc_sum(const void *buf, int64_t count, int dtype)
+{
+    int64_t d[SUM_DIGITS] = {0};
+    int nan = 0, pinf = 0, ninf = 0;
+    for (int64_t j = 0; j < count; ++j) {
+        uint32_t u = (dtype == ORC_F32) ? ((const uint32_t *)buf)[j]
+                                        : (uint32_t)((const uint16_t *)buf)[j] << 16;
+        uint32_t e = (u >> 23) & 0xFFu, f = u & 0x7FFFFFu;
+        int neg = (int)(u >> 31);
+        if (e == 0xFFu) {
+            if (f)
+                nan = 1;
+            else if (neg)
+                ninf = 1;
+            else
+                pinf = 1;
+            continue;
+        }
+        /* value = m * 2^(p - 149) */
+        uint64_t m = e ? (f | 0x800000u) : f;
+        int p = e ? (int)e - 1 : 0;
+        uint64_t v = m << (p % 32);
+        int64_t lo = (int64_t)(v & 0xFFFFFFFFu), hi = (int64_t)(v >> 32);
+        d[p / 32] += neg ? -lo : lo;
+        d[p / 32 + 1] += neg ? -hi : hi;
+        if ((j + 1) % sum_carry_period == 0)
+            sum_carry(d);
+    }
+    if (nan || (pinf && ninf))
+        return NAN;
+    if (pinf)
+        return INFINITY;
+    if (ninf)
+        return -INFINITY;
+    sum_carry(d);
+    int neg = d[SUM_DIGITS - 1] < 0;
+    if (neg) {
+        for (int L = 0; L < SUM_DIGITS; ++L)
+            d[L] = -d[L];
+        sum_carry(d);
+    }
+    /* magnitude: digits in [0, 2^32); B = its highest set bit */
+    int B = 32 * SUM_DIGITS - 1;
+    while (B >= 0 && !sum_bit(d, B))
+        --B;
+    if (B < 0)
+        return 0.0;
+    uint64_t mant = 0;
+    for (int i = 0; i <= 52; ++i)
+        if (B - i >= 0 && sum_bit(d, B - i))
+            mant |= (uint64_t)1 << (52 - i);
+    int round = B - 53 >= 0 ? sum_bit(d, B - 53) : 0;
+    int sticky = 0;
+    for (int i = 0; i < B - 53; ++i)
+        sticky |= sum_bit(d, i);
+    if (round && (sticky || (mant & 1u))) {
+        mant += 1;
+        if (mant == (uint64_t)1 << 53) {
+            mant >>= 1;
+            B += 1;
+        }
+    }
+    double r = ldexp((double)mant, B - 52 - 149);
+    return neg ? -r : r;
+}
+
+/*
  * Client-side top-k selection for partial sharing.  A client shares only a
  * fraction of its update, which it chooses itself (Clara page, introduction
  * and client-side workflow section); the fraction kept is the k = floor(p*N)

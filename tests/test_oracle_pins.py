@@ -542,3 +542,64 @@ def test_controller_invariants():
     a, _ = controller.controller_step([3, 5, 7], [1, 1, 1], [10, 10, 10], 999, 1.0, 0.0, 1.0, 0.0)
     b, _ = controller.controller_step([30, 50, 70], [1, 1, 1], [10, 10, 10], 999, 1.0, 0.0, 1.0, 0.0)
     assert a == b
+
+
+def _fsum(a):
+    # Python's math.fsum returns the correctly rounded sum of its floats
+    return math.fsum(np.asarray(a, np.float64).tolist())
+
+
+@pytest.mark.parametrize("period", [0, 1, 7])
+def test_value_sum_is_the_correctly_rounded_exact_sum(period):
+    """Pinned to math.fsum (an independent correctly rounded summation) on
+    values spread over fp32's whole range, subnormals included, with heavy
+    cancellation; also with the carry pass run after every few additions."""
+    oracle.set_sum_carry_period(period)
+    try:
+        r = np.random.default_rng(31 + period)
+        cases = [
+            r.standard_normal(10_000).astype(np.float32),
+            # log-uniform magnitudes over 2^-149 .. 2^127, random signs
+            (np.exp2(r.uniform(-149, 127, 5000)) * r.choice([-1.0, 1.0], 5000)).astype(np.float32),
+            # many values cancelling around a few large ones
+            np.concatenate([np.float32([3e38, -3e38, 1e30, -1e30]),
+                            r.standard_normal(3000).astype(np.float32) * np.float32(1e-30)]),
+            np.full(100_000, np.float32(3.4e38)),
+            r.integers(-(1 << 24), 1 << 24, 20_000).astype(np.float32) * np.float32(2.0 ** -149),
+        ]
+        for a in cases:
+            a = r.permutation(a)
+            assert oracle.value_sum(a, oracle.F32) == _fsum(a)
+            bits = synth.bf16_bits_from_f32(a)
+            widened = (bits.astype(np.uint32) << 16).view(np.float32)
+            assert oracle.value_sum(bits, oracle.BF16) == _fsum(widened)
+    finally:
+        oracle.set_sum_carry_period(0)
+
+
+def test_value_sum_rounds_once_with_ties_to_even():
+    """Exact sums halfway between fp64 neighbours round to the even one;
+    anything beyond halfway rounds away; a naive fp64 loop loses the small
+    terms these cases hinge on."""
+    t = np.float32(2.0 ** 53)
+    assert oracle.value_sum(np.float32([t, 1.0]), oracle.F32) == 2.0 ** 53
+    assert oracle.value_sum(np.float32([t, 3.0]), oracle.F32) == 2.0 ** 53 + 4
+    assert oracle.value_sum(np.float32([t, 1.0, 2.0 ** -20]), oracle.F32) == 2.0 ** 53 + 2
+    assert oracle.value_sum(np.float32([t, 1.0, -(2.0 ** -20)]), oracle.F32) == 2.0 ** 53
+    assert oracle.value_sum(np.float32([-t, -1.0, -(2.0 ** -20)]), oracle.F32) == -(2.0 ** 53 + 2)
+    assert oracle.value_sum(np.float32([1e30, 1.0, -1e30]), oracle.F32) == 1.0
+    assert oracle.value_sum(np.float32([2.0 ** -149] * 3), oracle.F32) == 3 * 2.0 ** -149
+
+
+def test_value_sum_special_values():
+    inf, nan = np.float32(np.inf), np.float32(np.nan)
+    assert math.isnan(oracle.value_sum(np.float32([1.0, nan, 2.0]), oracle.F32))
+    assert math.isnan(oracle.value_sum(np.float32([inf, 1.0, -inf]), oracle.F32))
+    assert oracle.value_sum(np.float32([inf, -3e38, -3e38]), oracle.F32) == math.inf
+    assert oracle.value_sum(np.float32([-inf, 3e38]), oracle.F32) == -math.inf
+    z = oracle.value_sum(np.float32([-0.0, -0.0]), oracle.F32)
+    assert z == 0.0 and math.copysign(1.0, z) == 1.0
+    assert oracle.value_sum(np.float32([5.0, -5.0]), oracle.F32) == 0.0
+    assert oracle.value_sum(np.zeros(0, np.float32), oracle.F32) == 0.0
+    assert oracle.value_sum(np.uint16([0x7F80, 0x3F80]), oracle.BF16) == math.inf
+    assert math.isnan(oracle.value_sum(np.uint16([0xFFC1, 0x3F80]), oracle.BF16))
