@@ -409,10 +409,20 @@ def bench_checksum(reps=10):
     h = torch.zeros(1, dtype=torch.int64, device="cuda")
     _, durs = timed(lambda i: fa.fedavg_checksum(x, hash_out=h), reps, 2)
     ms = sum(durs) / len(durs)
-    del x, h
+    # the same read giving the hash and the fixed-order fp64 value sum, and
+    # the sum alone (each call: the tile pass plus a one-block finish)
+    ws = torch.empty(fa.fedavg_sum_workspace_size(N), dtype=torch.uint8, device="cuda")
+    sm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    _, d2 = timed(lambda i: fa.fedavg_checksum_sum(x, workspace=ws, hash_out=h, sum_out=sm), reps, 2)
+    _, d3 = timed(lambda i: fa.fedavg_checksum_sum(x, workspace=ws, sum_out=sm), reps, 2)
+    ms2, ms3 = sum(d2) / len(d2), sum(d3) / len(d3)
+    del x, h, ws, sm
     free_gpu()
+    gbs = lambda m: 4 * N / (m * 1e-3) / 1e9
     return {"N": N, "dtype": "f32", "ms_per_call": ms, "algo_bytes": 4 * N,
-            "hbm_gbs": 4 * N / (ms * 1e-3) / 1e9, "hbm_frac": 4 * N / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "hbm_gbs": gbs(ms), "hbm_frac": gbs(ms) / HBM_PEAK_GBS,
+            "hash_and_sum_ms_per_call": ms2, "hash_and_sum_hbm_frac": gbs(ms2) / HBM_PEAK_GBS,
+            "sum_ms_per_call": ms3, "sum_hbm_frac": gbs(ms3) / HBM_PEAK_GBS}
 
 
 def bench_copy_calibration(gib=4):
@@ -536,7 +546,9 @@ def main():
         log(f"sparse_stream: {modes['sparse_stream']['ms_per_client']:.3f} ms per client")
     if "checksum" in only:
         modes["checksum"] = bench_checksum()
-        log(f"checksum: {modes['checksum']['ms_per_call']:.3f} ms/call")
+        log(f"checksum: {modes['checksum']['ms_per_call']:.3f} ms/call, with the value sum "
+            f"{modes['checksum']['hash_and_sum_ms_per_call']:.3f}, sum alone "
+            f"{modes['checksum']['sum_ms_per_call']:.3f}")
     if "copycal" in only:
         modes["copy_calibration"] = bench_copy_calibration()
     cpu = cpu_baseline() if "cpu" in only else None

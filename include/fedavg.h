@@ -419,6 +419,31 @@ int topk_select(const void *x, fa_dtype dtype, int64_t N, int64_t k, int64_t *id
 int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *hash_dev,
                     void *stream);
 
+/*
+ * fedavg_sum_workspace_size -- bytes of workspace fedavg_checksum_sum needs
+ * for `count` elements: 8 per tile of 8192 elements (count/1024 bytes),
+ * 0 for count == 0.  count > FA_MAX_N: FA_ERR_RANGE.
+ *
+ * fedavg_checksum_sum -- in one read of the buffer, the checksum above (when
+ * hash_dev is not NULL) and a deterministic fp64 sum of the element values
+ * into *sum_dev (device double, overwritten).  The additions run in an order
+ * fixed by `count` alone: tiles of 8192 elements; in a tile, each of 256
+ * threads adds its 32 elements (those of 16-byte vectors j, j + 256, ...)
+ * in order from +0, then a butterfly over each wavefront and
+ * (w0 + w1) + (w2 + w3) over the four; the tile sums are added by 1024
+ * threads (thread j: sums j, j + 1024, ... in order), a butterfly, and a
+ * pairwise tree over the 16 wavefronts.  So the result is the same bits on
+ * every call and every launch shape, and within h * 2^-53 / (1 - h * 2^-53)
+ * of sum |x_i| of the exact sum, h = 48 + ceil(T / 1024) for T tiles.  NaN,
+ * or infinities of both signs, give NaN; a zero sum is +0.  workspace:
+ * device memory of fedavg_sum_workspace_size bytes, 8-byte aligned, holding
+ * the tile sums.  The buffer, the workspace and the results must not overlap
+ * (FA_ERR_ARG); a short workspace is FA_ERR_WORKSPACE.
+ */
+int fedavg_sum_workspace_size(int64_t count, size_t *bytes);
+int fedavg_checksum_sum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *hash_dev,
+                        double *sum_dev, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------
  * Launch-shape options (process-wide, for tuning and measurement).  They
  * change how work is spread over the GPU, never the results.

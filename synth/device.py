@@ -145,9 +145,12 @@ def laplace(N, scale, g, device="cuda"):
     float32, by inverting the CDF of uniform draws in (-1/2, 1/2)."""
     u = torch.empty(N, dtype=torch.float32, device=device)
     u.uniform_(-0.5, 0.5, generator=g)
-    # x = -b * sign(u) * ln(1 - 2|u|); |u| = 0.5 exactly never occurs because
-    # uniform_ draws from [-0.5, 0.5)
+    # x = -b * sign(u) * ln(1 - 2|u|).  uniform_ draws from [-0.5, 0.5), so
+    # u = -0.5 does occur (about once in 2^24 draws) and would give an
+    # infinity: |u| is held to the largest float below 0.5, the tail's next
+    # draw, 0.5 - 2^-25
     a = u.abs()
+    a.clamp_(max=0.5 - 2.0 ** -25)
     a.mul_(-2.0).add_(1.0).log_().mul_(-scale)
     return a.copysign_(u)
 

@@ -231,3 +231,30 @@ def test_topk_1b_client_update_properties():
     oi, ov = oracle.topk(w, oracle.F32, kw)
     assert np.array_equal(wi.cpu().numpy(), oi) and np.array_equal(wv.cpu().numpy().view(np.uint32),
                                                                    ov.view(np.uint32))
+
+
+def test_value_sum_1b_fp32_against_the_exact_sum():
+    """The fused checksum and fp64 value sum of a 10^9-parameter fp32 client
+    update: the hash equals the oracle's bit for bit, the sum lies within the
+    rounding bound of the exact sum (h = 48 + ceil(T / 1024) additions on the
+    longest chain, T tiles of 8192), and other launch shapes give the same
+    bits."""
+    N = 10 ** 9
+    x = sd.client_delta_1b(0, N)
+    h, s = fa.fedavg_checksum_sum(x)
+    fa.fedavg_set_option(fa.FA_OPT_BLOCKS_PER_CU, 2)
+    try:
+        _, s2 = fa.fedavg_checksum_sum(x, with_hash=False)
+    finally:
+        fa.fedavg_set_option(fa.FA_OPT_BLOCKS_PER_CU, 0)
+    assert s2.hex() == s.hex()
+    a = x.cpu().numpy()
+    del x
+    assert np.isfinite(a).all()          # the Laplace generator yields no infinities
+    assert h == oracle.checksum(a, oracle.F32)
+    want = oracle.value_sum(a, oracle.F32)
+    absum = oracle.value_sum((a.view(np.uint32) & np.uint32(0x7FFFFFFF)).view(np.float32), oracle.F32)
+    T = -(-N // 8192)
+    hh = 48 + -(-T // 1024)
+    u = 2.0 ** -53
+    assert abs(s - want) <= hh * u / (1 - hh * u) * absum * (1 + 4 * u), (s, want, absum)

@@ -71,6 +71,14 @@ def test_host_side_argument_errors_need_no_device():
     assert lib.topk_workspace_size(7, 100, 10, ctypes.byref(b)) == -2    # unknown dtype
     assert lib.topk_workspace_size(0, 100, 10, None) == -1
     assert lib.fedavg_checksum(None, 10, 0, None, None) == -1
+    d = ctypes.c_void_p
+    assert lib.fedavg_checksum_sum(d(1 << 20), 10, 0, None, None, None, 0, None) == -1   # no sum
+    assert lib.fedavg_checksum_sum(d(1 << 20), 10, 5, None, d(1 << 22), d(1 << 23), 8, None) == -2
+    assert lib.fedavg_checksum_sum(d(1 << 20), 10, 0, None, d(1 << 22), None, 0, None) == -8
+    assert lib.fedavg_checksum_sum(d(1 << 20), 10, 0, None, d(1 << 22), d(1 << 23), 7, None) == -8
+    assert lib.fedavg_checksum_sum(d(1 << 20), 10, 0, None, d(1 << 22), d((1 << 23) + 4), 8, None) == -1
+    assert lib.fedavg_checksum_sum(d(1 << 20), 10, 0, None, d((1 << 20) + 8), d(1 << 23), 8, None) == -1
+    assert lib.fedavg_checksum_sum(d(1 << 20), 10, 0, d(1 << 23), d(1 << 22), d(1 << 23), 8, None) == -1
 
 
 def test_topk_workspace_holds_a_staging_copy_only_while_it_pays():
@@ -96,6 +104,9 @@ def test_workspace_sizes_do_not_depend_on_the_number_of_clients():
         fa.fedavg_workspace_size(10, 0, 0, 2)
     assert fa.sparse_workspace_size(20, 10 ** 9) < 16 << 20
     assert fa.sparse_workspace_size(20, 4096) < 2048
+    # the value sum keeps one fp64 per tile of 8192 elements
+    assert [fa.fedavg_sum_workspace_size(n) for n in (0, 1, 8192, 8193, 10 ** 9)] == \
+        [0, 8, 8, 16, 8 * 122071]
 
 
 def test_sizes_beyond_the_parameter_cap_are_range_errors():
@@ -116,6 +127,7 @@ def test_sizes_beyond_the_parameter_cap_are_range_errors():
     P = ctypes.c_void_p
     assert lib.fedavg_aggregate(1, x, 0, n, M + 1, 0, None, 0, P(1 << 21), 0, 0, None, None, None) == -3
     assert lib.fedavg_checksum(P(1 << 20), M + 1, 0, P(1 << 21), None) == -3
+    assert lib.fedavg_sum_workspace_size(M + 1, ctypes.byref(z)) == -3
     assert b"2^40" in lib.fedavg_last_error()
 
 

@@ -1237,4 +1237,52 @@ int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *ha
     return e == hipSuccess ? ok() : hip_fail(e, "checksum launch");
 }
 
+
+int fedavg_sum_workspace_size(int64_t count, size_t *bytes)
+{
+    if (!bytes || count < 0)
+        return fail(FA_ERR_ARG, "need count >= 0 and a result pointer");
+    if (count > FA_MAX_N)
+        return fail(FA_ERR_RANGE, "count=%lld exceeds 2^40", (long long)count);
+    *bytes = (size_t)((count + fa::SUM_TILE - 1) / fa::SUM_TILE) * sizeof(double);
+    return ok();
+}
+
+int fedavg_checksum_sum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *hash_dev,
+                        double *sum_dev, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!sum_dev || (count > 0 && !buf) || count < 0)
+        return fail(FA_ERR_ARG, "need a sum pointer, a buffer and count >= 0");
+    if (count > FA_MAX_N)
+        return fail(FA_ERR_RANGE, "count=%lld exceeds 2^40", (long long)count);
+    if (!dtype_ok(dtype))
+        return fail(FA_ERR_DTYPE, "dtype must be FA_F32 or FA_BF16");
+    size_t need = 0;
+    fedavg_sum_workspace_size(count, &need);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+        return fail(FA_ERR_ARG, "workspace must be 8-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(sum_dev) & 7u) != 0 ||
+        (hash_dev && (reinterpret_cast<uintptr_t>(hash_dev) & 7u) != 0))
+        return fail(FA_ERR_ARG, "sum_dev and hash_dev must be 8-byte aligned");
+    // the tile sums are written while the buffer is read, and the results
+    // after: none of them may share bytes with the buffer or the tile sums
+    auto apart = [](const void *a, size_t an, const void *b, size_t bn) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+        return !a || !b || an == 0 || bn == 0 || a0 + an <= b0 || b0 + bn <= a0;
+    };
+    const size_t bbytes = (size_t)count * dsize(dtype);
+    if (!apart(workspace, need, buf, bbytes) || !apart(sum_dev, 8, buf, bbytes) ||
+        !apart(hash_dev, 8, buf, bbytes) || !apart(sum_dev, 8, workspace, need) ||
+        !apart(hash_dev, 8, workspace, need) || !apart(hash_dev, 8, sum_dev, 8))
+        return fail(FA_ERR_ARG, "the buffer, the workspace and the results must not overlap");
+    // workgroups walk the tiles: a few per CU by default
+    const int64_t cap = grid_cap() > 0 ? grid_cap() : (int64_t)cu_count() * 32;
+    hipError_t e = fa::launch_checksum_sum(buf, count, dtype, hash_dev, sum_dev,
+                                           static_cast<double *>(workspace), cap,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "checksum and sum launch");
+}
+
 } // extern "C"

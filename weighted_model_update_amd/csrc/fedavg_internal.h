@@ -130,6 +130,11 @@ hipError_t launch_topk(const void *x, int dt, int64_t N, int64_t k, int64_t *idx
                        float *val_out, void *ws, int cus, hipStream_t s);
 hipError_t launch_checksum(const void *buf, int64_t count, int dt, uint64_t *hash,
                            hipStream_t s);
+// Elements per tile sum, and the threads that add the tile sums.
+constexpr int SUM_TILE = 8192;
+constexpr int SUM_FINISH_THREADS = 1024;
+hipError_t launch_checksum_sum(const void *buf, int64_t count, int dt, uint64_t *hash, double *sum,
+                               double *part, int64_t cap, hipStream_t s);
 hipError_t launch_fill_u32(void *p, int64_t words, uint32_t value, hipStream_t s);
 hipError_t launch_convert(const void *src, int sdt, void *dst, int ddt, int64_t N, hipStream_t s);
 

@@ -1143,7 +1143,8 @@ template <int DT> __device__ __forceinline__ uint64_t vec_hash(const u32x4 &r, i
 // Integer sum of per-element hashes: exact and independent of the order the
 // lanes add in.  16-byte vectors, four issued per step, then the elements
 // past the last whole vector; lanes reduce across the wavefront with
-// butterfly shuffles, then one 64-bit atomic add per wavefront.
+// butterfly shuffles, the four wavefronts through LDS, then one 64-bit
+// atomic add per workgroup.
 template <int DT>
 __global__ __launch_bounds__(256) void checksum_kernel(const void *buf, int64_t count, bool aligned,
                                                        unsigned long long *out)
@@ -1170,11 +1171,142 @@ __global__ __launch_bounds__(256) void checksum_kernel(const void *buf, int64_t 
                                            : (uint32_t) static_cast<const uint16_t *>(buf)[i];
         h += elem_hash(i, bits);
     }
+    __shared__ unsigned long long wh[4];
     unsigned long long r = h;
     for (int off = 32; off > 0; off >>= 1)
         r += __shfl_xor(r, off);
     if ((threadIdx.x & 63) == 0)
-        atomicAdd(out, r);
+        wh[threadIdx.x >> 6] = r;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicAdd(out, wh[0] + wh[1] + wh[2] + wh[3]);
+}
+
+// fp64 sum of a value from each of the 64 lanes by a butterfly.  Lanes i and
+// i^off add the same two values (in either order, which IEEE addition does
+// not see), so every lane ends with the same sum and the pairing is fixed.
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+template <int DT> __device__ __forceinline__ double elem_value(uint32_t bits)
+{
+    return DT == DT_F32 ? (double)__uint_as_float(bits) : (double)__uint_as_float(bits << 16);
+}
+
+// Hash and fp64 value sum in one read.  The order of the additions is set by
+// the element count alone (not by the grid, the alignment or the device), so
+// the sum is the same bits on every call: tiles of SUM_TILE elements; in a
+// tile, thread j adds, from +0 and in element order, the elements of the
+// 16-byte vectors j, j + 256, ... of the tile (fp32: 8 vectors of 4, bf16: 4
+// of 8); the thread sums meet in a butterfly per wavefront and the four
+// wavefront sums as (w0 + w1) + (w2 + w3), giving part[t].  Tiles wholly
+// inside an aligned buffer are read as vectors, the rest element by element
+// in the same order.
+template <int DT, bool HASH>
+__global__ __launch_bounds__(256) void checksum_sum_kernel(const void *buf, int64_t count,
+                                                           bool aligned,
+                                                           unsigned long long *hash, double *part)
+{
+    constexpr int EPV = DT == DT_F32 ? 4 : 8;
+    constexpr int VPT = SUM_TILE / EPV; // vectors per tile
+    constexpr int RV = VPT / 256;       // vectors per thread and tile
+    const int64_t T = (count + SUM_TILE - 1) / SUM_TILE;
+    const int64_t full = aligned ? count / SUM_TILE : 0;
+    const int j = threadIdx.x;
+    __shared__ double wsum[4];
+    uint64_t h = 0;
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+        double s = 0.0;
+        if (t < full) {
+            // with the hash, GV vectors at a time: its 64-bit products would
+            // otherwise hold enough registers to cut the waves per SIMD
+            constexpr int GV = HASH ? (DT == DT_F32 ? 4 : 2) : RV;
+            const u32x4 *vp = static_cast<const u32x4 *>(buf) + t * VPT + j;
+#pragma unroll 1
+            for (int u0 = 0; u0 < RV; u0 += GV) {
+                u32x4 r[GV];
+#pragma unroll
+                for (int u = 0; u < GV; ++u)
+                    r[u] = __builtin_nontemporal_load(vp + (u0 + u) * 256);
+#pragma unroll
+                for (int u = 0; u < GV; ++u) {
+                    const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if constexpr (DT == DT_F32) {
+                            s += elem_value<DT>(w[q]);
+                        } else {
+                            s += elem_value<DT>(w[q] & 0xFFFFu);
+                            s += elem_value<DT>(w[q] >> 16);
+                        }
+                    }
+                    if constexpr (HASH)
+                        h += vec_hash<DT>(r[u], (t * VPT + (u0 + u) * 256 + j) * EPV);
+                }
+            }
+        } else {
+            for (int u = 0; u < RV; ++u)
+                for (int c = 0; c < EPV; ++c) {
+                    const int64_t e = t * SUM_TILE + (int64_t)(u * 256 + j) * EPV + c;
+                    if (e >= count)
+                        break;
+                    const uint32_t bits = DT == DT_F32
+                                              ? static_cast<const uint32_t *>(buf)[e]
+                                              : (uint32_t) static_cast<const uint16_t *>(buf)[e];
+                    s += elem_value<DT>(bits);
+                    if constexpr (HASH)
+                        h += elem_hash(e, bits);
+                }
+        }
+        s = wave_sum_f64(s);
+        if ((j & 63) == 0)
+            wsum[j >> 6] = s;
+        __syncthreads();
+        if (j == 0)
+            part[t] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+        __syncthreads();
+    }
+    if constexpr (HASH) {
+        // one atomic per workgroup: they all land on one word
+        __shared__ unsigned long long wh[4];
+        unsigned long long r = h;
+        for (int off = 32; off > 0; off >>= 1)
+            r += __shfl_xor(r, off);
+        if ((j & 63) == 0)
+            wh[j >> 6] = r;
+        __syncthreads();
+        if (j == 0)
+            atomicAdd(hash, wh[0] + wh[1] + wh[2] + wh[3]);
+    }
+}
+
+// The tile sums' total, in a fixed order: thread j adds part[j], part[j +
+// 1024], ... from +0, then a butterfly per wavefront, then the 16 wavefront
+// sums pairwise ((w0 + w1) + (w2 + w3)) + ... .  T = 0 gives +0.
+__global__ __launch_bounds__(SUM_FINISH_THREADS) void sum_finish_kernel(const double *part,
+                                                                        int64_t T, double *out)
+{
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < T; i += SUM_FINISH_THREADS)
+        s += part[i];
+    s = wave_sum_f64(s);
+    __shared__ double w[SUM_FINISH_THREADS / 64];
+    if ((threadIdx.x & 63) == 0)
+        w[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double v[SUM_FINISH_THREADS / 64];
+        for (int i = 0; i < SUM_FINISH_THREADS / 64; ++i)
+            v[i] = w[i];
+        for (int n = SUM_FINISH_THREADS / 64; n > 1; n >>= 1)
+            for (int i = 0; i < n / 2; ++i)
+                v[i] = v[2 * i] + v[2 * i + 1];
+        *out = v[0];
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t words, uint32_t value)
@@ -1522,6 +1654,39 @@ hipError_t launch_checksum(const void *buf, int64_t count, int dt, uint64_t *has
     else
         checksum_kernel<DT_BF16><<<g, 256, 0, s>>>(buf, count, aligned,
                                                     reinterpret_cast<unsigned long long *>(hash));
+    return hipGetLastError();
+}
+
+hipError_t launch_checksum_sum(const void *buf, int64_t count, int dt, uint64_t *hash, double *sum,
+                               double *part, int64_t cap, hipStream_t s)
+{
+    if (hash) {
+        fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t *>(hash), 2, 0u);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    const int64_t T = ceil_div(count, SUM_TILE);
+    if (T > 0) {
+        const bool aligned = (reinterpret_cast<uintptr_t>(buf) & 15u) == 0;
+        const unsigned g = grid_for(T, 1, cap);
+        auto *hp = reinterpret_cast<unsigned long long *>(hash);
+        if (dt == DT_F32) {
+            if (hash)
+                checksum_sum_kernel<DT_F32, true><<<g, 256, 0, s>>>(buf, count, aligned, hp, part);
+            else
+                checksum_sum_kernel<DT_F32, false><<<g, 256, 0, s>>>(buf, count, aligned, hp, part);
+        } else {
+            if (hash)
+                checksum_sum_kernel<DT_BF16, true><<<g, 256, 0, s>>>(buf, count, aligned, hp, part);
+            else
+                checksum_sum_kernel<DT_BF16, false><<<g, 256, 0, s>>>(buf, count, aligned, hp, part);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    sum_finish_kernel<<<1, SUM_FINISH_THREADS, 0, s>>>(part, T, sum);
     return hipGetLastError();
 }
 

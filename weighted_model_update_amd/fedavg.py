@@ -36,6 +36,7 @@ EXPORTS = [
     "fedavg_accumulate_partial", "fedavg_partial_info", "fedavg_state_size", "fedavg_export_state",
     "fedavg_resume", "topk_workspace_size", "topk_select", "fedavg_controller_step",
     "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
+    "fedavg_sum_workspace_size", "fedavg_checksum_sum",
 ]
 
 
@@ -82,6 +83,8 @@ def load(build_if_missing=True):
         "sparse_workspace_size": ([i32, i64, P], i32),
         "sparse_masked_accumulate": ([i32, P, P, P, P, i64, i32, P, P, P, i32, P, P, sz, P, P], i32),
         "fedavg_checksum": ([P, i64, i32, P, P], i32),
+        "fedavg_sum_workspace_size": ([i64, P], i32),
+        "fedavg_checksum_sum": ([P, i64, i32, P, P, P, sz, P], i32),
         "topk_workspace_size": ([i32, i64, i64, P], i32),
         "fedavg_controller_step": ([i32, P, P, P, i64, P, P, P, i32, P], i32),
         "topk_select": ([P, i32, i64, i64, P, P, P, sz, P], i32),
@@ -515,6 +518,38 @@ def fedavg_checksum(t, stream=None, hash_out=None):
                                   _stream_handle(stream)))
     if own:
         return int(hash_out.item()) & 0xFFFFFFFFFFFFFFFF
+    return None
+
+
+def fedavg_sum_workspace_size(count):
+    """Bytes of workspace fedavg_checksum_sum needs for `count` elements."""
+    b = ctypes.c_size_t(0)
+    _check(load().fedavg_sum_workspace_size(int(count), ctypes.byref(b)))
+    return b.value
+
+
+def fedavg_checksum_sum(t, stream=None, workspace=None, hash_out=None, sum_out=None, with_hash=True):
+    """In one read of a contiguous float32/bfloat16 GPU tensor, its checksum
+    and a deterministic fp64 sum of its values (fixed order of additions).
+    Returns (hash or None, sum) as Python values (synchronizing the stream)
+    unless sum_out (a float64 tensor of one element) is given; then the
+    results stay on the device (hash_out: an int64 tensor of one element, or
+    None for no hash)."""
+    _contig(t, "tensor")
+    if workspace is None:
+        workspace = torch.empty(max(fedavg_sum_workspace_size(t.numel()), 8), dtype=torch.uint8,
+                                device=t.device)
+    own = sum_out is None
+    if own:
+        sum_out = torch.empty(1, dtype=torch.float64, device=t.device)
+        if with_hash:
+            hash_out = torch.empty(1, dtype=torch.int64, device=t.device)
+    _check(load().fedavg_checksum_sum(_ptr(t), t.numel(), _dtype(t), _ptr(hash_out), _ptr(sum_out),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream_handle(stream)))
+    if own:
+        h = int(hash_out.item()) & 0xFFFFFFFFFFFFFFFF if hash_out is not None else None
+        return h, float(sum_out.item())
     return None
 
 
