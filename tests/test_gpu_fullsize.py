@@ -109,6 +109,50 @@ def test_sparse_1b_k20_sampled():
           label="sparse 1B sampled")
 
 
+def test_client_at_a_time_sparse_1b_k20_equals_the_one_pass_merge():
+    """The 20 top-10% lists of the 10^9-parameter sparse workload, scattered
+    one client at a time into the partial-mode streaming accumulator, give
+    the one-pass merge's output bit for bit over the whole buffer (both take
+    each parameter's clients in order with one fused multiply-add each, then
+    one division and the base), the same client counts and weight sums, and
+    agree with the oracle at sampled parameters."""
+    n, idx, val, base = sd.sparse_1b()
+    N = base.numel()
+    K = len(idx)
+    out1 = torch.empty(N, dtype=torch.float32, device="cuda")
+    counts1 = torch.empty(N, dtype=torch.uint8, device="cuda")
+    wsum1 = torch.empty(N, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fa.sparse_masked_accumulate(idx, val, n.tolist(), N, base, out1, counts=counts1, wsum=wsum1,
+                                err_flag=err)
+    out2 = torch.empty(N, dtype=torch.float32, device="cuda")
+    with fa.StreamingAccumulator(N, mode="deltas", partial=True, chunk_bytes=1 << 20, n_slots=2) as acc:
+        for k in range(K):
+            acc.accumulate(k, int(n[k]), val[k], indices=idx[k])
+        acc.finalize(base, out2)
+        acc.sync()
+        assert torch.equal(acc.count[:N], counts1)
+        assert torch.equal(acc.wsum[:N].view(torch.int32), wsum1)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32))
+    del out1, counts1, wsum1
+    at = sample_positions(N, 100_000, 11)
+    at_dev = torch.from_numpy(at).cuda()
+    sent, vals = [], []
+    for k in range(K):
+        pos = torch.searchsorted(idx[k], at_dev)
+        pos_c = pos.clamp(max=idx[k].numel() - 1)
+        found = (idx[k].index_select(0, pos_c) == at_dev)
+        sent.append(found.cpu().numpy().astype(np.uint8))
+        vals.append(torch.where(found, val[k].index_select(0, pos_c), torch.zeros_like(at_dev, dtype=torch.float32))
+                    .cpu().numpy())
+    hb = gather_bits(base, at_dev)
+    ref, mag, rcnt, _ = oracle.weighted_average(vals, n, mode=oracle.DELTAS, base=hb, sent=sent)
+    check(gather_bits(out2, at_dev), ref, mag, "f32", copied=rcnt == 0, copy_expect=hb,
+          label="client-at-a-time sparse 1B sampled")
+
+
 def test_streaming_8b_k32_sampled():
     per = synth.CHUNK_BYTES_8B // 2
     pool = sd.stream_8b_pool()
