@@ -433,9 +433,10 @@ int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *ha
  * (w0 + w1) + (w2 + w3) over the four; the tile sums are added by 1024
  * threads (thread j: sums j, j + 1024, ... in order), a butterfly, and a
  * pairwise tree over the 16 wavefronts.  So the result is the same bits on
- * every call and every launch shape, and within h * 2^-53 / (1 - h * 2^-53)
- * of sum |x_i| of the exact sum, h = 48 + ceil(T / 1024) for T tiles.  NaN,
- * or infinities of both signs, give NaN; a zero sum is +0.  workspace:
+ * every call and every launch shape.  It differs from the exact sum by at
+ * most g * (sum of |x_i|), g = h * 2^-53 / (1 - h * 2^-53), where
+ * h = 48 + ceil(T / 1024) is the longest chain of roundings for T tiles.
+ * NaN, or infinities of both signs, give NaN; a zero sum is +0.  workspace:
  * device memory of fedavg_sum_workspace_size bytes, 8-byte aligned, holding
  * the tile sums.  The buffer, the workspace and the results must not overlap
  * (FA_ERR_ARG); a short workspace is FA_ERR_WORKSPACE.
