@@ -66,6 +66,37 @@ def test_topk_partial_sharing_matches_oracle(blocks, tile):
     check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base, label=f"blocks={blocks}")
 
 
+@pytest.mark.parametrize("blocks", [0, 5, 997])
+def test_skewed_supports_place_every_range_boundary(blocks):
+    """Index lists far from uniform -- a dense cluster with a far outlier,
+    quadratically spaced indices, one narrow band, huge gaps, a single
+    entry -- so that estimating a range boundary's list position from the
+    index values misses by far; the positions (and so the merge) must still
+    be exact."""
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, blocks)
+    N = 1_000_003
+    r = np.random.default_rng(41)
+    lists = [
+        np.concatenate([np.arange(0, N // 100), [N - 1]]),
+        np.unique((np.arange(1000, dtype=np.int64) ** 2) % N),
+        np.arange(N // 2, N // 2 + 3000),
+        np.array([0, 1, 2, N - 3, N - 2, N - 1]),
+        np.array([N // 3]),
+        np.sort(r.choice(N, 50_000, replace=False)),
+        np.unique(np.minimum((r.pareto(0.5, 40_000) * 10).astype(np.int64), N - 1)),
+    ]
+    idx = [np.asarray(l, np.int64) for l in lists]
+    val = [r.laplace(0.0, 1e-3, len(i)).astype(np.float32) for i in idx]
+    n = synth.sample_counts(17, len(idx), 100, 1000)
+    base = synth.normal_f32(17, synth.ROLE_BASE, 0, N, 0.02)
+    got, cnt, ws, err = run_sparse(idx, val, n, N, base)
+    assert err == 0
+    ref, mag, rcnt, rws = oracle.sparse_average(idx, val, n, N, base=base)
+    assert np.array_equal(cnt, rcnt.astype(np.uint8))
+    assert np.array_equal(ws, rws.astype(np.uint32))
+    check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=base, label=f"skewed blocks={blocks}")
+
+
 @pytest.mark.parametrize("tile", TILES)
 def test_dense_support_overflows_batches(tile):
     # 60% density: several batches of each client per tile

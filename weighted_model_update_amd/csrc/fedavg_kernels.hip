@@ -814,6 +814,40 @@ __global__ __launch_bounds__(256) void stream_finalize_scalar_kernel(const Final
 
 // ================================================================ sparse merge
 
+// First position in ix[0, n) whose index is >= target, for a list sorted
+// ascending over [0, N).  Every probe lies inside the bracket [lo, hi) that
+// holds the answer, so the choice of probe changes only how fast it is found:
+// the first SPARSE_INTERP_STEPS probes interpolate between the index values
+// known at the bracket's ends (top-k supports are close to uniform, so a few
+// probes land next to the answer), the rest bisect, which bounds the probes
+// for any list.  An unsorted list gives some position in [0, n]; the merge
+// reports such lists whatever the offsets are.
+constexpr int SPARSE_INTERP_STEPS = 6;
+
+__device__ __forceinline__ int64_t sparse_lower_bound(const int64_t *ix, int64_t n, int64_t target,
+                                                      int64_t N)
+{
+    int64_t lo = 0, hi = n;
+    int64_t vlo = -1, vhi = N; // index values just outside the bracket (when sorted)
+    for (int step = 0; lo < hi; ++step) {
+        int64_t mid = lo + (hi - lo) / 2;
+        if (step < SPARSE_INTERP_STEPS && vhi > vlo && target > vlo && target <= vhi) {
+            const double f = (double)(target - vlo) / (double)(vhi - vlo);
+            const int64_t m = lo + (int64_t)(f * (double)(hi - lo));
+            mid = m < lo ? lo : (m > hi - 1 ? hi - 1 : m);
+        }
+        const int64_t v = ix[mid];
+        if (v < target) {
+            lo = mid + 1;
+            vlo = v;
+        } else {
+            hi = mid;
+            vhi = v;
+        }
+    }
+    return lo;
+}
+
 // For every client k and range boundary b (0..NB), the first position of k's
 // sorted index list at or after parameter b*R.  Also flags lists that hold
 // negative indices or indices >= N (those fall outside every range).
@@ -824,15 +858,7 @@ __global__ __launch_bounds__(256) void sparse_offsets_kernel(const SparseArgs a)
         const int k = (int)(t / (a.NB + 1));
         const int b = (int)(t % (a.NB + 1));
         const int64_t target = min((int64_t)b * a.R, a.N);
-        const int64_t *ix = a.idx[k];
-        int64_t lo = 0, hi = a.nnz[k];
-        while (lo < hi) {
-            const int64_t mid = lo + (hi - lo) / 2;
-            if (ix[mid] < target)
-                lo = mid + 1;
-            else
-                hi = mid;
-        }
+        const int64_t lo = sparse_lower_bound(a.idx[k], a.nnz[k], target, a.N);
         a.offs[t] = lo;
         if ((b == 0 && lo > 0) || (b == a.NB && lo < a.nnz[k]))
             *a.err = FA_ERR_INDEX;
