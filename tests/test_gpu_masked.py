@@ -169,3 +169,29 @@ def test_masked_argument_errors():
         fa.fedavg_aggregate([x], [1], torch.zeros(16, device="cuda"),
                             seg_bounds=torch.tensor([0, 16], device="cuda"),
                             present=torch.ones(1, dtype=torch.uint8, device="cuda"))  # no base
+
+
+@pytest.mark.parametrize("K", [33, 64])
+@pytest.mark.parametrize("T", [40, 700])
+def test_many_clients_use_every_mask_bit(K, T):
+    """Up to 64 clients: the per-segment client masks and weight sums use
+    all 64 bits, in the whole-table kernel (40 segments) and the windowed
+    one (700).  Clients above 32 alone send some segments, so a mask cut to
+    32 bits would drop them."""
+    r = np.random.default_rng(300 + K + T)
+    sizes = r.integers(1, 400, size=T)
+    bounds = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N = int(bounds[-1])
+    present = (r.random((K, T)) < 0.3).astype(np.uint8)
+    present[:, 0] = 0
+    present[K - 1, 0] = 1              # only the last client sent segment 0
+    present[:, 1] = 0
+    present[32:, 1] = 1                # only clients 32.. sent segment 1
+    present[:, 2] = 0                  # nobody sent segment 2
+    n = synth.sample_counts(21, K, 1, 1000)
+    xs = [(r.standard_normal(N) * 1e-3).astype(np.float32) for _ in range(K)]
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    for mode in ("weights", "deltas"):
+        got = run_masked(xs, n, bounds, present, base, "f32", "f32", "f32", mode)
+        ref, mag, cnt, _ = oracle_masked(xs, n, bounds, present, base, "f32", "f32", mode)
+        check(got, ref, mag, "f32", copied=cnt == 0, copy_expect=base, label=f"K={K} T={T} {mode}")

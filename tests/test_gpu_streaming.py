@@ -173,6 +173,42 @@ def test_stream_partial_counts_and_weight_sums_are_exact():
         acc.close()
 
 
+def test_partial_mode_holds_255_clients_and_refuses_the_256th():
+    """Partial mode keeps one uint8 client count per parameter, so a handle
+    takes at most 255 clients: parameters every client sent count 255
+    exactly, counts, weight sums and results match the oracle, and a 256th
+    client -- or a merged partial that would pass 255 -- is refused before
+    any launch."""
+    N, K = 2000, 255
+    r = np.random.default_rng(255)
+    n = synth.sample_counts(255, K, 1, 200)
+    sent = (r.random((K, N)) < 0.5).astype(np.uint8)
+    sent[:, :8] = 1
+    vals = [(r.standard_normal(N) * 1e-3).astype(np.float32) for _ in range(K)]
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    with fa.StreamingAccumulator(N, mode="deltas", partial=True, chunk_bytes=4 * N) as acc:
+        for k in range(K):
+            acc.accumulate(k, int(n[k]), dev_of(vals[k], "f32"), mask=torch.from_numpy(sent[k]).cuda())
+        with pytest.raises(fa.FedAvgError) as e:
+            acc.accumulate(K, 3, dev_of(vals[0], "f32"), mask=torch.from_numpy(sent[0]).cuda())
+        assert e.value.code == -3
+        part = torch.zeros(N, dtype=torch.float32, device="cuda")
+        ones = torch.ones(N, dtype=torch.int32, device="cuda")
+        cnt1 = torch.ones(N, dtype=torch.uint8, device="cuda")
+        with pytest.raises(fa.FedAvgError) as e:
+            acc.accumulate_partial(K + 1, 7, 1, part, ones, cnt1)
+        assert e.value.code == -3
+        out = empty(N, "f32")
+        acc.finalize(dev_of(base, "f32"), out)
+        acc.sync()
+        ref, mag, cnt, ws = oracle.weighted_average(vals, n, mode=oracle.DELTAS, base=base,
+                                                    sent=list(sent))
+        assert int(cnt[:8].min()) == 255
+        assert np.array_equal(acc.count[:N].cpu().numpy(), cnt.astype(np.uint8))
+        assert np.array_equal(acc.wsum[:N].cpu().numpy().view(np.uint32), ws.astype(np.uint32))
+        check(host_of(out), ref, mag, "f32", copied=cnt == 0, copy_expect=base)
+
+
 def test_stream_bad_indices_are_reported_by_sync():
     N = 1000
     with fa.StreamingAccumulator(N, mode="weights", partial=True, chunk_bytes=4096) as acc:
