@@ -14,5 +14,5 @@ from .fedavg import (  # noqa: F401
     fedavg_accumulate_partial, fedavg_partial_info, fedavg_export_state, fedavg_resume,
     sparse_workspace_size, sparse_masked_accumulate, fedavg_checksum, fedavg_sum_workspace_size,
     fedavg_checksum_sum,
-    topk_workspace_size, topk_select, topk_count, SampleController,
+    topk_workspace_size, topk_select, topk_count, SampleController, stream_windows,
 )

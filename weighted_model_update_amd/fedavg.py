@@ -504,6 +504,70 @@ def sparse_masked_accumulate(idx, val, n, N, base, out, mode="deltas", counts=No
     return workspace
 
 
+# ------------------------------------------------------------------ windows
+
+def stream_windows(N, clients, base, out, window=None, mode="weights", partial=False,
+                   chunk_bytes=64 << 20, n_slots=2, counts=True, device="cuda"):
+    """Streaming aggregation of an N-parameter model one window of the
+    parameter space at a time, for models whose accumulator (4 B per
+    parameter, 9 B in partial mode) does not fit in device memory beside the
+    rest.  A parameter's result depends only on its own clients' values in
+    client order, so the windows give the same bits as one handle over all N.
+
+    clients: a sequence of (client_id, n_k, chunks), where chunks() returns,
+    each time it is called, the client's chunks as (offset, values) or
+    (offset, values, mask), in ascending offset; values live on the device
+    or in pinned host memory.  chunks() is called once per window, and only
+    the part of each chunk inside the window is accumulated (a view, no
+    copy).  A host buffer may be reused n_slots chunks later, as with
+    fedavg_accumulate.  Every client is entered in every window, also where
+    it sent nothing inside it, so zero-fill mode divides by the same S.
+    base, out: N elements each, on the device or on the host (then copied a
+    window at a time); base may be None in dense weights mode.
+    window: parameters per window (default N).  The window's accumulator,
+    weight sums, counts and staging are allocated once and reused.
+    Returns the number of windows."""
+    N = int(N)
+    window = max(N, 1) if window is None else int(window)
+    if window < 1:
+        raise ValueError("window must be >= 1")
+    window = max(1, min(window, N))
+    acc_b, wsum_b, count_b, stag_b = fedavg_workspace_size(window, partial, chunk_bytes, n_slots)
+    acc = torch.empty(max(acc_b // 4, 1), dtype=torch.float32, device=device)
+    wsum = torch.empty(max(wsum_b // 4, 1), dtype=torch.int32, device=device) if partial else None
+    count = (torch.empty(max(count_b, 1), dtype=torch.uint8, device=device)
+             if partial and counts else None)
+    staging = torch.empty(stag_b, dtype=torch.uint8, device=device)
+    empty = torch.empty(0, dtype=torch.float32, device=device)
+    windows = 0
+    for w0 in range(0, N, window):
+        w1 = min(w0 + window, N)
+        h = fedavg_begin(w1 - w0, mode, partial, acc, wsum, count, staging, chunk_bytes, n_slots)
+        try:
+            for cid, n_k, chunks in clients:
+                fedavg_accumulate(h, cid, n_k, empty, 0)
+                for item in chunks():
+                    off, vals = int(item[0]), item[1]
+                    mask = item[2] if len(item) > 2 else None
+                    lo, hi = max(off, w0), min(off + vals.numel(), w1)
+                    if lo >= hi:
+                        continue
+                    fedavg_accumulate(h, cid, n_k, vals[lo - off:hi - off], lo - w0,
+                                      None if mask is None else mask[lo - off:hi - off])
+            bw = None if base is None else base[w0:w1]
+            if bw is not None and not bw.is_cuda:
+                bw = bw.to(device)
+            ow = out[w0:w1] if out.is_cuda else torch.empty(w1 - w0, dtype=out.dtype, device=device)
+            fedavg_finalize(h, bw, ow)
+            fedavg_sync(h)
+            if not out.is_cuda:
+                out[w0:w1].copy_(ow)
+        finally:
+            fedavg_destroy(h)
+        windows += 1
+    return windows
+
+
 # ------------------------------------------------------------------ checksum
 
 def fedavg_checksum(t, stream=None, hash_out=None):
