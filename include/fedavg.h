@@ -397,7 +397,7 @@ int topk_workspace_size(fa_dtype dtype, int64_t N, int64_t k, size_t *bytes);
  * int64[k]) in increasing order and their values, widened to fp32, to val_out
  * (device float[k]): exactly the per-client lists sparse_masked_accumulate
  * takes.  The result is unique, hence deterministic.
- * k == 0 returns FA_OK with no work; k > N or N > 2^39 is FA_ERR_RANGE.  workspace:
+ * k == 0 returns FA_OK with no work; k > N or N > 2^36 is FA_ERR_RANGE.  workspace:
  * device, 16-byte aligned, topk_workspace_size(dtype, N, k) bytes,
  * overwritten.  Outputs must not overlap x.  Asynchronous on `stream`.
  * The threshold is bounded first from a sample of about 2^20 values, so that

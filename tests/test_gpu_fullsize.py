@@ -302,3 +302,36 @@ def test_value_sum_1b_fp32_against_the_exact_sum():
     hh = 48 + -(-T // 1024)
     u = 2.0 ** -53
     assert abs(s - want) <= hh * u / (1 - hh * u) * absum * (1 + 4 * u), (s, want, absum)
+
+
+def test_past_2_35_parameters_the_grid_stride_covers_every_vector():
+    """Two bf16 clients of 2^35 + 8003 parameters: one 8-parameter vector
+    per lane would take more than the 2^32 - 1 work-items a launch holds, so
+    the grid stops at that and the dense kernel walks the rest grid-stride.
+    Sampled outputs, among them the last vectors and the ragged tail, match
+    the oracle."""
+    N = (1 << 35) + 8003
+
+    def normal_bf16(g, piece=1 << 30):
+        # drawn in fp32 pieces so that no full-size fp32 copy is ever held
+        x = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+        tmp = torch.empty(piece, dtype=torch.float32, device="cuda")
+        for o in range(0, N, piece):
+            m = min(piece, N - o)
+            tmp[:m].normal_(0.0, 0.02, generator=g)
+            x[o:o + m].copy_(tmp[:m])
+        return x
+
+    xs = [normal_bf16(sd.generator(synth.CFG_DENSE_2B, synth.ROLE_VALUES, 900 + c)) for c in range(2)]
+    n = np.array([300, 700], dtype=np.int64)
+    out = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    fa.fedavg_aggregate(xs, n.tolist(), out)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(35)
+    at = np.unique(np.concatenate([np.arange(N - 20_000, N), (1 << 35) - 8 + np.arange(16),
+                                   r.integers(0, N, 200_000)])).astype(np.int64)
+    at_dev = torch.from_numpy(at).cuda()
+    got = gather_bits(out, at_dev)
+    xk = [gather_bits(x, at_dev) for x in xs]
+    ref, mag, _, _ = oracle.weighted_average(xk, n, x_dtype=oracle.BF16)
+    check(got, ref, mag, "bf16", label="2^35 + 8003 dense")

@@ -70,6 +70,10 @@ def test_host_side_argument_errors_need_no_device():
     assert lib.topk_workspace_size(0, 100, 101, ctypes.byref(b)) == -3   # k > N
     assert lib.topk_workspace_size(7, 100, 10, ctypes.byref(b)) == -2    # unknown dtype
     assert lib.topk_workspace_size(0, 100, 10, None) == -1
+    assert lib.topk_workspace_size(0, (1 << 36) + 1, 10, ctypes.byref(b)) == -3   # one tile per workgroup
+    assert lib.topk_workspace_size(0, 1 << 36, 10, ctypes.byref(b)) == 0
+    assert lib.topk_select(P(1 << 20), 0, (1 << 36) + 1, 10, P(1 << 21), P(1 << 22), P(1 << 23), 1 << 40,
+                           None) == -3
     assert lib.fedavg_checksum(None, 10, 0, None, None) == -1
     d = ctypes.c_void_p
     assert lib.fedavg_checksum_sum(d(1 << 20), 10, 0, None, None, None, 0, None) == -1   # no sum

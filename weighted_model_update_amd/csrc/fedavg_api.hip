@@ -1182,6 +1182,10 @@ int fedavg_controller_step(int P, const double *t, const double *e, const int64_
 
 // ============================================================ top-k selection
 
+// One workgroup per 8192-element tile, and a launch holds at most 2^32 - 1
+// work-items: 2^36 elements (256 GB of fp32) is the most top-k takes.
+constexpr int64_t TOPK_MAX_N = 1ll << 36;
+
 int topk_workspace_size(fa_dtype dtype, int64_t N, int64_t k, size_t *bytes)
 {
     if (!bytes)
@@ -1190,6 +1194,8 @@ int topk_workspace_size(fa_dtype dtype, int64_t N, int64_t k, size_t *bytes)
         return fail(FA_ERR_DTYPE, "dtype must be FA_F32 or FA_BF16");
     if (N < 0 || k < 0 || k > N)
         return fail(FA_ERR_RANGE, "need 0 <= k <= N (k=%lld, N=%lld)", (long long)k, (long long)N);
+    if (N > TOPK_MAX_N)
+        return fail(FA_ERR_RANGE, "N=%lld is too large (at most 2^36)", (long long)N);
     *bytes = fa::topk_workspace_bytes(dtype, N, k);
     return ok();
 }
@@ -1205,8 +1211,8 @@ int topk_select(const void *x, fa_dtype dtype, int64_t N, int64_t k, int64_t *id
         return ok();
     if (!x || !idx_out || !val_out || !workspace)
         return fail(FA_ERR_ARG, "x, idx_out, val_out and workspace are required");
-    if (N > (1ll << 39)) // the per-region reservation counters hold 32-bit fields
-        return fail(FA_ERR_RANGE, "N=%lld is too large (at most 2^39)", (long long)N);
+    if (N > TOPK_MAX_N)
+        return fail(FA_ERR_RANGE, "N=%lld is too large (at most 2^36)", (long long)N);
     const size_t need = fa::topk_workspace_bytes(dtype, N, k);
     if (workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);

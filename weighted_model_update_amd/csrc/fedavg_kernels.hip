@@ -1397,6 +1397,12 @@ static size_t residency_lds(F *kernel, int cap)
     return bytes;
 }
 
+// Workgroups for `work` items, `threads` per workgroup, at most `cap` (0: no
+// cap).  A launch holds at most 2^32 - 1 work-items per dimension, so with
+// the 256-lane workgroups every launch through here uses, the grid stops at
+// MAX_GRID_256; the kernels walk their work grid-stride and cover the rest.
+constexpr int64_t MAX_GRID_256 = 0xFFFFFFFFll / 256;
+
 static inline unsigned grid_for(int64_t work, int threads, int64_t cap)
 {
     int64_t g = ceil_div(work, threads);
@@ -1404,8 +1410,8 @@ static inline unsigned grid_for(int64_t work, int threads, int64_t cap)
         g = cap;
     if (g < 1)
         g = 1;
-    if (g > 0x7fffffff)
-        g = 0x7fffffff;
+    if (g > MAX_GRID_256)
+        g = MAX_GRID_256;
     return (unsigned)g;
 }
 
@@ -1480,11 +1486,16 @@ template <int X, int O, int B, int M> struct MaskedRun {
     {
         if (aligned) {
             const int64_t nvec_all = ceil_div(a.N, VEC);
-            const unsigned g = grid_for(nvec_all, (int)a.vpb, 0);
-            if (a.T <= TAB_SEGS)
-                masked_table_kernel<X, O, B, M, 1><<<g, 256, 0, s>>>(a);
+            // the windowed kernel takes one run of vpb vectors per workgroup:
+            // runs long enough that their workgroups fit one launch
+            MaskedArgs b = a;
+            if (ceil_div(nvec_all, b.vpb) > MAX_GRID_256)
+                b.vpb = ceil_div(nvec_all, MAX_GRID_256);
+            const unsigned g = grid_for(nvec_all, (int)b.vpb, 0);
+            if (b.T <= TAB_SEGS)
+                masked_table_kernel<X, O, B, M, 1><<<g, 256, 0, s>>>(b);
             else
-                masked_vec_kernel<X, O, B, M><<<g, 256, 0, s>>>(a);
+                masked_vec_kernel<X, O, B, M><<<g, 256, 0, s>>>(b);
         } else {
             masked_scalar_kernel<X, O, B, M><<<grid_for(a.N, 256, 65536), 256, 0, s>>>(a);
         }
