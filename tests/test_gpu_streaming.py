@@ -54,6 +54,50 @@ def stream_dense(xs, n, dt, chunk, mode, base_dev, odt, where="pinned", n_slots=
     return out
 
 
+def test_two_handles_on_their_own_streams_interleaved():
+    """Two aggregations at once (two models, or two halves of one), each
+    handle with its own compute stream and copy stream, their pinned-host
+    chunks interleaved call by call: each gives the bits of the same
+    aggregation run alone, and the resident call's."""
+    K, N, chunk = 4, 200_003, 16_384
+    r = np.random.default_rng(77)
+    sets = []
+    for s in range(2):
+        n = synth.sample_counts(77 + s, K, 100, 10000)
+        ds = [synth.bf16_bits_from_f32((r.standard_normal(N) * 1e-3).astype(np.float32)) for _ in range(K)]
+        base = synth.bf16_bits_from_f32((r.standard_normal(N) * 0.02).astype(np.float32))
+        sets.append((n, ds, base))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [empty(N, "bf16"), empty(N, "bf16")]
+    accs = [fa.StreamingAccumulator(N, mode="deltas", chunk_bytes=2 * chunk, n_slots=2,
+                                    compute_stream=streams[s]) for s in range(2)]
+    try:
+        srcs = [[host_tensor(d, "bf16") for d in sets[s][1]] for s in range(2)]
+        for k in range(K):
+            for off in range(0, N, chunk):
+                for s in range(2):
+                    accs[s].accumulate(k, int(sets[s][0][k]), srcs[s][k][off:off + chunk], offset=off)
+        for s in range(2):
+            d_base = dev_of(sets[s][2], "bf16")
+            torch.cuda.synchronize()
+            with torch.cuda.stream(streams[s]):
+                accs[s].finalize(d_base, outs[s])
+            accs[s].sync()
+    finally:
+        for a in accs:
+            a.close()
+    torch.cuda.synchronize()
+    for s in range(2):
+        n, ds, base = sets[s]
+        alone = stream_dense(ds, n, "bf16", chunk, "deltas", dev_of(base, "bf16"), "bf16")
+        assert torch.equal(outs[s].view(torch.int16), alone.view(torch.int16))
+        res = empty(N, "bf16")
+        fa.fedavg_aggregate([dev_of(d, "bf16") for d in ds], n.tolist(), res, mode="deltas",
+                            base=dev_of(base, "bf16"))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[s].view(torch.int16), res.view(torch.int16))
+
+
 @pytest.mark.parametrize("where", ["pinned", "device"])
 @pytest.mark.parametrize("chunk", [4096, 1000, 1 << 20])
 def test_stream_deltas_match_oracle_and_resident(where, chunk):
