@@ -245,3 +245,42 @@ def test_resume_accepts_a_good_record_up_to_the_first_hip_call():
     assert _resume(_state(clients=((3, 1, 5, 400), (9, 4, 70000, 1000)))) == -9
     assert _resume(_state(partial=1, has_count=1, clients=((0, 255, 7, 10),)), partial=1,
                    count=ctypes.c_void_p(1 << 43)) == -9
+
+
+@pytest.mark.skipif(not _no_gpu_here(), reason="host-only check; needs a machine without a GPU")
+def test_resume_survives_any_record():
+    """Random records -- mutated bytes of a good record, truncations,
+    extensions, and well-formed records with random fields and a correct
+    checksum -- are either refused with an error status or pass validation
+    up to the first HIP call; none crashes the parser or reads past the
+    buffer it is given."""
+    from hypothesis import given, settings, strategies as st, HealthCheck
+
+    good = _state(partial=1, has_count=1, clients=((3, 2, 5, 400), (9, 4, 70000, 1000)))
+
+    @settings(max_examples=400, derandomize=True, deadline=None,
+              suppress_health_check=[HealthCheck.too_slow])
+    @given(st.data())
+    def run(data):
+        kind = data.draw(st.sampled_from(["flip", "cut", "grow", "fields"]))
+        if kind == "flip":
+            b = bytearray(good)
+            for _ in range(data.draw(st.integers(1, 8))):
+                b[data.draw(st.integers(0, len(b) - 1))] = data.draw(st.integers(0, 255))
+            rec = bytes(b)
+        elif kind == "cut":
+            rec = good[:data.draw(st.integers(0, len(good) - 1))]
+        elif kind == "grow":
+            rec = good + bytes(data.draw(st.binary(min_size=1, max_size=64)))
+        else:
+            nc = data.draw(st.integers(0, 6))
+            clients = tuple((data.draw(st.integers(-2, 5)), data.draw(st.integers(-1, 300)),
+                             data.draw(st.integers(-1, 1 << 33)), data.draw(st.integers(-5, 1100)))
+                            for _ in range(nc))
+            rec = _state(N=data.draw(st.sampled_from([1000, 0, -1, 1 << 41])),
+                         partial=data.draw(st.integers(0, 2)), has_count=data.draw(st.integers(0, 1)),
+                         finalized=data.draw(st.integers(-1, 2)), clients=clients)
+        rc = _resume(rec, partial=1, count=ctypes.c_void_p(1 << 43))
+        assert rc in (-1, -3, -9), rc
+
+    run()
