@@ -158,7 +158,7 @@ typedef struct fa_stream_state *fa_handle;
  *              1: partial (clients send ranges, masked ranges or index lists;
  *                 each parameter is averaged over the clients that sent it).
  * chunk_bytes  largest chunk payload per call (values), > 0.
- * n_slots      staging slots for host-resident chunks (>= 1; 2 or more lets
+ * n_slots      staging slots for host-resident chunks (1 to 64; 2 or more lets
  *              the next copy overlap the current accumulate).
  * acc_bytes    N fp32;  wsum_bytes  N uint32 (partial only, else 0);
  * count_bytes  N uint8 (partial only, else 0);

@@ -438,10 +438,10 @@ static int open_handle(fa_handle *h, int64_t N, int mode, int partial, float *ac
     if (!h)
         return fail(FA_ERR_ARG, "handle pointer is NULL");
     *h = nullptr;
-    if (N < 0 || chunk_bytes <= 0 || n_slots < 1 || n_slots > 64)
-        return fail(FA_ERR_ARG, "need N >= 0, chunk_bytes > 0, 1 <= n_slots <= 64");
-    if (N > FA_MAX_N || chunk_bytes > FA_MAX_N)
-        return fail(FA_ERR_RANGE, "need N <= 2^40 and chunk_bytes <= 2^40");
+    if (N < 0 || chunk_bytes <= 0 || n_slots < 1)
+        return fail(FA_ERR_ARG, "need N >= 0, chunk_bytes > 0, n_slots >= 1");
+    if (N > FA_MAX_N || chunk_bytes > FA_MAX_N || n_slots > 64)
+        return fail(FA_ERR_RANGE, "need N <= 2^40, chunk_bytes <= 2^40, n_slots <= 64");
     if (mode != FA_WEIGHTS && mode != FA_DELTAS && mode != FA_DELTAS_ZERO_FILL)
         return fail(FA_ERR_ARG, "unknown mode %d", mode);
     if (partial != 0 && partial != 1)
@@ -1242,7 +1242,6 @@ int fedavg_checksum(const void *buf, int64_t count, fa_dtype dtype, uint64_t *ha
     hipError_t e = fa::launch_checksum(buf, count, dtype, hash_dev, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "checksum launch");
 }
-
 
 int fedavg_sum_workspace_size(int64_t count, size_t *bytes)
 {
