@@ -56,6 +56,18 @@ def test_dense_2b_k16_bf16_sampled():
     xk = [gather_bits(x, at_dev) for x in xs]
     ref, mag, _, _ = oracle.weighted_average(xk, n, x_dtype=oracle.BF16)
     check(got, ref, mag, "bf16", label="dense 2B sampled")
+    # the bf16 output's checksum and value sum against the oracle's, over the
+    # whole 1.92-billion-element buffer
+    h, vs = fa.fedavg_checksum_sum(out)
+    assert h == h1
+    bits = host_of(out)
+    assert h == oracle.checksum(bits, oracle.BF16)
+    want = oracle.value_sum(bits, oracle.BF16)
+    absum = oracle.value_sum(bits & np.uint16(0x7FFF), oracle.BF16)
+    T = -(-N // 8192)
+    hh = 48 + -(-T // 1024)
+    u = 2.0 ** -53
+    assert abs(vs - want) <= hh * u / (1 - hh * u) * absum * (1 + 4 * u), (vs, want)
 
 
 def test_adapter_k8_full_compare():
