@@ -347,3 +347,44 @@ def test_past_2_35_parameters_the_grid_stride_covers_every_vector():
     xk = [gather_bits(x, at_dev) for x in xs]
     ref, mag, _, _ = oracle.weighted_average(xk, n, x_dtype=oracle.BF16)
     check(got, ref, mag, "bf16", label="2^35 + 8003 dense")
+
+
+def test_topk_1b_bf16_client_update_properties():
+    """Top-10% of a 10^9-parameter bf16 update (the fp32 Laplace update
+    rounded to bf16, so many magnitudes tie): k entries, strictly increasing
+    indices, values read at those indices and widened to fp32, every kept
+    key at least every dropped key, the kept ties below the dropped ones;
+    the sampled and three-pass paths agree bit for bit; the oracle agrees on
+    a window."""
+    N = 10 ** 9
+    x = sd.client_delta_1b(0, N).to(torch.bfloat16)
+    k = fa.topk_count(N, 0.1)
+    idx, val = fa.topk_select(x, k)
+    torch.cuda.synchronize()
+    assert idx.numel() == k
+    assert bool((idx[1:] > idx[:-1]).all()) and int(idx[0]) >= 0 and int(idx[-1]) < N
+    assert torch.equal(val, x[idx].float())
+    key = x.view(torch.int16).to(torch.int32) & 0x7FFF
+    kept = torch.zeros(N, dtype=torch.bool, device="cuda")
+    kept[idx] = True
+    T = int(key[idx].min())
+    dropped_max = int(key.masked_fill(kept, -1).max())
+    assert dropped_max <= T
+    if dropped_max == T:
+        tie = key == T
+        assert int(torch.nonzero(tie & kept).flatten().max()) < int(torch.nonzero(tie & ~kept).flatten().min())
+    del key, kept
+    fa.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 0)
+    try:
+        i3, v3 = fa.topk_select(x, k)
+        torch.cuda.synchronize()
+    finally:
+        fa.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 1)
+    assert torch.equal(i3, idx) and torch.equal(v3.view(torch.int32), val.view(torch.int32))
+    del i3, v3
+    w = host_of(x[:2_000_000])
+    kw = 200_000
+    wi, wv = fa.topk_select(x[:2_000_000], kw)
+    oi, ov = oracle.topk(w, oracle.BF16, kw)
+    assert np.array_equal(wi.cpu().numpy(), oi) and np.array_equal(wv.cpu().numpy().view(np.uint32),
+                                                                   ov.view(np.uint32))
