@@ -12,8 +12,17 @@ also carries every other aggregation mode at its full workload size:
   streaming    8,030,261,248 bf16 parameters, K=32 clients arriving one by
                one as 64 MiB chunks from pinned host memory (PCIe bound), and
                the accumulate kernel alone on device-resident chunks
+  windows      the streaming workload with the accumulator cut into 4 windows
+               of the parameter space (for accumulators larger than HBM)
   sparse       10^9 fp32 parameters, K=20 clients each sending its top 10%
                (sorted int64 index, fp32 value) pairs
+  topk         client-side top-10% selection from a 10^9-parameter fp32 update
+  hierarchical two-level aggregation: 4 silo partials of 8,030,261,248 fp32
+               sums merged into the top-level accumulator
+  sparse_stream  the sparse lists scattered one client at a time into the
+               streaming accumulator (partial mode)
+  checksum     order-independent hash and fixed-order fp64 value sum of a
+               10^9-element fp32 buffer
 
 Inputs are seeded synthetic data generated on the GPU before timing.  The
 roofline object reports the headline kernel against MI355X's 8 TB/s HBM; the
@@ -348,6 +357,50 @@ def bench_topk(steps=10, warmup=2):
                     "candidates, and the ordered write reads the staged entries"}
 
 
+def bench_windows(clients=32, windows=4, slots=3):
+    """The 8B streaming workload with the accumulator cut into `windows`
+    windows of the parameter space (stream_windows: for models whose fp32
+    accumulator does not fit in HBM): every client's chunks are streamed once
+    per window, clipped to it, so the PCIe bytes equal the single-handle
+    run's."""
+    import torch
+    import synth.device as sd
+    import synth
+    import weighted_model_update_amd as fa
+    chunk_bytes = synth.CHUNK_BYTES_8B
+    per = chunk_bytes // 2
+    log(f"windows: the 8B streaming workload in {windows} windows")
+    pool = sd.stream_8b_pool()
+    P = pool.shape[0]
+    base = sd.stream_8b_base()
+    N = base.numel()
+    n = sd.stream_8b_counts(32)[:clients]
+    cpc = (N + per - 1) // per
+    window = -(-N // windows)
+
+    def chunks_of(k):
+        def gen():
+            for c in range(cpc):
+                off = c * per
+                yield off, pool[sd.pool_index(k, c, cpc, P)][:min(per, N - off)]
+        return gen
+
+    fa.stream_windows(N, [(0, int(n[0]), chunks_of(0))], base, base, window=window, mode="deltas",
+                      chunk_bytes=chunk_bytes, n_slots=slots)                       # warm-up, 1 client
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    nw = fa.stream_windows(N, [(k, int(n[k]), chunks_of(k)) for k in range(clients)], base, base,
+                           window=window, mode="deltas", chunk_bytes=chunk_bytes, n_slots=slots)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pcie_bytes = 2 * N * clients
+    del pool, base
+    free_gpu()
+    return {"K": clients, "N": N, "windows": nw, "window_params": window,
+            "accumulator_bytes_per_window": 4 * window, "wall_s": wall, "pcie_bytes": pcie_bytes,
+            "pcie_gbs": pcie_bytes / wall / 1e9, "pcie_frac": pcie_bytes / wall / 1e9 / PCIE_PEAK_GBS}
+
+
 def bench_sparse(steps=10, warmup=2):
     import torch
     import synth.device as sd
@@ -519,8 +572,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
-                    help="comma list of: dense,dense_small,adapter,streaming,sparse,topk,hierarchical,"
-                         "sparse_stream,checksum,cpu,copycal "
+                    help="comma list of: dense,dense_small,adapter,streaming,windows,sparse,topk,"
+                         "hierarchical,sparse_stream,checksum,cpu,copycal "
                          "(default all but copycal)")
     ap.add_argument("--stream-clients", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -537,7 +590,7 @@ def main():
     fa.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     only = set(args.only.split(",")) if args.only != "all" else {"dense", "dense_small", "adapter",
-                                                                 "streaming", "sparse", "topk",
+                                                                 "streaming", "windows", "sparse", "topk",
                                                                  "hierarchical", "sparse_stream",
                                                                  "checksum", "cpu"}
     if args.no_cpu_baseline:
@@ -570,6 +623,10 @@ def main():
     if "sparse_stream" in only:
         modes["sparse_stream"] = bench_sparse_stream()
         log(f"sparse_stream: {modes['sparse_stream']['ms_per_client']:.3f} ms per client")
+    if "windows" in only:
+        modes["windows"] = bench_windows(args.stream_clients)
+        log(f"windows: {modes['windows']['wall_s']:.2f} s in {modes['windows']['windows']} windows "
+            f"({modes['windows']['pcie_gbs']:.1f} GB/s over PCIe)")
     if "checksum" in only:
         modes["checksum"] = bench_checksum()
         log(f"checksum: {modes['checksum']['ms_per_call']:.3f} ms/call, with the value sum "
