@@ -284,3 +284,33 @@ def test_resume_survives_any_record():
         assert rc in (-1, -3, -9), rc
 
     run()
+
+
+def test_missing_library_fails_loudly():
+    """Without libfedavg.so (and no way to build it) every entry point raises;
+    nothing falls back to a CPU path.  Run in a fresh interpreter so the
+    library this session loaded stays untouched."""
+    import subprocess
+    import sys
+    code = r"""
+import torch
+import weighted_model_update_amd as fa
+import weighted_model_update_amd.build as b
+b.LIB_PATH = "/nonexistent/libfedavg.so"
+def no_build(*a, **k):
+    raise RuntimeError("no toolchain")
+b.build = no_build
+for call in (lambda: fa.load(build_if_missing=False),
+             lambda: fa.fedavg_aggregate([torch.zeros(8)], [1], torch.zeros(8)),
+             lambda: fa.fedavg_checksum(torch.zeros(8))):
+    try:
+        call()
+    except RuntimeError as e:
+        print("raised", "libfedavg" in str(e) or "toolchain" in str(e))
+    else:
+        print("returned")
+"""
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    lines = [l for l in r.stdout.splitlines() if l.startswith(("raised", "returned"))]
+    assert lines == ["raised True"] * 3, r.stdout + r.stderr
