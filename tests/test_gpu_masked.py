@@ -195,3 +195,39 @@ def test_many_clients_use_every_mask_bit(K, T):
         got = run_masked(xs, n, bounds, present, base, "f32", "f32", "f32", mode)
         ref, mag, cnt, _ = oracle_masked(xs, n, bounds, present, base, "f32", "f32", mode)
         check(got, ref, mag, "f32", copied=cnt == 0, copy_expect=base, label=f"K={K} T={T} {mode}")
+
+
+@pytest.mark.parametrize("T,misalign", [(300, False), (900, False), (300, True)])
+def test_absent_segments_are_never_read_and_nothing_outside_out_is_written(T, misalign):
+    """Every client's absent segments hold NaN: none may reach the output
+    (a read times a zero weight would still give NaN).  The output sits
+    inside a larger buffer whose neighbouring words must stay untouched.
+    The whole-table kernel (300 segments), the windowed kernel (900) and the
+    element-wise path (an unaligned output) are all checked."""
+    r = np.random.default_rng(500 + T + misalign)
+    sizes = r.integers(0, 700, size=T)
+    bounds = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    N, K = int(bounds[-1]), 5
+    present = (r.random((K, T)) < 0.5).astype(np.uint8)
+    sent = sent_from_segments(bounds, present)
+    xs = []
+    for k in range(K):
+        x = (r.standard_normal(N) * 1e-3).astype(np.float32)
+        x[sent[k] == 0] = np.nan
+        xs.append(x)
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    n = synth.sample_counts(31, K, 1, 1000)
+    G = 64 + (1 if misalign else 0)
+    whole = torch.full((G + N + 64,), -7.25, dtype=torch.float32, device="cuda")
+    out = whole[G:G + N]
+    fa.fedavg_aggregate([dev_of(x, "f32") for x in xs], list(n), out, mode="deltas",
+                        base=dev_of(base, "f32"),
+                        seg_bounds=torch.tensor(bounds, dtype=torch.int64, device="cuda"),
+                        present=torch.from_numpy(present).cuda())
+    torch.cuda.synchronize()
+    got = host_of(out)
+    assert not np.isnan(got).any()
+    ref, mag, cnt, _ = oracle.weighted_average(xs, n, mode=oracle.DELTAS, base=base, sent=sent)
+    check(got, ref, mag, "f32", copied=cnt == 0, copy_expect=base, label=f"T={T}")
+    guard = torch.cat([whole[:G], whole[G + N:]])
+    assert bool((guard == -7.25).all())
