@@ -61,6 +61,9 @@ def _load():
     lib.orc_round_to_bf16.restype = None
     lib.orc_checksum.argtypes = [P, i64, ctypes.c_int, i64]
     lib.orc_checksum.restype = ctypes.c_uint64
+    lib.orc_mirror_f32.argtypes = [ctypes.c_int, P, ctypes.c_int, P, P, i64, ctypes.c_int, P,
+                                   ctypes.c_int, ctypes.c_int, P]
+    lib.orc_mirror_f32.restype = ctypes.c_int
     lib.orc_sum.argtypes = [P, i64, ctypes.c_int]
     lib.orc_sum.restype = ctypes.c_double
     lib.orc_sum_set_carry_period.argtypes = [i64]
@@ -187,6 +190,31 @@ def checksum(a, dtype, first=0):
     lib = _load()
     a = _raw(a, dtype)
     return int(lib.orc_checksum(_ptr(a), a.size, dtype, first))
+
+
+def mirror_f32(xs, n, mode=WEIGHTS, base=None, x_dtype=F32, base_dtype=F32, out_dtype=F32, sent=None):
+    """The library's stated fp32 rounding order, for bit-for-bit checks: per
+    parameter, fused multiply-adds of fp32(n_k) * x in client order from +0,
+    one fp32 division by fp32(W) (fp32(S) in zero-fill mode), the base added
+    in fp32 in delta modes, rounded to nearest-even into out_dtype.  Returns
+    float32 values, or uint16 bf16 bits."""
+    lib = _load()
+    K = len(xs)
+    xs = [_raw(x, x_dtype) for x in xs]
+    N = int(xs[0].shape[0]) if K else 0
+    n = np.ascontiguousarray(n, dtype=np.int64)
+    if base is not None:
+        base = _raw(base, base_dtype)
+    sent_arrs = None
+    if sent is not None:
+        sent = [np.ascontiguousarray(s_, dtype=np.uint8) for s_ in sent]
+        sent_arrs = _ptr_array(sent)
+    out = np.empty(N, np.float32 if out_dtype == F32 else np.uint16)
+    rc = lib.orc_mirror_f32(K, _ptr_array(xs), x_dtype, _ptr(n), sent_arrs, N, mode, _ptr(base),
+                            base_dtype, out_dtype, _ptr(out))
+    if rc != 0:
+        raise OracleError(f"orc_mirror_f32 failed: {rc}")
+    return out
 
 
 def value_sum(a, dtype):

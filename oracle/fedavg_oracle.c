@@ -319,6 +319,62 @@ void orc_round_to_bf16(const float *in, uint16_t *out, int64_t count)
 }
 
 /*
+ * fp32 mirror of the rounding order the library states for every
+ * aggregation path, so that GPU results can be checked bit for bit (the fp64
+ * weighted average above is the definition; this is one particular fp32
+ * evaluation of it).  For each parameter: acc = +0; for each client in
+ * order with n_k > 0 that sent the parameter, acc = fmaf((float)n_k, x,
+ * acc), one fused rounding; q = acc / (float)D, an IEEE fp32 division, with
+ * D = W (or S, every client with n_k > 0, in zero-fill mode); the delta
+ * modes add the base in fp32; the result is rounded to nearest-even into
+ * the output type.  A parameter nobody sent takes the base, rounded the
+ * same way.  x, base: as for orc_weighted_average; out: N elements of
+ * out_dtype (fp32, or bf16 bits).
+ */
+int orc_mirror_f32(int K, const void *const *x, int x_dtype, const int64_t *n,
+                   const uint8_t *const *sent, int64_t N, int mode, const void *base,
+                   int base_dtype, int out_dtype, void *out)
+{
+    if (K < 1 || N < 0 || !x || !n || !out || !dtype_ok(x_dtype) || !dtype_ok(out_dtype))
+        return ORC_ERR_ARG;
+    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS && mode != ORC_DELTAS_ZERO_FILL)
+        return ORC_ERR_ARG;
+    if ((mode != ORC_WEIGHTS && !base) || (base && !dtype_ok(base_dtype)))
+        return ORC_ERR_ARG;
+    uint64_t S = 0;
+    for (int k = 0; k < K; ++k) {
+        if (n[k] < 0 || (n[k] > 0 && !x[k]))
+            return ORC_ERR_ARG;
+        S += (uint64_t)n[k];
+    }
+    for (int64_t i = 0; i < N; ++i) {
+        float acc = 0.0f;
+        uint64_t W = 0;
+        for (int k = 0; k < K; ++k) {
+            if (n[k] == 0 || (sent && !sent[k][i]))
+                continue;
+            acc = fmaf((float)n[k], (float)value_at(x[k], x_dtype, i), acc);
+            W += (uint64_t)n[k];
+        }
+        float r;
+        if (W == 0) {
+            if (!base)
+                return ORC_ERR_ZERO_WEIGHT;
+            r = (float)value_at(base, base_dtype, i);
+        } else {
+            const float D = (float)(mode == ORC_DELTAS_ZERO_FILL ? S : W);
+            const float q = acc / D;
+            r = (mode == ORC_WEIGHTS) ? q : (float)value_at(base, base_dtype, i) + q;
+        }
+        if (out_dtype == ORC_F32)
+            ((float *)out)[i] = r;
+        else
+            orc_round_to_bf16(&r, (uint16_t *)out + i, 1);
+    }
+    return ORC_OK;
+}
+
+/*
  * Order-independent checksum of a buffer of elements of the given type:
  * H = sum over i of fmix64(i * 0x9E3779B97F4A7C15 XOR bits_i), modulo
  * 2^64, where bits_i is the element's raw bit pattern (16 or 32 bits) and

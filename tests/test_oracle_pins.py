@@ -603,3 +603,92 @@ def test_value_sum_special_values():
     assert oracle.value_sum(np.zeros(0, np.float32), oracle.F32) == 0.0
     assert oracle.value_sum(np.uint16([0x7F80, 0x3F80]), oracle.BF16) == math.inf
     assert math.isnan(oracle.value_sum(np.uint16([0xFFC1, 0x3F80]), oracle.BF16))
+
+
+# ---------------------------------------------------------------- fp32 mirror
+
+def _np_f32_sequence(xs, n, sent, mode, base, S_all):
+    """With weights that are powers of two, fp32(n_k) * x is exact, so each
+    fused multiply-add is one IEEE fp32 addition: numpy's float32 arithmetic
+    computes the same sequence independently."""
+    N = len(xs[0])
+    acc = np.zeros(N, np.float32)
+    W = np.zeros(N, np.int64)
+    for k in range(len(xs)):
+        if n[k] == 0:
+            continue
+        on = np.ones(N, bool) if sent is None else sent[k].astype(bool)
+        prod = np.float32(n[k]) * xs[k]                      # exact for n_k = 2^j
+        acc = np.where(on, (acc + prod).astype(np.float32), acc)
+        W = W + np.where(on, n[k], 0)
+    D = np.float32(S_all) if mode == oracle.DELTAS_ZERO_FILL else W.astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = (acc / D).astype(np.float32)
+    r = q if mode == oracle.WEIGHTS else (base + q).astype(np.float32)
+    return np.where(W > 0, r, base if base is not None else r).astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", [oracle.WEIGHTS, oracle.DELTAS, oracle.DELTAS_ZERO_FILL])
+def test_mirror_equals_float32_arithmetic_for_power_of_two_weights(mode):
+    r = np.random.default_rng(70 + mode)
+    N, K = 5000, 7
+    xs = [(r.standard_normal(N) * 10.0 ** r.integers(-4, 2)).astype(np.float32) for _ in range(K)]
+    n = [int(2 ** r.integers(0, 12)) for _ in range(K)]
+    n[2] = 0
+    sent = [(r.random(N) < 0.6).astype(np.uint8) for _ in range(K)]
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    S_all = sum(v for v in n if v > 0)
+    got = oracle.mirror_f32(xs, n, mode=mode, base=base, sent=sent)
+    want = _np_f32_sequence(xs, n, sent, mode, base, S_all)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_mirror_follows_client_order_with_one_rounding_per_step():
+    """1 + 2^-24 is a tie and rounds back to 1, while 2^-24 + 2^-24 + 1 is
+    exact: the same three clients in two orders give different bits, as the
+    fp32 steps in client order say they must."""
+    one, tiny = np.float32(1.0), np.float32(2.0 ** -24)
+    a = oracle.mirror_f32([np.float32([one]), np.float32([tiny]), np.float32([tiny])], [1, 1, 1])
+    b = oracle.mirror_f32([np.float32([tiny]), np.float32([tiny]), np.float32([one])], [1, 1, 1])
+    assert a[0] == np.float32(1.0) / np.float32(3.0)
+    assert b[0] == np.float32(1.0 + 2.0 ** -23) / np.float32(3.0)
+    assert a[0] != b[0]
+
+
+@pytest.mark.parametrize("x_dtype,out_dtype", [(oracle.F32, oracle.F32), (oracle.BF16, oracle.BF16),
+                                               (oracle.BF16, oracle.F32), (oracle.F32, oracle.BF16)])
+def test_mirror_within_the_rounding_bound_of_the_definition(x_dtype, out_dtype):
+    """General weights (fused products not exact): the mirror stays within
+    the fp32 tolerance of the fp64 definition, and parameters nobody sent
+    are the base rounded to the output type."""
+    from parity import check
+    r = np.random.default_rng(90 + x_dtype + 2 * out_dtype)
+    N, K = 4000, 9
+    x32 = [(r.standard_normal(N) * 1e-2).astype(np.float32) for _ in range(K)]
+    xs = [synth.bf16_bits_from_f32(x) for x in x32] if x_dtype == oracle.BF16 else x32
+    n = synth.sample_counts(3, K, 100, 10000)
+    sent = [(r.random(N) < 0.4).astype(np.uint8) for _ in range(K)]
+    sent[0][:50] = 1
+    for s_ in sent:
+        s_[50:60] = 0                        # nobody sent these
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    for mode in (oracle.WEIGHTS, oracle.DELTAS):
+        got = oracle.mirror_f32(xs, n, mode=mode, base=base, x_dtype=x_dtype, out_dtype=out_dtype, sent=sent)
+        ref, mag, cnt, _ = oracle.weighted_average(xs, n, mode=mode, base=base, x_dtype=x_dtype, sent=sent)
+        odt = "bf16" if out_dtype == oracle.BF16 else "f32"
+        expect_copy = oracle.round_to_bf16(base) if out_dtype == oracle.BF16 else base
+        check(got, ref, mag, odt, copied=cnt == 0, copy_expect=expect_copy)
+
+
+def test_mirror_products_are_fused():
+    """The rounding error of an fp32 product is itself an fp32 number: when
+    the accumulator holds -RN(3x), a fused multiply-add of 3 * x leaves
+    exactly that error, where a rounded product and a separate addition
+    leave 0.  The result divides by W = 1 + 3 = 4, exactly."""
+    r = np.random.default_rng(5)
+    x = (1.0 + r.random(64)).astype(np.float32)
+    rn3x = (np.float32(3.0) * x).astype(np.float32)          # numpy: one IEEE rounding
+    err = 3.0 * x.astype(np.float64) - rn3x.astype(np.float64)  # exact in float64
+    assert (err != 0).sum() > 32
+    got = oracle.mirror_f32([-rn3x, x], [1, 3])
+    assert np.array_equal(got, (err / 4.0).astype(np.float32))
