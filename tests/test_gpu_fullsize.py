@@ -18,6 +18,15 @@ import weighted_model_update_amd as fa
 from parity import check
 from gpu_util import host_of
 
+
+def same_bits(got, want):
+    """Equal bit patterns (the stated fp32 rounding order, checked against
+    the oracle's fp32 mirror of it)."""
+    g, w = np.asarray(got), np.asarray(want)
+    assert g.dtype == w.dtype and g.shape == w.shape
+    v = np.uint32 if g.dtype == np.float32 else np.uint16
+    assert np.array_equal(g.view(v), w.view(v)), int((g.view(v) != w.view(v)).sum())
+
 pytestmark = pytest.mark.gpu
 
 
@@ -56,6 +65,7 @@ def test_dense_2b_k16_bf16_sampled():
     xk = [gather_bits(x, at_dev) for x in xs]
     ref, mag, _, _ = oracle.weighted_average(xk, n, x_dtype=oracle.BF16)
     check(got, ref, mag, "bf16", label="dense 2B sampled")
+    same_bits(got, oracle.mirror_f32(xk, n, x_dtype=oracle.BF16, out_dtype=oracle.BF16))
     # the bf16 output's checksum and value sum against the oracle's, over the
     # whole 1.92-billion-element buffer
     h, vs = fa.fedavg_checksum_sum(out)
@@ -84,6 +94,8 @@ def test_adapter_k8_full_compare():
     ref, mag, cnt, _ = oracle.weighted_average([host_of(x) for x in xs], n, x_dtype=oracle.BF16,
                                                base=hb, base_dtype=oracle.BF16, sent=sent)
     check(host_of(out), ref, mag, "bf16", copied=cnt == 0, copy_expect=hb, label="adapter full")
+    same_bits(host_of(out), oracle.mirror_f32([host_of(x) for x in xs], n, x_dtype=oracle.BF16, base=hb,
+                                              base_dtype=oracle.BF16, out_dtype=oracle.BF16, sent=sent))
 
 
 def test_sparse_1b_k20_sampled():
@@ -119,6 +131,7 @@ def test_sparse_1b_k20_sampled():
     assert np.array_equal(wsum.index_select(0, at_dev).cpu().numpy().view(np.uint32), rws.astype(np.uint32))
     check(gather_bits(out, at_dev), ref, mag, "f32", copied=rcnt == 0, copy_expect=hb,
           label="sparse 1B sampled")
+    same_bits(gather_bits(out, at_dev), oracle.mirror_f32(vals, n, mode=oracle.DELTAS, base=hb, sent=sent))
 
 
 def test_client_at_a_time_sparse_1b_k20_equals_the_one_pass_merge():
@@ -193,6 +206,8 @@ def test_streaming_8b_k32_sampled():
     ref, mag, _, _ = oracle.weighted_average(deltas, n, mode=oracle.DELTAS, base=base_before,
                                              x_dtype=oracle.BF16, base_dtype=oracle.BF16)
     check(got, ref, mag, "bf16", label="streaming 8B sampled")
+    same_bits(got, oracle.mirror_f32(deltas, n, mode=oracle.DELTAS, base=base_before, x_dtype=oracle.BF16,
+                                     base_dtype=oracle.BF16, out_dtype=oracle.BF16))
 
 
 def test_two_level_8b_three_silos_sampled():
@@ -347,6 +362,7 @@ def test_past_2_35_parameters_the_grid_stride_covers_every_vector():
     xk = [gather_bits(x, at_dev) for x in xs]
     ref, mag, _, _ = oracle.weighted_average(xk, n, x_dtype=oracle.BF16)
     check(got, ref, mag, "bf16", label="2^35 + 8003 dense")
+    same_bits(got, oracle.mirror_f32(xk, n, x_dtype=oracle.BF16, out_dtype=oracle.BF16))
 
 
 def test_topk_1b_bf16_client_update_properties():
