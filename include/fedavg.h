@@ -193,9 +193,11 @@ int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc,
  *             stream) or device memory (read in place).  Pageable host memory
  *             is rejected with FA_ERR_ARG.
  * offset,len  without mask/indices: the chunk holds parameters
- *             [offset, offset+len).  Dense mode: each client's chunks must
- *             arrive in ascending order and tile [0,N) exactly.  Partial
- *             mode: a client's ranges must be ascending and non-overlapping.
+ *             [offset, offset+len); a range reaching past N (tested without
+ *             forming offset+len, so huge values cannot wrap) is
+ *             FA_ERR_RANGE.  Dense mode: each client's chunks must arrive in
+ *             ascending order and tile [0,N) exactly.  Partial mode: a
+ *             client's ranges must be ascending and non-overlapping.
  * mask        partial mode only, nullable: len bytes, nonzero = sent.
  * indices     partial mode only, nullable: len strictly increasing int64
  *             indices relative to offset (parameter offset+indices[j] gets
