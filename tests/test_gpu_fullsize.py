@@ -254,6 +254,15 @@ def test_two_level_8b_three_silos_sampled():
     ref, mag, _, _ = oracle.weighted_average(xs, np.array(W, np.int64), mode=oracle.DELTAS, base=base_at,
                                              x_dtype=oracle.BF16, base_dtype=oracle.BF16)
     check(got, ref, mag, "bf16", label="two-level 8B sampled")
+    # the stated order, in numpy's IEEE float32: each partial one rounded
+    # product, the partials added in call order, one division, the base added
+    x32 = [(xb.astype(np.uint32) << 16).view(np.float32) for xb in xs]
+    acc32 = np.zeros(len(at), np.float32)
+    for k in range(3):
+        acc32 = (acc32 + (np.float32(W[k]) * x32[k]).astype(np.float32)).astype(np.float32)
+    q = (acc32 / np.float32(sum(W))).astype(np.float32)
+    r = ((base_at.astype(np.uint32) << 16).view(np.float32) + q).astype(np.float32)
+    same_bits(got, oracle.round_to_bf16(r))
 
 
 def test_topk_1b_client_update_properties():
