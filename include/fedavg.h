@@ -258,7 +258,10 @@ int fedavg_partial_info(fa_handle h, int64_t *W, int *n_clients);
  * W_i == 0 copy base_i.  base (device, N of base_dtype) is required in
  * FA_DELTAS and partial modes; out may alias base.  Dense mode returns
  * FA_ERR_INCOMPLETE if some client has not covered [0,N).  The accumulator is
- * left intact, so finalize may be repeated; no accumulate may follow.
+ * left intact, so finalize may be repeated; no accumulate may follow a
+ * successful finalize (FA_ERR_STATE).  A finalize refused by its checks
+ * (FA_ERR_ARG, FA_ERR_DTYPE, FA_ERR_INCOMPLETE, FA_ERR_ZERO_WEIGHT) leaves the
+ * handle as it was.
  */
 int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *out,
                     fa_dtype out_dtype);

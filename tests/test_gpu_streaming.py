@@ -367,3 +367,8 @@ def test_stream_state_errors():
             acc.finalize(base, out)
         assert e.value.code == -4
 
+        # a rejected finalize leaves the handle open: a client can still come
+        acc.accumulate(3, 2, x, offset=0)
+        acc.finalize(base, out)
+        acc.sync()
+    assert torch.equal(out, torch.ones(N, device="cuda"))

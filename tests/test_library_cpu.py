@@ -314,3 +314,28 @@ for call in (lambda: fa.load(build_if_missing=False),
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     lines = [l for l in r.stdout.splitlines() if l.startswith(("raised", "returned"))]
     assert lines == ["raised True"] * 3, r.stdout + r.stderr
+
+
+def test_binding_refuses_host_tensors_where_the_device_is_required():
+    """A host pointer handed to a kernel would fault the device: the binding
+    refuses CPU tensors for device-only arguments, and client lists whose
+    length differs from the weights, before any library call."""
+    x = torch.zeros(16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fedavg_aggregate([x, x], [1, 2], torch.zeros(16))
+    with pytest.raises(ValueError, match="entries for 2 clients"):
+        fa.fedavg_aggregate([x, x], [1], torch.zeros(16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.sparse_masked_accumulate([torch.zeros(2, dtype=torch.int64)], [torch.zeros(2)], [1], 16,
+                                    torch.zeros(16), torch.zeros(16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.topk_select(x, 4)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fedavg_checksum(x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fedavg_checksum_sum(x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fedavg_begin(16, "weights", False, torch.zeros(16), None, None,
+                        torch.zeros(4096, dtype=torch.uint8), 64, 2)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fedavg_finalize(None, None, torch.zeros(16))

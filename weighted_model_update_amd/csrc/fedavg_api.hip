@@ -885,13 +885,14 @@ int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *ou
                         (long long)c.second.covered, (long long)st.N);
     }
     const uint64_t S = st.total_weight();
+    // a rejected finalize leaves the handle open for more clients
+    if (st.N > 0 && !st.partial && S == 0 && st.mode == FA_WEIGHTS)
+        return fail(FA_ERR_ZERO_WEIGHT, "no client was accumulated in dense weights mode");
     st.finalized = true;
     if (st.N == 0)
         return ok();
     hipError_t e;
     if (!st.partial && S == 0) {
-        if (st.mode == FA_WEIGHTS)
-            return fail(FA_ERR_ZERO_WEIGHT, "no client was accumulated in dense weights mode");
         e = fa::launch_convert(base, base_dtype, out, out_dtype, st.N, st.compute);
         return e == hipSuccess ? ok() : hip_fail(e, "convert launch");
     }

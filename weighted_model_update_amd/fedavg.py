@@ -136,6 +136,13 @@ def _contig(t, name):
     return t
 
 
+def _on_gpu(t, name):
+    # device-only arguments: a host pointer would reach a kernel
+    if t is not None and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
 def _stream_handle(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -173,28 +180,31 @@ def fedavg_aggregate(xs, n, out, mode="weights", base=None, seg_bounds=None, pre
     K = len(xs)
     if K == 0:
         raise ValueError("need at least one client")
+    if len(n) != K:
+        raise ValueError(f"n has {len(n)} entries for {K} clients")
     N = out.numel()
     xdt = None
     for k, x in enumerate(xs):
         if x is None:
             continue
         _contig(x, f"xs[{k}]")
+        _on_gpu(x, f"xs[{k}]")
         if x.numel() != N:
             raise ValueError(f"xs[{k}] has {x.numel()} elements, out has {N}")
         d = _dtype(x)
         if xdt is not None and d != xdt:
             raise TypeError("all clients must share one dtype")
         xdt = d
-    _contig(out, "out")
-    _contig(base, "base")
+    _on_gpu(_contig(out, "out"), "out")
+    _on_gpu(_contig(base, "base"), "base")
     if base is not None and base.numel() != N:
         raise ValueError("base must have as many elements as out")
     T = 0
     if seg_bounds is not None or present is not None:
         if seg_bounds is None or present is None:
             raise ValueError("seg_bounds and present go together")
-        _contig(seg_bounds, "seg_bounds")
-        _contig(present, "present")
+        _on_gpu(_contig(seg_bounds, "seg_bounds"), "seg_bounds")
+        _on_gpu(_contig(present, "present"), "present")
         if seg_bounds.dtype != torch.int64 or present.dtype != torch.uint8:
             raise TypeError("seg_bounds must be int64 and present uint8")
         T = seg_bounds.numel() - 1
@@ -220,6 +230,8 @@ def fedavg_workspace_size(N, partial, chunk_bytes, n_slots):
 def fedavg_begin(N, mode, partial, acc, wsum, count, staging, chunk_bytes, n_slots,
                  compute_stream=None, copy_stream=None):
     """Returns an opaque handle (ctypes pointer)."""
+    for t, name in ((acc, "acc"), (wsum, "wsum"), (count, "count"), (staging, "staging")):
+        _on_gpu(t, name)
     h = ctypes.c_void_p(0)
     rc = load().fedavg_begin(ctypes.byref(h), int(N), _mode(mode), int(bool(partial)), _ptr(acc),
                              _ptr(wsum), _ptr(count), _ptr(staging),
@@ -255,8 +267,8 @@ def fedavg_accumulate_partial(h, client_id, W, n_clients, acc_src, wsum_src=None
     if acc_src.dtype != torch.float32:
         raise TypeError("acc_src must be float32")
     n = acc_src.numel()
-    if wsum_src is not None and (wsum_src.numel() != n or wsum_src.element_size() != 4):
-        raise ValueError("wsum_src must hold one 32-bit weight sum per element of acc_src")
+    if wsum_src is not None and (wsum_src.numel() != n or wsum_src.dtype != torch.int32):
+        raise ValueError("wsum_src must be int32 (holding uint32) with one entry per element of acc_src")
     if count_src is not None and (count_src.numel() != n or count_src.dtype != torch.uint8):
         raise ValueError("count_src must hold one uint8 count per element of acc_src")
     rc = load().fedavg_accumulate_partial(h, int(client_id), int(W), int(n_clients), _ptr(acc_src),
@@ -286,6 +298,8 @@ def fedavg_resume(state, N, mode, partial, acc, wsum, count, staging, chunk_byte
                   compute_stream=None, copy_stream=None):
     """Open a handle over restored acc/wsum/count tensors and an exported
     record (bytes).  Returns the handle."""
+    for t, name in ((acc, "acc"), (wsum, "wsum"), (count, "count"), (staging, "staging")):
+        _on_gpu(t, name)
     h = ctypes.c_void_p(0)
     rc = load().fedavg_resume(ctypes.byref(h), state, len(state), int(N), _mode(mode),
                               int(bool(partial)), _ptr(acc), _ptr(wsum), _ptr(count),
@@ -297,8 +311,8 @@ def fedavg_resume(state, N, mode, partial, acc, wsum, count, staging, chunk_byte
 
 
 def fedavg_finalize(h, base, out):
-    _contig(base, "base")
-    _contig(out, "out")
+    _on_gpu(_contig(base, "base"), "base")
+    _on_gpu(_contig(out, "out"), "out")
     rc = load().fedavg_finalize(h, _ptr(base), _dtype(base) if base is not None else FA_F32,
                                 _ptr(out), _dtype(out))
     _check(rc)
@@ -472,28 +486,32 @@ def sparse_masked_accumulate(idx, val, n, N, base, out, mode="deltas", counts=No
     if len(val) != K or len(n) != K:
         raise ValueError("idx, val and n must have one entry per client")
     for k in range(K):
-        _contig(idx[k], f"idx[{k}]")
-        _contig(val[k], f"val[{k}]")
+        _on_gpu(_contig(idx[k], f"idx[{k}]"), f"idx[{k}]")
+        _on_gpu(_contig(val[k], f"val[{k}]"), f"val[{k}]")
         if idx[k].dtype != torch.int64 or val[k].dtype != torch.float32:
             raise TypeError("indices must be int64 and values float32")
         if idx[k].numel() != val[k].numel():
             raise ValueError(f"idx[{k}] and val[{k}] differ in length")
     for t, name in ((base, "base"), (out, "out")):
-        _contig(t, name)
+        _on_gpu(_contig(t, name), name)
         if t.dtype != torch.float32 or t.numel() != N:
             raise ValueError(f"{name} must be float32 with N elements")
     cdt = FA_COUNT_U8
     if counts is not None:
-        _contig(counts, "counts")
+        _on_gpu(_contig(counts, "counts"), "counts")
         if counts.numel() != N or counts.dtype not in (torch.uint8, torch.int32):
             raise ValueError("counts must be uint8 or int32 with N elements")
         cdt = FA_COUNT_U8 if counts.dtype == torch.uint8 else FA_COUNT_U32
     if wsum is not None:
-        _contig(wsum, "wsum")
+        _on_gpu(_contig(wsum, "wsum"), "wsum")
         if wsum.numel() != N or wsum.dtype != torch.int32:
             raise ValueError("wsum must be int32 (holding uint32) with N elements")
+    if err_flag is not None and (err_flag.numel() < 1 or err_flag.dtype != torch.int32):
+        raise ValueError("err_flag must be an int32 tensor of at least one element")
+    _on_gpu(err_flag, "err_flag")
     if workspace is None:
         workspace = torch.empty(sparse_workspace_size(K, N), dtype=torch.uint8, device=out.device)
+    _on_gpu(workspace, "workspace")
     rc = lib.sparse_masked_accumulate(K, _ptr_array(idx), _ptr_array(val),
                                       _i64_array([t.numel() for t in idx]), _i64_array(n), int(N),
                                       _mode(mode), _ptr(base), _ptr(out), _ptr(counts), cdt,
@@ -574,11 +592,15 @@ def fedavg_checksum(t, stream=None, hash_out=None):
     """Order-independent 64-bit checksum of a contiguous float32/bfloat16 GPU
     tensor.  Returns the value as a Python int (synchronizes the stream)
     unless hash_out (an int64 tensor of one element) is given."""
-    _contig(t, "tensor")
+    lib = load()
+    _on_gpu(_contig(t, "tensor"), "tensor")
+    if hash_out is not None and (hash_out.numel() < 1 or hash_out.element_size() != 8):
+        raise ValueError("hash_out must be a 64-bit tensor of at least one element")
+    _on_gpu(hash_out, "hash_out")
     own = hash_out is None
     if own:
         hash_out = torch.empty(1, dtype=torch.int64, device=t.device)
-    _check(load().fedavg_checksum(_ptr(t), t.numel(), _dtype(t), _ptr(hash_out),
+    _check(lib.fedavg_checksum(_ptr(t), t.numel(), _dtype(t), _ptr(hash_out),
                                   _stream_handle(stream)))
     if own:
         return int(hash_out.item()) & 0xFFFFFFFFFFFFFFFF
@@ -599,16 +621,22 @@ def fedavg_checksum_sum(t, stream=None, workspace=None, hash_out=None, sum_out=N
     unless sum_out (a float64 tensor of one element) is given; then the
     results stay on the device (hash_out: an int64 tensor of one element, or
     None for no hash)."""
-    _contig(t, "tensor")
+    lib = load()
+    _on_gpu(_contig(t, "tensor"), "tensor")
     if workspace is None:
         workspace = torch.empty(max(fedavg_sum_workspace_size(t.numel()), 8), dtype=torch.uint8,
                                 device=t.device)
+    for o, name in ((hash_out, "hash_out"), (sum_out, "sum_out")):
+        if o is not None and (o.numel() < 1 or o.element_size() != 8):
+            raise ValueError(f"{name} must be a 64-bit tensor of at least one element")
+        _on_gpu(o, name)
+    _on_gpu(workspace, "workspace")
     own = sum_out is None
     if own:
         sum_out = torch.empty(1, dtype=torch.float64, device=t.device)
         if with_hash:
             hash_out = torch.empty(1, dtype=torch.int64, device=t.device)
-    _check(load().fedavg_checksum_sum(_ptr(t), t.numel(), _dtype(t), _ptr(hash_out), _ptr(sum_out),
+    _check(lib.fedavg_checksum_sum(_ptr(t), t.numel(), _dtype(t), _ptr(hash_out), _ptr(sum_out),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream_handle(stream)))
     if own:
@@ -629,7 +657,8 @@ def topk_workspace_size(N, k, dtype=torch.float32):
 def topk_select(x, k, idx_out=None, val_out=None, workspace=None, stream=None):
     """The k entries of largest magnitude of the 1-D update x (ties to the
     lower index), as (int64 indices in increasing order, float32 values)."""
-    _contig(x, "x")
+    lib = load()
+    _on_gpu(_contig(x, "x"), "x")
     N = x.numel()
     k = int(k)
     dev = x.device
@@ -640,9 +669,12 @@ def topk_select(x, k, idx_out=None, val_out=None, workspace=None, stream=None):
     if idx_out.numel() < k or val_out.numel() < k or idx_out.dtype != torch.int64 \
             or val_out.dtype != torch.float32:
         raise ValueError("idx_out must be int64 and val_out float32, each with room for k entries")
+    _on_gpu(_contig(idx_out, "idx_out"), "idx_out")
+    _on_gpu(_contig(val_out, "val_out"), "val_out")
     if workspace is None:
         workspace = torch.empty(max(topk_workspace_size(N, k, x.dtype), 1), dtype=torch.uint8, device=dev)
-    rc = load().topk_select(_ptr(x), _dtype(x), N, k, _ptr(idx_out), _ptr(val_out), _ptr(workspace),
+    _on_gpu(workspace, "workspace")
+    rc = lib.topk_select(_ptr(x), _dtype(x), N, k, _ptr(idx_out), _ptr(val_out), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(rc)
     return idx_out[:k], val_out[:k]
