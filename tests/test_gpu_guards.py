@@ -78,3 +78,25 @@ def test_streaming_finalize_writes_only_out(shift):
     assert intact(wo, N, shift, 1234.5)
     ref, mag, _, _ = oracle.weighted_average(xs, n, mode=oracle.DELTAS, base=base)
     check(host_of(out), ref, mag, "f32")
+
+
+@pytest.mark.parametrize("N", [1001, 1002, 1003, 1004])
+def test_begin_clears_exactly_the_buffers_it_is_given(N):
+    """fedavg_begin zeroes N accumulator words, N weight sums and N count
+    bytes, and nothing past them (N not a multiple of 4 leaves a count tail
+    shorter than a word)."""
+    acc_b, wsum_b, count_b, stag_b = fa.fedavg_workspace_size(N, True, 4096, 2)
+    assert (acc_b, wsum_b, count_b) == (4 * N, 4 * N, N)
+    wa, acc = guarded(N, torch.float32, 0, -2.5)
+    ww, ws = guarded(N, torch.int32, 0, -77)
+    wc, cnt = guarded(N, torch.uint8, 0, 201)
+    staging = torch.empty(stag_b, dtype=torch.uint8, device="cuda")
+    h = fa.fedavg_begin(N, "weights", True, acc, ws, cnt, staging, 4096, 2)
+    try:
+        fa.fedavg_sync(h)
+    finally:
+        fa.fedavg_destroy(h)
+    torch.cuda.synchronize()
+    assert intact(wa, N, 0, -2.5) and intact(ww, N, 0, -77) and intact(wc, N, 0, 201)
+    assert int(torch.count_nonzero(acc)) == 0 and int(torch.count_nonzero(ws)) == 0
+    assert int(torch.count_nonzero(cnt)) == 0

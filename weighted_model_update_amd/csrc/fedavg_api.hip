@@ -512,7 +512,7 @@ int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc,
     if (e == hipSuccess && st->partial)
         e = fa::launch_fill_u32(st->wsum, N, 0u, st->compute);
     if (e == hipSuccess && st->count)
-        e = fa::launch_fill_u32(st->count, (N + 3) / 4, 0u, st->compute);
+        e = fa::launch_fill_bytes(st->count, N, 0, st->compute);
     if (e != hipSuccess) {
         fedavg_destroy(st);
         *h = nullptr;

@@ -136,6 +136,8 @@ constexpr int SUM_FINISH_THREADS = 1024;
 hipError_t launch_checksum_sum(const void *buf, int64_t count, int dt, uint64_t *hash, double *sum,
                                double *part, int64_t cap, hipStream_t s);
 hipError_t launch_fill_u32(void *p, int64_t words, uint32_t value, hipStream_t s);
+// p must be 4-byte aligned; writes exactly `bytes` bytes.
+hipError_t launch_fill_bytes(void *p, int64_t bytes, uint8_t value, hipStream_t s);
 hipError_t launch_convert(const void *src, int sdt, void *dst, int ddt, int64_t N, hipStream_t s);
 
 } // namespace fa

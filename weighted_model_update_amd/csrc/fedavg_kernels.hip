@@ -1341,6 +1341,12 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t word
         p[i] = value;
 }
 
+__global__ __launch_bounds__(64) void fill_u8_kernel(uint8_t *p, int64_t bytes, uint8_t value)
+{
+    for (int64_t i = global_tid(); i < bytes; i += grid_threads())
+        p[i] = value;
+}
+
 // Element copy with type conversion (round-to-nearest-even when narrowing):
 // the result when no client contributed at all.
 template <int SDT, int DDT>
@@ -1733,6 +1739,22 @@ hipError_t launch_fill_u32(void *p, int64_t words, uint32_t value, hipStream_t s
         return hipSuccess;
     fill_u32_kernel<<<grid_for(words, 256, 8192), 256, 0, s>>>(static_cast<uint32_t *>(p), words, value);
     return hipGetLastError();
+}
+
+hipError_t launch_fill_bytes(void *p, int64_t bytes, uint8_t value, hipStream_t s)
+{
+    // whole words from a 4-byte aligned start, then the last 0-3 bytes alone,
+    // so nothing past p[bytes-1] is written
+    if (bytes <= 0)
+        return hipSuccess;
+    const uint32_t v4 = value * 0x01010101u;
+    hipError_t e = launch_fill_u32(p, bytes / 4, v4, s);
+    if (e == hipSuccess && (bytes & 3) != 0) {
+        fill_u8_kernel<<<1, 64, 0, s>>>(static_cast<uint8_t *>(p) + (bytes & ~int64_t(3)), bytes & 3,
+                                        value);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 hipError_t launch_convert(const void *src, int sdt, void *dst, int ddt, int64_t N, hipStream_t s)
