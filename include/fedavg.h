@@ -122,7 +122,8 @@ const char *fedavg_last_error(void);
  *          (client models in FA_WEIGHTS mode, client deltas in FA_DELTAS).
  * n        host array of K sample counts.  n_k == 0: client k is skipped and
  *          x[k] is never read (it may be NULL).
- * N        parameters per client (N == 0 is a no-op).
+ * N        parameters per client (N == 0 is a no-op; every pointer may then
+ *          be NULL).
  * base     device, N elements of base_dtype.  Required in FA_DELTAS mode and
  *          whenever T > 0; unused in dense FA_WEIGHTS mode (may be NULL).
  * out      device, N elements of out_dtype.
@@ -256,7 +257,7 @@ int fedavg_partial_info(fa_handle h, int64_t *W, int *n_clients);
  * fedavg_finalize -- out_i = base_i + acc_i / W_i (FA_DELTAS) or acc_i / W_i
  * (FA_WEIGHTS), W_i = sum of n_k (dense) or wsum_i (partial); parameters with
  * W_i == 0 copy base_i.  base (device, N of base_dtype) is required in
- * FA_DELTAS and partial modes; out may alias base.  Dense mode returns
+ * FA_DELTAS and partial modes when N > 0; out may alias base.  Dense mode returns
  * FA_ERR_INCOMPLETE if some client has not covered [0,N).  The accumulator is
  * left intact, so finalize may be repeated; no accumulate may follow a
  * successful finalize (FA_ERR_STATE).  A finalize refused by its checks

@@ -328,12 +328,13 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
         return fail(FA_ERR_ARG, "unknown mode %d", (int)mode);
     if (T < 0)
         return fail(FA_ERR_ARG, "T=%d is negative", T);
-    if (mode != FA_WEIGHTS && !base)
+    // an empty model is a no-op: its (empty) buffers may be NULL
+    if (N > 0 && mode != FA_WEIGHTS && !base)
         return fail(FA_ERR_ARG, "delta modes need base");
     // kernels see weights or deltas; zero fill only changes the divisor of
     // the masked path (with every client sending everything, W_i = S)
     const int kmode = mode == FA_WEIGHTS ? FA_WEIGHTS : FA_DELTAS;
-    if (T > 0 && (!base || !seg_bounds || !present))
+    if (N > 0 && T > 0 && (!base || !seg_bounds || !present))
         return fail(FA_ERR_ARG, "segment masks need base, seg_bounds and present");
     if (N > 0 && !out)
         return fail(FA_ERR_ARG, "out must not be NULL");
@@ -874,7 +875,7 @@ int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *ou
         return fail(FA_ERR_DTYPE, "dtypes must be FA_F32 or FA_BF16");
     if (st.N > 0 && !out)
         return fail(FA_ERR_ARG, "out must not be NULL");
-    if ((st.mode != FA_WEIGHTS || st.partial) && !base)
+    if (st.N > 0 && (st.mode != FA_WEIGHTS || st.partial) && !base)
         return fail(FA_ERR_ARG, "base is required in delta and partial modes");
     if (base && !overlap_ok(out, (size_t)st.N * dsize(out_dtype), base,
                             (size_t)st.N * dsize(base_dtype)))
