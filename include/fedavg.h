@@ -53,6 +53,9 @@
  *     Only the streaming handle (host memory and its HIP events, plus one
  *     internal copy stream when the caller passes none) belongs to the
  *     library; fedavg_destroy releases it.
+ *   - Threads: the resident calls may run on several threads at once, each
+ *     on its own buffers.  A streaming handle is used by one thread at a
+ *     time (its calls update host-side coverage and staging slots).
  *   - Limits: K <= FA_MAX_CLIENTS resident clients per call;
  *     0 <= n_k <= FA_MAX_WEIGHT (so fp32(n_k) is exact); sums of weights
  *     below 2^32; at most FA_MAX_N parameters per buffer and chunk_bytes at
