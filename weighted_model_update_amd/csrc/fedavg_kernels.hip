@@ -15,6 +15,8 @@
 // introduction and server-side workflow) with fp32 master-weight
 // accumulation and nearest-even rounding of weights ("NVFP4 training with JAX
 // and MaxText", training-recipe section).
+#include <atomic>
+
 #include "fedavg_internal.h"
 
 namespace fa {
@@ -1362,19 +1364,20 @@ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 static int lds_bytes_per_cu()
 {
-    static int cache[64] = {0};
+    // per device, filled on first use; threads that race store the same value
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 0;
-    if (cache[dev] == 0) {
-        int v = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
                 hipSuccess ||
             v <= 0)
             v = 65536;
-        cache[dev] = v;
+        cache[dev].store(v, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return v;
 }
 
 // Streaming kernels over HBM run fastest with few resident waves per CU (a
@@ -1391,14 +1394,18 @@ static size_t residency_lds(F *kernel, int cap)
     if (lds <= 0)
         return 0;
     const size_t bytes = ((size_t)lds / cap + (size_t)lds / (cap + 1)) / 2;
-    static int configured_max = 0; // one per kernel instantiation
-    if ((int)bytes > configured_max) {
+    // the largest request allowed so far, per kernel instantiation and device
+    static std::atomic<int> configured_max[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    if ((int)bytes > configured_max[dev].load(std::memory_order_relaxed)) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess) {
             (void)hipGetLastError();
             return 0;
         }
-        configured_max = (int)bytes;
+        configured_max[dev].store((int)bytes, std::memory_order_relaxed);
     }
     return bytes;
 }
