@@ -88,6 +88,14 @@ def timed(fn, steps, warmup):
     return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
+def stats(durs):
+    """mean, median and min of per-launch durations (ms)."""
+    d = sorted(durs)
+    m = len(d)
+    med = d[m // 2] if m % 2 else 0.5 * (d[m // 2 - 1] + d[m // 2])
+    return {"mean_ms": sum(d) / m, "median_ms": med, "min_ms": d[0]}
+
+
 def free_gpu():
     import gc
     import torch
@@ -524,6 +532,120 @@ def bench_copy_calibration(gib=4):
 
 
 # --------------------------------------------------------------------------
+# HBM ceilings of the dense pattern
+# --------------------------------------------------------------------------
+
+# Pol codes of the ceiling kernels (csrc/hbm_ceiling.hip)
+P_GLOBAL, P_GLOBAL_NT, P_BUF, P_BUF_NT, P_BUF_SC1, P_BUF_SC0SC1, P_BUF_SC1NT, P_BUF_SC0SC1NT = range(8)
+POL_NAMES = ["global", "global nt", "buffer", "buffer nt", "buffer sc1", "buffer sc0 sc1",
+             "buffer sc1 nt", "buffer sc0 sc1 nt"]
+# (name, pattern 0 read / 1 read+write, streams read, load policy, store policy, vectors per thread)
+CEILING_CASES = [
+    ("read16 nt", 0, 16, P_GLOBAL_NT, P_GLOBAL, 1),
+    ("read16", 0, 16, P_GLOBAL, P_GLOBAL, 1),
+    ("read17 nt", 0, 17, P_GLOBAL_NT, P_GLOBAL, 1),
+    ("read17", 0, 17, P_GLOBAL, P_GLOBAL, 1),
+    ("copy nt/nt", 1, 1, P_GLOBAL_NT, P_GLOBAL_NT, 1),
+    ("copy plain/plain", 1, 1, P_GLOBAL, P_GLOBAL, 1),
+    ("copy nt/plain", 1, 1, P_GLOBAL_NT, P_GLOBAL, 1),
+    ("copy nt/nt vpt4", 1, 1, P_GLOBAL_NT, P_GLOBAL_NT, 4),
+    ("mix16 nt/nt", 1, 16, P_GLOBAL_NT, P_GLOBAL_NT, 1),
+    ("mix16 plain/nt", 1, 16, P_GLOBAL, P_GLOBAL_NT, 1),
+    ("mix16 buf/nt", 1, 16, P_BUF, P_GLOBAL_NT, 1),
+    ("mix16 buf nt/nt", 1, 16, P_BUF_NT, P_GLOBAL_NT, 1),
+    ("mix16 buf sc1/nt", 1, 16, P_BUF_SC1, P_GLOBAL_NT, 1),
+    ("mix16 buf sc0sc1/nt", 1, 16, P_BUF_SC0SC1, P_GLOBAL_NT, 1),
+    ("mix16 buf sc1nt/nt", 1, 16, P_BUF_SC1NT, P_GLOBAL_NT, 1),
+    ("mix16 nt/plain", 1, 16, P_GLOBAL_NT, P_GLOBAL, 1),
+    ("mix16 nt/buf", 1, 16, P_GLOBAL_NT, P_BUF, 1),
+    ("mix16 nt/buf nt", 1, 16, P_GLOBAL_NT, P_BUF_NT, 1),
+    ("mix16 nt/buf sc1", 1, 16, P_GLOBAL_NT, P_BUF_SC1, 1),
+    ("mix16 nt/buf sc0sc1", 1, 16, P_GLOBAL_NT, P_BUF_SC0SC1, 1),
+    ("mix16 nt/buf sc1nt", 1, 16, P_GLOBAL_NT, P_BUF_SC1NT, 1),
+    ("mix16 nt/buf sc0sc1nt", 1, 16, P_GLOBAL_NT, P_BUF_SC0SC1NT, 1),
+    ("mix16 nt/nt vpt2", 1, 16, P_GLOBAL_NT, P_GLOBAL_NT, 2),
+    ("mix16 nt/nt vpt4", 1, 16, P_GLOBAL_NT, P_GLOBAL_NT, 4),
+    ("mix16 nt/plain vpt2", 1, 16, P_GLOBAL_NT, P_GLOBAL, 2),
+    ("mix16 nt/plain vpt4", 1, 16, P_GLOBAL_NT, P_GLOBAL, 4),
+]
+
+
+def bench_ceiling(reps=10, warmup=2, residents=(3, 0, 2, 4)):
+    """What HBM gives the headline's byte pattern on this part, measured in
+    the same run as the headline kernel: kernels that move the dense
+    aggregation's bytes (16 bf16 client streams of 1,921,878,016 parameters
+    read, one written) with no arithmetic, over load and store cache
+    policies, write batching and residency caps; the 16- and 17-stream reads
+    alone and a plain copy bound it from both sides.  The dense kernel itself
+    is timed on the same buffers at each residency cap."""
+    import ctypes
+    import torch
+    import synth
+    import weighted_model_update_amd as fa
+    from weighted_model_update_amd import build as nb
+    lib = ctypes.CDLL(nb.CEILING_PATH)
+    lib.hc_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                              ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_int64, ctypes.c_void_p]
+    lib.hc_stream.restype = ctypes.c_int
+    N = synth.numel_of(synth.dense_2b_tensor_shapes())
+    nvec = N * 2 // 16
+    log(f"ceiling: 17 streams of {nvec * 16} bytes")
+    bufs = [torch.empty(nvec * 16, dtype=torch.uint8, device="cuda") for _ in range(17)]
+    for i, b in enumerate(bufs):
+        b.view(torch.int32).fill_(0x3c003c00 + i)        # bf16 values near 1, distinct per stream
+    srcs = (ctypes.c_void_p * 17)(*[b.data_ptr() for b in bufs])
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rows = []
+
+    def record(name, pattern, ns, lp, sp, vpt, res, fn, nbytes):
+        _, d = timed(fn, reps, warmup)
+        st = stats(d)
+        rows.append({"name": name, "streams_read": ns, "stream_written": pattern == 1,
+                     "load": POL_NAMES[lp] if lp is not None else "kernel",
+                     "store": POL_NAMES[sp] if sp is not None else "kernel",
+                     "vectors_per_thread": vpt, "resident_per_cu": res, "bytes": nbytes, **st,
+                     "gbs_median": nbytes / (st["median_ms"] * 1e-3) / 1e9,
+                     "frac_median": nbytes / (st["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "frac_min_time": nbytes / (st["min_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS})
+
+    for res in residents:
+        for name, pattern, ns, lp, sp, vpt in CEILING_CASES:
+            if res != residents[0] and not name.startswith(("mix16 nt/nt", "read16 nt", "copy nt/nt")):
+                continue        # the policy sweep runs at the default cap only
+            dst = bufs[16].data_ptr() if ns < 17 else bufs[0].data_ptr()
+            nb_ = (ns + (1 if pattern == 1 else 0)) * nvec * 16
+
+            def fn(i, pattern=pattern, ns=ns, lp=lp, sp=sp, vpt=vpt, res=res, dst=dst):
+                rc = lib.hc_stream(pattern, ns, srcs, ctypes.c_void_p(dst), nvec, lp, sp, vpt, res, 0,
+                                   stream)
+                if rc != 0:
+                    raise RuntimeError(f"hc_stream failed: {rc}")
+            record(name, pattern, ns, lp, sp, vpt, res, fn, nb_)
+        # the dense aggregation kernel itself on the same buffers
+        xs = [b.view(torch.bfloat16) for b in bufs[:16]]
+        out = bufs[16].view(torch.bfloat16)
+        n = [int(v) for v in synth.sample_counts(synth.CFG_DENSE_2B, 16, 100, 1000)]
+        fa.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, res)
+        try:
+            record("dense kernel K=16 bf16", 1, 16, None, None, 1, res,
+                   lambda i: fa.fedavg_aggregate(xs, n, out), 17 * 2 * N)
+        finally:
+            fa.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, 3)
+        log(f"ceiling: resident {res} done")
+    del bufs
+    free_gpu()
+    mixed = [r for r in rows if r["streams_read"] == 16 and r["stream_written"] and r["load"] != "kernel"]
+    best = min(mixed, key=lambda r: r["median_ms"])
+    dense_default = [r for r in rows if r["load"] == "kernel" and r["resident_per_cu"] == residents[0]][0]
+    return {"N": N, "bytes_per_stream": nvec * 16, "rows": rows,
+            "best_mixed": {"name": best["name"], "resident_per_cu": best["resident_per_cu"],
+                           "median_ms": best["median_ms"], "frac_median": best["frac_median"]},
+            "dense_median_ms": dense_default["median_ms"],
+            "dense_over_best_mixed": dense_default["median_ms"] / best["median_ms"]}
+
+
+# --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
 
@@ -573,7 +695,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
                     help="comma list of: dense,dense_small,adapter,streaming,windows,sparse,topk,"
-                         "hierarchical,sparse_stream,checksum,cpu,copycal "
+                         "hierarchical,sparse_stream,checksum,ceiling,cpu,copycal "
                          "(default all but copycal)")
     ap.add_argument("--stream-clients", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -592,7 +714,7 @@ def main():
     only = set(args.only.split(",")) if args.only != "all" else {"dense", "dense_small", "adapter",
                                                                  "streaming", "windows", "sparse", "topk",
                                                                  "hierarchical", "sparse_stream",
-                                                                 "checksum", "cpu"}
+                                                                 "checksum", "ceiling", "cpu"}
     if args.no_cpu_baseline:
         only.discard("cpu")
 
@@ -632,6 +754,11 @@ def main():
         log(f"checksum: {modes['checksum']['ms_per_call']:.3f} ms/call, with the value sum "
             f"{modes['checksum']['hash_and_sum_ms_per_call']:.3f}, sum alone "
             f"{modes['checksum']['sum_ms_per_call']:.3f}")
+    if "ceiling" in only:
+        modes["ceiling"] = bench_ceiling()
+        c = modes["ceiling"]
+        log(f"ceiling: best mixed pattern {c['best_mixed']['name']} at {c['best_mixed']['median_ms']:.3f} ms; "
+            f"dense kernel {c['dense_median_ms']:.3f} ms ({c['dense_over_best_mixed']:.3f}x)")
     if "copycal" in only:
         modes["copy_calibration"] = bench_copy_calibration()
     cpu = cpu_baseline() if "cpu" in only else None

@@ -209,8 +209,13 @@ int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc,
  *             by fedavg_sync as FA_ERR_INDEX; the bad entries are skipped.
  *             The caller must not send one parameter twice for a client.
  *             mask and indices live where chunk lives.
- * A host buffer passed here may be reused once n_slots further accumulate
- * calls have returned on this handle, or after fedavg_sync.
+ * An empty chunk (len == 0) enters the client but carries no parameter, so
+ * the ordering and tiling rules above do not apply to it.
+ * A host buffer passed here may be reused once n_slots further calls of
+ * fedavg_accumulate or fedavg_accumulate_partial on this handle have
+ * returned -- calls of every kind count: device or empty chunks, n_k == 0,
+ * refused calls -- or after fedavg_sync.  (Each call waits, if need be, for
+ * the host-to-device copy of the call n_slots before it.)
  */
 int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk, fa_dtype dtype,
                       int64_t offset, int64_t len, const uint8_t *mask, const int64_t *indices);
@@ -337,7 +342,8 @@ int sparse_workspace_size(int K, int64_t N, size_t *bytes);
  * base, out  device fp32[N]; out may alias base.
  * counts     device, N of counts_dtype (nullable): per-parameter client count.
  * wsum       device uint32[N] (nullable): per-parameter weight sum W_i.
- * workspace  device, >= sparse_workspace_size bytes.
+ * workspace  device, >= sparse_workspace_size bytes (may be NULL when
+ *            N == 0).
  * err_flag   device int (nullable): set to 0 by this call, then to
  *            FA_ERR_INDEX if some list is unsorted, has duplicates or an
  *            index outside [0,N) (those entries are skipped).

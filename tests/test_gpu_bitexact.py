@@ -105,19 +105,35 @@ def _lists_as_dense(idx, val, N):
     return xs, sent
 
 
-@pytest.mark.parametrize("mode", ["weights", "deltas", "deltas_zero_fill"])
-@pytest.mark.parametrize("K", [6, 40])
-def test_sparse(mode, K):
+def _sparse_bits(mode, K, tile):
     N = 200_003
     idx, val = zip(*[synth.topk_sparse_deltas(11, k, N, 0.1, 1e-3) for k in range(K)])
     base = synth.normal_f32(11, synth.ROLE_BASE, 0, N, 0.02)
     n = synth.sample_counts(11, K, 100, 1000)
     out = torch.empty(N, device="cuda")
-    fa.sparse_masked_accumulate([torch.from_numpy(np.asarray(i, np.int64)).cuda() for i in idx],
-                                [dev_f32(v) for v in val], n.tolist(), N, dev_f32(base), out, mode=mode)
-    torch.cuda.synchronize()
+    fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, tile)
+    try:
+        fa.sparse_masked_accumulate([torch.from_numpy(np.asarray(i, np.int64)).cuda() for i in idx],
+                                    [dev_f32(v) for v in val], n.tolist(), N, dev_f32(base), out,
+                                    mode=mode)
+        torch.cuda.synchronize()
+    finally:
+        fa.fedavg_set_option(fa.FA_OPT_SPARSE_TILE, 2048)
     xs, sent = _lists_as_dense(idx, val, N)
     same_bits(host_of(out), oracle.mirror_f32(xs, n, mode=MODES[mode], base=base, sent=sent))
+
+
+@pytest.mark.parametrize("mode", ["weights", "deltas", "deltas_zero_fill"])
+@pytest.mark.parametrize("K", [6, 40])
+def test_sparse(mode, K):
+    _sparse_bits(mode, K, 2048)
+
+
+@pytest.mark.parametrize("tile", [512, 1024, 4096, 8192])
+def test_sparse_two_mask_words_every_tile(tile):
+    # K > 32 takes the kernels with two client-mask words; the 8192 tile is
+    # the largest LDS footprint (about 98 KB with 1024 threads)
+    _sparse_bits("deltas", 40, tile)
 
 
 @pytest.mark.parametrize("kind", ["dense", "masks", "indices"])

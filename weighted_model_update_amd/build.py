@@ -32,21 +32,33 @@ def hipcc():
     return path
 
 
-def build(verbose=False):
-    """Compile the library; always rebuilds.  Returns the path of the .so."""
-    fd, tmp = tempfile.mkstemp(prefix="libfedavg.", suffix=".so.tmp", dir=HERE)
+# Measurement kernels for the benchmark's HBM ceilings (byte patterns of the
+# aggregation kernels without their arithmetic); not part of the library.
+CEILING_PATH = os.path.join(HERE, "libhbm_ceiling.so")
+CEILING_SOURCES = [os.path.join(HERE, "csrc", "hbm_ceiling.hip")]
+
+
+def _compile(sources, path, verbose):
+    fd, tmp = tempfile.mkstemp(prefix=os.path.basename(path) + ".", suffix=".so.tmp", dir=HERE)
     os.close(fd)
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + SOURCES
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + sources
     if verbose:
         print(" ".join(cmd), flush=True)
     try:
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-        os.replace(tmp, LIB_PATH)
+        os.replace(tmp, path)
     finally:
         if os.path.exists(tmp):
             os.remove(tmp)
+
+
+def build(verbose=False):
+    """Compile the library and the benchmark's ceiling kernels; always
+    rebuilds.  Returns the path of the library."""
+    _compile(SOURCES, LIB_PATH, verbose)
+    _compile(CEILING_SOURCES, CEILING_PATH, verbose)
     return LIB_PATH
 
 

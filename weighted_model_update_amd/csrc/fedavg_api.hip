@@ -178,9 +178,14 @@ struct fa_stream_state {
     hipStream_t compute = nullptr;
     hipStream_t copy = nullptr;
     bool own_copy = false;
+    // copy_done[j]: the host-to-device copy of the call whose number is j
+    // modulo n_slots (recorded only when that call staged); slot_free[s]: the
+    // last kernel that read staging slot s
     std::vector<hipEvent_t> copy_done, slot_free;
-    std::vector<bool> slot_used;
-    int64_t calls = 0;
+    std::vector<bool> copy_pending, slot_used;
+    int64_t calls = 0;  // accumulate calls of any kind on this handle
+    int64_t staged = 0; // calls that staged host memory (slot round robin)
+    int ring = 0;       // copy_done entry of the current call
     bool finalized = false;
     std::unordered_map<int, Client> clients;
     int *err_flag() { return reinterpret_cast<int *>(staging); }
@@ -224,27 +229,42 @@ struct fa_stream_state {
         cl.covered = offset + len;
         return FA_OK;
     }
+    // Opens an accumulate call.  A host buffer handed to call j may be reused
+    // once n_slots further calls have returned: call j + n_slots waits here
+    // for call j's copy, whatever kinds of calls came in between (device
+    // chunks, empty chunks, zero weights and refused calls count too).
+    // Returns FA_OK or the failure of the wait.
+    int open_call()
+    {
+        ring = (int)(calls % n_slots);
+        ++calls;
+        if (copy_pending[ring]) {
+            const hipError_t e = hipEventSynchronize(copy_done[ring]);
+            if (e != hipSuccess)
+                return hip_fail(e, "waiting for an earlier copy");
+            copy_pending[ring] = false;
+        }
+        return FA_OK;
+    }
     // Stages `parts` host arrays into the next slot (host buffers given as
     // (src, bytes, offset in slot)); returns the slot, or -1 after a failure
     // of a HIP call (recorded as FA_ERR_HIP).
     int stage(const void *const *src, const size_t *bytes, const size_t *at, int parts)
     {
-        const int sl = (int)(calls % n_slots);
+        const int sl = (int)(staged % n_slots);
         hipError_t e = hipSuccess;
-        if (slot_used[sl]) {
-            // the host buffer of the copy that last used this slot is free once
-            // that copy is done; the slot itself once its kernel is done
-            e = hipEventSynchronize(copy_done[sl]);
-            if (e == hipSuccess)
-                e = hipStreamWaitEvent(copy, slot_free[sl], 0);
-        }
+        // the slot is free once the kernel that last read it is done
+        if (slot_used[sl])
+            e = hipStreamWaitEvent(copy, slot_free[sl], 0);
         for (int i = 0; i < parts && e == hipSuccess; ++i)
             if (src[i] && bytes[i])
                 e = hipMemcpyAsync(slot(sl) + at[i], src[i], bytes[i], hipMemcpyHostToDevice, copy);
         if (e == hipSuccess)
-            e = hipEventRecord(copy_done[sl], copy);
+            e = hipEventRecord(copy_done[ring], copy);
         if (e == hipSuccess)
-            e = hipStreamWaitEvent(compute, copy_done[sl], 0);
+            copy_pending[ring] = true;
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(compute, copy_done[ring], 0);
         if (e != hipSuccess) {
             hip_fail(e, "staging copy");
             return -1;
@@ -258,7 +278,7 @@ struct fa_stream_state {
         if (e != hipSuccess)
             return hip_fail(e, "event record");
         slot_used[sl] = true;
-        ++calls;
+        ++staged;
         return FA_OK;
     }
     char *slot(int s) { return staging + HEADER_BYTES + (size_t)s * slot_size; }
@@ -485,6 +505,7 @@ static int open_handle(fa_handle *h, int64_t N, int mode, int partial, float *ac
     }
     st->copy_done.resize(n_slots);
     st->slot_free.resize(n_slots);
+    st->copy_pending.assign(n_slots, false);
     st->slot_used.assign(n_slots, false);
     for (int i = 0; i < n_slots && e == hipSuccess; ++i) {
         e = hipEventCreateWithFlags(&st->copy_done[i], hipEventDisableTiming);
@@ -640,6 +661,11 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
     if (!h)
         return fail(FA_ERR_ARG, "NULL handle");
     fa_stream_state &st = *h;
+    {
+        const int rc = st.open_call();
+        if (rc != FA_OK)
+            return rc;
+    }
     if (st.finalized)
         return fail(FA_ERR_STATE, "accumulate after finalize");
     if (client_id < 0)
@@ -675,14 +701,16 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
     }
     fa_stream_state::Client cl =
         it != st.clients.end() ? it->second : fa_stream_state::Client{n_k, 0, 1};
+    // an empty chunk carries no parameter: it enters the client (and counts
+    // as a call) but is outside the ordering and tiling rules
+    if (len == 0) {
+        st.clients[client_id] = cl;
+        return ok();
+    }
     if (!indices) {
         const int rc = st.cover(client_id, cl, offset, len);
         if (rc != FA_OK)
             return rc;
-    }
-    if (len == 0) {
-        st.clients[client_id] = cl;
-        return ok();
     }
 
     const size_t esize = dsize(dtype);
@@ -757,6 +785,11 @@ int fedavg_accumulate_partial(fa_handle h, int client_id, int64_t W, int n_clien
     if (!h)
         return fail(FA_ERR_ARG, "NULL handle");
     fa_stream_state &st = *h;
+    {
+        const int rc = st.open_call();
+        if (rc != FA_OK)
+            return rc;
+    }
     if (st.finalized)
         return fail(FA_ERR_STATE, "accumulate after finalize");
     if (client_id < 0)
@@ -787,14 +820,14 @@ int fedavg_accumulate_partial(fa_handle h, int client_id, int64_t W, int n_clien
     }
     fa_stream_state::Client cl =
         it != st.clients.end() ? it->second : fa_stream_state::Client{W, 0, n_clients};
+    if (len == 0) {
+        st.clients[client_id] = cl;
+        return ok();
+    }
     {
         const int rc = st.cover(client_id, cl, offset, len);
         if (rc != FA_OK)
             return rc;
-    }
-    if (len == 0) {
-        st.clients[client_id] = cl;
-        return ok();
     }
 
     const bool use_wsum = st.partial;
@@ -990,11 +1023,15 @@ int sparse_workspace_size(int K, int64_t N, size_t *bytes)
     return ok();
 }
 
-int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *const *val,
-                             const int64_t *nnz, const int64_t *n, int64_t N, fa_mode mode,
-                             const float *base, float *out, void *counts,
-                             fa_count_dtype counts_dtype, uint32_t *wsum, void *workspace,
-                             size_t workspace_bytes, int *err_flag, void *stream)
+} // extern "C"
+
+namespace {
+
+// Body of the sparse merge entry point.
+int sparse_run(int K, const int64_t *const *idx, const float *const *val, const int64_t *nnz,
+               const int64_t *n, int64_t N, fa_mode mode, const float *base, float *out,
+               void *counts, fa_count_dtype counts_dtype, uint32_t *wsum, void *workspace,
+               size_t workspace_bytes, int *err_flag, void *stream)
 {
     if (K < 1 || K > FA_MAX_CLIENTS)
         return fail(FA_ERR_RANGE, "K=%d outside [1, %d]", K, FA_MAX_CLIENTS);
@@ -1010,10 +1047,6 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
         return fail(FA_ERR_DTYPE, "counts dtype must be FA_COUNT_U8 or FA_COUNT_U32");
     if (N > 0 && (!base || !out))
         return fail(FA_ERR_ARG, "base and out are required");
-    size_t need = 0;
-    sparse_workspace_size(K, N, &need);
-    if (!workspace || workspace_bytes < need)
-        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     if (!overlap_ok(out, (size_t)N * 4, base, (size_t)N * 4))
         return fail(FA_ERR_ARG, "out partially overlaps base");
 
@@ -1040,23 +1073,36 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
     }
     if (S_all >= (1ull << 32))
         return fail(FA_ERR_RANGE, "sum of n_k must be below 2^32");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // an empty model has nothing to merge: only the caller's flag is reset,
+    // and no workspace is needed
+    if (N == 0) {
+        if (err_flag) {
+            const hipError_t e = fa::launch_fill_u32(err_flag, 1, 0u, s);
+            if (e != hipSuccess)
+                return hip_fail(e, "flag reset");
+        }
+        return ok();
+    }
     // plan the ranges and check the workspace before anything is enqueued:
     // the offsets kernel writes Kc * (NB + 1) list positions
     const int64_t tile = g_sparse_tile;
-    const int64_t NB = N > 0 ? sparse_blocks_for(N, tile) : 0;
+    const int64_t NB = sparse_blocks_for(N, tile);
     const int64_t tiles = (N + tile - 1) / tile;
-    const int64_t R = NB > 0 ? ((tiles + NB - 1) / NB) * tile : tile;
+    const int64_t R = ((tiles + NB - 1) / NB) * tile;
     const size_t used = HEADER_BYTES + (size_t)Kc * (size_t)(NB + 1) * sizeof(int64_t);
+    size_t need = 0;
+    sparse_workspace_size(K, N, &need);
+    if (!workspace || workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    need);
     if (used > workspace_bytes)
-        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %lld ranges need %zu", workspace_bytes,
-                    (long long)NB, used);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %lld ranges need %zu",
+                    workspace_bytes, (long long)NB, used);
     int *flag = err_flag ? err_flag : static_cast<int *>(workspace);
     hipError_t e = fa::launch_fill_u32(flag, 1, 0u, s);
     if (e != hipSuccess)
         return hip_fail(e, "flag reset");
-    if (N == 0)
-        return ok();
     a.K = Kc;
     a.NB = (int)NB;
     a.N = N;
@@ -1076,6 +1122,20 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
     a.err = flag;
     e = fa::launch_sparse(a, s);
     return e == hipSuccess ? ok() : hip_fail(e, "sparse launch");
+}
+
+} // namespace
+
+extern "C" {
+
+int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *const *val,
+                             const int64_t *nnz, const int64_t *n, int64_t N, fa_mode mode,
+                             const float *base, float *out, void *counts,
+                             fa_count_dtype counts_dtype, uint32_t *wsum, void *workspace,
+                             size_t workspace_bytes, int *err_flag, void *stream)
+{
+    return sparse_run(K, idx, val, nnz, n, N, mode, base, out, counts, counts_dtype, wsum, workspace,
+                      workspace_bytes, err_flag, stream);
 }
 
 // ============================================================ sample allocation

@@ -476,12 +476,8 @@ def sparse_workspace_size(K, N):
     return b.value
 
 
-def sparse_masked_accumulate(idx, val, n, N, base, out, mode="deltas", counts=None, wsum=None,
-                             workspace=None, err_flag=None, stream=None):
-    """One-pass merge of K sorted sparse client lists (see include/fedavg.h).
-    counts: uint8 or int32 tensor of N (nullable); wsum: int32 tensor of N
-    holding the uint32 weight sums (nullable); err_flag: int32 tensor of 1."""
-    lib = load()
+def _sparse_args(idx, val, n, N, base, out, counts, wsum, err_flag):
+    """Checks the sparse merge's tensors; returns the counts dtype code."""
     K = len(idx)
     if len(val) != K or len(n) != K:
         raise ValueError("idx, val and n must have one entry per client")
@@ -509,14 +505,25 @@ def sparse_masked_accumulate(idx, val, n, N, base, out, mode="deltas", counts=No
     if err_flag is not None and (err_flag.numel() < 1 or err_flag.dtype != torch.int32):
         raise ValueError("err_flag must be an int32 tensor of at least one element")
     _on_gpu(err_flag, "err_flag")
-    if workspace is None:
+    return cdt
+
+
+def sparse_masked_accumulate(idx, val, n, N, base, out, mode="deltas", counts=None, wsum=None,
+                             workspace=None, err_flag=None, stream=None):
+    """One-pass merge of K sorted sparse client lists (see include/fedavg.h).
+    counts: uint8 or int32 tensor of N (nullable); wsum: int32 tensor of N
+    holding the uint32 weight sums (nullable); err_flag: int32 tensor of 1."""
+    lib = load()
+    K = len(idx)
+    cdt = _sparse_args(idx, val, n, N, base, out, counts, wsum, err_flag)
+    if workspace is None and N > 0:      # an empty model needs none
         workspace = torch.empty(sparse_workspace_size(K, N), dtype=torch.uint8, device=out.device)
     _on_gpu(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.sparse_masked_accumulate(K, _ptr_array(idx), _ptr_array(val),
                                       _i64_array([t.numel() for t in idx]), _i64_array(n), int(N),
                                       _mode(mode), _ptr(base), _ptr(out), _ptr(counts), cdt,
-                                      _ptr(wsum), _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(), _ptr(err_flag),
+                                      _ptr(wsum), _ptr(workspace), ws_bytes, _ptr(err_flag),
                                       _stream_handle(stream))
     _check(rc)
     return workspace
@@ -537,8 +544,9 @@ def stream_windows(N, clients, base, out, window=None, mode="weights", partial=F
     (offset, values, mask), in ascending offset; values live on the device
     or in pinned host memory.  chunks() is called once per window, and only
     the part of each chunk inside the window is accumulated (a view, no
-    copy).  A host buffer may be reused n_slots chunks later, as with
-    fedavg_accumulate.  Every client is entered in every window, also where
+    copy); a chunk wholly outside it is passed as an empty chunk, so every
+    chunk is one library call and a host buffer may be reused n_slots chunks
+    later, as with fedavg_accumulate.  Every client is entered in every window, also where
     it sent nothing inside it, so zero-fill mode divides by the same S.
     base, out: N elements each, on the device or on the host (then copied a
     window at a time); base may be None in dense weights mode.
@@ -569,6 +577,9 @@ def stream_windows(N, clients, base, out, window=None, mode="weights", partial=F
                     mask = item[2] if len(item) > 2 else None
                     lo, hi = max(off, w0), min(off + vals.numel(), w1)
                     if lo >= hi:
+                        # nothing inside the window; still one call, which
+                        # keeps the host-buffer reuse count of the chunks
+                        fedavg_accumulate(h, cid, n_k, empty, 0)
                         continue
                     fedavg_accumulate(h, cid, n_k, vals[lo - off:hi - off], lo - w0,
                                       None if mask is None else mask[lo - off:hi - off])
