@@ -354,6 +354,29 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
                              fa_count_dtype counts_dtype, uint32_t *wsum, void *workspace,
                              size_t workspace_bytes, int *err_flag, void *stream);
 
+/*
+ * sparse_masked_accumulate_noalloc -- for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  The same merge, results and arguments
+ * as sparse_masked_accumulate, without the workspace: the list offsets
+ * (and the error flag when err_flag is NULL) live in a static device array
+ * of FA_SPARSE_SCRATCH_BYTES per GPU, held until the process ends.  The
+ * call allocates and frees nothing.  It needs 256 + 8 * Kc * (ranges + 1)
+ * bytes of that array, Kc the clients with n_k > 0 and nnz > 0 and ranges
+ * the parameter ranges the merge uses (at most 65536: any N with Kc <= 31);
+ * beyond FA_SPARSE_SCRATCH_BYTES it returns FA_ERR_RANGE before any device
+ * work.  All calls on one GPU share its array: calls that overlap in time
+ * on one GPU (other streams, other threads) race on it and must be
+ * serialized by the caller.  The flag is reset by each call; the offsets
+ * are rewritten by each call before they are read.
+ */
+#define FA_SPARSE_SCRATCH_BYTES (16ll << 20)
+int sparse_masked_accumulate_noalloc(int K, const int64_t *const *idx, const float *const *val,
+                                     const int64_t *nnz, const int64_t *n, int64_t N, fa_mode mode,
+                                     const float *base, float *out, void *counts,
+                                     fa_count_dtype counts_dtype, uint32_t *wsum, int *err_flag,
+                                     void *stream);
+
 /* ------------------------------------------------------------------------
  * Per-round sample counts (host only, no device work).
  * ------------------------------------------------------------------------ */

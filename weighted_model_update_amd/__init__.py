@@ -12,7 +12,8 @@ from .fedavg import (  # noqa: F401
     fedavg_abi_version, fedavg_set_option, fedavg_aggregate, fedavg_workspace_size,
     fedavg_begin, fedavg_accumulate, fedavg_finalize, fedavg_sync, fedavg_destroy,
     fedavg_accumulate_partial, fedavg_partial_info, fedavg_export_state, fedavg_resume,
-    sparse_workspace_size, sparse_masked_accumulate, fedavg_checksum, fedavg_sum_workspace_size,
+    sparse_workspace_size, sparse_masked_accumulate, sparse_masked_accumulate_noalloc, fedavg_checksum,
+    fedavg_sum_workspace_size,
     fedavg_checksum_sum,
     topk_workspace_size, topk_select, topk_count, SampleController, stream_windows,
 )

@@ -1025,13 +1025,50 @@ int sparse_workspace_size(int K, int64_t N, size_t *bytes)
 
 } // extern "C"
 
+// Scratch of the allocation-free sparse merge: the range offsets (and the
+// error flag when the caller passes none).  One copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never
+// passed to a kernel: the device address comes from hipGetSymbolAddress,
+// looked up per device.
+constexpr size_t SPARSE_SCRATCH_BYTES = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[SPARSE_SCRATCH_BYTES];
+
 namespace {
 
-// Body of the sparse merge entry point.
+// Device address of `scratch` on the current device, looked up on the first
+// call there; threads that race store the same address.  NULL after a failed
+// lookup (recorded as FA_ERR_HIP in *rc).
+void *scratch_address(int *rc)
+{
+    static std::atomic<void *> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *rc = hip_fail(e, "current device");
+        return nullptr;
+    }
+    if (dev < 0 || dev >= 64) {
+        *rc = fail(FA_ERR_RANGE, "device %d: at most 64 devices", dev);
+        return nullptr;
+    }
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *rc = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch address");
+            return nullptr;
+        }
+        cache[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+// Shared body of the sparse merge entry points.  workspace == nullptr with
+// use_scratch: the workspace is this device's `scratch`.
 int sparse_run(int K, const int64_t *const *idx, const float *const *val, const int64_t *nnz,
                const int64_t *n, int64_t N, fa_mode mode, const float *base, float *out,
                void *counts, fa_count_dtype counts_dtype, uint32_t *wsum, void *workspace,
-               size_t workspace_bytes, int *err_flag, void *stream)
+               size_t workspace_bytes, bool use_scratch, int *err_flag, void *stream)
 {
     if (K < 1 || K > FA_MAX_CLIENTS)
         return fail(FA_ERR_RANGE, "K=%d outside [1, %d]", K, FA_MAX_CLIENTS);
@@ -1091,14 +1128,27 @@ int sparse_run(int K, const int64_t *const *idx, const float *const *val, const 
     const int64_t tiles = (N + tile - 1) / tile;
     const int64_t R = ((tiles + NB - 1) / NB) * tile;
     const size_t used = HEADER_BYTES + (size_t)Kc * (size_t)(NB + 1) * sizeof(int64_t);
-    size_t need = 0;
-    sparse_workspace_size(K, N, &need);
-    if (!workspace || workspace_bytes < need)
-        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
-                    need);
-    if (used > workspace_bytes)
-        return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %lld ranges need %zu",
-                    workspace_bytes, (long long)NB, used);
+    if (use_scratch) {
+        if (used > SPARSE_SCRATCH_BYTES)
+            return fail(FA_ERR_RANGE,
+                        "%d contributing clients over %lld ranges need %zu bytes of offsets; the "
+                        "allocation-free call holds %zu", Kc, (long long)NB, used,
+                        SPARSE_SCRATCH_BYTES);
+        int rc = FA_OK;
+        workspace = scratch_address(&rc);
+        if (!workspace)
+            return rc;
+        workspace_bytes = SPARSE_SCRATCH_BYTES;
+    } else {
+        size_t need = 0;
+        sparse_workspace_size(K, N, &need);
+        if (!workspace || workspace_bytes < need)
+            return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                        need);
+        if (used > workspace_bytes)
+            return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %lld ranges need %zu",
+                        workspace_bytes, (long long)NB, used);
+    }
     int *flag = err_flag ? err_flag : static_cast<int *>(workspace);
     hipError_t e = fa::launch_fill_u32(flag, 1, 0u, s);
     if (e != hipSuccess)
@@ -1135,7 +1185,17 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
                              size_t workspace_bytes, int *err_flag, void *stream)
 {
     return sparse_run(K, idx, val, nnz, n, N, mode, base, out, counts, counts_dtype, wsum, workspace,
-                      workspace_bytes, err_flag, stream);
+                      workspace_bytes, false, err_flag, stream);
+}
+
+int sparse_masked_accumulate_noalloc(int K, const int64_t *const *idx, const float *const *val,
+                                     const int64_t *nnz, const int64_t *n, int64_t N, fa_mode mode,
+                                     const float *base, float *out, void *counts,
+                                     fa_count_dtype counts_dtype, uint32_t *wsum, int *err_flag,
+                                     void *stream)
+{
+    return sparse_run(K, idx, val, nnz, n, N, mode, base, out, counts, counts_dtype, wsum, nullptr,
+                      0, true, err_flag, stream);
 }
 
 // ============================================================ sample allocation

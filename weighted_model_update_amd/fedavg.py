@@ -36,7 +36,7 @@ EXPORTS = [
     "fedavg_accumulate_partial", "fedavg_partial_info", "fedavg_state_size", "fedavg_export_state",
     "fedavg_resume", "topk_workspace_size", "topk_select", "fedavg_controller_step",
     "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
-    "fedavg_sum_workspace_size", "fedavg_checksum_sum",
+    "fedavg_sum_workspace_size", "fedavg_checksum_sum", "sparse_masked_accumulate_noalloc",
 ]
 
 
@@ -82,6 +82,7 @@ def load(build_if_missing=True):
         "fedavg_destroy": ([P], i32),
         "sparse_workspace_size": ([i32, i64, P], i32),
         "sparse_masked_accumulate": ([i32, P, P, P, P, i64, i32, P, P, P, i32, P, P, sz, P, P], i32),
+        "sparse_masked_accumulate_noalloc": ([i32, P, P, P, P, i64, i32, P, P, P, i32, P, P, P], i32),
         "fedavg_checksum": ([P, i64, i32, P, P], i32),
         "fedavg_sum_workspace_size": ([i64, P], i32),
         "fedavg_checksum_sum": ([P, i64, i32, P, P, P, sz, P], i32),
@@ -527,6 +528,22 @@ def sparse_masked_accumulate(idx, val, n, N, base, out, mode="deltas", counts=No
                                       _stream_handle(stream))
     _check(rc)
     return workspace
+
+
+def sparse_masked_accumulate_noalloc(idx, val, n, N, base, out, mode="deltas", counts=None, wsum=None,
+                                     err_flag=None, stream=None):
+    """The same merge without a workspace: the library keeps the list
+    offsets in a static per-GPU scratch array and allocates nothing (for
+    callers that cannot allocate, e.g. under graph capture).  Calls that
+    overlap in time on one GPU share that array and must be serialized."""
+    lib = load()
+    K = len(idx)
+    cdt = _sparse_args(idx, val, n, N, base, out, counts, wsum, err_flag)
+    rc = lib.sparse_masked_accumulate_noalloc(K, _ptr_array(idx), _ptr_array(val),
+                                              _i64_array([t.numel() for t in idx]), _i64_array(n),
+                                              int(N), _mode(mode), _ptr(base), _ptr(out), _ptr(counts),
+                                              cdt, _ptr(wsum), _ptr(err_flag), _stream_handle(stream))
+    _check(rc)
 
 
 # ------------------------------------------------------------------ windows
