@@ -35,7 +35,7 @@ def build():
     """Compile the C oracle with gcc (IEEE arithmetic: no fast-math, no FMA
     contraction)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-o", _LIB + ".tmp", _SRC, "-lm"]
+           "-fno-fast-math", "-fopenmp", "-o", _LIB + ".tmp", _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
 
@@ -70,6 +70,11 @@ def _load():
     lib.orc_sum_set_carry_period.restype = None
     lib.orc_topk.argtypes = [P, ctypes.c_int, i64, i64, P, P]
     lib.orc_topk.restype = ctypes.c_int
+    lib.orc_sparse_mirror_f32.argtypes = [ctypes.c_int, P, P, P, P, i64, i64, ctypes.c_int, P, P,
+                                          P, P]
+    lib.orc_sparse_mirror_f32.restype = ctypes.c_int
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -215,6 +220,38 @@ def mirror_f32(xs, n, mode=WEIGHTS, base=None, x_dtype=F32, base_dtype=F32, out_
     if rc != 0:
         raise OracleError(f"orc_mirror_f32 failed: {rc}")
     return out
+
+
+def sparse_mirror_f32(idx, val, n, first, length, mode=DELTAS, base=None):
+    """The library's fp32 rounding order for sparse lists over the window
+    [first, first + length): client by client in order, fused multiply-adds
+    of fp32(n_k) * v into each parameter's sum from +0, one fp32 division by
+    fp32(W_i) (fp32(S) in zero-fill mode), the base added in fp32 in delta
+    modes; a parameter nobody sent keeps base.  idx[k], val[k]: client k's
+    entries inside the window (global indices).  base: the window's float32
+    values.  Returns (out float32, count uint32, wsum uint64)."""
+    lib = _load()
+    K = len(idx)
+    idx = [np.ascontiguousarray(i, dtype=np.int64) for i in idx]
+    val = [np.ascontiguousarray(v, dtype=np.float32) for v in val]
+    nnz = np.array([i.size for i in idx], dtype=np.int64)
+    n = np.ascontiguousarray(n, dtype=np.int64)
+    base = np.ascontiguousarray(base, dtype=np.float32)
+    assert base.shape == (length,)
+    out = np.empty(length, np.float32)
+    cnt = np.empty(length, np.uint32)
+    ws = np.empty(length, np.uint64)
+    rc = lib.orc_sparse_mirror_f32(K, _ptr_array(idx), _ptr_array(val), _ptr(nnz), _ptr(n), int(first),
+                                   int(length), mode, _ptr(base), _ptr(out), _ptr(cnt), _ptr(ws))
+    if rc != 0:
+        raise OracleError(f"orc_sparse_mirror_f32 failed: {rc}")
+    return out, cnt, ws
+
+
+def set_threads(t=0):
+    """Threads of the oracle's per-parameter loops (t <= 0: leave as is);
+    returns the count in use."""
+    return int(_load().orc_set_threads(int(t)))
 
 
 def value_sum(a, dtype):

@@ -51,9 +51,24 @@
  * mode).  The exact-rational brute force in oracle/exact.py pins this.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/*
+ * Threads.  The per-parameter loops below run in OpenMP threads, each
+ * parameter on one thread with its own arithmetic exactly as written (no
+ * parameter's result depends on another's), so the thread count changes the
+ * time only.  orc_set_threads(t) sets it (t <= 0 keeps the current one) and
+ * returns the count the loops use.
+ */
+int orc_set_threads(int t)
+{
+    if (t > 0)
+        omp_set_num_threads(t);
+    return omp_get_max_threads();
+}
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { ORC_WEIGHTS = 0, ORC_DELTAS = 1, ORC_DELTAS_ZERO_FILL = 2 };
@@ -137,6 +152,8 @@ int orc_weighted_average(int K, const void *const *x, int x_dtype, const int64_t
         S += (uint64_t)n[k];
     }
 
+    int status = ORC_OK;
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N; ++i) {
         double s = 0.0, m = 0.0;
         uint64_t W = 0;
@@ -153,14 +170,30 @@ int orc_weighted_average(int K, const void *const *x, int x_dtype, const int64_t
             c += 1;
         }
         int rc = resolve(s, m, W, S, mode, base, base_dtype, i, &ref32[i], &mag[i]);
-        if (rc != ORC_OK)
-            return rc;
+        if (rc != ORC_OK) {
+#pragma omp atomic write
+            status = rc;
+        }
         if (count)
             count[i] = c;
         if (wsum)
             wsum[i] = W;
     }
-    return ORC_OK;
+    return status;
+}
+
+/* First position j of the sorted a[0..len) with a[j] >= v. */
+static int64_t lower_bound_i64(const int64_t *a, int64_t len, int64_t v)
+{
+    int64_t lo = 0, hi = len;
+    while (lo < hi) {
+        int64_t mid = lo + (hi - lo) / 2;
+        if (a[mid] < v)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo;
 }
 
 /*
@@ -204,20 +237,45 @@ int orc_sparse_average(int K, const int64_t *const *idx, const float *const *val
                 rc = ORC_ERR_INDEX;
                 break;
             }
-            double v = (double)val[k][j];
-            s[i] += (double)n[k] * v;
-            m[i] += (double)n[k] * fabs(v);
-            W[i] += (uint64_t)n[k];
-            c[i] += 1;
         }
     }
-    for (int64_t i = 0; i < N && rc == ORC_OK; ++i) {
-        rc = resolve(s[i], m[i], W[i], S, mode, base, ORC_F32, i, &ref32[i], &mag[i]);
+    /* client by client in order for every parameter; the parameters are
+       split into blocks, one thread per block, each block visiting every
+       client's entries inside it */
+    const int64_t B = (int64_t)1 << 16;
+    const int64_t nb = rc == ORC_OK ? (N + B - 1) / B : 0;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t lo = b * B, hi = lo + B < N ? lo + B : N;
+        for (int k = 0; k < K; ++k) {
+            if (n[k] == 0)
+                continue;
+            for (int64_t j = lower_bound_i64(idx[k], nnz[k], lo); j < nnz[k] && idx[k][j] < hi; ++j) {
+                int64_t i = idx[k][j];
+                double v = (double)val[k][j];
+                s[i] += (double)n[k] * v;
+                m[i] += (double)n[k] * fabs(v);
+                W[i] += (uint64_t)n[k];
+                c[i] += 1;
+            }
+        }
+    }
+    int status = ORC_OK;
+    const int64_t nfin = rc == ORC_OK ? N : 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nfin; ++i) {
+        int r = resolve(s[i], m[i], W[i], S, mode, base, ORC_F32, i, &ref32[i], &mag[i]);
+        if (r != ORC_OK) {
+#pragma omp atomic write
+            status = r;
+        }
         if (count)
             count[i] = c[i];
         if (wsum)
             wsum[i] = W[i];
     }
+    if (rc == ORC_OK)
+        rc = status;
 done:
     free(s);
     free(m);
@@ -260,10 +318,13 @@ int orc_sparse_average_at(int K, const int64_t *const *idx, const float *const *
     for (int k = 0; k < K; ++k)
         if (n[k] > 0)
             Sall += (uint64_t)n[k];
+    for (int64_t q = 0; q < S; ++q)
+        if (at[q] < 0 || at[q] >= N)
+            return ORC_ERR_ARG;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(static)
     for (int64_t q = 0; q < S; ++q) {
         int64_t i = at[q];
-        if (i < 0 || i >= N)
-            return ORC_ERR_ARG;
         double s = 0.0, m = 0.0;
         uint64_t W = 0;
         uint32_t c = 0;
@@ -281,14 +342,16 @@ int orc_sparse_average_at(int K, const int64_t *const *idx, const float *const *
         }
         /* base is indexed by parameter, so resolve against base[i] */
         int rc = resolve(s, m, W, Sall, mode, base, ORC_F32, i, &ref32[q], &mag[q]);
-        if (rc != ORC_OK)
-            return rc;
+        if (rc != ORC_OK) {
+#pragma omp atomic write
+            status = rc;
+        }
         if (count)
             count[q] = c;
         if (wsum)
             wsum[q] = W;
     }
-    return ORC_OK;
+    return status;
 }
 
 /*
@@ -301,6 +364,7 @@ int orc_sparse_average_at(int K, const int64_t *const *idx, const float *const *
  */
 void orc_round_to_bf16(const float *in, uint16_t *out, int64_t count)
 {
+#pragma omp parallel for schedule(static) if (count > 65536)
     for (int64_t i = 0; i < count; ++i) {
         uint32_t u;
         memcpy(&u, &in[i], sizeof u);
@@ -347,6 +411,8 @@ int orc_mirror_f32(int K, const void *const *x, int x_dtype, const int64_t *n,
             return ORC_ERR_ARG;
         S += (uint64_t)n[k];
     }
+    int status = ORC_OK;
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < N; ++i) {
         float acc = 0.0f;
         uint64_t W = 0;
@@ -358,8 +424,11 @@ int orc_mirror_f32(int K, const void *const *x, int x_dtype, const int64_t *n,
         }
         float r;
         if (W == 0) {
-            if (!base)
-                return ORC_ERR_ZERO_WEIGHT;
+            if (!base) {
+#pragma omp atomic write
+                status = ORC_ERR_ZERO_WEIGHT;
+                continue;
+            }
             r = (float)value_at(base, base_dtype, i);
         } else {
             const float D = (float)(mode == ORC_DELTAS_ZERO_FILL ? S : W);
@@ -371,7 +440,88 @@ int orc_mirror_f32(int K, const void *const *x, int x_dtype, const int64_t *n,
         else
             orc_round_to_bf16(&r, (uint16_t *)out + i, 1);
     }
-    return ORC_OK;
+    return status;
+}
+
+/*
+ * The same fp32 rounding order for sparse (index, value) lists, over the
+ * window [first, first + len) of the parameters: client by client in list
+ * order, acc_i = fmaf((float)n_k, v, acc_i) from +0 for every entry of the
+ * window, W_i += n_k; then each parameter as in orc_mirror_f32 (W_i == 0:
+ * base_i; else q = acc_i / (float)D, D = W_i, or S -- every client with
+ * n_k > 0 -- in zero-fill mode; weights mode q, delta modes base_i + q in
+ * fp32).  idx[k], val[k]: the entries of client k inside the window
+ * (nnz[k] of them, strictly increasing global indices), base/out/count/wsum:
+ * len elements for the window (base required, as in the library's sparse
+ * call; count, wsum nullable).
+ */
+int orc_sparse_mirror_f32(int K, const int64_t *const *idx, const float *const *val,
+                          const int64_t *nnz, const int64_t *n, int64_t first, int64_t len,
+                          int mode, const float *base, float *out, uint32_t *count,
+                          uint64_t *wsum)
+{
+    if (K < 1 || first < 0 || len < 0 || !idx || !val || !nnz || !n || !out)
+        return ORC_ERR_ARG;
+    if (mode != ORC_WEIGHTS && mode != ORC_DELTAS && mode != ORC_DELTAS_ZERO_FILL)
+        return ORC_ERR_ARG;
+    if (!base)
+        return ORC_ERR_ARG;
+    uint64_t S = 0;
+    for (int k = 0; k < K; ++k) {
+        if (n[k] < 0 || nnz[k] < 0 || (nnz[k] > 0 && (!idx[k] || !val[k])))
+            return ORC_ERR_ARG;
+        S += (uint64_t)n[k];
+        for (int64_t j = 0; j < nnz[k]; ++j)
+            if (idx[k][j] < first || idx[k][j] >= first + len || (j > 0 && idx[k][j] <= idx[k][j - 1]))
+                return ORC_ERR_INDEX;
+    }
+    float *acc = calloc((size_t)(len ? len : 1), sizeof(float));
+    uint64_t *W = calloc((size_t)(len ? len : 1), sizeof(uint64_t));
+    uint32_t *c = calloc((size_t)(len ? len : 1), sizeof(uint32_t));
+    int rc = ORC_OK;
+    if (!acc || !W || !c) {
+        rc = ORC_ERR_NOMEM;
+        goto done;
+    }
+    /* as in orc_sparse_average: blocks of parameters, one thread each, and
+       inside a block the clients in order */
+    const int64_t B = (int64_t)1 << 16;
+    const int64_t nb = (len + B - 1) / B;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t b = 0; b < nb; ++b) {
+        const int64_t lo = first + b * B, hi = lo + B < first + len ? lo + B : first + len;
+        for (int k = 0; k < K; ++k) {
+            if (n[k] == 0)
+                continue;
+            for (int64_t j = lower_bound_i64(idx[k], nnz[k], lo); j < nnz[k] && idx[k][j] < hi; ++j) {
+                const int64_t i = idx[k][j] - first;
+                acc[i] = fmaf((float)n[k], val[k][j], acc[i]);
+                W[i] += (uint64_t)n[k];
+                c[i] += 1;
+            }
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < len; ++i) {
+        float r;
+        if (W[i] == 0) {
+            r = base[i];
+        } else {
+            const float D = (float)(mode == ORC_DELTAS_ZERO_FILL ? S : W[i]);
+            const float q = acc[i] / D;
+            r = (mode == ORC_WEIGHTS) ? q : base[i] + q;
+        }
+        out[i] = r;
+        if (count)
+            count[i] = c[i];
+        if (wsum)
+            wsum[i] = W[i];
+    }
+done:
+    free(acc);
+    free(W);
+    free(c);
+    return rc;
 }
 
 /*
@@ -395,6 +545,7 @@ uint64_t orc_checksum(const void *buf, int64_t count, int dtype, int64_t first)
     /* `first` is the index of buf[0] in the whole buffer, so the checksum of
        a buffer is the sum of the checksums of its pieces */
     uint64_t h = 0;
+#pragma omp parallel for schedule(static) reduction(+ : h) if (count > 65536)
     for (int64_t j = 0; j < count; ++j) {
         uint64_t bits = (dtype == ORC_F32) ? (uint64_t)((const uint32_t *)buf)[j]
                                            : (uint64_t)((const uint16_t *)buf)[j];

@@ -692,3 +692,100 @@ def test_mirror_products_are_fused():
     assert (err != 0).sum() > 32
     got = oracle.mirror_f32([-rn3x, x], [1, 3])
     assert np.array_equal(got, (err / 4.0).astype(np.float32))
+
+
+# ---------------------------------------------------------------- sparse fp32 mirror
+
+def _sparse_lists(r, N, K, p):
+    idx = [np.flatnonzero(r.random(N) < p).astype(np.int64) for _ in range(K)]
+    val = [(r.standard_normal(i.size) * 10.0 ** r.integers(-4, 1)).astype(np.float32) for i in idx]
+    return idx, val
+
+
+def _dense_of(idx, val, N):
+    xs, sent = [], []
+    for i, v in zip(idx, val):
+        x = np.zeros(N, np.float32)
+        s_ = np.zeros(N, np.uint8)
+        x[i] = v
+        s_[i] = 1
+        xs.append(x)
+        sent.append(s_)
+    return xs, sent
+
+
+@pytest.mark.parametrize("mode", [oracle.WEIGHTS, oracle.DELTAS, oracle.DELTAS_ZERO_FILL])
+def test_sparse_mirror_equals_float32_arithmetic_for_power_of_two_weights(mode):
+    """Power-of-two weights make every product exact, so numpy's float32
+    additions in client order give the same bits; counts and weight sums are
+    bincounts of the lists."""
+    r = np.random.default_rng(120 + mode)
+    N, K = 6000, 9
+    idx, val = _sparse_lists(r, N, K, 0.3)
+    n = [int(2 ** r.integers(0, 12)) for _ in range(K)]
+    n[4] = 0
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    out, cnt, ws = oracle.sparse_mirror_f32(idx, val, n, 0, N, mode=mode, base=base)
+    xs, sent = _dense_of(idx, val, N)
+    want = _np_f32_sequence(xs, n, sent, mode, base, sum(v for v in n if v > 0))
+    assert np.array_equal(out.view(np.uint32), want.view(np.uint32))
+    live = [k for k in range(K) if n[k] > 0]
+    assert np.array_equal(cnt, np.bincount(np.concatenate([idx[k] for k in live]), minlength=N))
+    wb = np.bincount(np.concatenate([idx[k] for k in live]),
+                     weights=np.concatenate([np.full(idx[k].size, float(n[k])) for k in live]), minlength=N)
+    assert np.array_equal(ws, wb.astype(np.uint64))
+
+
+def test_sparse_mirror_follows_client_order_and_fuses_products():
+    one, tiny = np.float32(1.0), np.float32(2.0 ** -24)
+    i0 = np.array([3], np.int64)
+    base = np.zeros(5, np.float32)
+    a, _, _ = oracle.sparse_mirror_f32([i0] * 3, [np.float32([one]), np.float32([tiny]), np.float32([tiny])],
+                                       [1, 1, 1], 0, 5, mode=oracle.WEIGHTS, base=base)
+    b, _, _ = oracle.sparse_mirror_f32([i0] * 3, [np.float32([tiny]), np.float32([tiny]), np.float32([one])],
+                                       [1, 1, 1], 0, 5, mode=oracle.WEIGHTS, base=base)
+    assert a[3] == np.float32(1.0) / np.float32(3.0)
+    assert b[3] == np.float32(1.0 + 2.0 ** -23) / np.float32(3.0)
+    # fused: -RN(3x) then 3 * x leaves the product's exact rounding error
+    r = np.random.default_rng(6)
+    x = (1.0 + r.random(40)).astype(np.float32)
+    rn3x = (np.float32(3.0) * x).astype(np.float32)
+    err = 3.0 * x.astype(np.float64) - rn3x.astype(np.float64)
+    ii = np.arange(40, dtype=np.int64)
+    got, _, _ = oracle.sparse_mirror_f32([ii, ii], [-rn3x, x], [1, 3], 0, 40, mode=oracle.WEIGHTS,
+                                         base=np.zeros(40, np.float32))
+    assert np.array_equal(got, (err / 4.0).astype(np.float32))
+
+
+def test_sparse_mirror_within_tolerance_of_the_definition_and_windows_agree():
+    """General weights: within the fp32 tolerance of the fp64 sparse
+    definition, unsent parameters a bit copy of base; a window computed
+    alone equals the same slice of the whole range, bit for bit."""
+    from parity import check
+    r = np.random.default_rng(130)
+    N, K = 20_000, 12
+    idx, val = _sparse_lists(r, N, K, 0.15)
+    n = synth.sample_counts(130, K, 100, 1000)
+    base = (r.standard_normal(N) * 0.02).astype(np.float32)
+    for mode in (oracle.WEIGHTS, oracle.DELTAS, oracle.DELTAS_ZERO_FILL):
+        out, cnt, ws = oracle.sparse_mirror_f32(idx, val, n, 0, N, mode=mode, base=base)
+        ref, mag, c64, w64 = oracle.sparse_average(idx, val, n, N, mode=mode, base=base)
+        check(out, ref, mag, "f32", copied=c64 == 0, copy_expect=base)
+        assert np.array_equal(cnt, c64) and np.array_equal(ws, w64)
+        lo, hi = 3_333, 15_001
+        wi = [i[(i >= lo) & (i < hi)] for i in idx]
+        wv = [v[(i >= lo) & (i < hi)] for i, v in zip(idx, val)]
+        # zero fill divides by every client's weight, also one with no entry in the window
+        o2, c2, w2 = oracle.sparse_mirror_f32(wi, wv, n, lo, hi - lo, mode=mode, base=base[lo:hi])
+        assert np.array_equal(o2.view(np.uint32), out[lo:hi].view(np.uint32))
+        assert np.array_equal(c2, cnt[lo:hi]) and np.array_equal(w2, ws[lo:hi])
+
+
+def test_sparse_mirror_rejects_entries_outside_the_window_or_unsorted():
+    base = np.zeros(10, np.float32)
+    with pytest.raises(oracle.OracleError):
+        oracle.sparse_mirror_f32([np.array([2, 12], np.int64)], [np.ones(2, np.float32)], [1], 5, 10,
+                                 base=base)
+    with pytest.raises(oracle.OracleError):
+        oracle.sparse_mirror_f32([np.array([7, 6], np.int64)], [np.ones(2, np.float32)], [1], 5, 10,
+                                 base=base)
