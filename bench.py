@@ -549,6 +549,9 @@ CEILING_CASES = [
     ("copy plain/plain", 1, 1, P_GLOBAL, P_GLOBAL, 1),
     ("copy nt/plain", 1, 1, P_GLOBAL_NT, P_GLOBAL, 1),
     ("copy nt/nt vpt4", 1, 1, P_GLOBAL_NT, P_GLOBAL_NT, 4),
+    ("mix2 nt/nt", 1, 2, P_GLOBAL_NT, P_GLOBAL_NT, 1),
+    ("mix4 nt/nt", 1, 4, P_GLOBAL_NT, P_GLOBAL_NT, 1),
+    ("mix8 nt/nt", 1, 8, P_GLOBAL_NT, P_GLOBAL_NT, 1),
     ("mix16 nt/nt", 1, 16, P_GLOBAL_NT, P_GLOBAL_NT, 1),
     ("mix16 plain/nt", 1, 16, P_GLOBAL, P_GLOBAL_NT, 1),
     ("mix16 buf/nt", 1, 16, P_BUF, P_GLOBAL_NT, 1),
@@ -570,7 +573,7 @@ CEILING_CASES = [
 ]
 
 
-def bench_ceiling(reps=10, warmup=2, residents=(3, 0, 2, 4)):
+def bench_ceiling(reps=10, warmup=2, residents=(3, 0, 1, 2, 4)):
     """What HBM gives the headline's byte pattern on this part, measured in
     the same run as the headline kernel: kernels that move the dense
     aggregation's bytes (16 bf16 client streams of 1,921,878,016 parameters
@@ -611,8 +614,10 @@ def bench_ceiling(reps=10, warmup=2, residents=(3, 0, 2, 4)):
 
     for res in residents:
         for name, pattern, ns, lp, sp, vpt in CEILING_CASES:
-            if res != residents[0] and not name.startswith(("mix16 nt/nt", "read16 nt", "copy nt/nt")):
+            if res != residents[0] and not name.startswith(("mix", "read16 nt", "copy nt/nt")):
                 continue        # the policy sweep runs at the default cap only
+            if res != residents[0] and name.startswith("mix16") and "nt/nt" not in name:
+                continue
             dst = bufs[16].data_ptr() if ns < 17 else bufs[0].data_ptr()
             nb_ = (ns + (1 if pattern == 1 else 0)) * nvec * 16
 
@@ -637,7 +642,8 @@ def bench_ceiling(reps=10, warmup=2, residents=(3, 0, 2, 4)):
     free_gpu()
     mixed = [r for r in rows if r["streams_read"] == 16 and r["stream_written"] and r["load"] != "kernel"]
     best = min(mixed, key=lambda r: r["median_ms"])
-    dense_default = [r for r in rows if r["load"] == "kernel" and r["resident_per_cu"] == residents[0]][0]
+    dense_default = [r for r in rows if r["name"].startswith("dense kernel")
+                     and r["resident_per_cu"] == residents[0]][0]
     return {"N": N, "bytes_per_stream": nvec * 16, "rows": rows,
             "best_mixed": {"name": best["name"], "resident_per_cu": best["resident_per_cu"],
                            "median_ms": best["median_ms"], "frac_median": best["frac_median"]},
