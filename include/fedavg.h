@@ -178,7 +178,9 @@ int fedavg_workspace_size(int64_t N, int partial, int64_t chunk_bytes, int n_slo
  * acc, wsum, count, staging: caller device buffers of at least the sizes from
  *     fedavg_workspace_size (wsum/count only in partial mode; count may be
  *     NULL in partial mode when per-parameter client counts are not wanted).
- * compute_stream: where accumulate and finalize kernels run.
+ * compute_stream: where accumulate and finalize kernels run.  The buffers are
+ *     taken in this stream's order: work queued on it before the call may
+ *     still write them (the copies into staging wait for that work too).
  * copy_stream: where host-to-device chunk copies run (NULL: the handle creates
  *     its own stream).  Copies and kernels are ordered with HIP events.
  */

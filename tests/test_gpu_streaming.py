@@ -372,3 +372,40 @@ def test_stream_state_errors():
         acc.finalize(base, out)
         acc.sync()
     assert torch.equal(out, torch.ones(N, device="cuda"))
+
+
+def test_staging_still_written_by_earlier_compute_work_is_waited_for():
+    """The staging buffer is taken in the compute stream's order: work queued
+    there before fedavg_begin may still write it (a caching allocator hands
+    out memory whose previous owner's kernels are still running).  A long
+    fill is queued on the compute stream, then a fill of the staging buffer
+    behind it, then the handle opens and pinned chunks stream in; the copies
+    into the slots must wait for that fill, so the result is the mirror's
+    bits."""
+    K, chunk = 3, 1 << 22
+    N = 3 * chunk + 1001
+    r = np.random.default_rng(301)
+    xs = [(r.standard_normal(N) * 1e-2).astype(np.float32) for _ in range(K)]
+    n = synth.sample_counts(301, K, 100, 10000)
+    host = [host_tensor(x, "f32") for x in xs]
+    acc_b, _, _, stag_b = fa.fedavg_workspace_size(N, 0, 4 * chunk, 3)
+    acc = torch.empty(acc_b // 4, dtype=torch.float32, device="cuda")
+    staging = torch.empty(stag_b, dtype=torch.uint8, device="cuda")
+    delay = torch.empty(4 << 30, dtype=torch.float32, device="cuda")       # 16 GiB
+    out = empty(N, "f32")
+    torch.cuda.synchronize()
+    delay.fill_(1.0)                        # milliseconds of work on the compute stream
+    staging.fill_(0x7F)                     # a pending write of the staging memory behind it
+    h = fa.fedavg_begin(N, "weights", False, acc, None, None, staging, 4 * chunk, 3)
+    try:
+        for k in range(K):
+            for off in range(0, N, chunk):
+                fa.fedavg_accumulate(h, k, int(n[k]), host[k][off:off + chunk], off)
+        fa.fedavg_finalize(h, None, out)
+        fa.fedavg_sync(h)
+    finally:
+        fa.fedavg_destroy(h)
+    torch.cuda.synchronize()
+    del delay
+    want = oracle.mirror_f32(xs, n)
+    assert np.array_equal(host_of(out).view(np.uint32), want.view(np.uint32))

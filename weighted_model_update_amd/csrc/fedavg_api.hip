@@ -515,6 +515,16 @@ static int open_handle(fa_handle *h, int64_t N, int mode, int partial, float *ac
     // the staging header holds the deferred error flag
     if (e == hipSuccess)
         e = fa::launch_fill_u32(st->staging, HEADER_BYTES / 4, 0u, st->compute);
+    // The caller's buffers are ordered by compute_stream, but the copies into
+    // the staging slots run on the copy stream: work already queued on the
+    // compute stream may still write that memory (a caching allocator hands
+    // out memory whose previous owner's kernels are still running on that
+    // stream).  Every slot counts as busy until the compute stream reaches
+    // this point, so the first copy into each slot waits for it.
+    for (int i = 0; i < n_slots && e == hipSuccess; ++i) {
+        e = hipEventRecord(st->slot_free[i], st->compute);
+        st->slot_used[i] = true;
+    }
     if (e != hipSuccess) {
         fedavg_destroy(st);
         return hip_fail(e, "handle set-up");
