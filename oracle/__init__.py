@@ -35,7 +35,7 @@ def build():
     """Compile the C oracle with gcc (IEEE arithmetic: no fast-math, no FMA
     contraction)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-fopenmp", "-o", _LIB + ".tmp", _SRC, "-lm"]
+           "-fno-fast-math", "-fopenmp", "-mfma", "-o", _LIB + ".tmp", _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
 

@@ -362,24 +362,26 @@ int orc_sparse_average_at(int K, const int64_t *const *idx, const float *const *
  * the fraction increments the exponent (the largest finite values round to
  * infinity).  NaN stays NaN (quiet, same sign).
  */
+static uint16_t round1_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t exp_bits = (u >> 23) & 0xFFu;
+    uint32_t frac = u & 0x7FFFFFu;
+    if (exp_bits == 0xFFu && frac != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t hi = u >> 16;
+    uint32_t lo = u & 0xFFFFu;
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))
+        hi += 1;
+    return (uint16_t)hi;
+}
+
 void orc_round_to_bf16(const float *in, uint16_t *out, int64_t count)
 {
 #pragma omp parallel for schedule(static) if (count > 65536)
-    for (int64_t i = 0; i < count; ++i) {
-        uint32_t u;
-        memcpy(&u, &in[i], sizeof u);
-        uint32_t exp_bits = (u >> 23) & 0xFFu;
-        uint32_t frac = u & 0x7FFFFFu;
-        if (exp_bits == 0xFFu && frac != 0) {
-            out[i] = (uint16_t)((u >> 16) | 0x0040u);
-            continue;
-        }
-        uint32_t hi = u >> 16;
-        uint32_t lo = u & 0xFFFFu;
-        if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))
-            hi += 1;
-        out[i] = (uint16_t)hi;
-    }
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = round1_bf16(in[i]);
 }
 
 /*
@@ -438,7 +440,7 @@ int orc_mirror_f32(int K, const void *const *x, int x_dtype, const int64_t *n,
         if (out_dtype == ORC_F32)
             ((float *)out)[i] = r;
         else
-            orc_round_to_bf16(&r, (uint16_t *)out + i, 1);
+            ((uint16_t *)out)[i] = round1_bf16(r);
     }
     return status;
 }

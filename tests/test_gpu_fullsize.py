@@ -1,8 +1,14 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (library defaults).  Inputs come from the same seeded device
-generators as bench.py; the oracle checks sampled outputs one by one (its
-inputs gathered at those parameters), and whole-buffer properties that hold
-at any size are checked exactly."""
+generators as bench.py.  The dense 2B, sparse 1B and streaming 8B outputs are
+checked whole: window by window, every output element against the oracle's
+fp32 mirror bit for bit (its inputs copied to the host), the mirror's
+checksum summed over the windows against the library's checksum of the whole
+buffer, client counts and weight sums exactly, and one window in eight
+against the fp64 definition within the stated tolerance (one in 24 for
+streaming).  The other workloads are checked at sampled outputs (the
+oracle's inputs gathered at those parameters) and through properties that
+hold at any size."""
 
 import gc
 import math
@@ -50,7 +56,41 @@ def gather_bits(t, at_dev):
     return host_of(t.index_select(0, at_dev))
 
 
-def test_dense_2b_k16_bf16_sampled():
+class HostWindows:
+    """Pinned host buffers that device windows are copied into, reused from
+    window to window."""
+
+    def __init__(self):
+        self.bufs = {}
+
+    def get(self, t, name):
+        """Host numpy copy of the contiguous device tensor t (float32, uint8,
+        int32/uint32 views kept; bfloat16 as uint16 bits)."""
+        n = t.numel()
+        b = self.bufs.get(name)
+        if b is None or b.numel() < n or b.dtype != t.dtype:
+            b = torch.empty(max(n, 1), dtype=t.dtype, pin_memory=True)
+            self.bufs[name] = b
+        b[:n].copy_(t, non_blocking=True)
+        return b[:n]
+
+    @staticmethod
+    def numpy(h):
+        if h.dtype == torch.bfloat16:
+            return h.view(torch.int16).numpy().view(np.uint16)
+        return h.numpy()
+
+
+def windows(N, W):
+    return [(w0, min(w0 + W, N)) for w0 in range(0, N, W)]
+
+
+def o1_window(i):
+    """Windows checked against the fp64 definition as well: one in eight."""
+    return i % 8 == 3
+
+
+def test_dense_2b_k16_bf16_whole_output():
     n, xs = sd.dense_2b()
     N = xs[0].numel()
     assert N == 1_921_878_016 and len(xs) == 16
@@ -59,19 +99,29 @@ def test_dense_2b_k16_bf16_sampled():
     h1 = fa.fedavg_checksum(out)
     fa.fedavg_aggregate(xs, n.tolist(), out)
     assert fa.fedavg_checksum(out) == h1          # bit-identical rerun
-    at = sample_positions(N, 200_000, 3)
-    at_dev = torch.from_numpy(at).cuda()
-    got = gather_bits(out, at_dev)
-    xk = [gather_bits(x, at_dev) for x in xs]
-    ref, mag, _, _ = oracle.weighted_average(xk, n, x_dtype=oracle.BF16)
-    check(got, ref, mag, "bf16", label="dense 2B sampled")
-    same_bits(got, oracle.mirror_f32(xk, n, x_dtype=oracle.BF16, out_dtype=oracle.BF16))
-    # the bf16 output's checksum and value sum against the oracle's, over the
-    # whole 1.92-billion-element buffer
+    hw = HostWindows()
+    want_hash = 0
+    o1_elems = 0
+    for i, (w0, w1) in enumerate(windows(N, 1 << 24)):
+        hx = [hw.get(x[w0:w1], f"x{k}") for k, x in enumerate(xs)]
+        ho = hw.get(out[w0:w1], "out")
+        torch.cuda.synchronize()
+        xk = [HostWindows.numpy(h) for h in hx]
+        got = HostWindows.numpy(ho)
+        mirror = oracle.mirror_f32(xk, n, x_dtype=oracle.BF16, out_dtype=oracle.BF16)
+        same_bits(got, mirror)
+        want_hash = (want_hash + oracle.checksum(mirror, oracle.BF16, first=w0)) % (1 << 64)
+        if o1_window(i):
+            ref, mag, _, _ = oracle.weighted_average(xk, n, x_dtype=oracle.BF16)
+            check(got, ref, mag, "bf16", label=f"dense 2B window {w0}")
+            o1_elems += w1 - w0
+    assert h1 == want_hash
+    assert o1_elems >= N // 10
+    # the bf16 output's fixed-order value sum against the exact sum, over
+    # the whole 1.92-billion-element buffer
     h, vs = fa.fedavg_checksum_sum(out)
     assert h == h1
     bits = host_of(out)
-    assert h == oracle.checksum(bits, oracle.BF16)
     want = oracle.value_sum(bits, oracle.BF16)
     absum = oracle.value_sum(bits & np.uint16(0x7FFF), oracle.BF16)
     T = -(-N // 8192)
@@ -98,7 +148,7 @@ def test_adapter_k8_full_compare():
                                               base_dtype=oracle.BF16, out_dtype=oracle.BF16, sent=sent))
 
 
-def test_sparse_1b_k20_sampled():
+def test_sparse_1b_k20_whole_output():
     n, idx, val, base = sd.sparse_1b()
     N = base.numel()
     K = len(idx)
@@ -111,27 +161,43 @@ def test_sparse_1b_k20_sampled():
                                 err_flag=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+    h_out, h_cnt = fa.fedavg_checksum(out), fa.fedavg_checksum(wsum.view(torch.float32))
+    # the lists on the host, whole (24 GB)
+    hidx = [i.cpu().numpy() for i in idx]
+    hval = [v.cpu().numpy() for v in val]
+    del idx, val
+    hw = HostWindows()
+    want_hash = want_wsum_hash = 0
+    o1_elems = 0
+    for i, (w0, w1) in enumerate(windows(N, 1 << 26)):
+        hb = hw.get(base[w0:w1], "base")
+        ho = hw.get(out[w0:w1], "out")
+        hc = hw.get(counts[w0:w1], "counts")
+        hws = hw.get(wsum[w0:w1], "wsum")
+        cuts = [np.searchsorted(ix, [w0, w1]) for ix in hidx]
+        wi = [ix[c0:c1] for ix, (c0, c1) in zip(hidx, cuts)]
+        wv = [v[c0:c1] for v, (c0, c1) in zip(hval, cuts)]
+        torch.cuda.synchronize()
+        hb_, got = hb.numpy(), ho.numpy()
+        mirror, mcnt, mws = oracle.sparse_mirror_f32(wi, wv, n, w0, w1 - w0, mode=oracle.DELTAS, base=hb_)
+        same_bits(got, mirror)
+        assert np.array_equal(hc.numpy(), mcnt.astype(np.uint8))
+        assert np.array_equal(hws.numpy().view(np.uint32), mws.astype(np.uint32))
+        want_hash = (want_hash + oracle.checksum(mirror, oracle.F32, first=w0)) % (1 << 64)
+        want_wsum_hash = (want_wsum_hash +
+                          oracle.checksum(mws.astype(np.uint32).view(np.float32), oracle.F32, first=w0)) % (1 << 64)
+        if o1_window(i):
+            ref, mag, rcnt, rws = oracle.sparse_average([x - w0 for x in wi], wv, n, w1 - w0,
+                                                        mode=oracle.DELTAS, base=hb_)
+            check(got, ref, mag, "f32", copied=rcnt == 0, copy_expect=hb_, label=f"sparse 1B window {w0}")
+            assert np.array_equal(hc.numpy(), rcnt.astype(np.uint8))
+            o1_elems += w1 - w0
+    assert h_out == want_hash and h_cnt == want_wsum_hash
+    assert o1_elems >= N // 10
     # every sent pair is counted exactly once
-    assert int(counts.sum(dtype=torch.int64).item()) == sum(i.numel() for i in idx)
+    assert int(counts.sum(dtype=torch.int64).item()) == sum(x.size for x in hidx)
     assert int(wsum.view(torch.int32).to(torch.int64).sum().item()) == \
-        sum(int(n[k]) * idx[k].numel() for k in range(K))
-    at = sample_positions(N, 200_000, 5)
-    at_dev = torch.from_numpy(at).cuda()
-    sent, vals = [], []
-    for k in range(K):
-        pos = torch.searchsorted(idx[k], at_dev)
-        pos_c = pos.clamp(max=idx[k].numel() - 1)
-        found = (idx[k].index_select(0, pos_c) == at_dev)
-        sent.append(found.cpu().numpy().astype(np.uint8))
-        vals.append(torch.where(found, val[k].index_select(0, pos_c), torch.zeros_like(at_dev, dtype=torch.float32))
-                    .cpu().numpy())
-    hb = gather_bits(base, at_dev)
-    ref, mag, rcnt, rws = oracle.weighted_average(vals, n, mode=oracle.DELTAS, base=hb, sent=sent)
-    assert np.array_equal(gather_bits(counts, at_dev), rcnt.astype(np.uint8))
-    assert np.array_equal(wsum.index_select(0, at_dev).cpu().numpy().view(np.uint32), rws.astype(np.uint32))
-    check(gather_bits(out, at_dev), ref, mag, "f32", copied=rcnt == 0, copy_expect=hb,
-          label="sparse 1B sampled")
-    same_bits(gather_bits(out, at_dev), oracle.mirror_f32(vals, n, mode=oracle.DELTAS, base=hb, sent=sent))
+        sum(int(n[k]) * hidx[k].size for k in range(K))
 
 
 def test_client_at_a_time_sparse_1b_k20_equals_the_one_pass_merge():
@@ -176,38 +242,6 @@ def test_client_at_a_time_sparse_1b_k20_equals_the_one_pass_merge():
     ref, mag, rcnt, _ = oracle.weighted_average(vals, n, mode=oracle.DELTAS, base=hb, sent=sent)
     check(gather_bits(out2, at_dev), ref, mag, "f32", copied=rcnt == 0, copy_expect=hb,
           label="client-at-a-time sparse 1B sampled")
-
-
-def test_streaming_8b_k32_sampled():
-    per = synth.CHUNK_BYTES_8B // 2
-    pool = sd.stream_8b_pool()
-    P = pool.shape[0]
-    base = sd.stream_8b_base()
-    N = base.numel()
-    assert N == 8_030_261_248
-    n = sd.stream_8b_counts(32)
-    cpc = (N + per - 1) // per
-    at = sample_positions(N, 100_000, 7)
-    at_dev = torch.from_numpy(at).cuda()
-    base_before = gather_bits(base, at_dev)
-    with fa.StreamingAccumulator(N, mode="deltas", chunk_bytes=synth.CHUNK_BYTES_8B, n_slots=3) as acc:
-        for k in range(32):
-            for c in range(cpc):
-                off = c * per
-                ln = min(per, N - off)
-                acc.accumulate(k, int(n[k]), pool[sd.pool_index(k, c, cpc, P)][:ln], offset=off)
-        acc.finalize(base, base)
-        acc.sync()
-    got = gather_bits(base, at_dev)
-    pool_bits = pool.view(torch.int16).numpy().view(np.uint16)
-    c_of = at // per
-    e_of = at - c_of * per
-    deltas = [pool_bits[[sd.pool_index(k, int(c), cpc, P) for c in c_of], e_of] for k in range(32)]
-    ref, mag, _, _ = oracle.weighted_average(deltas, n, mode=oracle.DELTAS, base=base_before,
-                                             x_dtype=oracle.BF16, base_dtype=oracle.BF16)
-    check(got, ref, mag, "bf16", label="streaming 8B sampled")
-    same_bits(got, oracle.mirror_f32(deltas, n, mode=oracle.DELTAS, base=base_before, x_dtype=oracle.BF16,
-                                     base_dtype=oracle.BF16, out_dtype=oracle.BF16))
 
 
 def test_two_level_8b_three_silos_sampled():
@@ -413,3 +447,67 @@ def test_topk_1b_bf16_client_update_properties():
     oi, ov = oracle.topk(w, oracle.BF16, kw)
     assert np.array_equal(wi.cpu().numpy(), oi) and np.array_equal(wv.cpu().numpy().view(np.uint32),
                                                                    ov.view(np.uint32))
+
+
+@pytest.fixture(scope="module")
+def streamed_8b():
+    """The 8B streaming workload run once: 32 clients, 240 chunks each from
+    the pinned pool; the output is kept beside an untouched base."""
+    per = synth.CHUNK_BYTES_8B // 2
+    pool = sd.stream_8b_pool()
+    P = pool.shape[0]
+    base = sd.stream_8b_base()
+    N = base.numel()
+    assert N == 8_030_261_248
+    n = sd.stream_8b_counts(32)
+    cpc = (N + per - 1) // per
+    out = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    with fa.StreamingAccumulator(N, mode="deltas", chunk_bytes=synth.CHUNK_BYTES_8B, n_slots=3) as acc:
+        for k in range(32):
+            for c in range(cpc):
+                off = c * per
+                ln = min(per, N - off)
+                acc.accumulate(k, int(n[k]), pool[sd.pool_index(k, c, cpc, P)][:ln], offset=off)
+        acc.finalize(base, out)
+        acc.sync()
+    torch.cuda.synchronize()
+    state = {"pool": pool, "base": base, "out": out, "n": n, "per": per, "cpc": cpc, "N": N,
+             "hash": fa.fedavg_checksum(out), "mirror_hash": {}}
+    yield state
+    del state["pool"], state["base"], state["out"]
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+STREAM_PARTS = 4
+
+
+@pytest.mark.parametrize("part", range(STREAM_PARTS))
+def test_streaming_8b_k32_whole_output(streamed_8b, part):
+    """The streamed output, one 64 MiB chunk window at a time (every
+    STREAM_PARTS-th window in each part): bit for bit against the mirror of
+    the same 32 pool chunks in arrival order, the fp64 definition on one
+    window in 24 (10 windows), and, once every part has run, the summed mirror
+    checksums against the library's checksum of the whole output."""
+    st = streamed_8b
+    pool, base, out, n, per, cpc, N = (st[k] for k in ("pool", "base", "out", "n", "per", "cpc", "N"))
+    P = pool.shape[0]
+    pool_bits = pool.view(torch.int16).numpy().view(np.uint16)
+    hw = HostWindows()
+    for c in range(part, cpc, STREAM_PARTS):
+        w0, w1 = c * per, min((c + 1) * per, N)
+        hb = hw.get(base[w0:w1], "base")
+        ho = hw.get(out[w0:w1], "out")
+        torch.cuda.synchronize()
+        deltas = [pool_bits[sd.pool_index(k, c, cpc, P)][:w1 - w0] for k in range(32)]
+        hb_, got = HostWindows.numpy(hb), HostWindows.numpy(ho)
+        mirror = oracle.mirror_f32(deltas, n, mode=oracle.DELTAS, base=hb_, x_dtype=oracle.BF16,
+                                   base_dtype=oracle.BF16, out_dtype=oracle.BF16)
+        same_bits(got, mirror)
+        st["mirror_hash"][c] = oracle.checksum(mirror, oracle.BF16, first=w0)
+        if c % 24 == 5:
+            ref, mag, _, _ = oracle.weighted_average(deltas, n, mode=oracle.DELTAS, base=hb_,
+                                                     x_dtype=oracle.BF16, base_dtype=oracle.BF16)
+            check(got, ref, mag, "bf16", label=f"streaming 8B window {c}")
+    if len(st["mirror_hash"]) == cpc:
+        assert sum(st["mirror_hash"].values()) % (1 << 64) == st["hash"]
