@@ -123,10 +123,10 @@ def bench_dense_2b(steps, warmup):
     del xs, out
     free_gpu()
     algo_bytes = (K + 1) * 2 * N
-    avg_ms = sum(durs) / len(durs)
+    st = stats(durs)
     return {
-        "K": K, "N": N, "wall_s": wall, "avg_launch_ms": avg_ms, "min_launch_ms": min(durs),
-        "algo_bytes": algo_bytes, "out_checksum": f"{out_hash:016x}",
+        "K": K, "N": N, "wall_s": wall, "avg_launch_ms": st["mean_ms"], "min_launch_ms": st["min_ms"],
+        "median_launch_ms": st["median_ms"], "algo_bytes": algo_bytes, "out_checksum": f"{out_hash:016x}",
     }
 
 
@@ -219,13 +219,44 @@ def bench_adapter(reps=400, replicas=4):
     e.record()
     torch.cuda.synchronize()
     us = s.elapsed_time(e) * 1000.0 / reps
-    del sets, outs, xs, base
+    # per-launch events as well, for the median and the minimum
+    _, d = timed(fn, reps, 0)
+    st = stats(d)
+    # the calls captured once in a HIP graph (one per replica set) and replayed
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(replicas):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(replicas):
+            fn(i)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    greps = max(1, reps // replicas)
+    s.record()
+    for _ in range(greps):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    us_graph = s.elapsed_time(e) * 1000.0 / (greps * replicas)
+    del sets, outs, xs, base, g
     free_gpu()
     return {"K": K, "N": N, "dtype": "bf16", "segments": int(len(seg)),
             "client_segments_sent": int(present.sum()), "us_per_call": us,
             "algo_bytes": algo_bytes, "hbm_gbs": algo_bytes / (us * 1e-6) / 1e9,
             "hbm_frac": algo_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-            "params_per_s": sent_params / (us * 1e-6), "replica_sets": replicas}
+            "params_per_s": sent_params / (us * 1e-6), "replica_sets": replicas,
+            "median_us_per_launch": st["median_ms"] * 1e3, "min_us_per_launch": st["min_ms"] * 1e3,
+            "hbm_frac_median_launch": algo_bytes / (st["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "us_per_call_graph": us_graph,
+            "hbm_frac_graph": algo_bytes / (us_graph * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "note": "us_per_call: back-to-back launches between two events; the graph figure "
+                    "replays the calls captured once"}
 
 
 def bench_streaming(clients=32, slots=3):
@@ -352,13 +383,15 @@ def bench_topk(steps=10, warmup=2):
     ws = torch.empty(fa.topk_workspace_size(N, k, x.dtype), dtype=torch.uint8, device="cuda")
     fn = lambda i: fa.topk_select(x, k, idx, val, ws)
     _, times = timed(fn, steps, warmup)
-    ms = sum(times) / len(times)
+    st = stats(times)
+    ms = st["mean_ms"]
     algo = 4 * N + 12 * k
     del x, idx, val, ws
     free_gpu()
     return {"N": N, "k": k, "dtype": "f32", "ms_per_call": ms, "algo_bytes": algo,
             "hbm_gbs": algo / (ms * 1e-3) / 1e9, "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "params_per_s": N / (ms * 1e-3), "input_passes": 1,
+            "params_per_s": N / (ms * 1e-3), "input_passes": 1, "median_ms": st["median_ms"],
+            "min_ms": st["min_ms"],
             "note": "a 2^20-key sample bounds the threshold; one pass over the update counts the "
                     "keys above the range, compacts the candidates inside it and stages every "
                     "entry at or above its floor; the radix digits and tile counts read only the "
@@ -427,12 +460,14 @@ def bench_sparse(steps=10, warmup=2):
     wall, durs = timed(fn, steps, warmup)
     assert int(err.item()) == 0
     algo = 12 * nnz + 9 * N
-    avg = sum(durs) / len(durs)
+    st = stats(durs)
+    avg = st["mean_ms"]
     del idx, val, base, out, counts, ws
     free_gpu()
     return {"K": K, "N": N, "dtype": "f32", "pairs": nnz, "ms_per_call": avg, "algo_bytes": algo,
             "hbm_gbs": algo / (avg * 1e-3) / 1e9, "hbm_frac": algo / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "params_per_s": nnz / (avg * 1e-3)}
+            "params_per_s": nnz / (avg * 1e-3), "median_ms": st["median_ms"], "min_ms": st["min_ms"],
+            "hbm_frac_median": algo / (st["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def bench_sparse_stream(clients=20):
@@ -529,6 +564,140 @@ def bench_copy_calibration(gib=4):
     free_gpu()
     return {"kernel": "convert_kernel<0, 0>", "bytes_read": gib << 30, "bytes_written": gib << 30,
             "launches": 3}
+
+
+def bench_dense_k(Ks=(4, 8, 16, 20, 32, 64), total_bytes=65_343_852_544, reps=10, warmup=2):
+    """Resident dense aggregation at runtime client counts: K bf16 clients
+    and a bf16 output of N parameters each, N chosen so the (K+1)*2*N bytes
+    match the 2.0B K=16 workload's 65.3 GB.  K = 8 and 16 have kernels of
+    their own; the others take the generic kernel (clients in batches of
+    8).  Values do not change the time, so the clients are filled with a
+    constant."""
+    import torch
+    import weighted_model_update_amd as fa
+    rows = []
+    for K in Ks:
+        N = total_bytes // ((K + 1) * 2) // 256 * 256
+        xs = [torch.full((N,), 0.01 * (k + 1), dtype=torch.bfloat16, device="cuda") for k in range(K)]
+        out = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+        n = [100 + 37 * k for k in range(K)]
+        _, d = timed(lambda i: fa.fedavg_aggregate(xs, n, out), reps, warmup)
+        st = stats(d)
+        nb = (K + 1) * 2 * N
+        rows.append({"K": K, "N": N, "bytes": nb, **st,
+                     "hbm_gbs_median": nb / (st["median_ms"] * 1e-3) / 1e9,
+                     "hbm_frac_median": nb / (st["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "params_per_s_median": K * N / (st["median_ms"] * 1e-3),
+                     "kernel": "dense_vec_kernel<K>" if K in (3, 8, 16) else "dense_vec_kernel<generic>"})
+        log(f"dense K={K}: {st['median_ms']:.3f} ms median, {rows[-1]['hbm_frac_median']:.3f} of peak")
+        del xs, out
+        free_gpu()
+    return {"rows": rows}
+
+
+def bench_streaming_chunks(chunk_mib=(16, 64, 256), slots=(2, 3, 4), clients=4):
+    """Chunk size against staging slots for the streaming path: the 8B bf16
+    workload's first `clients` clients streamed from pinned host memory in
+    chunks of each size, through 2, 3 or 4 staging slots (chunk size trades
+    request overhead against per-chunk memory: FLARE page, Tensor
+    Downloader).  Chunks come from a pinned pool of 4 GiB cut at each size."""
+    import torch
+    import synth
+    import synth.device as sd
+    import weighted_model_update_amd as fa
+    base = sd.stream_8b_base()
+    N = base.numel()
+    n = sd.stream_8b_counts(32)[:clients]
+    pool = sd.stream_8b_pool().view(-1)           # 4 GiB of distinct bf16 deltas
+    rows = []
+    acc_b, _, _, _ = fa.fedavg_workspace_size(N, 0, 1 << 20, 1)
+    acc = torch.empty(acc_b // 4, dtype=torch.float32, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    for mib in chunk_mib:
+        per = (mib << 20) // 2
+        P = pool.numel() // per
+        chunks = pool[:P * per].view(P, per)
+        cpc = (N + per - 1) // per
+        for sl in slots:
+            _, _, _, stag_b = fa.fedavg_workspace_size(N, 0, mib << 20, sl)
+            staging = torch.empty(stag_b, dtype=torch.uint8, device="cuda")
+
+            def one_pass(nc):
+                h = fa.fedavg_begin(N, "deltas", False, acc, None, None, staging, mib << 20, sl,
+                                    copy_stream=copy_stream)
+                for k in range(nc):
+                    for c in range(cpc):
+                        off = c * per
+                        fa.fedavg_accumulate(h, k, int(n[k]), chunks[(k * cpc + c) * 37 % P][:min(per, N - off)],
+                                             off)
+                fa.fedavg_finalize(h, base, base)
+                fa.fedavg_sync(h)
+                fa.fedavg_destroy(h)
+
+            one_pass(1)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            one_pass(clients)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            pb = 2 * N * clients
+            rows.append({"chunk_mib": mib, "slots": sl, "clients": clients, "wall_s": wall,
+                         "pcie_gbs": pb / wall / 1e9, "pcie_frac": pb / wall / 1e9 / PCIE_PEAK_GBS,
+                         "staging_bytes": stag_b})
+            log(f"streaming {mib} MiB x {sl} slots: {pb / wall / 1e9:.1f} GB/s")
+            del staging
+    del base, pool, acc, chunks
+    free_gpu()
+    return {"N": N, "rows": rows}
+
+
+def bench_spill(gib=1):
+    """Spill and resume of a streaming aggregate (FLARE page, "Offload
+    Aggregation to Disk"): a partial-mode accumulator of gib GiB of fp32
+    sums (plus its uint32 weight sums and uint8 counts) written to a
+    directory under the temporary directory with StreamingAccumulator.save
+    and read back with load.  Reported: bytes per second for each, and for
+    the device-to-pinned-host copies alone (the library's side of it)."""
+    import shutil
+    import tempfile
+    import torch
+    import weighted_model_update_amd as fa
+    N = (gib << 30) // 4
+    d = tempfile.mkdtemp(prefix="fedavg_spill_")
+    try:
+        acc = fa.StreamingAccumulator(N, mode="deltas", partial=True, chunk_bytes=1 << 20, n_slots=2)
+        x = torch.full((N,), 0.5, dtype=torch.float32, device="cuda")
+        acc.accumulate(0, 3, x, offset=0)
+        acc.sync()
+        nbytes = 9 * N
+        t0 = time.perf_counter()
+        acc.save(d)
+        t_save = time.perf_counter() - t0
+        acc.close()
+        del acc
+        t0 = time.perf_counter()
+        back = fa.StreamingAccumulator.load(d, N, mode="deltas", partial=True, chunk_bytes=1 << 20, n_slots=2)
+        torch.cuda.synchronize()
+        t_load = time.perf_counter() - t0
+        ok = bool(torch.equal(back.acc[:N], torch.full((N,), 1.5, dtype=torch.float32, device="cuda")))
+        back.close()
+        # the device <-> pinned host copies alone, 64 MiB at a time
+        bounce = torch.empty(64 << 20, dtype=torch.uint8, pin_memory=True)
+        flat = x.view(torch.uint8)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for off in range(0, flat.numel(), bounce.numel()):
+            m = min(bounce.numel(), flat.numel() - off)
+            bounce[:m].copy_(flat[off:off + m])
+        t_d2h = time.perf_counter() - t0
+        del x, flat, bounce
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+        free_gpu()
+    return {"N": N, "bytes": nbytes, "save_s": t_save, "save_gbs": nbytes / t_save / 1e9,
+            "load_s": t_load, "load_gbs": nbytes / t_load / 1e9, "resumed_bits_ok": ok,
+            "d2h_pinned_gbs": 4 * N / t_d2h / 1e9,
+            "where": "a directory under the temporary directory of the host"}
 
 
 # --------------------------------------------------------------------------
@@ -655,25 +824,98 @@ def bench_ceiling(reps=10, warmup=2, residents=(3, 0, 1, 2, 4)):
 # CPU oracle baseline
 # --------------------------------------------------------------------------
 
-def cpu_baseline(target_s=10.0):
-    import numpy as np
-    import oracle
-    import synth
-    K, S = 16, 1 << 22
-    log(f"cpu baseline: oracle on a {S}-parameter sample of the K=16 bf16 workload")
-    base, xs = synth.dense_clients_bf16(synth.CFG_DENSE_2B, K, S, 0.02, 1e-3)
-    n = synth.sample_counts(synth.CFG_DENSE_2B, K, 100, 1000)
+def _time_oracle(fn, units, budget_s):
+    """Calls fn() until budget_s has passed (at least once); returns units
+    per second and the number of calls."""
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.weighted_average(xs, n, x_dtype=oracle.BF16)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
-        if el >= target_s or reps >= 1000:
+        if el >= budget_s:
             break
-    return {"value": K * S * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"the first {S} parameters of the K=16 bf16 dense workload (same distributions), "
-                      f"{reps} passes, {el:.1f} s, single-threaded C oracle (fp64)"}
+    return units * reps / el, reps
+
+
+def cpu_baseline(budget_s=2.0):
+    """The oracle (plain C, fp64, OpenMP over parameters) timed on this
+    host, on every host thread and on one, for the small dense, adapter,
+    2.0B dense and sparse workloads, each on a bounded sample of the
+    workload (whole for the two small ones).  Inputs are host-generated with
+    the same distributions, already in host memory when the clock starts;
+    the unit is aggregated params/s (parameters the clients contributed, per
+    second), the headline's unit."""
+    import numpy as np
+    import oracle
+    import synth
+    all_threads = oracle.set_threads(0)
+    host = {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "omp_threads": all_threads}
+    log(f"cpu baseline: oracle on {all_threads} threads and on 1 (host nproc {host['nproc']})")
+    cases = {}
+
+    # small dense: K=3 fp32 clients of 10^6, whole
+    K, N = 3, 1_000_000
+    xs = synth.dense_clients_f32(synth.CFG_DENSE_SMALL, K, N, 0.02)
+    n = synth.sample_counts(synth.CFG_DENSE_SMALL, K, 100, 1000)
+    cases["dense_small"] = (lambda: oracle.weighted_average(xs, n), K * N,
+                            "whole workload: K=3 fp32 clients of 1,000,000 parameters")
+
+    # adapters: K=8 LoRA q,k,v,o adapters of 32 layers, whole, per-module masks
+    bounds, module_of = synth.adapter_segments()
+    bounds = np.asarray(bounds, np.int64)
+    Na, Ka = int(bounds[-1]), 8
+    na = synth.sample_counts(synth.CFG_ADAPTER, Ka, 500, 5000)
+    pres = synth.adapter_presence(synth.CFG_ADAPTER, Ka, max(module_of) + 1, 0.6)[:, module_of]
+    seg_of = np.repeat(np.arange(len(bounds) - 1), np.diff(bounds))
+    sent = [np.ascontiguousarray(pres[k][seg_of], np.uint8) for k in range(Ka)]
+    xa = [synth.bf16_bits_from_f32(synth.normal_f32(synth.CFG_ADAPTER, synth.ROLE_VALUES, k, Na, 0.01))
+          for k in range(Ka)]
+    ba = synth.bf16_bits_from_f32(synth.normal_f32(synth.CFG_ADAPTER, synth.ROLE_BASE, 0, Na, 0.01))
+    sent_params = int(sum(s_.sum(dtype=np.int64) for s_ in sent))
+    cases["adapter"] = (lambda: oracle.weighted_average(xa, na, base=ba, x_dtype=oracle.BF16,
+                                                        base_dtype=oracle.BF16, sent=sent),
+                        sent_params, "whole workload: K=8 clients, 16,777,216 bf16 parameters, "
+                                     "Bernoulli(0.6) module masks")
+
+    # 2.0B dense: K=16 bf16, the first 2^22 parameters
+    S = 1 << 22
+    _, xd = synth.dense_clients_bf16(synth.CFG_DENSE_2B, 16, S, 0.02, 1e-3)
+    nd = synth.sample_counts(synth.CFG_DENSE_2B, 16, 100, 1000)
+    cases["dense_2b"] = (lambda: oracle.weighted_average(xd, nd, x_dtype=oracle.BF16), 16 * S,
+                         f"the first {S} parameters of the K=16 bf16 dense workload")
+
+    # sparse: K=20 top-10% lists over a 2^22-parameter slice of the index space
+    Ns = 1 << 22
+    si = [synth.uniform_sparse_support(synth.CFG_SPARSE_1B, k, Ns, Ns // 10) for k in range(20)]
+    sv = [synth.laplace_tail_values(synth.CFG_SPARSE_1B, k, Ns // 10, 0.1, 1e-3) for k in range(20)]
+    bs = synth.normal_f32(synth.CFG_SPARSE_1B, synth.ROLE_BASE, 0, Ns, 0.02)
+    ns = synth.sample_counts(synth.CFG_SPARSE_1B, 20, 100, 1000)
+    cases["sparse"] = (lambda: oracle.sparse_average(si, sv, ns, Ns, mode=oracle.DELTAS, base=bs),
+                       sum(x.size for x in si),
+                       f"K=20 top-10% lists over {Ns} parameters (the workload's density and "
+                       f"value distribution)")
+
+    out = {}
+    for name, (fn, units, sample) in cases.items():
+        fn()                                            # warm-up
+        res = {"sample": sample}
+        for label, t in (("all", all_threads), ("one", 1)):
+            oracle.set_threads(t)
+            v, reps = _time_oracle(fn, units, budget_s)
+            res[f"params_per_s_{label}_threads"] = v
+            res[f"calls_{label}_threads"] = reps
+        oracle.set_threads(all_threads)
+        out[name] = res
+        log(f"cpu baseline {name}: {res['params_per_s_all_threads']:.3e} params/s on {all_threads} "
+            f"threads, {res['params_per_s_one_threads']:.3e} on 1")
+    head = out["dense_2b"]
+    return {"value": head["params_per_s_all_threads"], "unit": "params/s", "cores": all_threads,
+            "kind": "oracle",
+            "sample": head["sample"] + f"; plain C oracle (fp64), OpenMP over parameters on "
+                                       f"{all_threads} threads",
+            "one_thread_value": head["params_per_s_one_threads"], "host": host, "workloads": out}
 
 
 def traffic_from_counters():
@@ -701,8 +943,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all",
                     help="comma list of: dense,dense_small,adapter,streaming,windows,sparse,topk,"
-                         "hierarchical,sparse_stream,checksum,ceiling,cpu,copycal "
-                         "(default all but copycal)")
+                         "hierarchical,sparse_stream,checksum,ceiling,dense_k,streaming_chunks,spill,"
+                         "cpu,copycal (default all but copycal)")
     ap.add_argument("--stream-clients", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -720,7 +962,8 @@ def main():
     only = set(args.only.split(",")) if args.only != "all" else {"dense", "dense_small", "adapter",
                                                                  "streaming", "windows", "sparse", "topk",
                                                                  "hierarchical", "sparse_stream",
-                                                                 "checksum", "ceiling", "cpu"}
+                                                                 "checksum", "ceiling", "dense_k",
+                                                                 "streaming_chunks", "spill", "cpu"}
     if args.no_cpu_baseline:
         only.discard("cpu")
 
@@ -765,6 +1008,13 @@ def main():
         c = modes["ceiling"]
         log(f"ceiling: best mixed pattern {c['best_mixed']['name']} at {c['best_mixed']['median_ms']:.3f} ms; "
             f"dense kernel {c['dense_median_ms']:.3f} ms ({c['dense_over_best_mixed']:.3f}x)")
+    if "dense_k" in only:
+        modes["dense_k"] = bench_dense_k()
+    if "streaming_chunks" in only:
+        modes["streaming_chunks"] = bench_streaming_chunks()
+    if "spill" in only:
+        modes["spill"] = bench_spill()
+        log(f"spill: save {modes['spill']['save_gbs']:.2f} GB/s, load {modes['spill']['load_gbs']:.2f} GB/s")
     if "copycal" in only:
         modes["copy_calibration"] = bench_copy_calibration()
     cpu = cpu_baseline() if "cpu" in only else None
@@ -786,7 +1036,9 @@ def main():
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(),
                          "kernel": "dense_vec_kernel<bf16,bf16,K=16>",
                          "algo_bytes_per_launch": head["algo_bytes"],
-                         "avg_launch_ms": head["avg_launch_ms"]},
+                         "avg_launch_ms": head["avg_launch_ms"],
+                         "median_launch_ms": head["median_launch_ms"],
+                         "min_launch_ms": head["min_launch_ms"]},
         })
     else:
         rec.update({"value": None, "ms_per_step": None, "config": {"workload": "partial run: " + args.only}})
