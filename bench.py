@@ -569,9 +569,9 @@ def bench_copy_calibration(gib=4):
 def bench_dense_k(Ks=(4, 8, 16, 20, 32, 64), total_bytes=65_343_852_544, reps=10, warmup=2):
     """Resident dense aggregation at runtime client counts: K bf16 clients
     and a bf16 output of N parameters each, N chosen so the (K+1)*2*N bytes
-    match the 2.0B K=16 workload's 65.3 GB.  K = 8 and 16 have kernels of
-    their own; the others take the generic kernel (clients in batches of
-    8).  Values do not change the time, so the clients are filled with a
+    match the 2.0B K=16 workload's 65.3 GB.  K = 3, 8 and 16 have kernels
+    of their own; the others take the generic kernel (clients in batches of
+    8, of 16 above 16 clients).  Values do not change the time, so the clients are filled with a
     constant."""
     import torch
     import weighted_model_update_amd as fa
@@ -588,7 +588,8 @@ def bench_dense_k(Ks=(4, 8, 16, 20, 32, 64), total_bytes=65_343_852_544, reps=10
                      "hbm_gbs_median": nb / (st["median_ms"] * 1e-3) / 1e9,
                      "hbm_frac_median": nb / (st["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "params_per_s_median": K * N / (st["median_ms"] * 1e-3),
-                     "kernel": "dense_vec_kernel<K>" if K in (3, 8, 16) else "dense_vec_kernel<generic>"})
+                     "kernel": ("dense_vec_kernel<K>" if K in (3, 8, 16) else
+                                "dense_vec_kernel<batches of 16>" if K > 16 else "dense_vec_kernel<batches of 8>")})
         log(f"dense K={K}: {st['median_ms']:.3f} ms median, {rows[-1]['hbm_frac_median']:.3f} of peak")
         del xs, out
         free_gpu()

@@ -41,7 +41,7 @@ def base_of(seed, N, bdt):
     return synth.bf16_bits_from_f32(b) if bdt == "bf16" else b
 
 
-@pytest.mark.parametrize("K", [1, 3, 5, 16, 20, 64])
+@pytest.mark.parametrize("K", [1, 3, 5, 8, 16, 17, 20, 64])
 @pytest.mark.parametrize("xdt,odt,mode", [("f32", "f32", "weights"), ("bf16", "bf16", "deltas"),
                                           ("bf16", "f32", "deltas"), ("f32", "bf16", "weights")])
 def test_dense(K, xdt, odt, mode):

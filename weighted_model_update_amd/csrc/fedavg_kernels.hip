@@ -150,11 +150,13 @@ __device__ __forceinline__ int64_t grid_threads() { return (int64_t)gridDim.x * 
 
 // One pass over K client buffers: each lane owns 8 consecutive parameters per
 // step, issues the 16-byte loads of every client (KC of them when the client
-// count is a compile-time constant, batches of 8 otherwise) before its FMAs,
-// then writes the 8 results with one non-temporal store.
+// count is a compile-time constant KC > 0; batches of -KC clients for a
+// client count known at run time) before its FMAs, then writes the 8 results
+// with one non-temporal store.
 template <int XDT, int ODT, int BDT, int MODE, int KC>
 __global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64_t nvec)
 {
+    constexpr int GB = KC < 0 ? -KC : 8;
     const int K = KC > 0 ? KC : a.K;
     for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
         const int64_t e = v * VEC;
@@ -171,14 +173,14 @@ __global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64
             for (int k = 0; k < KC; ++k)
                 io<XDT>::fma8(xr[k], a.w[k], acc);
         } else {
-            for (int k0 = 0; k0 < K; k0 += 8) {
-                typename io<XDT>::raw xr[8];
+            for (int k0 = 0; k0 < K; k0 += GB) {
+                typename io<XDT>::raw xr[GB];
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
+                for (int k = 0; k < GB; ++k)
                     if (k0 + k < K)
                         xr[k] = io<XDT>::load_raw(a.x[k0 + k], e);
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
+                for (int k = 0; k < GB; ++k)
                     if (k0 + k < K)
                         io<XDT>::fma8(xr[k], a.w[k0 + k], acc);
             }
@@ -1441,11 +1443,20 @@ static hipError_t dense_launch_t(const DenseArgs &a, bool aligned, int64_t cap, 
 {
     const int64_t nvec = aligned ? a.N / VEC : 0;
     if (nvec > 0) {
+        // Fixed client counts get kernels of their own; other counts load
+        // their clients in batches, of 16 once there are more than 16 (one
+        // batch boundary fewer per 16 clients: 2-3% at K = 20 ... 64, where
+        // dedicated K = 32 or 64 kernels need up to 256 VGPRs and run slower).
         switch (a.K) {
         case 3: dense_vec_launch<XDT, ODT, BDT, MODE, 3>(a, nvec, cap, resident, s); break;
         case 8: dense_vec_launch<XDT, ODT, BDT, MODE, 8>(a, nvec, cap, resident, s); break;
         case 16: dense_vec_launch<XDT, ODT, BDT, MODE, 16>(a, nvec, cap, resident, s); break;
-        default: dense_vec_launch<XDT, ODT, BDT, MODE, 0>(a, nvec, cap, resident, s); break;
+        default:
+            if (a.K > 16)
+                dense_vec_launch<XDT, ODT, BDT, MODE, -16>(a, nvec, cap, resident, s);
+            else
+                dense_vec_launch<XDT, ODT, BDT, MODE, -8>(a, nvec, cap, resident, s);
+            break;
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
