@@ -75,6 +75,12 @@ template <> struct io<DT_F32> {
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
+    static __device__ __forceinline__ void load4(const void *p, int64_t e, float (&v)[4])
+    {
+        const f32x4 a = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + e));
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    }
     static __device__ __forceinline__ float load1(const void *p, int64_t e)
     {
         return static_cast<const float *>(p)[e];
@@ -124,6 +130,13 @@ template <> struct io<DT_BF16> {
         v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
         v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
     }
+    static __device__ __forceinline__ void load4(const void *p, int64_t e, float (&v)[4])
+    {
+        const u32x2 w = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(p) + e));
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    }
     static __device__ __forceinline__ float load1(const void *p, int64_t e)
     {
         return bf16_lo(static_cast<const uint16_t *>(p)[e]);
@@ -145,6 +158,24 @@ template <> struct io<DT_BF16> {
 
 __device__ __forceinline__ int64_t global_tid() { return (int64_t)blockIdx.x * blockDim.x + threadIdx.x; }
 __device__ __forceinline__ int64_t grid_threads() { return (int64_t)gridDim.x * blockDim.x; }
+
+// First parameters of the two 4-parameter quads that step v takes in a
+// grid-stride loop of 256-lane workgroups over nvec steps of 8 fp32
+// parameters.  In a full run of 256 steps these are quads l and l + 256 of
+// the run (l = v mod 256), so the 16-byte accesses of a wave are contiguous
+// and each of its store instructions writes 1 KiB of whole cache lines; in
+// the last, short run they are quads 2l and 2l + 1.  Two 16-byte stores per
+// lane 32 bytes apart would instead leave each line half written by each
+// instruction, and a non-temporal line evicted in between reaches HBM twice
+// (11% more written bytes, measured, in a read-modify-write of fp32 sums).
+__device__ __forceinline__ void quad_pair(int64_t v, int64_t nvec, int64_t &e0, int64_t &e1)
+{
+    const int64_t run = v & ~(int64_t)255;
+    const int64_t l = v & 255;
+    const bool full = run + 256 <= nvec;
+    e0 = run * VEC + (full ? l * 4 : l * 8);
+    e1 = e0 + (full ? 1024 : 4);
+}
 
 // ================================================================ resident dense
 
@@ -597,59 +628,52 @@ template <int DT, int PART>
 __global__ __launch_bounds__(256) void stream_acc_vec_kernel(const StreamArgs a, int64_t nvec)
 {
     for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
-        const int64_t e = v * VEC;
-        const int64_t g = a.offset + e;
-        float xv[VEC];
-        io<DT>::load8(a.chunk, e, xv);
-        f32x4 *ap = reinterpret_cast<f32x4 *>(a.acc + g);
-        f32x4 lo = __builtin_nontemporal_load(ap);
-        f32x4 hi = __builtin_nontemporal_load(ap + 1);
-        uint32_t sent = 0xffu;
-        if constexpr (PART == PART_MASK) {
-            u32x2 mb = *reinterpret_cast<const u32x2 *>(a.mask + e);
-            sent = 0;
+        int64_t eq[2];
+        quad_pair(v, nvec, eq[0], eq[1]);
+        float xv[2][4];
+        f32x4 acc[2];
+        uint32_t sent[2] = {0xfu, 0xfu};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sent |= (((mb.x >> (8 * j)) & 0xffu) != 0) << j;
-                sent |= (((mb.y >> (8 * j)) & 0xffu) != 0) << (j + 4);
+        for (int q = 0; q < 2; ++q) {
+            io<DT>::load4(a.chunk, eq[q], xv[q]);
+            acc[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.acc + a.offset + eq[q]));
+            if constexpr (PART == PART_MASK) {
+                const uint32_t mb = *reinterpret_cast<const uint32_t *>(a.mask + eq[q]);
+                sent[q] = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sent[q] |= (((mb >> (8 * j)) & 0xffu) != 0) << j;
             }
         }
-        float acc[VEC] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-        for (int j = 0; j < VEC; ++j)
-            if ((sent >> j) & 1)
-                acc[j] = __builtin_fmaf(a.w, xv[j], acc[j]);
-        lo = f32x4{acc[0], acc[1], acc[2], acc[3]};
-        hi = f32x4{acc[4], acc[5], acc[6], acc[7]};
-        __builtin_nontemporal_store(lo, ap);
-        __builtin_nontemporal_store(hi, ap + 1);
+        for (int q = 0; q < 2; ++q) {
+            f32x4 &s = acc[q];
+            if (sent[q] & 1) s.x = __builtin_fmaf(a.w, xv[q][0], s.x);
+            if (sent[q] & 2) s.y = __builtin_fmaf(a.w, xv[q][1], s.y);
+            if (sent[q] & 4) s.z = __builtin_fmaf(a.w, xv[q][2], s.z);
+            if (sent[q] & 8) s.w = __builtin_fmaf(a.w, xv[q][3], s.w);
+            __builtin_nontemporal_store(s, reinterpret_cast<f32x4 *>(a.acc + a.offset + eq[q]));
+        }
         if constexpr (PART != PART_DENSE) {
-            u32x4 *wp = reinterpret_cast<u32x4 *>(a.wsum + g);
-            u32x4 w0 = wp[0], w1 = wp[1];
-            w0.x += (sent & 1) ? a.wi : 0u;
-            w0.y += (sent & 2) ? a.wi : 0u;
-            w0.z += (sent & 4) ? a.wi : 0u;
-            w0.w += (sent & 8) ? a.wi : 0u;
-            w1.x += (sent & 16) ? a.wi : 0u;
-            w1.y += (sent & 32) ? a.wi : 0u;
-            w1.z += (sent & 64) ? a.wi : 0u;
-            w1.w += (sent & 128) ? a.wi : 0u;
-            wp[0] = w0;
-            wp[1] = w1;
-            if (a.count) {
-                // one byte per parameter; a client adds at most 1 and there
-                // are at most 255 clients, so no byte carries into the next
-                u32x2 *cp = reinterpret_cast<u32x2 *>(a.count + g);
-                u32x2 c = *cp;
-                uint32_t add_lo = 0, add_hi = 0;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    add_lo |= ((sent >> j) & 1u) << (8 * j);
-                    add_hi |= ((sent >> (j + 4)) & 1u) << (8 * j);
+            for (int q = 0; q < 2; ++q) {
+                u32x4 *wp = reinterpret_cast<u32x4 *>(a.wsum + a.offset + eq[q]);
+                u32x4 w = *wp;
+                w.x += (sent[q] & 1) ? a.wi : 0u;
+                w.y += (sent[q] & 2) ? a.wi : 0u;
+                w.z += (sent[q] & 4) ? a.wi : 0u;
+                w.w += (sent[q] & 8) ? a.wi : 0u;
+                *wp = w;
+                if (a.count) {
+                    // one byte per parameter; a client adds at most 1 and
+                    // there are at most 255 clients, so no byte carries into
+                    // the next
+                    uint32_t add = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        add |= ((sent[q] >> j) & 1u) << (8 * j);
+                    *reinterpret_cast<uint32_t *>(a.count + a.offset + eq[q]) += add;
                 }
-                c.x += add_lo;
-                c.y += add_hi;
-                *cp = c;
             }
         }
     }
@@ -712,35 +736,37 @@ __global__ __launch_bounds__(256) void stream_merge_vec_kernel(const StreamArgs 
 {
     const float *src = static_cast<const float *>(a.chunk);
     for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
-        const int64_t e = v * VEC;
-        const int64_t g = a.offset + e;
-        const f32x4 *sp = reinterpret_cast<const f32x4 *>(src + e);
-        f32x4 *ap = reinterpret_cast<f32x4 *>(a.acc + g);
-        const f32x4 s0 = __builtin_nontemporal_load(sp);
-        const f32x4 s1 = __builtin_nontemporal_load(sp + 1);
-        f32x4 lo = __builtin_nontemporal_load(ap);
-        f32x4 hi = __builtin_nontemporal_load(ap + 1);
+        int64_t e0, e1;
+        quad_pair(v, nvec, e0, e1);
+        const f32x4 *sp0 = reinterpret_cast<const f32x4 *>(src + e0);
+        const f32x4 *sp1 = reinterpret_cast<const f32x4 *>(src + e1);
+        f32x4 *ap0 = reinterpret_cast<f32x4 *>(a.acc + a.offset + e0);
+        f32x4 *ap1 = reinterpret_cast<f32x4 *>(a.acc + a.offset + e1);
+        const f32x4 s0 = __builtin_nontemporal_load(sp0);
+        const f32x4 s1 = __builtin_nontemporal_load(sp1);
+        f32x4 lo = __builtin_nontemporal_load(ap0);
+        f32x4 hi = __builtin_nontemporal_load(ap1);
         lo = f32x4{lo.x + s0.x, lo.y + s0.y, lo.z + s0.z, lo.w + s0.w};
         hi = f32x4{hi.x + s1.x, hi.y + s1.y, hi.z + s1.z, hi.w + s1.w};
-        __builtin_nontemporal_store(lo, ap);
-        __builtin_nontemporal_store(hi, ap + 1);
+        __builtin_nontemporal_store(lo, ap0);
+        __builtin_nontemporal_store(hi, ap1);
         if constexpr (PARTIAL) {
-            const u32x4 *ws = reinterpret_cast<const u32x4 *>(a.src_wsum + e);
-            u32x4 *wp = reinterpret_cast<u32x4 *>(a.wsum + g);
-            const u32x4 a0 = __builtin_nontemporal_load(ws);
-            const u32x4 a1 = __builtin_nontemporal_load(ws + 1);
-            u32x4 w0 = wp[0], w1 = wp[1];
+            const u32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.src_wsum + e0));
+            const u32x4 a1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.src_wsum + e1));
+            u32x4 *wp0 = reinterpret_cast<u32x4 *>(a.wsum + a.offset + e0);
+            u32x4 *wp1 = reinterpret_cast<u32x4 *>(a.wsum + a.offset + e1);
+            u32x4 w0 = *wp0, w1 = *wp1;
             w0 = u32x4{w0.x + a0.x, w0.y + a0.y, w0.z + a0.z, w0.w + a0.w};
             w1 = u32x4{w1.x + a1.x, w1.y + a1.y, w1.z + a1.z, w1.w + a1.w};
-            wp[0] = w0;
-            wp[1] = w1;
+            *wp0 = w0;
+            *wp1 = w1;
             if (a.count) {
-                const u32x2 cs = *reinterpret_cast<const u32x2 *>(a.src_count + e);
-                u32x2 *cp = reinterpret_cast<u32x2 *>(a.count + g);
-                u32x2 c = *cp;
-                c.x += cs.x;
-                c.y += cs.y;
-                *cp = c;
+                const uint32_t c0 = *reinterpret_cast<const uint32_t *>(a.src_count + e0);
+                const uint32_t c1 = *reinterpret_cast<const uint32_t *>(a.src_count + e1);
+                uint32_t *cp0 = reinterpret_cast<uint32_t *>(a.count + a.offset + e0);
+                uint32_t *cp1 = reinterpret_cast<uint32_t *>(a.count + a.offset + e1);
+                *cp0 += c0;
+                *cp1 += c1;
             }
         }
     }
@@ -1041,80 +1067,81 @@ sparse_merge_kernel(const SparseArgs a)
         }
         __syncthreads();
 
-        // finalize the tile: 8 consecutive parameters per lane
-        const int l0 = tid * VEC;
-        const int64_t e0 = t0 + l0;
-        float acc[VEC];
-        uint32_t W[VEC], cnt[VEC];
+        // finalize the tile: each lane takes the 4-parameter quads at 4 * tid
+        // and SP_TILE / 2 + 4 * tid, so the 16-byte stores of a wave cover
+        // whole cache lines
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            uint32_t wsum = 0, c = 0;
+        for (int h = 0; h < 2; ++h) {
+            const int lq = h * (SP_TILE / 2) + tid * 4;
+            const int64_t eq = t0 + lq;
+            float acc[4];
+            uint32_t W[4], cnt[4];
 #pragma unroll
-            for (int m = 0; m < MW; ++m) {
-                uint32_t bits = s_mask[m][l0 + j];
-                c += __popc(bits);
-                while (bits) {
-                    wsum += s_nk[m * 32 + __ffs(bits) - 1];
-                    bits &= bits - 1;
-                }
-                s_mask[m][l0 + j] = 0u;
-            }
-            W[j] = wsum;
-            cnt[j] = c;
-            acc[j] = s_acc[l0 + j];
-            s_acc[l0 + j] = 0.0f;
-        }
-        if (a.aligned && e0 + VEC <= t1) {
-            float base8[VEC];
-            io<DT_F32>::load8(a.base, e0, base8);
-            float r[VEC];
+            for (int j = 0; j < 4; ++j) {
+                uint32_t wsum = 0, c = 0;
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                if (W[j] > 0) {
-                    const float q = acc[j] / (a.zero_fill ? a.S_all : (float)W[j]);
-                    r[j] = a.mode == MODE_DELTAS ? base8[j] + q : q;
-                } else {
-                    r[j] = base8[j];
+                for (int m = 0; m < MW; ++m) {
+                    uint32_t bits = s_mask[m][lq + j];
+                    c += __popc(bits);
+                    while (bits) {
+                        wsum += s_nk[m * 32 + __ffs(bits) - 1];
+                        bits &= bits - 1;
+                    }
+                    s_mask[m][lq + j] = 0u;
                 }
+                W[j] = wsum;
+                cnt[j] = c;
+                acc[j] = s_acc[lq + j];
+                s_acc[lq + j] = 0.0f;
             }
-            io<DT_F32>::store8(a.out, e0, r);
-            if (a.counts) {
-                if (a.counts_u32) {
-                    u32x4 *cp = reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(a.counts) + e0);
-                    __builtin_nontemporal_store(u32x4{cnt[0], cnt[1], cnt[2], cnt[3]}, cp);
-                    __builtin_nontemporal_store(u32x4{cnt[4], cnt[5], cnt[6], cnt[7]}, cp + 1);
-                } else {
-                    u32x2 c8;
-                    c8.x = cnt[0] | (cnt[1] << 8) | (cnt[2] << 16) | (cnt[3] << 24);
-                    c8.y = cnt[4] | (cnt[5] << 8) | (cnt[6] << 16) | (cnt[7] << 24);
-                    __builtin_nontemporal_store(
-                        c8, reinterpret_cast<u32x2 *>(static_cast<uint8_t *>(a.counts) + e0));
-                }
-            }
-            if (a.wsum) {
-                u32x4 *wp = reinterpret_cast<u32x4 *>(a.wsum + e0);
-                __builtin_nontemporal_store(u32x4{W[0], W[1], W[2], W[3]}, wp);
-                __builtin_nontemporal_store(u32x4{W[4], W[5], W[6], W[7]}, wp + 1);
-            }
-        } else {
-            for (int j = 0; j < VEC; ++j) {
-                const int64_t e = e0 + j;
-                if (e < t1) {
-                    const float bv = a.base[e];
-                    float r = bv;
+            if (a.aligned && eq + 4 <= t1) {
+                float b4[4];
+                io<DT_F32>::load4(a.base, eq, b4);
+                float r[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
                     if (W[j] > 0) {
                         const float q = acc[j] / (a.zero_fill ? a.S_all : (float)W[j]);
-                        r = a.mode == MODE_DELTAS ? bv + q : q;
+                        r[j] = a.mode == MODE_DELTAS ? b4[j] + q : q;
+                    } else {
+                        r[j] = b4[j];
                     }
-                    a.out[e] = r;
-                    if (a.counts) {
-                        if (a.counts_u32)
-                            static_cast<uint32_t *>(a.counts)[e] = cnt[j];
-                        else
-                            static_cast<uint8_t *>(a.counts)[e] = (uint8_t)cnt[j];
+                }
+                __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]},
+                                            reinterpret_cast<f32x4 *>(a.out + eq));
+                if (a.counts) {
+                    if (a.counts_u32)
+                        __builtin_nontemporal_store(
+                            u32x4{cnt[0], cnt[1], cnt[2], cnt[3]},
+                            reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(a.counts) + eq));
+                    else
+                        __builtin_nontemporal_store(
+                            cnt[0] | (cnt[1] << 8) | (cnt[2] << 16) | (cnt[3] << 24),
+                            reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(a.counts) + eq));
+                }
+                if (a.wsum)
+                    __builtin_nontemporal_store(u32x4{W[0], W[1], W[2], W[3]},
+                                                reinterpret_cast<u32x4 *>(a.wsum + eq));
+            } else {
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t e = eq + j;
+                    if (e < t1) {
+                        const float bv = a.base[e];
+                        float r = bv;
+                        if (W[j] > 0) {
+                            const float q = acc[j] / (a.zero_fill ? a.S_all : (float)W[j]);
+                            r = a.mode == MODE_DELTAS ? bv + q : q;
+                        }
+                        a.out[e] = r;
+                        if (a.counts) {
+                            if (a.counts_u32)
+                                static_cast<uint32_t *>(a.counts)[e] = cnt[j];
+                            else
+                                static_cast<uint8_t *>(a.counts)[e] = (uint8_t)cnt[j];
+                        }
+                        if (a.wsum)
+                            a.wsum[e] = W[j];
                     }
-                    if (a.wsum)
-                        a.wsum[e] = W[j];
                 }
             }
         }
