@@ -81,6 +81,25 @@ template <> struct io<DT_F32> {
             reinterpret_cast<const f32x4 *>(static_cast<const float *>(p) + e));
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     }
+    // the 8 parameters as two quads at e0 and e1 (contiguous when e1 = e0 + 4)
+    static __device__ __forceinline__ raw load_raw2(const void *p, int64_t e0, int64_t e1)
+    {
+        const float *f = static_cast<const float *>(p);
+        return raw{__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(f + e0)),
+                   __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(f + e1))};
+    }
+    static __device__ __forceinline__ void load8_2(const void *p, int64_t e0, int64_t e1, float (&v)[VEC])
+    {
+        const raw r = load_raw2(p, e0, e1);
+        v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+        v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+    }
+    static __device__ __forceinline__ void store8_2(void *p, int64_t e0, int64_t e1, const float (&v)[VEC])
+    {
+        float *f = static_cast<float *>(p);
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(f + e0));
+        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(f + e1));
+    }
     static __device__ __forceinline__ float load1(const void *p, int64_t e)
     {
         return static_cast<const float *>(p)[e];
@@ -137,6 +156,22 @@ template <> struct io<DT_BF16> {
         v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
         v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
     }
+    // the 8 parameters as two quads at e0 and e1
+    static __device__ __forceinline__ raw load_raw2(const void *p, int64_t e0, int64_t e1)
+    {
+        const uint16_t *h = static_cast<const uint16_t *>(p);
+        const u32x2 a = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(h + e0));
+        const u32x2 b = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(h + e1));
+        return raw{u32x4{a.x, a.y, b.x, b.y}};
+    }
+    static __device__ __forceinline__ void load8_2(const void *p, int64_t e0, int64_t e1, float (&v)[VEC])
+    {
+        const raw r = load_raw2(p, e0, e1);
+        v[0] = bf16_lo(r.v.x); v[1] = bf16_hi(r.v.x);
+        v[2] = bf16_lo(r.v.y); v[3] = bf16_hi(r.v.y);
+        v[4] = bf16_lo(r.v.z); v[5] = bf16_hi(r.v.z);
+        v[6] = bf16_lo(r.v.w); v[7] = bf16_hi(r.v.w);
+    }
     static __device__ __forceinline__ float load1(const void *p, int64_t e)
     {
         return bf16_lo(static_cast<const uint16_t *>(p)[e]);
@@ -164,10 +199,11 @@ __device__ __forceinline__ int64_t grid_threads() { return (int64_t)gridDim.x * 
 // parameters.  In a full run of 256 steps these are quads l and l + 256 of
 // the run (l = v mod 256), so the 16-byte accesses of a wave are contiguous
 // and each of its store instructions writes 1 KiB of whole cache lines; in
-// the last, short run they are quads 2l and 2l + 1.  Two 16-byte stores per
-// lane 32 bytes apart would instead leave each line half written by each
-// instruction, and a non-temporal line evicted in between reaches HBM twice
-// (11% more written bytes, measured, in a read-modify-write of fp32 sums).
+// the last, short run they are quads 2l and 2l + 1.  With two 16-byte
+// stores per lane 32 bytes apart instead, each store instruction of a wave
+// leaves every line it touches half written; such stores were measured to
+// move 11% more bytes to HBM than written (the read-modify-write of fp32
+// sums), and to run 6-12% slower.
 __device__ __forceinline__ void quad_pair(int64_t v, int64_t nvec, int64_t &e0, int64_t &e1)
 {
     const int64_t run = v & ~(int64_t)255;
@@ -179,18 +215,25 @@ __device__ __forceinline__ void quad_pair(int64_t v, int64_t nvec, int64_t &e0, 
 
 // ================================================================ resident dense
 
-// One pass over K client buffers: each lane owns 8 consecutive parameters per
-// step, issues the 16-byte loads of every client (KC of them when the client
-// count is a compile-time constant KC > 0; batches of -KC clients for a
-// client count known at run time) before its FMAs, then writes the 8 results
-// with one non-temporal store.
+// One pass over K client buffers: each lane owns 8 parameters per step (8
+// consecutive ones for a bf16 output, two quads 1024 apart for an fp32 one),
+// issues the loads of every client (KC of them when the client count is a
+// compile-time constant KC > 0; batches of -KC clients for a client count
+// known at run time) before its FMAs, then writes the 8 results with
+// non-temporal stores.
 template <int XDT, int ODT, int BDT, int MODE, int KC>
 __global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64_t nvec)
 {
+    // an fp32 output is written as two quads per lane (whole-line stores);
+    // a bf16 output's 8 values are one contiguous 16-byte store
+    constexpr bool SPLIT = ODT == DT_F32;
     constexpr int GB = KC < 0 ? -KC : 8;
     const int K = KC > 0 ? KC : a.K;
     for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
         const int64_t e = v * VEC;
+        int64_t e0 = e, e1 = e + 4;
+        if constexpr (SPLIT)
+            quad_pair(v, nvec, e0, e1);
         float acc[VEC];
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
@@ -199,7 +242,7 @@ __global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64
             typename io<XDT>::raw xr[KC];
 #pragma unroll
             for (int k = 0; k < KC; ++k)
-                xr[k] = io<XDT>::load_raw(a.x[k], e);
+                xr[k] = SPLIT ? io<XDT>::load_raw2(a.x[k], e0, e1) : io<XDT>::load_raw(a.x[k], e);
 #pragma unroll
             for (int k = 0; k < KC; ++k)
                 io<XDT>::fma8(xr[k], a.w[k], acc);
@@ -209,7 +252,8 @@ __global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64
 #pragma unroll
                 for (int k = 0; k < GB; ++k)
                     if (k0 + k < K)
-                        xr[k] = io<XDT>::load_raw(a.x[k0 + k], e);
+                        xr[k] = SPLIT ? io<XDT>::load_raw2(a.x[k0 + k], e0, e1)
+                                  : io<XDT>::load_raw(a.x[k0 + k], e);
 #pragma unroll
                 for (int k = 0; k < GB; ++k)
                     if (k0 + k < K)
@@ -219,7 +263,10 @@ __global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64
         float r[VEC];
         if constexpr (MODE == MODE_DELTAS) {
             float b[VEC];
-            io<BDT>::load8(a.base, e, b);
+            if constexpr (SPLIT)
+                io<BDT>::load8_2(a.base, e0, e1, b);
+            else
+                io<BDT>::load8(a.base, e, b);
 #pragma unroll
             for (int j = 0; j < VEC; ++j)
                 r[j] = b[j] + acc[j] / a.S;
@@ -228,7 +275,10 @@ __global__ __launch_bounds__(256) void dense_vec_kernel(const DenseArgs a, int64
             for (int j = 0; j < VEC; ++j)
                 r[j] = acc[j] / a.S;
         }
-        io<ODT>::store8(a.out, e, r);
+        if constexpr (SPLIT)
+            io<ODT>::store8_2(a.out, e0, e1, r);
+        else
+            io<ODT>::store8(a.out, e, r);
     }
 }
 
@@ -806,27 +856,38 @@ __device__ __forceinline__ float finalize_one(float acc, uint32_t W, float S, fl
 template <int BDT, int ODT, int MODE, int PARTIAL>
 __global__ __launch_bounds__(256) void stream_finalize_vec_kernel(const FinalizeArgs a, int64_t nvec)
 {
+    // an fp32 output is written as two quads per lane (whole-line stores);
+    // a bf16 output's 8 values are one contiguous 16-byte store
+    constexpr bool SPLIT = ODT == DT_F32;
     for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
-        const int64_t e = v * VEC;
-        const f32x4 *ap = reinterpret_cast<const f32x4 *>(a.acc + e);
-        const f32x4 lo = __builtin_nontemporal_load(ap);
-        const f32x4 hi = __builtin_nontemporal_load(ap + 1);
+        int64_t e0 = v * VEC, e1 = e0 + 4;
+        if constexpr (SPLIT)
+            quad_pair(v, nvec, e0, e1);
+        const f32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.acc + e0));
+        const f32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.acc + e1));
         const float acc[VEC] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         uint32_t W[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
         if constexpr (PARTIAL) {
-            const u32x4 *wp = reinterpret_cast<const u32x4 *>(a.wsum + e);
-            const u32x4 w0 = wp[0], w1 = wp[1];
+            const u32x4 w0 = *reinterpret_cast<const u32x4 *>(a.wsum + e0);
+            const u32x4 w1 = *reinterpret_cast<const u32x4 *>(a.wsum + e1);
             W[0] = w0.x; W[1] = w0.y; W[2] = w0.z; W[3] = w0.w;
             W[4] = w1.x; W[5] = w1.y; W[6] = w1.z; W[7] = w1.w;
         }
         float b[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (MODE == MODE_DELTAS || PARTIAL)
-            io<BDT>::load8(a.base, e, b);
+        if (MODE == MODE_DELTAS || PARTIAL) {
+            if constexpr (SPLIT)
+                io<BDT>::load8_2(a.base, e0, e1, b);
+            else
+                io<BDT>::load8(a.base, e0, b);
+        }
         float r[VEC];
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
             r[j] = finalize_one<BDT, ODT, MODE, PARTIAL>(acc[j], W[j], a.S, b[j], a.zero_fill);
-        io<ODT>::store8(a.out, e, r);
+        if constexpr (SPLIT)
+            io<ODT>::store8_2(a.out, e0, e1, r);
+        else
+            io<ODT>::store8(a.out, e0, r);
     }
 }
 
