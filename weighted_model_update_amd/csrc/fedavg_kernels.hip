@@ -905,21 +905,21 @@ __global__ __launch_bounds__(256) void stream_finalize_scalar_kernel(const Final
 
 // ================================================================ sparse merge
 
-// First position in ix[0, n) whose index is >= target, for a list sorted
-// ascending over [0, N).  Every probe lies inside the bracket [lo, hi) that
-// holds the answer, so the choice of probe changes only how fast it is found:
-// the first SPARSE_INTERP_STEPS probes interpolate between the index values
-// known at the bracket's ends (top-k supports are close to uniform, so a few
-// probes land next to the answer), the rest bisect, which bounds the probes
-// for any list.  An unsorted list gives some position in [0, n]; the merge
-// reports such lists whatever the offsets are.
+// First position in ix[lo, hi) whose index is >= target (hi when there is
+// none), for a list sorted ascending whose values in [lo, hi) lie above vlo
+// and at most vhi (a whole list over [0, N): lo = 0, hi = n, vlo = -1,
+// vhi = N).  Every probe lies inside the bracket that holds the answer, so
+// the choice of probe changes only how fast it is found: the first
+// SPARSE_INTERP_STEPS probes interpolate between the index values known at
+// the bracket's ends (top-k supports are close to uniform, so a few probes
+// land next to the answer), the rest bisect, which bounds the probes for any
+// list.  An unsorted list gives some position in [lo, hi]; the merge reports
+// such lists whatever the offsets are.
 constexpr int SPARSE_INTERP_STEPS = 6;
 
-__device__ __forceinline__ int64_t sparse_lower_bound(const int64_t *ix, int64_t n, int64_t target,
-                                                      int64_t N)
+__device__ __forceinline__ int64_t sparse_lower_bound(const int64_t *ix, int64_t lo, int64_t hi,
+                                                      int64_t target, int64_t vlo, int64_t vhi)
 {
-    int64_t lo = 0, hi = n;
-    int64_t vlo = -1, vhi = N; // index values just outside the bracket (when sorted)
     for (int step = 0; lo < hi; ++step) {
         int64_t mid = lo + (hi - lo) / 2;
         if (step < SPARSE_INTERP_STEPS && vhi > vlo && target > vlo && target <= vhi) {
@@ -942,16 +942,44 @@ __device__ __forceinline__ int64_t sparse_lower_bound(const int64_t *ix, int64_t
 // For every client k and range boundary b (0..NB), the first position of k's
 // sorted index list at or after parameter b*R.  Also flags lists that hold
 // negative indices or indices >= N (those fall outside every range).
+//
+// A wave takes 64 consecutive boundaries of one client: its first and last
+// lanes search the whole list for the outer two, and the other lanes search
+// only between those two answers, where every index lies in [first target,
+// last target).  The inner searches start within a few hundred positions of
+// their answers, so a wave costs about half the random line reads of 64
+// independent whole-list searches (the kernel is bound by those reads).
 __global__ __launch_bounds__(256) void sparse_offsets_kernel(const SparseArgs a)
 {
-    const int64_t total = (int64_t)a.K * (a.NB + 1);
-    for (int64_t t = global_tid(); t < total; t += grid_threads()) {
-        const int k = (int)(t / (a.NB + 1));
-        const int b = (int)(t % (a.NB + 1));
-        const int64_t target = min((int64_t)b * a.R, a.N);
-        const int64_t lo = sparse_lower_bound(a.idx[k], a.nnz[k], target, a.N);
-        a.offs[t] = lo;
-        if ((b == 0 && lo > 0) || (b == a.NB && lo < a.nnz[k]))
+    const int64_t nbnd = (int64_t)a.NB + 1;
+    const int64_t wpc = (nbnd + 63) / 64; // waves per client
+    const int64_t waves = (int64_t)a.K * wpc;
+    const int lane = threadIdx.x & 63;
+    for (int64_t w = global_tid() / 64; w < waves; w += grid_threads() / 64) {
+        const int k = (int)(w / wpc);
+        const int64_t b0 = (w % wpc) * 64;
+        const int64_t b1 = min(b0 + 63, nbnd - 1);
+        const int64_t *ix = a.idx[k];
+        const int64_t n = a.nnz[k];
+        const int64_t t0 = min(b0 * a.R, a.N), t1 = min(b1 * a.R, a.N);
+        int64_t edge = 0;
+        if (lane == 0)
+            edge = sparse_lower_bound(ix, 0, n, t0, -1, a.N);
+        else if (lane == 63)
+            edge = sparse_lower_bound(ix, 0, n, t1, -1, a.N);
+        const int64_t p0 = __shfl(edge, 0, 64), p1 = __shfl(edge, 63, 64);
+        const int64_t b = b0 + lane;
+        if (b > b1)
+            continue;
+        int64_t lo;
+        if (b == b0)
+            lo = p0;
+        else if (b == b1)
+            lo = p1;
+        else
+            lo = sparse_lower_bound(ix, p0, max(p0, p1), min(b * a.R, a.N), t0 - 1, t1);
+        a.offs[(int64_t)k * nbnd + b] = lo;
+        if ((b == 0 && lo > 0) || (b == a.NB && lo < n))
             *a.err = FA_ERR_INDEX;
     }
 }
@@ -1773,8 +1801,8 @@ template <int TILE, int THREADS> static void merge_launch(const SparseArgs &a, h
 
 hipError_t launch_sparse(const SparseArgs &a, hipStream_t s)
 {
-    const int64_t total = (int64_t)a.K * (a.NB + 1);
-    sparse_offsets_kernel<<<grid_for(total, 256, 0), 256, 0, s>>>(a);
+    const int64_t lanes = (int64_t)a.K * (((int64_t)a.NB + 64) / 64) * 64;
+    sparse_offsets_kernel<<<grid_for(lanes, 256, 0), 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
