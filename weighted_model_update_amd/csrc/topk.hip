@@ -480,8 +480,12 @@ __global__ __launch_bounds__(TK_SELECT_THREADS) void topk_sample_select_kernel(T
             st->khi = has_hi ? (bh << TK_TOP_SHIFT) | ((uint32_t)max(dh, 0) << TK_SUB_SHIFT) |
                                    ((1u << TK_SUB_SHIFT) - 1u)
                              : 0x7FFFFFFFu;
-            st->klo = (bl << TK_TOP_SHIFT) | ((uint32_t)max(dl, 0) << TK_SUB_SHIFT);
-            st->ranged = ok && dh >= 0 && dl >= 0;
+            const uint32_t klo = (bl << TK_TOP_SHIFT) | ((uint32_t)max(dl, 0) << TK_SUB_SHIFT);
+            st->klo = klo;
+            // a range down to key 0 (an update mostly of zeros) takes the
+            // full path: the split reads positions past N as key 0 and
+            // relies on klo > 0 never to choose them
+            st->ranged = ok && dh >= 0 && dl >= 0 && klo > 0u;
         }
         for (int b = t; b < 2 * TK_MAX_BINS; b += blockDim.x)
             w.hist[b] = 0ull;
@@ -514,119 +518,199 @@ template <int DT> __device__ __forceinline__ uint32_t stage_bits(const TopkWs &w
 // staging segment -- both in index order.  Segments are reserved in the
 // tile's region (tile mod TK_REGIONS) with one atomic each; a region that
 // runs out sets `fov` and the check sends the call down the full path.
-// Resident waves per SIMD the split is compiled for: 6 fits fp32 tiles with a
-// 12-byte spill and is faster; bf16 tiles spill heavily above 5.
-template <int DT> constexpr int split_waves() { return DT == DT_F32 ? 6 : 5; }
+//
+// Wave w of the workgroup takes the tile's elements [w S, (w + 1) S),
+// S = TK_TILE / TT_WAVES, as SPLIT_COLS columns of 64 consecutive elements,
+// lane l holding element l of each column.  Index order is then column
+// order, lane order inside a column, so an element's rank among the chosen
+// ones is a wave-uniform running count plus the number of chosen lanes below
+// it in its column's ballot: a few instructions per column of 64 elements,
+// where ranking each lane's own consecutive elements one after another took
+// a divergent branch per element.
+constexpr int SPLIT_COLS = TK_TILE / TT_THREADS;
+constexpr int SPLIT_SPAN = TK_TILE / TT_WAVES;
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Raw buffer over `bytes` bytes from p: a load past them returns 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t split_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+constexpr int SPLIT_CAND = 1024; // candidates a tile gathers in LDS (more go out directly)
 
 template <int DT>
-__global__ __launch_bounds__(TT_THREADS, split_waves<DT>()) void topk_split_range_kernel(const void *x, int64_t N,
-                                                                      bool vec_ok, int64_t nt,
+__device__ __forceinline__ void split_tile(const void *x, int64_t tile, int64_t tile0, uint32_t lim,
+                                           uint32_t lo, uint32_t hi, const TopkWs &w, bool staging,
+                                           uint32_t *s_ge, uint32_t *s_in,
+                                           unsigned long long *s_seg, uint32_t *s_bits,
+                                           uint16_t *s_loc, uint32_t *s_ckey, uint16_t *s_cloc)
+{
+    constexpr uint32_t EB = DT == DT_F32 ? 4 : 2; // bytes per element
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t first = (uint32_t)wave * SPLIT_SPAN + lane; // local position in column 0
+    // elements past N read as 0 through the buffer's range: key 0 is below
+    // lo (> 0 on this path), so they are never chosen
+    const auto xr = split_rsrc(static_cast<const char *>(x) + tile0 * EB, lim * EB);
+    uint32_t b[SPLIT_COLS];
+#pragma unroll
+    for (int c = 0; c < SPLIT_COLS; ++c) {
+        if constexpr (DT == DT_F32)
+            b[c] = __builtin_amdgcn_raw_buffer_load_b32(xr, (int)(first * EB), c * 64 * EB, 2);
+        else
+            b[c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(xr, (int)(first * EB), c * 64 * EB, 2) << 16;
+    }
+    uint32_t n_ge = 0, n_in = 0; // this wave's counts (wave-uniform)
+#pragma unroll
+    for (int c = 0; c < SPLIT_COLS; ++c) {
+        const uint32_t key = key_of_bits(b[c]);
+        n_ge += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key >= lo));
+        n_in += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(key >= lo && key <= hi));
+    }
+    if (lane == 0) {
+        s_ge[wave] = n_ge;
+        s_in[wave] = n_in;
+    }
+    __syncthreads();
+    uint32_t t_ge = 0, t_in = 0, rt = 0, rc = 0;
+#pragma unroll
+    for (int v = 0; v < TT_WAVES; ++v) {
+        const uint32_t g = s_ge[v], i = s_in[v];
+        t_ge += g;
+        t_in += i;
+        rt += v < wave ? g : 0u; // ranks of this wave's first chosen elements
+        rc += v < wave ? i : 0u;
+    }
+    // wave-uniform, kept in scalar registers
+    t_ge = __builtin_amdgcn_readfirstlane(t_ge);
+    t_in = __builtin_amdgcn_readfirstlane(t_in);
+    rt = __builtin_amdgcn_readfirstlane(rt);
+    rc = __builtin_amdgcn_readfirstlane(rc);
+    if (threadIdx.x == 0) {
+        // The segments are reserved while the tile ranks its entries into
+        // LDS: the atomic's round trip overlaps that pass, and only the
+        // copy-out below needs the reserved offsets.  One atomic reserves
+        // both segments; the staging count runs with or without staging: the
+        // check reads the keys >= klo from it.
+        const int region = (int)(tile % TK_REGIONS);
+        const unsigned long long o =
+            t_ge ? atomicAdd(&w.rcnt[region * TK_CSTRIDE], ((unsigned long long)t_ge << 32) | t_in) : 0ull;
+        const unsigned long long ot = o >> 32, oc = o & 0xFFFFFFFFull;
+        const bool tfits = !staging || (int64_t)(ot + t_ge) <= w.tcap;
+        const bool cfits = (int64_t)(oc + t_in) <= w.rcap;
+        if (!tfits || !cfits)
+            w.st->fov = 1u;
+        s_seg[0] = staging && tfits ? (unsigned long long)region * w.tcap + ot : ~0ull;
+        s_seg[1] = cfits ? (unsigned long long)region * w.rcap + oc : ~0ull;
+        w.def[tile] = t_ge - t_in;
+        w.ccnt[tile] = t_in;
+        w.coff[tile] = (unsigned long long)region * w.rcap + oc;
+        w.tcnt[tile] = t_ge;
+        w.toff[tile] = staging ? (unsigned long long)region * w.tcap + ot : 0ull;
+    }
+    // the ranking pass derives keys and tests from the raw bits again rather
+    // than keeping the count pass's per-column results live across the
+    // barrier (64 more registers)
+#pragma unroll
+    for (int c = 0; c < SPLIT_COLS; ++c)
+        asm volatile("" : "+v"(b[c]));
+#pragma unroll
+    for (int c = 0; c < SPLIT_COLS; ++c) {
+        const uint32_t key = key_of_bits(b[c]);
+        const bool ge = key >= lo;
+        const bool in = ge && key <= hi;
+        const uint64_t mg = __builtin_amdgcn_ballot_w64(ge), mi = __builtin_amdgcn_ballot_w64(in);
+        // formed here from an opaque copy: kept for all columns (they do
+        // not change from tile to tile) they would hold 32 registers
+        uint32_t local = first;
+        asm volatile("" : "+v"(local));
+        local += c * 64;
+        if (ge) {
+            const uint32_t r = rt + lanes_below(mg);
+            if (r < TK_STAGE) {
+                s_bits[r] = b[c];
+                s_loc[r] = (uint16_t)local;
+            }
+        }
+        if (in) {
+            const uint32_t r = rc + lanes_below(mi);
+            if (r < SPLIT_CAND) {
+                s_ckey[r] = key;
+                s_cloc[r] = (uint16_t)local;
+            }
+        }
+        rt += (uint32_t)__popcll(mg);
+        rc += (uint32_t)__popcll(mi);
+    }
+    __syncthreads();
+    const unsigned long long toff = s_seg[0], coff = s_seg[1];
+    if (toff != ~0ull) {
+        const uint32_t n = min((uint32_t)TK_STAGE, t_ge);
+        for (uint32_t i = threadIdx.x; i < n; i += TT_THREADS)
+            stage_put<DT>(w, toff + i, s_bits[i], s_loc[i]);
+    }
+    if (coff != ~0ull) {
+        const uint32_t n = min((uint32_t)SPLIT_CAND, t_in);
+        for (uint32_t i = threadIdx.x; i < n; i += TT_THREADS)
+            w.cand[coff + i] = u32x2{s_ckey[i], (uint32_t)s_cloc[i]};
+    }
+    // A tile with more entries than LDS holds (over a quarter of it staged,
+    // or an eighth of it candidates) writes the rest straight out.
+    if ((t_ge > TK_STAGE && toff != ~0ull) || (t_in > SPLIT_CAND && coff != ~0ull)) {
+        uint32_t qt = __builtin_amdgcn_readfirstlane(rt - n_ge), qc = __builtin_amdgcn_readfirstlane(rc - n_in);
+#pragma unroll
+        for (int c = 0; c < SPLIT_COLS; ++c)
+            asm volatile("" : "+v"(b[c]));
+#pragma unroll
+        for (int c = 0; c < SPLIT_COLS; ++c) {
+            const uint32_t key = key_of_bits(b[c]);
+            const bool ge = key >= lo;
+            const bool in = ge && key <= hi;
+            const uint64_t mg = __builtin_amdgcn_ballot_w64(ge), mi = __builtin_amdgcn_ballot_w64(in);
+            uint32_t local = first;
+            asm volatile("" : "+v"(local));
+            local += c * 64;
+            if (ge && toff != ~0ull) {
+                const uint32_t r = qt + lanes_below(mg);
+                if (r >= TK_STAGE)
+                    stage_put<DT>(w, toff + r, b[c], local);
+            }
+            if (in && coff != ~0ull) {
+                const uint32_t r = qc + lanes_below(mi);
+                if (r >= SPLIT_CAND)
+                    w.cand[coff + r] = u32x2{key, local};
+            }
+            qt += (uint32_t)__popcll(mg);
+            qc += (uint32_t)__popcll(mi);
+        }
+    }
+    __syncthreads(); // the LDS arrays are reused by the next tile
+}
+
+template <int DT>
+__global__ __launch_bounds__(TT_THREADS) void topk_split_range_kernel(const void *x, int64_t N, int64_t nt,
                                                                       TopkWs w, bool staging)
 {
-    using TL = Tile<DT>;
-    __shared__ uint32_t s_tot[TL::ROUNDS][TT_WAVES];
-    __shared__ u32x2 s_ent[TK_STAGE];
-    __shared__ unsigned long long s_toff, s_coff;
+    __shared__ uint32_t s_ge[TT_WAVES], s_in[TT_WAVES];
+    __shared__ unsigned long long s_seg[2];
+    // values and positions apart: a 64-bit pair per entry made the compiler
+    // hold each value in the low half of a register pair
+    __shared__ uint32_t s_bits[TK_STAGE];
+    __shared__ uint16_t s_loc[TK_STAGE];
+    __shared__ uint32_t s_ckey[SPLIT_CAND];
+    __shared__ uint16_t s_cloc[SPLIT_CAND];
     if (!w.st->ranged)
         return;
     const uint32_t lo = w.st->klo, hi = w.st->khi;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
         const int64_t tile0 = tile * TK_TILE;
-        TL tl;
-        tl.load(x, N, vec_ok, tile0);
-        // per round: (keys >= lo) << 16 | (keys in [lo, hi]); a tile holds at
-        // most TK_TILE < 2^16 of either, so the fields never carry
-        uint32_t exw[TL::ROUNDS];
-#pragma unroll
-        for (int j = 0; j < TL::ROUNDS; ++j) {
-            uint32_t v = 0;
-#pragma unroll
-            for (int q = 0; q < TL::V; ++q) {
-                const uint32_t key = key_of_bits(tl.b[j][q]);
-                v += key >= lo ? ((1u << 16) | (key <= hi ? 1u : 0u)) : 0u;
-            }
-            const uint32_t sc = wave_inclusive_scan(v);
-            if (lane == 63)
-                s_tot[j][wave] = sc;
-            exw[j] = sc - v; // this lane's exclusive prefix inside its wave
-        }
-        __syncthreads();
-        uint32_t tot = 0;
-#pragma unroll
-        for (int j = 0; j < TL::ROUNDS; ++j)
-#pragma unroll
-            for (int v = 0; v < TT_WAVES; ++v)
-                tot += s_tot[j][v];
-        // padding (key 0) meets key >= lo only when lo is 0, and then also
-        // key <= hi
-        const uint32_t pad_in = lo == 0u ? tl.pad() : 0u;
-        const uint32_t n_ge = (tot >> 16) - pad_in, n_cand = (tot & 0xFFFFu) - pad_in;
-        if (threadIdx.x == 0) {
-            const int region = (int)(tile % TK_REGIONS);
-            // one atomic reserves both segments; the staging count runs with
-            // or without staging: the check reads the keys >= klo from it
-            const unsigned long long o =
-                n_ge ? atomicAdd(&w.rcnt[region * TK_CSTRIDE], ((unsigned long long)n_ge << 32) | n_cand) : 0ull;
-            const unsigned long long ot = o >> 32, oc = o & 0xFFFFFFFFull;
-            const bool tfits = !staging || (int64_t)(ot + n_ge) <= w.tcap;
-            const bool cfits = (int64_t)(oc + n_cand) <= w.rcap;
-            if (!tfits || !cfits)
-                w.st->fov = 1u;
-            s_toff = staging && tfits ? (unsigned long long)region * w.tcap + ot : ~0ull;
-            s_coff = cfits ? (unsigned long long)region * w.rcap + oc : ~0ull;
-            w.def[tile] = n_ge - n_cand;
-            w.ccnt[tile] = n_cand;
-            w.coff[tile] = (unsigned long long)region * w.rcap + oc;
-            w.tcnt[tile] = n_ge;
-            w.toff[tile] = staging ? (unsigned long long)region * w.tcap + ot : 0ull;
-        }
-        __syncthreads();
-        const unsigned long long toff = s_toff, coff = s_coff;
-        tl.reuse();
-        uint32_t carry = 0;
-#pragma unroll
-        for (int j = 0; j < TL::ROUNDS; ++j) {
-            uint32_t before = 0, round_total = 0;
-#pragma unroll
-            for (int v = 0; v < TT_WAVES; ++v) {
-                const uint32_t t = s_tot[j][v];
-                before += v < wave ? t : 0u;
-                round_total += t;
-            }
-            const uint32_t run = carry + before + exw[j];
-            carry += round_total;
-            uint32_t rt = run >> 16, rc = run & 0xFFFFu;
-#pragma unroll
-            for (int q = 0; q < TL::V; ++q) {
-                const uint32_t bits = tl.b[j][q];
-                const uint32_t key = key_of_bits(bits);
-                if (key < lo)
-                    continue;
-                const uint32_t local = tl.local(j, q);
-                if (toff != ~0ull && rt < n_ge) { // padding ranks last: rt >= n_ge
-                    if (rt < TK_STAGE)
-                        s_ent[rt] = u32x2{bits, local};
-                    else
-                        stage_put<DT>(w, toff + rt, bits, local);
-                }
-                ++rt;
-                if (key <= hi) {
-                    if (coff != ~0ull && rc < n_cand)
-                        w.cand[coff + rc] = u32x2{key, local};
-                    ++rc;
-                }
-            }
-        }
-        __syncthreads();
-        if (toff != ~0ull) {
-            const int n = (int)min((uint32_t)TK_STAGE, n_ge);
-            for (int i = threadIdx.x; i < n; i += TT_THREADS) {
-                const u32x2 e = s_ent[i];
-                stage_put<DT>(w, toff + i, e.x, e.y);
-            }
-        }
-        __syncthreads(); // s_tot and s_ent are reused by the next tile
+        const int64_t left = N - tile0;
+        split_tile<DT>(x, tile, tile0, left < TK_TILE ? (uint32_t)left : (uint32_t)TK_TILE, lo, hi, w, staging,
+                       s_ge, s_in, s_seg, s_bits, s_loc, s_ckey, s_cloc);
     }
 }
 
@@ -1310,7 +1394,7 @@ hipError_t topk_run(const void *x, int64_t N, int64_t k, int64_t *idx_out, float
         topk_sample_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 1, plan.has_hi, plan.r_hi, plan.r_lo);
         topk_sample_hist_kernel<DT><<<sg, TK_THREADS, 0, s>>>(x, plan.vec_units, plan.units, plan.mu, w, 2, plan.has_hi);
         topk_sample_select_kernel<<<1, TK_SELECT_THREADS, 0, s>>>(w, 2, plan.has_hi, plan.r_hi, plan.r_lo);
-        topk_split_range_kernel<DT><<<work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w, staging);
+        topk_split_range_kernel<DT><<<work_grid, TT_THREADS, 0, s>>>(x, N, nt, w, staging);
         topk_check_kernel<<<1, TK_REGIONS, 0, s>>>(w, k, DT == DT_BF16 ? 16 : 0);
     }
     // Full path: digit 1 (key bits 30..20) from the whole input, the split,
