@@ -365,14 +365,16 @@ int sparse_masked_accumulate(int K, const int64_t *const *idx, const float *cons
  * of FA_SPARSE_SCRATCH_BYTES per GPU, held until the process ends.  The
  * call allocates and frees nothing.  It needs 256 + 8 * Kc * (ranges + 1)
  * bytes of that array, Kc the clients with n_k > 0 and nnz > 0 and ranges
- * the parameter ranges the merge uses (at most 65536: any N with Kc <= 31);
+ * the parameter ranges the merge uses (by default N / 8192 for N beyond
+ * about 3.4e7, 122,071 at N = 10^9, so up to 34 clients there; at most
+ * 2^19, which every N admits for Kc <= 7);
  * beyond FA_SPARSE_SCRATCH_BYTES it returns FA_ERR_RANGE before any device
  * work.  All calls on one GPU share its array: calls that overlap in time
  * on one GPU (other streams, other threads) race on it and must be
  * serialized by the caller.  The flag is reset by each call; the offsets
  * are rewritten by each call before they are read.
  */
-#define FA_SPARSE_SCRATCH_BYTES (16ll << 20)
+#define FA_SPARSE_SCRATCH_BYTES (32ll << 20)
 int sparse_masked_accumulate_noalloc(int K, const int64_t *const *idx, const float *const *val,
                                      const int64_t *nnz, const int64_t *n, int64_t N, fa_mode mode,
                                      const float *base, float *out, void *counts,
@@ -499,8 +501,10 @@ typedef enum {
                                           per workgroup, which sets the grid
                                           (default 2048) */
     FA_OPT_SPARSE_BLOCKS = 3,          /* sparse merge: parameter ranges, i.e.
-                                          workgroups (default 0: 65536, fewer
-                                          when N is small; max 65536) */
+                                          workgroups (default 0: ranges of 4
+                                          tiles, but at least 4096 ranges while
+                                          there are that many tiles, at most
+                                          2^19; max 2^19) */
     FA_OPT_RESIDENT_PER_CU = 4,        /* resident dense kernel: workgroups of
                                           256 threads resident per CU
                                           (default 3; 0 = hardware limit) */

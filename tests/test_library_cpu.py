@@ -64,7 +64,7 @@ def test_host_side_argument_errors_need_no_device():
                                         (ctypes.c_int64 * 1)(1), 100, 1, P(1 << 22), P(1 << 23), None, 0,
                                         None, P(1 << 24), 8, None, None) == -8
     assert lib.fedavg_set_option(99, 1) == -1
-    assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, 70000) == -3
+    assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, (1 << 19) + 1) == -3
     assert lib.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 2) == -3
     b = ctypes.c_size_t(0)
     assert lib.topk_workspace_size(0, 100, 101, ctypes.byref(b)) == -3   # k > N
@@ -106,7 +106,8 @@ def test_workspace_sizes_do_not_depend_on_the_number_of_clients():
     assert ws == 4 * 10 ** 6 and cnt == 10 ** 6 and stag2 > stag
     with pytest.raises(fa.FedAvgError):
         fa.fedavg_workspace_size(10, 0, 0, 2)
-    assert fa.sparse_workspace_size(20, 10 ** 9) < 16 << 20
+    # one list offset per client and range boundary, at most 2^19 ranges
+    assert fa.sparse_workspace_size(20, 10 ** 9) <= 256 + 20 * ((1 << 19) + 1) * 8
     assert fa.sparse_workspace_size(20, 4096) < 2048
     # the value sum keeps one fp64 per tile of 8192 elements
     assert [fa.fedavg_sum_workspace_size(n) for n in (0, 1, 8192, 8193, 10 ** 9)] == \

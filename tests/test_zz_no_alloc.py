@@ -68,9 +68,10 @@ def test_noalloc_reports_a_bad_list_then_recovers():
 
 
 def test_noalloc_rejects_offsets_beyond_the_scratch():
-    # 40 contributing clients over 65,536 ranges need 40 * 65,537 * 8 bytes of
-    # offsets, more than the 16 MiB scratch: refused before any device work
-    N, K = 65_536 * 2048, 40
+    # 40 contributing clients over the 131,072 ranges of 2^30 parameters need
+    # 40 * 131,073 * 8 bytes of offsets, more than the 32 MiB scratch:
+    # refused before any device work
+    N, K = 1 << 30, 40
     base = torch.zeros(N, dtype=torch.float32, device="cuda")
     out = torch.empty_like(base)
     d_idx = [torch.tensor([k], dtype=torch.int64, device="cuda") for k in range(K)]
