@@ -1156,72 +1156,114 @@ __global__ __launch_bounds__(256) void topk_scan_down_kernel(int64_t nt, TopkWs 
 // in LDS.  Small workgroups with many entries per thread keep more tiles,
 // and so more loads, in flight per CU.
 constexpr int TW_THREADS = 128;
+constexpr int TW_TILES = 2; // tiles a workgroup of the staged write takes at once
 constexpr int TW_WAVES = TW_THREADS / 64;
 constexpr int TW_ROUNDS = 8;
 
+// One chunk of up to TW_ROUNDS * TW_THREADS staged entries of a tile,
+// loaded (ent, entries at or past n read as key 0), ranked and written.
+// `carry` holds the packed counts of the tile's entries before the chunk.
+template <int DT>
+__device__ __forceinline__ void write_staged_chunk(const u32x2 (&ent)[TW_ROUNDS], uint32_t c0, uint32_t n,
+                                                   uint32_t T, uint32_t tk, int64_t base, int64_t tile0,
+                                                   int64_t k_out, int64_t *idx_out, float *val_out,
+                                                   uint32_t (*s_tot)[TW_WAVES], uint32_t &carry)
+{
+    constexpr int R = TW_ROUNDS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t exw[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
+        const uint32_t key = key_of_bits(ent[i].x);
+        const uint32_t v = p < n ? (key > T ? (1u << 16) : (key == T ? 1u : 0u)) : 0u;
+        const uint32_t sc = wave_inclusive_scan(v);
+        if (lane == 63)
+            s_tot[i][wave] = sc;
+        exw[i] = sc - v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        uint32_t before = 0, round_total = 0;
+#pragma unroll
+        for (int v = 0; v < TW_WAVES; ++v) {
+            const uint32_t t = s_tot[i][v];
+            before += v < wave ? t : 0u;
+            round_total += t;
+        }
+        const uint32_t run = carry + before + exw[i];
+        carry += round_total;
+        const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
+        const uint32_t key = key_of_bits(ent[i].x);
+        if (p >= n || key < T)
+            continue;
+        const uint32_t gt_before = run >> 16, eq_before = run & 0xFFFFu;
+        if (key == T && eq_before >= tk)
+            continue;
+        const int64_t r = base + gt_before + min(eq_before, tk);
+        if (r < k_out) { // keeps inconsistent counts from writing out of range
+            idx_out[r] = tile0 + ent[i].y;
+            val_out[r] = __uint_as_float(ent[i].x);
+        }
+    }
+    __syncthreads(); // s_tot is reused by the next chunk
+}
+
+template <int DT>
+__device__ __forceinline__ void load_staged_chunk(const TopkWs &w, uint64_t seg, uint32_t c0, uint32_t n,
+                                                  u32x2 (&ent)[TW_ROUNDS])
+{
+#pragma unroll
+    for (int i = 0; i < TW_ROUNDS; ++i) {
+        const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
+        ent[i] = p < n ? u32x2{stage_bits<DT>(w, seg + p), (uint32_t)w.sloc[seg + p]} : u32x2{0u, 0u};
+    }
+}
+
+// Each workgroup writes TW_TILES consecutive tiles: the first chunks of all
+// of them are loaded before any is ranked, so a workgroup has that many
+// tiles' entries in flight at once.
 template <int DT>
 __global__ __launch_bounds__(TW_THREADS) void topk_write_staged_kernel(int64_t nt, TopkWs w,
                                                                        int64_t k_out,
                                                                        int64_t *idx_out,
                                                                        float *val_out)
 {
-    constexpr int R = TW_ROUNDS;
-    __shared__ uint32_t s_tot[R][TW_WAVES];
+    constexpr int CH = TW_ROUNDS * TW_THREADS;
+    __shared__ uint32_t s_tot[TW_ROUNDS][TW_WAVES];
     if (!w.st->fast)
         return;
     const uint32_t T = w.st->prefix;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int64_t tile = blockIdx.x; tile < nt; tile += gridDim.x) {
-        const uint32_t n = w.tcnt[tile];
-        const uint64_t seg = w.toff[tile];
-        const uint32_t tk = w.take[tile];
-        const int64_t base = w.off[tile];
-        const int64_t tile0 = tile * TK_TILE;
-        uint32_t carry = 0; // packed counts of the entries before this chunk
-        for (uint32_t c0 = 0; c0 < n; c0 += R * TW_THREADS) {
-            u32x2 ent[R];
+    for (int64_t t0 = (int64_t)blockIdx.x * TW_TILES; t0 < nt; t0 += (int64_t)gridDim.x * TW_TILES) {
+        uint32_t n[TW_TILES], tk[TW_TILES];
+        uint64_t seg[TW_TILES];
+        int64_t base[TW_TILES];
+        u32x2 ent[TW_TILES][TW_ROUNDS];
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
-                ent[i] = p < n ? u32x2{stage_bits<DT>(w, seg + p), (uint32_t)w.sloc[seg + p]} : u32x2{0u, 0u};
+        for (int u = 0; u < TW_TILES; ++u) {
+            const bool has = t0 + u < nt;
+            n[u] = has ? w.tcnt[t0 + u] : 0u;
+            seg[u] = has ? w.toff[t0 + u] : 0ull;
+            tk[u] = has ? w.take[t0 + u] : 0u;
+            base[u] = has ? w.off[t0 + u] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < TW_TILES; ++u)
+            load_staged_chunk<DT>(w, seg[u], 0, n[u], ent[u]);
+#pragma unroll
+        for (int u = 0; u < TW_TILES; ++u) {
+            const int64_t tile0 = (t0 + u) * TK_TILE;
+            uint32_t carry = 0; // packed counts of the entries before this chunk
+            write_staged_chunk<DT>(ent[u], 0, n[u], T, tk[u], base[u], tile0, k_out, idx_out, val_out, s_tot,
+                                   carry);
+            // a tile keeping more than CH entries (over an eighth of it)
+            for (uint32_t c0 = CH; c0 < n[u]; c0 += CH) {
+                u32x2 more[TW_ROUNDS];
+                load_staged_chunk<DT>(w, seg[u], c0, n[u], more);
+                write_staged_chunk<DT>(more, c0, n[u], T, tk[u], base[u], tile0, k_out, idx_out, val_out,
+                                       s_tot, carry);
             }
-            uint32_t exw[R];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
-                const uint32_t key = key_of_bits(ent[i].x);
-                const uint32_t v = p < n ? (key > T ? (1u << 16) : (key == T ? 1u : 0u)) : 0u;
-                const uint32_t sc = wave_inclusive_scan(v);
-                if (lane == 63)
-                    s_tot[i][wave] = sc;
-                exw[i] = sc - v;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                uint32_t before = 0, round_total = 0;
-#pragma unroll
-                for (int v = 0; v < TW_WAVES; ++v) {
-                    const uint32_t t = s_tot[i][v];
-                    before += v < wave ? t : 0u;
-                    round_total += t;
-                }
-                const uint32_t run = carry + before + exw[i];
-                carry += round_total;
-                const uint32_t p = c0 + i * TW_THREADS + threadIdx.x;
-                const uint32_t key = key_of_bits(ent[i].x);
-                if (p >= n || key < T)
-                    continue;
-                const uint32_t gt_before = run >> 16, eq_before = run & 0xFFFFu;
-                if (key == T && eq_before >= tk)
-                    continue;
-                const int64_t r = base + gt_before + min(eq_before, tk);
-                if (r < k_out) { // keeps inconsistent counts from writing out of range
-                    idx_out[r] = tile0 + ent[i].y;
-                    val_out[r] = __uint_as_float(ent[i].x);
-                }
-            }
-            __syncthreads(); // s_tot is reused by the next chunk
         }
     }
 }
@@ -1419,7 +1461,8 @@ hipError_t topk_run(const void *x, int64_t N, int64_t k, int64_t *idx_out, float
     topk_scan_down_kernel<<<(unsigned)sz.nch, 256, 0, s>>>(nt, w);
     const bool staged = plan.on && staging;
     if (staged)
-        topk_write_staged_kernel<DT><<<work_grid, TW_THREADS, 0, s>>>(nt, w, k, idx_out, val_out);
+        topk_write_staged_kernel<DT><<<(unsigned)((nt + TW_TILES - 1) / TW_TILES), TW_THREADS, 0, s>>>(
+            nt, w, k, idx_out, val_out);
     topk_write_input_kernel<DT><<<staged ? idle_grid : work_grid, TT_THREADS, 0, s>>>(x, N, vec_ok, nt, w, staged, k, idx_out, val_out);
     return hipGetLastError();
 }
