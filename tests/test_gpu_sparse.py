@@ -181,7 +181,9 @@ def test_order_violations_at_every_kind_of_edge(tile, blocks):
     fa.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, blocks)
     N = 50_000
     tiles = -(-N // tile)
-    nb = min(tiles, blocks if blocks > 0 else 65536)
+    # the library's range count: the option, else ranges of 4 tiles but at
+    # least 4096 ranges while there are that many tiles
+    nb = min(tiles, blocks if blocks > 0 else max(-(-tiles // 4), min(tiles, 4096)))
     R = -(-tiles // nb) * tile                     # parameters per range
     base = np.zeros(N, np.float32)
     good = np.arange(N, dtype=np.int64)
