@@ -571,7 +571,8 @@ def bench_dense_k(Ks=(4, 8, 16, 20, 32, 64), total_bytes=65_343_852_544, reps=10
     and a bf16 output of N parameters each, N chosen so the (K+1)*2*N bytes
     match the 2.0B K=16 workload's 65.3 GB.  K = 3, 8 and 16 have kernels
     of their own; the others take the generic kernel (clients in batches of
-    8, of 16 above 16 clients).  Values do not change the time, so the clients are filled with a
+    8, of 16 above 16 clients).  The residency cap follows the client count
+    (the library's default).  Values do not change the time, so the clients are filled with a
     constant."""
     import torch
     import weighted_model_update_amd as fa
@@ -806,7 +807,7 @@ def bench_ceiling(reps=10, warmup=2, residents=(3, 0, 1, 2, 4)):
             record("dense kernel K=16 bf16", 1, 16, None, None, 1, res,
                    lambda i: fa.fedavg_aggregate(xs, n, out), 17 * 2 * N)
         finally:
-            fa.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, 3)
+            fa.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, -1)
         log(f"ceiling: resident {res} done")
     del bufs
     free_gpu()

@@ -59,7 +59,8 @@ bool overlap_ok(const void *a, size_t abytes, const void *b, size_t bbytes)
 
 // Launch-shape options (fedavg_set_option).
 int64_t g_blocks_per_cu = 0;     // grid-stride cap, workgroups per CU (0: none)
-int64_t g_resident_per_cu = 3;   // dense kernel: resident workgroups per CU (0: no cap)
+int64_t g_resident_per_cu = -1;  // dense kernel: resident workgroups per CU (0: no cap,
+                                 // -1: by client count, dense_resident_for)
 int64_t g_mask_vpb = 2048;       // masked kernel: 8-parameter vectors per block
 int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: the default rule)
 int64_t g_sparse_tile = fa::SP_DEFAULT_TILE;
@@ -87,6 +88,27 @@ int cu_count()
 }
 
 int64_t grid_cap() { return g_blocks_per_cu > 0 ? g_blocks_per_cu * cu_count() : 0; }
+
+// Resident dense workgroups per CU when the caller sets none.  A lane keeps
+// one 16-byte load per client in flight, so the bytes a CU has in flight
+// grow with K; past a point more of them only queue.  Measured on MI355X
+// at 65.3 GB per launch (bf16 clients and output), best cap per client
+// count (fraction of HBM peak there, and at a cap of 3):
+//   K = 2: none (0.80; 0.51)   K = 3: 6 (0.79; 0.64)   K = 4: 6 (0.78; 0.72)
+//   K = 5, 6, 8: 3 (0.76, 0.78, 0.75)   K = 12: none (0.74; 0.72)
+//   K = 16: 3 (0.74)   K = 20, 32, 64: 5-8 (0.72, 0.72, 0.73; 0.70, 0.69, 0.70)
+int dense_resident_for(int K)
+{
+    if (K <= 2)
+        return 0;
+    if (K <= 4)
+        return 6;
+    if (K <= 8)
+        return 3;
+    if (K < 16)
+        return 0;
+    return K == 16 ? 3 : 6;
+}
 
 enum class Residence { Device, PinnedHost, Pageable };
 
@@ -305,8 +327,8 @@ int fedavg_set_option(int option, int64_t value)
         g_mask_vpb = value;
         return ok();
     case FA_OPT_RESIDENT_PER_CU:
-        if (value < 0 || value > 32)
-            return fail(FA_ERR_RANGE, "resident workgroups per CU must be in [0, 32]");
+        if (value < -1 || value > 32)
+            return fail(FA_ERR_RANGE, "resident workgroups per CU must be in [-1, 32]");
         g_resident_per_cu = value;
         return ok();
     case FA_OPT_SPARSE_TILE:
@@ -410,8 +432,9 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
         d.base = base;
         d.out = out;
         d.S = (float)S;
+        const int resident = g_resident_per_cu >= 0 ? (int)g_resident_per_cu : dense_resident_for(Kc);
         hipError_t e = fa::launch_dense(d, x_dtype, out_dtype, base_dtype, kmode, aligned,
-                                        grid_cap(), (int)g_resident_per_cu, s);
+                                        grid_cap(), resident, s);
         return e == hipSuccess ? ok() : hip_fail(e, "dense aggregate launch");
     }
 
