@@ -64,6 +64,14 @@ int64_t g_resident_per_cu = -1;  // dense kernel: resident workgroups per CU (0:
 int64_t g_mask_vpb = 2048;       // masked kernel: 8-parameter vectors per block
 int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: the default rule)
 int64_t g_sparse_tile = fa::SP_DEFAULT_TILE;
+// Resident workgroups per CU of the streaming kernels (by residency_lds).
+// Measured on MI355X over 2^31 parameters held in HBM, as fractions of
+// HBM peak: the accumulate (a bf16 chunk into the fp32 sums) 0.79 at 3
+// against 0.74 uncapped; the two-level merge (fp32 partial into the sums)
+// 0.77 at 2 against 0.73; the finalize was fastest uncapped (0.76; 0.57-0.74
+// at caps of 2 to 8).
+constexpr int STREAM_ACC_RESIDENT = 3;
+constexpr int STREAM_MERGE_RESIDENT = 2;
 constexpr int64_t SPARSE_MAX_BLOCKS = 1 << 19;
 constexpr int64_t SPARSE_RANGE_TILES = 4;  // default: tiles per range
 constexpr int64_t SPARSE_MIN_RANGES = 4096; // default: ranges while there are that many tiles
@@ -799,7 +807,7 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
         const int part = !st.partial ? fa::PART_DENSE : (mask ? fa::PART_MASK : fa::PART_RANGE);
         const bool aligned = (offset % fa::VEC) == 0 && aligned16(a.chunk) &&
                              (!a.mask || (reinterpret_cast<uintptr_t>(a.mask) & 7u) == 0);
-        e = fa::launch_stream_accumulate(a, dtype, part, aligned, grid_cap(), 0, st.compute);
+        e = fa::launch_stream_accumulate(a, dtype, part, aligned, grid_cap(), STREAM_ACC_RESIDENT, st.compute);
     }
     if (e != hipSuccess)
         return hip_fail(e, "accumulate launch");
@@ -911,7 +919,8 @@ int fedavg_accumulate_partial(fa_handle h, int client_id, int64_t W, int n_clien
     const bool aligned = (offset % fa::VEC) == 0 && aligned16(a.chunk) &&
                          (!use_wsum || aligned16(a.src_wsum)) &&
                          (!use_count || (reinterpret_cast<uintptr_t>(a.src_count) & 7u) == 0);
-    hipError_t e = fa::launch_stream_merge(a, use_wsum, aligned, grid_cap(), st.compute);
+    hipError_t e =
+        fa::launch_stream_merge(a, use_wsum, aligned, grid_cap(), STREAM_MERGE_RESIDENT, st.compute);
     if (e != hipSuccess)
         return hip_fail(e, "merge launch");
     if (slot >= 0) {

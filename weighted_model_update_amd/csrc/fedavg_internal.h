@@ -117,7 +117,7 @@ hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool 
                                     int64_t grid_cap, int resident, hipStream_t s);
 hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStream_t s);
 hipError_t launch_stream_merge(const StreamArgs &a, bool partial, bool aligned, int64_t cap,
-                               hipStream_t s);
+                               int resident, hipStream_t s);
 hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int mode, int partial,
                                   bool aligned, int64_t grid_cap, int resident, hipStream_t s);
 int sparse_resident_blocks_per_cu(int tile);

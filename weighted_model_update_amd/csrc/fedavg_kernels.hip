@@ -1703,11 +1703,12 @@ hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStre
 }
 
 template <int PARTIAL>
-static hipError_t merge_t(const StreamArgs &a, bool aligned, int64_t cap, hipStream_t s)
+static hipError_t merge_t(const StreamArgs &a, bool aligned, int64_t cap, int resident, hipStream_t s)
 {
     const int64_t nvec = aligned ? a.len / VEC : 0;
     if (nvec > 0) {
-        stream_merge_vec_kernel<PARTIAL><<<grid_for(nvec, 256, cap), 256, 0, s>>>(a, nvec);
+        auto *k = &stream_merge_vec_kernel<PARTIAL>;
+        k<<<grid_for(nvec, 256, cap), 256, residency_lds(k, resident), s>>>(a, nvec);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -1722,9 +1723,9 @@ static hipError_t merge_t(const StreamArgs &a, bool aligned, int64_t cap, hipStr
 }
 
 hipError_t launch_stream_merge(const StreamArgs &a, bool partial, bool aligned, int64_t cap,
-                               hipStream_t s)
+                               int resident, hipStream_t s)
 {
-    return partial ? merge_t<1>(a, aligned, cap, s) : merge_t<0>(a, aligned, cap, s);
+    return partial ? merge_t<1>(a, aligned, cap, resident, s) : merge_t<0>(a, aligned, cap, resident, s);
 }
 
 template <int B, int O, int M, int P>
