@@ -340,15 +340,32 @@ __device__ int64_t wave_find_segment(const int64_t *bounds, int64_t T, int64_t e
     return lo;
 }
 
+// The clients' presence bytes of segment t are read 8 at a time, each
+// batch issued before any is tested: read one after another, with a test
+// between, every load waited for the one before it, and a workgroup's table
+// took K round trips before its first client load.
 __device__ __forceinline__ void segment_weights(const MaskedArgs &a, int64_t t, uint64_t &mask,
                                                 uint32_t &W)
 {
     uint64_t m = 0;
     uint32_t s = 0;
-    for (int k = 0; k < a.K; ++k) {
-        if (a.present[(int64_t)a.row[k] * a.T + t]) {
-            m |= 1ull << k;
-            s += a.wi[k];
+    for (int k0 = 0; k0 < a.K; k0 += 8) {
+        uint32_t p[8];
+        // unconditional loads (a client index past K reads the last
+        // client's byte and drops it): a load under a branch is waited for
+        // before the next one is issued
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int k = min(k0 + j, a.K - 1);
+            const uint32_t byte = a.present[(int64_t)a.row[k] * a.T + t];
+            p[j] = k0 + j < a.K ? byte : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (p[j]) {
+                m |= 1ull << (k0 + j);
+                s += a.wi[k0 + j];
+            }
         }
     }
     mask = m;
@@ -568,10 +585,13 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
 
     const int tid = threadIdx.x;
     const int T = (int)a.T;
-    for (int t = tid; t <= T; t += blockDim.x)
-        s_lo[t] = a.bounds[t];
-    for (int t = tid; t < T; t += blockDim.x)
-        segment_weights(a, t, s_mask[t], s_W[t]);
+    // a segment's bound and its clients' presence bytes in one round trip
+    for (int t = tid; t <= T; t += blockDim.x) {
+        const int64_t lo = a.bounds[t];
+        if (t < T)
+            segment_weights(a, t, s_mask[t], s_W[t]);
+        s_lo[t] = lo;
+    }
     __syncthreads();
 
     // Grid-stride over the vectors (the grid holds about N / (8 vpb)
