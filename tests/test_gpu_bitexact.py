@@ -58,6 +58,29 @@ def test_dense(K, xdt, odt, mode):
     same_bits(host_of(out), want)
 
 
+@pytest.mark.parametrize("K", [2, 4, 12, 20])
+def test_dense_residency_caps_give_the_same_bits(K):
+    """The resident-workgroup cap (by default chosen from the number of
+    contributing clients) changes only how many workgroups share a CU:
+    every cap gives the oracle mirror's bits."""
+    N = 300_007
+    xs = clients(100 + K, K, N, "bf16")
+    n = synth.sample_counts(K, K, 1, 100_000)
+    base = base_of(K, N, "bf16")
+    want = oracle.mirror_f32(xs, n, mode=oracle.DELTAS, base=base, x_dtype=oracle.BF16,
+                             base_dtype=oracle.BF16, out_dtype=oracle.BF16)
+    try:
+        for cap in (-1, 0, 1, 3, 6, 8):
+            fa.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, cap)
+            out = empty(N, "bf16")
+            fa.fedavg_aggregate([dev_of(x, "bf16") for x in xs], n.tolist(), out, mode="deltas",
+                                base=dev_of(base, "bf16"))
+            torch.cuda.synchronize()
+            same_bits(host_of(out), want)
+    finally:
+        fa.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, -1)
+
+
 def test_dense_unaligned_view():
     N, K = 50_001, 4
     xs = clients(2, K, N + 1, "bf16")

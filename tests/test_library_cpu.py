@@ -66,6 +66,11 @@ def test_host_side_argument_errors_need_no_device():
     assert lib.fedavg_set_option(99, 1) == -1
     assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, (1 << 19) + 1) == -3
     assert lib.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 2) == -3
+    # residency: -1 (by client count, the default), 0 (no cap) .. 32
+    assert lib.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, -2) == -3
+    assert lib.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, 33) == -3
+    assert lib.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, 32) == 0
+    assert lib.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, -1) == 0
     b = ctypes.c_size_t(0)
     assert lib.topk_workspace_size(0, 100, 101, ctypes.byref(b)) == -3   # k > N
     assert lib.topk_workspace_size(7, 100, 10, ctypes.byref(b)) == -2    # unknown dtype
