@@ -94,25 +94,30 @@ def test_dense_unaligned_view():
 
 @pytest.mark.parametrize("T", [300, 900])
 @pytest.mark.parametrize("mode", ["weights", "deltas", "deltas_zero_fill"])
-def test_masked(T, mode):
+@pytest.mark.parametrize("xdt,odt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")])
+def test_masked(T, mode, xdt, odt):
+    # T = 300: the whole-table kernel; 900: the windowed one.  An fp32
+    # output takes two 4-parameter quads per lane, 1 KiB apart, and falls
+    # back to elements where they lie in different segments.
     r = np.random.default_rng(T)
     sizes = r.integers(0, 600, size=T)
+    sizes[::7] = r.integers(2000, 9000, size=len(sizes[::7]))  # segments longer than a run of quads
     bounds = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     N, K = int(bounds[-1]), 8
     present = (r.random((K, T)) < 0.6).astype(np.uint8)
-    xs = clients(T + 1, K, N, "bf16")
-    base = base_of(T, N, "bf16")
+    xs = clients(T + 1, K, N, xdt)
+    base = base_of(T, N, xdt)
     n = synth.sample_counts(T, K, 500, 5000)
-    out = empty(N, "bf16")
-    fa.fedavg_aggregate([dev_of(x, "bf16") for x in xs], n.tolist(), out, mode=mode,
-                        base=dev_of(base, "bf16"),
+    out = empty(N, odt)
+    fa.fedavg_aggregate([dev_of(x, xdt) for x in xs], n.tolist(), out, mode=mode,
+                        base=dev_of(base, xdt),
                         seg_bounds=torch.tensor(bounds, dtype=torch.int64, device="cuda"),
                         present=torch.from_numpy(present).cuda())
     torch.cuda.synchronize()
     seg_of = np.repeat(np.arange(T), np.diff(bounds))
     sent = [present[k][seg_of] for k in range(K)]
-    want = oracle.mirror_f32(xs, n, mode=MODES[mode], base=base, x_dtype=oracle.BF16,
-                             base_dtype=oracle.BF16, out_dtype=oracle.BF16, sent=sent)
+    want = oracle.mirror_f32(xs, n, mode=MODES[mode], base=base, x_dtype=OD[xdt],
+                             base_dtype=OD[xdt], out_dtype=OD[odt], sent=sent)
     same_bits(host_of(out), want)
 
 

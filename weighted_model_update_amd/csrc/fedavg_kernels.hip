@@ -393,14 +393,17 @@ __device__ __forceinline__ void masked_element(const MaskedArgs &a, int64_t e)
     io<ODT>::store1(a.out, e, r);
 }
 
-// Element-wise path for a vector whose 8 parameters do not all lie in one
-// segment (or run past the end of the buffer).
+// Element-wise path for a vector (the quads at e0 and e1) whose 8 parameters
+// do not all lie in one segment (or run past the end of the buffer).
 template <int XDT, int ODT, int BDT, int MODE>
-__device__ __forceinline__ void masked_vector_elementwise(const MaskedArgs &a, int64_t e)
+__device__ __forceinline__ void masked_vector_elementwise(const MaskedArgs &a, int64_t e0, int64_t e1)
 {
-    for (int j = 0; j < VEC; ++j)
-        if (e + j < a.N)
-            masked_element<XDT, ODT, BDT, MODE>(a, e + j);
+    for (int j = 0; j < 4; ++j)
+        if (e0 + j < a.N)
+            masked_element<XDT, ODT, BDT, MODE>(a, e0 + j);
+    for (int j = 0; j < 4; ++j)
+        if (e1 + j < a.N)
+            masked_element<XDT, ODT, BDT, MODE>(a, e1 + j);
 }
 
 // Each workgroup owns a contiguous run of `vpb` 8-parameter vectors, walked
@@ -415,6 +418,7 @@ __device__ __forceinline__ void masked_vector_elementwise(const MaskedArgs &a, i
 template <int XDT, int ODT, int BDT, int MODE>
 __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
 {
+    constexpr bool SPLIT = ODT == DT_F32;
     __shared__ int64_t s_lo[SEG_WIN + 1];
     __shared__ uint64_t s_mask[SEG_WIN];
     __shared__ uint32_t s_W[SEG_WIN];
@@ -468,8 +472,14 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
             const int64_t v = s0 + tid;
             if (v >= s1)
                 continue;
-            const int64_t e = v * VEC;
-            if (one_segment && e + VEC <= a.N) {
+            // an fp32 output: in a full span of 256 vectors the lane takes
+            // the quads tid and 256 + tid of the span (whole-line stores)
+            int64_t e0 = v * VEC, e1 = e0 + 4;
+            if (SPLIT && s1 - s0 == 256) {
+                e0 = s0 * VEC + tid * 4;
+                e1 = e0 + 1024;
+            }
+            if (one_segment && e1 + 4 <= a.N) {
                 const uint64_t smask = s_mask[lo];
                 const uint32_t mlo = __builtin_amdgcn_readfirstlane((uint32_t)smask);
                 const uint32_t mhi = __builtin_amdgcn_readfirstlane((uint32_t)(smask >> 32));
@@ -492,7 +502,8 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
                             xr[k] = io<XDT>::zero_raw();
                             wk[k] = on ? a.w[k0 + k] : 0.0f;
                             if (on)
-                                xr[k] = io<XDT>::load_raw(a.x[k0 + k], e);
+                                xr[k] = SPLIT ? io<XDT>::load_raw2(a.x[k0 + k], e0, e1)
+                                              : io<XDT>::load_raw(a.x[k0 + k], e0);
                         }
 #pragma unroll
                         for (int k = 0; k < 8; ++k)
@@ -501,7 +512,10 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
                     const float Wf = a.zero_fill ? a.S_all : (float)W;
                     if constexpr (MODE == MODE_DELTAS) {
                         float b[VEC];
-                        io<BDT>::load8(a.base, e, b);
+                        if constexpr (SPLIT)
+                            io<BDT>::load8_2(a.base, e0, e1, b);
+                        else
+                            io<BDT>::load8(a.base, e0, b);
 #pragma unroll
                         for (int j = 0; j < VEC; ++j)
                             r[j] = b[j] + acc[j] / Wf;
@@ -510,12 +524,17 @@ __global__ __launch_bounds__(256) void masked_vec_kernel(const MaskedArgs a)
                         for (int j = 0; j < VEC; ++j)
                             r[j] = acc[j] / Wf;
                     }
+                } else if constexpr (SPLIT) {
+                    io<BDT>::load8_2(a.base, e0, e1, r);
                 } else {
-                    io<BDT>::load8(a.base, e, r);
+                    io<BDT>::load8(a.base, e0, r);
                 }
-                io<ODT>::store8(a.out, e, r);
+                if constexpr (SPLIT)
+                    io<ODT>::store8_2(a.out, e0, e1, r);
+                else
+                    io<ODT>::store8(a.out, e0, r);
             } else {
-                masked_vector_elementwise<XDT, ODT, BDT, MODE>(a, e);
+                masked_vector_elementwise<XDT, ODT, BDT, MODE>(a, e0, e1);
             }
         }
         e_cur = win_end;
@@ -600,15 +619,22 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
     const int64_t nvec_all = (a.N + VEC - 1) / VEC;
     const int64_t v_end = nvec_all;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    // an fp32 output: a lane takes the quads quad_pair gives (whole-line
+    // stores); the first quad moves the segment cursor, and a vector is fast
+    // when both quads lie in its segment
+    constexpr bool SPLIT = ODT == DT_F32;
     int t = -1;
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + tid; v < v_end; v += NV * stride) {
-        int64_t ev[NV];
+        int64_t ev[NV], ew[NV];
         bool has[NV], fast[NV];
         uint64_t m[NV];
         uint32_t W[NV];
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             ev[u] = (v + u * stride) * VEC;
+            ew[u] = ev[u] + 4;
+            if constexpr (SPLIT)
+                quad_pair(v + u * stride, v_end, ev[u], ew[u]);
             has[u] = v + u * stride < v_end;
             fast[u] = false;
             m[u] = 0;
@@ -616,7 +642,7 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
             if (has[u]) {
                 if (t < 0 || s_lo[t + 1] <= ev[u])
                     t = lds_find_segment(s_lo, min(t + 1, T - 1), T, ev[u]);
-                fast[u] = s_lo[t] <= ev[u] && ev[u] + VEC <= s_lo[t + 1] && ev[u] + VEC <= a.N;
+                fast[u] = s_lo[t] <= ev[u] && ew[u] + 4 <= s_lo[t + 1] && ew[u] + 4 <= a.N;
                 if (fast[u]) {
                     m[u] = s_mask[t];
                     W[u] = s_W[t];
@@ -644,7 +670,8 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
                     xr[u][k] = io<XDT>::zero_raw();
                     wk[u][k] = on ? a.w[k0 + k] : 0.0f;
                     if (on)
-                        xr[u][k] = io<XDT>::load_raw(a.x[k0 + k], ev[u]);
+                        xr[u][k] = SPLIT ? io<XDT>::load_raw2(a.x[k0 + k], ev[u], ew[u])
+                                         : io<XDT>::load_raw(a.x[k0 + k], ev[u]);
                 }
 #pragma unroll
             for (int u = 0; u < NV; ++u)
@@ -657,8 +684,10 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
             if (!has[u])
                 continue;
             if (!fast[u]) {
-                for (int j = 0; j < VEC && ev[u] + j < a.N; ++j)
+                for (int j = 0; j < 4 && ev[u] + j < a.N; ++j)
                     masked_element_lds<XDT, ODT, BDT, MODE>(a, s_lo, s_mask, s_W, ev[u] + j);
+                for (int j = 0; j < 4 && ew[u] + j < a.N; ++j)
+                    masked_element_lds<XDT, ODT, BDT, MODE>(a, s_lo, s_mask, s_W, ew[u] + j);
                 continue;
             }
             float r[VEC];
@@ -666,7 +695,10 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
                 const float Wf = a.zero_fill ? a.S_all : (float)W[u];
                 if constexpr (MODE == MODE_DELTAS) {
                     float b[VEC];
-                    io<BDT>::load8(a.base, ev[u], b);
+                    if constexpr (SPLIT)
+                        io<BDT>::load8_2(a.base, ev[u], ew[u], b);
+                    else
+                        io<BDT>::load8(a.base, ev[u], b);
 #pragma unroll
                     for (int j = 0; j < VEC; ++j)
                         r[j] = b[j] + acc[u][j] / Wf;
@@ -675,10 +707,15 @@ __global__ __launch_bounds__(256) void masked_table_kernel(const MaskedArgs a)
                     for (int j = 0; j < VEC; ++j)
                         r[j] = acc[u][j] / Wf;
                 }
+            } else if constexpr (SPLIT) {
+                io<BDT>::load8_2(a.base, ev[u], ew[u], r);
             } else {
                 io<BDT>::load8(a.base, ev[u], r);
             }
-            io<ODT>::store8(a.out, ev[u], r);
+            if constexpr (SPLIT)
+                io<ODT>::store8_2(a.out, ev[u], ew[u], r);
+            else
+                io<ODT>::store8(a.out, ev[u], r);
         }
     }
 }
