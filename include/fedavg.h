@@ -508,7 +508,7 @@ typedef enum {
     FA_OPT_RESIDENT_PER_CU = 4,        /* resident dense kernel: workgroups of
                                           256 threads resident per CU (default
                                           -1: chosen by the number of
-                                          contributing clients, 3 for 16;
+                                          contributing clients, 2 for 16;
                                           0 = hardware limit) */
     FA_OPT_SPARSE_TILE = 5,            /* sparse merge: parameters per LDS tile,
                                           512, 1024, 2048 (default), 4096 or

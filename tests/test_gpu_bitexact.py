@@ -41,6 +41,29 @@ def base_of(seed, N, bdt):
     return synth.bf16_bits_from_f32(b) if bdt == "bf16" else b
 
 
+def test_bf16_output_every_fp32_pattern():
+    # One client with n = 1 passes each fp32 value through fma(1, x, +0) and a
+    # division by 1 (only -0 and NaN payloads change) to the bf16 rounding of
+    # the output stage, so the 2^32 bit patterns, in 16 pieces, cover every
+    # rounding case of that stage: ties, carries into the exponent, overflow
+    # to infinity, subnormals and NaNs.
+    piece = 1 << 28
+    out = empty(piece, "bf16")
+    for p in range(16):
+        x = np.arange(p * piece, (p + 1) * piece, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        xd = dev_f32(x)
+        fa.fedavg_aggregate([xd], [1], out)
+        torch.cuda.synchronize()
+        want = oracle.mirror_f32([x], np.array([1]), x_dtype=oracle.F32, out_dtype=oracle.BF16)
+        got = host_of(out)
+        # NaN matches NaN: the payload after the fused product is the FMA unit's
+        nan = ((got & 0x7fff) > 0x7f80) & ((want & 0x7fff) > 0x7f80)
+        bad = np.nonzero((got != want) & ~nan)[0]
+        assert bad.size == 0, (p, bad.size, bad[:5], got[bad[:5]], want[bad[:5]])
+        assert np.array_equal((got & 0x7fff) > 0x7f80, (want & 0x7fff) > 0x7f80)
+        del xd
+
+
 @pytest.mark.parametrize("K", [1, 3, 5, 8, 16, 17, 20, 64])
 @pytest.mark.parametrize("xdt,odt,mode", [("f32", "f32", "weights"), ("bf16", "bf16", "deltas"),
                                           ("bf16", "f32", "deltas"), ("f32", "bf16", "weights")])

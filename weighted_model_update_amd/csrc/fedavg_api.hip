@@ -100,22 +100,22 @@ int64_t grid_cap() { return g_blocks_per_cu > 0 ? g_blocks_per_cu * cu_count() :
 // Resident dense workgroups per CU when the caller sets none.  A lane keeps
 // one 16-byte load per client in flight, so the bytes a CU has in flight
 // grow with K; past a point more of them only queue.  Measured on MI355X
-// at 65.3 GB per launch (bf16 clients and output), best cap per client
-// count (fraction of HBM peak there, and at a cap of 3):
-//   K = 2: none (0.80; 0.51)   K = 3: 6 (0.79; 0.64)   K = 4: 6 (0.78; 0.72)
-//   K = 5, 6, 8: 3 (0.76, 0.78, 0.75)   K = 12: none (0.74; 0.72)
-//   K = 16: 3 (0.74)   K = 20, 32, 64: 5-8 (0.72, 0.72, 0.73; 0.70, 0.69, 0.70)
+// at 65.3 GB per launch (bf16 clients and output), two allocations on two
+// devices, best cap per client count (fraction of HBM peak there):
+//   K = 2: none (0.78)   K = 3: 4 or 6 (0.77)   K = 4, 5: 4 (0.77-0.80, 0.75)
+//   K = 6, 7, 8, 10: 3 (0.73-0.75)   K = 12, 14: none (0.71-0.76)
+//   K = 16: 2 (0.74-0.75; 0.73 at 3)   K = 20 ... 64: none (0.72-0.74)
 int dense_resident_for(int K)
 {
     if (K <= 2)
         return 0;
-    if (K <= 4)
-        return 6;
-    if (K <= 8)
+    if (K <= 5)
+        return 4;
+    if (K <= 10)
         return 3;
     if (K < 16)
         return 0;
-    return K == 16 ? 3 : 6;
+    return K == 16 ? 2 : 0;
 }
 
 enum class Residence { Device, PinnedHost, Pageable };
@@ -419,6 +419,10 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
     }
     if (S >= (1ull << 32))
         return fail(FA_ERR_RANGE, "sum of n_k must be below 2^32");
+    // the dense kernel's last batch of clients adds its unused slots with
+    // weight -0, which changes no accumulator bit
+    for (int k = Kc; k < FA_MAX_CLIENTS; ++k)
+        d.w[k] = -0.0f;
     if (base && !overlap_ok(out, obytes, base, (size_t)N * dsize(base_dtype)))
         return fail(FA_ERR_ARG, "out partially overlaps base");
     if (N == 0)

@@ -20,7 +20,7 @@ constexpr int TAB_SEGS = 512; // segment tables up to this size are staged whole
 // ---------------------------------------------------------------- resident
 struct DenseArgs {
     const void *x[FA_MAX_CLIENTS]; // contributing clients only (n_k > 0)
-    float w[FA_MAX_CLIENTS];       // fp32(n_k), exact
+    float w[FA_MAX_CLIENTS];       // fp32(n_k), exact; -0 past K
     int K;                         // number of contributing clients
     int64_t N;
     const void *base;
