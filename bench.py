@@ -737,6 +737,8 @@ CEILING_CASES = [
     ("mix16 nt/buf sc0sc1", 1, 16, P_GLOBAL_NT, P_BUF_SC0SC1, 1),
     ("mix16 nt/buf sc1nt", 1, 16, P_GLOBAL_NT, P_BUF_SC1NT, 1),
     ("mix16 nt/buf sc0sc1nt", 1, 16, P_GLOBAL_NT, P_BUF_SC0SC1NT, 1),
+    ("mix16 buf nt/buf nt", 1, 16, P_BUF_NT, P_BUF_NT, 1),
+    ("mix16 buf nt/buf sc1nt", 1, 16, P_BUF_NT, P_BUF_SC1NT, 1),
     ("mix16 nt/nt vpt2", 1, 16, P_GLOBAL_NT, P_GLOBAL_NT, 2),
     ("mix16 nt/nt vpt4", 1, 16, P_GLOBAL_NT, P_GLOBAL_NT, 4),
     ("mix16 nt/plain vpt2", 1, 16, P_GLOBAL_NT, P_GLOBAL, 2),
@@ -787,7 +789,8 @@ def bench_ceiling(reps=10, warmup=2, residents=(2, 0, 1, 3, 4)):
         for name, pattern, ns, lp, sp, vpt in CEILING_CASES:
             if res != residents[0] and not name.startswith(("mix", "read16 nt", "copy nt/nt")):
                 continue        # the policy sweep runs at the default cap only
-            if res != residents[0] and name.startswith("mix16") and "nt/nt" not in name:
+            if (res != residents[0] and name.startswith("mix16") and "nt/nt" not in name
+                    and name != "mix16 buf nt/buf sc1nt"):
                 continue
             dst = bufs[16].data_ptr() if ns < 17 else bufs[0].data_ptr()
             nb_ = (ns + (1 if pattern == 1 else 0)) * nvec * 16

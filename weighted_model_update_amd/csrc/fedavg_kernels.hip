@@ -220,15 +220,19 @@ __device__ __forceinline__ void quad_pair(int64_t v, int64_t nvec, int64_t &e0, 
 
 // A raw buffer over the `bytes` bytes from p (clamped to 2^32 - 1): a load
 // past its end reads zero without touching memory and a store past it is
-// dropped, so accesses near the end of an array need no branch.  The
-// cache-policy bits of every access through it are nt (non-temporal).
+// dropped, so accesses near the end of an array need no branch.  Loads
+// through it carry the nt (non-temporal) bit, stores sc1 and nt: with K = 16
+// bf16 clients at 2 workgroups per CU stores ran 10.85-10.87 ms with sc1 nt,
+// 10.87-10.90 with sc1 or sc0 sc1, 10.93 with nt alone and 11.62 with no
+// bits, on one allocation.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void *p, int64_t bytes)
 {
     const uint32_t n = bytes < 0xFFFFFFFFll ? (uint32_t)bytes : 0xFFFFFFFFu;
     // stride 0 (raw), the raw-buffer format word of gfx9 parts
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)n, 0x00020000);
 }
-constexpr int BUF_NT = 2;
+constexpr int BUF_NT = 2;     // loads: nt
+constexpr int BUF_STORE = 18; // stores: sc1 nt
 
 // 8 parameters through a span: 8 consecutive ones at byte offset o, or two
 // quads at byte offsets o0 and o1.
@@ -253,8 +257,8 @@ template <> struct bio<DT_F32> {
     }
     static __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, int o0, int o1, const float (&v)[VEC])
     {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), r, o0, 0, BUF_NT);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[4], v[5], v[6], v[7]}), r, o1, 0, BUF_NT);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), r, o0, 0, BUF_STORE);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[4], v[5], v[6], v[7]}), r, o1, 0, BUF_STORE);
     }
 };
 template <> struct bio<DT_BF16> {
@@ -279,7 +283,7 @@ template <> struct bio<DT_BF16> {
     {
         const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                          pack_bf16x2(v[6], v[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(w, r, o, 0, BUF_NT);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, o, 0, BUF_STORE);
     }
 };
 

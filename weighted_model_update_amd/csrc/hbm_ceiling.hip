@@ -216,6 +216,9 @@ int hc_stream(int pattern, int ns, const void *const *src, void *dst, int64_t nv
     HC(1, 16, P_GLOBAL_NT, P_BUF_SC0SC1, 1)
     HC(1, 16, P_GLOBAL_NT, P_BUF_SC1NT, 1)
     HC(1, 16, P_GLOBAL_NT, P_BUF_SC0SC1NT, 1)
+    // buffer loads and stores (the dense kernel's accesses)
+    HC(1, 16, P_BUF_NT, P_BUF_NT, 1)
+    HC(1, 16, P_BUF_NT, P_BUF_SC1NT, 1)
     // fewer read streams per written one
     HC(1, 2, P_GLOBAL_NT, P_GLOBAL_NT, 1)
     HC(1, 4, P_GLOBAL_NT, P_GLOBAL_NT, 1)
