@@ -65,13 +65,14 @@ int64_t g_mask_vpb = 2048;       // masked kernel: 8-parameter vectors per block
 int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: the default rule)
 int64_t g_sparse_tile = fa::SP_DEFAULT_TILE;
 // Resident workgroups per CU of the streaming kernels (by residency_lds).
-// Measured on MI355X over 2^31 parameters held in HBM, as fractions of
-// HBM peak: the accumulate (a bf16 chunk into the fp32 sums) 0.79 at 3
-// against 0.74 uncapped; the two-level merge (fp32 partial into the sums)
-// 0.77 at 2 against 0.73; the finalize was fastest uncapped (0.76; 0.57-0.74
-// at caps of 2 to 8).
+// Measured on MI355X over 2^31 parameters held in HBM, as fractions of HBM
+// peak, caps 0 (none), 1, 2, 3, 4, 6: the accumulate (a bf16 chunk into the
+// fp32 sums) 0.73, 0.51, 0.78, 0.82, 0.79, 0.75; the two-level merge (an
+// fp32 partial into the sums) 0.77, 0.61, 0.81, 0.80, 0.79, 0.76; the
+// finalize to bf16 0.79, 0.42, 0.65, 0.76, 0.81, 0.79.
 constexpr int STREAM_ACC_RESIDENT = 3;
 constexpr int STREAM_MERGE_RESIDENT = 2;
+constexpr int STREAM_FIN_RESIDENT = 4;
 constexpr int64_t SPARSE_MAX_BLOCKS = 1 << 19;
 constexpr int64_t SPARSE_RANGE_TILES = 4;  // default: tiles per range
 constexpr int64_t SPARSE_MIN_RANGES = 4096; // default: ranges while there are that many tiles
@@ -990,7 +991,7 @@ int fedavg_finalize(fa_handle h, const void *base, fa_dtype base_dtype, void *ou
     const bool aligned = aligned16(out) && (!base || aligned16(base));
     e = fa::launch_stream_finalize(a, base_dtype, out_dtype,
                                    st.mode == FA_WEIGHTS ? FA_WEIGHTS : FA_DELTAS, st.partial,
-                                   aligned, grid_cap(), 0, st.compute);
+                                   aligned, grid_cap(), STREAM_FIN_RESIDENT, st.compute);
     return e == hipSuccess ? ok() : hip_fail(e, "finalize launch");
 }
 

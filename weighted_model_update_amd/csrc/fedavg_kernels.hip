@@ -845,18 +845,35 @@ __global__ __launch_bounds__(256) void masked_scalar_kernel(const MaskedArgs a)
 template <int DT, int PART>
 __global__ __launch_bounds__(256) void stream_acc_vec_kernel(const StreamArgs a, int64_t nvec)
 {
-    for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
-        int64_t eq[2];
-        quad_pair(v, nvec, eq[0], eq[1]);
+    // a workgroup takes 256 consecutive steps of 8 parameters through
+    // buffers based at its first parameter; a lane's two quads are
+    // quad_pair's (whole-line stores of the sums)
+    constexpr int XB = DT == DT_F32 ? 4 : 2;
+    const int l = threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t b = (int64_t)blockIdx.x * 256; b < nvec; b += stride) {
+        const int64_t left = nvec - b, e = b * VEC;
+        const bool full = left >= 256;
+        const int pq[2] = {full ? l * 4 : l * 8, (full ? l * 4 : l * 8) + (full ? 1024 : 4)};
+        const auto rx = span_rsrc(static_cast<const char *>(a.chunk) + e * XB, left * VEC * XB);
+        const auto ra = span_rsrc(a.acc + a.offset + e, left * VEC * 4);
         float xv[2][4];
         f32x4 acc[2];
         uint32_t sent[2] = {0xfu, 0xfu};
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            io<DT>::load4(a.chunk, eq[q], xv[q]);
-            acc[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.acc + a.offset + eq[q]));
+            if constexpr (DT == DT_F32) {
+                const f32x4 x = bio<DT_F32>::q(rx, pq[q] * 4);
+                xv[q][0] = x.x; xv[q][1] = x.y; xv[q][2] = x.z; xv[q][3] = x.w;
+            } else {
+                const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rx, pq[q] * 2, 0, BUF_NT);
+                xv[q][0] = bf16_lo(x.x); xv[q][1] = bf16_hi(x.x);
+                xv[q][2] = bf16_lo(x.y); xv[q][3] = bf16_hi(x.y);
+            }
+            acc[q] = bio<DT_F32>::q(ra, pq[q] * 4);
             if constexpr (PART == PART_MASK) {
-                const uint32_t mb = *reinterpret_cast<const uint32_t *>(a.mask + eq[q]);
+                const auto rm = span_rsrc(a.mask + e, left * VEC);
+                const uint32_t mb = __builtin_amdgcn_raw_buffer_load_b32(rm, pq[q], 0, 0);
                 sent[q] = 0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -865,32 +882,34 @@ __global__ __launch_bounds__(256) void stream_acc_vec_kernel(const StreamArgs a,
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            f32x4 &s = acc[q];
-            if (sent[q] & 1) s.x = __builtin_fmaf(a.w, xv[q][0], s.x);
-            if (sent[q] & 2) s.y = __builtin_fmaf(a.w, xv[q][1], s.y);
-            if (sent[q] & 4) s.z = __builtin_fmaf(a.w, xv[q][2], s.z);
-            if (sent[q] & 8) s.w = __builtin_fmaf(a.w, xv[q][3], s.w);
-            __builtin_nontemporal_store(s, reinterpret_cast<f32x4 *>(a.acc + a.offset + eq[q]));
+            f32x4 &sm = acc[q];
+            if (sent[q] & 1) sm.x = __builtin_fmaf(a.w, xv[q][0], sm.x);
+            if (sent[q] & 2) sm.y = __builtin_fmaf(a.w, xv[q][1], sm.y);
+            if (sent[q] & 4) sm.z = __builtin_fmaf(a.w, xv[q][2], sm.z);
+            if (sent[q] & 8) sm.w = __builtin_fmaf(a.w, xv[q][3], sm.w);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sm), ra, pq[q] * 4, 0, BUF_STORE);
         }
         if constexpr (PART != PART_DENSE) {
+            const auto rw = span_rsrc(a.wsum + a.offset + e, left * VEC * 4);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                u32x4 *wp = reinterpret_cast<u32x4 *>(a.wsum + a.offset + eq[q]);
-                u32x4 w = *wp;
+                u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rw, pq[q] * 4, 0, 0);
                 w.x += (sent[q] & 1) ? a.wi : 0u;
                 w.y += (sent[q] & 2) ? a.wi : 0u;
                 w.z += (sent[q] & 4) ? a.wi : 0u;
                 w.w += (sent[q] & 8) ? a.wi : 0u;
-                *wp = w;
+                __builtin_amdgcn_raw_buffer_store_b128(w, rw, pq[q] * 4, 0, 0);
                 if (a.count) {
                     // one byte per parameter; a client adds at most 1 and
                     // there are at most 255 clients, so no byte carries into
                     // the next
+                    const auto rc = span_rsrc(a.count + a.offset + e, left * VEC);
                     uint32_t add = 0;
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         add |= ((sent[q] >> j) & 1u) << (8 * j);
-                    *reinterpret_cast<uint32_t *>(a.count + a.offset + eq[q]) += add;
+                    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rc, pq[q], 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(c + add, rc, pq[q], 0, 0);
                 }
             }
         }
@@ -952,39 +971,44 @@ __global__ __launch_bounds__(256) void stream_acc_index_kernel(const StreamArgs 
 template <int PARTIAL>
 __global__ __launch_bounds__(256) void stream_merge_vec_kernel(const StreamArgs a, int64_t nvec)
 {
+    // a workgroup takes 256 consecutive steps of 8 parameters through
+    // buffers based at its first parameter (as the dense kernel does); a
+    // lane's two quads are quad_pair's (whole-line stores)
     const float *src = static_cast<const float *>(a.chunk);
-    for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
-        int64_t e0, e1;
-        quad_pair(v, nvec, e0, e1);
-        const f32x4 *sp0 = reinterpret_cast<const f32x4 *>(src + e0);
-        const f32x4 *sp1 = reinterpret_cast<const f32x4 *>(src + e1);
-        f32x4 *ap0 = reinterpret_cast<f32x4 *>(a.acc + a.offset + e0);
-        f32x4 *ap1 = reinterpret_cast<f32x4 *>(a.acc + a.offset + e1);
-        const f32x4 s0 = __builtin_nontemporal_load(sp0);
-        const f32x4 s1 = __builtin_nontemporal_load(sp1);
-        f32x4 lo = __builtin_nontemporal_load(ap0);
-        f32x4 hi = __builtin_nontemporal_load(ap1);
+    const int l = threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t b = (int64_t)blockIdx.x * 256; b < nvec; b += stride) {
+        const int64_t left = nvec - b, e = b * VEC;
+        const bool full = left >= 256;
+        const int p0 = full ? l * 4 : l * 8, p1 = p0 + (full ? 1024 : 4);
+        const auto rs = span_rsrc(src + e, left * VEC * 4);
+        const auto ra = span_rsrc(a.acc + a.offset + e, left * VEC * 4);
+        const f32x4 s0 = bio<DT_F32>::q(rs, p0 * 4), s1 = bio<DT_F32>::q(rs, p1 * 4);
+        f32x4 lo = bio<DT_F32>::q(ra, p0 * 4), hi = bio<DT_F32>::q(ra, p1 * 4);
         lo = f32x4{lo.x + s0.x, lo.y + s0.y, lo.z + s0.z, lo.w + s0.w};
         hi = f32x4{hi.x + s1.x, hi.y + s1.y, hi.z + s1.z, hi.w + s1.w};
-        __builtin_nontemporal_store(lo, ap0);
-        __builtin_nontemporal_store(hi, ap1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), ra, p0 * 4, 0, BUF_STORE);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), ra, p1 * 4, 0, BUF_STORE);
         if constexpr (PARTIAL) {
-            const u32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.src_wsum + e0));
-            const u32x4 a1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.src_wsum + e1));
-            u32x4 *wp0 = reinterpret_cast<u32x4 *>(a.wsum + a.offset + e0);
-            u32x4 *wp1 = reinterpret_cast<u32x4 *>(a.wsum + a.offset + e1);
-            u32x4 w0 = *wp0, w1 = *wp1;
+            const auto rsw = span_rsrc(a.src_wsum + e, left * VEC * 4);
+            const auto rw = span_rsrc(a.wsum + a.offset + e, left * VEC * 4);
+            const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(rsw, p0 * 4, 0, BUF_NT);
+            const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rsw, p1 * 4, 0, BUF_NT);
+            u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, p0 * 4, 0, 0);
+            u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, p1 * 4, 0, 0);
             w0 = u32x4{w0.x + a0.x, w0.y + a0.y, w0.z + a0.z, w0.w + a0.w};
             w1 = u32x4{w1.x + a1.x, w1.y + a1.y, w1.z + a1.z, w1.w + a1.w};
-            *wp0 = w0;
-            *wp1 = w1;
+            __builtin_amdgcn_raw_buffer_store_b128(w0, rw, p0 * 4, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(w1, rw, p1 * 4, 0, 0);
             if (a.count) {
-                const uint32_t c0 = *reinterpret_cast<const uint32_t *>(a.src_count + e0);
-                const uint32_t c1 = *reinterpret_cast<const uint32_t *>(a.src_count + e1);
-                uint32_t *cp0 = reinterpret_cast<uint32_t *>(a.count + a.offset + e0);
-                uint32_t *cp1 = reinterpret_cast<uint32_t *>(a.count + a.offset + e1);
-                *cp0 += c0;
-                *cp1 += c1;
+                const auto rsc = span_rsrc(a.src_count + e, left * VEC);
+                const auto rc = span_rsrc(a.count + a.offset + e, left * VEC);
+                const uint32_t c0 = __builtin_amdgcn_raw_buffer_load_b32(rsc, p0, 0, 0);
+                const uint32_t c1 = __builtin_amdgcn_raw_buffer_load_b32(rsc, p1, 0, 0);
+                const uint32_t d0 = __builtin_amdgcn_raw_buffer_load_b32(rc, p0, 0, 0);
+                const uint32_t d1 = __builtin_amdgcn_raw_buffer_load_b32(rc, p1, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(d0 + c0, rc, p0, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(d1 + c1, rc, p1, 0, 0);
             }
         }
     }
@@ -1024,38 +1048,48 @@ __device__ __forceinline__ float finalize_one(float acc, uint32_t W, float S, fl
 template <int BDT, int ODT, int MODE, int PARTIAL>
 __global__ __launch_bounds__(256) void stream_finalize_vec_kernel(const FinalizeArgs a, int64_t nvec)
 {
-    // an fp32 output is written as two quads per lane (whole-line stores);
-    // a bf16 output's 8 values are one contiguous 16-byte store
+    // a workgroup takes 256 consecutive steps of 8 parameters through
+    // buffers based at its first parameter; an fp32 output is written as
+    // quad_pair's two quads per lane (whole-line stores), a bf16 output's 8
+    // values as one contiguous 16-byte store
     constexpr bool SPLIT = ODT == DT_F32;
-    for (int64_t v = global_tid(); v < nvec; v += grid_threads()) {
-        int64_t e0 = v * VEC, e1 = e0 + 4;
-        if constexpr (SPLIT)
-            quad_pair(v, nvec, e0, e1);
-        const f32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.acc + e0));
-        const f32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.acc + e1));
+    constexpr int BB = BDT == DT_F32 ? 4 : 2, OB = ODT == DT_F32 ? 4 : 2;
+    const int l = threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t b = (int64_t)blockIdx.x * 256; b < nvec; b += stride) {
+        const int64_t left = nvec - b, e = b * VEC;
+        int p0 = l * 8, p1 = l * 8 + 4;
+        if constexpr (SPLIT) {
+            const bool full = left >= 256;
+            p0 = full ? l * 4 : l * 8;
+            p1 = p0 + (full ? 1024 : 4);
+        }
+        const auto ra = span_rsrc(a.acc + e, left * VEC * 4);
+        const f32x4 lo = bio<DT_F32>::q(ra, p0 * 4);
+        const f32x4 hi = bio<DT_F32>::q(ra, p1 * 4);
         const float acc[VEC] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         uint32_t W[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
         if constexpr (PARTIAL) {
-            const u32x4 w0 = *reinterpret_cast<const u32x4 *>(a.wsum + e0);
-            const u32x4 w1 = *reinterpret_cast<const u32x4 *>(a.wsum + e1);
+            const auto rw = span_rsrc(a.wsum + e, left * VEC * 4);
+            const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, p0 * 4, 0, 0);
+            const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, p1 * 4, 0, 0);
             W[0] = w0.x; W[1] = w0.y; W[2] = w0.z; W[3] = w0.w;
             W[4] = w1.x; W[5] = w1.y; W[6] = w1.z; W[7] = w1.w;
         }
-        float b[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
+        float bv[VEC] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (MODE == MODE_DELTAS || PARTIAL) {
-            if constexpr (SPLIT)
-                io<BDT>::load8_2(a.base, e0, e1, b);
-            else
-                io<BDT>::load8(a.base, e0, b);
+            const auto rb = span_rsrc(static_cast<const char *>(a.base) + e * BB, left * VEC * BB);
+            bio<BDT>::unpack(SPLIT ? bio<BDT>::load2(rb, p0 * BB, p1 * BB) : bio<BDT>::load(rb, p0 * BB), bv);
         }
         float r[VEC];
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
-            r[j] = finalize_one<BDT, ODT, MODE, PARTIAL>(acc[j], W[j], a.S, b[j], a.zero_fill);
+            r[j] = finalize_one<BDT, ODT, MODE, PARTIAL>(acc[j], W[j], a.S, bv[j], a.zero_fill);
+        const auto ro = span_rsrc(static_cast<char *>(a.out) + e * OB, left * VEC * OB);
         if constexpr (SPLIT)
-            io<ODT>::store8_2(a.out, e0, e1, r);
+            bio<DT_F32>::store2(ro, p0 * 4, p1 * 4, r);
         else
-            io<ODT>::store8(a.out, e0, r);
+            bio<DT_BF16>::store(ro, p0 * 2, r);
     }
 }
 
