@@ -1386,8 +1386,11 @@ sparse_merge_kernel(const SparseArgs a)
                 s_acc[lq + j] = 0.0f;
             }
             if (a.aligned && eq + 4 <= t1) {
-                float b4[4];
-                io<DT_F32>::load4(a.base, eq, b4);
+                // through buffers over the tile's part of each array (nt
+                // loads, sc1 nt stores)
+                const int64_t tn = t1 - t0;
+                const f32x4 bq = bio<DT_F32>::q(span_rsrc(a.base + t0, tn * 4), lq * 4);
+                const float b4[4] = {bq.x, bq.y, bq.z, bq.w};
                 float r[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -1398,21 +1401,21 @@ sparse_merge_kernel(const SparseArgs a)
                         r[j] = b4[j];
                     }
                 }
-                __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]},
-                                            reinterpret_cast<f32x4 *>(a.out + eq));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{r[0], r[1], r[2], r[3]}),
+                                                       span_rsrc(a.out + t0, tn * 4), lq * 4, 0, BUF_STORE);
                 if (a.counts) {
                     if (a.counts_u32)
-                        __builtin_nontemporal_store(
+                        __builtin_amdgcn_raw_buffer_store_b128(
                             u32x4{cnt[0], cnt[1], cnt[2], cnt[3]},
-                            reinterpret_cast<u32x4 *>(static_cast<uint32_t *>(a.counts) + eq));
+                            span_rsrc(static_cast<uint32_t *>(a.counts) + t0, tn * 4), lq * 4, 0, BUF_STORE);
                     else
-                        __builtin_nontemporal_store(
+                        __builtin_amdgcn_raw_buffer_store_b32(
                             cnt[0] | (cnt[1] << 8) | (cnt[2] << 16) | (cnt[3] << 24),
-                            reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(a.counts) + eq));
+                            span_rsrc(static_cast<uint8_t *>(a.counts) + t0, tn), lq, 0, BUF_STORE);
                 }
                 if (a.wsum)
-                    __builtin_nontemporal_store(u32x4{W[0], W[1], W[2], W[3]},
-                                                reinterpret_cast<u32x4 *>(a.wsum + eq));
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{W[0], W[1], W[2], W[3]},
+                                                           span_rsrc(a.wsum + t0, tn * 4), lq * 4, 0, BUF_STORE);
             } else {
                 for (int j = 0; j < 4; ++j) {
                     const int64_t e = eq + j;
