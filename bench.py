@@ -472,12 +472,14 @@ def bench_sparse(steps=10, warmup=2):
 
 def bench_sparse_stream(clients=20):
     """Client-at-a-time sparse accumulate: the 10^9-parameter top-10% lists
-    of the sparse workload, each client's (index, value) pairs scattered into
+    of the sparse workload, each client's (index, value) pairs entered into
     the streaming accumulator in partial mode (fp32 sum, uint32 weight sum,
     uint8 count per parameter), then one finalize.  Pair-level bytes are 12 B
     read plus 18 B of read-modify-write per pair; DRAM moves whole lines, so
     the line-level figure counts every 64-byte line of the three arrays a
-    client touches, read and written, plus the pairs."""
+    client touches, read and written, plus the pairs.  The default path
+    reads and writes the accumulator in dense tiles at this density; the
+    scatter path (FA_OPT_INDEX_TILES = 1) is timed on the same lists."""
     import torch
     import synth.device as sd
     import weighted_model_update_amd as fa
@@ -490,34 +492,47 @@ def bench_sparse_stream(clients=20):
         lines.append(int(torch.unique_consecutive(i // 16).numel()) * 2 * 64 * 2   # acc, wsum
                      + int(torch.unique_consecutive(i // 64).numel()) * 64 * 2)    # count
     out = torch.empty(N, dtype=torch.float32, device="cuda")
-    times = []
-    with fa.StreamingAccumulator(N, mode="deltas", partial=True, chunk_bytes=1 << 20, n_slots=2) as acc:
-        for k in range(K):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
-            acc.accumulate(k, int(n[k]), val[k], indices=idx[k])
-            e.record()
-            times.append((s, e))
-        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fs.record()
-        acc.finalize(base, out)
-        fe.record()
-        acc.sync()
-    torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in times[1:]]     # the first client warms up
-    ms = sum(per) / len(per)
-    pair_bytes = 30 * sum(nnz[1:]) / len(per)
-    line_bytes = (12 * sum(nnz[1:]) + sum(lines[1:])) / len(per)
-    fin_ms = fs.elapsed_time(fe)
+
+    def run(path):
+        fa.fedavg_set_option(fa.FA_OPT_INDEX_TILES, path)
+        times = []
+        try:
+            with fa.StreamingAccumulator(N, mode="deltas", partial=True, chunk_bytes=1 << 20, n_slots=2) as acc:
+                for k in range(K):
+                    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    s.record()
+                    acc.accumulate(k, int(n[k]), val[k], indices=idx[k])
+                    e.record()
+                    times.append((s, e))
+                fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                fs.record()
+                acc.finalize(base, out)
+                fe.record()
+                acc.sync()
+        finally:
+            fa.fedavg_set_option(fa.FA_OPT_INDEX_TILES, 0)
+        torch.cuda.synchronize()
+        per = [a.elapsed_time(b) for a, b in times[1:]]     # the first client warms up
+        return sum(per) / len(per), fs.elapsed_time(fe)
+
+    ms, fin_ms = run(0)
+    ms_scatter, _ = run(1)
+    pair_bytes = 30 * sum(nnz[1:]) / (K - 1)
+    line_bytes = (12 * sum(nnz[1:]) + sum(lines[1:])) / (K - 1)
     del idx, val, base, out
     free_gpu()
     return {"K": K, "N": N, "pairs_per_client": nnz[0], "ms_per_client": ms,
             "pair_bytes_per_client": pair_bytes, "line_bytes_per_client": line_bytes,
             "hbm_gbs_lines": line_bytes / (ms * 1e-3) / 1e9,
             "hbm_frac_lines": line_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "ms_per_client_scatter": ms_scatter,
+            "hbm_frac_lines_scatter": line_bytes / (ms_scatter * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "finalize_ms": fin_ms, "finalize_bytes": 13 * N,
-            "note": "each client's scatter moves whole 64-byte lines of acc, wsum and count; the one-pass "
-                    "sparse merge (mode sparse) avoids this"}
+            "note": "default path: each client's list is checked, then the accumulator's tiles holding it "
+                    "are read and written whole (about 19 GB per client at this density, the sums and "
+                    "weight sums of 64-byte runs no entry touched not written); the scatter path moves "
+                    "the touched lines as scattered read-modify-writes; the one-pass sparse merge "
+                    "(mode sparse) avoids both"}
 
 
 def bench_checksum(reps=10):
@@ -998,7 +1013,8 @@ def main():
         log(f"hierarchical: {modes['hierarchical']['ms_per_merge']:.3f} ms per silo merge")
     if "sparse_stream" in only:
         modes["sparse_stream"] = bench_sparse_stream()
-        log(f"sparse_stream: {modes['sparse_stream']['ms_per_client']:.3f} ms per client")
+        log(f"sparse_stream: {modes['sparse_stream']['ms_per_client']:.3f} ms per client "
+            f"({modes['sparse_stream']['ms_per_client_scatter']:.3f} scattered)")
     if "windows" in only:
         modes["windows"] = bench_windows(args.stream_clients)
         log(f"windows: {modes['windows']['wall_s']:.2f} s in {modes['windows']['windows']} windows "

@@ -210,6 +210,12 @@ int fedavg_begin(fa_handle *h, int64_t N, fa_mode mode, int partial, float *acc,
  *             value j).  Violations are detected on the device and reported
  *             by fedavg_sync as FA_ERR_INDEX; the bad entries are skipped.
  *             The caller must not send one parameter twice for a client.
+ *             A list dense enough (FA_OPT_INDEX_TILES) is checked first and
+ *             then applied by reading and writing the accumulator's
+ *             2048-parameter tiles that hold it (a device word in the
+ *             staging header carries the check's verdict); other lists, and
+ *             lists the check refuses, are scattered.  Both give the same
+ *             bits.
  *             mask and indices live where chunk lives.
  * An empty chunk (len == 0) enters the client but carries no parameter, so
  * the ordering and tiling rules above do not apply to it.
@@ -513,9 +519,20 @@ typedef enum {
     FA_OPT_SPARSE_TILE = 5,            /* sparse merge: parameters per LDS tile,
                                           512, 1024, 2048 (default), 4096 or
                                           8192 */
-    FA_OPT_TOPK_SAMPLED = 6            /* top-k: 1 (default) bounds the
+    FA_OPT_TOPK_SAMPLED = 6,           /* top-k: 1 (default) bounds the
                                           threshold from a sample first; 0
                                           always takes the three-pass path */
+    FA_OPT_INDEX_TILES = 7             /* fedavg_accumulate with indices:
+                                          0 (default) reads and writes the
+                                          accumulator in dense tiles when the
+                                          list holds at least 2^16 entries
+                                          and one parameter in 16 of
+                                          [offset, N), else scatters; 1
+                                          always scatters; 2 always tiles.
+                                          Tiles need N % 4 == 0 and 16-byte
+                                          aligned sums and weight sums
+                                          (4-byte aligned counts); otherwise
+                                          the call scatters */
 } fa_option;
 
 /* Set one option; FA_ERR_ARG for an unknown option, FA_ERR_RANGE for a value

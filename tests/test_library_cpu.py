@@ -66,6 +66,9 @@ def test_host_side_argument_errors_need_no_device():
     assert lib.fedavg_set_option(99, 1) == -1
     assert lib.fedavg_set_option(fa.FA_OPT_SPARSE_BLOCKS, (1 << 19) + 1) == -3
     assert lib.fedavg_set_option(fa.FA_OPT_TOPK_SAMPLED, 2) == -3
+    assert lib.fedavg_set_option(fa.FA_OPT_INDEX_TILES, 3) == -3
+    assert lib.fedavg_set_option(fa.FA_OPT_INDEX_TILES, -1) == -3
+    assert lib.fedavg_set_option(fa.FA_OPT_INDEX_TILES, 0) == 0
     # residency: -1 (by client count, the default), 0 (no cap) .. 32
     assert lib.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, -2) == -3
     assert lib.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, 33) == -3

@@ -7,7 +7,7 @@ in include/fedavg.h (libfedavg.so); this package is its torch binding.
 from .fedavg import (  # noqa: F401
     FA_F32, FA_BF16, FA_WEIGHTS, FA_DELTAS, FA_DELTAS_ZERO_FILL, FA_COUNT_U8, FA_COUNT_U32, FA_MAX_CLIENTS, FA_MAX_N,
     FA_OPT_BLOCKS_PER_CU, FA_OPT_MASK_VECTORS_PER_BLOCK, FA_OPT_SPARSE_BLOCKS, FA_OPT_RESIDENT_PER_CU, FA_OPT_SPARSE_TILE,
-    FA_OPT_TOPK_SAMPLED,
+    FA_OPT_TOPK_SAMPLED, FA_OPT_INDEX_TILES,
     EXPORTS, FedAvgError, StreamingAccumulator, load, library_path,
     fedavg_abi_version, fedavg_set_option, fedavg_aggregate, fedavg_workspace_size,
     fedavg_begin, fedavg_accumulate, fedavg_finalize, fedavg_sync, fedavg_destroy,

@@ -64,6 +64,7 @@ int64_t g_resident_per_cu = -1;  // dense kernel: resident workgroups per CU (0:
 int64_t g_mask_vpb = 2048;       // masked kernel: 8-parameter vectors per block
 int64_t g_sparse_blocks = 0;     // sparse merge: parameter ranges (0: the default rule)
 int64_t g_sparse_tile = fa::SP_DEFAULT_TILE;
+int64_t g_index_tiles = 0;       // client-at-a-time sparse: 0 by density, 1 scatter, 2 tiles
 // Resident workgroups per CU of the streaming kernels (by residency_lds).
 // Measured on MI355X over 2^31 parameters held in HBM, as fractions of HBM
 // peak, caps 0 (none), 1, 2, 3, 4, 6: the accumulate (a bf16 chunk into the
@@ -78,6 +79,7 @@ constexpr int64_t SPARSE_RANGE_TILES = 4;  // default: tiles per range
 constexpr int64_t SPARSE_MIN_RANGES = 4096; // default: ranges while there are that many tiles
 constexpr int64_t SPARSE_MIN_TILE = 512;
 constexpr size_t HEADER_BYTES = 256;
+constexpr int64_t INDEX_TILES_MIN_LEN = 1 << 16; // shorter lists are scattered
 
 int cu_count()
 {
@@ -221,6 +223,8 @@ struct fa_stream_state {
     bool finalized = false;
     std::unordered_map<int, Client> clients;
     int *err_flag() { return reinterpret_cast<int *>(staging); }
+    // the tiled index path's verdict on a list (its own 128-byte line)
+    int *list_gate() { return reinterpret_cast<int *>(staging + 128); }
     uint64_t total_weight() const
     {
         uint64_t S = 0;
@@ -349,6 +353,11 @@ int fedavg_set_option(int option, int64_t value)
         if (value != 0 && value != 1)
             return fail(FA_ERR_RANGE, "top-k sampled path must be 0 or 1");
         fa::topk_set_sampled((int)value);
+        return ok();
+    case FA_OPT_INDEX_TILES:
+        if (value < 0 || value > 2)
+            return fail(FA_ERR_RANGE, "index tiles must be 0, 1 or 2");
+        g_index_tiles = value;
         return ok();
     case FA_OPT_SPARSE_BLOCKS:
         if (value < 0 || value > SPARSE_MAX_BLOCKS)
@@ -807,7 +816,16 @@ int fedavg_accumulate(fa_handle h, int client_id, int64_t n_k, const void *chunk
     }
 
     if (indices) {
-        e = fa::launch_stream_accumulate_indices(a, dtype, st.compute);
+        // Dense tiles pay once the list holds about one parameter in 16 of
+        // the span it may address: its scattered updates would then touch
+        // most cache lines of the sums, weight sums and counts anyway.  They
+        // need whole 16-byte quads (N a multiple of 4, aligned arrays).
+        const int64_t span = st.N - offset;
+        const bool can_tile = st.N % 4 == 0 && aligned16(st.acc) && aligned16(st.wsum) &&
+                              (reinterpret_cast<uintptr_t>(st.count) & 3u) == 0;
+        const bool tiled = can_tile && (g_index_tiles == 2 ||
+                                        (g_index_tiles == 0 && len >= INDEX_TILES_MIN_LEN && len >= span / 16));
+        e = fa::launch_stream_accumulate_indices(a, dtype, tiled, st.list_gate(), st.compute);
     } else {
         const int part = !st.partial ? fa::PART_DENSE : (mask ? fa::PART_MASK : fa::PART_RANGE);
         const bool aligned = (offset % fa::VEC) == 0 && aligned16(a.chunk) &&

@@ -65,6 +65,9 @@ struct StreamArgs {
     // sums and client counts (chunk then holds its fp32 sums)
     const uint32_t *src_wsum;
     const uint8_t *src_count;
+    // client-at-a-time sparse accumulate: when set, the scatter kernel runs
+    // only if *gate is nonzero (the list failed the tiled path's check)
+    const int *gate;
 };
 
 struct FinalizeArgs {
@@ -115,7 +118,13 @@ hipError_t launch_masked(const MaskedArgs &a, int xdt, int odt, int bdt, int mod
                          hipStream_t s);
 hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool aligned,
                                     int64_t grid_cap, int resident, hipStream_t s);
-hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStream_t s);
+// Client-at-a-time sparse accumulate.  tiled: check the list, and if it is
+// sorted and inside the accumulator apply it over dense tiles, else scatter
+// it; gate is a device word of scratch the tiled path needs.
+hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, bool tiled, int *gate, hipStream_t s);
+// Parameters per tile of the tiled index accumulate (fp32 sums, weight sums
+// and counts of one tile are read and written whole).
+constexpr int IT_TILE = 2048;
 hipError_t launch_stream_merge(const StreamArgs &a, bool partial, bool aligned, int64_t cap,
                                int resident, hipStream_t s);
 hipError_t launch_stream_finalize(const FinalizeArgs &a, int bdt, int odt, int mode, int partial,

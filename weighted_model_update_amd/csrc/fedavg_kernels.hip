@@ -947,6 +947,8 @@ __global__ __launch_bounds__(256) void stream_acc_index_kernel(const StreamArgs 
     // predecessor; the bounds are tested on the index itself, so neither a
     // negative one (also in a run that increases) nor offset + index
     // wrapping past 2^63 can address memory outside the accumulator
+    if (a.gate && *a.gate == 0)
+        return; // the tiled path took this list
     const int64_t span = a.N - a.offset;
     for (int64_t j = global_tid(); j < a.len; j += grid_threads()) {
         const int64_t ix = a.idx[j];
@@ -1451,6 +1453,150 @@ sparse_merge_kernel(const SparseArgs a)
         *a.err = FA_ERR_INDEX;
 }
 
+// ================================================================ tiled index accumulate
+
+// Client-at-a-time sparse accumulate over dense tiles.  A client's list of
+// about one parameter in 16 or more touches nearly every cache line of the
+// accumulator's fp32 sums, weight sums and counts, so scattered updates move
+// whole lines anyway, as read-modify-writes interleaved at random; reading
+// and writing the tiles that hold the list as whole streams costs about as
+// many bytes in long runs instead.
+//
+// The tiled path needs a sorted list inside the accumulator: a first kernel
+// checks it and sets *gate when it is not, and the tiled kernel then leaves
+// the call to the scatter kernel, which reports and skips the bad entries.
+__global__ __launch_bounds__(256) void stream_index_check_kernel(const StreamArgs a, int *gate)
+{
+    const int64_t span = a.N - a.offset;
+    bool bad = false;
+    for (int64_t j = global_tid(); j < a.len; j += grid_threads()) {
+        const int64_t ix = a.idx[j];
+        const int64_t prev = j > 0 ? a.idx[j - 1] : -1;
+        bad = bad || ix < 0 || ix >= span || ix <= prev;
+    }
+    if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0)
+        *gate = 1;
+}
+
+// Each workgroup takes IT_TPW consecutive tiles of IT_TILE parameters,
+// tiles aligned to the accumulator, counted from the one holding the list's
+// first parameter up to the one holding its last.  Per tile, each lane reads
+// the sums, weight sums and counts of its two 4-parameter quads (at 4 tid and
+// half a tile further: whole-line accesses); the tile's entries, consecutive
+// in the sorted list, arrive in batches of 256 from the list cursor (the
+// in-tile ones are a prefix, counted by wave ballots) and are scattered into
+// LDS as a value and a presence bit; then each lane applies its present
+// parameters with the scatter kernel's operations (acc = fma(n_k, x, acc),
+// wsum += n_k, count += 1) and writes its quads back.  A 64-byte run of sums
+// (or weight sums) that no entry touched, four lanes' quads, is not written.
+//
+// Requesting the next tile's batch and quads while the current tile is
+// applied (two register sets, every load through a range-bounded buffer so
+// none sat under a branch) ran no faster: 3.74-3.79 against 3.78 ms per
+// 10^8-entry client of a 10^9-parameter accumulator.
+constexpr int IT_TPW = 4;
+
+template <int DT>
+__global__ __launch_bounds__(256) void stream_acc_index_tile_kernel(const StreamArgs a, const int *gate)
+{
+    __shared__ float s_val[IT_TILE];
+    __shared__ uint32_t s_bit[IT_TILE / 32];
+    __shared__ int s_count[2][4];
+    __shared__ int64_t s_p;
+    if (*gate != 0 || a.len == 0)
+        return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the list's ends, as parameters of the accumulator (the list is sorted)
+    const int64_t first = a.offset + a.idx[0];
+    const int64_t last = a.offset + a.idx[a.len - 1];
+    const int64_t tb = first / IT_TILE + (int64_t)blockIdx.x * IT_TPW;
+    const int64_t tl = last / IT_TILE;
+    if (tb > tl)
+        return;
+    const int64_t te = min(tb + IT_TPW, tl + 1);
+    if (tid < IT_TILE / 32)
+        s_bit[tid] = 0u;
+    if (tid == 0)
+        s_p = blockIdx.x == 0 ? 0
+                              : sparse_lower_bound(a.idx, 0, a.len, tb * IT_TILE - a.offset, -1, a.N - a.offset);
+    __syncthreads();
+    int64_t p = s_p;
+    int parity = 0;
+    const int q0 = tid * 4, q1 = IT_TILE / 2 + tid * 4;
+    for (int64_t t = tb; t < te; ++t) {
+        const int64_t t0 = t * IT_TILE, t1 = t0 + IT_TILE;
+        const int64_t tn = min((int64_t)IT_TILE, a.N - t0);
+        const auto ra = span_rsrc(a.acc + t0, tn * 4);
+        const auto rw = span_rsrc(a.wsum + t0, tn * 4);
+        const auto rc = span_rsrc(a.count + t0, a.count ? tn : 0);
+        const f32x4 c0 = bio<DT_F32>::q(ra, q0 * 4), c1 = bio<DT_F32>::q(ra, q1 * 4);
+        const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, q0 * 4, 0, BUF_NT);
+        const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, q1 * 4, 0, BUF_NT);
+        uint32_t n0 = __builtin_amdgcn_raw_buffer_load_b32(rc, q0, 0, BUF_NT);
+        uint32_t n1 = __builtin_amdgcn_raw_buffer_load_b32(rc, q1, 0, BUF_NT);
+        int c;
+        do {
+            const int64_t q = p + tid;
+            int64_t ix = INT64_MAX;
+            float v = 0.0f;
+            if (q < a.len) {
+                ix = a.offset + a.idx[q];
+                v = io<DT>::load1(a.chunk, q);
+            }
+            const bool in = ix < t1;
+            const uint64_t bal = __ballot(in);
+            if (lane == 0)
+                s_count[parity][wave] = __popcll(bal);
+            __syncthreads();
+            c = s_count[parity][0] + s_count[parity][1] + s_count[parity][2] + s_count[parity][3];
+            parity ^= 1;
+            if (in) {
+                const int l = (int)(ix - t0);
+                s_val[l] = v;
+                atomicOr(&s_bit[l >> 5], 1u << (l & 31));
+            }
+            p += c;
+        } while (c == 256 && p < a.len);
+        __syncthreads();
+        const uint32_t b0 = (s_bit[q0 >> 5] >> (q0 & 31)) & 15u;
+        const uint32_t b1 = (s_bit[q1 >> 5] >> (q1 & 31)) & 15u;
+        // 16 parameters (four lanes' quads) share a 64-byte run
+        const bool t0run = (s_bit[q0 >> 5] >> (q0 & 16)) & 0xFFFFu;
+        const bool t1run = (s_bit[q1 >> 5] >> (q1 & 16)) & 0xFFFFu;
+        float x0[4] = {c0.x, c0.y, c0.z, c0.w}, x1[4] = {c1.x, c1.y, c1.z, c1.w};
+        uint32_t y0[4] = {w0.x, w0.y, w0.z, w0.w}, y1[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if ((b0 >> j) & 1u) {
+                x0[j] = __builtin_fmaf(a.w, s_val[q0 + j], x0[j]);
+                y0[j] += a.wi;
+                n0 += 1u << (8 * j);
+            }
+            if ((b1 >> j) & 1u) {
+                x1[j] = __builtin_fmaf(a.w, s_val[q1 + j], x1[j]);
+                y1[j] += a.wi;
+                n1 += 1u << (8 * j);
+            }
+        }
+        if (t0run) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{x0[0], x0[1], x0[2], x0[3]}),
+                                                   ra, q0 * 4, 0, BUF_STORE);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{y0[0], y0[1], y0[2], y0[3]}, rw, q0 * 4, 0, BUF_STORE);
+        }
+        if (t1run) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{x1[0], x1[1], x1[2], x1[3]}),
+                                                   ra, q1 * 4, 0, BUF_STORE);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{y1[0], y1[1], y1[2], y1[3]}, rw, q1 * 4, 0, BUF_STORE);
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(n0, rc, q0, 0, BUF_STORE);
+        __builtin_amdgcn_raw_buffer_store_b32(n1, rc, q1, 0, BUF_STORE);
+        __syncthreads(); // every lane has read the tile's bits and values
+        if (tid < IT_TILE / 32)
+            s_bit[tid] = 0u;
+        // the next tile's first batch barrier orders these zeroes before its scatter
+    }
+}
+
 // ================================================================ checksum
 
 __device__ __forceinline__ uint64_t fmix64(uint64_t k)
@@ -1897,13 +2043,37 @@ hipError_t launch_stream_accumulate(const StreamArgs &a, int dt, int part, bool 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, hipStream_t s)
+hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, bool tiled, int *gate, hipStream_t s)
 {
     const unsigned g = grid_for(a.len, 256, 65536);
+    if (!tiled) {
+        StreamArgs b = a;
+        b.gate = nullptr;
+        if (dt == DT_F32)
+            stream_acc_index_kernel<DT_F32><<<g, 256, 0, s>>>(b);
+        else
+            stream_acc_index_kernel<DT_BF16><<<g, 256, 0, s>>>(b);
+        return hipGetLastError();
+    }
+    fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t *>(gate), 1, 0u);
+    stream_index_check_kernel<<<g, 256, 0, s>>>(a, gate);
+    // tiles from the list's first parameter to its last: at most this many
+    // workgroups of IT_TPW tiles each
+    const int64_t tiles = (a.N - a.offset) / IT_TILE + 2;
+    const unsigned gt = (unsigned)((tiles + IT_TPW - 1) / IT_TPW);
     if (dt == DT_F32)
-        stream_acc_index_kernel<DT_F32><<<g, 256, 0, s>>>(a);
+        stream_acc_index_tile_kernel<DT_F32><<<gt, 256, 0, s>>>(a, gate);
     else
-        stream_acc_index_kernel<DT_BF16><<<g, 256, 0, s>>>(a);
+        stream_acc_index_tile_kernel<DT_BF16><<<gt, 256, 0, s>>>(a, gate);
+    // the scatter kernel runs only for a list the check refused: few
+    // workgroups, each striding over the list
+    StreamArgs b = a;
+    b.gate = gate;
+    const unsigned gs = g < 2048u ? g : 2048u;
+    if (dt == DT_F32)
+        stream_acc_index_kernel<DT_F32><<<gs, 256, 0, s>>>(b);
+    else
+        stream_acc_index_kernel<DT_BF16><<<gs, 256, 0, s>>>(b);
     return hipGetLastError();
 }
 

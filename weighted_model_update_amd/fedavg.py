@@ -20,6 +20,7 @@ FA_COUNT_U8, FA_COUNT_U32 = 0, 1
 FA_OPT_BLOCKS_PER_CU, FA_OPT_MASK_VECTORS_PER_BLOCK, FA_OPT_SPARSE_BLOCKS, FA_OPT_RESIDENT_PER_CU = 1, 2, 3, 4
 FA_OPT_SPARSE_TILE = 5
 FA_OPT_TOPK_SAMPLED = 6
+FA_OPT_INDEX_TILES = 7
 FA_MAX_CLIENTS = 64
 FA_MAX_N = 1 << 40
 
