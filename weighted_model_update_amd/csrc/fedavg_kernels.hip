@@ -16,6 +16,8 @@
 // accumulation and nearest-even rounding of weights ("NVFP4 training with JAX
 // and MaxText", training-recipe section).
 #include <atomic>
+#include <map>
+#include <mutex>
 
 #include "fedavg_internal.h"
 
@@ -1490,11 +1492,16 @@ __global__ __launch_bounds__(256) void stream_index_check_kernel(const StreamArg
 // wsum += n_k, count += 1) and writes its quads back.  A 64-byte run of sums
 // (or weight sums) that no entry touched, four lanes' quads, is not written.
 //
-// Requesting the next tile's batch and quads while the current tile is
-// applied (two register sets, every load through a range-bounded buffer so
-// none sat under a branch) ran no faster: 3.74-3.79 against 3.78 ms per
-// 10^8-entry client of a 10^9-parameter accumulator.
-constexpr int IT_TPW = 4;
+// One tile per workgroup and 7 resident workgroups per CU, measured on a
+// 10^8-entry client of a 10^9-parameter accumulator (ms per client with the
+// check): tiles per workgroup 1, 2, 4, 8 at no cap 3.44, 3.53, 3.58, 3.66;
+// one tile at caps of 4, 5, 6, 7, 8 workgroups per CU 3.74, 3.75, 3.29,
+// 3.10, 3.44.  Requesting the next tile's batch and quads while the current
+// tile is applied (two register sets, every load through a range-bounded
+// buffer so none sat under a branch) ran no faster: 3.74-3.79 against 3.78
+// ms at 4 tiles per workgroup.
+constexpr int IT_TPW = 1;
+constexpr int IT_RESIDENT = 7;
 
 template <int DT>
 __global__ __launch_bounds__(256) void stream_acc_index_tile_kernel(const StreamArgs a, const int *gate)
@@ -1529,9 +1536,6 @@ __global__ __launch_bounds__(256) void stream_acc_index_tile_kernel(const Stream
         const auto ra = span_rsrc(a.acc + t0, tn * 4);
         const auto rw = span_rsrc(a.wsum + t0, tn * 4);
         const auto rc = span_rsrc(a.count + t0, a.count ? tn : 0);
-        const f32x4 c0 = bio<DT_F32>::q(ra, q0 * 4), c1 = bio<DT_F32>::q(ra, q1 * 4);
-        const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, q0 * 4, 0, BUF_NT);
-        const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, q1 * 4, 0, BUF_NT);
         uint32_t n0 = __builtin_amdgcn_raw_buffer_load_b32(rc, q0, 0, BUF_NT);
         uint32_t n1 = __builtin_amdgcn_raw_buffer_load_b32(rc, q1, 0, BUF_NT);
         int c;
@@ -1563,6 +1567,16 @@ __global__ __launch_bounds__(256) void stream_acc_index_tile_kernel(const Stream
         // 16 parameters (four lanes' quads) share a 64-byte run
         const bool t0run = (s_bit[q0 >> 5] >> (q0 & 16)) & 0xFFFFu;
         const bool t1run = (s_bit[q1 >> 5] >> (q1 & 16)) & 0xFFFFu;
+        f32x4 c0 = {0, 0, 0, 0}, c1 = {0, 0, 0, 0};
+        u32x4 w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
+        if (t0run) {
+            c0 = bio<DT_F32>::q(ra, q0 * 4);
+            w0 = __builtin_amdgcn_raw_buffer_load_b128(rw, q0 * 4, 0, BUF_NT);
+        }
+        if (t1run) {
+            c1 = bio<DT_F32>::q(ra, q1 * 4);
+            w1 = __builtin_amdgcn_raw_buffer_load_b128(rw, q1 * 4, 0, BUF_NT);
+        }
         float x0[4] = {c0.x, c0.y, c0.z, c0.w}, x1[4] = {c1.x, c1.y, c1.z, c1.w};
         uint32_t y0[4] = {w0.x, w0.y, w0.z, w0.w}, y1[4] = {w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
@@ -1852,8 +1866,9 @@ static int lds_bytes_per_cu()
 // Streaming kernels over HBM run fastest with few resident waves per CU (a
 // measured property of MI355X when reads and writes mix: more waves in
 // flight only add DRAM read/write turnarounds).  Residency is capped by
-// reserving dynamic LDS: a request between 1/(cap+1) and 1/cap of the CU's
-// LDS admits exactly `cap` workgroups per CU.  The kernels do not use it.
+// reserving dynamic LDS: a workgroup's LDS (its own plus the request)
+// between 1/(cap+1) and 1/cap of the CU's LDS admits exactly `cap`
+// workgroups per CU.  The kernels do not use the request.
 template <typename F>
 static size_t residency_lds(F *kernel, int cap)
 {
@@ -1862,19 +1877,39 @@ static size_t residency_lds(F *kernel, int cap)
     const int lds = lds_bytes_per_cu();
     if (lds <= 0)
         return 0;
-    const size_t bytes = ((size_t)lds / cap + (size_t)lds / (cap + 1)) / 2;
-    // the largest request allowed so far, per kernel instantiation and device
-    static std::atomic<int> configured_max[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    if (hipGetDevice(&dev) != hipSuccess)
         return 0;
-    if ((int)bytes > configured_max[dev].load(std::memory_order_relaxed)) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess) {
+    // per kernel and device: the kernel's own LDS, and the largest request
+    // allowed so far
+    struct Entry {
+        size_t own = 0, allowed = 0;
+        bool known = false;
+    };
+    static std::mutex mu;
+    static std::map<std::pair<const void *, int>, Entry> table;
+    const void *fn = reinterpret_cast<const void *>(kernel);
+    std::lock_guard<std::mutex> lock(mu);
+    Entry &en = table[{fn, dev}];
+    if (!en.known) {
+        hipFuncAttributes attr;
+        if (hipFuncGetAttributes(&attr, fn) != hipSuccess) {
             (void)hipGetLastError();
             return 0;
         }
-        configured_max[dev].store((int)bytes, std::memory_order_relaxed);
+        en.own = attr.sharedSizeBytes;
+        en.known = true;
+    }
+    const size_t total = ((size_t)lds / cap + (size_t)lds / (cap + 1)) / 2;
+    if (total <= en.own)
+        return 0;
+    const size_t bytes = total - en.own;
+    if (bytes > en.allowed) {
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        en.allowed = bytes;
     }
     return bytes;
 }
@@ -2061,10 +2096,13 @@ hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, bool ti
     // workgroups of IT_TPW tiles each
     const int64_t tiles = (a.N - a.offset) / IT_TILE + 2;
     const unsigned gt = (unsigned)((tiles + IT_TPW - 1) / IT_TPW);
-    if (dt == DT_F32)
-        stream_acc_index_tile_kernel<DT_F32><<<gt, 256, 0, s>>>(a, gate);
-    else
-        stream_acc_index_tile_kernel<DT_BF16><<<gt, 256, 0, s>>>(a, gate);
+    if (dt == DT_F32) {
+        auto *k = &stream_acc_index_tile_kernel<DT_F32>;
+        k<<<gt, 256, residency_lds(k, IT_RESIDENT), s>>>(a, gate);
+    } else {
+        auto *k = &stream_acc_index_tile_kernel<DT_BF16>;
+        k<<<gt, 256, residency_lds(k, IT_RESIDENT), s>>>(a, gate);
+    }
     // the scatter kernel runs only for a list the check refused: few
     // workgroups, each striding over the list
     StreamArgs b = a;
