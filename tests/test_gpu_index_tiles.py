@@ -183,3 +183,27 @@ def test_unaligned_or_ragged_accumulators_scatter():
             acc.sync()
             res.append(acc.acc[:N].clone())
     assert torch.equal(res[0].view(torch.int32), res[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("flaw", [1, 2, 64, 127, 128, 129, 256])
+def test_the_check_finds_a_single_flaw_anywhere(flaw):
+    """A 257-entry list (an odd length) whose only flaw is one entry equal to
+    the one before it: inside a pair, between pairs, between two waves' runs
+    of 128 entries and in the unpaired last entry.  Forced tiles refuse the
+    list and the scatter path reports it and lands the rest, as alone."""
+    N = 4096
+    rel = np.arange(0, 3 * 257, 3, dtype=np.int64)
+    rel[flaw] = rel[flaw - 1]
+    vals = torch.arange(1, 258, dtype=torch.float32, device="cuda")
+    got = []
+    for path in (SCATTER, TILES):
+        fa.fedavg_set_option(fa.FA_OPT_INDEX_TILES, path)
+        with fa.StreamingAccumulator(N, mode="weights", partial=True, chunk_bytes=4 * N) as acc:
+            acc.accumulate(0, 3, vals, offset=0, indices=torch.from_numpy(rel).cuda())
+            with pytest.raises(fa.FedAvgError) as e:
+                acc.sync()
+            assert e.value.code == -7
+            got.append((acc.acc[:N].clone(), acc.wsum[:N].clone(), acc.count[:N].clone()))
+    for x, y in zip(*got):
+        assert torch.equal(x, y)
+    assert int(torch.count_nonzero(got[1][2])) == 256
