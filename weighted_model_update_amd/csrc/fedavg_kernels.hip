@@ -1484,7 +1484,7 @@ __global__ __launch_bounds__(256) void stream_index_check_kernel(const StreamArg
 // them from the lane below) ran slower: 3.16 against 3.10 ms per client
 // with the tiles.
 
-// Each workgroup takes IT_TPW consecutive tiles of IT_TILE parameters,
+// Each workgroup takes tpw consecutive tiles of IT_TILE parameters,
 // tiles aligned to the accumulator, counted from the one holding the list's
 // first parameter up to the one holding its last.  Per tile, each lane reads
 // the sums, weight sums and counts of its two 4-parameter quads (at 4 tid and
@@ -1496,7 +1496,8 @@ __global__ __launch_bounds__(256) void stream_index_check_kernel(const StreamArg
 // wsum += n_k, count += 1) and writes its quads back.  A 64-byte run of sums
 // (or weight sums) that no entry touched, four lanes' quads, is not written.
 //
-// One tile per workgroup and 7 resident workgroups per CU, measured on a
+// One tile per workgroup (tpw, the tiles per workgroup, is 1 below 2^35
+// parameters) and 7 resident workgroups per CU, measured on a
 // 10^8-entry client of a 10^9-parameter accumulator (ms per client with the
 // check): tiles per workgroup 1, 2, 4, 8 at no cap 3.44, 3.53, 3.58, 3.66;
 // one tile at caps of 4, 5, 6, 7, 8 workgroups per CU 3.74, 3.75, 3.29,
@@ -1504,11 +1505,11 @@ __global__ __launch_bounds__(256) void stream_index_check_kernel(const StreamArg
 // tile is applied (two register sets, every load through a range-bounded
 // buffer so none sat under a branch) ran no faster: 3.74-3.79 against 3.78
 // ms at 4 tiles per workgroup.
-constexpr int IT_TPW = 1;
 constexpr int IT_RESIDENT = 7;
 
 template <int DT>
-__global__ __launch_bounds__(256) void stream_acc_index_tile_kernel(const StreamArgs a, const int *gate)
+__global__ __launch_bounds__(256) void stream_acc_index_tile_kernel(const StreamArgs a, const int *gate,
+                                                                    int64_t tpw)
 {
     __shared__ float s_val[IT_TILE];
     __shared__ uint32_t s_bit[IT_TILE / 32];
@@ -1520,11 +1521,11 @@ __global__ __launch_bounds__(256) void stream_acc_index_tile_kernel(const Stream
     // the list's ends, as parameters of the accumulator (the list is sorted)
     const int64_t first = a.offset + a.idx[0];
     const int64_t last = a.offset + a.idx[a.len - 1];
-    const int64_t tb = first / IT_TILE + (int64_t)blockIdx.x * IT_TPW;
+    const int64_t tb = first / IT_TILE + (int64_t)blockIdx.x * tpw;
     const int64_t tl = last / IT_TILE;
     if (tb > tl)
         return;
-    const int64_t te = min(tb + IT_TPW, tl + 1);
+    const int64_t te = min(tb + tpw, tl + 1);
     if (tid < IT_TILE / 32)
         s_bit[tid] = 0u;
     if (tid == 0)
@@ -2096,16 +2097,19 @@ hipError_t launch_stream_accumulate_indices(const StreamArgs &a, int dt, bool ti
     }
     fill_u32_kernel<<<1, 64, 0, s>>>(reinterpret_cast<uint32_t *>(gate), 1, 0u);
     stream_index_check_kernel<<<g, 256, 0, s>>>(a, gate);
-    // tiles from the list's first parameter to its last: at most this many
-    // workgroups of IT_TPW tiles each
+    // tiles from the list's first parameter to its last: at most this many;
+    // one per workgroup, or consecutive runs of them where a grid of one per
+    // workgroup would exceed the dispatch limit (accumulators beyond 2^35
+    // parameters)
     const int64_t tiles = (a.N - a.offset) / IT_TILE + 2;
-    const unsigned gt = (unsigned)((tiles + IT_TPW - 1) / IT_TPW);
+    const unsigned gt = grid_for(tiles, 1, 0);
+    const int64_t tpw = ceil_div(tiles, (int64_t)gt);
     if (dt == DT_F32) {
         auto *k = &stream_acc_index_tile_kernel<DT_F32>;
-        k<<<gt, 256, residency_lds(k, IT_RESIDENT), s>>>(a, gate);
+        k<<<gt, 256, residency_lds(k, IT_RESIDENT), s>>>(a, gate, tpw);
     } else {
         auto *k = &stream_acc_index_tile_kernel<DT_BF16>;
-        k<<<gt, 256, residency_lds(k, IT_RESIDENT), s>>>(a, gate);
+        k<<<gt, 256, residency_lds(k, IT_RESIDENT), s>>>(a, gate, tpw);
     }
     // the scatter kernel runs only for a list the check refused: few
     // workgroups, each striding over the list
