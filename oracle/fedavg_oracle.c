@@ -228,23 +228,29 @@ int orc_sparse_average(int K, const int64_t *const *idx, const float *const *val
         rc = ORC_ERR_NOMEM;
         goto done;
     }
-    for (int k = 0; k < K && rc == ORC_OK; ++k) {
+    /* every list checked whole, one client per thread */
+    int bad = 0;
+    const int Kv = rc == ORC_OK ? K : 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int k = 0; k < Kv; ++k) {
         if (n[k] == 0)
             continue;
         for (int64_t j = 0; j < nnz[k]; ++j) {
             int64_t i = idx[k][j];
             if (i < 0 || i >= N || (j > 0 && i <= idx[k][j - 1])) {
-                rc = ORC_ERR_INDEX;
+                bad = 1;
                 break;
             }
         }
     }
+    if (bad)
+        rc = ORC_ERR_INDEX;
     /* client by client in order for every parameter; the parameters are
        split into blocks, one thread per block, each block visiting every
        client's entries inside it */
     const int64_t B = (int64_t)1 << 16;
     const int64_t nb = rc == ORC_OK ? (N + B - 1) / B : 0;
-#pragma omp parallel for schedule(dynamic, 16)
+#pragma omp parallel for schedule(dynamic, 1)
     for (int64_t b = 0; b < nb; ++b) {
         const int64_t lo = b * B, hi = lo + B < N ? lo + B : N;
         for (int k = 0; k < K; ++k) {
@@ -489,7 +495,7 @@ int orc_sparse_mirror_f32(int K, const int64_t *const *idx, const float *const *
        inside a block the clients in order */
     const int64_t B = (int64_t)1 << 16;
     const int64_t nb = (len + B - 1) / B;
-#pragma omp parallel for schedule(dynamic, 16)
+#pragma omp parallel for schedule(dynamic, 1)
     for (int64_t b = 0; b < nb; ++b) {
         const int64_t lo = first + b * B, hi = lo + B < first + len ? lo + B : first + len;
         for (int k = 0; k < K; ++k) {
