@@ -109,24 +109,40 @@ def free_gpu():
 # --------------------------------------------------------------------------
 
 def bench_dense_2b(steps, warmup):
+    """The headline: the 16 clients and the output in one allocation laid out
+    by the library's arena_layout (buffer j staggered j x 64 KiB within its
+    2 MiB page); then the same clients copied into separate allocations,
+    timed the same way for comparison (same bits required)."""
     import torch
+    import synth
     import synth.device as sd
     import weighted_model_update_amd as fa
-    log("dense 2B: generating 16 bf16 clients")
-    n, xs = sd.dense_2b()
-    K, N = len(xs), xs[0].numel()
-    out = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    K, N = 16, synth.numel_of(synth.dense_2b_tensor_shapes())
+    log("dense 2B: generating 16 bf16 clients in one staggered allocation")
+    arena, views = fa.client_arena(K + 1, N, torch.bfloat16)
+    n, xs = sd.dense_2b(K=K, N=N, dest=views[:K])
+    out = views[K]
     nl = n.tolist()
     log(f"dense 2B: K={K} N={N} timing {steps} steps")
     wall, durs = timed(lambda i: fa.fedavg_aggregate(xs, nl, out), steps, warmup)
     out_hash = fa.fedavg_checksum(out)
-    del xs, out
+    log("dense 2B: the same clients in separate allocations")
+    sep = [x.clone() for x in xs]
+    out_sep = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    _, durs_sep = timed(lambda i: fa.fedavg_aggregate(sep, nl, out_sep), steps, warmup)
+    same = bool(torch.equal(out.view(torch.int16), out_sep.view(torch.int16)))
+    del xs, out, views, arena, sep, out_sep
     free_gpu()
+    assert same, "the two layouts gave different outputs"
     algo_bytes = (K + 1) * 2 * N
-    st = stats(durs)
+    st, st_sep = stats(durs), stats(durs_sep)
     return {
         "K": K, "N": N, "wall_s": wall, "avg_launch_ms": st["mean_ms"], "min_launch_ms": st["min_ms"],
         "median_launch_ms": st["median_ms"], "algo_bytes": algo_bytes, "out_checksum": f"{out_hash:016x}",
+        "separate_allocations": {"avg_launch_ms": st_sep["mean_ms"], "median_launch_ms": st_sep["median_ms"],
+                                 "min_launch_ms": st_sep["min_ms"],
+                                 "hbm_frac": algo_bytes / (st_sep["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "same_output": same},
     }
 
 
@@ -991,7 +1007,8 @@ def main():
     head = None
     if "dense" in only:
         head = bench_dense_2b(args.steps, args.warmup)
-        log(f"dense 2B: {head['avg_launch_ms']:.3f} ms/launch")
+        log(f"dense 2B: {head['avg_launch_ms']:.3f} ms/launch "
+            f"({head['separate_allocations']['avg_launch_ms']:.3f} in separate allocations)")
     if "dense_small" in only:
         modes["dense_small"] = bench_dense_small()
         log(f"dense_small: {modes['dense_small']['us_per_call']:.2f} us/call, "
@@ -1052,6 +1069,8 @@ def main():
             "config": {"workload": "dense FedAvg, K=16 resident bf16 clients of a 1,921,878,016-parameter "
                                    "transformer tensor list, fp32 accumulation, bf16 output",
                        "K": head["K"], "N": head["N"], "mode": "weights", "io_dtype": "bf16",
+                       "buffers": "the 16 clients and the output in one allocation, buffer j at "
+                                  "j x (2 MiB-rounded size + 64 KiB) (arena_layout)",
                        "hbm_gbs": achieved},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(),
@@ -1059,7 +1078,8 @@ def main():
                          "algo_bytes_per_launch": head["algo_bytes"],
                          "avg_launch_ms": head["avg_launch_ms"],
                          "median_launch_ms": head["median_launch_ms"],
-                         "min_launch_ms": head["min_launch_ms"]},
+                         "min_launch_ms": head["min_launch_ms"],
+                         "separate_allocations": head["separate_allocations"]},
         })
     else:
         rec.update({"value": None, "ms_per_step": None, "config": {"workload": "partial run: " + args.only}})

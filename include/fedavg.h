@@ -150,6 +150,28 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
                      fa_dtype out_dtype, int T, const int64_t *seg_bounds, const uint8_t *present,
                      void *stream);
 
+/*
+ * fedavg_arena_layout -- where to put the buffers of one resident
+ * aggregation (the K client updates the server holds for a round, Clara
+ * page, section "Server-side workflow", and the output) inside a single
+ * device allocation that the caller makes.  The dense pass reads the same
+ * parameter of every client at the same moment; buffers from separate
+ * allocations start at the same position within a 2 MiB page, so those
+ * addresses share their low 21 bits.  Here buffer j starts at
+ *     offsets[j] = j * (round_up(bytes, 2 MiB) + 64 KiB),
+ * that is 64 KiB further into its page than buffer j - 1 (modulo 2 MiB).
+ * count        buffers, 1 to FA_ARENA_MAX_BUFFERS.
+ * bytes        bytes per buffer, >= 0.
+ * offsets      host int64[count], written (multiples of 64 KiB: every buffer
+ *              is 16-byte aligned when the allocation is).
+ * total_bytes  host, written: the allocation's size, offsets[count-1] + bytes.
+ * Host only, no device work and no allocation.  FA_ERR_ARG for a count out of
+ * range, a negative size or a NULL pointer; FA_ERR_RANGE when the total would
+ * exceed 2^62 bytes.
+ */
+#define FA_ARENA_MAX_BUFFERS 4096
+int fedavg_arena_layout(int count, int64_t bytes, int64_t *offsets, int64_t *total_bytes);
+
 /* ------------------------------------------------------------------------
  * Streaming: clients arrive one after another, each as chunks, into one
  * resident fp32 accumulator, so device memory does not grow with K.

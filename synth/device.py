@@ -54,9 +54,10 @@ def adapter(device="cuda", K=8, p=0.6):
     return n, xs, base, np.asarray(bounds, np.int64), present
 
 
-def dense_2b(device="cuda", K=16, N=None):
+def dense_2b(device="cuda", K=16, N=None, dest=None):
     """K bf16 clients of the 2.0B-parameter tensor list: base ~N(0,0.02) in
-    fp32, client k = bf16(base + N(0,1e-3)); n_k in [100,1000]."""
+    fp32, client k = bf16(base + N(0,1e-3)); n_k in [100,1000].  dest: K bf16
+    tensors of N elements to write the clients into (else new tensors)."""
     if N is None:
         N = numel_of(dense_2b_tensor_shapes())
     n = sample_counts(CFG_DENSE_2B, K, 100, 1000)
@@ -65,7 +66,11 @@ def dense_2b(device="cuda", K=16, N=None):
     for k in range(K):
         pert = normal(N, 1e-3, generator(CFG_DENSE_2B, ROLE_VALUES, k, device), device=device)
         pert.add_(base)
-        xs.append(pert.to(torch.bfloat16))
+        if dest is None:
+            xs.append(pert.to(torch.bfloat16))
+        else:
+            dest[k].copy_(pert)          # the same round-to-nearest-even conversion
+            xs.append(dest[k])
         del pert
     del base
     return n, xs

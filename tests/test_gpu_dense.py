@@ -174,3 +174,27 @@ def test_dense_argument_errors():
     with pytest.raises(fa.FedAvgError) as e:
         fa.fedavg_aggregate([x] * 65, [1] * 65, out)
     assert e.value.code == -3
+
+
+@pytest.mark.parametrize("K", [3, 16])
+def test_clients_in_one_staggered_allocation(K):
+    """The clients and the output placed by client_arena (arena_layout) sit at
+    the offsets the layout gives and aggregate to the same bits as separate
+    buffers, which are the oracle mirror's bits."""
+    N = 3 * (1 << 20) + 1235                    # not a whole number of pages
+    xs = make_clients(41, K, N, "bf16")
+    n = [int(v) for v in np.random.default_rng(42).integers(100, 1001, K)]
+    arena, views = fa.client_arena(K + 1, N, torch.bfloat16)
+    offs, total = fa.arena_layout(K + 1, 2 * N)
+    assert arena.numel() == total
+    assert [v.data_ptr() - arena.data_ptr() for v in views] == offs
+    sep = [dev_of(x, "bf16") for x in xs]
+    for v, x in zip(views, sep):
+        v.copy_(x)
+    out_sep = empty(N, "bf16")
+    fa.fedavg_aggregate(sep, n, out_sep)
+    fa.fedavg_aggregate(views[:K], n, views[K])
+    torch.cuda.synchronize()
+    want = oracle.mirror_f32(xs, n, x_dtype=oracle.BF16, out_dtype=oracle.BF16)
+    assert np.array_equal(host_of(out_sep), want)
+    assert np.array_equal(host_of(views[K]), want)

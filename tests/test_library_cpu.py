@@ -47,6 +47,37 @@ def _lib():
     return fa.load()
 
 
+@pytest.mark.parametrize("nbytes", [0, 1, 4096, (2 << 20) - 1, 2 << 20, (2 << 20) + 16, 3_843_756_032])
+@pytest.mark.parametrize("count", [1, 2, 17, 33, 65])
+def test_arena_layout_staggers_disjoint_buffers(count, nbytes):
+    """Buffer j lies 64 KiB further into its 2 MiB page than buffer j - 1
+    (modulo 2 MiB), buffers never overlap, every offset is 16-byte aligned
+    and the total ends with the last buffer."""
+    offs, total = fa.arena_layout(count, nbytes)
+    page, step = 2 << 20, 64 << 10
+    assert offs[0] == 0 and total == offs[-1] + nbytes
+    for j in range(1, count):
+        assert offs[j] >= offs[j - 1] + nbytes
+        assert offs[j] % 16 == 0
+        assert offs[j] % page == (j * step) % page
+        assert offs[j] - offs[j - 1] < nbytes + page + step
+
+
+def test_arena_layout_argument_errors():
+    lib = _lib()
+    offs = (ctypes.c_int64 * 4)()
+    total = ctypes.c_int64()
+    assert lib.fedavg_arena_layout(0, 10, offs, ctypes.byref(total)) == -1
+    assert lib.fedavg_arena_layout(4097, 10, offs, ctypes.byref(total)) == -1
+    assert lib.fedavg_arena_layout(4, -1, offs, ctypes.byref(total)) == -1
+    assert lib.fedavg_arena_layout(4, 10, None, ctypes.byref(total)) == -1
+    assert lib.fedavg_arena_layout(4, 10, offs, None) == -1
+    assert lib.fedavg_arena_layout(4, 1 << 61, offs, ctypes.byref(total)) == -3
+    assert lib.fedavg_arena_layout(4, (1 << 62) - (4 << 20), offs, ctypes.byref(total)) == -3
+    assert lib.fedavg_arena_layout(1, (1 << 62) - (4 << 20), offs, ctypes.byref(total)) == 0
+    assert total.value == (1 << 62) - (4 << 20)
+
+
 def test_host_side_argument_errors_need_no_device():
     lib = _lib()
     P = ctypes.c_void_p

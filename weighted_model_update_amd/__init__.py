@@ -10,6 +10,7 @@ from .fedavg import (  # noqa: F401
     FA_OPT_TOPK_SAMPLED, FA_OPT_INDEX_TILES,
     EXPORTS, FedAvgError, StreamingAccumulator, load, library_path,
     fedavg_abi_version, fedavg_set_option, fedavg_aggregate, fedavg_workspace_size,
+    arena_layout, client_arena,
     fedavg_begin, fedavg_accumulate, fedavg_finalize, fedavg_sync, fedavg_destroy,
     fedavg_accumulate_partial, fedavg_partial_info, fedavg_export_state, fedavg_resume,
     sparse_workspace_size, sparse_masked_accumulate, sparse_masked_accumulate_noalloc, fedavg_checksum,

@@ -324,6 +324,25 @@ extern "C" {
 
 int fedavg_abi_version(void) { return FEDAVG_ABI_VERSION; }
 
+int fedavg_arena_layout(int count, int64_t bytes, int64_t *offsets, int64_t *total_bytes)
+{
+    if (count < 1 || count > FA_ARENA_MAX_BUFFERS)
+        return fail(FA_ERR_ARG, "count=%d outside [1, %d]", count, FA_ARENA_MAX_BUFFERS);
+    if (bytes < 0 || !offsets || !total_bytes)
+        return fail(FA_ERR_ARG, "need bytes >= 0 and both result pointers");
+    constexpr int64_t PAGE = (int64_t)2 << 20, STAGGER = (int64_t)64 << 10, LIMIT = (int64_t)1 << 62;
+    if (bytes > LIMIT - PAGE)
+        return fail(FA_ERR_RANGE, "bytes=%lld is too large", (long long)bytes);
+    // each buffer rounded up to whole pages, then one stagger step more
+    const int64_t pitch = (bytes + PAGE - 1) / PAGE * PAGE + STAGGER;
+    if ((int64_t)(count - 1) > (LIMIT - bytes) / pitch)
+        return fail(FA_ERR_RANGE, "%d buffers of %lld bytes exceed 2^62 bytes", count, (long long)bytes);
+    for (int j = 0; j < count; ++j)
+        offsets[j] = (int64_t)j * pitch;
+    *total_bytes = (int64_t)(count - 1) * pitch + bytes;
+    return ok();
+}
+
 const char *fedavg_last_error(void) { return g_last_error.c_str(); }
 
 int fedavg_set_option(int option, int64_t value)

@@ -38,6 +38,7 @@ EXPORTS = [
     "fedavg_resume", "topk_workspace_size", "topk_select", "fedavg_controller_step",
     "sparse_workspace_size", "sparse_masked_accumulate", "fedavg_checksum", "fedavg_set_option",
     "fedavg_sum_workspace_size", "fedavg_checksum_sum", "sparse_masked_accumulate_noalloc",
+    "fedavg_arena_layout",
 ]
 
 
@@ -91,6 +92,7 @@ def load(build_if_missing=True):
         "fedavg_controller_step": ([i32, P, P, P, i64, P, P, P, i32, P], i32),
         "topk_select": ([P, i32, i64, i64, P, P, P, sz, P], i32),
         "fedavg_set_option": ([i32, i64], i32),
+        "fedavg_arena_layout": ([i32, i64, P, P], i32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -217,6 +219,28 @@ def fedavg_aggregate(xs, n, out, mode="weights", base=None, seg_bounds=None, pre
                               _ptr(out), _dtype(out), T, _ptr(seg_bounds), _ptr(present),
                               _stream_handle(stream))
     _check(rc)
+
+
+def arena_layout(count, nbytes):
+    """(offsets, total_bytes): byte offsets of `count` buffers of `nbytes`
+    bytes inside one allocation of total_bytes, each 64 KiB further into its
+    2 MiB page than the one before (fedavg_arena_layout in include/fedavg.h)."""
+    offs = (ctypes.c_int64 * int(count))()
+    total = ctypes.c_int64(0)
+    _check(load().fedavg_arena_layout(int(count), int(nbytes), offs, ctypes.byref(total)))
+    return list(offs), total.value
+
+
+def client_arena(count, numel, dtype=torch.bfloat16, device="cuda"):
+    """One device allocation holding `count` tensors of `numel` elements of
+    `dtype`, placed by arena_layout (for example the K clients and the output
+    of a resident aggregation).  Returns (arena, [tensor, ...]); the tensors
+    are views of the arena, which must outlive them."""
+    esize = torch.empty(0, dtype=dtype).element_size()
+    offs, total = arena_layout(count, int(numel) * esize)
+    arena = torch.empty(total, dtype=torch.uint8, device=device)
+    views = [arena[o:o + int(numel) * esize].view(dtype) for o in offs]
+    return arena, views
 
 
 # ------------------------------------------------------------------ streaming
