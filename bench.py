@@ -110,7 +110,7 @@ def free_gpu():
 
 def bench_dense_2b(steps, warmup):
     """The headline: the 16 clients and the output in one allocation laid out
-    by the library's arena_layout (buffer j staggered j x 64 KiB within its
+    by the library's arena_layout (buffer j staggered j x 32 KiB within its
     2 MiB page); then the same clients copied into separate allocations,
     timed the same way for comparison (same bits required)."""
     import torch
@@ -604,7 +604,8 @@ def bench_dense_k(Ks=(4, 8, 16, 20, 32, 64), total_bytes=65_343_852_544, reps=10
     of their own; the others take the generic kernel (clients in batches of
     8, of 16 above 16 clients).  The residency cap follows the client count
     (the library's default).  Values do not change the time, so the clients are filled with a
-    constant."""
+    constant.  Each K runs with separate allocations and again with the
+    clients and output in one arena_layout allocation."""
     import torch
     import weighted_model_update_amd as fa
     rows = []
@@ -615,16 +616,26 @@ def bench_dense_k(Ks=(4, 8, 16, 20, 32, 64), total_bytes=65_343_852_544, reps=10
         n = [100 + 37 * k for k in range(K)]
         _, d = timed(lambda i: fa.fedavg_aggregate(xs, n, out), reps, warmup)
         st = stats(d)
+        del xs, out
+        free_gpu()
+        arena, views = fa.client_arena(K + 1, N, torch.bfloat16)
+        for k in range(K):
+            views[k].fill_(0.01 * (k + 1))
+        _, d = timed(lambda i: fa.fedavg_aggregate(views[:K], n, views[K]), reps, warmup)
+        sta = stats(d)
+        del arena, views
+        free_gpu()
         nb = (K + 1) * 2 * N
         rows.append({"K": K, "N": N, "bytes": nb, **st,
                      "hbm_gbs_median": nb / (st["median_ms"] * 1e-3) / 1e9,
                      "hbm_frac_median": nb / (st["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "params_per_s_median": K * N / (st["median_ms"] * 1e-3),
+                     "arena_median_ms": sta["median_ms"], "arena_min_ms": sta["min_ms"],
+                     "arena_hbm_frac_median": nb / (sta["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "kernel": ("dense_vec_kernel<K>" if K in (3, 8, 16) else
                                 "dense_vec_kernel<batches of 16>" if K > 16 else "dense_vec_kernel<batches of 8>")})
-        log(f"dense K={K}: {st['median_ms']:.3f} ms median, {rows[-1]['hbm_frac_median']:.3f} of peak")
-        del xs, out
-        free_gpu()
+        log(f"dense K={K}: {st['median_ms']:.3f} ms median, {rows[-1]['hbm_frac_median']:.3f} of peak; "
+            f"in an arena {sta['median_ms']:.3f} ms, {rows[-1]['arena_hbm_frac_median']:.3f}")
     return {"rows": rows}
 
 
@@ -784,7 +795,8 @@ def bench_ceiling(reps=10, warmup=2, residents=(2, 0, 1, 3, 4)):
     read, one written) with no arithmetic, over load and store cache
     policies, write batching and residency caps; the 16- and 17-stream reads
     alone and a plain copy bound it from both sides.  The dense kernel itself
-    is timed on the same buffers at each residency cap."""
+    is timed on the same buffers at each residency cap.  The 17 buffers lie
+    in one allocation placed by arena_layout, as the headline's do."""
     import ctypes
     import torch
     import synth
@@ -798,7 +810,8 @@ def bench_ceiling(reps=10, warmup=2, residents=(2, 0, 1, 3, 4)):
     N = synth.numel_of(synth.dense_2b_tensor_shapes())
     nvec = N * 2 // 16
     log(f"ceiling: 17 streams of {nvec * 16} bytes")
-    bufs = [torch.empty(nvec * 16, dtype=torch.uint8, device="cuda") for _ in range(17)]
+    # laid out as the headline's clients and output are (arena_layout)
+    arena, bufs = fa.client_arena(17, nvec * 16, torch.uint8)
     for i, b in enumerate(bufs):
         b.view(torch.int32).fill_(0x3c003c00 + i)        # bf16 values near 1, distinct per stream
     srcs = (ctypes.c_void_p * 17)(*[b.data_ptr() for b in bufs])
@@ -843,7 +856,7 @@ def bench_ceiling(reps=10, warmup=2, residents=(2, 0, 1, 3, 4)):
         finally:
             fa.fedavg_set_option(fa.FA_OPT_RESIDENT_PER_CU, -1)
         log(f"ceiling: resident {res} done")
-    del bufs
+    del bufs, arena
     free_gpu()
     mixed = [r for r in rows if r["streams_read"] == 16 and r["stream_written"] and r["load"] != "kernel"]
     best = min(mixed, key=lambda r: r["median_ms"])
@@ -1070,7 +1083,7 @@ def main():
                                    "transformer tensor list, fp32 accumulation, bf16 output",
                        "K": head["K"], "N": head["N"], "mode": "weights", "io_dtype": "bf16",
                        "buffers": "the 16 clients and the output in one allocation, buffer j at "
-                                  "j x (2 MiB-rounded size + 64 KiB) (arena_layout)",
+                                  "j x (2 MiB-rounded size + 32 KiB) (arena_layout)",
                        "hbm_gbs": achieved},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_counters(),

@@ -158,11 +158,11 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
  * parameter of every client at the same moment; buffers from separate
  * allocations start at the same position within a 2 MiB page, so those
  * addresses share their low 21 bits.  Here buffer j starts at
- *     offsets[j] = j * (round_up(bytes, 2 MiB) + 64 KiB),
- * that is 64 KiB further into its page than buffer j - 1 (modulo 2 MiB).
+ *     offsets[j] = j * (round_up(bytes, 2 MiB) + 32 KiB),
+ * that is 32 KiB further into its page than buffer j - 1 (modulo 2 MiB).
  * count        buffers, 1 to FA_ARENA_MAX_BUFFERS.
  * bytes        bytes per buffer, >= 0.
- * offsets      host int64[count], written (multiples of 64 KiB: every buffer
+ * offsets      host int64[count], written (multiples of 32 KiB: every buffer
  *              is 16-byte aligned when the allocation is).
  * total_bytes  host, written: the allocation's size, offsets[count-1] + bytes.
  * Host only, no device work and no allocation.  FA_ERR_ARG for a count out of

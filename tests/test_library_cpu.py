@@ -50,11 +50,11 @@ def _lib():
 @pytest.mark.parametrize("nbytes", [0, 1, 4096, (2 << 20) - 1, 2 << 20, (2 << 20) + 16, 3_843_756_032])
 @pytest.mark.parametrize("count", [1, 2, 17, 33, 65])
 def test_arena_layout_staggers_disjoint_buffers(count, nbytes):
-    """Buffer j lies 64 KiB further into its 2 MiB page than buffer j - 1
+    """Buffer j lies 32 KiB further into its 2 MiB page than buffer j - 1
     (modulo 2 MiB), buffers never overlap, every offset is 16-byte aligned
     and the total ends with the last buffer."""
     offs, total = fa.arena_layout(count, nbytes)
-    page, step = 2 << 20, 64 << 10
+    page, step = 2 << 20, 32 << 10
     assert offs[0] == 0 and total == offs[-1] + nbytes
     for j in range(1, count):
         assert offs[j] >= offs[j - 1] + nbytes

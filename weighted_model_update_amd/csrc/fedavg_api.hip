@@ -330,7 +330,7 @@ int fedavg_arena_layout(int count, int64_t bytes, int64_t *offsets, int64_t *tot
         return fail(FA_ERR_ARG, "count=%d outside [1, %d]", count, FA_ARENA_MAX_BUFFERS);
     if (bytes < 0 || !offsets || !total_bytes)
         return fail(FA_ERR_ARG, "need bytes >= 0 and both result pointers");
-    constexpr int64_t PAGE = (int64_t)2 << 20, STAGGER = (int64_t)64 << 10, LIMIT = (int64_t)1 << 62;
+    constexpr int64_t PAGE = (int64_t)2 << 20, STAGGER = (int64_t)32 << 10, LIMIT = (int64_t)1 << 62;
     if (bytes > LIMIT - PAGE)
         return fail(FA_ERR_RANGE, "bytes=%lld is too large", (long long)bytes);
     // each buffer rounded up to whole pages, then one stagger step more

@@ -223,7 +223,7 @@ def fedavg_aggregate(xs, n, out, mode="weights", base=None, seg_bounds=None, pre
 
 def arena_layout(count, nbytes):
     """(offsets, total_bytes): byte offsets of `count` buffers of `nbytes`
-    bytes inside one allocation of total_bytes, each 64 KiB further into its
+    bytes inside one allocation of total_bytes, each 32 KiB further into its
     2 MiB page than the one before (fedavg_arena_layout in include/fedavg.h)."""
     offs = (ctypes.c_int64 * int(count))()
     total = ctypes.c_int64(0)
