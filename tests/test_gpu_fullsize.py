@@ -91,14 +91,22 @@ def o1_window(i):
 
 
 def test_dense_2b_k16_bf16_whole_output():
-    n, xs = sd.dense_2b()
-    N = xs[0].numel()
+    # the clients and the output laid out as the benchmark's headline has them
+    N = synth.numel_of(synth.dense_2b_tensor_shapes())
+    arena, views = fa.client_arena(17, N, torch.bfloat16)
+    n, xs = sd.dense_2b(N=N, dest=views[:16])
+    out = views[16]
     assert N == 1_921_878_016 and len(xs) == 16
-    out = torch.empty(N, dtype=torch.bfloat16, device="cuda")
     fa.fedavg_aggregate(xs, n.tolist(), out)
     h1 = fa.fedavg_checksum(out)
     fa.fedavg_aggregate(xs, n.tolist(), out)
     assert fa.fedavg_checksum(out) == h1          # bit-identical rerun
+    # the same clients in separate allocations give the same bits
+    sep = [x.clone() for x in xs]
+    out_sep = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    fa.fedavg_aggregate(sep, n.tolist(), out_sep)
+    assert fa.fedavg_checksum(out_sep) == h1
+    del sep, out_sep
     hw = HostWindows()
     want_hash = 0
     o1_elems = 0
