@@ -160,6 +160,9 @@ int fedavg_aggregate(int K, const void *const *x, fa_dtype x_dtype, const int64_
  * addresses share their low 21 bits.  Here buffer j starts at
  *     offsets[j] = j * (round_up(bytes, 2 MiB) + 32 KiB),
  * that is 32 KiB further into its page than buffer j - 1 (modulo 2 MiB).
+ * Measured on MI355X with 16 bf16 clients of 1.92e9 parameters and the
+ * output: about 5% faster than separate allocations, on every allocation
+ * tried; with 8 or 32 clients the two were within their run-to-run spread.
  * count        buffers, 1 to FA_ARENA_MAX_BUFFERS.
  * bytes        bytes per buffer, >= 0.
  * offsets      host int64[count], written (multiples of 32 KiB: every buffer
